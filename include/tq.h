@@ -1,0 +1,181 @@
+/*
+ * tq.h - C ABI of the TurboQuant compressed KV-cache library for AMD MI355X
+ * (gfx950).  Plain pointers and sizes only; every device pointer is memory the
+ * caller owns (the library owns only the constant tables inside a tq_ctx).
+ *
+ * Method sources (web pages this library implements):
+ *  - "aither-kvcache" PyPI README, section "Algorithm": normalise (L2 norm
+ *    stored as f32), rotate by a fixed random orthogonal matrix, quantise each
+ *    coordinate with a precomputed Lloyd-Max codebook, pack the indices.
+ *  - "TurboQuant on a 16GB MacBook" (yashrajpandey.com), sections "Why this
+ *    caught my eye" and "The QJL detective story": for keys, a 1-bit QJL sketch
+ *    sign(S r) of the quantisation residual r with Gaussian S, dequantised
+ *    with scale sqrt(pi/2)/d.
+ *  - "TurboQuant Family Design Study for CPU and Browser WASM KV Caches"
+ *    (iarpg.com): post-RoPE placement and the query transformed into the same
+ *    basis (section "Placement relative to RoPE and attention"), fixed-size
+ *    pages with a 64-byte header and a recent FP16 window (sections "Packed
+ *    format and complete bit accounting", "Paging, lifecycle, and cache
+ *    identity"), compressed-domain key scan and rotated-domain value
+ *    accumulation with one inverse transform per head (section "CPU and WASM
+ *    kernel design"), the randomized Hadamard transform (section "Dense and
+ *    structured transform comparison").
+ *
+ * Conventions
+ *  - All calls return 0 (TQ_OK) or a negative TQ_ERR_* code; arguments are
+ *    validated on the host before anything is launched, and a failing call
+ *    launches nothing.  No exceptions cross the ABI.
+ *  - Calls that take a stream enqueue asynchronous work on it (a hipStream_t
+ *    passed as void*; NULL is the default stream) and do not synchronise,
+ *    except tq_codebook_init (uploads tables, then synchronises the stream)
+ *    and tq_get_status (reads the status word back).  No device memory is
+ *    allocated in hot calls.  A tq_ctx is immutable after init apart from its
+ *    status word, so calls on different streams may share it.
+ *  - head_dim d = 128 is the size the kernels are built for.
+ *
+ * Page format (one page = one layer x one sequence x P tokens x all H_kv heads):
+ *   page_bytes = roundup(256 + H_kv * head_bytes, 256); 64-byte header at 0
+ *   (u32 magic 0x564B5154, u16 version 1, u16 d, u8 key_bits, u8 key_qjl,
+ *   u8 value_bits, u8 rotation, u16 H_kv, u16 P, u32 valid tokens, u32
+ *   codebook version 1, u64 seed, u32 page index, zeros); head h's body at
+ *   256 + h * head_bytes holds, in order: key norms f32[P]; key residual norms
+ *   f32[P] (QJL only); key codes u8[P][d*bK/8] token-major, LSB-first; key
+ *   signs u8[P][d/8] (QJL only); value norms f32[P]; value codes
+ *   u32[P/32][bV][d], where for each 32-token group and coordinate j the bV
+ *   words w = 0..bV-1 form a little-endian 32*bV-bit string holding token i's
+ *   code at bits [i*bV, (i+1)*bV).
+ * FP16 window: k_win, v_win [B][H_kv][W][d] fp16; the token at position t
+ *   lives in slot t mod W while it is among the last W tokens of its sequence.
+ *   A sequence of length T has max(T - W, 0) compressed tokens (positions
+ *   0 .. T-W-1, position t in page block_table[b][t / P], slot t mod P).
+ */
+#ifndef TQ_H_
+#define TQ_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define TQ_API __attribute__((visibility("default")))
+
+enum {
+  TQ_OK = 0,
+  TQ_ERR_INVALID_ARG = -1, /* null pointer, size out of range, inconsistent shapes */
+  TQ_ERR_UNSUPPORTED = -2, /* valid request that this build has no kernel for */
+  TQ_ERR_WORKSPACE = -3,   /* workspace smaller than tq_decode_workspace_bytes() */
+  TQ_ERR_HIP = -4,         /* a HIP runtime call failed (no device, launch error) */
+};
+
+enum { TQ_ROT_DENSE = 0, TQ_ROT_HADAMARD = 1 };
+enum { TQ_DTYPE_F16 = 0, TQ_DTYPE_BF16 = 1, TQ_DTYPE_F32 = 2 };
+enum { TQ_KIND_KEY = 0, TQ_KIND_VALUE = 1 };
+
+/* Bits of the device status word (tq_get_status). */
+enum {
+  TQ_STATUS_BAD_PAGE = 1, /* a block-table entry needed by a call was < 0 or >= num_pages;
+                             that sequence was left unchanged (append) or skipped (decode) */
+  TQ_STATUS_BAD_COUNT = 2 /* a per-sequence new-token count was < 0 or > n_new */
+};
+
+typedef struct tq_params {
+  int32_t head_dim;     /* d; 128 */
+  int32_t key_bits;     /* MSE bits per key coordinate, 2..4 */
+  int32_t key_qjl;      /* 1: keys carry the QJL sign sketch and residual norm */
+  int32_t value_bits;   /* bits per value coordinate, 2..4 */
+  int32_t rotation;     /* TQ_ROT_DENSE or TQ_ROT_HADAMARD */
+  int32_t num_q_heads;  /* H_q */
+  int32_t num_kv_heads; /* H_kv; H_q % H_kv == 0, query head g reads kv head g / (H_q/H_kv) */
+  int32_t page_tokens;  /* P, a multiple of 32, at most 1024 */
+  int32_t window;       /* W, FP16 recent tokens per sequence, 0..1024 */
+  int32_t reserved;
+  uint64_t seed;        /* recorded in page headers (cache identity); draws come from the caller */
+} tq_params;
+
+typedef struct tq_ctx tq_ctx;
+
+/* Host-only: compute the constant tables exactly as tq_codebook_init stores
+ * them, without touching a GPU.  rot_draws: DENSE: d*d i.i.d. N(0,1) values
+ * (row-major) whose QR Q factor, with the signs of diag(R) folded in, is the
+ * rotation Pi (y = Pi x); HADAMARD: d values whose signs (x < 0 -> -1, else +1)
+ * are the Rademacher stage.  qjl_draws: d*d N(0,1) values, the QJL matrix S
+ * itself (row i gives sign bit i); may be NULL when key_qjl == 0.
+ * Outputs (each nullable): rotation d*d f32 (DENSE: Pi row-major; HADAMARD:
+ * the d signs), qjl d*d f32, key/value centroids 2^b f32 (Lloyd-Max levels of
+ * N(0,1) times 1/sqrt(d)), key/value boundaries 2^b - 1 f32 (midpoints).
+ * Returns TQ_ERR_INVALID_ARG for bad params or missing draws. */
+TQ_API int tq_host_tables(const tq_params* params, const double* rot_draws, const double* qjl_draws,
+                          float* rotation, float* qjl, float* key_centroids, float* key_boundaries,
+                          float* value_centroids, float* value_boundaries);
+
+/* Build a context on the current HIP device: computes the tables above (host,
+ * double precision, rounded to f32) and uploads them.  *out receives the
+ * context, to be released with tq_destroy.  Host pointers; the stream is used
+ * for the upload and synchronised before return. */
+TQ_API int tq_codebook_init(tq_ctx** out, const tq_params* params, const double* rot_draws,
+                            const double* qjl_draws, void* stream);
+
+TQ_API int tq_destroy(tq_ctx* ctx);
+
+/* Bytes of one page for these params (see the page format above); <0 on bad params. */
+TQ_API int64_t tq_page_bytes(const tq_params* params);
+
+/* Encode n vectors (device pointers) into flat records:
+ *   x: [n][row_stride] elements of dtype (F16, BF16 or F32), first d used;
+ *   codes: [n][d*b/8] u8 LSB-first, b = key_bits or value_bits by kind;
+ *   norms: [n] f32 L2 norms;
+ *   signs: [n][d/8] u8 and rnorms: [n] f32, required iff kind == KEY and key_qjl.
+ * A vector with zero norm gets all-zero codes, signs and rnorm. */
+TQ_API int tq_encode(const tq_ctx* ctx, int kind, const void* x, int dtype, int64_t n, int64_t row_stride,
+                     uint8_t* codes, uint8_t* signs, float* norms, float* rnorms, void* stream);
+
+/* Append new tokens to every sequence of one layer's cache (device pointers).
+ *   page_pool: num_pages * tq_page_bytes bytes; block_table: [batch][max_pages] page ids;
+ *   seq_lens: [batch] tokens held so far, advanced by this call;
+ *   k_new, v_new: [batch][H_kv][n_new][d] fp16 (bit patterns as uint16);
+ *   new_counts: [batch] tokens to take from each sequence's rows (<= n_new), or NULL for n_new each;
+ *   k_win, v_win: [batch][H_kv][W][d] fp16 rings (may be NULL when W == 0).
+ * For each sequence, tokens that leave the last-W window are encoded (from their
+ * FP16 values) into their page slots, the page headers are rewritten, the new
+ * tokens still inside the window go to the ring, and seq_lens[b] grows by its
+ * count.  The caller reserves pages: every page a token lands in must be a valid
+ * id in block_table.  A sequence whose pages or count are invalid is left
+ * unchanged and raises a status bit (tq_get_status). */
+TQ_API int tq_append_page(const tq_ctx* ctx, uint8_t* page_pool, int64_t num_pages, const int32_t* block_table,
+                          int max_pages, int batch, int32_t* seq_lens, const uint16_t* k_new,
+                          const uint16_t* v_new, int n_new, const int32_t* new_counts, uint16_t* k_win,
+                          uint16_t* v_win, void* stream);
+
+/* Workspace bytes tq_decode_attn needs for this batch and block-table width. */
+TQ_API int64_t tq_decode_workspace_bytes(const tq_ctx* ctx, int batch, int max_pages, int pages_per_split);
+
+/* Decode attention for one query token per sequence (device pointers).
+ *   q: [batch][H_q][d] post-RoPE queries, dtype F16, BF16 or F32;
+ *   cache arguments as in tq_append_page (seq_lens[b] tokens, at most
+ *   max_pages * P + W);
+ *   sm_scale: logit scale (1/sqrt(d) for standard attention);
+ *   out: [batch][H_q][d] f32, softmax(q.k * sm_scale) weighted sum of values
+ *   over all seq_lens[b] tokens (zeros for an empty sequence);
+ *   workspace: >= tq_decode_workspace_bytes(ctx, batch, max_pages, pages_per_split);
+ *   pages_per_split: compressed pages per work-group (0 = chosen by the library);
+ *   dbg_logits: NULL, or [batch][H_q][logits_stride] f32 receiving each token's
+ *   logit q.k*sm_scale at its position index (for tests). */
+TQ_API int tq_decode_attn(const tq_ctx* ctx, const void* q, int q_dtype, const uint8_t* page_pool, int64_t num_pages,
+                          const int32_t* block_table, int max_pages, int batch, const int32_t* seq_lens,
+                          const uint16_t* k_win, const uint16_t* v_win, float sm_scale, float* out,
+                          void* workspace, size_t workspace_bytes, int pages_per_split, float* dbg_logits,
+                          int64_t logits_stride, void* stream);
+
+/* Read and clear the device status word (synchronises the context's device). */
+TQ_API int tq_get_status(tq_ctx* ctx, int* code);
+
+/* Text for a TQ_ERR_* code. */
+TQ_API const char* tq_strerror(int err);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TQ_H_ */

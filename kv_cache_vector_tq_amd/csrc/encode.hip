@@ -1,0 +1,431 @@
+// Encode kernels: flat records (tq_encode) and paged append (tq_append_page).
+//
+// Per vector x ("aither-kvcache" README, section "Algorithm"; keys' residual
+// sketch from "TurboQuant on a 16GB MacBook", sections "Why this caught my
+// eye" and "The QJL detective story"):
+//   n = ||x|| (accumulated in double, stored f32); y = Pi x / n;
+//   code_j = #{k : y_j > boundary_k} (ties to the lower index);
+//   keys: r = Pi x - n c[code], ||r||, sign bit j = [(S r)_j >= 0].
+// A work-group of 128 threads (thread = coordinate) handles a tile of 32
+// vectors held in LDS; rotations are fp32 VALU matrix-vector products with the
+// matrix row in registers and the tile broadcast from LDS, or sign flips plus
+// Walsh-Hadamard butterflies (wave shuffles, one LDS exchange for stride 64)
+// for the Hadamard variant; sign bits come from wave ballots.
+#include "device_common.h"
+#include "tq_internal.h"
+
+namespace tq {
+namespace {
+
+constexpr int kTile = 32;
+constexpr int kThreads = 128;
+
+struct Smem {
+  float xs[kTile][kD];   // input tile (f32)
+  float rs[kTile][kD];   // residuals / butterfly scratch
+  uint8_t code[kTile][kD];
+  float n32[kTile], invn[kTile], rn[kTile];
+  uint32_t sgn[kTile][4];
+  float ctab[16];
+};
+
+struct CoreParams {
+  int bits;
+  bool qjl;
+  float bnd[16];  // decision boundaries (uniform values)
+  float cen[16];  // centroids
+};
+
+__device__ inline CoreParams make_core(const Codebooks& cb, bool key, int bits, bool qjl) {
+  CoreParams cp;
+  cp.bits = bits;
+  cp.qjl = qjl;
+#pragma unroll
+  for (int k = 0; k < 16; ++k) {
+    cp.bnd[k] = key ? cb.kb[k] : cb.vb[k];
+    cp.cen[k] = key ? cb.kc[k] : cb.vc[k];
+  }
+  return cp;
+}
+
+// Rotate, quantise and (for keys) sketch the residual of the tile in LDS.
+// nv = number of live vectors (the rest are zero and produce zero records).
+template <bool HAD>
+__device__ void encode_core(Smem& sm, const DevTables& t, const CoreParams& cp, int nv) {
+  const int tid = threadIdx.x;
+  const int nb = (1 << cp.bits) - 1;
+  if (tid < 16) {
+    float cv = 0.0f;
+#pragma unroll
+    for (int k = 0; k < 16; ++k)
+      if (k == tid && k <= nb) cv = cp.cen[k];
+    sm.ctab[tid] = cv;
+  }
+  // norms in double: thread t sums a quarter of vector t/4
+  {
+    const int v = tid >> 2, part = tid & 3;
+    double s = 0.0;
+#pragma unroll 8
+    for (int j = 0; j < 32; ++j) {
+      const double e = sm.xs[v][part * 32 + j];
+      s = fma(e, e, s);
+    }
+    s += __shfl_xor(s, 1, 64);
+    s += __shfl_xor(s, 2, 64);
+    if (part == 0) {
+      const double n = sqrt(s);
+      sm.n32[v] = static_cast<float>(n);
+      sm.invn[v] = n > 0.0 ? static_cast<float>(1.0 / n) : 0.0f;
+    }
+  }
+  __syncthreads();
+  // quantise one vector's coordinate (this thread's) and keep the key residual
+  auto finish = [&](int v, float accv) {
+    const float n = sm.n32[v];
+    const float y = accv * sm.invn[v];
+    int c = 0;
+#pragma unroll
+    for (int k = 0; k < 15; ++k)
+      if (k < nb) c += (y > cp.bnd[k]) ? 1 : 0;
+    if (!(n > 0.0f)) c = 0;
+    sm.code[v][tid] = static_cast<uint8_t>(c);
+    if (cp.qjl) sm.rs[v][tid] = (n > 0.0f) ? fmaf(-n, sm.ctab[c], accv) : 0.0f;
+  };
+  if constexpr (!HAD) {
+    // two passes over halves of the rotation row keep the register count
+    // low; the first pass parks its partial sums in this thread's rs slots
+#pragma unroll
+    for (int hp = 0; hp < 2; ++hp) {
+      float pr[kD / 2];
+#pragma unroll
+      for (int j = 0; j < kD / 2; ++j) pr[j] = t.rotT[(hp * (kD / 2) + j) * kD + tid];
+#pragma unroll 1
+      for (int v = 0; v < kTile; ++v) {
+        float s = hp ? sm.rs[v][tid] : 0.0f;
+        if (v < nv) {
+          const float4* xr = reinterpret_cast<const float4*>(sm.xs[v]) + hp * (kD / 8);
+#pragma unroll
+          for (int j4 = 0; j4 < kD / 8; ++j4) {
+            const float4 x = xr[j4];
+            s = fmaf(pr[4 * j4 + 0], x.x, s);
+            s = fmaf(pr[4 * j4 + 1], x.y, s);
+            s = fmaf(pr[4 * j4 + 2], x.z, s);
+            s = fmaf(pr[4 * j4 + 3], x.w, s);
+          }
+        }
+        if (hp == 0)
+          sm.rs[v][tid] = s;
+        else
+          finish(v, s);
+      }
+    }
+  } else {
+    const float eps = t.rot[tid];
+    // strides 1..32 inside the wave, stride 64 through LDS
+    for (int v = 0; v < kTile; ++v) {
+      float val = sm.xs[v][tid] * eps;
+#pragma unroll
+      for (int s = 1; s < 64; s <<= 1) {
+        const float o = __shfl_xor(val, s, 64);
+        val = (tid & s) ? (o - val) : (val + o);
+      }
+      sm.rs[v][tid] = val;
+    }
+    __syncthreads();
+    float acc[kTile];
+    const float inv_sqrt_d = 0.08838834764831845f;  // 1/sqrt(128)
+#pragma unroll
+    for (int v = 0; v < kTile; ++v) {
+      const float a = sm.rs[v][tid], b = sm.rs[v][tid ^ 64];
+      acc[v] = ((tid & 64) ? (b - a) : (a + b)) * inv_sqrt_d;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int v = 0; v < kTile; ++v) finish(v, acc[v]);
+  }
+  if (!cp.qjl) return;
+  __syncthreads();
+  {
+    const int v = tid >> 2, part = tid & 3;
+    double s = 0.0;
+#pragma unroll 8
+    for (int j = 0; j < 32; ++j) {
+      const double e = sm.rs[v][part * 32 + j];
+      s = fma(e, e, s);
+    }
+    s += __shfl_xor(s, 1, 64);
+    s += __shfl_xor(s, 2, 64);
+    if (part == 0) sm.rn[v] = static_cast<float>(sqrt(s));
+  }
+  const int wave = tid >> 6, lane = tid & 63;
+  __syncthreads();  // xs is free from here on: it holds the first half of S r
+#pragma unroll
+  for (int hp = 0; hp < 2; ++hp) {
+    float sr[kD / 2];
+#pragma unroll
+    for (int j = 0; j < kD / 2; ++j) sr[j] = t.ST[(hp * (kD / 2) + j) * kD + tid];
+#pragma unroll 1
+    for (int v = 0; v < kTile; ++v) {
+      float z = hp ? sm.xs[v][tid] : 0.0f;
+      const float4* rr = reinterpret_cast<const float4*>(sm.rs[v]) + hp * (kD / 8);
+#pragma unroll
+      for (int j4 = 0; j4 < kD / 8; ++j4) {
+        const float4 r = rr[j4];
+        z = fmaf(sr[4 * j4 + 0], r.x, z);
+        z = fmaf(sr[4 * j4 + 1], r.y, z);
+        z = fmaf(sr[4 * j4 + 2], r.z, z);
+        z = fmaf(sr[4 * j4 + 3], r.w, z);
+      }
+      if (hp == 0) {
+        sm.xs[v][tid] = z;
+      } else {
+        const bool bit = (z >= 0.0f) && (sm.n32[v] > 0.0f);
+        const uint64_t m = __ballot(bit);
+        if (lane == 0) {
+          sm.sgn[v][2 * wave] = static_cast<uint32_t>(m);
+          sm.sgn[v][2 * wave + 1] = static_cast<uint32_t>(m >> 32);
+        }
+      }
+    }
+  }
+}
+
+// Word w (32 bits) of vector v's LSB-first code stream.
+__device__ inline uint32_t code_word(const Smem& sm, int v, int w, int bits) {
+  const int first = (32 * w) / bits;
+  const int base = first * bits;
+  uint64_t acc = 0;
+  for (int c = first; c < kD && c * bits < 32 * w + 32; ++c)
+    acc |= static_cast<uint64_t>(sm.code[v][c]) << (c * bits - base);
+  return static_cast<uint32_t>(acc >> (32 * w - base));
+}
+
+template <bool HAD>
+__global__ __launch_bounds__(kThreads) void encode_flat_kernel(EncodeArgs a, DevTables t, Codebooks cb, int kind,
+                                                              int dtype, int bits, int qjl) {
+  __shared__ Smem sm;
+  const int tid = threadIdx.x;
+  const int64_t n0 = static_cast<int64_t>(blockIdx.x) * kTile;
+  const int nv = static_cast<int>(a.n - n0 < kTile ? a.n - n0 : kTile);
+  for (int v = 0; v < kTile; ++v)
+    sm.xs[v][tid] = v < nv ? load_any(a.x, (n0 + v) * a.row_stride + tid, dtype) : 0.0f;
+  __syncthreads();
+  const CoreParams cp = make_core(cb, kind == TQ_KIND_KEY, bits, qjl != 0);
+  encode_core<HAD>(sm, t, cp, nv);
+  __syncthreads();
+  if (tid < nv) {
+    a.norms[n0 + tid] = sm.n32[tid];
+    if (qjl) a.rnorms[n0 + tid] = sm.rn[tid];
+  }
+  const int wpv = 4 * bits;  // 32-bit words per vector (d = 128)
+  uint32_t* cw = reinterpret_cast<uint32_t*>(a.codes);
+  for (int k = tid; k < nv * wpv; k += kThreads) {
+    const int v = k / wpv, w = k % wpv;
+    cw[(n0 + v) * wpv + w] = code_word(sm, v, w, bits);
+  }
+  if (qjl) {
+    uint32_t* sw = reinterpret_cast<uint32_t*>(a.signs);
+    if (tid < 4 * nv) sw[(n0 + (tid >> 2)) * 4 + (tid & 3)] = sm.sgn[tid >> 2][tid & 3];
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Append.  For sequence b: T0 = seq_lens[b], T1 = T0 + count; the tokens at
+// positions [max(T0-W,0), max(T1-W,0)) leave the FP16 window and are encoded
+// into their pages (from the ring if they were already cached, else from the
+// new input), the new tokens that stay within the last W go to the ring, and
+// seq_lens[b] becomes T1 ("TurboQuant Family Design Study", sections "Packed
+// format and complete bit accounting" (recent FP16 window, fixed pages) and
+// "Paging, lifecycle, and cache identity" (fixed-page append, rollback)).
+// A sequence with an invalid count or page id is left untouched.
+
+struct SeqPlan {
+  int T0, cnt, c0, c1;
+  bool ok;
+};
+
+__device__ inline SeqPlan plan_seq(const AppendArgs& a, const Layout& L, int W, int b, int* status, bool report) {
+  SeqPlan s;
+  s.T0 = a.seq_lens[b];
+  s.cnt = a.counts ? a.counts[b] : a.n_new;
+  s.ok = true;
+  if (s.cnt < 0 || s.cnt > a.n_new || s.T0 < 0) {
+    s.ok = false;
+    if (report) atomicOr(status, TQ_STATUS_BAD_COUNT);
+    s.c0 = s.c1 = 0;
+    return s;
+  }
+  const int T1 = s.T0 + s.cnt;
+  s.c0 = s.T0 - W > 0 ? s.T0 - W : 0;
+  s.c1 = T1 - W > 0 ? T1 - W : 0;
+  if (s.c1 > s.c0) {
+    const int pg0 = s.c0 / L.P, pg1 = (s.c1 - 1) / L.P;
+    if (pg1 >= a.max_pages) s.ok = false;
+    for (int pg = pg0; s.ok && pg <= pg1; ++pg) {
+      const int pid = a.block_table[static_cast<int64_t>(b) * a.max_pages + pg];
+      if (pid < 0 || pid >= a.num_pages) s.ok = false;
+    }
+    if (!s.ok && report) atomicOr(status, TQ_STATUS_BAD_PAGE);
+  }
+  return s;
+}
+
+template <bool HAD>
+__global__ __launch_bounds__(kThreads) void append_encode_kernel(AppendArgs a, DevTables t, Codebooks cb, Layout L,
+                                                                int W) {
+  __shared__ Smem sm;
+  const int tid = threadIdx.x, h = blockIdx.y, b = blockIdx.z;
+  // every work-group of b evaluates the same plan; the commit kernel reports
+  const SeqPlan sp = plan_seq(a, L, W, b, t.status, false);
+  if (!sp.ok || sp.c1 <= sp.c0) return;
+  const int kv = static_cast<int>(blockIdx.x & 1u);  // 0: keys, 1: values
+  const int g = sp.c0 / kVGroup + static_cast<int>(blockIdx.x >> 1);
+  const int gpos = g * kVGroup;
+  if (gpos >= sp.c1) return;
+  const int lo = sp.c0 > gpos ? sp.c0 : gpos;
+  const int hi = sp.c1 < gpos + kVGroup ? sp.c1 : gpos + kVGroup;
+  const int pg = gpos / L.P, slot0 = gpos % L.P;
+  const int pid = a.block_table[static_cast<int64_t>(b) * a.max_pages + pg];
+  uint8_t* hb = a.pool + static_cast<int64_t>(pid) * L.page_bytes + kBodyOffset + static_cast<int64_t>(h) * L.head_bytes;
+  const int64_t bh = static_cast<int64_t>(b) * L.H + h;
+  {
+    const uint16_t* win = kv == 0 ? a.k_win : a.v_win;
+    const uint16_t* src = kv == 0 ? a.k_new : a.v_new;
+    for (int v = 0; v < kTile; ++v) {
+      const int pos = gpos + v;
+      float x = 0.0f;
+      if (pos >= lo && pos < hi) {
+        const uint16_t bits = pos < sp.T0 ? win[(bh * W + pos % W) * kD + tid]
+                                          : src[(bh * a.n_new + (pos - sp.T0)) * kD + tid];
+        x = half_bits_to_float(bits);
+      }
+      sm.xs[v][tid] = x;
+    }
+    __syncthreads();
+    const bool key = kv == 0;
+    const CoreParams cp = make_core(cb, key, key ? L.bK : L.bV, key && L.qjl);
+    encode_core<HAD>(sm, t, cp, kTile);
+    __syncthreads();
+    const int vlo = lo - gpos, vhi = hi - gpos;
+    if (key) {
+      float* kn = reinterpret_cast<float*>(hb + L.k_norm);
+      if (tid >= vlo && tid < vhi) {
+        kn[slot0 + tid] = sm.n32[tid];
+        if (L.qjl) reinterpret_cast<float*>(hb + L.k_rnorm)[slot0 + tid] = sm.rn[tid];
+      }
+      const int wpv = 4 * L.bK;
+      uint32_t* cw = reinterpret_cast<uint32_t*>(hb + L.k_codes);
+      for (int k = tid; k < kTile * wpv; k += kThreads) {
+        const int v = k / wpv, w = k % wpv;
+        if (v >= vlo && v < vhi) cw[(slot0 + v) * wpv + w] = code_word(sm, v, w, L.bK);
+      }
+      if (L.qjl) {
+        uint32_t* sw = reinterpret_cast<uint32_t*>(hb + L.k_signs);
+        const int v = tid >> 2;
+        if (v >= vlo && v < vhi) sw[(slot0 + v) * 4 + (tid & 3)] = sm.sgn[v][tid & 3];
+      }
+    } else {
+      float* vn = reinterpret_cast<float*>(hb + L.v_norm);
+      if (tid >= vlo && tid < vhi) vn[slot0 + tid] = sm.n32[tid];
+      // group-interleaved value codes: coordinate tid, words w = 0..bV-1
+      uint32_t* gw = reinterpret_cast<uint32_t*>(hb + L.v_codes) + static_cast<int64_t>(slot0 / kVGroup) * L.bV * kD;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        if (w >= L.bV) break;
+        uint32_t word = gw[w * kD + tid];
+        for (int v = vlo; v < vhi; ++v) {
+          const uint32_t c = sm.code[v][tid];
+          for (int k = 0; k < L.bV; ++k) {
+            const int p = v * L.bV + k;
+            if ((p >> 5) == w) {
+              const uint32_t m = 1u << (p & 31);
+              word = (word & ~m) | (((c >> k) & 1u) << (p & 31));
+            }
+          }
+        }
+        gw[w * kD + tid] = word;
+      }
+    }
+    __syncthreads();
+  }
+}
+
+// New tokens that remain among the last W go to the FP16 ring.
+__global__ __launch_bounds__(kThreads) void append_ring_kernel(AppendArgs a, DevTables t, Layout L, int W) {
+  const int tid = threadIdx.x, h = blockIdx.x, b = blockIdx.y;
+  const SeqPlan sp = plan_seq(a, L, W, b, t.status, false);
+  if (!sp.ok) return;
+  const int64_t bh = static_cast<int64_t>(b) * L.H + h;
+  const int j0 = sp.cnt > W ? sp.cnt - W : 0;
+  for (int j = j0; j < sp.cnt; ++j) {
+    const int pos = sp.T0 + j;
+    a.k_win[(bh * W + pos % W) * kD + tid] = a.k_new[(bh * a.n_new + j) * kD + tid];
+    a.v_win[(bh * W + pos % W) * kD + tid] = a.v_new[(bh * a.n_new + j) * kD + tid];
+  }
+}
+
+// Advance seq_lens and rewrite the headers of the pages the append touched.
+__global__ void append_commit_kernel(AppendArgs a, DevTables t, Layout L, int W, int rotation, uint64_t seed) {
+  for (int b = blockIdx.x * blockDim.x + threadIdx.x; b < a.batch; b += gridDim.x * blockDim.x) {
+    const SeqPlan sp = plan_seq(a, L, W, b, t.status, true);
+    if (!sp.ok) continue;
+    if (sp.c1 > sp.c0) {
+      for (int pg = sp.c0 / L.P; pg <= (sp.c1 - 1) / L.P; ++pg) {
+        const int pid = a.block_table[static_cast<int64_t>(b) * a.max_pages + pg];
+        uint32_t* hd = reinterpret_cast<uint32_t*>(a.pool + static_cast<int64_t>(pid) * L.page_bytes);
+        const int valid = sp.c1 - pg * L.P < L.P ? sp.c1 - pg * L.P : L.P;
+        hd[0] = kMagic;
+        hd[1] = 1u | (static_cast<uint32_t>(L.d) << 16);
+        hd[2] = static_cast<uint32_t>(L.bK) | (static_cast<uint32_t>(L.qjl) << 8) |
+                (static_cast<uint32_t>(L.bV) << 16) | (static_cast<uint32_t>(rotation) << 24);
+        hd[3] = static_cast<uint32_t>(L.H) | (static_cast<uint32_t>(L.P) << 16);
+        hd[4] = static_cast<uint32_t>(valid);
+        hd[5] = 1u;
+        hd[6] = static_cast<uint32_t>(seed);
+        hd[7] = static_cast<uint32_t>(seed >> 32);
+        hd[8] = static_cast<uint32_t>(pg);
+        for (int i = 9; i < 16; ++i) hd[i] = 0u;
+      }
+    }
+    a.seq_lens[b] = sp.T0 + sp.cnt;
+  }
+}
+
+}  // namespace
+
+int launch_encode(const tq_ctx* c, int kind, int dtype, const EncodeArgs& a, void* stream) {
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int bits = kind == TQ_KIND_KEY ? c->p.key_bits : c->p.value_bits;
+  const int qjl = (kind == TQ_KIND_KEY && c->p.key_qjl) ? 1 : 0;
+  const int64_t tiles = (a.n + kTile - 1) / kTile;
+  if (tiles > 0x7fffffff) return 1;
+  dim3 grid(static_cast<unsigned>(tiles));
+  if (c->p.rotation == TQ_ROT_HADAMARD)
+    hipLaunchKernelGGL(encode_flat_kernel<true>, grid, dim3(kThreads), 0, s, a, c->t, c->cb, kind, dtype, bits, qjl);
+  else
+    hipLaunchKernelGGL(encode_flat_kernel<false>, grid, dim3(kThreads), 0, s, a, c->t, c->cb, kind, dtype, bits, qjl);
+  return hipGetLastError() == hipSuccess ? 0 : 1;
+}
+
+int launch_append(const tq_ctx* c, const AppendArgs& a, void* stream) {
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int W = c->p.window;
+  const Layout& L = c->lay;
+  // groups a sequence can touch: ceil(n_new / 32) + 1 (unaligned start)
+  const int gmax = (a.n_new + kVGroup - 1) / kVGroup + 1;
+  dim3 grid(2 * gmax, L.H, a.batch);  // even x: keys, odd x: values
+  if (c->p.rotation == TQ_ROT_HADAMARD)
+    hipLaunchKernelGGL(append_encode_kernel<true>, grid, dim3(kThreads), 0, s, a, c->t, c->cb, L, W);
+  else
+    hipLaunchKernelGGL(append_encode_kernel<false>, grid, dim3(kThreads), 0, s, a, c->t, c->cb, L, W);
+  if (hipGetLastError() != hipSuccess) return 1;
+  if (W > 0) {
+    hipLaunchKernelGGL(append_ring_kernel, dim3(L.H, a.batch), dim3(kThreads), 0, s, a, c->t, L, W);
+    if (hipGetLastError() != hipSuccess) return 1;
+  }
+  const int cb = (a.batch + 255) / 256;
+  hipLaunchKernelGGL(append_commit_kernel, dim3(cb), dim3(256), 0, s, a, c->t, L, W, c->p.rotation, c->p.seed);
+  return hipGetLastError() == hipSuccess ? 0 : 1;
+}
+
+}  // namespace tq

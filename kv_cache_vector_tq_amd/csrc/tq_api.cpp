@@ -1,0 +1,277 @@
+// C ABI of the library: argument validation, context tables, workspace
+// sizing and kernel launches.  See include/tq.h for the contract.
+#include <hip/hip_runtime_api.h>
+
+#include <cmath>
+#include <cstring>
+#include <new>
+#include <vector>
+
+#include "tq_internal.h"
+
+namespace {
+
+bool params_ok(const tq_params* p) {
+  if (!p) return false;
+  if (p->head_dim <= 0 || p->head_dim % 8) return false;
+  if (p->key_bits < 2 || p->key_bits > 4 || p->value_bits < 2 || p->value_bits > 4) return false;
+  if (p->key_qjl != 0 && p->key_qjl != 1) return false;
+  if (p->rotation != TQ_ROT_DENSE && p->rotation != TQ_ROT_HADAMARD) return false;
+  if (p->rotation == TQ_ROT_HADAMARD && (p->head_dim & (p->head_dim - 1))) return false;
+  if (p->num_q_heads <= 0 || p->num_kv_heads <= 0 || p->num_q_heads % p->num_kv_heads) return false;
+  if (p->page_tokens <= 0 || p->page_tokens % tq::kVGroup || p->page_tokens > tq::kMaxPage) return false;
+  if (p->window < 0 || p->window > tq::kMaxWindow) return false;
+  return true;
+}
+
+// What the kernels in this build cover.
+bool params_supported(const tq_params* p) {
+  const int G = p->num_q_heads / p->num_kv_heads;
+  return p->head_dim == tq::kD && (G == 1 || G == 2 || G == 4 || G == 8) && p->num_kv_heads <= 65535;
+}
+
+bool aligned(const void* ptr, size_t a) { return (reinterpret_cast<uintptr_t>(ptr) % a) == 0; }
+
+void transpose(const float* a, float* at, int d) {
+  for (int i = 0; i < d; ++i)
+    for (int j = 0; j < d; ++j) at[j * d + i] = a[i * d + j];
+}
+
+int decode_splits(int batch, int hkv, int max_pages, int pages_per_split, int* pps_out) {
+  int pps = pages_per_split;
+  if (pps <= 0) {
+    // aim for >= 2048 work-groups over the whole batch, 1..max_pages pages each
+    const long long bh = static_cast<long long>(batch) * hkv;
+    long long want = (2048 + bh - 1) / bh;
+    if (want < 1) want = 1;
+    pps = static_cast<int>((max_pages + want - 1) / want);
+    if (pps < 1) pps = 1;
+  }
+  if (pps > max_pages) pps = max_pages;
+  if (pps < 1) pps = 1;
+  if (pps_out) *pps_out = pps;
+  const int splits = (max_pages + pps - 1) / pps;
+  return splits < 1 ? 1 : splits;
+}
+
+struct WsLayout {
+  size_t qs, ps, psum, qwin, pm, pl, pacc, total;
+};
+
+WsLayout ws_layout(const tq_params& p, int batch, int splits) {
+  const int G = p.num_q_heads / p.num_kv_heads;
+  const size_t d = p.head_dim;
+  const size_t bq = static_cast<size_t>(batch) * p.num_q_heads;
+  const size_t nb = static_cast<size_t>(batch) * p.num_kv_heads * splits * G;
+  auto up = [](size_t x) { return (x + 255) / 256 * 256; };
+  WsLayout w{};
+  size_t off = 0;
+  w.qs = off; off += up(bq * d * 4);
+  w.ps = off; off += up(bq * d * 4);
+  w.psum = off; off += up(bq * 4);
+  w.qwin = off; off += up(bq * d * 4);
+  w.pm = off; off += up(nb * 4);
+  w.pl = off; off += up(nb * 4);
+  w.pacc = off; off += up(nb * d * 4);
+  w.total = off;
+  return w;
+}
+
+}  // namespace
+
+extern "C" {
+
+TQ_API const char* tq_strerror(int err) {
+  switch (err) {
+    case TQ_OK: return "ok";
+    case TQ_ERR_INVALID_ARG: return "invalid argument";
+    case TQ_ERR_UNSUPPORTED: return "unsupported configuration";
+    case TQ_ERR_WORKSPACE: return "workspace too small";
+    case TQ_ERR_HIP: return "HIP runtime error";
+    default: return "unknown error";
+  }
+}
+
+TQ_API int64_t tq_page_bytes(const tq_params* p) {
+  if (!params_ok(p)) return TQ_ERR_INVALID_ARG;
+  return tq::make_layout(*p).page_bytes;
+}
+
+TQ_API int tq_host_tables(const tq_params* p, const double* rot_draws, const double* qjl_draws, float* rotation,
+                          float* qjl, float* key_centroids, float* key_boundaries, float* value_centroids,
+                          float* value_boundaries) {
+  if (!params_ok(p) || !rot_draws) return TQ_ERR_INVALID_ARG;
+  if (p->key_qjl && !qjl_draws && qjl) return TQ_ERR_INVALID_ARG;
+  const int d = p->head_dim;
+  if (rotation) {
+    if (p->rotation == TQ_ROT_DENSE) {
+      tq::haar_rotation_f32(rot_draws, d, rotation);
+    } else {
+      for (int i = 0; i < d; ++i) rotation[i] = rot_draws[i] < 0.0 ? -1.0f : 1.0f;
+    }
+  }
+  if (qjl) {
+    if (!qjl_draws) return TQ_ERR_INVALID_ARG;
+    for (int i = 0; i < d * d; ++i) qjl[i] = static_cast<float>(qjl_draws[i]);
+  }
+  tq::codebook_f32(p->key_bits, d, key_centroids, key_boundaries);
+  tq::codebook_f32(p->value_bits, d, value_centroids, value_boundaries);
+  return TQ_OK;
+}
+
+TQ_API int tq_codebook_init(tq_ctx** out, const tq_params* p, const double* rot_draws, const double* qjl_draws,
+                            void* stream) {
+  if (!out || !params_ok(p) || !rot_draws) return TQ_ERR_INVALID_ARG;
+  if (p->key_qjl && !qjl_draws) return TQ_ERR_INVALID_ARG;
+  if (!params_supported(p)) return TQ_ERR_UNSUPPORTED;
+  *out = nullptr;
+  const int d = p->head_dim;
+  tq_ctx* c = new (std::nothrow) tq_ctx();
+  if (!c) return TQ_ERR_HIP;
+  c->p = *p;
+  c->lay = tq::make_layout(*p);
+  std::vector<float> rot(d * d, 0.0f), rotT(d * d, 0.0f), S(d * d, 0.0f), ST(d * d, 0.0f);
+  std::memset(&c->cb, 0, sizeof(c->cb));
+  int rc = tq_host_tables(p, rot_draws, p->key_qjl ? qjl_draws : nullptr, rot.data(),
+                          p->key_qjl ? S.data() : nullptr, c->cb.kc, c->cb.kb, c->cb.vc, c->cb.vb);
+  if (rc != TQ_OK) {
+    delete c;
+    return rc;
+  }
+  if (p->rotation == TQ_ROT_DENSE) transpose(rot.data(), rotT.data(), d);
+  transpose(S.data(), ST.data(), d);
+  c->h_rot = rot;
+  c->h_S = S;
+  const size_t mat = static_cast<size_t>(d) * d * sizeof(float);
+  const size_t total = 4 * mat + 256;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (hipGetDevice(&c->device) != hipSuccess || hipMalloc(&c->dmem, total) != hipSuccess) {
+    delete c;
+    return TQ_ERR_HIP;
+  }
+  char* base = static_cast<char*>(c->dmem);
+  c->t.rot = reinterpret_cast<float*>(base);
+  c->t.rotT = reinterpret_cast<float*>(base + mat);
+  c->t.S = reinterpret_cast<float*>(base + 2 * mat);
+  c->t.ST = reinterpret_cast<float*>(base + 3 * mat);
+  c->t.status = reinterpret_cast<int*>(base + 4 * mat);
+  bool ok = hipMemcpyAsync(base, rot.data(), mat, hipMemcpyHostToDevice, s) == hipSuccess &&
+            hipMemcpyAsync(base + mat, rotT.data(), mat, hipMemcpyHostToDevice, s) == hipSuccess &&
+            hipMemcpyAsync(base + 2 * mat, S.data(), mat, hipMemcpyHostToDevice, s) == hipSuccess &&
+            hipMemcpyAsync(base + 3 * mat, ST.data(), mat, hipMemcpyHostToDevice, s) == hipSuccess &&
+            hipMemsetAsync(base + 4 * mat, 0, 256, s) == hipSuccess && hipStreamSynchronize(s) == hipSuccess;
+  if (!ok) {
+    (void)hipFree(c->dmem);
+    delete c;
+    return TQ_ERR_HIP;
+  }
+  *out = c;
+  return TQ_OK;
+}
+
+TQ_API int tq_destroy(tq_ctx* c) {
+  if (!c) return TQ_ERR_INVALID_ARG;
+  int rc = TQ_OK;
+  if (c->dmem && hipFree(c->dmem) != hipSuccess) rc = TQ_ERR_HIP;
+  delete c;
+  return rc;
+}
+
+TQ_API int tq_get_status(tq_ctx* c, int* code) {
+  if (!c || !code) return TQ_ERR_INVALID_ARG;
+  int prev = 0;
+  if (hipSetDevice(c->device) != hipSuccess || hipDeviceSynchronize() != hipSuccess ||
+      hipMemcpy(&prev, c->t.status, sizeof(int), hipMemcpyDeviceToHost) != hipSuccess ||
+      hipMemset(c->t.status, 0, sizeof(int)) != hipSuccess || hipDeviceSynchronize() != hipSuccess)
+    return TQ_ERR_HIP;
+  *code = prev;
+  return TQ_OK;
+}
+
+TQ_API int tq_encode(const tq_ctx* c, int kind, const void* x, int dtype, int64_t n, int64_t row_stride,
+                     uint8_t* codes, uint8_t* signs, float* norms, float* rnorms, void* stream) {
+  if (!c || (kind != TQ_KIND_KEY && kind != TQ_KIND_VALUE)) return TQ_ERR_INVALID_ARG;
+  if (dtype != TQ_DTYPE_F16 && dtype != TQ_DTYPE_BF16 && dtype != TQ_DTYPE_F32) return TQ_ERR_INVALID_ARG;
+  if (n < 0 || row_stride < c->p.head_dim) return TQ_ERR_INVALID_ARG;
+  if (n == 0) return TQ_OK;
+  const bool qjl = kind == TQ_KIND_KEY && c->p.key_qjl;
+  if (!x || !codes || !norms || (qjl && (!signs || !rnorms))) return TQ_ERR_INVALID_ARG;
+  const size_t esz = dtype == TQ_DTYPE_F32 ? 4 : 2;
+  if (!aligned(x, esz) || !aligned(codes, 4) || !aligned(norms, 4) || (qjl && (!aligned(signs, 4) || !aligned(rnorms, 4))))
+    return TQ_ERR_INVALID_ARG;
+  if (n > (int64_t(1) << 40)) return TQ_ERR_INVALID_ARG;
+  tq::EncodeArgs a{x, n, row_stride, codes, qjl ? signs : nullptr, norms, qjl ? rnorms : nullptr};
+  return tq::launch_encode(c, kind, dtype, a, stream) == 0 ? TQ_OK : TQ_ERR_HIP;
+}
+
+TQ_API int tq_append_page(const tq_ctx* c, uint8_t* pool, int64_t num_pages, const int32_t* block_table,
+                          int max_pages, int batch, int32_t* seq_lens, const uint16_t* k_new, const uint16_t* v_new,
+                          int n_new, const int32_t* new_counts, uint16_t* k_win, uint16_t* v_win, void* stream) {
+  if (!c || batch < 0 || n_new < 0 || max_pages < 0 || num_pages < 0) return TQ_ERR_INVALID_ARG;
+  if (batch == 0 || n_new == 0) return TQ_OK;
+  if (batch > 65535) return TQ_ERR_INVALID_ARG;
+  if (!seq_lens || !k_new || !v_new || !block_table || !pool) return TQ_ERR_INVALID_ARG;
+  if (c->p.window > 0 && (!k_win || !v_win)) return TQ_ERR_INVALID_ARG;
+  if (!aligned(pool, 256) || !aligned(k_new, 16) || !aligned(v_new, 16) ||
+      (c->p.window > 0 && (!aligned(k_win, 16) || !aligned(v_win, 16))))
+    return TQ_ERR_INVALID_ARG;
+  tq::AppendArgs a{pool, num_pages, block_table, max_pages, batch, seq_lens, k_new, v_new, n_new, new_counts, k_win, v_win};
+  return tq::launch_append(c, a, stream) == 0 ? TQ_OK : TQ_ERR_HIP;
+}
+
+TQ_API int64_t tq_decode_workspace_bytes(const tq_ctx* c, int batch, int max_pages, int pages_per_split) {
+  if (!c || batch < 0 || max_pages < 0 || pages_per_split < 0) return TQ_ERR_INVALID_ARG;
+  const int splits = decode_splits(batch, c->p.num_kv_heads, max_pages, pages_per_split, nullptr);
+  return static_cast<int64_t>(ws_layout(c->p, batch, splits).total);
+}
+
+TQ_API int tq_decode_attn(const tq_ctx* c, const void* q, int q_dtype, const uint8_t* pool, int64_t num_pages,
+                          const int32_t* block_table, int max_pages, int batch, const int32_t* seq_lens,
+                          const uint16_t* k_win, const uint16_t* v_win, float sm_scale, float* out, void* workspace,
+                          size_t workspace_bytes, int pages_per_split, float* dbg_logits, int64_t logits_stride,
+                          void* stream) {
+  if (!c || batch < 0 || max_pages < 0 || num_pages < 0 || pages_per_split < 0) return TQ_ERR_INVALID_ARG;
+  if (q_dtype != TQ_DTYPE_F16 && q_dtype != TQ_DTYPE_BF16 && q_dtype != TQ_DTYPE_F32) return TQ_ERR_INVALID_ARG;
+  if (!std::isfinite(sm_scale)) return TQ_ERR_INVALID_ARG;
+  if (batch == 0) return TQ_OK;
+  if (batch > 65535) return TQ_ERR_INVALID_ARG;
+  if (!q || !seq_lens || !out || !workspace) return TQ_ERR_INVALID_ARG;
+  if (max_pages > 0 && (!pool || !block_table)) return TQ_ERR_INVALID_ARG;
+  if (c->p.window > 0 && (!k_win || !v_win)) return TQ_ERR_INVALID_ARG;
+  if (dbg_logits && logits_stride < 1) return TQ_ERR_INVALID_ARG;
+  if ((pool && !aligned(pool, 256)) || !aligned(out, 16) || !aligned(workspace, 256) ||
+      !aligned(q, q_dtype == TQ_DTYPE_F32 ? 16 : 8))
+    return TQ_ERR_INVALID_ARG;
+  int pps = 1;
+  const int splits = decode_splits(batch, c->p.num_kv_heads, max_pages, pages_per_split, &pps);
+  const WsLayout w = ws_layout(c->p, batch, splits);
+  if (workspace_bytes < w.total) return TQ_ERR_WORKSPACE;
+  char* base = static_cast<char*>(workspace);
+  tq::DecodeArgs a{};
+  a.q = q;
+  a.q_dtype = q_dtype;
+  a.pool = pool;
+  a.num_pages = num_pages;
+  a.block_table = block_table;
+  a.max_pages = max_pages;
+  a.batch = batch;
+  a.seq_lens = seq_lens;
+  a.k_win = k_win;
+  a.v_win = v_win;
+  a.sm_scale = sm_scale;
+  a.out = out;
+  a.dbg_logits = dbg_logits;
+  a.logits_stride = logits_stride;
+  a.pages_per_split = pps;
+  a.splits = splits;
+  a.qs = reinterpret_cast<float*>(base + w.qs);
+  a.ps = reinterpret_cast<float*>(base + w.ps);
+  a.psum = reinterpret_cast<float*>(base + w.psum);
+  a.qwin = reinterpret_cast<float*>(base + w.qwin);
+  a.pm = reinterpret_cast<float*>(base + w.pm);
+  a.pl = reinterpret_cast<float*>(base + w.pl);
+  a.pacc = reinterpret_cast<float*>(base + w.pacc);
+  return tq::launch_decode(c, a, stream) == 0 ? TQ_OK : TQ_ERR_HIP;
+}
+
+}  // extern "C"

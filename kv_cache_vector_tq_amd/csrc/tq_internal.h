@@ -1,0 +1,138 @@
+// Internal declarations shared by the host API and the HIP kernels.
+#pragma once
+
+#include <cstdint>
+#include <vector>
+
+#include "../../include/tq.h"
+
+namespace tq {
+
+constexpr int kD = 128;           // head_dim the kernels are built for
+constexpr int kBodyOffset = 256;  // page body starts after the 64-byte header and padding
+constexpr int kVGroup = 32;       // value codes are interleaved in 32-token groups
+constexpr uint32_t kMagic = 0x564B5154u;  // "TQKV"
+constexpr int kMaxWindow = 1024;
+constexpr int kMaxPage = 1024;
+
+// Host table builders (tables.cpp).
+std::vector<double> lloyd_max_normal(int bits);
+void codebook_f32(int bits, int d, float* centroids, float* boundaries);
+void haar_rotation_f32(const double* g, int d, float* out);
+
+// Byte offsets of one head's streams inside its head block, and page sizes.
+struct Layout {
+  int P, bK, bV, qjl, H, d;
+  int64_t k_norm, k_rnorm, k_codes, k_signs, v_norm, v_codes;
+  int64_t head_bytes, page_bytes;
+};
+
+inline Layout make_layout(const tq_params& p) {
+  Layout l{};
+  l.P = p.page_tokens;
+  l.bK = p.key_bits;
+  l.bV = p.value_bits;
+  l.qjl = p.key_qjl ? 1 : 0;
+  l.H = p.num_kv_heads;
+  l.d = p.head_dim;
+  int64_t off = 0;
+  l.k_norm = off;
+  off += 4LL * l.P;
+  l.k_rnorm = off;
+  if (l.qjl) off += 4LL * l.P;
+  l.k_codes = off;
+  off += int64_t(l.P) * l.d * l.bK / 8;
+  l.k_signs = off;
+  if (l.qjl) off += int64_t(l.P) * l.d / 8;
+  l.v_norm = off;
+  off += 4LL * l.P;
+  l.v_codes = off;
+  off += int64_t(l.P) * l.d * l.bV / 8;
+  l.head_bytes = off;
+  l.page_bytes = (kBodyOffset + int64_t(l.H) * off + 255) / 256 * 256;
+  return l;
+}
+
+// Device-resident constant tables (one allocation owned by the context).
+struct DevTables {
+  const float* rot;    // DENSE: Pi [d][d] row-major; HADAMARD: signs [d]
+  const float* rotT;   // DENSE: Pi^T [d][d] row-major
+  const float* S;      // QJL matrix [d][d] row-major (sign bit i from row i)
+  const float* ST;     // S^T [d][d] row-major
+  int* status;         // status word (TQ_STATUS_* bits)
+};
+
+// Codebook values passed by value to kernels (uniform across lanes).
+struct Codebooks {
+  float kc[16], kb[16], vc[16], vb[16];
+};
+
+struct EncodeArgs {
+  const void* x;
+  int64_t n, row_stride;
+  uint8_t* codes;
+  uint8_t* signs;
+  float* norms;
+  float* rnorms;
+};
+
+struct AppendArgs {
+  uint8_t* pool;
+  int64_t num_pages;
+  const int32_t* block_table;
+  int max_pages;
+  int batch;
+  int32_t* seq_lens;
+  const uint16_t* k_new;
+  const uint16_t* v_new;
+  int n_new;
+  const int32_t* counts;
+  uint16_t* k_win;
+  uint16_t* v_win;
+};
+
+struct DecodeArgs {
+  const void* q;
+  int q_dtype;
+  const uint8_t* pool;
+  int64_t num_pages;
+  const int32_t* block_table;
+  int max_pages;
+  int batch;
+  const int32_t* seq_lens;
+  const uint16_t* k_win;
+  const uint16_t* v_win;
+  float sm_scale;
+  float* out;
+  float* dbg_logits;
+  int64_t logits_stride;
+  int pages_per_split;
+  int splits;
+  // workspace carve-up
+  float* qs;      // [B][Hq][d] rotated query * sm_scale * log2(e)
+  float* ps;      // [B][Hq][d] S q_rot * qjl_scale * sm_scale * log2(e)
+  float* psum;    // [B][Hq] sum of ps
+  float* qwin;    // [B][Hq][d] query * sm_scale * log2(e)
+  float* pm;      // [B][Hkv][splits][G] running max (log2 units)
+  float* pl;      // [B][Hkv][splits][G] running sum
+  float* pacc;    // [B][Hkv][splits][G][d] rotated-basis accumulator
+};
+
+struct Ctx;  // tq_ctx
+
+// Launchers (return hipError_t as int).
+int launch_encode(const tq_ctx* ctx, int kind, int dtype, const EncodeArgs& a, void* stream);
+int launch_append(const tq_ctx* ctx, const AppendArgs& a, void* stream);
+int launch_decode(const tq_ctx* ctx, const DecodeArgs& a, void* stream);
+
+}  // namespace tq
+
+struct tq_ctx {
+  tq_params p;
+  tq::Layout lay;
+  int device;
+  void* dmem;
+  tq::DevTables t;
+  tq::Codebooks cb;
+  std::vector<float> h_rot, h_S;
+};

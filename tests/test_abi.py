@@ -1,0 +1,112 @@
+"""CPU-side tests of the C-ABI library: it loads, exports every symbol its
+header declares, sizes pages like the stated format, rejects bad arguments,
+and its host-built tables (an independent Lloyd-Max and Householder QR in
+C++) agree with the oracle's."""
+
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import kv_cache_vector_tq_amd as tqa
+from oracle import codebook as cbm
+from oracle import pages
+from oracle import rotation as rot
+import tq_inputs
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(tqa.LIB_PATH):
+        from kv_cache_vector_tq_amd import build
+        build.build()
+    return tqa.lib()
+
+
+def header_functions():
+    src = open(os.path.join(ROOT, "include", "tq.h")).read()
+    return re.findall(r"TQ_API\s+[\w\s\*]+?\b(tq_\w+)\s*\(", src)
+
+
+def test_exports_every_declared_symbol(L):
+    names = header_functions()
+    assert len(names) >= 10
+    assert sorted(names) == sorted(tqa.EXPORTED)
+    for n in names:
+        assert hasattr(L, n), n
+
+
+@pytest.mark.parametrize("bK,qjl,bV,H,P", [(3, 1, 4, 8, 256), (2, 1, 2, 8, 256), (4, 0, 3, 2, 64), (3, 1, 4, 1, 32)])
+def test_page_bytes_matches_layout(L, bK, qjl, bV, H, P):
+    p = tqa.make_params(key_bits=bK, key_qjl=qjl, value_bits=bV, num_q_heads=H, num_kv_heads=H, page_tokens=P)
+    assert tqa.tq_page_bytes(p) == pages.Layout(128, bK, qjl, bV, H, P).page_bytes
+
+
+def test_target_page_size(L):
+    p = tqa.make_params(key_bits=3, key_qjl=1, value_bits=4, num_q_heads=32, num_kv_heads=8, page_tokens=256)
+    # 8 heads x 256 tokens x (72 + 68) bytes + 256-byte header block
+    assert tqa.tq_page_bytes(p) == 256 + 8 * 256 * 140
+
+
+@pytest.mark.parametrize("field,value", [
+    ("key_bits", 1), ("key_bits", 5), ("value_bits", 0), ("key_qjl", 2), ("rotation", 7),
+    ("num_q_heads", 6), ("num_kv_heads", 0), ("page_tokens", 48), ("page_tokens", 2048), ("window", -1),
+    ("head_dim", 0),
+])
+def test_bad_params_rejected(L, field, value):
+    p = tqa.make_params(num_q_heads=8, num_kv_heads=4)
+    setattr(p, field, value)
+    assert L.tq_page_bytes(ctypes.byref(p)) == tqa.TQ_ERR_INVALID_ARG
+    out = ctypes.c_void_p()
+    d = np.zeros(128 * 128)
+    assert L.tq_codebook_init(ctypes.byref(out), ctypes.byref(p), d.ctypes.data, d.ctypes.data, None) == \
+        tqa.TQ_ERR_INVALID_ARG
+
+
+def test_null_context_and_pointers(L):
+    assert L.tq_encode(None, 0, None, 0, 1, 128, None, None, None, None, None) == tqa.TQ_ERR_INVALID_ARG
+    assert L.tq_decode_attn(None, None, 0, None, 0, None, 0, 1, None, None, None, 0.1, None, None, 0, 0, None, 0,
+                            None) == tqa.TQ_ERR_INVALID_ARG
+    assert L.tq_append_page(None, None, 0, None, 0, 1, None, None, None, 1, None, None, None, None) == \
+        tqa.TQ_ERR_INVALID_ARG
+    assert L.tq_destroy(None) == tqa.TQ_ERR_INVALID_ARG
+    assert L.tq_decode_workspace_bytes(None, 1, 1, 0) == tqa.TQ_ERR_INVALID_ARG
+    p = tqa.make_params()
+    assert L.tq_host_tables(ctypes.byref(p), None, None, None, None, None, None, None, None) == \
+        tqa.TQ_ERR_INVALID_ARG
+    assert L.tq_strerror(tqa.TQ_ERR_WORKSPACE) == b"workspace too small"
+
+
+@pytest.mark.parametrize("bits", [2, 3, 4])
+def test_library_codebook_equals_oracle(L, bits):
+    p = tqa.make_params(key_bits=bits, value_bits=bits)
+    t = tqa.tq_host_tables(p, tq_inputs.rotation_draws(0, 128), tq_inputs.qjl_draws(0, 128))
+    cb = cbm.Codebook(bits, 128)
+    assert np.array_equal(t["key_centroids"].astype(np.float64), cb.centroids)
+    assert np.array_equal(t["key_boundaries"].astype(np.float64), cb.boundaries)
+    assert np.array_equal(t["value_centroids"], t["key_centroids"])
+
+
+@pytest.mark.parametrize("seed", [0, 1, 7])
+def test_library_rotation_equals_oracle(L, seed):
+    p = tqa.make_params(seed=seed)
+    draws = tq_inputs.rotation_draws(seed, 128)
+    t = tqa.tq_host_tables(p, draws, tq_inputs.qjl_draws(seed, 128))
+    P = rot.dense_rotation(draws)
+    diff = np.abs(t["rotation"].astype(np.float64) - P)
+    # independent double-precision QR in both; float32 rounding may differ by one ulp
+    assert np.max(diff) <= 2.0 ** -30
+    assert np.mean(diff == 0) > 0.999
+    S = rot.qjl_matrix(tq_inputs.qjl_draws(seed, 128), 128)
+    assert np.array_equal(t["qjl"].astype(np.float64), S)
+
+
+def test_library_hadamard_signs(L):
+    p = tqa.make_params(rotation=tqa.TQ_ROT_HADAMARD)
+    draws = tq_inputs.hadamard_draws(3, 128)
+    t = tqa.tq_host_tables(p, draws, tq_inputs.qjl_draws(3, 128))
+    assert np.array_equal(t["rotation"], rot.rademacher_signs(draws).astype(np.float32))

@@ -1,0 +1,150 @@
+"""GPU parity of tq_append_page: the pages and rings the GPU writes, read
+back through the oracle's page reader, hold the oracle's records (codes and
+signs under the guard-band rule), the rings and lengths match exactly, bulk
+prefill and token-by-token appends agree, and decode over GPU-built pages
+matches the oracle's attention over the same pages."""
+
+import numpy as np
+import pytest
+import torch
+
+import kv_cache_vector_tq_amd as tqa
+from oracle import attention as att
+from oracle import codec, pages
+import tq_inputs
+from gpu_helpers import check_codes, check_signs, context_for, rel_close, run_decode, upload_cache
+from oracle_cache import Setup, fill
+
+pytestmark = pytest.mark.gpu
+
+
+def _gpu_append(ctx, dev, k, v, counts=None):
+    tqa.tq_append_page(ctx, dev["pool"], dev["block_table"], dev["seq_lens"],
+                       torch.from_numpy(k.view(np.uint16)).cuda().view(torch.float16),
+                       torch.from_numpy(v.view(np.uint16)).cuda().view(torch.float16),
+                       dev["k_win"], dev["v_win"],
+                       None if counts is None else torch.from_numpy(np.asarray(counts, np.int32)).cuda(),
+                       num_pages=dev["num_pages"])
+
+
+def _compare_caches(s, ref, pool_gpu, kwin, vwin, lens_gpu):
+    assert np.array_equal(lens_gpu, ref.seq_lens)
+    assert np.array_equal(kwin, ref.k_win.view(np.uint16)) and np.array_equal(vwin, ref.v_win.view(np.uint16))
+    gcache = s.cache(len(lens_gpu), 1)
+    gcache.pool = pool_gpu.reshape(ref.pool.shape)
+    gcache.block_table = ref.block_table
+    gcache.seq_lens = ref.seq_lens
+    for b in range(len(lens_gpu)):
+        C = max(int(ref.seq_lens[b]) - s.W, 0)
+        for pg in range(-(-C // s.P)):
+            pid = int(ref.block_table[b, pg])
+            # header identical
+            assert np.array_equal(gcache.pool[pid, :64], ref.pool[pid, :64]), (b, pg)
+        for h in range(s.Hkv):
+            comp_g = gcache.compressed(b, h)
+            if comp_g is None:
+                continue
+            kg, vng, vig = comp_g
+            kr, vnr, vir = ref.compressed(b, h)
+            # the FP16 inputs of these compressed tokens: reconstruct from the oracle's encode inputs
+            x = ref._src_k[(b, h)][:C]
+            xv = ref._src_v[(b, h)][:C]
+            assert np.array_equal(kg.norms, kr.norms) and np.array_equal(vng, vnr)
+            gidx = codec.unpack_bits(kg.codes, s.bK, 128)
+            check_codes(x, gidx, codec.unpack_bits(kr.codes, s.bK, 128), s.R, s.kcb)
+            check_codes(xv, vig, vir, s.R, s.vcb)
+            if s.qjl:
+                check_signs(x, gidx, kg.norms, kg.signs, s.R, s.kcb, s.S)
+                assert np.allclose(kg.rnorms, kr.rnorms, rtol=2e-5, atol=1e-30)
+    return gcache
+
+
+def _track_sources(s, cache, k, v, lens):
+    cache._src_k, cache._src_v = {}, {}
+    for b in range(len(lens)):
+        for h in range(s.Hkv):
+            cache._src_k[(b, h)] = k[b, h, :lens[b]].astype(np.float64)
+            cache._src_v[(b, h)] = v[b, h, :lens[b]].astype(np.float64)
+
+
+CASES = [
+    ("cfg0_W128", dict(Hq=1, Hkv=1, W=128), [1024]),
+    ("gqa_ragged_P64", dict(Hq=8, Hkv=2, W=40, P=64), [300, 41, 40, 7, 0, 129]),
+    ("hadamard_k2v2_W0", dict(Hq=8, Hkv=1, key_bits=2, value_bits=2, rotation="hadamard", W=0, P=32), [100, 33]),
+    ("k4_noqjl_v3", dict(Hq=2, Hkv=2, key_bits=4, key_qjl=0, value_bits=3, W=16, P=32), [77, 16, 15]),
+]
+
+
+@pytest.mark.parametrize("name,kw,lens", CASES, ids=[c[0] for c in CASES])
+def test_bulk_prefill_parity(name, kw, lens):
+    print(f"case {name}", flush=True)
+    s = Setup(**kw)
+    ref = s.cache(len(lens), max(lens))
+    k, v = fill(s, ref, lens)
+    _track_sources(s, ref, k, v, lens)
+    ctx = context_for(s)
+    empty = s.cache(len(lens), max(lens))
+    dev = upload_cache(empty)
+    _gpu_append(ctx, dev, k, v, counts=lens)
+    torch.cuda.synchronize()
+    assert tqa.tq_get_status(ctx) == 0
+    g = _compare_caches(s, ref, dev["pool"].cpu().numpy(), dev["k_win"].cpu().view(torch.int16).numpy().view(np.uint16),
+                        dev["v_win"].cpu().view(torch.int16).numpy().view(np.uint16), dev["seq_lens"].cpu().numpy())
+    # decode over the GPU-built cache against the oracle's attention over the same bytes
+    q = tq_inputs.queries(8, (len(lens), s.Hq, 128))
+    out, dbg = run_decode(ctx, torch.from_numpy(q.astype(np.float32)).cuda(), dev, 1 / np.sqrt(128),
+                          logits_len=max(lens) + 1)
+    ref_o, _ = att.attention_plain(g, q.astype(np.float32).astype(np.float64), 1 / np.sqrt(128))
+    for b in range(len(lens)):
+        for hq in range(s.Hq):
+            if lens[b]:
+                assert rel_close(out[b, hq], ref_o[b, hq]), (b, hq)
+
+
+def test_streaming_appends_match_bulk():
+    s = Setup(Hq=4, Hkv=2, W=24, P=32)
+    lens = [90, 30]
+    ref = s.cache(2, 90)
+    k, v = fill(s, ref, lens)
+    ctx = context_for(s)
+    # bulk on one cache, 1-token and 5-token chunks on another
+    d1 = upload_cache(s.cache(2, 90))
+    _gpu_append(ctx, d1, k, v, counts=lens)
+    d2 = upload_cache(s.cache(2, 90))
+    t = 0
+    while t < max(lens):
+        step = 1 if t < 40 else 5
+        cnt = np.clip(np.asarray(lens) - t, 0, step)
+        kk = np.ascontiguousarray(k[:, :, t:t + step])
+        vv = np.ascontiguousarray(v[:, :, t:t + step])
+        if kk.shape[2] < step:
+            pad = step - kk.shape[2]
+            kk = np.concatenate([kk, np.zeros(kk.shape[:2] + (pad, 128), np.float16)], 2)
+            vv = np.concatenate([vv, np.zeros(vv.shape[:2] + (pad, 128), np.float16)], 2)
+        _gpu_append(ctx, d2, kk, vv, counts=cnt)
+        t += step
+    torch.cuda.synchronize()
+    assert tqa.tq_get_status(ctx) == 0
+    for key in ("pool", "k_win", "v_win", "seq_lens"):
+        assert torch.equal(d1[key].cpu(), d2[key].cpu()), key
+
+
+def test_invalid_page_leaves_sequence_unchanged():
+    s = Setup(Hq=2, Hkv=1, W=8, P=32)
+    lens = [50, 50]
+    c = s.cache(2, 50)
+    k, v = fill(s, s.cache(2, 50), lens)
+    dev = upload_cache(c)
+    dev["block_table"][1, 1] = -1
+    ctx = context_for(s)
+    before = dev["pool"].clone()
+    _gpu_append(ctx, dev, k, v, counts=lens)
+    torch.cuda.synchronize()
+    assert tqa.tq_get_status(ctx) & tqa.TQ_STATUS_BAD_PAGE
+    lens_after = dev["seq_lens"].cpu().numpy()
+    assert lens_after[0] == 50 and lens_after[1] == 0
+    # sequence 1's pages untouched
+    pb = tqa.tq_page_bytes(ctx.params)
+    pid0 = int(c.block_table[1, 0])
+    assert torch.equal(dev["pool"][pid0 * pb:(pid0 + 1) * pb].cpu(), before[pid0 * pb:(pid0 + 1) * pb].cpu())
+    assert not dev["k_win"][1].any()

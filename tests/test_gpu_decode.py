@@ -1,0 +1,113 @@
+"""GPU parity of tq_decode_attn on oracle-built pages (isolates the decode
+arithmetic): logits per (b, q-head) within 1e-3 of max|logit| and outputs
+within 1e-3 relative (L2) of the oracle's plain dequantise-then-softmax
+attention.  Also: split-K partition invariance, repeat bit-identity, ragged
+and degenerate lengths, GQA groupings, bf16/f16/f32 queries, bad pages."""
+
+import numpy as np
+import pytest
+import torch
+
+import kv_cache_vector_tq_amd as tqa
+from oracle import attention as att
+import tq_inputs
+from gpu_helpers import context_for, rel_close, run_decode, upload_cache
+from oracle_cache import Setup, fill
+
+pytestmark = pytest.mark.gpu
+
+
+def _check(cache, q, out, dbg, tol=1e-3):
+    ref_o, ref_l = att.attention_plain(cache, q, 1 / np.sqrt(128))
+    B, Hq, _ = q.shape
+    for b in range(B):
+        T = int(cache.seq_lens[b])
+        for g in range(Hq):
+            if T == 0:
+                assert np.all(out[b, g] == 0)
+                continue
+            l = ref_l[b][g]
+            assert np.max(np.abs(dbg[b, g, :T] - l)) <= tol * np.max(np.abs(l)), (b, g)
+            assert rel_close(out[b, g], ref_o[b, g], tol), (b, g)
+
+
+CASES = [
+    # name, setup kwargs, lens
+    ("cfg0_T1024_W0", dict(Hq=1, Hkv=1, W=0), [1024]),
+    ("cfg0_T1024_W128", dict(Hq=1, Hkv=1, W=128), [1024]),
+    ("gqa4_ragged", dict(Hq=8, Hkv=2, W=128), [700, 129, 128, 40, 1, 0, 1000]),
+    ("gqa8_2bit_hadamard", dict(Hq=8, Hkv=1, key_bits=2, value_bits=2, rotation="hadamard", W=128), [900, 300]),
+    ("k4_noqjl_v3_P64", dict(Hq=2, Hkv=2, key_bits=4, key_qjl=0, value_bits=3, P=64, W=16), [333, 64, 17]),
+    ("mha_k2_v4_W0_P32", dict(Hq=4, Hkv=4, key_bits=2, value_bits=4, P=32, W=0), [95, 32, 31]),
+]
+
+
+@pytest.mark.parametrize("name,kw,lens", CASES, ids=[c[0] for c in CASES])
+def test_decode_parity_oracle_pages(name, kw, lens):
+    print(f"case {name}", flush=True)
+    s = Setup(**kw)
+    cache = s.cache(len(lens), max(lens))
+    fill(s, cache, lens)
+    ctx = context_for(s)
+    dev = upload_cache(cache)
+    q = tq_inputs.queries(5, (len(lens), s.Hq, 128))
+    qt = torch.from_numpy(q.astype(np.float32)).cuda()
+    out, dbg = run_decode(ctx, qt, dev, 1 / np.sqrt(128), logits_len=max(lens) + 1)
+    _check(cache, q.astype(np.float32).astype(np.float64), out, dbg)
+    assert tqa.tq_get_status(ctx) == 0
+
+
+@pytest.mark.parametrize("qdtype", [torch.bfloat16, torch.float16])
+def test_decode_query_dtypes(qdtype):
+    s = Setup(Hq=4, Hkv=1, W=128)
+    lens = [800]
+    cache = s.cache(1, 800)
+    fill(s, cache, lens)
+    ctx = context_for(s)
+    dev = upload_cache(cache)
+    qt = torch.from_numpy(tq_inputs.queries(6, (1, 4, 128)).astype(np.float32)).to(qdtype).cuda()
+    out, dbg = run_decode(ctx, qt, dev, 1 / np.sqrt(128), logits_len=801)
+    _check(cache, qt.float().cpu().numpy().astype(np.float64), out, dbg)
+
+
+def test_split_invariance_and_repeatability():
+    s = Setup(Hq=8, Hkv=2, W=128, P=64)
+    lens = [2000, 1500]
+    cache = s.cache(2, 2000)
+    fill(s, cache, lens)
+    ctx = context_for(s)
+    dev = upload_cache(cache)
+    qt = torch.from_numpy(tq_inputs.queries(7, (2, 8, 128)).astype(np.float32)).cuda()
+    outs = [run_decode(ctx, qt, dev, 1 / np.sqrt(128), pages_per_split=pps)[0] for pps in (0, 1, 3, 100)]
+    for o in outs[1:]:
+        assert np.max(np.abs(o - outs[0])) <= 1e-5 * np.max(np.abs(outs[0]))
+    again = run_decode(ctx, qt, dev, 1 / np.sqrt(128), pages_per_split=3)[0]
+    assert np.array_equal(again, outs[2])
+
+
+def test_bad_page_sets_status():
+    s = Setup(Hq=2, Hkv=1, W=16, P=32)
+    cache = s.cache(1, 200)
+    fill(s, cache, [200])
+    ctx = context_for(s)
+    dev = upload_cache(cache)
+    dev["block_table"][0, 1] = -1
+    qt = torch.zeros((1, 2, 128), dtype=torch.float32, device="cuda")
+    out, _ = run_decode(ctx, qt, dev, 1 / np.sqrt(128))
+    assert np.all(np.isfinite(out))
+    assert tqa.tq_get_status(ctx) & tqa.TQ_STATUS_BAD_PAGE
+    assert tqa.tq_get_status(ctx) == 0
+
+
+def test_workspace_too_small():
+    s = Setup(Hq=2, Hkv=1)
+    ctx = context_for(s)
+    ws = torch.empty(16, dtype=torch.uint8, device="cuda")
+    z = torch.zeros(4096, dtype=torch.uint8, device="cuda")
+    with pytest.raises(tqa.TQError) as e:
+        tqa.tq_decode_attn(ctx, torch.zeros((1, 2, 128), device="cuda"), z, torch.zeros((1, 4), dtype=torch.int32,
+                           device="cuda"), torch.zeros(1, dtype=torch.int32, device="cuda"),
+                           torch.zeros((1, 1, 128, 128), dtype=torch.float16, device="cuda"),
+                           torch.zeros((1, 1, 128, 128), dtype=torch.float16, device="cuda"),
+                           torch.zeros((1, 2, 128), device="cuda"), ws, 0.1, num_pages=0)
+    assert e.value.code == tqa.TQ_ERR_WORKSPACE

@@ -1,0 +1,90 @@
+"""GPU parity of tq_encode against the oracle (codes and sign bits under the
+guard-band rule in gpu_helpers, norms to float32, residual norms to 1e-5)."""
+
+import numpy as np
+import pytest
+import torch
+
+import kv_cache_vector_tq_amd as tqa
+from oracle import codec
+import tq_inputs
+from gpu_helpers import check_codes, check_signs, context_for
+from oracle_cache import Setup
+
+pytestmark = pytest.mark.gpu
+
+
+def _inputs(n, seed=0):
+    x = tq_inputs.keys(seed, 128, np.arange(n)).astype(np.float64)
+    x[3] = 0.0                      # zero vector
+    x[5] = 1e-3 * x[5]              # tiny
+    x[7, :] = 0.0
+    x[7, 11] = -2.5                 # one-hot
+    return tq_inputs.fp16(x)
+
+
+def _gpu_encode(ctx, kind, x16, qjl, dtype=torch.float16):
+    n = x16.shape[0]
+    bits = ctx.params.key_bits if kind == tqa.TQ_KIND_KEY else ctx.params.value_bits
+    xt = torch.from_numpy(x16.astype(np.float32)).to(dtype).cuda()
+    codes = torch.zeros((n, 16 * bits), dtype=torch.uint8, device="cuda")
+    norms = torch.zeros(n, dtype=torch.float32, device="cuda")
+    signs = torch.zeros((n, 16), dtype=torch.uint8, device="cuda") if qjl else None
+    rnorms = torch.zeros(n, dtype=torch.float32, device="cuda") if qjl else None
+    tqa.tq_encode(ctx, kind, xt, codes, norms, signs, rnorms)
+    torch.cuda.synchronize()
+    cpu = lambda t: None if t is None else t.cpu().numpy()
+    return cpu(codes), cpu(norms), cpu(signs), cpu(rnorms)
+
+
+@pytest.mark.parametrize("rotation", ["dense", "hadamard"])
+@pytest.mark.parametrize("bK,bV", [(3, 4), (2, 2), (4, 3)])
+@pytest.mark.parametrize("n", [1024, 77])
+def test_encode_parity(rotation, bK, bV, n):
+    s = Setup(key_bits=bK, value_bits=bV, rotation=rotation)
+    ctx = context_for(s)
+    x16 = _inputs(n)
+    x = x16.astype(np.float64)
+    print(f"case rotation={rotation} bK={bK} bV={bV} n={n}", flush=True)
+    # keys with QJL
+    codes, norms, signs, rnorms = _gpu_encode(ctx, tqa.TQ_KIND_KEY, x16, True)
+    ref = codec.encode(x, s.R, s.kcb, s.S)
+    assert np.array_equal(norms, ref.norms)
+    gidx = codec.unpack_bits(codes, bK, 128)
+    nband = check_codes(x, gidx, ref.idx, s.R, s.kcb)
+    check_signs(x, gidx, norms, signs, s.R, s.kcb, s.S)
+    r = codec.residual_from_codes(x, s.R, s.kcb, norms, gidx)
+    assert np.allclose(rnorms, np.linalg.norm(r, axis=1), rtol=1e-5, atol=1e-30)
+    assert nband <= 0.002 * x.size
+    # zero vector
+    assert norms[3] == 0 and rnorms[3] == 0 and not codes[3].any() and not signs[3].any()
+    # values
+    vcodes, vnorms, _, _ = _gpu_encode(ctx, tqa.TQ_KIND_VALUE, x16, False)
+    vref = codec.encode(x, s.R, s.vcb)
+    assert np.array_equal(vnorms, vref.norms)
+    check_codes(x, codec.unpack_bits(vcodes, bV, 128), vref.idx, s.R, s.vcb)
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+def test_encode_other_dtypes(dtype):
+    s = Setup()
+    ctx = context_for(s)
+    x16 = _inputs(300, seed=4)
+    xin = torch.from_numpy(x16.astype(np.float32)).to(dtype)
+    x = xin.float().numpy().astype(np.float64)  # exactly what the library reads
+    codes, norms, signs, rnorms = _gpu_encode(ctx, tqa.TQ_KIND_KEY, x.astype(np.float32), True, dtype)
+    ref = codec.encode(x, s.R, s.kcb, s.S)
+    assert np.array_equal(norms, ref.norms)
+    gidx = codec.unpack_bits(codes, 3, 128)
+    check_codes(x, gidx, ref.idx, s.R, s.kcb)
+    check_signs(x, gidx, norms, signs, s.R, s.kcb, s.S)
+
+
+def test_encode_repeatable():
+    s = Setup()
+    ctx = context_for(s)
+    x16 = _inputs(500, seed=9)
+    a = _gpu_encode(ctx, tqa.TQ_KIND_KEY, x16, True)
+    b = _gpu_encode(ctx, tqa.TQ_KIND_KEY, x16, True)
+    for u, v in zip(a, b):
+        assert np.array_equal(u, v)
