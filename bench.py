@@ -1,0 +1,165 @@
+"""Benchmark of the TurboQuant KV-cache hot path on one MI355X.
+
+Workload (one decode step per layer call): B=16 sequences, H_q=32 query heads
+over H_kv=8 KV heads (GQA 4:1), head_dim 128, a 32K-token context per
+sequence (the last 128 tokens in the FP16 window, the rest in 256-token
+pages of 3-bit+QJL keys and 4-bit values, dense rotation), bf16 queries.
+A step appends one new token to every sequence (tq_append_page: the token
+leaving the window is encoded into its page) and runs tq_decode_attn over
+the whole context.  The context is prefilled so that the last timed step
+decodes at exactly T = 32768.  Inputs are seeded synthetic data with the
+key recipe of tq_inputs (heavy-tailed channels, RoPE) drawn on the GPU.
+
+Prints one JSON line: tokens/s (sum of context lengths attended per second),
+the step time, the scan kernel's roofline (algorithmic bytes per launch /
+its HIP-event time vs the 8 TB/s HBM peak) and a CPU baseline (the float64
+oracle on a bounded sample of the same workload).
+"""
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0
+METRIC = "decode-attn compressed-KV tokens/s & HBM GB/s vs peak; encode vectors/s"
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--T", type=int, default=32768)
+    ap.add_argument("--batch", type=int, default=16)
+    return ap.parse_args()
+
+
+def cpu_baseline(T, W, P, G, Hkv, min_seconds):
+    """The oracle's decode (dequantise + float64 softmax attention) on one
+    sequence and one KV head (G query heads) at context T, repeated until
+    min_seconds of CPU work; converted to sequence-tokens/s at H_kv heads."""
+    from threadpoolctl import threadpool_info
+    sys.path.insert(0, os.path.join(ROOT, "tests"))
+    from oracle import attention as att
+    from oracle_cache import Setup, fill
+    import tq_inputs
+    s = Setup(Hq=G, Hkv=1, key_bits=3, key_qjl=1, value_bits=4, P=P, W=W)
+    cache = s.cache(1, T)
+    fill(s, cache, [T])
+    q = tq_inputs.queries(3, (1, G, 128))
+    calls, t0 = 0, time.perf_counter()
+    while True:
+        att.attention_plain(cache, q, 1 / np.sqrt(128))
+        calls += 1
+        el = time.perf_counter() - t0
+        if el >= min_seconds:
+            break
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    return {"value": calls * T / Hkv / el, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"{calls} oracle decode call(s) of 1 sequence x 1 KV head ({G} query heads) at T={T}, "
+                      f"{el:.1f} s; rate scaled to {Hkv} KV heads"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU; --gpus above 1 is not supported",
+                          "n_gpus": args.gpus}))
+        sys.exit(2)
+    import torch
+    import kv_cache_vector_tq_amd as tqa
+    import tq_inputs
+    if not os.path.exists(tqa.LIB_PATH):
+        from kv_cache_vector_tq_amd import build
+        build.build()
+    dev = "cuda"
+    B, Hq, Hkv, d, P, W = args.batch, 32, 8, 128, 256, 128
+    G = Hq // Hkv
+    Tf = args.T
+    nsteps = args.warmup + args.steps
+    T0 = Tf - nsteps
+    params = tqa.make_params(key_bits=3, key_qjl=1, value_bits=4, rotation=tqa.TQ_ROT_DENSE, num_q_heads=Hq,
+                             num_kv_heads=Hkv, page_tokens=P, window=W, seed=0)
+    ctx = tqa.Context(params, tq_inputs.rotation_draws(0, d), tq_inputs.qjl_draws(0, d))
+    pb = tqa.tq_page_bytes(params)
+    max_pages = -(-(Tf - W) // P)
+    npages = B * max_pages
+    pool = torch.zeros(npages * pb, dtype=torch.uint8, device=dev)
+    # pages of a sequence are scattered over the pool
+    perm = torch.from_numpy(np.random.default_rng(1).permutation(npages).astype(np.int32))
+    block_table = perm.reshape(B, max_pages).to(dev)
+    seq_lens = torch.zeros(B, dtype=torch.int32, device=dev)
+    k_win = torch.zeros((B, Hkv, W, d), dtype=torch.float16, device=dev)
+    v_win = torch.zeros_like(k_win)
+    k_all, v_all = tq_inputs.torch_kv(0, B, Hkv, Tf, d, dev)
+    kpre = k_all[:, :, :T0].contiguous()
+    vpre = v_all[:, :, :T0].contiguous()
+    tqa.tq_append_page(ctx, pool, block_table, seq_lens, kpre, vpre, k_win, v_win, num_pages=npages)
+    del kpre, vpre
+    ksteps = [k_all[:, :, T0 + i:T0 + i + 1].contiguous() for i in range(nsteps)]
+    vsteps = [v_all[:, :, T0 + i:T0 + i + 1].contiguous() for i in range(nsteps)]
+    del k_all, v_all
+    qsteps = [tq_inputs.torch_queries(0, (B, Hq, d), dev, torch.bfloat16, step=i) for i in range(nsteps)]
+    ws = torch.empty(tqa.tq_decode_workspace_bytes(ctx, B, max_pages), dtype=torch.uint8, device=dev)
+    out = torch.empty((B, Hq, d), dtype=torch.float32, device=dev)
+    sm = 1.0 / np.sqrt(d)
+    torch.cuda.synchronize()
+    assert tqa.tq_get_status(ctx) == 0
+
+    def step(i):
+        tqa.tq_append_page(ctx, pool, block_table, seq_lens, ksteps[i], vsteps[i], k_win, v_win, num_pages=npages)
+        tqa.tq_decode_attn(ctx, qsteps[i], pool, block_table, seq_lens, k_win, v_win, out, ws, sm, num_pages=npages)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    tqa.tq_profile_begin(ctx, args.steps)
+    t0 = time.perf_counter()
+    for i in range(args.warmup, nsteps):
+        step(i)
+    torch.cuda.synchronize()
+    el = time.perf_counter() - t0
+    scan_ms, ncalls = tqa.tq_profile_end(ctx)
+    status = tqa.tq_get_status(ctx)
+    if status != 0 or not torch.isfinite(out).all():
+        raise SystemExit(f"bench: bad status {status} or non-finite output")
+    # tokens attended in the timed steps: after step i the length is T0 + i + 1
+    lens = [T0 + i + 1 for i in range(args.warmup, nsteps)]
+    tokens = B * sum(lens)
+    per_tok_head = (48 + 16 + 4 + 4) + (64 + 4)   # key 3-bit + signs + norm + rnorm, value 4-bit + norm
+    comp_bytes = [B * Hkv * (T - W) * per_tok_head for T in lens]
+    win_bytes = B * Hkv * W * d * 2 * 2
+    scan_s = scan_ms / 1e3 / max(ncalls, 1)
+    achieved = (sum(comp_bytes) / len(comp_bytes)) / scan_s / 1e9
+    ms_step = el / args.steps * 1e3
+    res = {
+        "metric": METRIC, "value": tokens / el, "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_step, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": f"decode step (append 1 token + decode attention), B={B}, Hq={Hq}, Hkv={Hkv}, "
+                               f"d={d}, T={Tf} (last step), W={W} fp16 window, P={P}, keys 3-bit+QJL, values "
+                               f"4-bit, dense rotation, bf16 queries",
+                   "batch": B, "seq_len": Tf, "parallelism": "none (1 GPU)"},
+        "hbm_gbps_step": (sum(comp_bytes) / len(comp_bytes) + win_bytes) / (ms_step / 1e3) / 1e9,
+        "scan_us": scan_s * 1e6,
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBPS, "traffic": None,
+                     "kernel": "scan_kernel (compressed-page scan)",
+                     "algorithmic_bytes_per_launch": sum(comp_bytes) / len(comp_bytes)},
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(Tf, W, P, G, Hkv, args.cpu_seconds)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

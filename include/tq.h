@@ -30,7 +30,8 @@
  *    except tq_codebook_init (uploads tables, then synchronises the stream)
  *    and tq_get_status (reads the status word back).  No device memory is
  *    allocated in hot calls.  A tq_ctx is immutable after init apart from its
- *    status word, so calls on different streams may share it.
+ *    status word and its profiling slots (tq_profile_begin), so calls on
+ *    different streams may share it while profiling is off.
  *  - head_dim d = 128 is the size the kernels are built for.
  *
  * Page format (one page = one layer x one sequence x P tokens x all H_kv heads):
@@ -167,6 +168,16 @@ TQ_API int tq_decode_attn(const tq_ctx* ctx, const void* q, int q_dtype, const u
                           const uint16_t* k_win, const uint16_t* v_win, float sm_scale, float* out,
                           void* workspace, size_t workspace_bytes, int pages_per_split, float* dbg_logits,
                           int64_t logits_stride, void* stream);
+
+/* Kernel timing for measurement.  tq_profile_begin(ctx, n) arms the context:
+ * the next n tq_decode_attn calls record a pair of HIP events on their stream
+ * around the compressed-page scan kernel (the kernel that streams the packed
+ * cache).  tq_profile_end waits for those events, writes the summed scan time
+ * in milliseconds and the number of recorded calls, and disarms the context.
+ * While armed, the context must not be used by two threads at once.
+ * Returns TQ_ERR_HIP if events cannot be created or read. */
+TQ_API int tq_profile_begin(tq_ctx* ctx, int max_calls);
+TQ_API int tq_profile_end(tq_ctx* ctx, double* scan_ms_total, int* calls);
 
 /* Read and clear the device status word (synchronises the context's device). */
 TQ_API int tq_get_status(tq_ctx* ctx, int* code);

@@ -27,6 +27,7 @@ TQ_STATUS_BAD_PAGE, TQ_STATUS_BAD_COUNT = 1, 2
 EXPORTED = [
     "tq_host_tables", "tq_codebook_init", "tq_destroy", "tq_page_bytes", "tq_encode",
     "tq_append_page", "tq_decode_workspace_bytes", "tq_decode_attn", "tq_get_status", "tq_strerror",
+    "tq_profile_begin", "tq_profile_end",
 ]
 
 
@@ -78,6 +79,8 @@ def lib():
         "tq_decode_attn": (i32, [P, P, i32, P, i64, P, i32, i32, P, P, P, f32, P, P, sz, i32, P, i64, P]),
         "tq_get_status": (i32, [P, ctypes.POINTER(ctypes.c_int)]),
         "tq_strerror": (ctypes.c_char_p, [i32]),
+        "tq_profile_begin": (i32, [P, i32]),
+        "tq_profile_end": (i32, [P, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int)]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(L, name)
@@ -227,3 +230,15 @@ def tq_get_status(ctx):
     code = ctypes.c_int(0)
     _check(lib().tq_get_status(ctx.handle, ctypes.byref(code)), "tq_get_status")
     return code.value
+
+
+def tq_profile_begin(ctx, max_calls):
+    _check(lib().tq_profile_begin(ctx.handle, max_calls), "tq_profile_begin")
+
+
+def tq_profile_end(ctx):
+    """Returns (summed scan-kernel milliseconds, number of recorded decode calls)."""
+    ms = ctypes.c_double(0.0)
+    n = ctypes.c_int(0)
+    _check(lib().tq_profile_end(ctx.handle, ctypes.byref(ms), ctypes.byref(n)), "tq_profile_end")
+    return ms.value, n.value

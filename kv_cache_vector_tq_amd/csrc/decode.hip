@@ -410,6 +410,8 @@ int launch_decode(const tq_ctx* c, const DecodeArgs& a, void* stream) {
   if (hipGetLastError() != hipSuccess) return 1;
   dim3 grid(a.splits, k.Hkv, a.batch);
   const int bk = c->p.key_bits, bv = c->p.value_bits;
+  void* ev0 = profile_slot(c, 0);
+  if (ev0 && hipEventRecord(static_cast<hipEvent_t>(ev0), s) != hipSuccess) return 1;
   switch (k.G) {
     case 1: launch_scan_g<1>(bk, bv, qjl, grid, s, a, c->t, c->cb, k); break;
     case 2: launch_scan_g<2>(bk, bv, qjl, grid, s, a, c->t, c->cb, k); break;
@@ -418,6 +420,7 @@ int launch_decode(const tq_ctx* c, const DecodeArgs& a, void* stream) {
     default: return 1;
   }
   if (hipGetLastError() != hipSuccess) return 1;
+  if (ev0 && hipEventRecord(static_cast<hipEvent_t>(profile_slot(c, 1)), s) != hipSuccess) return 1;
   hipLaunchKernelGGL(merge_kernel, dim3(k.G, k.Hkv, a.batch), dim3(kD), 0, s, a, c->t, k);
   return hipGetLastError() == hipSuccess ? 0 : 1;
 }

@@ -177,6 +177,41 @@ TQ_API int tq_destroy(tq_ctx* c) {
   return rc;
 }
 
+TQ_API int tq_profile_begin(tq_ctx* c, int max_calls) {
+  if (!c || max_calls < 0 || max_calls > 100000) return TQ_ERR_INVALID_ARG;
+  int rc = TQ_OK;
+  for (void* e : c->prof_events)
+    if (hipEventDestroy(static_cast<hipEvent_t>(e)) != hipSuccess) rc = TQ_ERR_HIP;
+  c->prof_events.clear();
+  c->prof_next = 0;
+  for (int i = 0; i < 2 * max_calls; ++i) {
+    hipEvent_t e;
+    if (hipEventCreate(&e) != hipSuccess) return TQ_ERR_HIP;
+    c->prof_events.push_back(e);
+  }
+  return rc;
+}
+
+TQ_API int tq_profile_end(tq_ctx* c, double* scan_ms_total, int* calls) {
+  if (!c || !scan_ms_total || !calls) return TQ_ERR_INVALID_ARG;
+  double tot = 0.0;
+  int rc = TQ_OK;
+  for (int i = 0; i < c->prof_next; ++i) {
+    hipEvent_t a = static_cast<hipEvent_t>(c->prof_events[2 * i]);
+    hipEvent_t b = static_cast<hipEvent_t>(c->prof_events[2 * i + 1]);
+    float ms = 0.0f;
+    if (hipEventSynchronize(b) != hipSuccess || hipEventElapsedTime(&ms, a, b) != hipSuccess) rc = TQ_ERR_HIP;
+    tot += ms;
+  }
+  *scan_ms_total = tot;
+  *calls = c->prof_next;
+  for (void* e : c->prof_events)
+    if (hipEventDestroy(static_cast<hipEvent_t>(e)) != hipSuccess) rc = TQ_ERR_HIP;
+  c->prof_events.clear();
+  c->prof_next = 0;
+  return rc;
+}
+
 TQ_API int tq_get_status(tq_ctx* c, int* code) {
   if (!c || !code) return TQ_ERR_INVALID_ARG;
   int prev = 0;
@@ -275,3 +310,16 @@ TQ_API int tq_decode_attn(const tq_ctx* c, const void* q, int q_dtype, const uin
 }
 
 }  // extern "C"
+
+namespace tq {
+// which = 0: start event of this call's scan (claims a slot), 1: its stop event.
+void* profile_slot(const tq_ctx* c, int which) {
+  if (which == 0) {
+    if (2 * (c->prof_next + 1) > static_cast<int>(c->prof_events.size())) return nullptr;
+    return c->prof_events[2 * c->prof_next];
+  }
+  void* e = c->prof_events[2 * c->prof_next + 1];
+  ++c->prof_next;
+  return e;
+}
+}  // namespace tq

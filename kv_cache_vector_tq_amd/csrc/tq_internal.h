@@ -124,11 +124,16 @@ struct Ctx;  // tq_ctx
 int launch_encode(const tq_ctx* ctx, int kind, int dtype, const EncodeArgs& a, void* stream);
 int launch_append(const tq_ctx* ctx, const AppendArgs& a, void* stream);
 int launch_decode(const tq_ctx* ctx, const DecodeArgs& a, void* stream);
+// Events to record around the scan kernel of this call (nullptr when not profiling).
+void* profile_slot(const tq_ctx* ctx, int which);
 
 }  // namespace tq
 
 struct tq_ctx {
   tq_params p;
+  // measurement hooks (tq_profile_begin / tq_profile_end)
+  mutable std::vector<void*> prof_events;  // hipEvent_t pairs
+  mutable int prof_next = 0;
   tq::Layout lay;
   int device;
   void* dmem;

@@ -34,6 +34,8 @@ def _compare_caches(s, ref, pool_gpu, kwin, vwin, lens_gpu):
     gcache.pool = pool_gpu.reshape(ref.pool.shape)
     gcache.block_table = ref.block_table
     gcache.seq_lens = ref.seq_lens
+    gcache.k_win = kwin.view(np.float16).reshape(ref.k_win.shape)
+    gcache.v_win = vwin.view(np.float16).reshape(ref.v_win.shape)
     for b in range(len(lens_gpu)):
         C = max(int(ref.seq_lens[b]) - s.W, 0)
         for pg in range(-(-C // s.P)):

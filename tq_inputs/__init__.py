@@ -108,3 +108,36 @@ def kv_block(seed, d, T, layer=0, head=0, seq=0, start=0):
     k = fp16(keys(seed, d, pos, layer, head, seq))
     v = fp16(values(seed, d, T, layer, head, seq, start))
     return k, v
+
+
+def torch_kv(seed, B, H, T, d, device, layer=0, start=0, out_dtype=None):
+    """The same key/value recipe drawn with torch's generator on a device (for
+    benchmark-sized workloads; a different random stream from ``keys`` /
+    ``values``).  Returns fp16 tensors [B, H, T, d]."""
+    import torch
+    g = torch.Generator(device=device)
+    g.manual_seed(int(np.random.SeedSequence([int(seed), TAG_KEY, layer]).generate_state(1)[0]))
+    scales = torch.tensor(np.stack([channel_scales(seed, d, layer, h) for h in range(H)]), dtype=torch.float32,
+                          device=device)
+    pos = torch.arange(start, start + T, device=device, dtype=torch.float64)
+    inv = torch.tensor(10000.0 ** (-np.arange(0, d, 2, dtype=np.float64) / d), device=device)
+    ang = (pos[:, None] * inv[None, :])
+    cos, sin = torch.cos(ang).float(), torch.sin(ang).float()
+    k = torch.empty((B, H, T, d), dtype=torch.float16, device=device)
+    v = torch.empty((B, H, T, d), dtype=torch.float16, device=device)
+    for b in range(B):
+        z = torch.randn((H, T, d), generator=g, device=device, dtype=torch.float32) * scales[:, None, :]
+        a, c = z[..., 0::2], z[..., 1::2]
+        r = torch.empty_like(z)
+        r[..., 0::2] = a * cos - c * sin
+        r[..., 1::2] = a * sin + c * cos
+        k[b] = r.half()
+        v[b] = torch.randn((H, T, d), generator=g, device=device, dtype=torch.float32).half()
+    return k, v
+
+
+def torch_queries(seed, shape, device, dtype, step=0):
+    import torch
+    g = torch.Generator(device=device)
+    g.manual_seed(int(np.random.SeedSequence([int(seed), TAG_QUERY, step]).generate_state(1)[0]))
+    return torch.randn(shape, generator=g, device=device, dtype=torch.float32).to(dtype)
