@@ -40,6 +40,7 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--T", type=int, default=32768)
     ap.add_argument("--batch", type=int, default=16)
+    ap.add_argument("--valu-scan", action="store_true", help="time the vector-ALU scan kernel instead")
     return ap.parse_args()
 
 
@@ -88,7 +89,8 @@ def main():
     nsteps = args.warmup + args.steps
     T0 = Tf - nsteps
     params = tqa.make_params(key_bits=3, key_qjl=1, value_bits=4, rotation=tqa.TQ_ROT_DENSE, num_q_heads=Hq,
-                             num_kv_heads=Hkv, page_tokens=P, window=W, seed=0)
+                             num_kv_heads=Hkv, page_tokens=P, window=W, seed=0,
+                             flags=tqa.TQ_FLAG_VALU_SCAN if args.valu_scan else 0)
     ctx = tqa.Context(params, tq_inputs.rotation_draws(0, d), tq_inputs.qjl_draws(0, d))
     pb = tqa.tq_page_bytes(params)
     max_pages = -(-(Tf - W) // P)
@@ -153,7 +155,7 @@ def main():
         "scan_us": scan_s * 1e6,
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBPS, "traffic": None,
-                     "kernel": "scan_kernel (compressed-page scan)",
+                     "kernel": "scan_kernel (VALU)" if args.valu_scan else "scan_mfma_kernel",
                      "algorithmic_bytes_per_launch": sum(comp_bytes) / len(comp_bytes)},
     }
     if not args.no_cpu_baseline:

@@ -73,6 +73,10 @@ enum {
 enum { TQ_ROT_DENSE = 0, TQ_ROT_HADAMARD = 1 };
 enum { TQ_DTYPE_F16 = 0, TQ_DTYPE_BF16 = 1, TQ_DTYPE_F32 = 2 };
 enum { TQ_KIND_KEY = 0, TQ_KIND_VALUE = 1 };
+/* tq_params.flags: TQ_FLAG_VALU_SCAN selects the vector-ALU decode scan
+ * instead of the matrix-core one (same results to the stated tolerance; kept
+ * for measurement and cross-checking). */
+enum { TQ_FLAG_VALU_SCAN = 1 };
 
 /* Bits of the device status word (tq_get_status). */
 enum {
@@ -91,7 +95,7 @@ typedef struct tq_params {
   int32_t num_kv_heads; /* H_kv; H_q % H_kv == 0, query head g reads kv head g / (H_q/H_kv) */
   int32_t page_tokens;  /* P, a multiple of 32, at most 1024 */
   int32_t window;       /* W, FP16 recent tokens per sequence, 0..1024 */
-  int32_t reserved;
+  int32_t flags;        /* TQ_FLAG_* bits, 0 for the default kernels */
   uint64_t seed;        /* recorded in page headers (cache identity); draws come from the caller */
 } tq_params;
 
@@ -105,7 +109,8 @@ typedef struct tq_ctx tq_ctx;
  * itself (row i gives sign bit i); may be NULL when key_qjl == 0.
  * Outputs (each nullable): rotation d*d f32 (DENSE: Pi row-major; HADAMARD:
  * the d signs), qjl d*d f32, key/value centroids 2^b f32 (Lloyd-Max levels of
- * N(0,1) times 1/sqrt(d)), key/value boundaries 2^b - 1 f32 (midpoints).
+ * N(0,1) times 1/sqrt(d), rounded to half-precision values), key/value
+ * boundaries 2^b - 1 f32 (midpoints of the stored levels).
  * Returns TQ_ERR_INVALID_ARG for bad params or missing draws. */
 TQ_API int tq_host_tables(const tq_params* params, const double* rot_draws, const double* qjl_draws,
                           float* rotation, float* qjl, float* key_centroids, float* key_boundaries,

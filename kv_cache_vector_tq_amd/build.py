@@ -21,7 +21,7 @@ COMMON = [
     # packed FP32 instructions are kept out of every kernel
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
 ]
-SOURCES = ["tables.cpp", "tq_api.cpp", "encode.hip", "decode.hip"]
+SOURCES = ["tables.cpp", "tq_api.cpp", "encode.hip", "decode.hip", "decode_mfma.hip"]
 
 
 def _hipcc():

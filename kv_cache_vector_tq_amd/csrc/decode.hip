@@ -13,40 +13,12 @@
 //  3. merge: per (b, query head) combine the split partials in fixed order,
 //     score the FP16 window exactly in the original basis, apply Pi^T to the
 //     rotated accumulator once and normalise.
+#include "decode_common.h"
 #include "device_common.h"
 #include "tq_internal.h"
 
 namespace tq {
 namespace {
-
-constexpr int kScanThreads = 256;
-
-struct KParams {
-  int Hq, Hkv, G, P, W;
-  int64_t page_bytes, head_bytes, k_norm, k_rnorm, k_codes, k_signs, v_norm, v_codes;
-  int rotation;
-  float qjl_scale;
-};
-
-KParams make_kparams(const tq_ctx* c) {
-  KParams k;
-  k.Hq = c->p.num_q_heads;
-  k.Hkv = c->p.num_kv_heads;
-  k.G = k.Hq / k.Hkv;
-  k.P = c->p.page_tokens;
-  k.W = c->p.window;
-  k.page_bytes = c->lay.page_bytes;
-  k.head_bytes = c->lay.head_bytes;
-  k.k_norm = c->lay.k_norm;
-  k.k_rnorm = c->lay.k_rnorm;
-  k.k_codes = c->lay.k_codes;
-  k.k_signs = c->lay.k_signs;
-  k.v_norm = c->lay.v_norm;
-  k.v_codes = c->lay.v_codes;
-  k.rotation = c->p.rotation;
-  k.qjl_scale = 1.2533141373155003f / static_cast<float>(c->p.head_dim);  // sqrt(pi/2)/d
-  return k;
-}
 
 // ---------------------------------------------------------------- prep
 __global__ __launch_bounds__(kD) void prep_kernel(DecodeArgs a, DevTables t, KParams k, int qjl) {
@@ -412,14 +384,18 @@ int launch_decode(const tq_ctx* c, const DecodeArgs& a, void* stream) {
   const int bk = c->p.key_bits, bv = c->p.value_bits;
   void* ev0 = profile_slot(c, 0);
   if (ev0 && hipEventRecord(static_cast<hipEvent_t>(ev0), s) != hipSuccess) return 1;
-  switch (k.G) {
-    case 1: launch_scan_g<1>(bk, bv, qjl, grid, s, a, c->t, c->cb, k); break;
-    case 2: launch_scan_g<2>(bk, bv, qjl, grid, s, a, c->t, c->cb, k); break;
-    case 4: launch_scan_g<4>(bk, bv, qjl, grid, s, a, c->t, c->cb, k); break;
-    case 8: launch_scan_g<8>(bk, bv, qjl, grid, s, a, c->t, c->cb, k); break;
-    default: return 1;
+  if (c->p.flags & TQ_FLAG_VALU_SCAN) {
+    switch (k.G) {
+      case 1: launch_scan_g<1>(bk, bv, qjl, grid, s, a, c->t, c->cb, k); break;
+      case 2: launch_scan_g<2>(bk, bv, qjl, grid, s, a, c->t, c->cb, k); break;
+      case 4: launch_scan_g<4>(bk, bv, qjl, grid, s, a, c->t, c->cb, k); break;
+      case 8: launch_scan_g<8>(bk, bv, qjl, grid, s, a, c->t, c->cb, k); break;
+      default: return 1;
+    }
+    if (hipGetLastError() != hipSuccess) return 1;
+  } else if (launch_scan_mfma(c, a, k, stream) != 0) {
+    return 1;
   }
-  if (hipGetLastError() != hipSuccess) return 1;
   if (ev0 && hipEventRecord(static_cast<hipEvent_t>(profile_slot(c, 1)), s) != hipSuccess) return 1;
   hipLaunchKernelGGL(merge_kernel, dim3(k.G, k.Hkv, a.batch), dim3(kD), 0, s, a, c->t, k);
   return hipGetLastError() == hipSuccess ? 0 : 1;

@@ -1,5 +1,6 @@
-// Host-side construction of the constant tables (double precision, rounded
-// to f32): Lloyd-Max codebooks for N(0,1) scaled by 1/sqrt(d), the dense
+// Host-side construction of the constant tables (double precision, then
+// rounded): Lloyd-Max codebooks for N(0,1) scaled by 1/sqrt(d) and stored as
+// half-precision values (the pages leave the storage precision open), the dense
 // Haar rotation from Gaussian draws by Householder QR, Rademacher signs for
 // the Hadamard variant, and the QJL matrix.
 //
@@ -69,8 +70,9 @@ void codebook_f32(int bits, int d, float* centroids, float* boundaries) {
   std::vector<double> unit = lloyd_max_normal(bits);
   const int L = 1 << bits;
   const double scale = 1.0 / std::sqrt(static_cast<double>(d));
+  // levels are stored as half-precision values (rounded once from double)
   std::vector<float> c(L);
-  for (int k = 0; k < L; ++k) c[k] = static_cast<float>(unit[k] * scale);
+  for (int k = 0; k < L; ++k) c[k] = static_cast<float>(static_cast<_Float16>(unit[k] * scale));
   if (centroids) std::memcpy(centroids, c.data(), L * sizeof(float));
   if (boundaries)
     for (int k = 0; k + 1 < L; ++k)

@@ -21,6 +21,7 @@ bool params_ok(const tq_params* p) {
   if (p->num_q_heads <= 0 || p->num_kv_heads <= 0 || p->num_q_heads % p->num_kv_heads) return false;
   if (p->page_tokens <= 0 || p->page_tokens % tq::kVGroup || p->page_tokens > tq::kMaxPage) return false;
   if (p->window < 0 || p->window > tq::kMaxWindow) return false;
+  if (p->flags & ~TQ_FLAG_VALU_SCAN) return false;
   return true;
 }
 

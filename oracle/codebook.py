@@ -12,9 +12,12 @@ Reading taken here (the pages do not spell out the construction):
   midpoint of neighbouring centroids), started from evenly spaced levels,
   stopped when no level moves by 1e-14; the quantiser is kept exactly
   symmetric by iterating the positive half and mirroring it;
-* the stored codebook is the scaled levels rounded to float32; decision
-  boundaries are the midpoints of the float32 levels, rounded to float32; a
-  value equal to a boundary takes the lower index.
+* the stored codebook is the scaled levels rounded (once, from double) to
+  IEEE half precision; the pages do not fix the storage precision, and the
+  package README's decode returns float16 vectors ("aither-kvcache",
+  "Where This Fits"), so reconstructions are half-precision values either
+  way.  Decision boundaries are the midpoints of the stored levels (exact in
+  float32); a value equal to a boundary takes the lower index.
 """
 
 import math
@@ -101,8 +104,8 @@ def gaussian_distortion(levels) -> float:
 class Codebook:
     """Stored codebook for one bit width and head dimension.
 
-    ``centroids`` and ``boundaries`` are float32 values held as float64 so that
-    every later step uses them as exact numbers.
+    ``centroids`` are half-precision values and ``boundaries`` float32 values,
+    held as float64 so that every later step uses them as exact numbers.
     """
 
     def __init__(self, bits: int, head_dim: int):
@@ -110,7 +113,7 @@ class Codebook:
         self.head_dim = head_dim
         unit = lloyd_max_normal(bits)
         scale = 1.0 / math.sqrt(head_dim)
-        self.centroids = np.array([np.float32(c * scale) for c in unit], dtype=np.float64)
+        self.centroids = np.array([np.float16(c * scale) for c in unit], dtype=np.float64)
         c = self.centroids
         self.boundaries = np.array(
             [np.float32((c[k] + c[k + 1]) * 0.5) for k in range(len(c) - 1)], dtype=np.float64

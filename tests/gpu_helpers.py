@@ -21,15 +21,15 @@ from oracle import codec
 BAND = 2.0 ** -16
 
 
-def params_for(setup):
-    return tqa.make_params(
+def params_for(setup, flags=0):
+    return tqa.make_params(flags=flags,
         head_dim=setup.d, key_bits=setup.bK, key_qjl=setup.qjl, value_bits=setup.bV,
         rotation=tqa.TQ_ROT_DENSE if setup.rotation == "dense" else tqa.TQ_ROT_HADAMARD,
         num_q_heads=setup.Hq, num_kv_heads=setup.Hkv, page_tokens=setup.P, window=setup.W, seed=setup.seed)
 
 
-def context_for(setup):
-    return tqa.Context(params_for(setup), setup.rot_draws, setup.qjl_draws if setup.qjl else None)
+def context_for(setup, flags=0):
+    return tqa.Context(params_for(setup, flags), setup.rot_draws, setup.qjl_draws if setup.qjl else None)
 
 
 def code_band(x, R, cb):

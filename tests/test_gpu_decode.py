@@ -42,13 +42,14 @@ CASES = [
 ]
 
 
+@pytest.mark.parametrize("kernel", ["mfma", "valu"])
 @pytest.mark.parametrize("name,kw,lens", CASES, ids=[c[0] for c in CASES])
-def test_decode_parity_oracle_pages(name, kw, lens):
-    print(f"case {name}", flush=True)
+def test_decode_parity_oracle_pages(name, kw, lens, kernel):
+    print(f"case {name} {kernel}", flush=True)
     s = Setup(**kw)
     cache = s.cache(len(lens), max(lens))
     fill(s, cache, lens)
-    ctx = context_for(s)
+    ctx = context_for(s, tqa.TQ_FLAG_VALU_SCAN if kernel == "valu" else 0)
     dev = upload_cache(cache)
     q = tq_inputs.queries(5, (len(lens), s.Hq, 128))
     qt = torch.from_numpy(q.astype(np.float32)).cuda()

@@ -83,10 +83,14 @@ def test_lloyd_fixed_point(bits):
 
 
 @pytest.mark.parametrize("bits", [2, 3, 4])
-def test_scaled_codebook_float32_and_boundaries(bits):
+def test_scaled_codebook_half_and_boundaries(bits):
     cb = cbm.Codebook(bits, 128)
     unit = np.array(cbm.lloyd_max_normal(bits))
-    assert np.array_equal(cb.centroids, (unit / math.sqrt(128)).astype(np.float32).astype(np.float64))
+    assert np.array_equal(cb.centroids, (unit / math.sqrt(128)).astype(np.float16).astype(np.float64))
+    # rounding to half moves each level by at most 2^-11 relative
+    assert np.all(np.abs(cb.centroids * math.sqrt(128) / unit - 1) <= 2.0 ** -11)
+    # boundaries are exact midpoints
+    assert np.array_equal(cb.boundaries, (cb.centroids[1:] + cb.centroids[:-1]) / 2)
     assert np.array_equal(cb.centroids, -cb.centroids[::-1])
     assert cb.boundaries[len(cb.boundaries) // 2] == 0.0
     assert np.all(cb.boundaries > cb.centroids[:-1]) and np.all(cb.boundaries < cb.centroids[1:])
