@@ -41,6 +41,8 @@ def parse():
     ap.add_argument("--T", type=int, default=32768)
     ap.add_argument("--batch", type=int, default=16)
     ap.add_argument("--valu-scan", action="store_true", help="time the vector-ALU scan kernel instead")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 1 GiB device-to-device copy (reference for HBM byte counters)")
     return ap.parse_args()
 
 
@@ -77,6 +79,14 @@ def main():
                           "n_gpus": args.gpus}))
         sys.exit(2)
     import torch
+    if args.copy_calibration:
+        src = torch.ones(1 << 30, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_read": 1 << 30, "copy_bytes_written": 1 << 30, "launches": 3}))
+        return
     import kv_cache_vector_tq_amd as tqa
     import tq_inputs
     if not os.path.exists(tqa.LIB_PATH):

@@ -27,19 +27,16 @@ namespace {
 typedef _Float16 h8 __attribute__((ext_vector_type(8)));
 typedef float f4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u3 __attribute__((ext_vector_type(3)));
+typedef uint32_t u2 __attribute__((ext_vector_type(2)));
 
-constexpr int kChunk = 32;
+constexpr int kChunk = 32;                   // tokens per wave iteration (one value group)
 constexpr int kWaves = kScanThreads / 64;
+constexpr float kLazy = 8.0f;                // log2 headroom before the running max moves
+constexpr uint32_t kRsrcWord3 = 0x00020000;  // raw buffer descriptor flags (gfx9 family)
 
 __device__ inline uint32_t h_bits(float x) {
   return static_cast<uint32_t>(__builtin_bit_cast(uint16_t, static_cast<_Float16>(x)));
-}
-
-// fp16 hi part and fp16 remainder of x
-__device__ inline void split_hl(float x, uint32_t& hi, uint32_t& lo) {
-  const _Float16 h = static_cast<_Float16>(x);
-  hi = static_cast<uint32_t>(__builtin_bit_cast(uint16_t, h));
-  lo = h_bits(x - static_cast<float>(h));
 }
 
 __device__ inline f4 mfma(u4 a, u4 b, f4 c) {
@@ -48,45 +45,87 @@ __device__ inline f4 mfma(u4 a, u4 b, f4 c) {
 
 __device__ inline void wave_sync() { __builtin_amdgcn_wave_barrier(); }
 
-// Lookup-table entries per bit width: a slice of the code stream -> fp16 values.
-//   B=2: 8-bit slice (4 codes) -> 4 fp16 (two words per entry, 256 entries)
-//   B=3: 6-bit slice (2 codes) -> 2 fp16 (one word, 64 entries)
-//   B=4: 8-bit slice (2 codes) -> 2 fp16 (one word, 256 entries)
+template <int CTRL>
+__device__ inline float dpp(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xF, 0xF, false));
+}
+
+// max / sum over the 16 lanes of a row (row_ror 8, row_ror 4, quad swaps)
+__device__ inline float row_max(float x) {
+  x = fmaxf(x, dpp<0x128>(x));
+  x = fmaxf(x, dpp<0x124>(x));
+  x = fmaxf(x, dpp<0x4E>(x));
+  return fmaxf(x, dpp<0xB1>(x));
+}
+__device__ inline float row_sum(float x) {
+  x += dpp<0x128>(x);
+  x += dpp<0x124>(x);
+  x += dpp<0x4E>(x);
+  return x + dpp<0xB1>(x);
+}
+
+// fp16 pair (RTZ) of two floats
+__device__ inline uint32_t pk_rtz(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(a, b));
+}
+
+// part 0: x truncated to fp16; part 1: x minus that truncation (exact in fp32),
+// selected by a per-lane mask (0 for part 0, 0xffffe000 for part 1).  For
+// |x| below the fp16 normal range the two parts still add up to x within 2^-24.
+__device__ inline float part_of(float x, uint32_t mask) {
+  return x - __builtin_bit_cast(float, __builtin_bit_cast(uint32_t, x) & mask);
+}
+
+// x rounded to fp16, packed pairs: part 0 = hi, part 1 = remainder
+__device__ inline uint32_t pack_part(float x0, float x1, int part) {
+  const _Float16 h0 = static_cast<_Float16>(x0), h1 = static_cast<_Float16>(x1);
+  if (part == 0)
+    return static_cast<uint32_t>(__builtin_bit_cast(uint16_t, h0)) |
+           (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, h1)) << 16);
+  return h_bits(x0 - static_cast<float>(h0)) | (h_bits(x1 - static_cast<float>(h1)) << 16);
+}
+
+// Lookup tables turning packed codes into fp16 MFMA operands.  A "pair"
+// table maps the 2B bits of two consecutive codes to their two fp16 centroids
+// (one word).  Tables of 16 or 64 words sit in distinct LDS banks, so random
+// lookups by the 64 lanes only broadcast or hit different banks; the 256-word
+// table of 4-bit codes is stored in 32 copies (word e of copy c at 32e + c)
+// and lane l reads copy l % 32, which keeps its lookups conflict-free too.
 template <int B>
-struct Lut {
-  static constexpr int kEntries = B == 3 ? 64 : 256;
-  static constexpr int kWords = B == 2 ? 2 : 1;
-  static constexpr int kSlice = B == 3 ? 6 : 8;
+struct PairLut {
+  static constexpr int kEntries = 1 << (2 * B);
+  static constexpr int kCopies = B == 4 ? 32 : 1;
+  static constexpr int kWords = kEntries * kCopies;
 };
 
 template <int B>
-__device__ void build_lut(uint32_t* lut, const float* cen, int tid) {
-  for (int e = tid; e < Lut<B>::kEntries; e += kScanThreads) {
-    if constexpr (B == 2) {
-      lut[2 * e] = h_bits(cen[e & 3]) | (h_bits(cen[(e >> 2) & 3]) << 16);
-      lut[2 * e + 1] = h_bits(cen[(e >> 4) & 3]) | (h_bits(cen[(e >> 6) & 3]) << 16);
-    } else if constexpr (B == 3) {
-      lut[e] = h_bits(cen[e & 7]) | (h_bits(cen[(e >> 3) & 7]) << 16);
-    } else {
-      lut[e] = h_bits(cen[e & 15]) | (h_bits(cen[(e >> 4) & 15]) << 16);
-    }
+__device__ void build_pair_lut(uint32_t* lut, const float* cen, int tid) {
+  using L = PairLut<B>;
+  constexpr int m = (1 << B) - 1;
+  for (int w = tid; w < L::kWords; w += kScanThreads) {
+    const int e = w / L::kCopies;
+    lut[w] = h_bits(cen[e & m]) | (h_bits(cen[(e >> B) & m]) << 16);
   }
 }
 
-// 8 consecutive codes (8*B bits, LSB-first in x) -> 8 fp16 values.
+// 8 consecutive codes (8*B bits, LSB-first in x) -> 8 fp16 values; `lut` is
+// the lane's copy (already offset by lane % 32 for replicated tables).
 template <int B>
 __device__ inline u4 dec8(uint32_t x, const uint32_t* lut) {
+  using L = PairLut<B>;
+  constexpr uint32_t m = (1u << (2 * B)) - 1u;
   u4 r;
-  if constexpr (B == 2) {
-    const uint2 a = reinterpret_cast<const uint2*>(lut)[x & 255u];
-    const uint2 b = reinterpret_cast<const uint2*>(lut)[(x >> 8) & 255u];
-    r.x = a.x; r.y = a.y; r.z = b.x; r.w = b.y;
-  } else if constexpr (B == 3) {
-    r.x = lut[x & 63u]; r.y = lut[(x >> 6) & 63u]; r.z = lut[(x >> 12) & 63u]; r.w = lut[(x >> 18) & 63u];
-  } else {
-    r.x = lut[x & 255u]; r.y = lut[(x >> 8) & 255u]; r.z = lut[(x >> 16) & 255u]; r.w = lut[x >> 24];
-  }
+  r.x = lut[(x & m) * L::kCopies];
+  r.y = lut[((x >> (2 * B)) & m) * L::kCopies];
+  r.z = lut[((x >> (4 * B)) & m) * L::kCopies];
+  r.w = lut[((x >> (6 * B)) & m) * L::kCopies];
   return r;
+}
+
+// sign bits -> fp16 +-1 (bit set = +1): a nibble table of 16 two-word entries
+__device__ inline u4 dec_signs8(uint32_t x, const u2* lutN) {
+  const u2 a = lutN[x & 15u], c = lutN[(x >> 4) & 15u];
+  return u4{a.x, a.y, c.x, c.y};
 }
 
 // Codes 8i .. 8i+7 of a lane's 32-code key slice held in B words.
@@ -97,31 +136,37 @@ __device__ inline uint32_t key_slice(const uint32_t* w, int i) {
   else return bits_at<24>(w, 24 * i);
 }
 
-template <int BK, int BV, bool QJL>
+template <int BK, int BV>
 struct Chunk {
-  uint32_t kc[2][BK];   // key codes: tile t, lane's 32-coordinate slice
-  uint32_t sg[2];       // sign bits of that slice
-  float kn[2], rn[2];   // key norms / residual norms of tokens n, 16+n
-  float vn;             // value norm of token (lane & 31)
-  uint32_t vw[8];       // value words for coordinates 8n..8n+7 (tokens 8kg..)
-  uint32_t vw2[8];      // second word when a 3-bit slice straddles words
-  int ntok;             // live tokens in the chunk (0 when the page is invalid)
-  int64_t pos0;         // position of the chunk's first token
+  uint32_t kc[2][BK];  // key codes of tokens n / 16+n, coordinates 32kg .. 32kg+31
+  uint32_t sg[2];      // their sign bits
+  float kn[2], rn[2], vn[2];
+  uint32_t vw[8];      // value words: coordinates 8n .. 8n+7, tokens 8kg .. 8kg+7
+  uint32_t vw2[8];     // next word when a 3-bit slice straddles two words
+  int ntok;            // live tokens (0 when the page id is invalid)
+  int pos0;            // position of the chunk's first token
 };
 
+// A row m of every MFMA holds query g = 2(m/4) + (m%2), part (m/2)%2 (0: fp16
+// hi, 1: remainder); the product's rows 4kg + r land in lane group kg, so a
+// lane sees query 2kg + i as rows i (hi) and i + 2 (remainder) and adds them.
 template <int G, int BK, int BV, bool QJL>
 __global__ __launch_bounds__(kScanThreads) void scan_mfma_kernel(DecodeArgs a, DevTables t, Codebooks cb,
                                                                  KParams k) {
-  __shared__ uint32_t lutK[Lut<BK>::kEntries * Lut<BK>::kWords];
-  __shared__ uint32_t lutV[Lut<BV>::kEntries * Lut<BV>::kWords];
-  __shared__ u4 lutS[QJL ? 256 : 1];
-  __shared__ float sc[kWaves][G][kChunk];  // scores, then weights * value norm
-  __shared__ float crr[kWaves][G];         // per-chunk rescale factors
+  // one table when keys and values share a bit width (same codebook)
+  __shared__ uint32_t lutV[PairLut<BV>::kWords];
+  __shared__ uint32_t lutKown[BK == BV ? 1 : PairLut<BK>::kWords];
+  __shared__ u2 lutN[16];
+  __shared__ float pv[kWaves][G][kChunk];  // softmax weights x value norms
   __shared__ float wm[kWaves][G], wl[kWaves][G];
-  __shared__ float red[16][kD];
+  __shared__ float red[G][kD];
+  __shared__ float ck[16], cvv[16];
 
   const int tid = threadIdx.x, split = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
-  const int wave = tid >> 6, l = tid & 63, n = l & 15, kg = l >> 4;
+  // the wave index is uniform within a wave; saying so keeps page addresses
+  // and buffer descriptors in scalar registers
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l = tid & 63, n = l & 15, kg = l >> 4;
   const int T = a.seq_lens[b];
   const int C = T - k.W > 0 ? T - k.W : 0;
   const int npages = (C + k.P - 1) / k.P;
@@ -140,8 +185,7 @@ __global__ __launch_bounds__(kScanThreads) void scan_mfma_kernel(DecodeArgs a, D
     for (int i = tid; i < G * kD; i += kScanThreads) a.pacc[pidx * kD + i] = 0.0f;
     return;
   }
-  // lookup tables (codebooks first copied to LDS: no dynamic indexing of kernel arguments)
-  __shared__ float ck[16], cvv[16];
+  // codebooks to LDS (no dynamic indexing of kernel arguments), then the tables
   if (tid < 16) {
     float kv = 0.0f, vv = 0.0f;
 #pragma unroll
@@ -154,223 +198,188 @@ __global__ __launch_bounds__(kScanThreads) void scan_mfma_kernel(DecodeArgs a, D
     cvv[tid] = vv;
   }
   __syncthreads();
-  build_lut<BK>(lutK, ck, tid);
-  build_lut<BV>(lutV, cvv, tid);
-  if constexpr (QJL) {
-    // byte of sign bits -> 8 fp16 values +-1 (bit set = +1)
+  build_pair_lut<BV>(lutV, cvv, tid);
+  if constexpr (BK != BV) build_pair_lut<BK>(lutKown, ck, tid);
+  if (tid < 16) {
     const int e = tid;
-    u4 v;
-    v.x = (e & 1 ? 0x3C00u : 0xBC00u) | ((e & 2 ? 0x3C00u : 0xBC00u) << 16);
-    v.y = (e & 4 ? 0x3C00u : 0xBC00u) | ((e & 8 ? 0x3C00u : 0xBC00u) << 16);
-    v.z = (e & 16 ? 0x3C00u : 0xBC00u) | ((e & 32 ? 0x3C00u : 0xBC00u) << 16);
-    v.w = (e & 64 ? 0x3C00u : 0xBC00u) | ((e & 128 ? 0x3C00u : 0xBC00u) << 16);
-    lutS[e] = v;
+    lutN[e] = u2{(e & 1 ? 0x3C00u : 0xBC00u) | ((e & 2 ? 0x3C00u : 0xBC00u) << 16),
+                 (e & 4 ? 0x3C00u : 0xBC00u) | ((e & 8 ? 0x3C00u : 0xBC00u) << 16)};
   }
-  // A operands of the key products: row m = n holds query m (hi) or m-G (lo);
-  // lane group kg covers coordinates 32kg .. 32kg+31, MFMA i the 8 at 32kg+8i.
+  const uint32_t* lutK = BK == BV ? lutV : lutKown;
+  const uint32_t* lutKl = lutK + (PairLut<BK>::kCopies > 1 ? (tid & 31) : 0);
+  const uint32_t* lutVl = lutV + (PairLut<BV>::kCopies > 1 ? (tid & 31) : 0);
+  // A operands of the key products: lane group kg covers coordinates
+  // 32kg .. 32kg+31, MFMA i the 8 starting at 32kg + 8i.
   const int64_t qrow = (static_cast<int64_t>(b) * k.Hq + static_cast<int64_t>(h) * G) * kD;
+  const int ag = 2 * (n >> 2) + (n & 1), apart = (n >> 1) & 1;
+  const uint32_t amask = apart ? 0xffffe000u : 0u;
   u4 aq[4], ap[4];
-  {
-    const int m = n;
-    const int g = m < G ? m : m - G;
-    const bool live = m < 2 * G;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      uint32_t wq[4] = {0, 0, 0, 0}, wp[4] = {0, 0, 0, 0};
-      if (live) {
-        const float4* q4 = reinterpret_cast<const float4*>(a.qs + qrow + g * kD + 32 * kg + 8 * i);
-        const float4* p4 = reinterpret_cast<const float4*>(a.ps + qrow + g * kD + 32 * kg + 8 * i);
-        float qv[8], pv[8];
-        const float4 q0 = q4[0], q1 = q4[1];
-        qv[0] = q0.x; qv[1] = q0.y; qv[2] = q0.z; qv[3] = q0.w; qv[4] = q1.x; qv[5] = q1.y; qv[6] = q1.z; qv[7] = q1.w;
-        if constexpr (QJL) {
-          const float4 p0 = p4[0], p1 = p4[1];
-          pv[0] = p0.x; pv[1] = p0.y; pv[2] = p0.z; pv[3] = p0.w; pv[4] = p1.x; pv[5] = p1.y; pv[6] = p1.z; pv[7] = p1.w;
-        }
-#pragma unroll
-        for (int e = 0; e < 8; e += 2) {
-          uint32_t h0, l0, h1, l1;
-          split_hl(qv[e], h0, l0);
-          split_hl(qv[e + 1], h1, l1);
-          wq[e / 2] = m < G ? (h0 | (h1 << 16)) : (l0 | (l1 << 16));
-          if constexpr (QJL) {
-            split_hl(pv[e], h0, l0);
-            split_hl(pv[e + 1], h1, l1);
-            wp[e / 2] = m < G ? (h0 | (h1 << 16)) : (l0 | (l1 << 16));
-          }
-        }
+  for (int i = 0; i < 4; ++i) {
+    aq[i] = u4{0u, 0u, 0u, 0u};
+    ap[i] = u4{0u, 0u, 0u, 0u};
+    if (ag < G) {
+      const float4* q4 = reinterpret_cast<const float4*>(a.qs + qrow + ag * kD + 32 * kg + 8 * i);
+      const float4 q0 = q4[0], q1 = q4[1];
+      aq[i] = u4{pack_part(q0.x, q0.y, apart), pack_part(q0.z, q0.w, apart), pack_part(q1.x, q1.y, apart),
+                 pack_part(q1.z, q1.w, apart)};
+      if constexpr (QJL) {
+        const float4* p4 = reinterpret_cast<const float4*>(a.ps + qrow + ag * kD + 32 * kg + 8 * i);
+        const float4 p0 = p4[0], p1 = p4[1];
+        ap[i] = u4{pack_part(p0.x, p0.y, apart), pack_part(p0.z, p0.w, apart), pack_part(p1.x, p1.y, apart),
+                   pack_part(p1.z, p1.w, apart)};
       }
-      aq[i] = u4{wq[0], wq[1], wq[2], wq[3]};
-      ap[i] = u4{wp[0], wp[1], wp[2], wp[3]};
     }
   }
   __syncthreads();
 
-  // per-wave online-softmax state; lane handles token (l & 31) of queries
-  // g = (l >> 5) + 2j (all G for G = 1 is lane < 32 only)
-  constexpr int GH = G >= 2 ? G / 2 : 1;  // queries per lane in the softmax phase
-  float mrun[GH], lrun[GH];
-#pragma unroll
-  for (int j = 0; j < GH; ++j) {
-    mrun[j] = -INFINITY;
-    lrun[j] = 0.0f;
-  }
+  // running state of queries 2kg (i = 0) and 2kg + 1 (i = 1)
+  float mrun[2] = {-INFINITY, -INFINITY}, lrun[2] = {0.0f, 0.0f};
   f4 acc[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) acc[i] = f4{0.0f, 0.0f, 0.0f, 0.0f};
 
-  const int64_t tot = static_cast<int64_t>(C < pe * k.P ? C : pe * k.P) - static_cast<int64_t>(pb) * k.P;
-  const int nchunks = static_cast<int>((tot + kChunk - 1) / kChunk);
-  const int gpp = k.P / kChunk;  // chunks per page
-  const int t32 = l & 31;
-  // value words: lane's 8 tokens of coordinate 8n + blk are bits [8*kg*BV, +8*BV)
+  const int tot = (C < pe * k.P ? C : pe * k.P) - pb * k.P;
+  const int nchunks = (tot + kChunk - 1) / kChunk;
+  // value words: the lane's 8 tokens of coordinate 8n + bl are bits [8*kg*BV, +8*BV)
   const int vbit = 8 * kg * BV;
   const int vw0 = vbit >> 5, vsh = vbit & 31;
   const bool vtwo = (vsh + 8 * BV) > 32;
+  // per-lane byte offsets inside a head block (the chunk adds a uniform offset)
+  const uint32_t o_tok0 = 4u * n, o_tok1 = 4u * (16 + n);
+  const uint32_t o_kc0 = static_cast<uint32_t>(n * 16 * BK + 4 * BK * kg);
+  const uint32_t o_kc1 = o_kc0 + 16u * 16u * BK;
+  const uint32_t o_sg0 = static_cast<uint32_t>(n * 16 + 4 * kg), o_sg1 = o_sg0 + 256u;
+  const uint32_t o_vw = static_cast<uint32_t>((vw0 * kD + 8 * n) * 4);
+  const uint32_t o_vw2 = static_cast<uint32_t>(((vtwo ? vw0 + 1 : vw0) * kD + 8 * n) * 4);
 
-  auto load = [&](int c, Chunk<BK, BV, QJL>& d) {
-    const int64_t tok0 = static_cast<int64_t>(c) * kChunk;
-    const int pg = pb + static_cast<int>(tok0 / k.P);
-    const int gi = static_cast<int>((tok0 % k.P) / kChunk);
-    const int64_t rem = tot - tok0;
-    d.ntok = rem < kChunk ? static_cast<int>(rem) : kChunk;
-    d.pos0 = static_cast<int64_t>(pg) * k.P + gi * kChunk;
-    const int pid = a.block_table[static_cast<int64_t>(b) * a.max_pages + pg];
-    if (pid < 0 || pid >= a.num_pages) {
-      if (l == 0) atomicOr(t.status, TQ_STATUS_BAD_PAGE);
-      d.ntok = 0;
-      return;
-    }
+  auto load = [&](int c, Chunk<BK, BV>& d) {
+    const int tok0 = c * kChunk;
+    const int pg = pb + tok0 / k.P;
+    const int gi = (tok0 % k.P) / kChunk;
+    const int rem = tot - tok0;
+    d.ntok = rem < kChunk ? rem : kChunk;
+    d.pos0 = pg * k.P + gi * kChunk;
+    const int pid0 = a.block_table[static_cast<int64_t>(b) * a.max_pages + pg];
+    const bool bad = pid0 < 0 || pid0 >= a.num_pages;  // flagged, then page 0 is read and the chunk skipped
+    if (bad && l == 0) atomicOr(t.status, TQ_STATUS_BAD_PAGE);
+    d.ntok = bad ? 0 : d.ntok;
+    const int pid = __builtin_amdgcn_readfirstlane(bad ? 0 : pid0);
     const uint8_t* hb = a.pool + static_cast<int64_t>(pid) * k.page_bytes + kBodyOffset + h * k.head_bytes;
+    const __amdgpu_buffer_rsrc_t rs =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(hb), 0, static_cast<int>(k.head_bytes), kRsrcWord3);
     const int s0 = gi * kChunk;
-    const float* kn = reinterpret_cast<const float*>(hb + k.k_norm);
-    const float* rn = reinterpret_cast<const float*>(hb + k.k_rnorm);
+    const int so_kn = static_cast<int>(k.k_norm) + 4 * s0;
+    d.kn[0] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, o_tok0, so_kn, 0));
+    d.kn[1] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, o_tok1, so_kn, 0));
+    if constexpr (QJL) {
+      const int so_rn = static_cast<int>(k.k_rnorm) + 4 * s0;
+      d.rn[0] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, o_tok0, so_rn, 0));
+      d.rn[1] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, o_tok1, so_rn, 0));
+      const int so_sg = static_cast<int>(k.k_signs) + 16 * s0;
+      d.sg[0] = __builtin_amdgcn_raw_buffer_load_b32(rs, o_sg0, so_sg, 0);
+      d.sg[1] = __builtin_amdgcn_raw_buffer_load_b32(rs, o_sg1, so_sg, 0);
+    }
+    const int so_kc = static_cast<int>(k.k_codes) + 16 * BK * s0;
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt) {
-      const int slot = s0 + 16 * tt + n;
-      d.kn[tt] = kn[slot];
-      if constexpr (QJL) d.rn[tt] = rn[slot];
-      const uint32_t* kw = reinterpret_cast<const uint32_t*>(hb + k.k_codes + static_cast<int64_t>(slot) * 16 * BK) + kg * BK;
+      const uint32_t o = tt ? o_kc1 : o_kc0;
       if constexpr (BK == 4) {
-        const uint4 v = *reinterpret_cast<const uint4*>(kw);
+        const u4 v = __builtin_amdgcn_raw_buffer_load_b128(rs, o, so_kc, 0);
         d.kc[tt][0] = v.x; d.kc[tt][1] = v.y; d.kc[tt][2] = v.z; d.kc[tt][3] = v.w;
-      } else if constexpr (BK == 2) {
-        const uint2 v = *reinterpret_cast<const uint2*>(kw);
-        d.kc[tt][0] = v.x; d.kc[tt][1] = v.y;
+      } else if constexpr (BK == 3) {
+        const u3 v = __builtin_amdgcn_raw_buffer_load_b96(rs, o, so_kc, 0);
+        d.kc[tt][0] = v.x; d.kc[tt][1] = v.y; d.kc[tt][2] = v.z;
       } else {
-#pragma unroll
-        for (int w = 0; w < BK; ++w) d.kc[tt][w] = kw[w];
+        const u2 v = __builtin_amdgcn_raw_buffer_load_b64(rs, o, so_kc, 0);
+        d.kc[tt][0] = v.x; d.kc[tt][1] = v.y;
       }
-      if constexpr (QJL) d.sg[tt] = reinterpret_cast<const uint32_t*>(hb + k.k_signs)[slot * 4 + kg];
     }
-    d.vn = reinterpret_cast<const float*>(hb + k.v_norm)[s0 + t32];
-    const uint32_t* vwp = reinterpret_cast<const uint32_t*>(hb + k.v_codes) + static_cast<int64_t>(gi) * BV * kD;
-    const uint4* r0 = reinterpret_cast<const uint4*>(vwp + vw0 * kD + 8 * n);
-    const uint4 x0 = r0[0], x1 = r0[1];
+    const int so_vn = static_cast<int>(k.v_norm) + 4 * s0;
+    d.vn[0] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, o_tok0, so_vn, 0));
+    d.vn[1] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, o_tok1, so_vn, 0));
+    const int so_vw = static_cast<int>(k.v_codes) + gi * BV * kD * 4;
+    const u4 x0 = __builtin_amdgcn_raw_buffer_load_b128(rs, o_vw, so_vw, 0);
+    const u4 x1 = __builtin_amdgcn_raw_buffer_load_b128(rs, o_vw + 16u, so_vw, 0);
     d.vw[0] = x0.x; d.vw[1] = x0.y; d.vw[2] = x0.z; d.vw[3] = x0.w;
     d.vw[4] = x1.x; d.vw[5] = x1.y; d.vw[6] = x1.z; d.vw[7] = x1.w;
     if constexpr (BV == 3) {
-      const int w1 = vtwo ? vw0 + 1 : vw0;
-      const uint4* r1 = reinterpret_cast<const uint4*>(vwp + w1 * kD + 8 * n);
-      const uint4 y0 = r1[0], y1 = r1[1];
+      const u4 y0 = __builtin_amdgcn_raw_buffer_load_b128(rs, o_vw2, so_vw, 0);
+      const u4 y1 = __builtin_amdgcn_raw_buffer_load_b128(rs, o_vw2 + 16u, so_vw, 0);
       d.vw2[0] = y0.x; d.vw2[1] = y0.y; d.vw2[2] = y0.z; d.vw2[3] = y0.w;
       d.vw2[4] = y1.x; d.vw2[5] = y1.y; d.vw2[6] = y1.z; d.vw2[7] = y1.w;
     }
   };
 
-  float* scw = &sc[wave][0][0];
-  auto process = [&](const Chunk<BK, BV, QJL>& d) {
+  float* pvw = &pv[wave][0][0];
+  const int64_t dbg_row = (static_cast<int64_t>(b) * k.Hq + h * G) * a.logits_stride;
+  auto process = [&](const Chunk<BK, BV>& d) {
     if (d.ntok == 0) return;
-    // ---- key scores: two 16-token tiles
+    // ---- key scores of tokens n (tile 0) and 16 + n (tile 1)
+    float sc[2][2];  // [query i][tile]
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt) {
       f4 dm = f4{0.0f, 0.0f, 0.0f, 0.0f}, dq = f4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        dm = mfma(aq[i], dec8<BK>(key_slice<BK>(d.kc[tt], i), lutK), dm);
-        if constexpr (QJL) dq = mfma(ap[i], lutS[(d.sg[tt] >> (8 * i)) & 255u], dq);
+        dm = mfma(aq[i], dec8<BK>(key_slice<BK>(d.kc[tt], i), lutKl), dm);
+        if constexpr (QJL) dq = mfma(ap[i], dec_signs8(d.sg[tt] >> (8 * i), lutN), dq);
       }
-      // rows g (hi) and g + G (lo) -> query g
-      float s[4];
-      if constexpr (G >= 4) {
-        constexpr int off = 16 * (G / 4);
+      const bool live = 16 * tt + n < d.ntok;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const float em = __shfl_down(dm[r], off, 64);
-          float v = (dm[r] + em) * d.kn[tt];
-          if constexpr (QJL) v = fmaf(dq[r] + __shfl_down(dq[r], off, 64), d.rn[tt], v);
-          s[r] = v;
-        }
-      } else {
-#pragma unroll
-        for (int r = 0; r < G; ++r) {
-          float v = (dm[r] + dm[r + G]) * d.kn[tt];
-          if constexpr (QJL) v = fmaf(dq[r] + dq[r + G], d.rn[tt], v);
-          s[r] = v;
-        }
+      for (int i = 0; i < 2; ++i) {
+        float v = (dm[i] + dm[i + 2]) * d.kn[tt];
+        if constexpr (QJL) v = fmaf(dq[i] + dq[i + 2], d.rn[tt], v);
+        sc[i][tt] = live ? v : -INFINITY;
       }
-      const int tok = 16 * tt + n;
-      const bool live = tok < d.ntok;
-      constexpr int lanes_g = G >= 4 ? G / 4 : 1;  // lane groups holding results
-      if (kg < lanes_g) {
+    }
+    if (a.dbg_logits) {
 #pragma unroll
-        for (int r = 0; r < (G >= 4 ? 4 : G); ++r) {
-          const int g = (G >= 4 ? 4 * kg : 0) + r;
-          const float v = live ? s[r] : -INFINITY;
-          scw[g * kChunk + tok] = v;
-          if (a.dbg_logits && live)
-            a.dbg_logits[(static_cast<int64_t>(b) * k.Hq + h * G + g) * a.logits_stride + d.pos0 + tok] = v * kLn2;
-        }
+      for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+          if (2 * kg + i < G && 16 * tt + n < d.ntok)
+            a.dbg_logits[dbg_row + (2 * kg + i) * a.logits_stride + d.pos0 + 16 * tt + n] = sc[i][tt] * kLn2;
+    }
+    // ---- online softmax; the running max moves only when exceeded by kLazy
+    float corr[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const float lm = fmaxf(sc[i][0], sc[i][1]);
+      bool move = false;
+      float mn = mrun[i];
+      if (__ballot(lm > mrun[i] + kLazy)) {  // rare after the first chunk
+        const float cm = row_max(lm);
+        move = cm > mrun[i] + kLazy;
+        mn = move ? cm : mrun[i];
+      }
+      corr[i] = move ? __builtin_amdgcn_exp2f(mrun[i] - mn) : 1.0f;
+      mrun[i] = mn;
+      const float w0 = __builtin_amdgcn_exp2f(sc[i][0] - mn), w1 = __builtin_amdgcn_exp2f(sc[i][1] - mn);
+      lrun[i] = fmaf(lrun[i], corr[i], w0 + w1);
+      const int g = 2 * kg + i;
+      if (g < G) {
+        pvw[g * kChunk + n] = n < d.ntok ? w0 * d.vn[0] : 0.0f;
+        pvw[g * kChunk + 16 + n] = 16 + n < d.ntok ? w1 * d.vn[1] : 0.0f;
+      }
+    }
+    if (corr[0] != 1.0f || corr[1] != 1.0f) {
+#pragma unroll
+      for (int bl = 0; bl < 8; ++bl) {
+        acc[bl][0] *= corr[0];
+        acc[bl][2] *= corr[0];
+        acc[bl][1] *= corr[1];
+        acc[bl][3] *= corr[1];
       }
     }
     wave_sync();
-    // ---- online softmax over the chunk
-    float crow[GH];
-    bool any = false;
-#pragma unroll
-    for (int j = 0; j < GH; ++j) {
-      const int g = G >= 2 ? (l >> 5) + 2 * j : 0;
-      const bool mine = G >= 2 || l < 32;
-      const float x = mine ? scw[g * kChunk + t32] : -INFINITY;
-      float cm = x;
-#pragma unroll
-      for (int o = 1; o < 32; o <<= 1) cm = fmaxf(cm, __shfl_xor(cm, o, 64));
-      const float mn = fmaxf(mrun[j], cm);
-      const float corr = exp2f(mrun[j] - mn);
-      const float w = exp2f(x - mn);
-      mrun[j] = mn;
-      lrun[j] = fmaf(lrun[j], corr, w);
-      crow[j] = corr;
-      any |= mine && corr != 1.0f;
-      if (mine) scw[g * kChunk + t32] = t32 < d.ntok ? w * d.vn : 0.0f;
-      if (mine && t32 == 0) crr[wave][g] = corr;
-    }
-    wave_sync();
-    // rescale the value accumulators if any running max moved
-    if (__ballot(any)) {
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const float f = crr[wave][(4 * kg + r) % G];
-#pragma unroll
-        for (int bl = 0; bl < 8; ++bl) acc[bl][r] *= f;
-      }
-    }
-    // ---- A operand of the value product: row m = n, tokens 8kg .. 8kg+7
+    // ---- A operand of the value product: row n, tokens 8kg .. 8kg+7
     u4 aw = u4{0u, 0u, 0u, 0u};
-    if (n < 2 * G) {
-      const int g = n < G ? n : n - G;
-      const float4* pw = reinterpret_cast<const float4*>(scw + g * kChunk + 8 * kg);
+    if (ag < G) {
+      const float4* pw = reinterpret_cast<const float4*>(pvw + ag * kChunk + 8 * kg);
       const float4 w0 = pw[0], w1 = pw[1];
-      const float wv[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
-      uint32_t ww[4];
-#pragma unroll
-      for (int e = 0; e < 8; e += 2) {
-        uint32_t h0, l0, h1, l1;
-        split_hl(wv[e], h0, l0);
-        split_hl(wv[e + 1], h1, l1);
-        ww[e / 2] = n < G ? (h0 | (h1 << 16)) : (l0 | (l1 << 16));
-      }
-      aw = u4{ww[0], ww[1], ww[2], ww[3]};
+      aw = u4{pk_rtz(part_of(w0.x, amask), part_of(w0.y, amask)), pk_rtz(part_of(w0.z, amask), part_of(w0.w, amask)),
+              pk_rtz(part_of(w1.x, amask), part_of(w1.y, amask)), pk_rtz(part_of(w1.z, amask), part_of(w1.w, amask))};
     }
     wave_sync();
     // ---- value product: block bl covers coordinates 8n' + bl
@@ -380,12 +389,12 @@ __global__ __launch_bounds__(kScanThreads) void scan_mfma_kernel(DecodeArgs a, D
       if constexpr (BV == 4) x = d.vw[bl];
       else if constexpr (BV == 2) x = (d.vw[bl] >> vsh) & 0xffffu;
       else x = vtwo ? ((d.vw[bl] >> vsh) | (d.vw2[bl] << (32 - vsh))) & 0xffffffu : (d.vw[bl] >> vsh) & 0xffffffu;
-      acc[bl] = mfma(aw, dec8<BV>(x, lutV), acc[bl]);
+      acc[bl] = mfma(aw, dec8<BV>(x, lutVl), acc[bl]);
     }
   };
 
   int c = wave;
-  Chunk<BK, BV, QJL> ca, cb2;
+  Chunk<BK, BV> ca, cb2;
   if (c < nchunks) load(c, ca);
   while (c < nchunks) {
     if (c + kWaves < nchunks) load(c + kWaves, cb2);
@@ -397,53 +406,45 @@ __global__ __launch_bounds__(kScanThreads) void scan_mfma_kernel(DecodeArgs a, D
     c += kWaves;
   }
 
-  // ---- merge the four waves
-  float lsum[GH];
+  // ---- merge the waves: per query max M, factors 2^(m_w - M)
+  float ls[2];
 #pragma unroll
-  for (int j = 0; j < GH; ++j) {
-    float v = (G >= 2 || l < 32) ? lrun[j] : 0.0f;
+  for (int i = 0; i < 2; ++i) ls[i] = row_sum(lrun[i]);
+  if (n == 0) {
 #pragma unroll
-    for (int o = 1; o < 32; o <<= 1) v += __shfl_xor(v, o, 64);
-    lsum[j] = v;
-  }
-  if (t32 == 0) {
-#pragma unroll
-    for (int j = 0; j < GH; ++j) {
-      const int g = G >= 2 ? (l >> 5) + 2 * j : 0;
-      if (G >= 2 || l < 32) {
-        wm[wave][g] = mrun[j];
-        wl[wave][g] = lsum[j];
+    for (int i = 0; i < 2; ++i)
+      if (2 * kg + i < G) {
+        wm[wave][2 * kg + i] = mrun[i];
+        wl[wave][2 * kg + i] = ls[i];
       }
-    }
   }
   __syncthreads();
-  // every lane needs M and its wave's factor for rows 4kg + r
-  float fac[4];
+  float fac[2];
 #pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const int g = (4 * kg + r) % G;
+  for (int i = 0; i < 2; ++i) {
+    const int g = 2 * kg + i < G ? 2 * kg + i : 0;
     float M = -INFINITY;
 #pragma unroll
     for (int w = 0; w < kWaves; ++w) M = fmaxf(M, wm[w][g]);
-    fac[r] = (M == -INFINITY || wm[wave][g] == -INFINITY) ? 0.0f : exp2f(wm[wave][g] - M);
+    fac[i] = (M == -INFINITY || wm[wave][g] == -INFINITY) ? 0.0f : exp2f(wm[wave][g] - M);
   }
   for (int w = 0; w < kWaves; ++w) {
     if (wave == w) {
 #pragma unroll
-      for (int bl = 0; bl < 8; ++bl)
+      for (int i = 0; i < 2; ++i) {
+        const int g = 2 * kg + i;
+        if (g < G) {
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int row = 4 * kg + r, col = 8 * n + bl;
-          const float v = acc[bl][r] * fac[r];
-          red[row][col] = (w == 0) ? v : red[row][col] + v;
+          for (int bl = 0; bl < 8; ++bl) {
+            const float v = (acc[bl][i] + acc[bl][i + 2]) * fac[i];
+            red[g][8 * n + bl] = (w == 0) ? v : red[g][8 * n + bl] + v;
+          }
         }
+      }
     }
     __syncthreads();
   }
-  for (int i = tid; i < G * kD; i += kScanThreads) {
-    const int g = i / kD, j = i % kD;
-    a.pacc[(pidx + g) * kD + j] = red[g][j] + red[g + G][j];
-  }
+  for (int i = tid; i < G * kD; i += kScanThreads) a.pacc[pidx * kD + i] = red[i / kD][i % kD];
   if (tid < G) {
     float M = -INFINITY;
 #pragma unroll
