@@ -21,46 +21,107 @@ namespace tq {
 namespace {
 
 // ---------------------------------------------------------------- prep
-__global__ __launch_bounds__(kD) void prep_kernel(DecodeArgs a, DevTables t, KParams k, int qjl) {
-  __shared__ float qv[kD], qr[kD], red[2];
-  const int j = threadIdx.x, g = blockIdx.x, b = blockIdx.y;
-  const int64_t row = (static_cast<int64_t>(b) * k.Hq + g) * kD;
-  const float c2 = a.sm_scale * kLog2e;
-  const float q = load_any(a.q, row + j, a.q_dtype);
-  a.qwin[row + j] = q * c2;
-  qv[j] = q;
-  __syncthreads();
-  float y;
-  if (k.rotation == TQ_ROT_DENSE) {
-    y = 0.0f;
-#pragma unroll 8
-    for (int i = 0; i < kD; ++i) y = fmaf(t.rotT[i * kD + j], qv[i], y);
-  } else {
-    float val = qv[j] * t.rot[j];
+constexpr int kSmallThreads = 256;
+
+// y[g][i] = sum_j M[j*kD + i] x[g][j] for the G vectors x (LDS), M a kD x kD
+// row-major table in global memory.  Thread (c, r) owns columns 4c..4c+3 and
+// rows 16r..16r+15: its 16 float4 loads are independent and in flight
+// together; the 8 row-group partials are summed in fixed order.  Called by
+// all kSmallThreads threads; ends with a barrier.
+template <int G>
+__device__ __forceinline__ void matvec_cols(const float* __restrict__ M, const float (*x)[kD],
+                                            float (*part)[G][kD], float (*y)[kD]) {
+  const int t = threadIdx.x, c4 = (t & 31) * 4, rg = t >> 5;
+  float4 m[16];
 #pragma unroll
-    for (int s = 1; s < 64; s <<= 1) {
-      const float o = __shfl_xor(val, s, 64);
-      val = (j & s) ? (o - val) : (val + o);
+  for (int r = 0; r < 16; ++r) m[r] = *reinterpret_cast<const float4*>(M + (rg * 16 + r) * kD + c4);
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    float4 acc = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const float xv = x[g][rg * 16 + r];
+      acc.x = fmaf(m[r].x, xv, acc.x);
+      acc.y = fmaf(m[r].y, xv, acc.y);
+      acc.z = fmaf(m[r].z, xv, acc.z);
+      acc.w = fmaf(m[r].w, xv, acc.w);
     }
-    qr[j] = val;
+    *reinterpret_cast<float4*>(&part[rg][g][c4]) = acc;
+  }
+  __syncthreads();
+  for (int e = t; e < G * kD; e += kSmallThreads) {
+    const int g = e / kD, i = e % kD;
+    float v = part[0][g][i];
+#pragma unroll
+    for (int r = 1; r < 8; ++r) v += part[r][g][i];
+    y[g][i] = v;
+  }
+  __syncthreads();
+}
+
+// y[g] = H (eps * x[g]) / sqrt(kD) for the randomised Hadamard rotation; in
+// place on x.  Thread (j = t & 127, hf = t >> 7) transforms g = hf, hf+2, ...
+// Called by all threads; ends with a barrier.
+template <int G>
+__device__ __forceinline__ void hadamard_lds(float (*x)[kD], const float* __restrict__ pre, const float* __restrict__ post) {
+  const int t = threadIdx.x, j = t & (kD - 1), hf = t >> 7;
+  for (int g0 = 0; g0 < G; g0 += 2) {
+    const int g = g0 + hf;
+    const bool act = g < G;
+    float val = act ? x[g][j] * (pre ? pre[j] : 1.0f) : 0.0f;
+#pragma unroll
+    for (int s2 = 1; s2 < 64; s2 <<= 1) {
+      const float ov = __shfl_xor(val, s2, 64);
+      val = (j & s2) ? (ov - val) : (val + ov);
+    }
     __syncthreads();
-    const float a0 = qr[j], b0 = qr[j ^ 64];
-    y = ((j & 64) ? (b0 - a0) : (a0 + b0)) * 0.08838834764831845f;
+    if (act) x[g][j] = val;
+    __syncthreads();
+    if (act) {
+      const float a0 = x[g][j], b0 = x[g][j ^ 64];
+      val = ((j & 64) ? (b0 - a0) : (a0 + b0)) * 0.08838834764831845f * (post ? post[j] : 1.0f);
+    }
+    __syncthreads();
+    if (act) x[g][j] = val;
+  }
+  __syncthreads();
+}
+
+// One work-group per (b, kv head) prepares its G query heads.
+template <int G>
+__global__ __launch_bounds__(kSmallThreads) void prep_kernel(DecodeArgs a, DevTables t, KParams k, int qjl) {
+  __shared__ float qv[G][kD], qr[G][kD], part[8][G][kD];
+  const int tid = threadIdx.x, h = blockIdx.x, b = blockIdx.y;
+  const int64_t row0 = (static_cast<int64_t>(b) * k.Hq + static_cast<int64_t>(h) * G) * kD;
+  const float c2 = a.sm_scale * kLog2e;
+  for (int e = tid; e < G * kD; e += kSmallThreads) {
+    const float q = load_any(a.q, row0 + e, a.q_dtype);
+    a.qwin[row0 + e] = q * c2;
+    qv[e / kD][e % kD] = q;
+  }
+  __syncthreads();
+  if (k.rotation == TQ_ROT_DENSE) {
+    matvec_cols<G>(t.rotT, qv, part, qr);
+  } else {
+    hadamard_lds<G>(qv, t.rot, nullptr);
+    for (int e = tid; e < G * kD; e += kSmallThreads) qr[e / kD][e % kD] = qv[e / kD][e % kD];
     __syncthreads();
   }
-  qr[j] = y;
-  a.qs[row + j] = y * c2;
+  for (int e = tid; e < G * kD; e += kSmallThreads) a.qs[row0 + e] = qr[e / kD][e % kD] * c2;
   if (!qjl) return;
-  __syncthreads();
-  float p = 0.0f;
-#pragma unroll 8
-  for (int i = 0; i < kD; ++i) p = fmaf(t.ST[i * kD + j], qr[i], p);
-  const float ps = p * k.qjl_scale * c2;
-  a.ps[row + j] = ps;
-  const float w = wave_sum(ps);
-  if ((j & 63) == 0) red[j >> 6] = w;
-  __syncthreads();
-  if (j == 0) a.psum[static_cast<int64_t>(b) * k.Hq + g] = red[0] + red[1];
+  matvec_cols<G>(t.ST, qr, part, qv);  // qv <- S q_rot
+  const float sc = k.qjl_scale * c2;
+  const int lane = tid & 63, w = tid >> 6;
+  for (int g = w; g < G; g += 4) {
+    float s2 = 0.0f;
+    for (int i = lane; i < kD; i += 64) {
+      const float ps = qv[g][i] * sc;
+      a.ps[row0 + g * kD + i] = ps;
+      s2 += ps;
+    }
+    s2 = wave_sum(s2);
+    if (lane == 0) a.psum[static_cast<int64_t>(b) * k.Hq + h * G + g] = s2;
+  }
 }
 
 // ---------------------------------------------------------------- scan
@@ -252,99 +313,183 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(DecodeArgs a, DevTab
 }
 
 // ---------------------------------------------------------------- merge
-__global__ __launch_bounds__(kD) void merge_kernel(DecodeArgs a, DevTables t, KParams k) {
-  __shared__ float accr[kD];
-  __shared__ float ls[kMaxWindow];
-  __shared__ float qw[kD];
-  __shared__ float red[2];
-  const int j = threadIdx.x, g = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
-  const int gq = h * k.G + g;
+// One work-group per (b, kv head) for its G query heads: the window K/V rows,
+// the split partials and Pi are each read once, with many loads in flight.
+template <int G>
+__global__ __launch_bounds__(kSmallThreads) void merge_kernel(DecodeArgs a, DevTables t, KParams k) {
+  __shared__ float accr[G][kD], ow[G][kD], qw[G][kD], part[8][G][kD];
+  __shared__ float ls[G][kMaxWindow];
+  __shared__ float sM[G], sL[8][G], sM2[G], sLw[G];
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int c4 = (tid & 31) * 4, q8 = tid >> 5;
+  const int h = blockIdx.x, b = blockIdx.y;
   const int T = a.seq_lens[b];
   const int nwin = T < k.W ? T : k.W;
-  const int64_t qrow = (static_cast<int64_t>(b) * k.Hq + gq) * kD;
-  // 1. combine split partials (fixed order)
-  float M = -INFINITY;
-  for (int s = 0; s < a.splits; ++s) {
-    const int64_t pi = ((static_cast<int64_t>(b) * k.Hkv + h) * a.splits + s) * k.G + g;
-    if (a.pl[pi] > 0.0f) M = fmaxf(M, a.pm[pi]);
-  }
-  float acc = 0.0f, L = 0.0f;
-  for (int s = 0; s < a.splits; ++s) {
-    const int64_t pi = ((static_cast<int64_t>(b) * k.Hkv + h) * a.splits + s) * k.G + g;
-    const float lv = a.pl[pi];
-    if (lv > 0.0f) {
-      const float f = exp2f(a.pm[pi] - M);
-      L = fmaf(f, lv, L);
-      acc = fmaf(f, a.pacc[pi * kD + j], acc);
-    }
-  }
-  accr[j] = acc;
-  qw[j] = a.qwin[qrow + j];
-  __syncthreads();
-  // 2. window scores (original basis, FP16 keys), log2 units
+  const int64_t row0 = (static_cast<int64_t>(b) * k.Hq + static_cast<int64_t>(h) * G) * kD;
   const int64_t bh = static_cast<int64_t>(b) * k.Hkv + h;
-  float lmax = -INFINITY;
-  for (int tk = j; tk < nwin; tk += kD) {
-    const uint4* kr = reinterpret_cast<const uint4*>(a.k_win + (bh * k.W + tk) * kD);
-    float s = 0.0f;
-#pragma unroll 4
-    for (int i = 0; i < kD / 8; ++i) {
-      const uint4 v = kr[i];
-      const uint32_t u[4] = {v.x, v.y, v.z, v.w};
+  for (int e = tid; e < G * kD; e += kSmallThreads) qw[e / kD][e % kD] = a.qwin[row0 + e];
+  // 1. combine the split partials: thread (c4, q8) takes query g = q8 % G and
+  //    splits s = sub, sub + nsub, ... (sub = q8 / G); fixed-order sums.
+  {
+    constexpr int nsub = 8 / G;
+    const int g = q8 % G, sub = q8 / G;
+    float M = -INFINITY;
+    for (int s0 = 0; s0 < a.splits; s0 += 16) {
+      float lv[16], mv[16];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        s = fmaf(qw[8 * i + 2 * e], half_bits_to_float(static_cast<uint16_t>(u[e] & 0xffffu)), s);
-        s = fmaf(qw[8 * i + 2 * e + 1], half_bits_to_float(static_cast<uint16_t>(u[e] >> 16)), s);
+      for (int u = 0; u < 16; ++u) {
+        const int64_t pi = (bh * a.splits + (s0 + u < a.splits ? s0 + u : s0)) * G + g;
+        lv[u] = s0 + u < a.splits ? a.pl[pi] : 0.0f;
+        mv[u] = a.pm[pi];
+      }
+#pragma unroll
+      for (int u = 0; u < 16; ++u)
+        if (lv[u] > 0.0f) M = fmaxf(M, mv[u]);
+    }
+    float4 acc = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+    float L = 0.0f;
+    // batches of 8 splits: all loads of a batch are issued before use; an
+    // empty split (l = 0) gets weight 0 and its accumulator is not used
+    for (int s0 = sub; s0 < a.splits; s0 += 8 * nsub) {
+      float4 v[8];
+      float lv[8], mv[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int s = s0 + u * nsub;
+        const int64_t pi = (bh * a.splits + (s < a.splits ? s : s0)) * G + g;
+        v[u] = *reinterpret_cast<const float4*>(a.pacc + pi * kD + c4);
+        lv[u] = s < a.splits ? a.pl[pi] : 0.0f;
+        mv[u] = a.pm[pi];
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        if (lv[u] > 0.0f) {
+          const float f = exp2f(mv[u] - M);
+          L = fmaf(f, lv[u], L);
+          acc.x = fmaf(f, v[u].x, acc.x);
+          acc.y = fmaf(f, v[u].y, acc.y);
+          acc.z = fmaf(f, v[u].z, acc.z);
+          acc.w = fmaf(f, v[u].w, acc.w);
+        }
       }
     }
-    ls[tk] = s;
-    lmax = fmaxf(lmax, s);
-    if (a.dbg_logits) {
+    *reinterpret_cast<float4*>(&part[sub][g][c4]) = acc;
+    if ((tid & 31) == 0) {
+      sL[sub][g] = L;
+      if (sub == 0) sM[g] = M;
+    }
+  }
+  __syncthreads();
+  for (int e = tid; e < G * kD; e += kSmallThreads) {
+    const int g = e / kD, i = e % kD;
+    float v = part[0][g][i];
+#pragma unroll
+    for (int r = 1; r < 8 / G; ++r) v += part[r][g][i];
+    accr[g][i] = v;
+  }
+  // 2. window scores (original basis, FP16 keys, log2 units): two threads per
+  //    token, 64 coordinates each.
+  for (int e = tid; e < 2 * nwin; e += kSmallThreads) {
+    const int tk = e >> 1, half = e & 1;
+    const uint4* kr = reinterpret_cast<const uint4*>(a.k_win + (bh * k.W + tk) * kD + 64 * half);
+    uint4 kv[8];
+#pragma unroll
+    for (int c = 0; c < 8; ++c) kv[c] = kr[c];
+    float sg[G];
+#pragma unroll
+    for (int g = 0; g < G; ++g) sg[g] = 0.0f;
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      const uint32_t u4v[4] = {kv[c].x, kv[c].y, kv[c].z, kv[c].w};
+#pragma unroll
+      for (int e2 = 0; e2 < 4; ++e2) {
+        const int i = 64 * half + 8 * c + 2 * e2;
+        const float k0 = half_bits_to_float(static_cast<uint16_t>(u4v[e2] & 0xffffu));
+        const float k1 = half_bits_to_float(static_cast<uint16_t>(u4v[e2] >> 16));
+#pragma unroll
+        for (int g = 0; g < G; ++g) sg[g] = fmaf(qw[g][i + 1], k1, fmaf(qw[g][i], k0, sg[g]));
+      }
+    }
+#pragma unroll
+    for (int g = 0; g < G; ++g) sg[g] += __shfl_xor(sg[g], 1, 64);
+    if (half == 0) {
       // slot tk holds the largest position p < T with p = tk (mod W)
       const int pos = tk + k.W * ((T - 1 - tk) / k.W);
-      a.dbg_logits[(static_cast<int64_t>(b) * k.Hq + gq) * a.logits_stride + pos] = s * kLn2;
-    }
-  }
-  lmax = wave_max(lmax);
-  if ((j & 63) == 0) red[j >> 6] = lmax;
-  __syncthreads();
-  const float M2 = fmaxf(M, fmaxf(red[0], red[1]));
-  __syncthreads();
-  const float corr = (M == -INFINITY) ? 0.0f : exp2f(M - M2);
-  float lw = 0.0f;
-  for (int tk = j; tk < nwin; tk += kD) {
-    const float w = exp2f(ls[tk] - M2);
-    ls[tk] = w;
-    lw += w;
-  }
-  lw = wave_sum(lw);
-  if ((j & 63) == 0) red[j >> 6] = lw;
-  __syncthreads();
-  const float Ltot = fmaf(L, corr, red[0] + red[1]);
-  float accw = 0.0f;
-  for (int tk = 0; tk < nwin; ++tk)
-    accw = fmaf(ls[tk], half_bits_to_float(a.v_win[(bh * k.W + tk) * kD + j]), accw);
-  // 3. one inverse rotation of the rotated accumulator
-  float o;
-  if (k.rotation == TQ_ROT_DENSE) {
-    o = 0.0f;
-#pragma unroll 8
-    for (int i = 0; i < kD; ++i) o = fmaf(t.rot[i * kD + j], accr[i], o);
-  } else {
-    float val = accr[j];
 #pragma unroll
-    for (int s = 1; s < 64; s <<= 1) {
-      const float ov = __shfl_xor(val, s, 64);
-      val = (j & s) ? (ov - val) : (val + ov);
+      for (int g = 0; g < G; ++g) {
+        ls[g][tk] = sg[g];
+        if (a.dbg_logits) a.dbg_logits[(static_cast<int64_t>(b) * k.Hq + h * G + g) * a.logits_stride + pos] = sg[g] * kLn2;
+      }
     }
-    __syncthreads();
-    accr[j] = val;
-    __syncthreads();
-    const float a0 = accr[j], b0 = accr[j ^ 64];
-    o = ((j & 64) ? (b0 - a0) : (a0 + b0)) * 0.08838834764831845f * t.rot[j];
   }
-  const float res = Ltot > 0.0f ? fmaf(o, corr, accw) / Ltot : 0.0f;
-  a.out[qrow + j] = res;
+  __syncthreads();
+  // 3. per query head (one wave each): window max, weights, their sum
+  for (int g = wv; g < G; g += kSmallThreads / 64) {
+    float m = sM[g];
+    for (int tk = lane; tk < nwin; tk += 64) m = fmaxf(m, ls[g][tk]);
+    m = wave_max(m);
+    float lw = 0.0f;
+    for (int tk = lane; tk < nwin; tk += 64) {
+      const float w = exp2f(ls[g][tk] - m);
+      ls[g][tk] = w;
+      lw += w;
+    }
+    lw = wave_sum(lw);
+    if (lane == 0) {
+      sM2[g] = m;
+      sLw[g] = lw;
+    }
+  }
+  __syncthreads();
+  // 4. weighted FP16 window values: thread (c4, q8) takes tokens q8, q8+8, ...
+  {
+    float4 acc[G];
+#pragma unroll
+    for (int g = 0; g < G; ++g) acc[g] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+    const uint16_t* vb = a.v_win + bh * k.W * kD + c4;
+#pragma unroll 8
+    for (int tk = q8; tk < nwin; tk += 8) {
+      const uint2 u = *reinterpret_cast<const uint2*>(vb + static_cast<int64_t>(tk) * kD);
+      const float v0 = half_bits_to_float(static_cast<uint16_t>(u.x & 0xffffu));
+      const float v1 = half_bits_to_float(static_cast<uint16_t>(u.x >> 16));
+      const float v2 = half_bits_to_float(static_cast<uint16_t>(u.y & 0xffffu));
+      const float v3 = half_bits_to_float(static_cast<uint16_t>(u.y >> 16));
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+        const float w = ls[g][tk];
+        acc[g].x = fmaf(w, v0, acc[g].x);
+        acc[g].y = fmaf(w, v1, acc[g].y);
+        acc[g].z = fmaf(w, v2, acc[g].z);
+        acc[g].w = fmaf(w, v3, acc[g].w);
+      }
+    }
+#pragma unroll
+    for (int g = 0; g < G; ++g) *reinterpret_cast<float4*>(&part[q8][g][c4]) = acc[g];
+  }
+  __syncthreads();
+  for (int e = tid; e < G * kD; e += kSmallThreads) {
+    const int g = e / kD, i = e % kD;
+    float v = part[0][g][i];
+#pragma unroll
+    for (int r = 1; r < 8; ++r) v += part[r][g][i];
+    ow[g][i] = v;
+  }
+  __syncthreads();
+  // 5. one inverse rotation per query head: o = Pi^T acc_rot
+  if (k.rotation == TQ_ROT_DENSE) {
+    matvec_cols<G>(t.rot, accr, part, accr);
+  } else {
+    hadamard_lds<G>(accr, nullptr, t.rot);
+  }
+  for (int e = tid; e < G * kD; e += kSmallThreads) {
+    const int g = e / kD, i = e % kD;
+    const float M = sM[g], M2 = sM2[g];
+    const float corr = (M == -INFINITY) ? 0.0f : exp2f(M - M2);
+    float L = 0.0f;
+    for (int r = 0; r < 8 / G; ++r) L += sL[r][g];
+    const float Ltot = fmaf(L, corr, sLw[g]);
+    a.out[row0 + e] = Ltot > 0.0f ? fmaf(accr[g][i], corr, ow[g][i]) / Ltot : 0.0f;
+  }
 }
 
 template <int G, int BK, int BV>
@@ -378,7 +523,14 @@ int launch_decode(const tq_ctx* c, const DecodeArgs& a, void* stream) {
   hipStream_t s = static_cast<hipStream_t>(stream);
   const KParams k = make_kparams(c);
   const int qjl = c->p.key_qjl;
-  hipLaunchKernelGGL(prep_kernel, dim3(k.Hq, a.batch), dim3(kD), 0, s, a, c->t, k, qjl);
+  const dim3 ghb(k.Hkv, a.batch);
+  switch (k.G) {
+    case 1: hipLaunchKernelGGL(prep_kernel<1>, ghb, dim3(kSmallThreads), 0, s, a, c->t, k, qjl); break;
+    case 2: hipLaunchKernelGGL(prep_kernel<2>, ghb, dim3(kSmallThreads), 0, s, a, c->t, k, qjl); break;
+    case 4: hipLaunchKernelGGL(prep_kernel<4>, ghb, dim3(kSmallThreads), 0, s, a, c->t, k, qjl); break;
+    case 8: hipLaunchKernelGGL(prep_kernel<8>, ghb, dim3(kSmallThreads), 0, s, a, c->t, k, qjl); break;
+    default: return 1;
+  }
   if (hipGetLastError() != hipSuccess) return 1;
   dim3 grid(a.splits, k.Hkv, a.batch);
   const int bk = c->p.key_bits, bv = c->p.value_bits;
@@ -397,7 +549,13 @@ int launch_decode(const tq_ctx* c, const DecodeArgs& a, void* stream) {
     return 1;
   }
   if (ev0 && hipEventRecord(static_cast<hipEvent_t>(profile_slot(c, 1)), s) != hipSuccess) return 1;
-  hipLaunchKernelGGL(merge_kernel, dim3(k.G, k.Hkv, a.batch), dim3(kD), 0, s, a, c->t, k);
+  switch (k.G) {
+    case 1: hipLaunchKernelGGL(merge_kernel<1>, ghb, dim3(kSmallThreads), 0, s, a, c->t, k); break;
+    case 2: hipLaunchKernelGGL(merge_kernel<2>, ghb, dim3(kSmallThreads), 0, s, a, c->t, k); break;
+    case 4: hipLaunchKernelGGL(merge_kernel<4>, ghb, dim3(kSmallThreads), 0, s, a, c->t, k); break;
+    case 8: hipLaunchKernelGGL(merge_kernel<8>, ghb, dim3(kSmallThreads), 0, s, a, c->t, k); break;
+    default: return 1;
+  }
   return hipGetLastError() == hipSuccess ? 0 : 1;
 }
 

@@ -49,9 +49,10 @@ __device__ inline CoreParams make_core(const Codebooks& cb, bool key, int bits, 
 }
 
 // Rotate, quantise and (for keys) sketch the residual of the tile in LDS.
-// nv = number of live vectors (the rest are zero and produce zero records).
+// Only vectors v0 <= v < v1 of the tile are encoded (the others are not
+// written by the callers).
 template <bool HAD>
-__device__ void encode_core(Smem& sm, const DevTables& t, const CoreParams& cp, int nv) {
+__device__ void encode_core(Smem& sm, const DevTables& t, const CoreParams& cp, int v0, int v1) {
   const int tid = threadIdx.x;
   const int nb = (1 << cp.bits) - 1;
   if (tid < 16) {
@@ -100,9 +101,9 @@ __device__ void encode_core(Smem& sm, const DevTables& t, const CoreParams& cp, 
 #pragma unroll
       for (int j = 0; j < kD / 2; ++j) pr[j] = t.rotT[(hp * (kD / 2) + j) * kD + tid];
 #pragma unroll 1
-      for (int v = 0; v < kTile; ++v) {
+      for (int v = v0; v < v1; ++v) {
         float s = hp ? sm.rs[v][tid] : 0.0f;
-        if (v < nv) {
+        {
           const float4* xr = reinterpret_cast<const float4*>(sm.xs[v]) + hp * (kD / 8);
 #pragma unroll
           for (int j4 = 0; j4 < kD / 8; ++j4) {
@@ -122,7 +123,7 @@ __device__ void encode_core(Smem& sm, const DevTables& t, const CoreParams& cp, 
   } else {
     const float eps = t.rot[tid];
     // strides 1..32 inside the wave, stride 64 through LDS
-    for (int v = 0; v < kTile; ++v) {
+    for (int v = v0; v < v1; ++v) {
       float val = sm.xs[v][tid] * eps;
 #pragma unroll
       for (int s = 1; s < 64; s <<= 1) {
@@ -141,7 +142,8 @@ __device__ void encode_core(Smem& sm, const DevTables& t, const CoreParams& cp, 
     }
     __syncthreads();
 #pragma unroll
-    for (int v = 0; v < kTile; ++v) finish(v, acc[v]);
+    for (int v = 0; v < kTile; ++v)
+      if (v >= v0 && v < v1) finish(v, acc[v]);
   }
   if (!cp.qjl) return;
   __syncthreads();
@@ -165,7 +167,7 @@ __device__ void encode_core(Smem& sm, const DevTables& t, const CoreParams& cp, 
 #pragma unroll
     for (int j = 0; j < kD / 2; ++j) sr[j] = t.ST[(hp * (kD / 2) + j) * kD + tid];
 #pragma unroll 1
-    for (int v = 0; v < kTile; ++v) {
+    for (int v = v0; v < v1; ++v) {
       float z = hp ? sm.xs[v][tid] : 0.0f;
       const float4* rr = reinterpret_cast<const float4*>(sm.rs[v]) + hp * (kD / 8);
 #pragma unroll
@@ -211,7 +213,7 @@ __global__ __launch_bounds__(kThreads) void encode_flat_kernel(EncodeArgs a, Dev
     sm.xs[v][tid] = v < nv ? load_any(a.x, (n0 + v) * a.row_stride + tid, dtype) : 0.0f;
   __syncthreads();
   const CoreParams cp = make_core(cb, kind == TQ_KIND_KEY, bits, qjl != 0);
-  encode_core<HAD>(sm, t, cp, nv);
+  encode_core<HAD>(sm, t, cp, 0, nv);
   __syncthreads();
   if (tid < nv) {
     a.norms[n0 + tid] = sm.n32[tid];
@@ -304,9 +306,9 @@ __global__ __launch_bounds__(kThreads) void append_encode_kernel(AppendArgs a, D
     __syncthreads();
     const bool key = kv == 0;
     const CoreParams cp = make_core(cb, key, key ? L.bK : L.bV, key && L.qjl);
-    encode_core<HAD>(sm, t, cp, kTile);
-    __syncthreads();
     const int vlo = lo - gpos, vhi = hi - gpos;
+    encode_core<HAD>(sm, t, cp, vlo, vhi);
+    __syncthreads();
     if (key) {
       float* kn = reinterpret_cast<float*>(hb + L.k_norm);
       if (tid >= vlo && tid < vhi) {
