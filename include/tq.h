@@ -165,7 +165,10 @@ TQ_API int64_t tq_decode_workspace_bytes(const tq_ctx* ctx, int batch, int max_p
  *   out: [batch][H_q][d] f32, softmax(q.k * sm_scale) weighted sum of values
  *   over all seq_lens[b] tokens (zeros for an empty sequence);
  *   workspace: >= tq_decode_workspace_bytes(ctx, batch, max_pages, pages_per_split);
- *   pages_per_split: compressed pages per work-group (0 = chosen by the library);
+ *   pages_per_split: compressed pages per work-group; 0 lets the library choose
+ *   from the batch, the block-table width and how many scan work-groups the
+ *   device holds at once (the fewest rounds of resident work-groups, each
+ *   work-group as long as possible);
  *   dbg_logits: NULL, or [batch][H_q][logits_stride] f32 receiving each token's
  *   logit q.k*sm_scale at its position index (for tests). */
 TQ_API int tq_decode_attn(const tq_ctx* ctx, const void* q, int q_dtype, const uint8_t* page_pool, int64_t num_pages,

@@ -493,28 +493,51 @@ __global__ __launch_bounds__(kSmallThreads) void merge_kernel(DecodeArgs a, DevT
 }
 
 template <int G, int BK, int BV>
-void launch_scan_bits(bool qjl, dim3 grid, hipStream_t s, const DecodeArgs& a, const DevTables& t, const Codebooks& cb,
-                      const KParams& k) {
-  if (qjl)
-    hipLaunchKernelGGL((scan_kernel<G, BK, BV, true>), grid, dim3(kScanThreads), 0, s, a, t, cb, k);
-  else
-    hipLaunchKernelGGL((scan_kernel<G, BK, BV, false>), grid, dim3(kScanThreads), 0, s, a, t, cb, k);
+const void* pick_scan_bits(bool qjl) {
+  return qjl ? reinterpret_cast<const void*>(&scan_kernel<G, BK, BV, true>)
+             : reinterpret_cast<const void*>(&scan_kernel<G, BK, BV, false>);
 }
 
 template <int G, int BK>
-void launch_scan_bv(int bv, bool qjl, dim3 grid, hipStream_t s, const DecodeArgs& a, const DevTables& t,
-                    const Codebooks& cb, const KParams& k) {
-  if (bv == 2) launch_scan_bits<G, BK, 2>(qjl, grid, s, a, t, cb, k);
-  else if (bv == 3) launch_scan_bits<G, BK, 3>(qjl, grid, s, a, t, cb, k);
-  else launch_scan_bits<G, BK, 4>(qjl, grid, s, a, t, cb, k);
+const void* pick_scan_bv(int bv, bool qjl) {
+  if (bv == 2) return pick_scan_bits<G, BK, 2>(qjl);
+  if (bv == 3) return pick_scan_bits<G, BK, 3>(qjl);
+  return pick_scan_bits<G, BK, 4>(qjl);
 }
 
 template <int G>
-void launch_scan_g(int bk, int bv, bool qjl, dim3 grid, hipStream_t s, const DecodeArgs& a, const DevTables& t,
-                   const Codebooks& cb, const KParams& k) {
-  if (bk == 2) launch_scan_bv<G, 2>(bv, qjl, grid, s, a, t, cb, k);
-  else if (bk == 3) launch_scan_bv<G, 3>(bv, qjl, grid, s, a, t, cb, k);
-  else launch_scan_bv<G, 4>(bv, qjl, grid, s, a, t, cb, k);
+const void* pick_scan_g(int bk, int bv, bool qjl) {
+  if (bk == 2) return pick_scan_bv<G, 2>(bv, qjl);
+  if (bk == 3) return pick_scan_bv<G, 3>(bv, qjl);
+  return pick_scan_bv<G, 4>(bv, qjl);
+}
+
+}  // namespace
+
+const void* scan_valu_kernel_ptr(const tq_ctx* c) {
+  const int G = c->p.num_q_heads / c->p.num_kv_heads, bk = c->p.key_bits, bv = c->p.value_bits;
+  const bool qjl = c->p.key_qjl != 0;
+  switch (G) {
+    case 1: return pick_scan_g<1>(bk, bv, qjl);
+    case 2: return pick_scan_g<2>(bk, bv, qjl);
+    case 4: return pick_scan_g<4>(bk, bv, qjl);
+    case 8: return pick_scan_g<8>(bk, bv, qjl);
+    default: return nullptr;
+  }
+}
+
+namespace {
+
+int launch_scan_valu(const tq_ctx* c, const DecodeArgs& a, const KParams& k, hipStream_t s) {
+  const void* f = scan_valu_kernel_ptr(c);
+  if (!f) return 1;
+  DecodeArgs aa = a;
+  DevTables tt = c->t;
+  Codebooks cc = c->cb;
+  KParams kk = k;
+  void* args[] = {&aa, &tt, &cc, &kk};
+  const dim3 grid(a.splits, k.Hkv, a.batch);
+  return hipLaunchKernel(f, grid, dim3(kScanThreads), args, 0, s) == hipSuccess ? 0 : 1;
 }
 
 }  // namespace
@@ -532,22 +555,10 @@ int launch_decode(const tq_ctx* c, const DecodeArgs& a, void* stream) {
     default: return 1;
   }
   if (hipGetLastError() != hipSuccess) return 1;
-  dim3 grid(a.splits, k.Hkv, a.batch);
-  const int bk = c->p.key_bits, bv = c->p.value_bits;
   void* ev0 = profile_slot(c, 0);
   if (ev0 && hipEventRecord(static_cast<hipEvent_t>(ev0), s) != hipSuccess) return 1;
-  if (c->p.flags & TQ_FLAG_VALU_SCAN) {
-    switch (k.G) {
-      case 1: launch_scan_g<1>(bk, bv, qjl, grid, s, a, c->t, c->cb, k); break;
-      case 2: launch_scan_g<2>(bk, bv, qjl, grid, s, a, c->t, c->cb, k); break;
-      case 4: launch_scan_g<4>(bk, bv, qjl, grid, s, a, c->t, c->cb, k); break;
-      case 8: launch_scan_g<8>(bk, bv, qjl, grid, s, a, c->t, c->cb, k); break;
-      default: return 1;
-    }
-    if (hipGetLastError() != hipSuccess) return 1;
-  } else if (launch_scan_mfma(c, a, k, stream) != 0) {
-    return 1;
-  }
+  const int rc = (c->p.flags & TQ_FLAG_VALU_SCAN) ? launch_scan_valu(c, a, k, s) : launch_scan_mfma(c, a, k, stream);
+  if (rc != 0) return 1;
   if (ev0 && hipEventRecord(static_cast<hipEvent_t>(profile_slot(c, 1)), s) != hipSuccess) return 1;
   switch (k.G) {
     case 1: hipLaunchKernelGGL(merge_kernel<1>, ghb, dim3(kSmallThreads), 0, s, a, c->t, k); break;

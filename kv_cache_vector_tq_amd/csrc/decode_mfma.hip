@@ -87,10 +87,13 @@ __device__ inline uint32_t pack_part(float x0, float x1, int part) {
 
 // Lookup tables turning packed codes into fp16 MFMA operands.  A "pair"
 // table maps the 2B bits of two consecutive codes to their two fp16 centroids
-// (one word).  Tables of 16 or 64 words sit in distinct LDS banks, so random
-// lookups by the 64 lanes only broadcast or hit different banks; the 256-word
-// table of 4-bit codes is stored in 32 copies (word e of copy c at 32e + c)
-// and lane l reads copy l % 32, which keeps its lookups conflict-free too.
+// (one word).  The LDS serves a 64-lane read as two halves of 32 lanes over
+// 32 four-byte banks: a 16-entry table is conflict-free (equal entries
+// broadcast) and a 64-entry one costs at most two passes, which measured
+// cheaper than replicating it (the replicated address takes one more VALU
+// op).  The 256-entry table of 4-bit codes is stored in 32 copies (word e of
+// copy c at 32e + c) and lane l reads copy l % 32, so every half-wave touches
+// 32 distinct banks whatever the codes are.
 template <int B>
 struct PairLut {
   static constexpr int kEntries = 1 << (2 * B);
@@ -459,45 +462,49 @@ __global__ __launch_bounds__(kScanThreads) void scan_mfma_kernel(DecodeArgs a, D
 }
 
 template <int G, int BK, int BV>
-void launch_bits(bool qjl, dim3 grid, hipStream_t s, const DecodeArgs& a, const DevTables& t, const Codebooks& cb,
-                 const KParams& k) {
-  if (qjl)
-    hipLaunchKernelGGL((scan_mfma_kernel<G, BK, BV, true>), grid, dim3(kScanThreads), 0, s, a, t, cb, k);
-  else
-    hipLaunchKernelGGL((scan_mfma_kernel<G, BK, BV, false>), grid, dim3(kScanThreads), 0, s, a, t, cb, k);
+const void* pick_bits(bool qjl) {
+  return qjl ? reinterpret_cast<const void*>(&scan_mfma_kernel<G, BK, BV, true>)
+             : reinterpret_cast<const void*>(&scan_mfma_kernel<G, BK, BV, false>);
 }
 
 template <int G, int BK>
-void launch_bv(int bv, bool qjl, dim3 grid, hipStream_t s, const DecodeArgs& a, const DevTables& t,
-               const Codebooks& cb, const KParams& k) {
-  if (bv == 2) launch_bits<G, BK, 2>(qjl, grid, s, a, t, cb, k);
-  else if (bv == 3) launch_bits<G, BK, 3>(qjl, grid, s, a, t, cb, k);
-  else launch_bits<G, BK, 4>(qjl, grid, s, a, t, cb, k);
+const void* pick_bv(int bv, bool qjl) {
+  if (bv == 2) return pick_bits<G, BK, 2>(qjl);
+  if (bv == 3) return pick_bits<G, BK, 3>(qjl);
+  return pick_bits<G, BK, 4>(qjl);
 }
 
 template <int G>
-void launch_g(int bk, int bv, bool qjl, dim3 grid, hipStream_t s, const DecodeArgs& a, const DevTables& t,
-              const Codebooks& cb, const KParams& k) {
-  if (bk == 2) launch_bv<G, 2>(bv, qjl, grid, s, a, t, cb, k);
-  else if (bk == 3) launch_bv<G, 3>(bv, qjl, grid, s, a, t, cb, k);
-  else launch_bv<G, 4>(bv, qjl, grid, s, a, t, cb, k);
+const void* pick_g(int bk, int bv, bool qjl) {
+  if (bk == 2) return pick_bv<G, 2>(bv, qjl);
+  if (bk == 3) return pick_bv<G, 3>(bv, qjl);
+  return pick_bv<G, 4>(bv, qjl);
 }
 
 }  // namespace
 
-int launch_scan_mfma(const tq_ctx* c, const DecodeArgs& a, const KParams& k, void* stream) {
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  dim3 grid(a.splits, k.Hkv, a.batch);
-  const int bk = c->p.key_bits, bv = c->p.value_bits;
+const void* scan_mfma_kernel_ptr(const tq_ctx* c) {
+  const int G = c->p.num_q_heads / c->p.num_kv_heads, bk = c->p.key_bits, bv = c->p.value_bits;
   const bool qjl = c->p.key_qjl != 0;
-  switch (k.G) {
-    case 1: launch_g<1>(bk, bv, qjl, grid, s, a, c->t, c->cb, k); break;
-    case 2: launch_g<2>(bk, bv, qjl, grid, s, a, c->t, c->cb, k); break;
-    case 4: launch_g<4>(bk, bv, qjl, grid, s, a, c->t, c->cb, k); break;
-    case 8: launch_g<8>(bk, bv, qjl, grid, s, a, c->t, c->cb, k); break;
-    default: return 1;
+  switch (G) {
+    case 1: return pick_g<1>(bk, bv, qjl);
+    case 2: return pick_g<2>(bk, bv, qjl);
+    case 4: return pick_g<4>(bk, bv, qjl);
+    case 8: return pick_g<8>(bk, bv, qjl);
+    default: return nullptr;
   }
-  return hipGetLastError() == hipSuccess ? 0 : 1;
+}
+
+int launch_scan_mfma(const tq_ctx* c, const DecodeArgs& a, const KParams& k, void* stream) {
+  const void* f = scan_mfma_kernel_ptr(c);
+  if (!f) return 1;
+  DecodeArgs aa = a;
+  DevTables tt = c->t;
+  Codebooks cc = c->cb;
+  KParams kk = k;
+  void* args[] = {&aa, &tt, &cc, &kk};
+  const dim3 grid(a.splits, k.Hkv, a.batch);
+  return hipLaunchKernel(f, grid, dim3(kScanThreads), args, 0, static_cast<hipStream_t>(stream)) == hipSuccess ? 0 : 1;
 }
 
 }  // namespace tq

@@ -7,6 +7,7 @@
 #include <new>
 #include <vector>
 
+#include "decode_common.h"
 #include "tq_internal.h"
 
 namespace {
@@ -38,15 +39,28 @@ void transpose(const float* a, float* at, int d) {
     for (int j = 0; j < d; ++j) at[j * d + i] = a[i * d + j];
 }
 
-int decode_splits(int batch, int hkv, int max_pages, int pages_per_split, int* pps_out) {
+// Pages per split-K work-group.  Automatic choice (pages_per_split = 0): the
+// split count s minimising rounds(s) * (ceil(max_pages / s) + 2), where
+// rounds(s) is how many waves of `slots` resident work-groups the
+// batch * hkv * s work-groups take and the 2 pages stand for a work-group's
+// fixed cost (tables, pipeline fill, final merge); ties go to the smaller s.
+int decode_splits(int batch, int hkv, int max_pages, int pages_per_split, int slots, int* pps_out) {
   int pps = pages_per_split;
   if (pps <= 0) {
-    // aim for >= 2048 work-groups over the whole batch, 1..max_pages pages each
     const long long bh = static_cast<long long>(batch) * hkv;
-    long long want = (2048 + bh - 1) / bh;
-    if (want < 1) want = 1;
-    pps = static_cast<int>((max_pages + want - 1) / want);
-    if (pps < 1) pps = 1;
+    const long long sl = slots > 0 ? slots : 1;
+    long long best = -1;
+    pps = max_pages > 0 ? max_pages : 1;
+    for (int s = 1; s <= (max_pages > 0 ? max_pages : 1); ++s) {
+      const long long per = (max_pages + s - 1) / s;
+      if (s > 1 && per == (max_pages + s - 2) / (s - 1)) continue;  // same pages per split as s - 1
+      const long long rounds = (bh * s + sl - 1) / sl;
+      const long long cost = rounds * (per + 2);
+      if (best < 0 || cost < best) {
+        best = cost;
+        pps = static_cast<int>(per);
+      }
+    }
   }
   if (pps > max_pages) pps = max_pages;
   if (pps < 1) pps = 1;
@@ -161,11 +175,17 @@ TQ_API int tq_codebook_init(tq_ctx** out, const tq_params* p, const double* rot_
             hipMemcpyAsync(base + 2 * mat, S.data(), mat, hipMemcpyHostToDevice, s) == hipSuccess &&
             hipMemcpyAsync(base + 3 * mat, ST.data(), mat, hipMemcpyHostToDevice, s) == hipSuccess &&
             hipMemsetAsync(base + 4 * mat, 0, 256, s) == hipSuccess && hipStreamSynchronize(s) == hipSuccess;
+  // resident scan work-groups per device, for the automatic split count
+  const void* kf = (p->flags & TQ_FLAG_VALU_SCAN) ? tq::scan_valu_kernel_ptr(c) : tq::scan_mfma_kernel_ptr(c);
+  int per_cu = 0, cus = 0;
+  ok = ok && kf && hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kf, tq::kScanThreads, 0) == hipSuccess &&
+       hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, c->device) == hipSuccess;
   if (!ok) {
     (void)hipFree(c->dmem);
     delete c;
     return TQ_ERR_HIP;
   }
+  c->scan_slots = (per_cu > 0 ? per_cu : 1) * (cus > 0 ? cus : 1);
   *out = c;
   return TQ_OK;
 }
@@ -257,7 +277,7 @@ TQ_API int tq_append_page(const tq_ctx* c, uint8_t* pool, int64_t num_pages, con
 
 TQ_API int64_t tq_decode_workspace_bytes(const tq_ctx* c, int batch, int max_pages, int pages_per_split) {
   if (!c || batch < 0 || max_pages < 0 || pages_per_split < 0) return TQ_ERR_INVALID_ARG;
-  const int splits = decode_splits(batch, c->p.num_kv_heads, max_pages, pages_per_split, nullptr);
+  const int splits = decode_splits(batch, c->p.num_kv_heads, max_pages, pages_per_split, c->scan_slots, nullptr);
   return static_cast<int64_t>(ws_layout(c->p, batch, splits).total);
 }
 
@@ -279,7 +299,7 @@ TQ_API int tq_decode_attn(const tq_ctx* c, const void* q, int q_dtype, const uin
       !aligned(q, q_dtype == TQ_DTYPE_F32 ? 16 : 8))
     return TQ_ERR_INVALID_ARG;
   int pps = 1;
-  const int splits = decode_splits(batch, c->p.num_kv_heads, max_pages, pages_per_split, &pps);
+  const int splits = decode_splits(batch, c->p.num_kv_heads, max_pages, pages_per_split, c->scan_slots, &pps);
   const WsLayout w = ws_layout(c->p, batch, splits);
   if (workspace_bytes < w.total) return TQ_ERR_WORKSPACE;
   char* base = static_cast<char*>(workspace);

@@ -124,6 +124,10 @@ struct Ctx;  // tq_ctx
 int launch_encode(const tq_ctx* ctx, int kind, int dtype, const EncodeArgs& a, void* stream);
 int launch_append(const tq_ctx* ctx, const AppendArgs& a, void* stream);
 int launch_decode(const tq_ctx* ctx, const DecodeArgs& a, void* stream);
+// The scan kernel a context's decode launches (MFMA or vector-ALU variant),
+// for occupancy queries; nullptr for an unsupported parameter set.
+const void* scan_mfma_kernel_ptr(const tq_ctx* ctx);
+const void* scan_valu_kernel_ptr(const tq_ctx* ctx);
 // Events to record around the scan kernel of this call (nullptr when not profiling).
 void* profile_slot(const tq_ctx* ctx, int which);
 
@@ -140,4 +144,7 @@ struct tq_ctx {
   tq::DevTables t;
   tq::Codebooks cb;
   std::vector<float> h_rot, h_S;
+  // scan work-groups resident at once on the device (compute units x
+  // work-groups per unit); the automatic split count fills one such round
+  int scan_slots = 0;
 };
