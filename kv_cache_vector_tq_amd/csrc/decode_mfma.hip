@@ -139,28 +139,41 @@ __device__ inline uint32_t key_slice(const uint32_t* w, int i) {
   else return bits_at<24>(w, 24 * i);
 }
 
-template <int BK, int BV>
-struct Chunk {
+// Per-chunk data, split so that key and value words can be loaded at
+// different times: a chunk's keys are scored one step before its values are
+// accumulated, and both are fetched one step ahead of use.
+template <int BK>
+struct KBuf {
   uint32_t kc[2][BK];  // key codes of tokens n / 16+n, coordinates 32kg .. 32kg+31
   uint32_t sg[2];      // their sign bits
-  float kn[2], rn[2], vn[2];
-  uint32_t vw[8];      // value words: coordinates 8n .. 8n+7, tokens 8kg .. 8kg+7
-  uint32_t vw2[8];     // next word when a 3-bit slice straddles two words
-  int ntok;            // live tokens (0 when the page id is invalid)
-  int pos0;            // position of the chunk's first token
+  float kn[2], rn[2];
+  float vn[2];         // value norms of tokens n / 16+n (used when scoring)
+};
+template <int BV>
+struct VBuf {
+  uint32_t vw[8];                   // value words: coordinates 8n .. 8n+7, tokens 8kg .. 8kg+7
+  uint32_t vw2[BV == 3 ? 8 : 1];    // next word when a 3-bit slice straddles two words
+};
+// wave-uniform chunk description (scalar registers)
+struct Meta {
+  __amdgpu_buffer_rsrc_t rs;
+  int s0;    // first token of the chunk inside its page
+  int gi;    // value group (32 tokens) inside the page
+  int ntok;  // live tokens (0 when the page id is invalid)
+  int pos0;  // position of the chunk's first token
 };
 
 // A row m of every MFMA holds query g = 2(m/4) + (m%2), part (m/2)%2 (0: fp16
 // hi, 1: remainder); the product's rows 4kg + r land in lane group kg, so a
 // lane sees query 2kg + i as rows i (hi) and i + 2 (remainder) and adds them.
 template <int G, int BK, int BV, bool QJL>
-__global__ __launch_bounds__(kScanThreads) void scan_mfma_kernel(DecodeArgs a, DevTables t, Codebooks cb,
+__global__ __launch_bounds__(kScanThreads, 4) void scan_mfma_kernel(DecodeArgs a, DevTables t, Codebooks cb,
                                                                  KParams k) {
   // one table when keys and values share a bit width (same codebook)
   __shared__ uint32_t lutV[PairLut<BV>::kWords];
   __shared__ uint32_t lutKown[BK == BV ? 1 : PairLut<BK>::kWords];
   __shared__ u2 lutN[16];
-  __shared__ float pv[kWaves][G][kChunk];  // softmax weights x value norms
+  __shared__ float pv[kWaves][2][G][kChunk];  // softmax weights x value norms, two chunks in flight
   __shared__ float wm[kWaves][G], wl[kWaves][G];
   __shared__ float red[G][kD];
   __shared__ float ck[16], cvv[16];
@@ -244,6 +257,8 @@ __global__ __launch_bounds__(kScanThreads) void scan_mfma_kernel(DecodeArgs a, D
 
   const int tot = (C < pe * k.P ? C : pe * k.P) - pb * k.P;
   const int nchunks = (tot + kChunk - 1) / kChunk;
+  // this wave takes chunks wave, wave + kWaves, ...
+  const int nmine = nchunks > wave ? (nchunks - wave + kWaves - 1) / kWaves : 0;
   // value words: the lane's 8 tokens of coordinate 8n + bl are bits [8*kg*BV, +8*BV)
   const int vbit = 8 * kg * BV;
   const int vw0 = vbit >> 5, vsh = vbit & 31;
@@ -256,69 +271,71 @@ __global__ __launch_bounds__(kScanThreads) void scan_mfma_kernel(DecodeArgs a, D
   const uint32_t o_vw = static_cast<uint32_t>((vw0 * kD + 8 * n) * 4);
   const uint32_t o_vw2 = static_cast<uint32_t>(((vtwo ? vw0 + 1 : vw0) * kD + 8 * n) * 4);
 
-  auto load = [&](int c, Chunk<BK, BV>& d) {
+  auto meta = [&](int i, Meta& m) {
+    const int c = wave + i * kWaves;
     const int tok0 = c * kChunk;
     const int pg = pb + tok0 / k.P;
-    const int gi = (tok0 % k.P) / kChunk;
+    m.gi = (tok0 % k.P) / kChunk;
+    m.s0 = m.gi * kChunk;
     const int rem = tot - tok0;
-    d.ntok = rem < kChunk ? rem : kChunk;
-    d.pos0 = pg * k.P + gi * kChunk;
+    m.pos0 = pg * k.P + m.s0;
     const int pid0 = a.block_table[static_cast<int64_t>(b) * a.max_pages + pg];
-    const bool bad = pid0 < 0 || pid0 >= a.num_pages;  // flagged, then page 0 is read and the chunk skipped
+    const bool bad = pid0 < 0 || pid0 >= a.num_pages;  // flagged, then page 0 is read and the chunk masked
     if (bad && l == 0) atomicOr(t.status, TQ_STATUS_BAD_PAGE);
-    d.ntok = bad ? 0 : d.ntok;
+    m.ntok = __builtin_amdgcn_readfirstlane(bad ? 0 : (rem < kChunk ? rem : kChunk));
     const int pid = __builtin_amdgcn_readfirstlane(bad ? 0 : pid0);
     const uint8_t* hb = a.pool + static_cast<int64_t>(pid) * k.page_bytes + kBodyOffset + h * k.head_bytes;
-    const __amdgpu_buffer_rsrc_t rs =
-        __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(hb), 0, static_cast<int>(k.head_bytes), kRsrcWord3);
-    const int s0 = gi * kChunk;
-    const int so_kn = static_cast<int>(k.k_norm) + 4 * s0;
-    d.kn[0] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, o_tok0, so_kn, 0));
-    d.kn[1] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, o_tok1, so_kn, 0));
+    m.rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(hb), 0, static_cast<int>(k.head_bytes), kRsrcWord3);
+  };
+  auto loadK = [&](const Meta& m, KBuf<BK>& d) {
+    const int so_kn = static_cast<int>(k.k_norm) + 4 * m.s0;
+    d.kn[0] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(m.rs, o_tok0, so_kn, 0));
+    d.kn[1] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(m.rs, o_tok1, so_kn, 0));
     if constexpr (QJL) {
-      const int so_rn = static_cast<int>(k.k_rnorm) + 4 * s0;
-      d.rn[0] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, o_tok0, so_rn, 0));
-      d.rn[1] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, o_tok1, so_rn, 0));
-      const int so_sg = static_cast<int>(k.k_signs) + 16 * s0;
-      d.sg[0] = __builtin_amdgcn_raw_buffer_load_b32(rs, o_sg0, so_sg, 0);
-      d.sg[1] = __builtin_amdgcn_raw_buffer_load_b32(rs, o_sg1, so_sg, 0);
+      const int so_rn = static_cast<int>(k.k_rnorm) + 4 * m.s0;
+      d.rn[0] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(m.rs, o_tok0, so_rn, 0));
+      d.rn[1] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(m.rs, o_tok1, so_rn, 0));
+      const int so_sg = static_cast<int>(k.k_signs) + 16 * m.s0;
+      d.sg[0] = __builtin_amdgcn_raw_buffer_load_b32(m.rs, o_sg0, so_sg, 0);
+      d.sg[1] = __builtin_amdgcn_raw_buffer_load_b32(m.rs, o_sg1, so_sg, 0);
     }
-    const int so_kc = static_cast<int>(k.k_codes) + 16 * BK * s0;
+    const int so_vn = static_cast<int>(k.v_norm) + 4 * m.s0;
+    d.vn[0] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(m.rs, o_tok0, so_vn, 0));
+    d.vn[1] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(m.rs, o_tok1, so_vn, 0));
+    const int so_kc = static_cast<int>(k.k_codes) + 16 * BK * m.s0;
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt) {
       const uint32_t o = tt ? o_kc1 : o_kc0;
       if constexpr (BK == 4) {
-        const u4 v = __builtin_amdgcn_raw_buffer_load_b128(rs, o, so_kc, 0);
+        const u4 v = __builtin_amdgcn_raw_buffer_load_b128(m.rs, o, so_kc, 0);
         d.kc[tt][0] = v.x; d.kc[tt][1] = v.y; d.kc[tt][2] = v.z; d.kc[tt][3] = v.w;
       } else if constexpr (BK == 3) {
-        const u3 v = __builtin_amdgcn_raw_buffer_load_b96(rs, o, so_kc, 0);
+        const u3 v = __builtin_amdgcn_raw_buffer_load_b96(m.rs, o, so_kc, 0);
         d.kc[tt][0] = v.x; d.kc[tt][1] = v.y; d.kc[tt][2] = v.z;
       } else {
-        const u2 v = __builtin_amdgcn_raw_buffer_load_b64(rs, o, so_kc, 0);
+        const u2 v = __builtin_amdgcn_raw_buffer_load_b64(m.rs, o, so_kc, 0);
         d.kc[tt][0] = v.x; d.kc[tt][1] = v.y;
       }
     }
-    const int so_vn = static_cast<int>(k.v_norm) + 4 * s0;
-    d.vn[0] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, o_tok0, so_vn, 0));
-    d.vn[1] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, o_tok1, so_vn, 0));
-    const int so_vw = static_cast<int>(k.v_codes) + gi * BV * kD * 4;
-    const u4 x0 = __builtin_amdgcn_raw_buffer_load_b128(rs, o_vw, so_vw, 0);
-    const u4 x1 = __builtin_amdgcn_raw_buffer_load_b128(rs, o_vw + 16u, so_vw, 0);
+  };
+  auto loadV = [&](const Meta& m, VBuf<BV>& d) {
+    const int so_vw = static_cast<int>(k.v_codes) + m.gi * BV * kD * 4;
+    const u4 x0 = __builtin_amdgcn_raw_buffer_load_b128(m.rs, o_vw, so_vw, 0);
+    const u4 x1 = __builtin_amdgcn_raw_buffer_load_b128(m.rs, o_vw + 16u, so_vw, 0);
     d.vw[0] = x0.x; d.vw[1] = x0.y; d.vw[2] = x0.z; d.vw[3] = x0.w;
     d.vw[4] = x1.x; d.vw[5] = x1.y; d.vw[6] = x1.z; d.vw[7] = x1.w;
     if constexpr (BV == 3) {
-      const u4 y0 = __builtin_amdgcn_raw_buffer_load_b128(rs, o_vw2, so_vw, 0);
-      const u4 y1 = __builtin_amdgcn_raw_buffer_load_b128(rs, o_vw2 + 16u, so_vw, 0);
+      const u4 y0 = __builtin_amdgcn_raw_buffer_load_b128(m.rs, o_vw2, so_vw, 0);
+      const u4 y1 = __builtin_amdgcn_raw_buffer_load_b128(m.rs, o_vw2 + 16u, so_vw, 0);
       d.vw2[0] = y0.x; d.vw2[1] = y0.y; d.vw2[2] = y0.z; d.vw2[3] = y0.w;
       d.vw2[4] = y1.x; d.vw2[5] = y1.y; d.vw2[6] = y1.z; d.vw2[7] = y1.w;
     }
   };
 
-  float* pvw = &pv[wave][0][0];
+  float* pvw = &pv[wave][0][0][0];
   const int64_t dbg_row = (static_cast<int64_t>(b) * k.Hq + h * G) * a.logits_stride;
-  auto process = [&](const Chunk<BK, BV>& d) {
-    if (d.ntok == 0) return;
-    // ---- key scores of tokens n (tile 0) and 16 + n (tile 1)
+  // ---- scores of one chunk, online softmax, weights x value norms to pv[slot]
+  auto keyphase = [&](const Meta& m, const KBuf<BK>& d, int slot) {
     float sc[2][2];  // [query i][tile]
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt) {
@@ -328,7 +345,7 @@ __global__ __launch_bounds__(kScanThreads) void scan_mfma_kernel(DecodeArgs a, D
         dm = mfma(aq[i], dec8<BK>(key_slice<BK>(d.kc[tt], i), lutKl), dm);
         if constexpr (QJL) dq = mfma(ap[i], dec_signs8(d.sg[tt] >> (8 * i), lutN), dq);
       }
-      const bool live = 16 * tt + n < d.ntok;
+      const bool live = 16 * tt + n < m.ntok;
 #pragma unroll
       for (int i = 0; i < 2; ++i) {
         float v = (dm[i] + dm[i + 2]) * d.kn[tt];
@@ -341,10 +358,10 @@ __global__ __launch_bounds__(kScanThreads) void scan_mfma_kernel(DecodeArgs a, D
       for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
         for (int i = 0; i < 2; ++i)
-          if (2 * kg + i < G && 16 * tt + n < d.ntok)
-            a.dbg_logits[dbg_row + (2 * kg + i) * a.logits_stride + d.pos0 + 16 * tt + n] = sc[i][tt] * kLn2;
+          if (2 * kg + i < G && 16 * tt + n < m.ntok)
+            a.dbg_logits[dbg_row + (2 * kg + i) * a.logits_stride + m.pos0 + 16 * tt + n] = sc[i][tt] * kLn2;
     }
-    // ---- online softmax; the running max moves only when exceeded by kLazy
+    float* pw = pvw + slot * (G * kChunk);
     float corr[2];
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
@@ -358,14 +375,18 @@ __global__ __launch_bounds__(kScanThreads) void scan_mfma_kernel(DecodeArgs a, D
       }
       corr[i] = move ? __builtin_amdgcn_exp2f(mrun[i] - mn) : 1.0f;
       mrun[i] = mn;
-      const float w0 = __builtin_amdgcn_exp2f(sc[i][0] - mn), w1 = __builtin_amdgcn_exp2f(sc[i][1] - mn);
+      // a dead token has score -inf: weight 0, also while mn is still -inf
+      const float w0 = sc[i][0] == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(sc[i][0] - mn);
+      const float w1 = sc[i][1] == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(sc[i][1] - mn);
       lrun[i] = fmaf(lrun[i], corr[i], w0 + w1);
       const int g = 2 * kg + i;
       if (g < G) {
-        pvw[g * kChunk + n] = n < d.ntok ? w0 * d.vn[0] : 0.0f;
-        pvw[g * kChunk + 16 + n] = 16 + n < d.ntok ? w1 * d.vn[1] : 0.0f;
+        // dead tokens may carry garbage norms: select, do not multiply by 0
+        pw[g * kChunk + n] = n < m.ntok ? w0 * d.vn[0] : 0.0f;
+        pw[g * kChunk + 16 + n] = 16 + n < m.ntok ? w1 * d.vn[1] : 0.0f;
       }
     }
+    wave_sync();
     if (corr[0] != 1.0f || corr[1] != 1.0f) {
 #pragma unroll
       for (int bl = 0; bl < 8; ++bl) {
@@ -375,17 +396,16 @@ __global__ __launch_bounds__(kScanThreads) void scan_mfma_kernel(DecodeArgs a, D
         acc[bl][3] *= corr[1];
       }
     }
-    wave_sync();
-    // ---- A operand of the value product: row n, tokens 8kg .. 8kg+7
+  };
+  // ---- value product of one chunk with the weights in pv[slot]
+  auto valuephase = [&](const VBuf<BV>& d, int slot) {
     u4 aw = u4{0u, 0u, 0u, 0u};
     if (ag < G) {
-      const float4* pw = reinterpret_cast<const float4*>(pvw + ag * kChunk + 8 * kg);
+      const float4* pw = reinterpret_cast<const float4*>(pvw + slot * (G * kChunk) + ag * kChunk + 8 * kg);
       const float4 w0 = pw[0], w1 = pw[1];
       aw = u4{pk_rtz(part_of(w0.x, amask), part_of(w0.y, amask)), pk_rtz(part_of(w0.z, amask), part_of(w0.w, amask)),
               pk_rtz(part_of(w1.x, amask), part_of(w1.y, amask)), pk_rtz(part_of(w1.z, amask), part_of(w1.w, amask))};
     }
-    wave_sync();
-    // ---- value product: block bl covers coordinates 8n' + bl
 #pragma unroll
     for (int bl = 0; bl < 8; ++bl) {
       uint32_t x;
@@ -396,50 +416,61 @@ __global__ __launch_bounds__(kScanThreads) void scan_mfma_kernel(DecodeArgs a, D
     }
   };
 
-  int c = wave;
-  Chunk<BK, BV> ca, cb2;
-  if (c < nchunks) load(c, ca);
-  while (c < nchunks) {
-    if (c + kWaves < nchunks) load(c + kWaves, cb2);
-    process(ca);
-    c += kWaves;
-    if (c >= nchunks) break;
-    if (c + kWaves < nchunks) load(c + kWaves, ca);
-    process(cb2);
-    c += kWaves;
+  // Software pipeline over this wave's chunks 0 .. nmine-1: step i
+  // accumulates the values of chunk i and scores chunk i+1.  Each buffer is
+  // refilled as soon as it is consumed: keys (with the value norms) of chunk
+  // i+1 load while chunk i's values are accumulated, values of chunk i+1
+  // while chunk i+1 is scored.  The weights alternate between two pv slots.
+  Meta m;
+  KBuf<BK> kb;
+  VBuf<BV> vb;
+  if (nmine > 0) {
+    meta(0, m);
+    loadK(m, kb);
+    loadV(m, vb);
+    keyphase(m, kb, 0);
+    int i = 0;
+    for (; i + 1 < nmine; ++i) {
+      meta(i + 1, m);
+      loadK(m, kb);
+      valuephase(vb, i & 1);
+      loadV(m, vb);
+      keyphase(m, kb, (i + 1) & 1);
+    }
+    valuephase(vb, i & 1);
   }
 
   // ---- merge the waves: per query max M, factors 2^(m_w - M)
   float ls[2];
 #pragma unroll
-  for (int i = 0; i < 2; ++i) ls[i] = row_sum(lrun[i]);
+  for (int i2 = 0; i2 < 2; ++i2) ls[i2] = row_sum(lrun[i2]);
   if (n == 0) {
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
-      if (2 * kg + i < G) {
-        wm[wave][2 * kg + i] = mrun[i];
-        wl[wave][2 * kg + i] = ls[i];
+    for (int i2 = 0; i2 < 2; ++i2)
+      if (2 * kg + i2 < G) {
+        wm[wave][2 * kg + i2] = mrun[i2];
+        wl[wave][2 * kg + i2] = ls[i2];
       }
   }
   __syncthreads();
   float fac[2];
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int g = 2 * kg + i < G ? 2 * kg + i : 0;
+  for (int i2 = 0; i2 < 2; ++i2) {
+    const int g = 2 * kg + i2 < G ? 2 * kg + i2 : 0;
     float M = -INFINITY;
 #pragma unroll
     for (int w = 0; w < kWaves; ++w) M = fmaxf(M, wm[w][g]);
-    fac[i] = (M == -INFINITY || wm[wave][g] == -INFINITY) ? 0.0f : exp2f(wm[wave][g] - M);
+    fac[i2] = (M == -INFINITY || wm[wave][g] == -INFINITY) ? 0.0f : exp2f(wm[wave][g] - M);
   }
   for (int w = 0; w < kWaves; ++w) {
     if (wave == w) {
 #pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        const int g = 2 * kg + i;
+      for (int i2 = 0; i2 < 2; ++i2) {
+        const int g = 2 * kg + i2;
         if (g < G) {
 #pragma unroll
           for (int bl = 0; bl < 8; ++bl) {
-            const float v = (acc[bl][i] + acc[bl][i + 2]) * fac[i];
+            const float v = (acc[bl][i2] + acc[bl][i2 + 2]) * fac[i2];
             red[g][8 * n + bl] = (w == 0) ? v : red[g][8 * n + bl] + v;
           }
         }
@@ -447,7 +478,7 @@ __global__ __launch_bounds__(kScanThreads) void scan_mfma_kernel(DecodeArgs a, D
     }
     __syncthreads();
   }
-  for (int i = tid; i < G * kD; i += kScanThreads) a.pacc[pidx * kD + i] = red[i / kD][i % kD];
+  for (int i2 = tid; i2 < G * kD; i2 += kScanThreads) a.pacc[pidx * kD + i2] = red[i2 / kD][i2 % kD];
   if (tid < G) {
     float M = -INFINITY;
 #pragma unroll

@@ -112,3 +112,40 @@ def test_workspace_too_small():
                            torch.zeros((1, 1, 128, 128), dtype=torch.float16, device="cuda"),
                            torch.zeros((1, 2, 128), device="cuda"), ws, 0.1, num_pages=0)
     assert e.value.code == tqa.TQ_ERR_WORKSPACE
+
+
+@pytest.mark.parametrize("kernel", ["mfma", "valu"])
+def test_garbage_beyond_live_tokens(kernel):
+    """Slots of a page past its live tokens hold NaN norms and all-ones key
+    codes/signs: the result must still equal the oracle's (dead tokens are
+    masked, never multiplied by zero)."""
+    print(f"case garbage {kernel}", flush=True)
+    s = Setup(Hq=8, Hkv=2, W=16, P=64)
+    lens = [16 + 64 * 3 + 5, 16 + 31, 16 + 64]
+    cache = s.cache(len(lens), max(lens))
+    fill(s, cache, lens)
+    pool = cache.pool.copy()
+    lay = s.lay
+    nan4 = np.frombuffer(np.float32(np.nan).tobytes(), np.uint8)
+    for b, T in enumerate(lens):
+        C = max(0, T - s.W)
+        for j in range(-(-C // s.P)):
+            live = min(s.P, C - j * s.P)
+            page = pool[int(cache.block_table[b, j])]
+            for h in range(s.Hkv):
+                base = lay.head_base(h)
+                for slot in range(live, s.P):
+                    for off in (lay.k_norm, lay.k_rnorm, lay.v_norm):
+                        page[base + off + 4 * slot: base + off + 4 * slot + 4] = nan4
+                    kc = base + lay.k_codes + slot * (lay.d * lay.bK // 8)
+                    page[kc: kc + lay.d * lay.bK // 8] = 0xFF
+                    sg = base + lay.k_signs + slot * (lay.d // 8)
+                    page[sg: sg + lay.d // 8] = 0xFF
+    ctx = context_for(s, tqa.TQ_FLAG_VALU_SCAN if kernel == "valu" else 0)
+    dev = upload_cache(cache)
+    dev["pool"].copy_(torch.from_numpy(pool.reshape(-1)).cuda())
+    q = tq_inputs.queries(9, (len(lens), s.Hq, 128))
+    qt = torch.from_numpy(q.astype(np.float32)).cuda()
+    out, dbg = run_decode(ctx, qt, dev, 1 / np.sqrt(128), logits_len=max(lens) + 1)
+    _check(cache, q.astype(np.float32).astype(np.float64), out, dbg)
+    assert tqa.tq_get_status(ctx) == 0
