@@ -314,7 +314,10 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(DecodeArgs a, DevTab
 
 // ---------------------------------------------------------------- merge
 // One work-group per (b, kv head) for its G query heads: the window K/V rows,
-// the split partials and Pi are each read once, with many loads in flight.
+// the split partials and Pi are each read once.  The kernel is a short chain
+// of dependent steps, so every independent load (window keys and values of
+// the first 128 slots, the columns of Pi) is issued at the start and lands
+// while the split partials are combined.
 template <int G>
 __global__ __launch_bounds__(kSmallThreads) void merge_kernel(DecodeArgs a, DevTables t, KParams k) {
   __shared__ float accr[G][kD], ow[G][kD], qw[G][kD], part[8][G][kD];
@@ -327,7 +330,31 @@ __global__ __launch_bounds__(kSmallThreads) void merge_kernel(DecodeArgs a, DevT
   const int nwin = T < k.W ? T : k.W;
   const int64_t row0 = (static_cast<int64_t>(b) * k.Hq + static_cast<int64_t>(h) * G) * kD;
   const int64_t bh = static_cast<int64_t>(b) * k.Hkv + h;
+  const bool dense = k.rotation == TQ_ROT_DENSE;
+
+  // ---- prefetch
+  // window keys: thread pair (tk, half) holds slot tk = tid / 2, coordinates 64 half ..
+  const int tk0 = tid >> 1, half = tid & 1;
+  uint4 kv[8];
+  if (tk0 < nwin) {
+    const uint4* kr = reinterpret_cast<const uint4*>(a.k_win + (bh * k.W + tk0) * kD + 64 * half);
+#pragma unroll
+    for (int c = 0; c < 8; ++c) kv[c] = kr[c];
+  }
+  // window values: thread (c4, q8) holds slots q8, q8 + 8, ... (first 16), coordinates c4 .. c4+3
+  const uint16_t* vbase = a.v_win + bh * k.W * kD + c4;
+  uint2 vv[16];
+#pragma unroll
+  for (int u = 0; u < 16; ++u)
+    if (q8 + 8 * u < nwin) vv[u] = *reinterpret_cast<const uint2*>(vbase + static_cast<int64_t>(q8 + 8 * u) * kD);
+  // columns c4 .. c4+3 of Pi, rows 16 q8 .. 16 q8 + 15 (dense rotation)
+  float4 rm[16];
+  if (dense) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) rm[r] = *reinterpret_cast<const float4*>(t.rot + (q8 * 16 + r) * kD + c4);
+  }
   for (int e = tid; e < G * kD; e += kSmallThreads) qw[e / kD][e % kD] = a.qwin[row0 + e];
+
   // 1. combine the split partials: thread (c4, q8) takes query g = q8 % G and
   //    splits s = sub, sub + nsub, ... (sub = q8 / G); fixed-order sums.
   {
@@ -387,14 +414,16 @@ __global__ __launch_bounds__(kSmallThreads) void merge_kernel(DecodeArgs a, DevT
     for (int r = 1; r < 8 / G; ++r) v += part[r][g][i];
     accr[g][i] = v;
   }
+
   // 2. window scores (original basis, FP16 keys, log2 units): two threads per
-  //    token, 64 coordinates each.
+  //    slot, 64 coordinates each; slots past the first 128 are loaded here.
   for (int e = tid; e < 2 * nwin; e += kSmallThreads) {
-    const int tk = e >> 1, half = e & 1;
-    const uint4* kr = reinterpret_cast<const uint4*>(a.k_win + (bh * k.W + tk) * kD + 64 * half);
-    uint4 kv[8];
+    const int tk = e >> 1;
+    if (e >= kSmallThreads) {
+      const uint4* kr = reinterpret_cast<const uint4*>(a.k_win + (bh * k.W + tk) * kD + 64 * half);
 #pragma unroll
-    for (int c = 0; c < 8; ++c) kv[c] = kr[c];
+      for (int c = 0; c < 8; ++c) kv[c] = kr[c];
+    }
     float sg[G];
 #pragma unroll
     for (int g = 0; g < G; ++g) sg[g] = 0.0f;
@@ -441,15 +470,12 @@ __global__ __launch_bounds__(kSmallThreads) void merge_kernel(DecodeArgs a, DevT
     }
   }
   __syncthreads();
-  // 4. weighted FP16 window values: thread (c4, q8) takes tokens q8, q8+8, ...
+  // 4. weighted FP16 window values: thread (c4, q8) takes slots q8, q8+8, ...
   {
     float4 acc[G];
 #pragma unroll
     for (int g = 0; g < G; ++g) acc[g] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-    const uint16_t* vb = a.v_win + bh * k.W * kD + c4;
-#pragma unroll 8
-    for (int tk = q8; tk < nwin; tk += 8) {
-      const uint2 u = *reinterpret_cast<const uint2*>(vb + static_cast<int64_t>(tk) * kD);
+    auto add = [&](int tk, uint2 u) {
       const float v0 = half_bits_to_float(static_cast<uint16_t>(u.x & 0xffffu));
       const float v1 = half_bits_to_float(static_cast<uint16_t>(u.x >> 16));
       const float v2 = half_bits_to_float(static_cast<uint16_t>(u.y & 0xffffu));
@@ -462,7 +488,12 @@ __global__ __launch_bounds__(kSmallThreads) void merge_kernel(DecodeArgs a, DevT
         acc[g].z = fmaf(w, v2, acc[g].z);
         acc[g].w = fmaf(w, v3, acc[g].w);
       }
-    }
+    };
+#pragma unroll
+    for (int u = 0; u < 16; ++u)
+      if (q8 + 8 * u < nwin) add(q8 + 8 * u, vv[u]);
+    for (int tk = q8 + 128; tk < nwin; tk += 8)
+      add(tk, *reinterpret_cast<const uint2*>(vbase + static_cast<int64_t>(tk) * kD));
 #pragma unroll
     for (int g = 0; g < G; ++g) *reinterpret_cast<float4*>(&part[q8][g][c4]) = acc[g];
   }
@@ -476,8 +507,30 @@ __global__ __launch_bounds__(kSmallThreads) void merge_kernel(DecodeArgs a, DevT
   }
   __syncthreads();
   // 5. one inverse rotation per query head: o = Pi^T acc_rot
-  if (k.rotation == TQ_ROT_DENSE) {
-    matvec_cols<G>(t.rot, accr, part, accr);
+  if (dense) {
+    // o[g][j] = sum_i Pi[i][j] accr[g][i]; thread (c4, q8) sums rows 16 q8 ..
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      float4 o = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float xv = accr[g][q8 * 16 + r];
+        o.x = fmaf(rm[r].x, xv, o.x);
+        o.y = fmaf(rm[r].y, xv, o.y);
+        o.z = fmaf(rm[r].z, xv, o.z);
+        o.w = fmaf(rm[r].w, xv, o.w);
+      }
+      *reinterpret_cast<float4*>(&part[q8][g][c4]) = o;
+    }
+    __syncthreads();
+    for (int e = tid; e < G * kD; e += kSmallThreads) {
+      const int g = e / kD, i = e % kD;
+      float v = part[0][g][i];
+#pragma unroll
+      for (int r = 1; r < 8; ++r) v += part[r][g][i];
+      accr[g][i] = v;
+    }
+    __syncthreads();
   } else {
     hadamard_lds<G>(accr, nullptr, t.rot);
   }

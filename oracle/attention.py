@@ -28,16 +28,22 @@ def _softmax_out(logits, values):
     return (w @ values) / np.sum(w), w
 
 
-def attention_plain(cache, q, sm_scale):
-    """Returns (out [B, Hq, d], logits list per (b, g) in token order)."""
+def attention_plain(cache, q, sm_scale, pairs=None):
+    """Returns (out [B, Hq, d], logits list per (b, g) in token order).
+
+    ``pairs``: optional list of (b, kv head) to evaluate (the others are left
+    at zero / None), for sampled checks of large caches."""
     q = np.asarray(q, dtype=np.float64)
     B, Hq, d = q.shape
     H = cache.lay.H
     G = Hq // H
     out = np.zeros((B, Hq, d))
     logits = [[None] * Hq for _ in range(B)]
+    want = None if pairs is None else set((int(b), int(h)) for b, h in pairs)
     for b in range(B):
         for h in range(H):
+            if want is not None and (b, h) not in want:
+                continue
             ks, vs = [], []
             comp = cache.compressed(b, h)
             if comp is not None:
