@@ -21,7 +21,7 @@ COMMON = [
     # packed FP32 instructions are kept out of every kernel
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
 ]
-SOURCES = ["tables.cpp", "tq_api.cpp", "encode.hip", "decode.hip", "decode_mfma.hip"]
+SOURCES = ["tables.cpp", "tq_api.cpp", "encode.hip", "encode_mma.hip", "decode.hip", "decode_mfma.hip"]
 
 
 def _hipcc():
@@ -32,7 +32,7 @@ def _hipcc():
 
 
 # matrix-core accumulators stay in ordinary VGPRs (no AGPR round trips in the scan loop)
-EXTRA = {"decode_mfma.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+EXTRA = {"decode_mfma.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"], "encode_mma.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
 def _compile(src, obj):

@@ -396,6 +396,9 @@ __global__ void append_commit_kernel(AppendArgs a, DevTables t, Layout L, int W,
 }  // namespace
 
 int launch_encode(const tq_ctx* c, int kind, int dtype, const EncodeArgs& a, void* stream) {
+  // fp16 rows take the matrix-core encoder; other inputs this one
+  const int rc = launch_encode_mma(c, kind, dtype, a, stream);
+  if (rc <= 0) return rc == 0 ? 0 : 1;
   hipStream_t s = static_cast<hipStream_t>(stream);
   const int bits = kind == TQ_KIND_KEY ? c->p.key_bits : c->p.value_bits;
   const int qjl = (kind == TQ_KIND_KEY && c->p.key_qjl) ? 1 : 0;

@@ -122,6 +122,9 @@ struct Ctx;  // tq_ctx
 
 // Launchers (return hipError_t as int).
 int launch_encode(const tq_ctx* ctx, int kind, int dtype, const EncodeArgs& a, void* stream);
+// Matrix-core encoder for fp16 rows (encode_mma.hip): 0 launched, 1 not
+// applicable (the caller falls back to the vector-ALU encoder), -1 error.
+int launch_encode_mma(const tq_ctx* ctx, int kind, int dtype, const EncodeArgs& a, void* stream);
 int launch_append(const tq_ctx* ctx, const AppendArgs& a, void* stream);
 int launch_decode(const tq_ctx* ctx, const DecodeArgs& a, void* stream);
 // The scan kernel a context's decode launches (MFMA or vector-ALU variant),
