@@ -74,6 +74,30 @@ struct EncCodebook {
   float bnd[16];
 };
 
+// Code of y for a symmetric codebook of 2^B levels (boundaries b_j = -b_{L-2-j},
+// middle boundary 0): the number of boundaries strictly below y.  With
+// m = |y| and the positive boundaries p_1 < .. < p_P (P = L/2 - 1): y > 0
+// gives L/2 + #{p_k < m}; y <= 0 gives L/2 - 1 - #{p_k <= m}.  Both counts
+// are #{p_k < m'} with m' = m or its float successor, found by binary search.
+template <int B>
+__device__ inline uint32_t quantize_sym(float y, const EncCodebook& cbk) {
+  constexpr int H = 1 << (B - 1);  // L/2
+  const float* p = cbk.bnd + (H - 1);  // p[k] = k-th positive boundary, p[0] = 0
+  const bool pos = y > 0.0f;
+  const uint32_t mb = __builtin_bit_cast(uint32_t, y) & 0x7fffffffu;
+  const float m = __builtin_bit_cast(float, pos ? mb : mb + 1u);
+  uint32_t cnt;
+  if constexpr (B == 2) {
+    cnt = m > p[1] ? 1u : 0u;
+  } else {
+    static_assert(B == 3, "binary search written for 2 and 3 bits");
+    const bool g2 = m > p[2];
+    const bool g1 = m > (g2 ? p[3] : p[1]);
+    cnt = (g2 ? 2u : 0u) + (g1 ? 1u : 0u);
+  }
+  return pos ? H + cnt : H - 1 - cnt;
+}
+
 // 32-lane-group sum of a double over the four lanes holding one vector
 __device__ inline double sum4(double v) {
   v += __shfl_xor(v, 16, 64);
@@ -81,8 +105,11 @@ __device__ inline double sum4(double v) {
   return v;
 }
 
+// Two work-groups per CU need <= 128 VGPRs; the dense key variant holds both
+// matrices (128 KB of LDS) and fits only one anyway.
 template <bool QJL, bool HAD, int BITS>
-__global__ __launch_bounds__(kEncThreads) void encode_mma_kernel(EncodeArgs a, DevTables t, EncCodebook cbk) {
+__global__ __launch_bounds__(kEncThreads) __attribute__((amdgpu_waves_per_eu((QJL && !HAD) ? 2 : 4)))
+void encode_mma_kernel(EncodeArgs a, DevTables t, EncCodebook cbk) {
   __shared__ u4 fragP[HAD ? 1 : 8 * 4 * 2 * 64];  // 64 KB
   __shared__ u4 fragS[QJL ? 8 * 4 * 2 * 64 : 1];  // 64 KB
   __shared__ float ctab[16];
@@ -101,7 +128,6 @@ __global__ __launch_bounds__(kEncThreads) void encode_mma_kernel(EncodeArgs a, D
   constexpr int kCols = cols_for(HAD), kTileVec = 16 * kCols;
   const int l = tid & 63, n = l & 15, kg = l >> 4;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  constexpr int nb = (1 << BITS) - 1;
   float eps[32];  // Hadamard signs of this lane's coordinates
   if constexpr (HAD) {
 #pragma unroll
@@ -149,21 +175,28 @@ __global__ __launch_bounds__(kEncThreads) void encode_mma_kernel(EncodeArgs a, D
       for (int c = 0; c < kCols; ++c)
 #pragma unroll
         for (int tt = 0; tt < 8; ++tt) acc[c][tt] = f4{0.0f, 0.0f, 0.0f, 0.0f};
+      // one output tile at a time: the scheduling barrier keeps later tiles'
+      // fragment reads from being hoisted (they would all be live at once;
+      // reading the next tile ahead measured no faster)
+      u4 fa[8];
+      auto ldP = [&](int tt, u4* f) {
 #pragma unroll
-      for (int tt = 0; tt < 8; ++tt)
+        for (int q = 0; q < 8; ++q) f[q] = fragP[(tt * 8 + q) * 64 + l];
+      };
+      ldP(0, fa);
 #pragma unroll
-        for (int s = 0; s < 4; ++s) {
-          const u4 ph = fragP[((tt * 4 + s) * 2 + 0) * 64 + l];
-          const u4 pl = fragP[((tt * 4 + s) * 2 + 1) * 64 + l];
+      for (int tt = 0; tt < 8; ++tt) {
+        u4* cur = fa;
+        if (tt > 0) ldP(tt, cur);
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
 #pragma unroll
           for (int c = 0; c < kCols; ++c) {
-            acc[c][tt] = mfma(ph, xb[c][s], acc[c][tt]);
-            acc[c][tt] = mfma(pl, xb[c][s], acc[c][tt]);
+            acc[c][tt] = mfma(cur[2 * s], xb[c][s], acc[c][tt]);
+            acc[c][tt] = mfma(cur[2 * s + 1], xb[c][s], acc[c][tt]);
           }
-          // keeps the fragment loads of later tiles from being hoisted here
-          // (they would all be live at once)
-          if (s == 3) __builtin_amdgcn_sched_barrier(0);
-        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
 #pragma unroll
       for (int c = 0; c < kCols; ++c)
 #pragma unroll
@@ -206,21 +239,26 @@ __global__ __launch_bounds__(kEncThreads) void encode_mma_kernel(EncodeArgs a, D
 #pragma unroll
       for (int w = 0; w < BITS; ++w) words[c][w] = 0u;
       float rv[32];
-      double rs = 0.0;
+      float rs = 0.0f;
 #pragma unroll
       for (int j = 0; j < 32; ++j) {
         const float accv = acc[c][j >> 2][j & 3];
         const float y = accv * invn[c];
         uint32_t code = 0;
+        if constexpr (BITS == 3 && !QJL) {
+          code = quantize_sym<BITS>(y, cbk);
+        } else {
+          // a linear count measured faster for 2 and 4 bits and for keys
 #pragma unroll
-        for (int k = 0; k < nb; ++k) code += (y > cbk.bnd[k]) ? 1u : 0u;
+          for (int k = 0; k < (1 << BITS) - 1; ++k) code += (y > cbk.bnd[k]) ? 1u : 0u;
+        }
         if (!(n32[c] > 0.0f)) code = 0;
         const int pos = j * BITS;
         words[c][pos >> 5] |= code << (pos & 31);
         if ((pos & 31) + BITS > 32) words[c][(pos >> 5) + 1] |= code >> (32 - (pos & 31));
         if constexpr (QJL) {
           const float r = (n32[c] > 0.0f) ? fmaf(-n32[c], ctab[code], accv) : 0.0f;
-          rs = fma(static_cast<double>(r), static_cast<double>(r), rs);
+          rs = fmaf(r, r, rs);
           rv[j] = r * (64.0f * invn[c]);
         }
       }
@@ -232,17 +270,20 @@ __global__ __launch_bounds__(kEncThreads) void encode_mma_kernel(EncodeArgs a, D
         if (kg == 0) a.norms[vid[c]] = n32[c];
       }
       if constexpr (QJL) {
-        rs = sum4(rs);
-        if (live[c] && kg == 0) a.rnorms[vid[c]] = static_cast<float>(sqrt(rs));
+        rs += __shfl_xor(rs, 16, 64);
+        rs += __shfl_xor(rs, 32, 64);
+        if (live[c] && kg == 0) a.rnorms[vid[c]] = sqrtf(rs);
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
           uint32_t hi[4], lo[4];
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
+            // hi truncated to fp16, lo = the exact fp32 remainder truncated again
             const float r0 = rv[8 * s + 2 * i], r1 = rv[8 * s + 2 * i + 1];
-            const uint32_t h0 = hbits(r0), h1 = hbits(r1);
-            hi[i] = h0 | (h1 << 16);
-            lo[i] = hbits(r0 - hval(h0)) | (hbits(r1 - hval(h1)) << 16);
+            const auto hp = __builtin_amdgcn_cvt_pkrtz(r0, r1);
+            hi[i] = __builtin_bit_cast(uint32_t, hp);
+            lo[i] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(r0 - static_cast<float>(hp[0]),
+                                                                            r1 - static_cast<float>(hp[1])));
           }
           rb[c][s][0] = u4{hi[0], hi[1], hi[2], hi[3]};
           rb[c][s][1] = u4{lo[0], lo[1], lo[2], lo[3]};
@@ -307,6 +348,11 @@ int launch_encode_mma(const tq_ctx* c, int kind, int dtype, const EncodeArgs& a,
     cbk.cen[k] = key ? c->cb.kc[k] : c->cb.vc[k];
     cbk.bnd[k] = key ? c->cb.kb[k] : c->cb.vb[k];
   }
+  // the quantiser relies on a symmetric codebook with a boundary at 0
+  const int L = 1 << bits;
+  if (cbk.bnd[L / 2 - 1] != 0.0f) return 1;
+  for (int k = 0; k + 1 < L; ++k)
+    if (cbk.bnd[k] != -cbk.bnd[L - 2 - k]) return 1;
   int dev = 0, cus = 0, per_cu = 0;
   if (hipGetDevice(&dev) != hipSuccess ||
       hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
