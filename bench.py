@@ -37,6 +37,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-encode", action="store_true", help="skip the tq_encode leg")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--T", type=int, default=32768)
     ap.add_argument("--batch", type=int, default=16)
@@ -70,6 +71,65 @@ def cpu_baseline(T, W, P, G, Hkv, min_seconds):
     return {"value": calls * T / Hkv / el, "unit": "tokens/s", "cores": threads, "kind": "oracle",
             "sample": f"{calls} oracle decode call(s) of 1 sequence x 1 KV head ({G} query heads) at T={T}, "
                       f"{el:.1f} s; rate scaled to {Hkv} KV heads"}
+
+
+SCAN_SOURCES = ["decode_mfma.hip", "decode_common.h", "device_common.h", "tq_internal.h"]
+
+
+def scan_traffic():
+    """HBM bytes per scan launch from the committed rocprofv3 counter summary
+    (profiles/decode_scan_traffic.json), when it was taken on the current
+    kernel source; None otherwise."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "decode_scan_traffic.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path))
+    h = hashlib.sha256()
+    for f in SCAN_SOURCES:
+        h.update(open(os.path.join(ROOT, "kv_cache_vector_tq_amd", "csrc", f), "rb").read())
+    if rec.get("source_sha256") != h.hexdigest():
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def encode_leg(tqa, tq_inputs, ctx, params, reps=10):
+    """tq_encode of 4M fp16 vectors (4,096 sequences x 1,024 positions of the
+    key recipe, and as many N(0,1) values) with the decode workload's formats:
+    keys 3-bit + QJL, values 4-bit, dense rotation.  HIP-event time per call;
+    MFMA work as executed (rotation in two fp16 passes, QJL projection in
+    three) and as the two d x d products count it (4 d^2 flop per key)."""
+    import torch
+    n, d = 4096 * 1024, 128
+    k, v = tq_inputs.torch_kv(5, 4096, 1, 1024, d, "cuda")
+    k, v = k.view(n, d), v.view(n, d)
+    codes = torch.empty((n, 64), dtype=torch.uint8, device="cuda")
+    norms = torch.empty(n, dtype=torch.float32, device="cuda")
+    signs = torch.empty((n, 16), dtype=torch.uint8, device="cuda")
+    rnorms = torch.empty(n, dtype=torch.float32, device="cuda")
+    out = {}
+    for name, kind, x, qjl in (("keys_3bit_qjl", tqa.TQ_KIND_KEY, k, True), ("values_4bit", tqa.TQ_KIND_VALUE, v, False)):
+        def call():
+            tqa.tq_encode(ctx, kind, x, codes, norms, signs if qjl else None, rnorms if qjl else None)
+        call()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            call()
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / reps
+        algo = (4 if qjl else 2) * d * d * n
+        executed = (5 if qjl else 2) * 2 * d * d * n
+        in_bytes = n * d * 2
+        out_bytes = n * ((48 + 16 + 8) if qjl else (64 + 4))
+        out[name] = {"ms": ms, "vectors_per_s": n / (ms / 1e3), "algorithmic_tflops": algo / (ms / 1e3) / 1e12,
+                     "mfma_tflops_executed": executed / (ms / 1e3) / 1e12,
+                     "hbm_gbps": (in_bytes + out_bytes) / (ms / 1e3) / 1e9}
+    out["workload"] = "tq_encode of 4,194,304 fp16 vectors d=128 (4,096 x 1,024 positions), dense rotation"
+    del k, v, codes, norms, signs, rnorms
+    return out
 
 
 def main():
@@ -164,10 +224,13 @@ def main():
         "hbm_gbps_step": (sum(comp_bytes) / len(comp_bytes) + win_bytes) / (ms_step / 1e3) / 1e9,
         "scan_us": scan_s * 1e6,
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBPS, "traffic": None,
+                     "frac": achieved / HBM_PEAK_GBPS, "traffic": scan_traffic(),
                      "kernel": "scan_kernel (VALU)" if args.valu_scan else "scan_mfma_kernel",
                      "algorithmic_bytes_per_launch": sum(comp_bytes) / len(comp_bytes)},
     }
+    del pool, k_win, v_win, ksteps, vsteps, ws
+    if not args.no_encode:
+        res["encode"] = encode_leg(tqa, tq_inputs, ctx, params)
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(Tf, W, P, G, Hkv, args.cpu_seconds)
     print(json.dumps(res), flush=True)
