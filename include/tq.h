@@ -36,7 +36,8 @@
  *
  * Page format (one page = one layer x one sequence x P tokens x all H_kv heads):
  *   page_bytes = roundup(256 + H_kv * head_bytes, 256); 64-byte header at 0
- *   (u32 magic 0x564B5154, u16 version 1, u16 d, u8 key_bits, u8 key_qjl,
+ *   (u32 magic 0x564B5154, u16 version 1, u16 d, u8 key_bits, u8 key QJL
+ *   (0 none, 1 Gaussian S, 2 orthogonal S),
  *   u8 value_bits, u8 rotation, u16 H_kv, u16 P, u32 valid tokens, u32
  *   codebook version 1, u64 seed, u32 page index, zeros); head h's body at
  *   256 + h * head_bytes holds, in order: key norms f32[P]; key residual norms
@@ -71,6 +72,7 @@ enum {
 };
 
 enum { TQ_ROT_DENSE = 0, TQ_ROT_HADAMARD = 1 };
+enum { TQ_QJL_GAUSSIAN = 0, TQ_QJL_ORTHOGONAL = 1 };
 enum { TQ_DTYPE_F16 = 0, TQ_DTYPE_BF16 = 1, TQ_DTYPE_F32 = 2 };
 enum { TQ_KIND_KEY = 0, TQ_KIND_VALUE = 1 };
 /* tq_params.flags: TQ_FLAG_VALU_SCAN selects the vector-ALU decode scan
@@ -97,6 +99,13 @@ typedef struct tq_params {
   int32_t window;       /* W, FP16 recent tokens per sequence, 0..1024 */
   int32_t flags;        /* TQ_FLAG_* bits, 0 for the default kernels */
   uint64_t seed;        /* recorded in page headers (cache identity); draws come from the caller */
+  int32_t qjl_kind;     /* TQ_QJL_GAUSSIAN (the paper's S, coefficient sqrt(pi/2)/d) or
+                           TQ_QJL_ORTHOGONAL (S = Haar orthogonal matrix from the same draws,
+                           matched coefficient sqrt(pi/2)/sqrt(d)): "TurboQuant on a 16GB
+                           MacBook", "The QJL detective story" */
+  float qjl_shrink;     /* factor on the QJL correction term in decode, (0, 4]; 1 = unbiased,
+                           2/pi = the MMSE shrinkage for orthogonal S (same section, the 0.7
+                           damping of the ablation) */
 } tq_params;
 
 typedef struct tq_ctx tq_ctx;
@@ -105,8 +114,10 @@ typedef struct tq_ctx tq_ctx;
  * them, without touching a GPU.  rot_draws: DENSE: d*d i.i.d. N(0,1) values
  * (row-major) whose QR Q factor, with the signs of diag(R) folded in, is the
  * rotation Pi (y = Pi x); HADAMARD: d values whose signs (x < 0 -> -1, else +1)
- * are the Rademacher stage.  qjl_draws: d*d N(0,1) values, the QJL matrix S
- * itself (row i gives sign bit i); may be NULL when key_qjl == 0.
+ * are the Rademacher stage.  qjl_draws: d*d N(0,1) values: the QJL matrix S
+ * itself (TQ_QJL_GAUSSIAN; row i gives sign bit i) or the draws its Haar
+ * orthogonal S is built from, like the dense rotation (TQ_QJL_ORTHOGONAL);
+ * may be NULL when key_qjl == 0.
  * Outputs (each nullable): rotation d*d f32 (DENSE: Pi row-major; HADAMARD:
  * the d signs), qjl d*d f32, key/value centroids 2^b f32 (Lloyd-Max levels of
  * N(0,1) times 1/sqrt(d), rounded to half-precision values), key/value

@@ -20,6 +20,7 @@ TQ_ERR_UNSUPPORTED = -2
 TQ_ERR_WORKSPACE = -3
 TQ_ERR_HIP = -4
 TQ_ROT_DENSE, TQ_ROT_HADAMARD = 0, 1
+TQ_QJL_GAUSSIAN, TQ_QJL_ORTHOGONAL = 0, 1
 TQ_DTYPE_F16, TQ_DTYPE_BF16, TQ_DTYPE_F32 = 0, 1, 2
 TQ_KIND_KEY, TQ_KIND_VALUE = 0, 1
 TQ_STATUS_BAD_PAGE, TQ_STATUS_BAD_COUNT = 1, 2
@@ -43,14 +44,15 @@ class tq_params(ctypes.Structure):
         ("head_dim", ctypes.c_int32), ("key_bits", ctypes.c_int32), ("key_qjl", ctypes.c_int32),
         ("value_bits", ctypes.c_int32), ("rotation", ctypes.c_int32), ("num_q_heads", ctypes.c_int32),
         ("num_kv_heads", ctypes.c_int32), ("page_tokens", ctypes.c_int32), ("window", ctypes.c_int32),
-        ("flags", ctypes.c_int32), ("seed", ctypes.c_uint64),
+        ("flags", ctypes.c_int32), ("seed", ctypes.c_uint64), ("qjl_kind", ctypes.c_int32),
+        ("qjl_shrink", ctypes.c_float),
     ]
 
 
 def make_params(head_dim=128, key_bits=3, key_qjl=1, value_bits=4, rotation=TQ_ROT_DENSE, num_q_heads=1,
-                num_kv_heads=1, page_tokens=256, window=128, seed=0, flags=0):
+                num_kv_heads=1, page_tokens=256, window=128, seed=0, flags=0, qjl_kind=0, qjl_shrink=1.0):
     return tq_params(head_dim, key_bits, key_qjl, value_bits, rotation, num_q_heads, num_kv_heads,
-                     page_tokens, window, flags, seed)
+                     page_tokens, window, flags, seed, qjl_kind, qjl_shrink)
 
 
 _lib = None

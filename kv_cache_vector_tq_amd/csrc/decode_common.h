@@ -1,6 +1,8 @@
 // Shared by the decode kernels.
 #pragma once
 
+#include <cmath>
+
 #include "tq_internal.h"
 
 namespace tq {
@@ -28,7 +30,12 @@ inline KParams make_kparams(const tq_ctx* c) {
   k.v_norm = c->lay.v_norm;
   k.v_codes = c->lay.v_codes;
   k.rotation = c->p.rotation;
-  k.qjl_scale = 1.2533141373155003f / static_cast<float>(c->p.head_dim);  // sqrt(pi/2)/d
+  // QJL coefficient: sqrt(pi/2)/d for Gaussian S, sqrt(pi/2)/sqrt(d) for
+  // orthogonal S, times the shrinkage factor
+  const double dd = static_cast<double>(c->p.head_dim);
+  const double base = c->p.qjl_kind == TQ_QJL_ORTHOGONAL ? 1.2533141373155003 / std::sqrt(dd)
+                                                          : 1.2533141373155003 / dd;
+  k.qjl_scale = static_cast<float>(base * static_cast<double>(c->p.qjl_shrink));
   return k;
 }
 

@@ -51,9 +51,19 @@ __device__ inline CoreParams make_core(const Codebooks& cb, bool key, int bits, 
 // Rotate, quantise and (for keys) sketch the residual of the tile in LDS.
 // Only vectors v0 <= v < v1 of the tile are encoded (the others are not
 // written by the callers).
-template <bool HAD>
+template <bool HAD, bool LAT>
 __device__ void encode_core(Smem& sm, const DevTables& t, const CoreParams& cp, int v0, int v1) {
   const int tid = threadIdx.x;
+  // LAT (appends of a few tokens, a pure latency chain): this thread's whole
+  // rows of Pi and S are requested first, so their loads land during the
+  // rest; otherwise rows are read in halves to keep registers for occupancy
+  float srow[LAT ? kD : 1];
+  if constexpr (LAT) {
+    if (cp.qjl) {
+#pragma unroll
+      for (int j = 0; j < kD; ++j) srow[j] = t.ST[j * kD + tid];
+    }
+  }
   const int nb = (1 << cp.bits) - 1;
   if (tid < 16) {
     float cv = 0.0f;
@@ -92,7 +102,25 @@ __device__ void encode_core(Smem& sm, const DevTables& t, const CoreParams& cp, 
     sm.code[v][tid] = static_cast<uint8_t>(c);
     if (cp.qjl) sm.rs[v][tid] = (n > 0.0f) ? fmaf(-n, sm.ctab[c], accv) : 0.0f;
   };
-  if constexpr (!HAD) {
+  if constexpr (!HAD && LAT) {
+    float pr[kD];
+#pragma unroll
+    for (int j = 0; j < kD; ++j) pr[j] = t.rotT[j * kD + tid];
+#pragma unroll 1
+    for (int v = v0; v < v1; ++v) {
+      float s = 0.0f;
+      const float4* xr = reinterpret_cast<const float4*>(sm.xs[v]);
+#pragma unroll
+      for (int j4 = 0; j4 < kD / 4; ++j4) {
+        const float4 x = xr[j4];
+        s = fmaf(pr[4 * j4 + 0], x.x, s);
+        s = fmaf(pr[4 * j4 + 1], x.y, s);
+        s = fmaf(pr[4 * j4 + 2], x.z, s);
+        s = fmaf(pr[4 * j4 + 3], x.w, s);
+      }
+      finish(v, s);
+    }
+  } else if constexpr (!HAD) {
     // two passes over halves of the rotation row keep the register count
     // low; the first pass parks its partial sums in this thread's rs slots
 #pragma unroll
@@ -160,6 +188,29 @@ __device__ void encode_core(Smem& sm, const DevTables& t, const CoreParams& cp, 
     if (part == 0) sm.rn[v] = static_cast<float>(sqrt(s));
   }
   const int wave = tid >> 6, lane = tid & 63;
+  if constexpr (LAT) {
+    __syncthreads();
+#pragma unroll 1
+    for (int v = v0; v < v1; ++v) {
+      float z = 0.0f;
+      const float4* rr = reinterpret_cast<const float4*>(sm.rs[v]);
+#pragma unroll
+      for (int j4 = 0; j4 < kD / 4; ++j4) {
+        const float4 r = rr[j4];
+        z = fmaf(srow[4 * j4 + 0], r.x, z);
+        z = fmaf(srow[4 * j4 + 1], r.y, z);
+        z = fmaf(srow[4 * j4 + 2], r.z, z);
+        z = fmaf(srow[4 * j4 + 3], r.w, z);
+      }
+      const bool bit = (z >= 0.0f) && (sm.n32[v] > 0.0f);
+      const uint64_t m = __ballot(bit);
+      if (lane == 0) {
+        sm.sgn[v][2 * wave] = static_cast<uint32_t>(m);
+        sm.sgn[v][2 * wave + 1] = static_cast<uint32_t>(m >> 32);
+      }
+    }
+    return;
+  }
   __syncthreads();  // xs is free from here on: it holds the first half of S r
 #pragma unroll
   for (int hp = 0; hp < 2; ++hp) {
@@ -213,7 +264,7 @@ __global__ __launch_bounds__(kThreads) void encode_flat_kernel(EncodeArgs a, Dev
     sm.xs[v][tid] = v < nv ? load_any(a.x, (n0 + v) * a.row_stride + tid, dtype) : 0.0f;
   __syncthreads();
   const CoreParams cp = make_core(cb, kind == TQ_KIND_KEY, bits, qjl != 0);
-  encode_core<HAD>(sm, t, cp, 0, nv);
+  encode_core<HAD, false>(sm, t, cp, 0, nv);
   __syncthreads();
   if (tid < nv) {
     a.norms[n0 + tid] = sm.n32[tid];
@@ -272,18 +323,30 @@ __device__ inline SeqPlan plan_seq(const AppendArgs& a, const Layout& L, int W, 
   return s;
 }
 
-template <bool HAD>
-__global__ __launch_bounds__(kThreads) void append_encode_kernel(AppendArgs a, DevTables t, Codebooks cb, Layout L,
-                                                                int W) {
-  __shared__ Smem sm;
-  const int tid = threadIdx.x, h = blockIdx.y, b = blockIdx.z;
-  // every work-group of b evaluates the same plan; the commit kernel reports
-  const SeqPlan sp = plan_seq(a, L, W, b, t.status, false);
-  if (!sp.ok || sp.c1 <= sp.c0) return;
-  const int kv = static_cast<int>(blockIdx.x & 1u);  // 0: keys, 1: values
-  const int g = sp.c0 / kVGroup + static_cast<int>(blockIdx.x >> 1);
-  const int gpos = g * kVGroup;
-  if (gpos >= sp.c1) return;
+// New tokens that remain among the last W go to the FP16 ring.  With at most
+// W new tokens, token q either evicts q - W from its slot, and is written by
+// the work-group that encodes q - W (after that one has read the slot), or
+// evicts nothing and is written by the first work-group; no slot is read by
+// one work-group and written by another.
+__device__ inline void ring_owned(const AppendArgs& a, const SeqPlan& sp, int W, int64_t bh, int kv, int gr,
+                                  int tid) {
+  const int j0 = sp.cnt > W ? sp.cnt - W : 0;
+  const int g0 = sp.c0 / kVGroup;
+  for (int j = j0; j < sp.cnt; ++j) {
+    const int q = sp.T0 + j;
+    if ((q >= W ? (q - W) / kVGroup - g0 : 0) != gr) continue;
+    if (kv == 0)
+      a.k_win[(bh * W + q % W) * kD + tid] = a.k_new[(bh * a.n_new + j) * kD + tid];
+    else
+      a.v_win[(bh * W + q % W) * kD + tid] = a.v_new[(bh * a.n_new + j) * kD + tid];
+  }
+}
+
+// Encode the evicted tokens of one 32-token group of sequence b, head h.
+template <bool HAD, bool LAT>
+__device__ void encode_group(Smem& sm, const AppendArgs& a, const DevTables& t, const Codebooks& cb, const Layout& L,
+                             int W, const SeqPlan& sp, int b, int h, int kv, int gpos) {
+  const int tid = threadIdx.x;
   const int lo = sp.c0 > gpos ? sp.c0 : gpos;
   const int hi = sp.c1 < gpos + kVGroup ? sp.c1 : gpos + kVGroup;
   const int pg = gpos / L.P, slot0 = gpos % L.P;
@@ -307,7 +370,7 @@ __global__ __launch_bounds__(kThreads) void append_encode_kernel(AppendArgs a, D
     const bool key = kv == 0;
     const CoreParams cp = make_core(cb, key, key ? L.bK : L.bV, key && L.qjl);
     const int vlo = lo - gpos, vhi = hi - gpos;
-    encode_core<HAD>(sm, t, cp, vlo, vhi);
+    encode_core<HAD, LAT>(sm, t, cp, vlo, vhi);
     __syncthreads();
     if (key) {
       float* kn = reinterpret_cast<float*>(hb + L.k_norm);
@@ -352,6 +415,23 @@ __global__ __launch_bounds__(kThreads) void append_encode_kernel(AppendArgs a, D
   }
 }
 
+template <bool HAD, bool LAT>
+__global__ __launch_bounds__(kThreads) void append_encode_kernel(AppendArgs a, DevTables t, Codebooks cb, Layout L,
+                                                                int W, int ring) {
+  __shared__ Smem sm;
+  const int tid = threadIdx.x, h = blockIdx.y, b = blockIdx.z;
+  // every work-group of b evaluates the same plan; the commit kernel reports
+  const SeqPlan sp = plan_seq(a, L, W, b, t.status, false);
+  if (!sp.ok) return;
+  const int kv = static_cast<int>(blockIdx.x & 1u);  // 0: keys, 1: values
+  const int gr = static_cast<int>(blockIdx.x >> 1);
+  const int g = sp.c0 / kVGroup + gr;
+  const int gpos = g * kVGroup;
+  if (sp.c1 > sp.c0 && gpos < sp.c1) encode_group<HAD, LAT>(sm, a, t, cb, L, W, sp, b, h, kv, gpos);
+  if (ring) ring_owned(a, sp, W, static_cast<int64_t>(b) * L.H + h, kv, gr, tid);
+}
+
+
 // New tokens that remain among the last W go to the FP16 ring.
 __global__ __launch_bounds__(kThreads) void append_ring_kernel(AppendArgs a, DevTables t, Layout L, int W) {
   const int tid = threadIdx.x, h = blockIdx.x, b = blockIdx.y;
@@ -367,7 +447,8 @@ __global__ __launch_bounds__(kThreads) void append_ring_kernel(AppendArgs a, Dev
 }
 
 // Advance seq_lens and rewrite the headers of the pages the append touched.
-__global__ void append_commit_kernel(AppendArgs a, DevTables t, Layout L, int W, int rotation, uint64_t seed) {
+__global__ void append_commit_kernel(AppendArgs a, DevTables t, Layout L, int W, int rotation, int qjl_code,
+                                     uint64_t seed) {
   for (int b = blockIdx.x * blockDim.x + threadIdx.x; b < a.batch; b += gridDim.x * blockDim.x) {
     const SeqPlan sp = plan_seq(a, L, W, b, t.status, true);
     if (!sp.ok) continue;
@@ -378,7 +459,7 @@ __global__ void append_commit_kernel(AppendArgs a, DevTables t, Layout L, int W,
         const int valid = sp.c1 - pg * L.P < L.P ? sp.c1 - pg * L.P : L.P;
         hd[0] = kMagic;
         hd[1] = 1u | (static_cast<uint32_t>(L.d) << 16);
-        hd[2] = static_cast<uint32_t>(L.bK) | (static_cast<uint32_t>(L.qjl) << 8) |
+        hd[2] = static_cast<uint32_t>(L.bK) | (static_cast<uint32_t>(qjl_code) << 8) |
                 (static_cast<uint32_t>(L.bV) << 16) | (static_cast<uint32_t>(rotation) << 24);
         hd[3] = static_cast<uint32_t>(L.H) | (static_cast<uint32_t>(L.P) << 16);
         hd[4] = static_cast<uint32_t>(valid);
@@ -419,17 +500,31 @@ int launch_append(const tq_ctx* c, const AppendArgs& a, void* stream) {
   // groups a sequence can touch: ceil(n_new / 32) + 1 (unaligned start)
   const int gmax = (a.n_new + kVGroup - 1) / kVGroup + 1;
   dim3 grid(2 * gmax, L.H, a.batch);  // even x: keys, odd x: values
-  if (c->p.rotation == TQ_ROT_HADAMARD)
-    hipLaunchKernelGGL(append_encode_kernel<true>, grid, dim3(kThreads), 0, s, a, c->t, c->cb, L, W);
+  // a few new tokens: each work-group encodes at most a handful of vectors
+  // and the kernel is a latency chain (see encode_core's LAT)
+  const bool lat = a.n_new <= 4;
+  const bool had = c->p.rotation == TQ_ROT_HADAMARD;
+  // the ring update rides along when no slot can be read and written by
+  // different work-groups (at most W new tokens)
+  const int ring = (W > 0 && a.n_new <= W) ? 1 : 0;
+  if (had && lat)
+    hipLaunchKernelGGL((append_encode_kernel<true, true>), grid, dim3(kThreads), 0, s, a, c->t, c->cb, L, W, ring);
+  else if (had)
+    hipLaunchKernelGGL((append_encode_kernel<true, false>), grid, dim3(kThreads), 0, s, a, c->t, c->cb, L, W, ring);
+  else if (lat)
+    hipLaunchKernelGGL((append_encode_kernel<false, true>), grid, dim3(kThreads), 0, s, a, c->t, c->cb, L, W, ring);
   else
-    hipLaunchKernelGGL(append_encode_kernel<false>, grid, dim3(kThreads), 0, s, a, c->t, c->cb, L, W);
+    hipLaunchKernelGGL((append_encode_kernel<false, false>), grid, dim3(kThreads), 0, s, a, c->t, c->cb, L, W, ring);
   if (hipGetLastError() != hipSuccess) return 1;
-  if (W > 0) {
+  if (W > 0 && !ring) {
     hipLaunchKernelGGL(append_ring_kernel, dim3(L.H, a.batch), dim3(kThreads), 0, s, a, c->t, L, W);
     if (hipGetLastError() != hipSuccess) return 1;
   }
   const int cb = (a.batch + 255) / 256;
-  hipLaunchKernelGGL(append_commit_kernel, dim3(cb), dim3(256), 0, s, a, c->t, L, W, c->p.rotation, c->p.seed);
+  // header byte: 0 no QJL, 1 Gaussian S, 2 orthogonal S
+  const int qjl_code = c->p.key_qjl ? 1 + c->p.qjl_kind : 0;
+  hipLaunchKernelGGL(append_commit_kernel, dim3(cb), dim3(256), 0, s, a, c->t, L, W, c->p.rotation, qjl_code,
+                     c->p.seed);
   return hipGetLastError() == hipSuccess ? 0 : 1;
 }
 

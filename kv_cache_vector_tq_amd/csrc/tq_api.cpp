@@ -23,6 +23,8 @@ bool params_ok(const tq_params* p) {
   if (p->page_tokens <= 0 || p->page_tokens % tq::kVGroup || p->page_tokens > tq::kMaxPage) return false;
   if (p->window < 0 || p->window > tq::kMaxWindow) return false;
   if (p->flags & ~TQ_FLAG_VALU_SCAN) return false;
+  if (p->qjl_kind != TQ_QJL_GAUSSIAN && p->qjl_kind != TQ_QJL_ORTHOGONAL) return false;
+  if (!(p->qjl_shrink > 0.0f && p->qjl_shrink <= 4.0f)) return false;  // also rejects NaN
   return true;
 }
 
@@ -127,7 +129,10 @@ TQ_API int tq_host_tables(const tq_params* p, const double* rot_draws, const dou
   }
   if (qjl) {
     if (!qjl_draws) return TQ_ERR_INVALID_ARG;
-    for (int i = 0; i < d * d; ++i) qjl[i] = static_cast<float>(qjl_draws[i]);
+    if (p->qjl_kind == TQ_QJL_ORTHOGONAL)
+      tq::haar_rotation_f32(qjl_draws, d, qjl);  // Haar orthogonal S from the draws
+    else
+      for (int i = 0; i < d * d; ++i) qjl[i] = static_cast<float>(qjl_draws[i]);
   }
   tq::codebook_f32(p->key_bits, d, key_centroids, key_boundaries);
   tq::codebook_f32(p->value_bits, d, value_centroids, value_boundaries);

@@ -49,7 +49,7 @@ def attention_plain(cache, q, sm_scale, pairs=None):
             if comp is not None:
                 krec, vn, vidx = comp
                 ks.append(codec.dequantize(krec.codes, krec.norms, cache.rot, cache.kcb,
-                                           krec.signs, krec.rnorms, cache.S))
+                                           krec.signs, krec.rnorms, cache.S, cache.qjl_coef))
                 vs.append(cache.rot.inverse(vn.astype(np.float64)[:, None] * cache.vcb.centroids[vidx]))
             _, kw, vw = cache.window_tokens(b, h)
             ks.append(kw)
@@ -73,7 +73,7 @@ def attention_compressed(cache, q, sm_scale):
     lay = cache.lay
     H = lay.H
     G = Hq // H
-    alpha = codec.qjl_scale(d)
+    alpha = cache.qjl_coef
     out = np.zeros((B, Hq, d))
     logits = [[None] * Hq for _ in range(B)]
     for b in range(B):

@@ -19,10 +19,13 @@ Encode of one post-RoPE vector x (float values, taken exactly as float64):
    quantisation residual; "The QJL detective story": Gaussian S).
 
 Dequantise (reverses the steps, README "Algorithm" last line):
-  k_hat = Pi^T ( n c_K[idx] + sqrt(pi/2)/d * ||r|| * S^T (2 sigma - 1) )
+  k_hat = Pi^T ( n c_K[idx] + a * ||r|| * S^T (2 sigma - 1) )
   v_hat = Pi^T ( n_V c_V[idx_V] )
-with the QJL dequantisation scale sqrt(pi/2)/d for Gaussian S ("The QJL
-detective story").
+with the QJL coefficient a = sqrt(pi/2)/d for Gaussian S (the paper's pair)
+or a = alpha * sqrt(pi/2)/sqrt(d) for an orthogonal S with shrinkage alpha
+(the variance-reduced variant; "The QJL detective story": orthogonal matrix
+and the matched 1/sqrt(d) scale are one coupled substitution, damping 0.7 is
+close to the MMSE shrinkage 2/pi).
 """
 
 import math
@@ -32,9 +35,15 @@ import numpy as np
 QJL_SCALE_NUM = math.sqrt(math.pi / 2.0)
 
 
-def qjl_scale(head_dim: int) -> float:
-    """sqrt(pi/2)/d: the unbiased dequantisation scale for Gaussian S with d rows."""
-    return QJL_SCALE_NUM / head_dim
+def qjl_scale(head_dim: int, kind: str = "gaussian", shrink: float = 1.0) -> float:
+    """QJL dequantisation coefficient.  Gaussian S with d rows: sqrt(pi/2)/d
+    (unbiased).  Orthogonal S: sqrt(pi/2)/sqrt(d) (the matched scale; rows of
+    unit norm), times the shrinkage factor."""
+    if kind == "gaussian":
+        return shrink * QJL_SCALE_NUM / head_dim
+    if kind == "orthogonal":
+        return shrink * QJL_SCALE_NUM / math.sqrt(head_dim)
+    raise ValueError(kind)
 
 
 def pack_bits(codes: np.ndarray, bits: int) -> np.ndarray:
@@ -104,24 +113,35 @@ def residual_from_codes(x: np.ndarray, rotation, codebook, norms32, idx) -> np.n
     return r
 
 
-def dequantize_rotated(codes, norms, codebook, d, signs=None, rnorms=None, qjl_S=None):
-    """Reconstruction in the rotated basis: n c[idx] (+ QJL term for keys)."""
+def dequantize_rotated(codes, norms, codebook, d, signs=None, rnorms=None, qjl_S=None, qjl_coef=None):
+    """Reconstruction in the rotated basis: n c[idx] (+ QJL term for keys,
+    coefficient ``qjl_coef``, default the Gaussian sqrt(pi/2)/d)."""
     idx = unpack_bits(codes, codebook.bits, d)
     out = np.asarray(norms, dtype=np.float64)[:, None] * codebook.centroids[idx]
     if signs is not None:
+        coef = qjl_scale(d) if qjl_coef is None else qjl_coef
         pm = 2.0 * unpack_bits(signs, 1, d) - 1.0
-        out = out + qjl_scale(d) * np.asarray(rnorms, dtype=np.float64)[:, None] * (pm @ qjl_S)
+        out = out + coef * np.asarray(rnorms, dtype=np.float64)[:, None] * (pm @ qjl_S)
     return out
 
 
-def dequantize(codes, norms, rotation, codebook, signs=None, rnorms=None, qjl_S=None):
+def dequantize(codes, norms, rotation, codebook, signs=None, rnorms=None, qjl_S=None, qjl_coef=None):
     """k_hat / v_hat in the original basis."""
     d = rotation.d
-    return rotation.inverse(dequantize_rotated(codes, norms, codebook, d, signs, rnorms, qjl_S))
+    return rotation.inverse(dequantize_rotated(codes, norms, codebook, d, signs, rnorms, qjl_S, qjl_coef))
 
 
-def qjl_inner_product(q: np.ndarray, r_norm: float, signs_pm: np.ndarray, S: np.ndarray) -> float:
-    """QJL estimate of <q, r> from the sketch: sqrt(pi/2)/m * ||r|| * <S q, sigma>
-    for S with m rows (m = d in the cache)."""
-    m = S.shape[0]
-    return qjl_scale(m) * r_norm * float(np.dot(S @ q, signs_pm))
+def qjl_reconstruct(r: np.ndarray, S: np.ndarray, coef: float) -> np.ndarray:
+    """The residual as the sketch gives it back: coef * ||r|| * S^T sign(S r)
+    (sign(0) = +1), for rows r."""
+    r = np.asarray(r, dtype=np.float64)
+    pm = np.where(r @ S.T >= 0.0, 1.0, -1.0)
+    return coef * np.linalg.norm(r, axis=-1, keepdims=True) * (pm @ S)
+
+
+def qjl_inner_product(q: np.ndarray, r_norm: float, signs_pm: np.ndarray, S: np.ndarray, coef=None) -> float:
+    """QJL estimate of <q, r> from the sketch: a * ||r|| * <S q, sigma>, with
+    a = sqrt(pi/2)/m for Gaussian S with m rows (m = d in the cache) unless
+    another coefficient is given."""
+    a = qjl_scale(S.shape[0]) if coef is None else coef
+    return a * r_norm * float(np.dot(S @ q, signs_pm))

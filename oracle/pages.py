@@ -16,7 +16,8 @@ the library implements, stated here independently of its source):
   page_bytes = roundup(256 + H_kv * head_bytes, 256)
   header, bytes [0, 64):
      0 u32 magic 0x564B5154 ("TQKV")     4 u16 format version (1)
-     6 u16 head_dim                        8 u8 key_bits   9 u8 key_qjl
+     6 u16 head_dim                        8 u8 key_bits   9 u8 key QJL (0 none,
+                                           1 Gaussian S, 2 orthogonal S)
     10 u8 value_bits                      11 u8 rotation (0 dense, 1 hadamard)
     12 u16 num_kv_heads                   14 u16 page_tokens
     16 u32 valid tokens in this page      20 u32 codebook version (1)
@@ -166,8 +167,9 @@ class PagedCache:
     """
 
     def __init__(self, lay: Layout, rotation, key_cb, value_cb, qjl_S, window, num_pages, batch,
-                 max_pages, rotation_kind=0, seed=0):
+                 max_pages, rotation_kind=0, seed=0, qjl_coef=None):
         self.lay, self.rot, self.kcb, self.vcb, self.S = lay, rotation, key_cb, value_cb, qjl_S
+        self.qjl_coef = codec.qjl_scale(lay.d) if qjl_coef is None else qjl_coef
         self.W = window
         self.pool = np.zeros((num_pages, lay.page_bytes), dtype=np.uint8)
         self.block_table = np.full((batch, max_pages), -1, dtype=np.int32)

@@ -10,7 +10,9 @@
   comparison").  Sylvester (natural) ordering.
 * QJL projection S: d x d i.i.d. N(0,1) entries, as in the paper's QJL
   definition quoted in "TurboQuant on a 16GB MacBook", section "The QJL
-  detective story"; stored as float32.
+  detective story"; stored as float32.  The variance-reduced variant from
+  the same section replaces it by an orthogonal matrix obtained by QR, here
+  the Haar construction of the dense rotation applied to the S draws.
 
 The random draws are inputs (they come from ``tq_inputs``); this module only
 does the arithmetic that turns them into the stored matrices.
@@ -98,6 +100,13 @@ class Rotation:
         return fwht(y) * self.eps / np.sqrt(self.d)
 
 
-def qjl_matrix(gauss_draws: np.ndarray, head_dim: int) -> np.ndarray:
-    """S: the draws rounded to float32, shape (d, d) (one row per sign bit)."""
-    return np.asarray(gauss_draws, dtype=np.float64).reshape(head_dim, head_dim).astype(np.float32).astype(np.float64)
+def qjl_matrix(gauss_draws: np.ndarray, head_dim: int, kind: str = "gaussian") -> np.ndarray:
+    """S, shape (d, d) (one row per sign bit), float32 values: the draws
+    themselves ("gaussian") or the Haar orthogonal matrix built from them
+    ("orthogonal")."""
+    g = np.asarray(gauss_draws, dtype=np.float64).reshape(head_dim, head_dim)
+    if kind == "gaussian":
+        return g.astype(np.float32).astype(np.float64)
+    if kind == "orthogonal":
+        return dense_rotation(g)
+    raise ValueError(kind)

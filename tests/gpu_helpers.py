@@ -25,7 +25,9 @@ def params_for(setup, flags=0):
     return tqa.make_params(flags=flags,
         head_dim=setup.d, key_bits=setup.bK, key_qjl=setup.qjl, value_bits=setup.bV,
         rotation=tqa.TQ_ROT_DENSE if setup.rotation == "dense" else tqa.TQ_ROT_HADAMARD,
-        num_q_heads=setup.Hq, num_kv_heads=setup.Hkv, page_tokens=setup.P, window=setup.W, seed=setup.seed)
+        num_q_heads=setup.Hq, num_kv_heads=setup.Hkv, page_tokens=setup.P, window=setup.W, seed=setup.seed,
+        qjl_kind=tqa.TQ_QJL_ORTHOGONAL if setup.qjl_kind == "orthogonal" else tqa.TQ_QJL_GAUSSIAN,
+        qjl_shrink=setup.qjl_shrink)
 
 
 def context_for(setup, flags=0):

@@ -3,6 +3,7 @@
 import numpy as np
 
 from oracle import codebook as cbm
+from oracle import codec
 from oracle import pages
 from oracle import rotation as rot
 import tq_inputs
@@ -10,8 +11,9 @@ import tq_inputs
 
 class Setup:
     def __init__(self, d=128, key_bits=3, key_qjl=1, value_bits=4, rotation="dense", seed=0,
-                 Hq=1, Hkv=1, P=256, W=128):
+                 Hq=1, Hkv=1, P=256, W=128, qjl_kind="gaussian", qjl_shrink=1.0):
         self.d, self.bK, self.qjl, self.bV = d, key_bits, key_qjl, value_bits
+        self.qjl_kind, self.qjl_shrink = qjl_kind, qjl_shrink
         self.rotation, self.seed, self.Hq, self.Hkv, self.P, self.W = rotation, seed, Hq, Hkv, P, W
         if rotation == "dense":
             self.rot_draws = tq_inputs.rotation_draws(seed, d)
@@ -21,14 +23,17 @@ class Setup:
         self.R = rot.Rotation(rotation, self.rot_draws, d)
         self.kcb = cbm.Codebook(key_bits, d)
         self.vcb = cbm.Codebook(value_bits, d)
-        self.S = rot.qjl_matrix(self.qjl_draws, d) if key_qjl else None
-        self.lay = pages.Layout(d, key_bits, key_qjl, value_bits, Hkv, P)
+        self.S = rot.qjl_matrix(self.qjl_draws, d, qjl_kind) if key_qjl else None
+        self.qjl_coef = codec.qjl_scale(d, qjl_kind, qjl_shrink)
+        # page-header QJL byte: 0 none, 1 Gaussian S, 2 orthogonal S
+        self.lay = pages.Layout(d, key_bits, (1 + (qjl_kind == "orthogonal")) if key_qjl else 0, value_bits, Hkv, P)
 
     def cache(self, batch, max_tokens):
         max_pages = max(1, -(-max(max_tokens - self.W, 0) // self.P))
         c = pages.PagedCache(self.lay, self.R, self.kcb, self.vcb, self.S, self.W,
                              num_pages=batch * max_pages + 3, batch=batch, max_pages=max_pages,
-                             rotation_kind=0 if self.rotation == "dense" else 1, seed=self.seed)
+                             rotation_kind=0 if self.rotation == "dense" else 1, seed=self.seed,
+                             qjl_coef=self.qjl_coef)
         # scatter pages over the pool (not in sequence order) so block tables matter
         perm = np.random.default_rng(123).permutation(batch * max_pages) + 3
         c.block_table[:] = perm.reshape(batch, max_pages)

@@ -55,7 +55,7 @@ def test_target_page_size(L):
 @pytest.mark.parametrize("field,value", [
     ("key_bits", 1), ("key_bits", 5), ("value_bits", 0), ("key_qjl", 2), ("rotation", 7),
     ("num_q_heads", 6), ("num_kv_heads", 0), ("page_tokens", 48), ("page_tokens", 2048), ("window", -1),
-    ("head_dim", 0),
+    ("head_dim", 0), ("qjl_kind", 2), ("qjl_shrink", 0.0), ("qjl_shrink", 5.0), ("qjl_shrink", float("nan")),
 ])
 def test_bad_params_rejected(L, field, value):
     p = tqa.make_params(num_q_heads=8, num_kv_heads=4)
@@ -103,6 +103,16 @@ def test_library_rotation_equals_oracle(L, seed):
     assert np.mean(diff == 0) > 0.999
     S = rot.qjl_matrix(tq_inputs.qjl_draws(seed, 128), 128)
     assert np.array_equal(t["qjl"].astype(np.float64), S)
+
+
+@pytest.mark.parametrize("seed", [0, 5])
+def test_library_orthogonal_qjl_equals_oracle(L, seed):
+    p = tqa.make_params(seed=seed, qjl_kind=tqa.TQ_QJL_ORTHOGONAL)
+    t = tqa.tq_host_tables(p, tq_inputs.rotation_draws(seed, 128), tq_inputs.qjl_draws(seed, 128))
+    S = rot.qjl_matrix(tq_inputs.qjl_draws(seed, 128), 128, "orthogonal")
+    diff = np.abs(t["qjl"].astype(np.float64) - S)
+    assert np.max(diff) <= 2.0 ** -30
+    assert np.mean(diff == 0) > 0.999
 
 
 def test_library_hadamard_signs(L):

@@ -103,7 +103,10 @@ def test_bulk_prefill_parity(name, kw, lens):
                 assert rel_close(out[b, hq], ref_o[b, hq]), (b, hq)
 
 
-def test_streaming_appends_match_bulk():
+@pytest.mark.parametrize("late_step", [5, 20, 30])
+def test_streaming_appends_match_bulk(late_step):
+    """Chunked appends (1 token, then late_step tokens: up to and beyond the
+    window, evictions spanning two 32-token groups) equal one bulk append."""
     s = Setup(Hq=4, Hkv=2, W=24, P=32)
     lens = [90, 30]
     ref = s.cache(2, 90)
@@ -115,7 +118,7 @@ def test_streaming_appends_match_bulk():
     d2 = upload_cache(s.cache(2, 90))
     t = 0
     while t < max(lens):
-        step = 1 if t < 40 else 5
+        step = 1 if t < 40 else late_step
         cnt = np.clip(np.asarray(lens) - t, 0, step)
         kk = np.ascontiguousarray(k[:, :, t:t + step])
         vv = np.ascontiguousarray(v[:, :, t:t + step])

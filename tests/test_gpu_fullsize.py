@@ -65,7 +65,7 @@ class GpuCache:
     def host(self):
         s = self.s
         c = pages.PagedCache(s.lay, s.R, s.kcb, s.vcb, s.S, s.W, num_pages=1, batch=1, max_pages=1,
-                             rotation_kind=0 if s.rotation == "dense" else 1, seed=s.seed)
+                             rotation_kind=0 if s.rotation == "dense" else 1, seed=s.seed, qjl_coef=s.qjl_coef)
         c.pool = self.pool.cpu().numpy().reshape(self.npages, self.pb)
         c.block_table = self.bt.cpu().numpy()
         c.seq_lens = self.sl.cpu().numpy()

@@ -25,9 +25,12 @@ def _q(setup, B, seed=1):
     return tq_inputs.queries(seed, (B, setup.Hq, setup.d))
 
 
-@pytest.mark.parametrize("rotation,bK,qjl,bV", [("dense", 3, 1, 4), ("hadamard", 2, 1, 2), ("dense", 4, 0, 3)])
-def test_two_routes_agree(rotation, bK, qjl, bV):
-    s = Setup(key_bits=bK, key_qjl=qjl, value_bits=bV, rotation=rotation, Hq=4, Hkv=2, P=64, W=32)
+@pytest.mark.parametrize("rotation,bK,qjl,bV,qk,shrink", [
+    ("dense", 3, 1, 4, "gaussian", 1.0), ("hadamard", 2, 1, 2, "gaussian", 1.0), ("dense", 4, 0, 3, "gaussian", 1.0),
+    ("dense", 3, 1, 4, "orthogonal", 2 / np.pi), ("hadamard", 3, 1, 4, "orthogonal", 0.7)])
+def test_two_routes_agree(rotation, bK, qjl, bV, qk, shrink):
+    s = Setup(key_bits=bK, key_qjl=qjl, value_bits=bV, rotation=rotation, Hq=4, Hkv=2, P=64, W=32,
+              qjl_kind=qk, qjl_shrink=shrink)
     lens = [300, 45, 32, 1]
     c = s.cache(len(lens), max(lens))
     fill(s, c, lens)
