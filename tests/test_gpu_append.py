@@ -74,6 +74,7 @@ CASES = [
     ("gqa_ragged_P64", dict(Hq=8, Hkv=2, W=40, P=64), [300, 41, 40, 7, 0, 129]),
     ("hadamard_k2v2_W0", dict(Hq=8, Hkv=1, key_bits=2, value_bits=2, rotation="hadamard", W=0, P=32), [100, 33]),
     ("k4_noqjl_v3", dict(Hq=2, Hkv=2, key_bits=4, key_qjl=0, value_bits=3, W=16, P=32), [77, 16, 15]),
+    ("orthoS_shrink", dict(Hq=4, Hkv=2, W=32, P=64, qjl_kind="orthogonal", qjl_shrink=2 / np.pi), [200, 33]),
 ]
 
 

@@ -39,6 +39,9 @@ CASES = [
     ("gqa8_2bit_hadamard", dict(Hq=8, Hkv=1, key_bits=2, value_bits=2, rotation="hadamard", W=128), [900, 300]),
     ("k4_noqjl_v3_P64", dict(Hq=2, Hkv=2, key_bits=4, key_qjl=0, value_bits=3, P=64, W=16), [333, 64, 17]),
     ("mha_k2_v4_W0_P32", dict(Hq=4, Hkv=4, key_bits=2, value_bits=4, P=32, W=0), [95, 32, 31]),
+    ("gqa4_orthoS_shrink", dict(Hq=8, Hkv=2, W=64, qjl_kind="orthogonal", qjl_shrink=2 / np.pi), [600, 70, 1]),
+    ("gqa8_orthoS_hadamard", dict(Hq=16, Hkv=2, key_bits=2, value_bits=2, rotation="hadamard", W=32,
+                                  qjl_kind="orthogonal", qjl_shrink=0.7), [500, 33]),
 ]
 
 

@@ -37,15 +37,16 @@ def _gpu_encode(ctx, kind, x16, qjl, dtype=torch.float16):
     return cpu(codes), cpu(norms), cpu(signs), cpu(rnorms)
 
 
+@pytest.mark.parametrize("qjl_kind", ["gaussian", "orthogonal"])
 @pytest.mark.parametrize("rotation", ["dense", "hadamard"])
 @pytest.mark.parametrize("bK,bV", [(3, 4), (2, 2), (4, 3)])
 @pytest.mark.parametrize("n", [1024, 77])
-def test_encode_parity(rotation, bK, bV, n):
-    s = Setup(key_bits=bK, value_bits=bV, rotation=rotation)
+def test_encode_parity(rotation, bK, bV, n, qjl_kind):
+    s = Setup(key_bits=bK, value_bits=bV, rotation=rotation, qjl_kind=qjl_kind)
     ctx = context_for(s)
     x16 = _inputs(n)
     x = x16.astype(np.float64)
-    print(f"case rotation={rotation} bK={bK} bV={bV} n={n}", flush=True)
+    print(f"case rotation={rotation} bK={bK} bV={bV} n={n} qjl={qjl_kind}", flush=True)
     # keys with QJL
     codes, norms, signs, rnorms = _gpu_encode(ctx, tqa.TQ_KIND_KEY, x16, True)
     ref = codec.encode(x, s.R, s.kcb, s.S)
