@@ -139,6 +139,18 @@ TQ_API int tq_destroy(tq_ctx* ctx);
 /* Bytes of one page for these params (see the page format above); <0 on bad params. */
 TQ_API int64_t tq_page_bytes(const tq_params* params);
 
+/* Dequantise n flat records (device pointers) back to vectors ("aither-
+ * kvcache" README, "Algorithm", last step; "TurboQuant on a 16GB MacBook",
+ * "The QJL detective story" for the key correction):
+ *   out[i] = Pi^T ( norms[i] c[codes[i]] + a rnorms[i] S^T (2 sigma_i - 1) )
+ * with the correction only for keys with key_qjl and a the context's QJL
+ * coefficient: qjl_shrink * sqrt(pi/2)/d for Gaussian S, qjl_shrink *
+ * sqrt(pi/2)/sqrt(d) for orthogonal S.  Record layouts as in
+ * tq_encode; out: [n][d] f32.  For quality measurements against exact
+ * attention; the decode path never dequantises. */
+TQ_API int tq_decode(const tq_ctx* ctx, int kind, const uint8_t* codes, const uint8_t* signs, const float* norms,
+                     const float* rnorms, int64_t n, float* out, void* stream);
+
 /* Encode n vectors (device pointers) into flat records:
  *   x: [n][row_stride] elements of dtype (F16, BF16 or F32), first d used;
  *   codes: [n][d*b/8] u8 LSB-first, b = key_bits or value_bits by kind;

@@ -29,7 +29,7 @@ TQ_FLAG_VALU_SCAN = 1
 EXPORTED = [
     "tq_host_tables", "tq_codebook_init", "tq_destroy", "tq_page_bytes", "tq_encode",
     "tq_append_page", "tq_decode_workspace_bytes", "tq_decode_attn", "tq_get_status", "tq_strerror",
-    "tq_profile_begin", "tq_profile_end",
+    "tq_profile_begin", "tq_profile_end", "tq_decode",
 ]
 
 
@@ -77,6 +77,7 @@ def lib():
         "tq_destroy": (i32, [P]),
         "tq_page_bytes": (i64, [pp]),
         "tq_encode": (i32, [P, i32, P, i32, i64, i64, P, P, P, P, P]),
+        "tq_decode": (i32, [P, i32, P, P, P, P, i64, P, P]),
         "tq_append_page": (i32, [P, P, i64, P, i32, i32, P, P, P, i32, P, P, P, P]),
         "tq_decode_workspace_bytes": (i64, [P, i32, i32, i32]),
         "tq_decode_attn": (i32, [P, P, i32, P, i64, P, i32, i32, P, P, P, f32, P, P, sz, i32, P, i64, P]),
@@ -194,6 +195,15 @@ def tq_encode(ctx, kind, x, codes, norms, signs=None, rnorms=None, stream=None):
     rc = lib().tq_encode(ctx.handle, kind, _ptr(x), _dtype_code(x), n, x.stride(0), _ptr(codes), _ptr(signs),
                          _ptr(norms), _ptr(rnorms), _stream(stream))
     _check(rc, "tq_encode")
+
+
+def tq_decode(ctx, kind, codes, norms, out, signs=None, rnorms=None, stream=None):
+    """Dequantise n flat records (cuda tensors as written by tq_encode) into
+    out: [n, d] float32."""
+    n = codes.shape[0]
+    rc = lib().tq_decode(ctx.handle, kind, _ptr(codes), _ptr(signs), _ptr(norms), _ptr(rnorms), n, _ptr(out),
+                         _stream(stream))
+    _check(rc, "tq_decode")
 
 
 def tq_append_page(ctx, page_pool, block_table, seq_lens, k_new, v_new, k_win, v_win, new_counts=None,

@@ -265,6 +265,20 @@ TQ_API int tq_encode(const tq_ctx* c, int kind, const void* x, int dtype, int64_
   return tq::launch_encode(c, kind, dtype, a, stream) == 0 ? TQ_OK : TQ_ERR_HIP;
 }
 
+TQ_API int tq_decode(const tq_ctx* c, int kind, const uint8_t* codes, const uint8_t* signs, const float* norms,
+                     const float* rnorms, int64_t n, float* out, void* stream) {
+  if (!c || (kind != TQ_KIND_KEY && kind != TQ_KIND_VALUE) || n < 0) return TQ_ERR_INVALID_ARG;
+  if (n == 0) return TQ_OK;
+  const bool qjl = kind == TQ_KIND_KEY && c->p.key_qjl;
+  if (!codes || !norms || !out || (qjl && (!signs || !rnorms))) return TQ_ERR_INVALID_ARG;
+  if (!aligned(codes, 4) || !aligned(norms, 4) || !aligned(out, 16) || (qjl && (!aligned(signs, 4) || !aligned(rnorms, 4))))
+    return TQ_ERR_INVALID_ARG;
+  if (n > (int64_t(1) << 40)) return TQ_ERR_INVALID_ARG;
+  return tq::launch_dequant(c, kind, codes, qjl ? signs : nullptr, norms, qjl ? rnorms : nullptr, n, out, stream) == 0
+             ? TQ_OK
+             : TQ_ERR_HIP;
+}
+
 TQ_API int tq_append_page(const tq_ctx* c, uint8_t* pool, int64_t num_pages, const int32_t* block_table,
                           int max_pages, int batch, int32_t* seq_lens, const uint16_t* k_new, const uint16_t* v_new,
                           int n_new, const int32_t* new_counts, uint16_t* k_win, uint16_t* v_win, void* stream) {

@@ -127,6 +127,8 @@ int launch_encode(const tq_ctx* ctx, int kind, int dtype, const EncodeArgs& a, v
 int launch_encode_mma(const tq_ctx* ctx, int kind, int dtype, const EncodeArgs& a, void* stream);
 int launch_append(const tq_ctx* ctx, const AppendArgs& a, void* stream);
 int launch_decode(const tq_ctx* ctx, const DecodeArgs& a, void* stream);
+int launch_dequant(const tq_ctx* ctx, int kind, const uint8_t* codes, const uint8_t* signs, const float* norms,
+                   const float* rnorms, int64_t n, float* out, void* stream);
 // The scan kernel a context's decode launches (MFMA or vector-ALU variant),
 // for occupancy queries; nullptr for an unsupported parameter set.
 const void* scan_mfma_kernel_ptr(const tq_ctx* ctx);
