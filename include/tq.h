@@ -210,6 +210,18 @@ TQ_API int tq_decode_attn(const tq_ctx* ctx, const void* q, int q_dtype, const u
 TQ_API int tq_profile_begin(tq_ctx* ctx, int max_calls);
 TQ_API int tq_profile_end(tq_ctx* ctx, double* scan_ms_total, int* calls);
 
+/* Streaming-read reference for the bandwidth roofline (no context needed):
+ * reads the whole device buffer `buf` (`bytes` > 0, a multiple of 16,
+ * 16-byte aligned, caller-owned) with coalesced 16-byte loads and an XOR fold,
+ * `reps` times (1..1000) on `stream`, each launch bracketed by HIP events, and
+ * writes the fastest launch's time in milliseconds to *best_ms (host).
+ * `sink` is a caller-owned 4-byte device word the kernel may write (once in
+ * 2^32 fold values).  Synchronises on the events.  The device's read rate is
+ * bytes / best_ms; it is the practical ceiling the scan's rate is compared
+ * with, beside the nominal HBM peak.  Returns TQ_ERR_INVALID_ARG for bad
+ * arguments, TQ_ERR_HIP if a launch or an event fails. */
+TQ_API int tq_read_probe(const void* buf, int64_t bytes, uint32_t* sink, int reps, double* best_ms, void* stream);
+
 /* Read and clear the device status word (synchronises the context's device). */
 TQ_API int tq_get_status(tq_ctx* ctx, int* code);
 

@@ -29,7 +29,7 @@ TQ_FLAG_VALU_SCAN = 1
 EXPORTED = [
     "tq_host_tables", "tq_codebook_init", "tq_destroy", "tq_page_bytes", "tq_encode",
     "tq_append_page", "tq_decode_workspace_bytes", "tq_decode_attn", "tq_get_status", "tq_strerror",
-    "tq_profile_begin", "tq_profile_end", "tq_decode",
+    "tq_profile_begin", "tq_profile_end", "tq_decode", "tq_read_probe",
 ]
 
 
@@ -85,6 +85,7 @@ def lib():
         "tq_strerror": (ctypes.c_char_p, [i32]),
         "tq_profile_begin": (i32, [P, i32]),
         "tq_profile_end": (i32, [P, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int)]),
+        "tq_read_probe": (i32, [P, i64, P, i32, ctypes.POINTER(ctypes.c_double), P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(L, name)
@@ -255,3 +256,13 @@ def tq_profile_end(ctx):
     n = ctypes.c_int(0)
     _check(lib().tq_profile_end(ctx.handle, ctypes.byref(ms), ctypes.byref(n)), "tq_profile_end")
     return ms.value, n.value
+
+
+def tq_read_probe(buf, sink, reps=5, stream=None):
+    """Fastest of `reps` streaming reads of the device tensor `buf` (bytes a
+    multiple of 16), in milliseconds; `sink` is a 4-byte device tensor."""
+    ms = ctypes.c_double(0.0)
+    nbytes = buf.numel() * buf.element_size()
+    _check(lib().tq_read_probe(_ptr(buf), nbytes, _ptr(sink), reps, ctypes.byref(ms), _stream(stream)),
+           "tq_read_probe")
+    return ms.value

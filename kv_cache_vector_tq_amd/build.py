@@ -21,7 +21,7 @@ COMMON = [
     # packed FP32 instructions are kept out of every kernel
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
 ]
-SOURCES = ["tables.cpp", "tq_api.cpp", "encode.hip", "encode_mma.hip", "decode.hip", "decode_mfma.hip", "dequant.hip"]
+SOURCES = ["tables.cpp", "tq_api.cpp", "encode.hip", "encode_mma.hip", "decode.hip", "decode_mfma.hip", "dequant.hip", "probe.hip"]
 
 
 def _hipcc():

@@ -526,6 +526,8 @@ const void* scan_mfma_kernel_ptr(const tq_ctx* c) {
   }
 }
 
+int scan_mfma_threads(const tq_ctx*) { return kScanThreads; }
+
 int launch_scan_mfma(const tq_ctx* c, const DecodeArgs& a, const KParams& k, void* stream) {
   const void* f = scan_mfma_kernel_ptr(c);
   if (!f) return 1;

@@ -181,9 +181,11 @@ TQ_API int tq_codebook_init(tq_ctx** out, const tq_params* p, const double* rot_
             hipMemcpyAsync(base + 3 * mat, ST.data(), mat, hipMemcpyHostToDevice, s) == hipSuccess &&
             hipMemsetAsync(base + 4 * mat, 0, 256, s) == hipSuccess && hipStreamSynchronize(s) == hipSuccess;
   // resident scan work-groups per device, for the automatic split count
-  const void* kf = (p->flags & TQ_FLAG_VALU_SCAN) ? tq::scan_valu_kernel_ptr(c) : tq::scan_mfma_kernel_ptr(c);
+  const bool valu = (p->flags & TQ_FLAG_VALU_SCAN) != 0;
+  const void* kf = valu ? tq::scan_valu_kernel_ptr(c) : tq::scan_mfma_kernel_ptr(c);
+  const int threads = valu ? tq::kScanThreads : tq::scan_mfma_threads(c);
   int per_cu = 0, cus = 0;
-  ok = ok && kf && hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kf, tq::kScanThreads, 0) == hipSuccess &&
+  ok = ok && kf && hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kf, threads, 0) == hipSuccess &&
        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, c->device) == hipSuccess;
   if (!ok) {
     (void)hipFree(c->dmem);

@@ -133,6 +133,8 @@ int launch_dequant(const tq_ctx* ctx, int kind, const uint8_t* codes, const uint
 // for occupancy queries; nullptr for an unsupported parameter set.
 const void* scan_mfma_kernel_ptr(const tq_ctx* ctx);
 const void* scan_valu_kernel_ptr(const tq_ctx* ctx);
+// Threads per work-group of the MFMA scan for this context's parameters.
+int scan_mfma_threads(const tq_ctx* ctx);
 // Events to record around the scan kernel of this call (nullptr when not profiling).
 void* profile_slot(const tq_ctx* ctx, int which);
 

@@ -81,6 +81,20 @@ def test_null_context_and_pointers(L):
     assert L.tq_strerror(tqa.TQ_ERR_WORKSPACE) == b"workspace too small"
 
 
+def test_read_probe_rejects_bad_arguments(L):
+    """tq_read_probe validates on the host before any HIP call (buffer,
+    sink and result pointers, size a positive multiple of 16, 16-byte
+    alignment, 1..1000 repetitions)."""
+    ms = ctypes.c_double(0.0)
+    good, sink = 1 << 20, 1 << 21  # aligned stand-in addresses; never dereferenced here
+    cases = [(None, 4096, sink, 1), (good, 4096, None, 1), (good, 0, sink, 1), (good, -16, sink, 1),
+             (good, 4100, sink, 1), (good + 8, 4096, sink, 1), (good, 4096, sink, 0), (good, 4096, sink, 1001)]
+    for buf, nbytes, snk, reps in cases:
+        assert L.tq_read_probe(buf, nbytes, snk, reps, ctypes.byref(ms), None) == tqa.TQ_ERR_INVALID_ARG, \
+            (buf, nbytes, snk, reps)
+    assert L.tq_read_probe(good, 4096, sink, 1, None, None) == tqa.TQ_ERR_INVALID_ARG
+
+
 @pytest.mark.parametrize("bits", [2, 3, 4])
 def test_library_codebook_equals_oracle(L, bits):
     p = tqa.make_params(key_bits=bits, value_bits=bits)
