@@ -17,7 +17,8 @@
 //  * packed codes are expanded to fp16 B operands through LDS lookup tables
 //    (a 6- or 8-bit slice of the code stream yields 2 or 4 fp16 values).
 // Each wave streams 32-token chunks (one value group) with its own online
-// softmax state; the four waves of a work-group merge at the end.
+// softmax state; the waves of a work-group (four, or eight with the wide
+// table below) merge at the end.
 #include "decode_common.h"
 #include "device_common.h"
 
@@ -31,9 +32,9 @@ typedef uint32_t u3 __attribute__((ext_vector_type(3)));
 typedef uint32_t u2 __attribute__((ext_vector_type(2)));
 
 constexpr int kChunk = 32;                   // tokens per wave iteration (one value group)
-constexpr int kWaves = kScanThreads / 64;
 constexpr float kLazy = 8.0f;                // log2 headroom before the running max moves
 constexpr uint32_t kRsrcWord3 = 0x00020000;  // raw buffer descriptor flags (gfx9 family)
+constexpr int kStream = 2;                   // buffer-load cache policy: non-temporal (pages are read once)
 
 __device__ inline uint32_t h_bits(float x) {
   return static_cast<uint32_t>(__builtin_bit_cast(uint16_t, static_cast<_Float16>(x)));
@@ -101,11 +102,11 @@ struct PairLut {
   static constexpr int kWords = kEntries * kCopies;
 };
 
-template <int B>
+template <int B, int NT>
 __device__ void build_pair_lut(uint32_t* lut, const float* cen, int tid) {
   using L = PairLut<B>;
   constexpr int m = (1 << B) - 1;
-  for (int w = tid; w < L::kWords; w += kScanThreads) {
+  for (int w = tid; w < L::kWords; w += NT) {
     const int e = w / L::kCopies;
     lut[w] = h_bits(cen[e & m]) | (h_bits(cen[(e >> B) & m]) << 16);
   }
@@ -129,6 +130,46 @@ __device__ inline u4 dec8(uint32_t x, const uint32_t* lut) {
 __device__ inline u4 dec_signs8(uint32_t x, const u2* lutN) {
   const u2 a = lutN[x & 15u], c = lutN[(x >> 4) & 15u];
   return u4{a.x, a.y, c.x, c.y};
+}
+
+// Work-group shape.  With 4-bit values (and at most four query heads per KV
+// head, for the LDS budget) one 64 KB "wide" table serves both the value
+// codes and the sign bits, addressed straight from a byte of the code word:
+// row e (256 bytes) holds the value pair e in 32 copies (words 64e + c, lane
+// reads copy lane % 32: a half-wave touches 32 distinct banks) and, in its
+// second half, the eight +-1 fp16 values of sign byte e in 8 copies of 16
+// bytes (lane reads copy lane % 8, one 16-byte read per 8 signs).  One v_perm
+// forms each address (byte e into bits 8..15, the lane's copy offset into
+// bits 0..7) where the narrow tables take a shift and a mask-or.  Eight waves
+// share the table so that two work-groups still fit in a CU.
+constexpr bool wide_scan(int G, int BV) { return BV == 4 && G <= 4; }
+constexpr int scan_threads(bool wide) { return wide ? 512 : 256; }
+
+template <int G, int BV>
+struct ScanShape {
+  static constexpr bool kWide = wide_scan(G, BV);
+  static constexpr int kThreads = scan_threads(kWide);
+  static constexpr int kWaves = kThreads / 64;
+  static constexpr int kLutWords = kWide ? 256 * 64 : PairLut<BV>::kWords;
+};
+
+// address of byte K of x in a 256-byte-row table, plus the lane's copy offset
+template <int K>
+__device__ inline uint32_t row_addr(uint32_t x, uint32_t base) {
+  return __builtin_amdgcn_perm(x, base, 0x0C0C0000u | ((4u + K) << 8));
+}
+__device__ inline uint32_t lds_word(const uint32_t* t, uint32_t byte_addr) {
+  return *reinterpret_cast<const uint32_t*>(reinterpret_cast<const char*>(t) + byte_addr);
+}
+// 8 consecutive 4-bit codes -> 8 fp16 values from the wide table
+__device__ inline u4 dec8_wide(uint32_t x, const uint32_t* t, uint32_t vbase) {
+  return u4{lds_word(t, row_addr<0>(x, vbase)), lds_word(t, row_addr<1>(x, vbase)),
+            lds_word(t, row_addr<2>(x, vbase)), lds_word(t, row_addr<3>(x, vbase))};
+}
+// sign byte K of x -> 8 fp16 +-1 from the wide table
+template <int K>
+__device__ inline u4 dec_signs_wide(uint32_t x, const uint32_t* t, uint32_t sbase) {
+  return *reinterpret_cast<const u4*>(reinterpret_cast<const char*>(t) + row_addr<K>(x, sbase));
 }
 
 // Codes 8i .. 8i+7 of a lane's 32-code key slice held in B words.
@@ -167,12 +208,19 @@ struct Meta {
 // hi, 1: remainder); the product's rows 4kg + r land in lane group kg, so a
 // lane sees query 2kg + i as rows i (hi) and i + 2 (remainder) and adds them.
 template <int G, int BK, int BV, bool QJL>
-__global__ __launch_bounds__(kScanThreads, 4) void scan_mfma_kernel(DecodeArgs a, DevTables t, Codebooks cb,
-                                                                 KParams k) {
-  // one table when keys and values share a bit width (same codebook)
-  __shared__ uint32_t lutV[PairLut<BV>::kWords];
-  __shared__ uint32_t lutKown[BK == BV ? 1 : PairLut<BK>::kWords];
-  __shared__ u2 lutN[16];
+__global__ __launch_bounds__((ScanShape<G, BV>::kThreads), 4) void scan_mfma_kernel(DecodeArgs a, DevTables t,
+                                                                                   Codebooks cb, KParams k) {
+  using Sh = ScanShape<G, BV>;
+  constexpr bool kWide = Sh::kWide;
+  constexpr int kThreads = Sh::kThreads, kWaves = Sh::kWaves;
+  // One array: the key table (absent when keys and values share a bit width,
+  // hence a codebook) first, so that every table address stays within the
+  // 16-bit immediate offset of the LDS instructions.
+  constexpr int kKeyWords = BK == BV ? 0 : PairLut<BK>::kWords;
+  __shared__ uint32_t luts[kKeyWords + Sh::kLutWords];
+  uint32_t* const lutKown = luts;
+  uint32_t* const lutV = luts + kKeyWords;
+  __shared__ u2 lutN[kWide ? 1 : 16];
   __shared__ float pv[kWaves][2][G][kChunk];  // softmax weights x value norms, two chunks in flight
   __shared__ float wm[kWaves][G], wl[kWaves][G];
   __shared__ float red[G][kD];
@@ -198,7 +246,7 @@ __global__ __launch_bounds__(kScanThreads, 4) void scan_mfma_kernel(DecodeArgs a
       a.pm[pidx + tid] = -INFINITY;
       a.pl[pidx + tid] = 0.0f;
     }
-    for (int i = tid; i < G * kD; i += kScanThreads) a.pacc[pidx * kD + i] = 0.0f;
+    for (int i = tid; i < G * kD; i += kThreads) a.pacc[pidx * kD + i] = 0.0f;
     return;
   }
   // codebooks to LDS (no dynamic indexing of kernel arguments), then the tables
@@ -214,9 +262,23 @@ __global__ __launch_bounds__(kScanThreads, 4) void scan_mfma_kernel(DecodeArgs a
     cvv[tid] = vv;
   }
   __syncthreads();
-  build_pair_lut<BV>(lutV, cvv, tid);
-  if constexpr (BK != BV) build_pair_lut<BK>(lutKown, ck, tid);
-  if (tid < 16) {
+  if constexpr (kWide) {
+    for (int w = tid; w < Sh::kLutWords; w += kThreads) {
+      const int e = w >> 6, c = w & 63;
+      uint32_t v;
+      if (c < 32) {
+        v = h_bits(cvv[e & 15]) | (h_bits(cvv[e >> 4]) << 16);
+      } else {  // word j of sign byte e: bits 2j (low half) and 2j + 1
+        const int j = c & 3;
+        v = ((e >> (2 * j)) & 1 ? 0x3C00u : 0xBC00u) | (((e >> (2 * j + 1)) & 1 ? 0x3C00u : 0xBC00u) << 16);
+      }
+      lutV[w] = v;
+    }
+  } else {
+    build_pair_lut<BV, kThreads>(lutV, cvv, tid);
+  }
+  if constexpr (BK != BV) build_pair_lut<BK, kThreads>(lutKown, ck, tid);
+  if (!kWide && tid < 16) {
     const int e = tid;
     lutN[e] = u2{(e & 1 ? 0x3C00u : 0xBC00u) | ((e & 2 ? 0x3C00u : 0xBC00u) << 16),
                  (e & 4 ? 0x3C00u : 0xBC00u) | ((e & 8 ? 0x3C00u : 0xBC00u) << 16)};
@@ -224,6 +286,7 @@ __global__ __launch_bounds__(kScanThreads, 4) void scan_mfma_kernel(DecodeArgs a
   const uint32_t* lutK = BK == BV ? lutV : lutKown;
   const uint32_t* lutKl = lutK + (PairLut<BK>::kCopies > 1 ? (tid & 31) : 0);
   const uint32_t* lutVl = lutV + (PairLut<BV>::kCopies > 1 ? (tid & 31) : 0);
+  const uint32_t vbase = static_cast<uint32_t>(tid & 31) * 4u, sbase = 128u + static_cast<uint32_t>(tid & 7) * 16u;
   // A operands of the key products: lane group kg covers coordinates
   // 32kg .. 32kg+31, MFMA i the 8 starting at 32kg + 8i.
   const int64_t qrow = (static_cast<int64_t>(b) * k.Hq + static_cast<int64_t>(h) * G) * kD;
@@ -271,6 +334,15 @@ __global__ __launch_bounds__(kScanThreads, 4) void scan_mfma_kernel(DecodeArgs a
   const uint32_t o_vw = static_cast<uint32_t>((vw0 * kD + 8 * n) * 4);
   const uint32_t o_vw2 = static_cast<uint32_t>(((vtwo ? vw0 + 1 : vw0) * kD + 8 * n) * 4);
 
+  // page ids of this split held in one register, 64 at a time: lane j has
+  // the id of page pbase + j, read with v_readlane (no scalar load, whose
+  // out-of-order return would make every later LDS wait a full drain)
+  int pbase = pb;
+  auto load_pids = [&](int base) {
+    const int j = base + l;
+    return j < pe ? a.block_table[static_cast<int64_t>(b) * a.max_pages + j] : 0;
+  };
+  int pids = load_pids(pb);
   auto meta = [&](int i, Meta& m) {
     const int c = wave + i * kWaves;
     const int tok0 = c * kChunk;
@@ -279,7 +351,11 @@ __global__ __launch_bounds__(kScanThreads, 4) void scan_mfma_kernel(DecodeArgs a
     m.s0 = m.gi * kChunk;
     const int rem = tot - tok0;
     m.pos0 = pg * k.P + m.s0;
-    const int pid0 = a.block_table[static_cast<int64_t>(b) * a.max_pages + pg];
+    if (pg - pbase >= 64) {
+      pbase += (pg - pbase) / 64 * 64;
+      pids = load_pids(pbase);
+    }
+    const int pid0 = __builtin_amdgcn_readlane(pids, pg - pbase);
     const bool bad = pid0 < 0 || pid0 >= a.num_pages;  // flagged, then page 0 is read and the chunk masked
     if (bad && l == 0) atomicOr(t.status, TQ_STATUS_BAD_PAGE);
     m.ntok = __builtin_amdgcn_readfirstlane(bad ? 0 : (rem < kChunk ? rem : kChunk));
@@ -289,44 +365,44 @@ __global__ __launch_bounds__(kScanThreads, 4) void scan_mfma_kernel(DecodeArgs a
   };
   auto loadK = [&](const Meta& m, KBuf<BK>& d) {
     const int so_kn = static_cast<int>(k.k_norm) + 4 * m.s0;
-    d.kn[0] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(m.rs, o_tok0, so_kn, 0));
-    d.kn[1] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(m.rs, o_tok1, so_kn, 0));
+    d.kn[0] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(m.rs, o_tok0, so_kn, kStream));
+    d.kn[1] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(m.rs, o_tok1, so_kn, kStream));
     if constexpr (QJL) {
       const int so_rn = static_cast<int>(k.k_rnorm) + 4 * m.s0;
-      d.rn[0] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(m.rs, o_tok0, so_rn, 0));
-      d.rn[1] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(m.rs, o_tok1, so_rn, 0));
+      d.rn[0] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(m.rs, o_tok0, so_rn, kStream));
+      d.rn[1] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(m.rs, o_tok1, so_rn, kStream));
       const int so_sg = static_cast<int>(k.k_signs) + 16 * m.s0;
-      d.sg[0] = __builtin_amdgcn_raw_buffer_load_b32(m.rs, o_sg0, so_sg, 0);
-      d.sg[1] = __builtin_amdgcn_raw_buffer_load_b32(m.rs, o_sg1, so_sg, 0);
+      d.sg[0] = __builtin_amdgcn_raw_buffer_load_b32(m.rs, o_sg0, so_sg, kStream);
+      d.sg[1] = __builtin_amdgcn_raw_buffer_load_b32(m.rs, o_sg1, so_sg, kStream);
     }
     const int so_vn = static_cast<int>(k.v_norm) + 4 * m.s0;
-    d.vn[0] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(m.rs, o_tok0, so_vn, 0));
-    d.vn[1] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(m.rs, o_tok1, so_vn, 0));
+    d.vn[0] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(m.rs, o_tok0, so_vn, kStream));
+    d.vn[1] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(m.rs, o_tok1, so_vn, kStream));
     const int so_kc = static_cast<int>(k.k_codes) + 16 * BK * m.s0;
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt) {
       const uint32_t o = tt ? o_kc1 : o_kc0;
       if constexpr (BK == 4) {
-        const u4 v = __builtin_amdgcn_raw_buffer_load_b128(m.rs, o, so_kc, 0);
+        const u4 v = __builtin_amdgcn_raw_buffer_load_b128(m.rs, o, so_kc, kStream);
         d.kc[tt][0] = v.x; d.kc[tt][1] = v.y; d.kc[tt][2] = v.z; d.kc[tt][3] = v.w;
       } else if constexpr (BK == 3) {
-        const u3 v = __builtin_amdgcn_raw_buffer_load_b96(m.rs, o, so_kc, 0);
+        const u3 v = __builtin_amdgcn_raw_buffer_load_b96(m.rs, o, so_kc, kStream);
         d.kc[tt][0] = v.x; d.kc[tt][1] = v.y; d.kc[tt][2] = v.z;
       } else {
-        const u2 v = __builtin_amdgcn_raw_buffer_load_b64(m.rs, o, so_kc, 0);
+        const u2 v = __builtin_amdgcn_raw_buffer_load_b64(m.rs, o, so_kc, kStream);
         d.kc[tt][0] = v.x; d.kc[tt][1] = v.y;
       }
     }
   };
   auto loadV = [&](const Meta& m, VBuf<BV>& d) {
     const int so_vw = static_cast<int>(k.v_codes) + m.gi * BV * kD * 4;
-    const u4 x0 = __builtin_amdgcn_raw_buffer_load_b128(m.rs, o_vw, so_vw, 0);
-    const u4 x1 = __builtin_amdgcn_raw_buffer_load_b128(m.rs, o_vw + 16u, so_vw, 0);
+    const u4 x0 = __builtin_amdgcn_raw_buffer_load_b128(m.rs, o_vw, so_vw, kStream);
+    const u4 x1 = __builtin_amdgcn_raw_buffer_load_b128(m.rs, o_vw + 16u, so_vw, kStream);
     d.vw[0] = x0.x; d.vw[1] = x0.y; d.vw[2] = x0.z; d.vw[3] = x0.w;
     d.vw[4] = x1.x; d.vw[5] = x1.y; d.vw[6] = x1.z; d.vw[7] = x1.w;
     if constexpr (BV == 3) {
-      const u4 y0 = __builtin_amdgcn_raw_buffer_load_b128(m.rs, o_vw2, so_vw, 0);
-      const u4 y1 = __builtin_amdgcn_raw_buffer_load_b128(m.rs, o_vw2 + 16u, so_vw, 0);
+      const u4 y0 = __builtin_amdgcn_raw_buffer_load_b128(m.rs, o_vw2, so_vw, kStream);
+      const u4 y1 = __builtin_amdgcn_raw_buffer_load_b128(m.rs, o_vw2 + 16u, so_vw, kStream);
       d.vw2[0] = y0.x; d.vw2[1] = y0.y; d.vw2[2] = y0.z; d.vw2[3] = y0.w;
       d.vw2[4] = y1.x; d.vw2[5] = y1.y; d.vw2[6] = y1.z; d.vw2[7] = y1.w;
     }
@@ -342,8 +418,18 @@ __global__ __launch_bounds__(kScanThreads, 4) void scan_mfma_kernel(DecodeArgs a
       f4 dm = f4{0.0f, 0.0f, 0.0f, 0.0f}, dq = f4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        dm = mfma(aq[i], dec8<BK>(key_slice<BK>(d.kc[tt], i), lutKl), dm);
-        if constexpr (QJL) dq = mfma(ap[i], dec_signs8(d.sg[tt] >> (8 * i), lutN), dq);
+        if constexpr (kWide && BK == 4) dm = mfma(aq[i], dec8_wide(d.kc[tt][i], lutV, vbase), dm);
+        else dm = mfma(aq[i], dec8<BK>(key_slice<BK>(d.kc[tt], i), lutKl), dm);
+        if constexpr (QJL && kWide) {
+          const uint32_t sgw = d.sg[tt];
+          const u4 sb = i == 0 ? dec_signs_wide<0>(sgw, lutV, sbase)
+                        : i == 1 ? dec_signs_wide<1>(sgw, lutV, sbase)
+                        : i == 2 ? dec_signs_wide<2>(sgw, lutV, sbase)
+                                 : dec_signs_wide<3>(sgw, lutV, sbase);
+          dq = mfma(ap[i], sb, dq);
+        } else if constexpr (QJL) {
+          dq = mfma(ap[i], dec_signs8(d.sg[tt] >> (8 * i), lutN), dq);
+        }
       }
       const bool live = 16 * tt + n < m.ntok;
 #pragma unroll
@@ -412,7 +498,8 @@ __global__ __launch_bounds__(kScanThreads, 4) void scan_mfma_kernel(DecodeArgs a
       if constexpr (BV == 4) x = d.vw[bl];
       else if constexpr (BV == 2) x = (d.vw[bl] >> vsh) & 0xffffu;
       else x = vtwo ? ((d.vw[bl] >> vsh) | (d.vw2[bl] << (32 - vsh))) & 0xffffffu : (d.vw[bl] >> vsh) & 0xffffffu;
-      acc[bl] = mfma(aw, dec8<BV>(x, lutVl), acc[bl]);
+      if constexpr (kWide) acc[bl] = mfma(aw, dec8_wide(x, lutV, vbase), acc[bl]);
+      else acc[bl] = mfma(aw, dec8<BV>(x, lutVl), acc[bl]);
     }
   };
 
@@ -478,7 +565,7 @@ __global__ __launch_bounds__(kScanThreads, 4) void scan_mfma_kernel(DecodeArgs a
     }
     __syncthreads();
   }
-  for (int i2 = tid; i2 < G * kD; i2 += kScanThreads) a.pacc[pidx * kD + i2] = red[i2 / kD][i2 % kD];
+  for (int i2 = tid; i2 < G * kD; i2 += kThreads) a.pacc[pidx * kD + i2] = red[i2 / kD][i2 % kD];
   if (tid < G) {
     float M = -INFINITY;
 #pragma unroll
@@ -526,7 +613,9 @@ const void* scan_mfma_kernel_ptr(const tq_ctx* c) {
   }
 }
 
-int scan_mfma_threads(const tq_ctx*) { return kScanThreads; }
+int scan_mfma_threads(const tq_ctx* c) {
+  return scan_threads(wide_scan(c->p.num_q_heads / c->p.num_kv_heads, c->p.value_bits));
+}
 
 int launch_scan_mfma(const tq_ctx* c, const DecodeArgs& a, const KParams& k, void* stream) {
   const void* f = scan_mfma_kernel_ptr(c);
@@ -537,7 +626,9 @@ int launch_scan_mfma(const tq_ctx* c, const DecodeArgs& a, const KParams& k, voi
   KParams kk = k;
   void* args[] = {&aa, &tt, &cc, &kk};
   const dim3 grid(a.splits, k.Hkv, a.batch);
-  return hipLaunchKernel(f, grid, dim3(kScanThreads), args, 0, static_cast<hipStream_t>(stream)) == hipSuccess ? 0 : 1;
+  return hipLaunchKernel(f, grid, dim3(scan_mfma_threads(c)), args, 0, static_cast<hipStream_t>(stream)) == hipSuccess
+             ? 0
+             : 1;
 }
 
 }  // namespace tq
