@@ -18,6 +18,8 @@ MacBook" is the blog post on debugging TurboQuant on an Apple M1 Pro,
                    randomized Hadamard transform, QJL projection matrix.
 * ``codec``      - per-vector encode (norm, rotate, quantise, pack, QJL residual
                    sketch) and dequantisation.
+* ``mixed``      - mixed-channel fractional rates (2.5 and 3.5 bits): half the
+                   rotated coordinates at b bits, half at b + 1.
 * ``pages``      - fixed-size page format, FP16 recent-token ring, append.
 * ``attention``  - decode attention two ways: dequantise-then-softmax (the
                    plain definition) and the compressed-domain formula.
@@ -28,4 +30,4 @@ against printed values, closed forms, brute force or invariants; none is
 "parity unpinned".
 """
 
-from . import accounting, attention, codebook, codec, pages, rotation  # noqa: F401
+from . import accounting, attention, codebook, codec, mixed, pages, rotation  # noqa: F401

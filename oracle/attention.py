@@ -50,7 +50,7 @@ def attention_plain(cache, q, sm_scale, pairs=None):
                 krec, vn, vidx = comp
                 ks.append(codec.dequantize(krec.codes, krec.norms, cache.rot, cache.kcb,
                                            krec.signs, krec.rnorms, cache.S, cache.qjl_coef))
-                vs.append(cache.rot.inverse(vn.astype(np.float64)[:, None] * cache.vcb.centroids[vidx]))
+                vs.append(cache.rot.inverse(vn.astype(np.float64)[:, None] * cache.vcb.values(vidx)))
             _, kw, vw = cache.window_tokens(b, h)
             ks.append(kw)
             vs.append(vw)
@@ -86,8 +86,8 @@ def attention_compressed(cache, q, sm_scale):
                 parts = []
                 if comp is not None:
                     krec, vn, vidx = comp
-                    kidx = codec.unpack_bits(krec.codes, lay.bK, d)
-                    s = krec.norms.astype(np.float64) * (cache.kcb.centroids[kidx] @ q_rot)
+                    kidx = cache.kcb.unpack(krec.codes, d)
+                    s = krec.norms.astype(np.float64) * (cache.kcb.values(kidx) @ q_rot)
                     if lay.qjl:
                         p = cache.S @ q_rot
                         pm = 2.0 * codec.unpack_bits(krec.signs, 1, d) - 1.0
@@ -103,7 +103,7 @@ def attention_compressed(cache, q, sm_scale):
                 nc = 0 if comp is None else comp[0].norms.shape[0]
                 acc_rot = np.zeros(d)
                 if nc:
-                    acc_rot = (w[:nc] * vn.astype(np.float64)) @ cache.vcb.centroids[vidx]
+                    acc_rot = (w[:nc] * vn.astype(np.float64)) @ cache.vcb.values(vidx)
                 acc_win = w[nc:] @ vw
                 out[b, g] = (cache.rot.inverse(acc_rot[None, :])[0] + acc_win) / np.sum(w)
                 logits[b][g] = l

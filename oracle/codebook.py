@@ -128,3 +128,25 @@ class Codebook:
         """Exhaustive nearest-centroid index (first minimum), the plain definition."""
         y = np.asarray(y, dtype=np.float64)
         return np.argmin(np.abs(y[..., None] - self.centroids), axis=-1).astype(np.int64)
+
+    # the record interface shared with the mixed-channel codebook (oracle.mixed)
+    mixed = False
+
+    def values(self, idx: np.ndarray) -> np.ndarray:
+        """Level values c[idx]."""
+        return self.centroids[np.asarray(idx, dtype=np.int64)]
+
+    def record_bytes(self, d: int) -> int:
+        return d * self.bits // 8
+
+    def pack(self, idx: np.ndarray) -> np.ndarray:
+        from . import codec
+        return codec.pack_bits(idx, self.bits)
+
+    def unpack(self, packed: np.ndarray, d: int) -> np.ndarray:
+        from . import codec
+        return codec.unpack_bits(packed, self.bits, d)
+
+    def width(self) -> np.ndarray:
+        """Bits per coordinate, [d]."""
+        return np.full(self.head_dim, self.bits, dtype=np.int64)

@@ -11,7 +11,8 @@ Encode of one post-RoPE vector x (float values, taken exactly as float64):
 4. Codes are bit-packed LSB-first: code j occupies bits [j*b, (j+1)*b) of the
    vector's bitstream, bit i of the stream is bit (i mod 8) of byte i//8
    (step 4; d*b/8 bytes, e.g. 64 bytes at d=128, b=4, from the README's
-   "Where This Fits" example).
+   "Where This Fits" example).  A mixed-channel rate b + 1/2 quantises and
+   packs each half of the coordinates with its own width (``oracle.mixed``).
 5. Keys only: the residual of the MSE reconstruction in the rotated basis,
    r = Pi x - n32 * c[idx]; its norm ||r|| (float32); and the 1-bit QJL sketch
    sigma_j = [ (S r)_j >= 0 ], packed LSB-first like the codes ("TurboQuant on
@@ -91,9 +92,9 @@ def encode(x: np.ndarray, rotation, codebook, qjl_S=None) -> Encoded:
     y32 = y.astype(np.float32).astype(np.float64)
     idx = codebook.quantize(y32)
     idx[~nonzero] = 0
-    rec = Encoded(pack_bits(idx, codebook.bits), norm32.astype(np.float32), idx=idx)
+    rec = Encoded(codebook.pack(idx), norm32.astype(np.float32), idx=idx)
     if qjl_S is not None:
-        r = rotation.forward(x) - norm32[:, None] * codebook.centroids[idx]
+        r = rotation.forward(x) - norm32[:, None] * codebook.values(idx)
         r[~nonzero] = 0.0
         rnorm = np.sqrt(np.sum(r * r, axis=1))
         z = r @ qjl_S.T
@@ -108,7 +109,7 @@ def residual_from_codes(x: np.ndarray, rotation, codebook, norms32, idx) -> np.n
     """r = Pi x - n32 * c[idx] for given codes (used to check sign bits against
     codes produced elsewhere)."""
     x = np.asarray(x, dtype=np.float64)
-    r = rotation.forward(x) - np.asarray(norms32, dtype=np.float64)[:, None] * codebook.centroids[idx]
+    r = rotation.forward(x) - np.asarray(norms32, dtype=np.float64)[:, None] * codebook.values(idx)
     r[np.asarray(norms32) == 0] = 0.0
     return r
 
@@ -116,8 +117,8 @@ def residual_from_codes(x: np.ndarray, rotation, codebook, norms32, idx) -> np.n
 def dequantize_rotated(codes, norms, codebook, d, signs=None, rnorms=None, qjl_S=None, qjl_coef=None):
     """Reconstruction in the rotated basis: n c[idx] (+ QJL term for keys,
     coefficient ``qjl_coef``, default the Gaussian sqrt(pi/2)/d)."""
-    idx = unpack_bits(codes, codebook.bits, d)
-    out = np.asarray(norms, dtype=np.float64)[:, None] * codebook.centroids[idx]
+    idx = codebook.unpack(codes, d)
+    out = np.asarray(norms, dtype=np.float64)[:, None] * codebook.values(idx)
     if signs is not None:
         coef = qjl_scale(d) if qjl_coef is None else qjl_coef
         pm = 2.0 * unpack_bits(signs, 1, d) - 1.0

@@ -33,6 +33,11 @@ the library implements, stated here independently of its source):
                 the bV words w=0..bV-1 (word w at index [group][w][j]) form a
                 32*bV-bit little-endian string; token i of the group has its
                 code at bits [i*bV, (i+1)*bV).
+  Mixed-channel rates b + 1/2 (``oracle.mixed``): the header bits byte holds
+  b + 16; a key record holds (d/2) b + (d/2)(b+1) bits (low-rate coordinates
+  first); a value group holds a low-rate block u32 [bV][d/2] followed by a
+  high-rate block u32 [bV+1][d/2], coordinates of each half in ascending
+  order, each coordinate's words forming its 32-token string as above.
   FP16 ring: k_win, v_win [B, H_kv, W, d]; token at position t lives in slot
   t mod W while it is one of the last W tokens.
 """
@@ -50,22 +55,41 @@ V_GROUP = 32
 
 
 class Layout:
-    def __init__(self, head_dim, key_bits, key_qjl, value_bits, num_kv_heads, page_tokens):
+    def __init__(self, head_dim, key_bits, key_qjl, value_bits, num_kv_heads, page_tokens, key_mixed=False,
+                 value_mixed=False):
         d, P = head_dim, page_tokens
         if P % V_GROUP:
             raise ValueError("page_tokens must be a multiple of 32")
         self.d, self.bK, self.qjl, self.bV, self.H, self.P = d, key_bits, int(key_qjl), value_bits, num_kv_heads, P
+        self.kmix, self.vmix = bool(key_mixed), bool(value_mixed)
+        # code bytes of one key record and of one token's value codes
+        self.k_rec = d * key_bits // 8 + (d // 16 if self.kmix else 0)
+        self.v_rec = d * value_bits // 8 + (d // 16 if self.vmix else 0)
         off = 0
         self.k_norm = off; off += 4 * P
         if self.qjl:
             self.k_rnorm = off; off += 4 * P
-        self.k_codes = off; off += P * d * key_bits // 8
+        self.k_codes = off; off += P * self.k_rec
         if self.qjl:
             self.k_signs = off; off += P * d // 8
         self.v_norm = off; off += 4 * P
-        self.v_codes = off; off += P * d * value_bits // 8
+        self.v_codes = off; off += P * self.v_rec
         self.head_bytes = off
         self.page_bytes = -(-(BODY_OFFSET + num_kv_heads * off) // 256) * 256
+        # value group words: coordinate j's word w sits at v_base[j] + w * v_stride
+        self.v_width = np.full(d, value_bits, dtype=np.int64)
+        if self.vmix:
+            hi = (np.arange(d) % 8) >= 4
+            rank = np.zeros(d, dtype=np.int64)
+            rank[~hi] = np.arange(d // 2)
+            rank[hi] = np.arange(d // 2)
+            self.v_width[hi] = value_bits + 1
+            self.v_base = np.where(hi, value_bits * (d // 2) + rank, rank)
+            self.v_stride = d // 2
+        else:
+            self.v_base = np.arange(d, dtype=np.int64)
+            self.v_stride = d
+        self.v_group_words = V_GROUP * self.v_rec // 4
 
     def head_base(self, h):
         return BODY_OFFSET + h * self.head_bytes
@@ -77,7 +101,7 @@ def write_header(page: np.ndarray, lay: Layout, rotation_kind: int, seed: int, v
     hv[0] = MAGIC
     hdr[4:6] = np.frombuffer(np.uint16(FORMAT_VERSION).tobytes(), np.uint8)
     hdr[6:8] = np.frombuffer(np.uint16(lay.d).tobytes(), np.uint8)
-    hdr[8], hdr[9], hdr[10], hdr[11] = lay.bK, lay.qjl, lay.bV, rotation_kind
+    hdr[8], hdr[9], hdr[10], hdr[11] = lay.bK + 16 * lay.kmix, lay.qjl, lay.bV + 16 * lay.vmix, rotation_kind
     hdr[12:14] = np.frombuffer(np.uint16(lay.H).tobytes(), np.uint8)
     hdr[14:16] = np.frombuffer(np.uint16(lay.P).tobytes(), np.uint8)
     hv[4] = valid
@@ -94,7 +118,7 @@ def _f32(page, off, n):
 def write_key_records(page, lay: Layout, h, slots, rec: codec.Encoded):
     """Store key records (flat ``codec.Encoded``) at the given token slots."""
     base = lay.head_base(h)
-    cb = lay.d * lay.bK // 8
+    cb = lay.k_rec
     _f32(page, base + lay.k_norm, lay.P)[slots] = rec.norms
     codes = page[base + lay.k_codes: base + lay.k_codes + lay.P * cb].reshape(lay.P, cb)
     codes[slots] = rec.codes
@@ -106,29 +130,32 @@ def write_key_records(page, lay: Layout, h, slots, rec: codec.Encoded):
 
 
 def _v_words(page, lay, h):
+    """Value code words of head h: u32 [P/32, words per group]."""
     base = lay.head_base(h) + lay.v_codes
-    n = lay.P * lay.d * lay.bV // 8
-    return page[base: base + n].view(np.uint32).reshape(lay.P // V_GROUP, lay.bV, lay.d)
+    n = lay.P * lay.v_rec
+    return page[base: base + n].view(np.uint32).reshape(lay.P // V_GROUP, lay.v_group_words)
 
 
-def write_value_records(page, lay: Layout, h, slots, rec: codec.Encoded):
+def write_value_records(page, lay: Layout, h, slots, value_cb, rec: codec.Encoded):
     """Store value records at the given slots, re-packing codes group-interleaved."""
     base = lay.head_base(h)
     _f32(page, base + lay.v_norm, lay.P)[slots] = rec.norms
     words = _v_words(page, lay, h)
-    idx = codec.unpack_bits(rec.codes, lay.bV, lay.d)
+    idx = value_cb.unpack(rec.codes, lay.d)
     for s, code_row in zip(np.asarray(slots), idx):
         g, i = divmod(int(s), V_GROUP)
-        for k in range(lay.bV):
-            bit = i * lay.bV + k
-            w, pos = divmod(bit, 32)
-            val = ((code_row >> k) & 1).astype(np.uint32) << np.uint32(pos)
-            words[g, w, :] = (words[g, w, :] & ~np.uint32(1 << pos)) | val
+        for wd in np.unique(lay.v_width):
+            js = np.nonzero(lay.v_width == wd)[0]
+            for k in range(int(wd)):
+                w, pos = divmod(i * int(wd) + k, 32)
+                at = lay.v_base[js] + w * lay.v_stride
+                val = ((code_row[js] >> k) & 1).astype(np.uint32) << np.uint32(pos)
+                words[g, at] = (words[g, at] & ~np.uint32(1 << pos)) | val
 
 
 def read_key_records(page, lay: Layout, h, n):
     base = lay.head_base(h)
-    cb = lay.d * lay.bK // 8
+    cb = lay.k_rec
     norms = _f32(page, base + lay.k_norm, lay.P)[:n].copy()
     codes = page[base + lay.k_codes: base + lay.k_codes + lay.P * cb].reshape(lay.P, cb)[:n].copy()
     signs = rnorms = None
@@ -148,9 +175,11 @@ def read_value_idx(page, lay: Layout, h, n):
     for s in range(n):
         g, i = divmod(s, V_GROUP)
         code = np.zeros(lay.d, dtype=np.int64)
-        for k in range(lay.bV):
-            w, pos = divmod(i * lay.bV + k, 32)
-            code |= ((words[g, w, :] >> pos) & 1) << k
+        for k in range(int(lay.v_width.max())):
+            live = k < lay.v_width
+            w, pos = np.divmod(i * lay.v_width + k, 32)
+            at = np.where(live, lay.v_base + w * lay.v_stride, 0)
+            code |= np.where(live, (words[g, at] >> pos) & 1, 0) << k
         idx[s] = code
     return norms, idx[:n]
 
@@ -223,7 +252,7 @@ class PagedCache:
                                           None if r.signs is None else r.signs[sel],
                                           None if r.rnorms is None else r.rnorms[sel])
             write_key_records(page, lay, h, slots, sub(krec))
-            write_value_records(page, lay, h, slots, sub(vrec))
+            write_value_records(page, lay, h, slots, self.vcb, sub(vrec))
 
     def _headers(self, b, T0, T1):
         lay, W = self.lay, self.W

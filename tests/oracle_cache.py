@@ -3,6 +3,7 @@
 import numpy as np
 
 from oracle import codebook as cbm
+from oracle import mixed
 from oracle import codec
 from oracle import pages
 from oracle import rotation as rot
@@ -11,8 +12,10 @@ import tq_inputs
 
 class Setup:
     def __init__(self, d=128, key_bits=3, key_qjl=1, value_bits=4, rotation="dense", seed=0,
-                 Hq=1, Hkv=1, P=256, W=128, qjl_kind="gaussian", qjl_shrink=1.0):
+                 Hq=1, Hkv=1, P=256, W=128, qjl_kind="gaussian", qjl_shrink=1.0, key_mixed=False,
+                 value_mixed=False):
         self.d, self.bK, self.qjl, self.bV = d, key_bits, key_qjl, value_bits
+        self.kmix, self.vmix = key_mixed, value_mixed
         self.qjl_kind, self.qjl_shrink = qjl_kind, qjl_shrink
         self.rotation, self.seed, self.Hq, self.Hkv, self.P, self.W = rotation, seed, Hq, Hkv, P, W
         if rotation == "dense":
@@ -21,12 +24,13 @@ class Setup:
             self.rot_draws = tq_inputs.hadamard_draws(seed, d)
         self.qjl_draws = tq_inputs.qjl_draws(seed, d)
         self.R = rot.Rotation(rotation, self.rot_draws, d)
-        self.kcb = cbm.Codebook(key_bits, d)
-        self.vcb = cbm.Codebook(value_bits, d)
+        self.kcb = mixed.make_codebook(key_bits, d, "key", key_mixed)
+        self.vcb = mixed.make_codebook(value_bits, d, "value", value_mixed)
         self.S = rot.qjl_matrix(self.qjl_draws, d, qjl_kind) if key_qjl else None
         self.qjl_coef = codec.qjl_scale(d, qjl_kind, qjl_shrink)
         # page-header QJL byte: 0 none, 1 Gaussian S, 2 orthogonal S
-        self.lay = pages.Layout(d, key_bits, (1 + (qjl_kind == "orthogonal")) if key_qjl else 0, value_bits, Hkv, P)
+        self.lay = pages.Layout(d, key_bits, (1 + (qjl_kind == "orthogonal")) if key_qjl else 0, value_bits, Hkv, P,
+                                key_mixed, value_mixed)
 
     def cache(self, batch, max_tokens):
         max_pages = max(1, -(-max(max_tokens - self.W, 0) // self.P))

@@ -140,7 +140,7 @@ def test_value_group_layout_literal():
     page = np.zeros(lay.page_bytes, np.uint8)
     idx = np.random.default_rng(0).integers(0, 8, (32, s.d))
     rec = codec.Encoded(codec.pack_bits(idx, 3), np.ones(32, np.float32))
-    pages.write_value_records(page, lay, 0, np.arange(32), rec)
+    pages.write_value_records(page, lay, 0, np.arange(32), s.vcb, rec)
     words = page[lay.head_base(0) + lay.v_codes:][:32 * s.d * 3 // 8].view(np.uint32).reshape(1, 3, s.d)
     j = 5
     big = int(words[0, 0, j]) | (int(words[0, 1, j]) << 32) | (int(words[0, 2, j]) << 64)
