@@ -46,6 +46,12 @@
  *   u32[P/32][bV][d], where for each 32-token group and coordinate j the bV
  *   words w = 0..bV-1 form a little-endian 32*bV-bit string holding token i's
  *   code at bits [i*bV, (i+1)*bV).
+ *   Mixed-channel rates (key_mixed / value_mixed): the header bits byte holds
+ *   b + 16; a key record is d*b/8 + d/16 bytes (the d/2 low-rate codes at b
+ *   bits, then the d/2 high-rate codes at b + 1 bits, each half in ascending
+ *   coordinate order); a value group is a low-rate block u32[bV][d/2] then a
+ *   high-rate block u32[bV+1][d/2], coordinates of each half in ascending
+ *   order, each coordinate's words forming its 32-token string as above.
  * FP16 window: k_win, v_win [B][H_kv][W][d] fp16; the token at position t
  *   lives in slot t mod W while it is among the last W tokens of its sequence.
  *   A sequence of length T has max(T - W, 0) compressed tokens (positions
@@ -106,6 +112,12 @@ typedef struct tq_params {
   float qjl_shrink;     /* factor on the QJL correction term in decode, (0, 4]; 1 = unbiased,
                            2/pi = the MMSE shrinkage for orthogonal S (same section, the 0.7
                            damping of the ablation) */
+  int32_t key_mixed;    /* 1: mixed-channel rate key_bits + 1/2 (key_bits 2 or 3): the rotated
+                           coordinates j with j mod 32 >= 16 take key_bits + 1 bits with their
+                           own Lloyd-Max codebook; a record holds the low-rate codes, then the
+                           high-rate ones ("TurboQuant Family Design Study", "Packed format and
+                           complete bit accounting": 2.5 / 3.5 bits per channel for d = 128) */
+  int32_t value_mixed;  /* 1: the same for values, high-rate coordinates j mod 8 >= 4 */
 } tq_params;
 
 typedef struct tq_ctx tq_ctx;
@@ -121,7 +133,9 @@ typedef struct tq_ctx tq_ctx;
  * Outputs (each nullable): rotation d*d f32 (DENSE: Pi row-major; HADAMARD:
  * the d signs), qjl d*d f32, key/value centroids 2^b f32 (Lloyd-Max levels of
  * N(0,1) times 1/sqrt(d), rounded to half-precision values), key/value
- * boundaries 2^b - 1 f32 (midpoints of the stored levels).
+ * boundaries 2^b - 1 f32 (midpoints of the stored levels); with a
+ * mixed-channel rate the b-bit arrays are followed by the (b+1)-bit ones
+ * (2^b + 2^(b+1) centroids, 2^b - 1 + 2^(b+1) - 1 boundaries).
  * Returns TQ_ERR_INVALID_ARG for bad params or missing draws. */
 TQ_API int tq_host_tables(const tq_params* params, const double* rot_draws, const double* qjl_draws,
                           float* rotation, float* qjl, float* key_centroids, float* key_boundaries,
@@ -153,7 +167,8 @@ TQ_API int tq_decode(const tq_ctx* ctx, int kind, const uint8_t* codes, const ui
 
 /* Encode n vectors (device pointers) into flat records:
  *   x: [n][row_stride] elements of dtype (F16, BF16 or F32), first d used;
- *   codes: [n][d*b/8] u8 LSB-first, b = key_bits or value_bits by kind;
+ *   codes: [n][d*b/8] u8 LSB-first, b = key_bits or value_bits by kind
+ *   ([n][d*b/8 + d/16] for a mixed-channel rate, layout as in the page);
  *   norms: [n] f32 L2 norms;
  *   signs: [n][d/8] u8 and rnorms: [n] f32, required iff kind == KEY and key_qjl.
  * A vector with zero norm gets all-zero codes, signs and rnorm. */

@@ -45,14 +45,16 @@ class tq_params(ctypes.Structure):
         ("value_bits", ctypes.c_int32), ("rotation", ctypes.c_int32), ("num_q_heads", ctypes.c_int32),
         ("num_kv_heads", ctypes.c_int32), ("page_tokens", ctypes.c_int32), ("window", ctypes.c_int32),
         ("flags", ctypes.c_int32), ("seed", ctypes.c_uint64), ("qjl_kind", ctypes.c_int32),
-        ("qjl_shrink", ctypes.c_float),
+        ("qjl_shrink", ctypes.c_float), ("key_mixed", ctypes.c_int32), ("value_mixed", ctypes.c_int32),
     ]
 
 
 def make_params(head_dim=128, key_bits=3, key_qjl=1, value_bits=4, rotation=TQ_ROT_DENSE, num_q_heads=1,
-                num_kv_heads=1, page_tokens=256, window=128, seed=0, flags=0, qjl_kind=0, qjl_shrink=1.0):
+                num_kv_heads=1, page_tokens=256, window=128, seed=0, flags=0, qjl_kind=0, qjl_shrink=1.0,
+                key_mixed=0, value_mixed=0):
+    """key_mixed / value_mixed: mixed-channel rate bits + 1/2 (bits 2 or 3)."""
     return tq_params(head_dim, key_bits, key_qjl, value_bits, rotation, num_q_heads, num_kv_heads,
-                     page_tokens, window, flags, seed, qjl_kind, qjl_shrink)
+                     page_tokens, window, flags, seed, qjl_kind, qjl_shrink, key_mixed, value_mixed)
 
 
 _lib = None
@@ -138,10 +140,13 @@ def tq_host_tables(params, rot_draws, qjl_draws=None):
     d = params.head_dim
     rot = np.zeros(d * d if params.rotation == TQ_ROT_DENSE else d, np.float32)
     S = np.zeros(d * d, np.float32) if qjl_draws is not None else None
-    kc = np.zeros(1 << params.key_bits, np.float32)
-    kb = np.zeros((1 << params.key_bits) - 1, np.float32)
-    vc = np.zeros(1 << params.value_bits, np.float32)
-    vb = np.zeros((1 << params.value_bits) - 1, np.float32)
+    # a mixed-channel rate appends the (b+1)-bit codebook to the b-bit one
+    nk = (1 << params.key_bits) * (3 if params.key_mixed else 1)
+    nv = (1 << params.value_bits) * (3 if params.value_mixed else 1)
+    kc = np.zeros(nk, np.float32)
+    kb = np.zeros(nk - (2 if params.key_mixed else 1), np.float32)
+    vc = np.zeros(nv, np.float32)
+    vb = np.zeros(nv - (2 if params.value_mixed else 1), np.float32)
     rd = np.ascontiguousarray(rot_draws, dtype=np.float64)
     qd = None if qjl_draws is None else np.ascontiguousarray(qjl_draws, dtype=np.float64)
     rc = lib().tq_host_tables(ctypes.byref(params), _ptr(rd), _ptr(qd), _ptr(rot), _ptr(S),

@@ -95,16 +95,17 @@ __device__ inline uint32_t pack_part(float x0, float x1, int part) {
 // op).  The 256-entry table of 4-bit codes is stored in 32 copies (word e of
 // copy c at 32e + c) and lane l reads copy l % 32, so every half-wave touches
 // 32 distinct banks whatever the codes are.
-template <int B>
+// (The high-rate key table of a mixed rate is kept as a single copy: C = 1.)
+template <int B, int C = (B == 4 ? 32 : 1)>
 struct PairLut {
   static constexpr int kEntries = 1 << (2 * B);
-  static constexpr int kCopies = B == 4 ? 32 : 1;
+  static constexpr int kCopies = C;
   static constexpr int kWords = kEntries * kCopies;
 };
 
-template <int B, int NT>
+template <int B, int NT, int C = (B == 4 ? 32 : 1)>
 __device__ void build_pair_lut(uint32_t* lut, const float* cen, int tid) {
-  using L = PairLut<B>;
+  using L = PairLut<B, C>;
   constexpr int m = (1 << B) - 1;
   for (int w = tid; w < L::kWords; w += NT) {
     const int e = w / L::kCopies;
@@ -114,9 +115,9 @@ __device__ void build_pair_lut(uint32_t* lut, const float* cen, int tid) {
 
 // 8 consecutive codes (8*B bits, LSB-first in x) -> 8 fp16 values; `lut` is
 // the lane's copy (already offset by lane % 32 for replicated tables).
-template <int B>
+template <int B, int C = (B == 4 ? 32 : 1)>
 __device__ inline u4 dec8(uint32_t x, const uint32_t* lut) {
-  using L = PairLut<B>;
+  using L = PairLut<B, C>;
   constexpr uint32_t m = (1u << (2 * B)) - 1u;
   u4 r;
   r.x = lut[(x & m) * L::kCopies];
@@ -142,12 +143,12 @@ __device__ inline u4 dec_signs8(uint32_t x, const u2* lutN) {
 // forms each address (byte e into bits 8..15, the lane's copy offset into
 // bits 0..7) where the narrow tables take a shift and a mask-or.  Eight waves
 // share the table so that two work-groups still fit in a CU.
-constexpr bool wide_scan(int G, int BV) { return BV == 4 && G <= 4; }
+constexpr bool wide_scan(int G, int BV, bool vmix) { return BV == 4 && G <= 4 && !vmix; }
 constexpr int scan_threads(bool wide) { return wide ? 512 : 256; }
 
-template <int G, int BV>
+template <int G, int BV, bool VMIX = false>
 struct ScanShape {
-  static constexpr bool kWide = wide_scan(G, BV);
+  static constexpr bool kWide = wide_scan(G, BV, VMIX);
   static constexpr int kThreads = scan_threads(kWide);
   static constexpr int kWaves = kThreads / 64;
   static constexpr int kLutWords = kWide ? 256 * 64 : PairLut<BV>::kWords;
@@ -180,20 +181,32 @@ __device__ inline uint32_t key_slice(const uint32_t* w, int i) {
   else return bits_at<24>(w, 24 * i);
 }
 
+// The lane's 8 codes of width W in a value word: bits [sh, sh + 8W), from
+// the next word too when a 3-bit slice straddles (two).
+template <int W>
+__device__ inline uint32_t vslice(uint32_t w0, uint32_t w1, int sh, bool two) {
+  if constexpr (W == 4) return w0;
+  else if constexpr (W == 2) return (w0 >> sh) & 0xffffu;
+  else return two ? ((w0 >> sh) | (w1 << (32 - sh))) & 0xffffffu : (w0 >> sh) & 0xffffffu;
+}
+
 // Per-chunk data, split so that key and value words can be loaded at
 // different times: a chunk's keys are scored one step before its values are
 // accumulated, and both are fetched one step ahead of use.
-template <int BK>
+template <int BK, bool KMIX>
 struct KBuf {
-  uint32_t kc[2][BK];  // key codes of tokens n / 16+n, coordinates 32kg .. 32kg+31
+  // key codes of tokens n / 16+n, coordinates 32kg .. 32kg+31; mixed rate:
+  // words 0-1 the low-rate piece (coordinates 32kg .. +15), 2-3 the high-rate one
+  uint32_t kc[2][KMIX ? 4 : BK];
   uint32_t sg[2];      // their sign bits
   float kn[2], rn[2];
   float vn[2];         // value norms of tokens n / 16+n (used when scoring)
 };
-template <int BV>
+template <int BV, bool VMIX>
 struct VBuf {
-  uint32_t vw[8];                   // value words: coordinates 8n .. 8n+7, tokens 8kg .. 8kg+7
-  uint32_t vw2[BV == 3 ? 8 : 1];    // next word when a 3-bit slice straddles two words
+  uint32_t vw[8];  // value words: coordinates 8n .. 8n+7, tokens 8kg .. 8kg+7
+  // next word when a 3-bit slice straddles two words (mixed: either half may be 3-bit)
+  uint32_t vw2[(BV == 3 || VMIX) ? 8 : 1];
 };
 // wave-uniform chunk description (scalar registers)
 struct Meta {
@@ -207,24 +220,34 @@ struct Meta {
 // A row m of every MFMA holds query g = 2(m/4) + (m%2), part (m/2)%2 (0: fp16
 // hi, 1: remainder); the product's rows 4kg + r land in lane group kg, so a
 // lane sees query 2kg + i as rows i (hi) and i + 2 (remainder) and adds them.
-template <int G, int BK, int BV, bool QJL>
-__global__ __launch_bounds__((ScanShape<G, BV>::kThreads), 4) void scan_mfma_kernel(DecodeArgs a, DevTables t,
-                                                                                   Codebooks cb, KParams k) {
-  using Sh = ScanShape<G, BV>;
+// KMIX / VMIX: mixed-channel rate BK + 1/2 (BV + 1/2): the high-rate half
+// of the coordinates (keys: j mod 32 >= 16, values: j mod 8 >= 4) takes one
+// more bit and its own codebook.  A lane's key slice then holds a low-rate
+// piece (MFMAs i = 0, 1) and a high-rate piece (i = 2, 3); value MFMA bl
+// reads the low-rate word block for bl < 4 and the high-rate one otherwise,
+// so every operand slice has one compile-time width.
+template <int G, int BK, int BV, bool QJL, bool KMIX, bool VMIX>
+__global__ __launch_bounds__((ScanShape<G, BV, VMIX>::kThreads), 4) void scan_mfma_kernel(DecodeArgs a, DevTables t,
+                                                                                         Codebooks cb, KParams k) {
+  using Sh = ScanShape<G, BV, VMIX>;
   constexpr bool kWide = Sh::kWide;
   constexpr int kThreads = Sh::kThreads, kWaves = Sh::kWaves;
   // One array: the key table (absent when keys and values share a bit width,
   // hence a codebook) first, so that every table address stays within the
   // 16-bit immediate offset of the LDS instructions.
   constexpr int kKeyWords = BK == BV ? 0 : PairLut<BK>::kWords;
-  __shared__ uint32_t luts[kKeyWords + Sh::kLutWords];
+  constexpr int kKeyHiWords = KMIX ? PairLut<BK + 1, 1>::kWords : 0;  // mixed keys: high-rate table, one copy
+  constexpr int kValHiWords = VMIX ? PairLut<BV + 1>::kWords : 0;     // mixed values: high-rate table
+  __shared__ uint32_t luts[kKeyWords + kKeyHiWords + Sh::kLutWords + kValHiWords];
   uint32_t* const lutKown = luts;
-  uint32_t* const lutV = luts + kKeyWords;
+  uint32_t* const lutKhi = luts + kKeyWords;
+  uint32_t* const lutV = luts + kKeyWords + kKeyHiWords;
+  uint32_t* const lutVhi = lutV + Sh::kLutWords;
   __shared__ u2 lutN[kWide ? 1 : 16];
   __shared__ float pv[kWaves][2][G][kChunk];  // softmax weights x value norms, two chunks in flight
   __shared__ float wm[kWaves][G], wl[kWaves][G];
   __shared__ float red[G][kD];
-  __shared__ float ck[16], cvv[16];
+  __shared__ float ck[16], cvv[16], ck2[16], cv2[16];
 
   const int tid = threadIdx.x, split = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   // the wave index is uniform within a wave; saying so keeps page addresses
@@ -251,15 +274,19 @@ __global__ __launch_bounds__((ScanShape<G, BV>::kThreads), 4) void scan_mfma_ker
   }
   // codebooks to LDS (no dynamic indexing of kernel arguments), then the tables
   if (tid < 16) {
-    float kv = 0.0f, vv = 0.0f;
+    float kv = 0.0f, vv = 0.0f, kv2 = 0.0f, vv2 = 0.0f;
 #pragma unroll
     for (int i = 0; i < 16; ++i)
       if (i == tid) {
         kv = cb.kc[i];
         vv = cb.vc[i];
+        kv2 = cb.kc2[i];
+        vv2 = cb.vc2[i];
       }
     ck[tid] = kv;
     cvv[tid] = vv;
+    ck2[tid] = kv2;
+    cv2[tid] = vv2;
   }
   __syncthreads();
   if constexpr (kWide) {
@@ -278,6 +305,8 @@ __global__ __launch_bounds__((ScanShape<G, BV>::kThreads), 4) void scan_mfma_ker
     build_pair_lut<BV, kThreads>(lutV, cvv, tid);
   }
   if constexpr (BK != BV) build_pair_lut<BK, kThreads>(lutKown, ck, tid);
+  if constexpr (KMIX) build_pair_lut<BK + 1, kThreads, 1>(lutKhi, ck2, tid);
+  if constexpr (VMIX) build_pair_lut<BV + 1, kThreads>(lutVhi, cv2, tid);
   if (!kWide && tid < 16) {
     const int e = tid;
     lutN[e] = u2{(e & 1 ? 0x3C00u : 0xBC00u) | ((e & 2 ? 0x3C00u : 0xBC00u) << 16),
@@ -286,6 +315,7 @@ __global__ __launch_bounds__((ScanShape<G, BV>::kThreads), 4) void scan_mfma_ker
   const uint32_t* lutK = BK == BV ? lutV : lutKown;
   const uint32_t* lutKl = lutK + (PairLut<BK>::kCopies > 1 ? (tid & 31) : 0);
   const uint32_t* lutVl = lutV + (PairLut<BV>::kCopies > 1 ? (tid & 31) : 0);
+  const uint32_t* lutVhil = lutVhi + ((VMIX && PairLut<BV + 1>::kCopies > 1) ? (tid & 31) : 0);
   const uint32_t vbase = static_cast<uint32_t>(tid & 31) * 4u, sbase = 128u + static_cast<uint32_t>(tid & 7) * 16u;
   // A operands of the key products: lane group kg covers coordinates
   // 32kg .. 32kg+31, MFMA i the 8 starting at 32kg + 8i.
@@ -328,8 +358,26 @@ __global__ __launch_bounds__((ScanShape<G, BV>::kThreads), 4) void scan_mfma_ker
   const bool vtwo = (vsh + 8 * BV) > 32;
   // per-lane byte offsets inside a head block (the chunk adds a uniform offset)
   const uint32_t o_tok0 = 4u * n, o_tok1 = 4u * (16 + n);
+  constexpr int kKRec = 16 * BK + (KMIX ? 8 : 0);  // key record bytes
   const uint32_t o_kc0 = static_cast<uint32_t>(n * 16 * BK + 4 * BK * kg);
   const uint32_t o_kc1 = o_kc0 + 16u * 16u * BK;
+  // mixed keys: the lane's low-rate piece (2 BK bytes at 2 BK kg) and
+  // high-rate piece (2 (BK+1) bytes at 8 BK + 2 (BK+1) kg) of the record, each
+  // read as 8 bytes from the 4-byte boundary below and shifted down
+  const uint32_t oL = 2u * BK * kg, oH = 8u * BK + 2u * (BK + 1) * kg;
+  const uint32_t o_kL0 = n * kKRec + (oL & ~3u), o_kH0 = n * kKRec + (oH & ~3u);
+  const uint32_t o_kL1 = o_kL0 + 16u * kKRec, o_kH1 = o_kH0 + 16u * kKRec;
+  const uint32_t shL = 8u * (oL & 3u), shH = 8u * (oH & 3u);
+  // mixed values: low-rate block [BV][64] then high-rate block [BV+1][64] per
+  // group; MFMA bl < 4 reads low-rate ranks 4n .. 4n+3, bl >= 4 high-rate ones
+  const int vbitL = 8 * kg * BV, vbitH = 8 * kg * (BV + 1);
+  const int vwL = vbitL >> 5, vshL = vbitL & 31, vwH = vbitH >> 5, vshH = vbitH & 31;
+  const bool vtwoL = (vshL + 8 * BV) > 32, vtwoH = (vshH + 8 * (BV + 1)) > 32;
+  const uint32_t vHiBlock = 64u * BV * 4u;
+  const uint32_t o_vwL = static_cast<uint32_t>((vwL * 64 + 4 * n) * 4);
+  const uint32_t o_vwL2 = static_cast<uint32_t>(((vtwoL ? vwL + 1 : vwL) * 64 + 4 * n) * 4);
+  const uint32_t o_vwH = vHiBlock + static_cast<uint32_t>((vwH * 64 + 4 * n) * 4);
+  const uint32_t o_vwH2 = vHiBlock + static_cast<uint32_t>(((vtwoH ? vwH + 1 : vwH) * 64 + 4 * n) * 4);
   const uint32_t o_sg0 = static_cast<uint32_t>(n * 16 + 4 * kg), o_sg1 = o_sg0 + 256u;
   const uint32_t o_vw = static_cast<uint32_t>((vw0 * kD + 8 * n) * 4);
   const uint32_t o_vw2 = static_cast<uint32_t>(((vtwo ? vw0 + 1 : vw0) * kD + 8 * n) * 4);
@@ -363,7 +411,7 @@ __global__ __launch_bounds__((ScanShape<G, BV>::kThreads), 4) void scan_mfma_ker
     const uint8_t* hb = a.pool + static_cast<int64_t>(pid) * k.page_bytes + kBodyOffset + h * k.head_bytes;
     m.rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(hb), 0, static_cast<int>(k.head_bytes), kRsrcWord3);
   };
-  auto loadK = [&](const Meta& m, KBuf<BK>& d) {
+  auto loadK = [&](const Meta& m, KBuf<BK, KMIX>& d) {
     const int so_kn = static_cast<int>(k.k_norm) + 4 * m.s0;
     d.kn[0] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(m.rs, o_tok0, so_kn, kStream));
     d.kn[1] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(m.rs, o_tok1, so_kn, kStream));
@@ -378,11 +426,18 @@ __global__ __launch_bounds__((ScanShape<G, BV>::kThreads), 4) void scan_mfma_ker
     const int so_vn = static_cast<int>(k.v_norm) + 4 * m.s0;
     d.vn[0] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(m.rs, o_tok0, so_vn, kStream));
     d.vn[1] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(m.rs, o_tok1, so_vn, kStream));
-    const int so_kc = static_cast<int>(k.k_codes) + 16 * BK * m.s0;
+    const int so_kc = static_cast<int>(k.k_codes) + kKRec * m.s0;
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt) {
       const uint32_t o = tt ? o_kc1 : o_kc0;
-      if constexpr (BK == 4) {
+      if constexpr (KMIX) {
+        const u2 lo = __builtin_amdgcn_raw_buffer_load_b64(m.rs, tt ? o_kL1 : o_kL0, so_kc, kStream);
+        const u2 hi = __builtin_amdgcn_raw_buffer_load_b64(m.rs, tt ? o_kH1 : o_kH0, so_kc, kStream);
+        d.kc[tt][0] = __builtin_amdgcn_alignbit(lo.y, lo.x, shL);
+        d.kc[tt][1] = lo.y >> shL;
+        d.kc[tt][2] = __builtin_amdgcn_alignbit(hi.y, hi.x, shH);
+        d.kc[tt][3] = hi.y >> shH;
+      } else if constexpr (BK == 4) {
         const u4 v = __builtin_amdgcn_raw_buffer_load_b128(m.rs, o, so_kc, kStream);
         d.kc[tt][0] = v.x; d.kc[tt][1] = v.y; d.kc[tt][2] = v.z; d.kc[tt][3] = v.w;
       } else if constexpr (BK == 3) {
@@ -394,7 +449,22 @@ __global__ __launch_bounds__((ScanShape<G, BV>::kThreads), 4) void scan_mfma_ker
       }
     }
   };
-  auto loadV = [&](const Meta& m, VBuf<BV>& d) {
+  auto loadV = [&](const Meta& m, VBuf<BV, VMIX>& d) {
+    if constexpr (VMIX) {
+      const int so_vw = static_cast<int>(k.v_codes) + m.gi * 256 * (2 * BV + 1);
+      const u4 x0 = __builtin_amdgcn_raw_buffer_load_b128(m.rs, o_vwL, so_vw, kStream);
+      const u4 x1 = __builtin_amdgcn_raw_buffer_load_b128(m.rs, o_vwH, so_vw, kStream);
+      d.vw[0] = x0.x; d.vw[1] = x0.y; d.vw[2] = x0.z; d.vw[3] = x0.w;
+      d.vw[4] = x1.x; d.vw[5] = x1.y; d.vw[6] = x1.z; d.vw[7] = x1.w;
+      if constexpr (BV == 3) {  // the 3-bit low-rate slice may straddle two words
+        const u4 y0 = __builtin_amdgcn_raw_buffer_load_b128(m.rs, o_vwL2, so_vw, kStream);
+        d.vw2[0] = y0.x; d.vw2[1] = y0.y; d.vw2[2] = y0.z; d.vw2[3] = y0.w;
+      } else {  // BV == 2: the 3-bit high-rate slice may
+        const u4 y1 = __builtin_amdgcn_raw_buffer_load_b128(m.rs, o_vwH2, so_vw, kStream);
+        d.vw2[4] = y1.x; d.vw2[5] = y1.y; d.vw2[6] = y1.z; d.vw2[7] = y1.w;
+      }
+      return;
+    }
     const int so_vw = static_cast<int>(k.v_codes) + m.gi * BV * kD * 4;
     const u4 x0 = __builtin_amdgcn_raw_buffer_load_b128(m.rs, o_vw, so_vw, kStream);
     const u4 x1 = __builtin_amdgcn_raw_buffer_load_b128(m.rs, o_vw + 16u, so_vw, kStream);
@@ -411,15 +481,21 @@ __global__ __launch_bounds__((ScanShape<G, BV>::kThreads), 4) void scan_mfma_ker
   float* pvw = &pv[wave][0][0][0];
   const int64_t dbg_row = (static_cast<int64_t>(b) * k.Hq + h * G) * a.logits_stride;
   // ---- scores of one chunk, online softmax, weights x value norms to pv[slot]
-  auto keyphase = [&](const Meta& m, const KBuf<BK>& d, int slot) {
+  auto keyphase = [&](const Meta& m, const KBuf<BK, KMIX>& d, int slot) {
     float sc[2][2];  // [query i][tile]
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt) {
       f4 dm = f4{0.0f, 0.0f, 0.0f, 0.0f}, dq = f4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        if constexpr (kWide && BK == 4) dm = mfma(aq[i], dec8_wide(d.kc[tt][i], lutV, vbase), dm);
-        else dm = mfma(aq[i], dec8<BK>(key_slice<BK>(d.kc[tt], i), lutKl), dm);
+        if constexpr (KMIX) {
+          if (i < 2) dm = mfma(aq[i], dec8<BK>(key_slice<BK>(&d.kc[tt][0], i), lutKl), dm);
+          else dm = mfma(aq[i], dec8<BK + 1, 1>(key_slice<BK + 1>(&d.kc[tt][2], i - 2), lutKhi), dm);
+        } else if constexpr (kWide && BK == 4) {
+          dm = mfma(aq[i], dec8_wide(d.kc[tt][i], lutV, vbase), dm);
+        } else {
+          dm = mfma(aq[i], dec8<BK>(key_slice<BK>(d.kc[tt], i), lutKl), dm);
+        }
         if constexpr (QJL && kWide) {
           const uint32_t sgw = d.sg[tt];
           const u4 sb = i == 0 ? dec_signs_wide<0>(sgw, lutV, sbase)
@@ -484,13 +560,23 @@ __global__ __launch_bounds__((ScanShape<G, BV>::kThreads), 4) void scan_mfma_ker
     }
   };
   // ---- value product of one chunk with the weights in pv[slot]
-  auto valuephase = [&](const VBuf<BV>& d, int slot) {
+  auto valuephase = [&](const VBuf<BV, VMIX>& d, int slot) {
     u4 aw = u4{0u, 0u, 0u, 0u};
     if (ag < G) {
       const float4* pw = reinterpret_cast<const float4*>(pvw + slot * (G * kChunk) + ag * kChunk + 8 * kg);
       const float4 w0 = pw[0], w1 = pw[1];
       aw = u4{pk_rtz(part_of(w0.x, amask), part_of(w0.y, amask)), pk_rtz(part_of(w0.z, amask), part_of(w0.w, amask)),
               pk_rtz(part_of(w1.x, amask), part_of(w1.y, amask)), pk_rtz(part_of(w1.z, amask), part_of(w1.w, amask))};
+    }
+    if constexpr (VMIX) {
+#pragma unroll
+      for (int bl = 0; bl < 8; ++bl) {
+        if (bl < 4)
+          acc[bl] = mfma(aw, dec8<BV>(vslice<BV>(d.vw[bl], d.vw2[bl], vshL, vtwoL), lutVl), acc[bl]);
+        else
+          acc[bl] = mfma(aw, dec8<BV + 1>(vslice<BV + 1>(d.vw[bl], d.vw2[bl], vshH, vtwoH), lutVhil), acc[bl]);
+      }
+      return;
     }
 #pragma unroll
     for (int bl = 0; bl < 8; ++bl) {
@@ -509,8 +595,8 @@ __global__ __launch_bounds__((ScanShape<G, BV>::kThreads), 4) void scan_mfma_ker
   // i+1 load while chunk i's values are accumulated, values of chunk i+1
   // while chunk i+1 is scored.  The weights alternate between two pv slots.
   Meta m;
-  KBuf<BK> kb;
-  VBuf<BV> vb;
+  KBuf<BK, KMIX> kb;
+  VBuf<BV, VMIX> vb;
   if (nmine > 0) {
     meta(0, m);
     loadK(m, kb);
@@ -579,42 +665,53 @@ __global__ __launch_bounds__((ScanShape<G, BV>::kThreads), 4) void scan_mfma_ker
   }
 }
 
-template <int G, int BK, int BV>
+template <int G, int BK, int BV, bool KMIX, bool VMIX>
 const void* pick_bits(bool qjl) {
-  return qjl ? reinterpret_cast<const void*>(&scan_mfma_kernel<G, BK, BV, true>)
-             : reinterpret_cast<const void*>(&scan_mfma_kernel<G, BK, BV, false>);
+  return qjl ? reinterpret_cast<const void*>(&scan_mfma_kernel<G, BK, BV, true, KMIX, VMIX>)
+             : reinterpret_cast<const void*>(&scan_mfma_kernel<G, BK, BV, false, KMIX, VMIX>);
 }
 
-template <int G, int BK>
-const void* pick_bv(int bv, bool qjl) {
-  if (bv == 2) return pick_bits<G, BK, 2>(qjl);
-  if (bv == 3) return pick_bits<G, BK, 3>(qjl);
-  return pick_bits<G, BK, 4>(qjl);
+// mixed-channel rates exist for 2.5 and 3.5 bits (low width 2 or 3)
+template <int G, int BK, bool KMIX>
+const void* pick_bv(int bv, bool vmix, bool qjl) {
+  if (vmix) {
+    if (bv == 2) return pick_bits<G, BK, 2, KMIX, true>(qjl);
+    if (bv == 3) return pick_bits<G, BK, 3, KMIX, true>(qjl);
+    return nullptr;
+  }
+  if (bv == 2) return pick_bits<G, BK, 2, KMIX, false>(qjl);
+  if (bv == 3) return pick_bits<G, BK, 3, KMIX, false>(qjl);
+  return pick_bits<G, BK, 4, KMIX, false>(qjl);
 }
 
 template <int G>
-const void* pick_g(int bk, int bv, bool qjl) {
-  if (bk == 2) return pick_bv<G, 2>(bv, qjl);
-  if (bk == 3) return pick_bv<G, 3>(bv, qjl);
-  return pick_bv<G, 4>(bv, qjl);
+const void* pick_g(int bk, bool kmix, int bv, bool vmix, bool qjl) {
+  if (kmix) {
+    if (bk == 2) return pick_bv<G, 2, true>(bv, vmix, qjl);
+    if (bk == 3) return pick_bv<G, 3, true>(bv, vmix, qjl);
+    return nullptr;
+  }
+  if (bk == 2) return pick_bv<G, 2, false>(bv, vmix, qjl);
+  if (bk == 3) return pick_bv<G, 3, false>(bv, vmix, qjl);
+  return pick_bv<G, 4, false>(bv, vmix, qjl);
 }
 
 }  // namespace
 
 const void* scan_mfma_kernel_ptr(const tq_ctx* c) {
   const int G = c->p.num_q_heads / c->p.num_kv_heads, bk = c->p.key_bits, bv = c->p.value_bits;
-  const bool qjl = c->p.key_qjl != 0;
+  const bool qjl = c->p.key_qjl != 0, kmix = c->p.key_mixed != 0, vmix = c->p.value_mixed != 0;
   switch (G) {
-    case 1: return pick_g<1>(bk, bv, qjl);
-    case 2: return pick_g<2>(bk, bv, qjl);
-    case 4: return pick_g<4>(bk, bv, qjl);
-    case 8: return pick_g<8>(bk, bv, qjl);
+    case 1: return pick_g<1>(bk, kmix, bv, vmix, qjl);
+    case 2: return pick_g<2>(bk, kmix, bv, vmix, qjl);
+    case 4: return pick_g<4>(bk, kmix, bv, vmix, qjl);
+    case 8: return pick_g<8>(bk, kmix, bv, vmix, qjl);
     default: return nullptr;
   }
 }
 
 int scan_mfma_threads(const tq_ctx* c) {
-  return scan_threads(wide_scan(c->p.num_q_heads / c->p.num_kv_heads, c->p.value_bits));
+  return scan_threads(wide_scan(c->p.num_q_heads / c->p.num_kv_heads, c->p.value_bits, c->p.value_mixed != 0));
 }
 
 int launch_scan_mfma(const tq_ctx* c, const DecodeArgs& a, const KParams& k, void* stream) {

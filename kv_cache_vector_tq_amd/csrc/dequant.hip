@@ -27,8 +27,10 @@ struct DequantArgs {
   float* out;
   int bits;
   int qjl;
+  int hmod;  // mixed-channel rate: coordinate j has bits + 1 when j mod hmod >= hmod/2; 0: integer rate
   float coef;
   float cen[16];
+  float cen2[16];  // the (bits+1)-bit codebook of a mixed rate
 };
 
 template <bool HAD>
@@ -36,15 +38,17 @@ __global__ __launch_bounds__(kThreads) void dequant_kernel(DequantArgs a, DevTab
   __shared__ float us[kTile][kD];      // rotated-basis vectors
   __shared__ uint32_t sg[kTile][4];    // sign words
   __shared__ float nv[kTile], rv[kTile];
-  __shared__ float ctab[16];
+  __shared__ float ctab[32];
   const int tid = threadIdx.x;
   const int64_t v0 = static_cast<int64_t>(blockIdx.x) * kTile;
   const int nvec = static_cast<int>(a.n - v0 < kTile ? a.n - v0 : kTile);
-  if (tid < 16) {
+  if (tid < 32) {
     float c = 0.0f;
 #pragma unroll
-    for (int k = 0; k < 16; ++k)
+    for (int k = 0; k < 16; ++k) {
       if (k == tid) c = a.cen[k];
+      if (k + 16 == tid) c = a.cen2[k];
+    }
     ctab[tid] = c;
   }
   if (tid < kTile) {
@@ -59,15 +63,20 @@ __global__ __launch_bounds__(kThreads) void dequant_kernel(DequantArgs a, DevTab
   __syncthreads();
   // u[v][j] = n c[code_j] for coordinate j = tid
   const uint32_t* cw = reinterpret_cast<const uint32_t*>(a.codes);
-  const int wpv = 4 * a.bits;  // 32-bit words per record (d = 128)
-  const int bitpos = tid * a.bits;
+  // record: d codes of `bits` bits, or (mixed rate) the d/2 low-rate codes,
+  // then the d/2 high-rate codes of bits + 1, each half in ascending order
+  const bool hi = a.hmod != 0 && mixed_hi(tid, a.hmod);
+  const int width = a.bits + (hi ? 1 : 0);
+  const int wpv = 4 * a.bits + (a.hmod ? 2 : 0);  // 32-bit words per record (d = 128)
+  const int bitpos = a.hmod == 0 ? tid * a.bits
+                                 : (hi ? (kD / 2) * a.bits : 0) + mixed_rank(tid, a.hmod) * width;
   for (int v = 0; v < nvec; ++v) {
     const uint32_t* w = cw + (v0 + v) * wpv;
     const int wi = bitpos >> 5, bi = bitpos & 31;
     uint32_t c = w[wi] >> bi;
-    if (bi + a.bits > 32) c |= w[wi + 1] << (32 - bi);
-    c &= (1u << a.bits) - 1u;
-    us[v][tid] = nv[v] * ctab[c];
+    if (bi + width > 32) c |= w[wi + 1] << (32 - bi);
+    c &= (1u << width) - 1u;
+    us[v][tid] = nv[v] * ctab[(hi ? 16 : 0) + c];
   }
   if (a.qjl) {
     // + coef ||r|| (S^T pm)_j: this thread's row of S^T is column j of S
@@ -136,7 +145,11 @@ int launch_dequant(const tq_ctx* c, int kind, const uint8_t* codes, const uint8_
   a.bits = key ? c->p.key_bits : c->p.value_bits;
   a.qjl = (key && c->p.key_qjl) ? 1 : 0;
   a.coef = make_kparams(c).qjl_scale;
-  for (int k = 0; k < 16; ++k) a.cen[k] = key ? c->cb.kc[k] : c->cb.vc[k];
+  a.hmod = (key ? c->p.key_mixed : c->p.value_mixed) ? (key ? kKeyHiMod : kValHiMod) : 0;
+  for (int k = 0; k < 16; ++k) {
+    a.cen[k] = key ? c->cb.kc[k] : c->cb.vc[k];
+    a.cen2[k] = key ? c->cb.kc2[k] : c->cb.vc2[k];
+  }
   const int64_t tiles = (n + kTile - 1) / kTile;
   if (tiles > 0x7fffffff) return 1;
   hipStream_t s = static_cast<hipStream_t>(stream);

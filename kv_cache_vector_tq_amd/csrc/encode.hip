@@ -26,24 +26,30 @@ struct Smem {
   uint8_t code[kTile][kD];
   float n32[kTile], invn[kTile], rn[kTile];
   uint32_t sgn[kTile][4];
-  float ctab[16];
+  float ctab[32];  // centroids; [16, 32): the (b+1)-bit codebook of a mixed rate
 };
 
 struct CoreParams {
   int bits;
   bool qjl;
-  float bnd[16];  // decision boundaries (uniform values)
-  float cen[16];  // centroids
+  int hmod;        // mixed-channel rate: coordinate j takes bits + 1 when j mod hmod >= hmod/2; 0: integer rate
+  float bnd[16];   // decision boundaries (uniform values)
+  float cen[16];   // centroids
+  float bnd2[16];  // the (bits+1)-bit codebook of a mixed rate
+  float cen2[16];
 };
 
-__device__ inline CoreParams make_core(const Codebooks& cb, bool key, int bits, bool qjl) {
+__device__ inline CoreParams make_core(const Codebooks& cb, bool key, int bits, bool qjl, bool mixed) {
   CoreParams cp;
   cp.bits = bits;
   cp.qjl = qjl;
+  cp.hmod = mixed ? (key ? kKeyHiMod : kValHiMod) : 0;
 #pragma unroll
   for (int k = 0; k < 16; ++k) {
     cp.bnd[k] = key ? cb.kb[k] : cb.vb[k];
     cp.cen[k] = key ? cb.kc[k] : cb.vc[k];
+    cp.bnd2[k] = key ? cb.kb2[k] : cb.vb2[k];
+    cp.cen2[k] = key ? cb.kc2[k] : cb.vc2[k];
   }
   return cp;
 }
@@ -64,12 +70,16 @@ __device__ void encode_core(Smem& sm, const DevTables& t, const CoreParams& cp, 
       for (int j = 0; j < kD; ++j) srow[j] = t.ST[j * kD + tid];
     }
   }
-  const int nb = (1 << cp.bits) - 1;
-  if (tid < 16) {
+  // this thread's coordinate (tid) and its codebook
+  const bool hi = cp.hmod != 0 && mixed_hi(tid, cp.hmod);
+  const int nb = (1 << (cp.bits + (hi ? 1 : 0))) - 1;
+  if (tid < 32) {
     float cv = 0.0f;
 #pragma unroll
-    for (int k = 0; k < 16; ++k)
-      if (k == tid && k <= nb) cv = cp.cen[k];
+    for (int k = 0; k < 16; ++k) {
+      if (k == tid) cv = cp.cen[k];
+      if (k + 16 == tid) cv = cp.cen2[k];
+    }
     sm.ctab[tid] = cv;
   }
   // norms in double: thread t sums a quarter of vector t/4
@@ -97,10 +107,10 @@ __device__ void encode_core(Smem& sm, const DevTables& t, const CoreParams& cp, 
     int c = 0;
 #pragma unroll
     for (int k = 0; k < 15; ++k)
-      if (k < nb) c += (y > cp.bnd[k]) ? 1 : 0;
+      if (k < nb) c += (y > (hi ? cp.bnd2[k] : cp.bnd[k])) ? 1 : 0;
     if (!(n > 0.0f)) c = 0;
     sm.code[v][tid] = static_cast<uint8_t>(c);
-    if (cp.qjl) sm.rs[v][tid] = (n > 0.0f) ? fmaf(-n, sm.ctab[c], accv) : 0.0f;
+    if (cp.qjl) sm.rs[v][tid] = (n > 0.0f) ? fmaf(-n, sm.ctab[(hi ? 16 : 0) + c], accv) : 0.0f;
   };
   if constexpr (!HAD && LAT) {
     float pr[kD];
@@ -243,19 +253,31 @@ __device__ void encode_core(Smem& sm, const DevTables& t, const CoreParams& cp, 
   }
 }
 
-// Word w (32 bits) of vector v's LSB-first code stream.
-__device__ inline uint32_t code_word(const Smem& sm, int v, int w, int bits) {
+// Word w (32 bits) of the LSB-first stream of n codes of `bits` bits each,
+// the i-th being code(i).
+template <class F>
+__device__ inline uint32_t stream_word(F code, int n, int w, int bits) {
   const int first = (32 * w) / bits;
   const int base = first * bits;
   uint64_t acc = 0;
-  for (int c = first; c < kD && c * bits < 32 * w + 32; ++c)
-    acc |= static_cast<uint64_t>(sm.code[v][c]) << (c * bits - base);
+  for (int c = first; c < n && c * bits < 32 * w + 32; ++c) acc |= static_cast<uint64_t>(code(c)) << (c * bits - base);
   return static_cast<uint32_t>(acc >> (32 * w - base));
+}
+
+// Word w of vector v's record: the d codes LSB-first, or for a mixed rate
+// (hmod != 0) the d/2 low-rate codes at `bits` bits, then the d/2 high-rate
+// codes at bits + 1, each half in ascending coordinate order.
+__device__ inline uint32_t code_word(const Smem& sm, int v, int w, int bits, int hmod) {
+  if (hmod == 0) return stream_word([&](int c) { return sm.code[v][c]; }, kD, w, bits);
+  const int lo_words = (kD / 2) * bits / 32;
+  if (w < lo_words)
+    return stream_word([&](int r) { return sm.code[v][mixed_coord(r, 0, hmod)]; }, kD / 2, w, bits);
+  return stream_word([&](int r) { return sm.code[v][mixed_coord(r, 1, hmod)]; }, kD / 2, w - lo_words, bits + 1);
 }
 
 template <bool HAD>
 __global__ __launch_bounds__(kThreads) void encode_flat_kernel(EncodeArgs a, DevTables t, Codebooks cb, int kind,
-                                                              int dtype, int bits, int qjl) {
+                                                              int dtype, int bits, int qjl, int mixed) {
   __shared__ Smem sm;
   const int tid = threadIdx.x;
   const int64_t n0 = static_cast<int64_t>(blockIdx.x) * kTile;
@@ -263,18 +285,18 @@ __global__ __launch_bounds__(kThreads) void encode_flat_kernel(EncodeArgs a, Dev
   for (int v = 0; v < kTile; ++v)
     sm.xs[v][tid] = v < nv ? load_any(a.x, (n0 + v) * a.row_stride + tid, dtype) : 0.0f;
   __syncthreads();
-  const CoreParams cp = make_core(cb, kind == TQ_KIND_KEY, bits, qjl != 0);
+  const CoreParams cp = make_core(cb, kind == TQ_KIND_KEY, bits, qjl != 0, mixed != 0);
   encode_core<HAD, false>(sm, t, cp, 0, nv);
   __syncthreads();
   if (tid < nv) {
     a.norms[n0 + tid] = sm.n32[tid];
     if (qjl) a.rnorms[n0 + tid] = sm.rn[tid];
   }
-  const int wpv = 4 * bits;  // 32-bit words per vector (d = 128)
+  const int wpv = 4 * bits + (mixed ? 2 : 0);  // 32-bit words per record (d = 128)
   uint32_t* cw = reinterpret_cast<uint32_t*>(a.codes);
   for (int k = tid; k < nv * wpv; k += kThreads) {
     const int v = k / wpv, w = k % wpv;
-    cw[(n0 + v) * wpv + w] = code_word(sm, v, w, bits);
+    cw[(n0 + v) * wpv + w] = code_word(sm, v, w, bits, cp.hmod);
   }
   if (qjl) {
     uint32_t* sw = reinterpret_cast<uint32_t*>(a.signs);
@@ -368,7 +390,7 @@ __device__ void encode_group(Smem& sm, const AppendArgs& a, const DevTables& t, 
     }
     __syncthreads();
     const bool key = kv == 0;
-    const CoreParams cp = make_core(cb, key, key ? L.bK : L.bV, key && L.qjl);
+    const CoreParams cp = make_core(cb, key, key ? L.bK : L.bV, key && L.qjl, key ? L.kmix : L.vmix);
     const int vlo = lo - gpos, vhi = hi - gpos;
     encode_core<HAD, LAT>(sm, t, cp, vlo, vhi);
     __syncthreads();
@@ -378,11 +400,11 @@ __device__ void encode_group(Smem& sm, const AppendArgs& a, const DevTables& t, 
         kn[slot0 + tid] = sm.n32[tid];
         if (L.qjl) reinterpret_cast<float*>(hb + L.k_rnorm)[slot0 + tid] = sm.rn[tid];
       }
-      const int wpv = 4 * L.bK;
+      const int wpv = L.k_rec / 4;
       uint32_t* cw = reinterpret_cast<uint32_t*>(hb + L.k_codes);
       for (int k = tid; k < kTile * wpv; k += kThreads) {
         const int v = k / wpv, w = k % wpv;
-        if (v >= vlo && v < vhi) cw[(slot0 + v) * wpv + w] = code_word(sm, v, w, L.bK);
+        if (v >= vlo && v < vhi) cw[(slot0 + v) * wpv + w] = code_word(sm, v, w, L.bK, cp.hmod);
       }
       if (L.qjl) {
         uint32_t* sw = reinterpret_cast<uint32_t*>(hb + L.k_signs);
@@ -392,23 +414,28 @@ __device__ void encode_group(Smem& sm, const AppendArgs& a, const DevTables& t, 
     } else {
       float* vn = reinterpret_cast<float*>(hb + L.v_norm);
       if (tid >= vlo && tid < vhi) vn[slot0 + tid] = sm.n32[tid];
-      // group-interleaved value codes: coordinate tid, words w = 0..bV-1
-      uint32_t* gw = reinterpret_cast<uint32_t*>(hb + L.v_codes) + static_cast<int64_t>(slot0 / kVGroup) * L.bV * kD;
+      // group-interleaved value codes: coordinate tid, words w = 0..width-1
+      // (mixed rate: a low-rate block [bV][d/2], then a high-rate block [bV+1][d/2])
+      uint32_t* gw = reinterpret_cast<uint32_t*>(hb + L.v_codes) + static_cast<int64_t>(slot0 / kVGroup) * 8 * L.v_rec;
+      const bool hi = L.vmix && mixed_hi(tid, kValHiMod);
+      const int width = L.bV + (hi ? 1 : 0);
+      const int stride = L.vmix ? kD / 2 : kD;
+      const int at0 = L.vmix ? (hi ? L.bV * (kD / 2) : 0) + mixed_rank(tid, kValHiMod) : tid;
 #pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        if (w >= L.bV) break;
-        uint32_t word = gw[w * kD + tid];
+      for (int w = 0; w < 5; ++w) {
+        if (w >= width) break;
+        uint32_t word = gw[at0 + w * stride];
         for (int v = vlo; v < vhi; ++v) {
           const uint32_t c = sm.code[v][tid];
-          for (int k = 0; k < L.bV; ++k) {
-            const int p = v * L.bV + k;
+          for (int k = 0; k < width; ++k) {
+            const int p = v * width + k;
             if ((p >> 5) == w) {
               const uint32_t m = 1u << (p & 31);
               word = (word & ~m) | (((c >> k) & 1u) << (p & 31));
             }
           }
         }
-        gw[w * kD + tid] = word;
+        gw[at0 + w * stride] = word;
       }
     }
     __syncthreads();
@@ -459,8 +486,9 @@ __global__ void append_commit_kernel(AppendArgs a, DevTables t, Layout L, int W,
         const int valid = sp.c1 - pg * L.P < L.P ? sp.c1 - pg * L.P : L.P;
         hd[0] = kMagic;
         hd[1] = 1u | (static_cast<uint32_t>(L.d) << 16);
-        hd[2] = static_cast<uint32_t>(L.bK) | (static_cast<uint32_t>(qjl_code) << 8) |
-                (static_cast<uint32_t>(L.bV) << 16) | (static_cast<uint32_t>(rotation) << 24);
+        // bits bytes: b, or b + 16 for a mixed-channel rate b + 1/2
+        hd[2] = static_cast<uint32_t>(L.bK + 16 * L.kmix) | (static_cast<uint32_t>(qjl_code) << 8) |
+                (static_cast<uint32_t>(L.bV + 16 * L.vmix) << 16) | (static_cast<uint32_t>(rotation) << 24);
         hd[3] = static_cast<uint32_t>(L.H) | (static_cast<uint32_t>(L.P) << 16);
         hd[4] = static_cast<uint32_t>(valid);
         hd[5] = 1u;
@@ -483,13 +511,16 @@ int launch_encode(const tq_ctx* c, int kind, int dtype, const EncodeArgs& a, voi
   hipStream_t s = static_cast<hipStream_t>(stream);
   const int bits = kind == TQ_KIND_KEY ? c->p.key_bits : c->p.value_bits;
   const int qjl = (kind == TQ_KIND_KEY && c->p.key_qjl) ? 1 : 0;
+  const int mixed = (kind == TQ_KIND_KEY ? c->p.key_mixed : c->p.value_mixed) ? 1 : 0;
   const int64_t tiles = (a.n + kTile - 1) / kTile;
   if (tiles > 0x7fffffff) return 1;
   dim3 grid(static_cast<unsigned>(tiles));
   if (c->p.rotation == TQ_ROT_HADAMARD)
-    hipLaunchKernelGGL(encode_flat_kernel<true>, grid, dim3(kThreads), 0, s, a, c->t, c->cb, kind, dtype, bits, qjl);
+    hipLaunchKernelGGL(encode_flat_kernel<true>, grid, dim3(kThreads), 0, s, a, c->t, c->cb, kind, dtype, bits, qjl,
+                       mixed);
   else
-    hipLaunchKernelGGL(encode_flat_kernel<false>, grid, dim3(kThreads), 0, s, a, c->t, c->cb, kind, dtype, bits, qjl);
+    hipLaunchKernelGGL(encode_flat_kernel<false>, grid, dim3(kThreads), 0, s, a, c->t, c->cb, kind, dtype, bits, qjl,
+                       mixed);
   return hipGetLastError() == hipSuccess ? 0 : 1;
 }
 

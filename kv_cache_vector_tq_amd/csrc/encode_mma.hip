@@ -338,6 +338,8 @@ int launch_encode_mma(const tq_ctx* c, int kind, int dtype, const EncodeArgs& a,
       (reinterpret_cast<uintptr_t>(a.x) % 16) != 0)
     return 1;
   const bool key = kind == TQ_KIND_KEY;
+  // mixed-channel rates take the vector-ALU encoder
+  if (key ? c->p.key_mixed : c->p.value_mixed) return 1;
   const bool qjl = key && c->p.key_qjl;
   const bool had = c->p.rotation == TQ_ROT_HADAMARD;
   const int bits = key ? c->p.key_bits : c->p.value_bits;

@@ -25,12 +25,19 @@ bool params_ok(const tq_params* p) {
   if (p->flags & ~TQ_FLAG_VALU_SCAN) return false;
   if (p->qjl_kind != TQ_QJL_GAUSSIAN && p->qjl_kind != TQ_QJL_ORTHOGONAL) return false;
   if (!(p->qjl_shrink > 0.0f && p->qjl_shrink <= 4.0f)) return false;  // also rejects NaN
+  // mixed-channel rates: 2.5 and 3.5 bits, halves of a multiple of 32 coordinates
+  if (p->key_mixed != 0 && p->key_mixed != 1) return false;
+  if (p->value_mixed != 0 && p->value_mixed != 1) return false;
+  if (p->key_mixed && (p->key_bits < 2 || p->key_bits > 3 || p->head_dim % 32)) return false;
+  if (p->value_mixed && (p->value_bits < 2 || p->value_bits > 3 || p->head_dim % 32)) return false;
   return true;
 }
 
 // What the kernels in this build cover.
 bool params_supported(const tq_params* p) {
   const int G = p->num_q_heads / p->num_kv_heads;
+  // the vector-ALU scan covers integer rates only
+  if ((p->flags & TQ_FLAG_VALU_SCAN) && (p->key_mixed || p->value_mixed)) return false;
   return p->head_dim == tq::kD && (G == 1 || G == 2 || G == 4 || G == 8) && p->num_kv_heads <= 65535;
 }
 
@@ -136,6 +143,14 @@ TQ_API int tq_host_tables(const tq_params* p, const double* rot_draws, const dou
   }
   tq::codebook_f32(p->key_bits, d, key_centroids, key_boundaries);
   tq::codebook_f32(p->value_bits, d, value_centroids, value_boundaries);
+  // mixed-channel rates: the (b+1)-bit codebook follows the b-bit one
+  auto after = [](float* a, int n) { return a ? a + n : nullptr; };
+  if (p->key_mixed)
+    tq::codebook_f32(p->key_bits + 1, d, after(key_centroids, 1 << p->key_bits),
+                     after(key_boundaries, (1 << p->key_bits) - 1));
+  if (p->value_mixed)
+    tq::codebook_f32(p->value_bits + 1, d, after(value_centroids, 1 << p->value_bits),
+                     after(value_boundaries, (1 << p->value_bits) - 1));
   return TQ_OK;
 }
 
@@ -152,11 +167,25 @@ TQ_API int tq_codebook_init(tq_ctx** out, const tq_params* p, const double* rot_
   c->lay = tq::make_layout(*p);
   std::vector<float> rot(d * d, 0.0f), rotT(d * d, 0.0f), S(d * d, 0.0f), ST(d * d, 0.0f);
   std::memset(&c->cb, 0, sizeof(c->cb));
+  float kc[48] = {}, kb[48] = {}, vc[48] = {}, vb[48] = {};
   int rc = tq_host_tables(p, rot_draws, p->key_qjl ? qjl_draws : nullptr, rot.data(),
-                          p->key_qjl ? S.data() : nullptr, c->cb.kc, c->cb.kb, c->cb.vc, c->cb.vb);
+                          p->key_qjl ? S.data() : nullptr, kc, kb, vc, vb);
   if (rc != TQ_OK) {
     delete c;
     return rc;
+  }
+  const int nk = 1 << p->key_bits, nv = 1 << p->value_bits;
+  std::memcpy(c->cb.kc, kc, nk * sizeof(float));
+  std::memcpy(c->cb.kb, kb, (nk - 1) * sizeof(float));
+  std::memcpy(c->cb.vc, vc, nv * sizeof(float));
+  std::memcpy(c->cb.vb, vb, (nv - 1) * sizeof(float));
+  if (p->key_mixed) {
+    std::memcpy(c->cb.kc2, kc + nk, 2 * nk * sizeof(float));
+    std::memcpy(c->cb.kb2, kb + nk - 1, (2 * nk - 1) * sizeof(float));
+  }
+  if (p->value_mixed) {
+    std::memcpy(c->cb.vc2, vc + nv, 2 * nv * sizeof(float));
+    std::memcpy(c->cb.vb2, vb + nv - 1, (2 * nv - 1) * sizeof(float));
   }
   if (p->rotation == TQ_ROT_DENSE) transpose(rot.data(), rotT.data(), d);
   transpose(S.data(), ST.data(), d);

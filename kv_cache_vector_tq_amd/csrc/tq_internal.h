@@ -1,6 +1,8 @@
 // Internal declarations shared by the host API and the HIP kernels.
 #pragma once
 
+#include <hip/hip_runtime.h>
+
 #include <cstdint>
 #include <vector>
 
@@ -21,11 +23,24 @@ void codebook_f32(int bits, int d, float* centroids, float* boundaries);
 void haar_rotation_f32(const double* g, int d, float* out);
 
 // Byte offsets of one head's streams inside its head block, and page sizes.
+// kmix / vmix: mixed-channel rate b + 1/2 (half the coordinates at b + 1 bits).
 struct Layout {
-  int P, bK, bV, qjl, H, d;
+  int P, bK, bV, qjl, H, d, kmix, vmix;
+  int k_rec, v_rec;  // code bytes of one key record / one token's value codes
   int64_t k_norm, k_rnorm, k_codes, k_signs, v_norm, v_codes;
   int64_t head_bytes, page_bytes;
 };
+
+// Mixed-channel rates: coordinate j takes b + 1 bits when j mod M >= M / 2,
+// with M = 32 for keys and 8 for values; a key record (and a value group)
+// holds the low-rate half first.  Rank of coordinate j within its half:
+constexpr int kKeyHiMod = 32, kValHiMod = 8;
+__host__ __device__ inline bool mixed_hi(int j, int mod) { return (j % mod) >= mod / 2; }
+__host__ __device__ inline int mixed_rank(int j, int mod) { return (j / mod) * (mod / 2) + (j % mod) % (mod / 2); }
+// Coordinate of rank r in the low (hi = 0) or high half.
+__host__ __device__ inline int mixed_coord(int r, int hi, int mod) {
+  return (r / (mod / 2)) * mod + (hi ? mod / 2 : 0) + r % (mod / 2);
+}
 
 inline Layout make_layout(const tq_params& p) {
   Layout l{};
@@ -35,19 +50,23 @@ inline Layout make_layout(const tq_params& p) {
   l.qjl = p.key_qjl ? 1 : 0;
   l.H = p.num_kv_heads;
   l.d = p.head_dim;
+  l.kmix = p.key_mixed ? 1 : 0;
+  l.vmix = p.value_mixed ? 1 : 0;
+  l.k_rec = l.d * l.bK / 8 + (l.kmix ? l.d / 16 : 0);
+  l.v_rec = l.d * l.bV / 8 + (l.vmix ? l.d / 16 : 0);
   int64_t off = 0;
   l.k_norm = off;
   off += 4LL * l.P;
   l.k_rnorm = off;
   if (l.qjl) off += 4LL * l.P;
   l.k_codes = off;
-  off += int64_t(l.P) * l.d * l.bK / 8;
+  off += int64_t(l.P) * l.k_rec;
   l.k_signs = off;
   if (l.qjl) off += int64_t(l.P) * l.d / 8;
   l.v_norm = off;
   off += 4LL * l.P;
   l.v_codes = off;
-  off += int64_t(l.P) * l.d * l.bV / 8;
+  off += int64_t(l.P) * l.v_rec;
   l.head_bytes = off;
   l.page_bytes = (kBodyOffset + int64_t(l.H) * off + 255) / 256 * 256;
   return l;
@@ -62,9 +81,11 @@ struct DevTables {
   int* status;         // status word (TQ_STATUS_* bits)
 };
 
-// Codebook values passed by value to kernels (uniform across lanes).
+// Codebook values passed by value to kernels (uniform across lanes); the
+// "2" arrays are the (b+1)-bit codebooks of mixed-channel rates.
 struct Codebooks {
   float kc[16], kb[16], vc[16], vb[16];
+  float kc2[16], kb2[16], vc2[16], vb2[16];
 };
 
 struct EncodeArgs {

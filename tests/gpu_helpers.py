@@ -27,7 +27,7 @@ def params_for(setup, flags=0):
         rotation=tqa.TQ_ROT_DENSE if setup.rotation == "dense" else tqa.TQ_ROT_HADAMARD,
         num_q_heads=setup.Hq, num_kv_heads=setup.Hkv, page_tokens=setup.P, window=setup.W, seed=setup.seed,
         qjl_kind=tqa.TQ_QJL_ORTHOGONAL if setup.qjl_kind == "orthogonal" else tqa.TQ_QJL_GAUSSIAN,
-        qjl_shrink=setup.qjl_shrink)
+        qjl_shrink=setup.qjl_shrink, key_mixed=int(setup.kmix), value_mixed=int(setup.vmix))
 
 
 def context_for(setup, flags=0):
@@ -39,7 +39,11 @@ def code_band(x, R, cb):
     x = np.asarray(x, dtype=np.float64)
     n = np.linalg.norm(x, axis=1)
     y = R.forward(x / np.where(n > 0, n, 1.0)[:, None]).astype(np.float32).astype(np.float64)
-    dist = np.min(np.abs(y[..., None] - cb.boundaries[None, None, :]), axis=-1)
+    near = lambda bnd: np.min(np.abs(y[..., None] - bnd[None, None, :]), axis=-1)
+    if getattr(cb, "mixed", False):  # each half against its own codebook
+        dist = np.where(cb.hi_mask, near(cb.hi.boundaries), near(cb.lo.boundaries))
+    else:
+        dist = near(cb.boundaries)
     return (dist < BAND) & (n[:, None] > 0)
 
 

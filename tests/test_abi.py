@@ -56,6 +56,7 @@ def test_target_page_size(L):
     ("key_bits", 1), ("key_bits", 5), ("value_bits", 0), ("key_qjl", 2), ("rotation", 7),
     ("num_q_heads", 6), ("num_kv_heads", 0), ("page_tokens", 48), ("page_tokens", 2048), ("window", -1),
     ("head_dim", 0), ("qjl_kind", 2), ("qjl_shrink", 0.0), ("qjl_shrink", 5.0), ("qjl_shrink", float("nan")),
+    ("key_mixed", 2), ("value_mixed", -1),
 ])
 def test_bad_params_rejected(L, field, value):
     p = tqa.make_params(num_q_heads=8, num_kv_heads=4)
@@ -134,3 +135,39 @@ def test_library_hadamard_signs(L):
     draws = tq_inputs.hadamard_draws(3, 128)
     t = tqa.tq_host_tables(p, draws, tq_inputs.qjl_draws(3, 128))
     assert np.array_equal(t["rotation"], rot.rademacher_signs(draws).astype(np.float32))
+
+
+@pytest.mark.parametrize("kb,kmix,vb,vmix", [(4, 1, 3, 0), (3, 0, 4, 1)])
+def test_mixed_needs_two_or_three_bits(L, kb, kmix, vb, vmix):
+    """Mixed-channel rates exist for 2.5 and 3.5 bits only."""
+    p = tqa.make_params(key_bits=kb, key_mixed=kmix, value_bits=vb, value_mixed=vmix)
+    assert L.tq_page_bytes(ctypes.byref(p)) == tqa.TQ_ERR_INVALID_ARG
+
+
+def test_mixed_unsupported_on_valu_scan(L):
+    """The vector-ALU scan covers integer rates only: rejected at init, before any HIP call."""
+    p = tqa.make_params(key_bits=3, key_mixed=1, flags=tqa.TQ_FLAG_VALU_SCAN)
+    out = ctypes.c_void_p()
+    d = np.zeros(128 * 128)
+    assert L.tq_codebook_init(ctypes.byref(out), ctypes.byref(p), d.ctypes.data, d.ctypes.data, None) == \
+        tqa.TQ_ERR_UNSUPPORTED
+
+
+@pytest.mark.parametrize("kb,kmix,vb,vmix,H,P", [(3, 1, 3, 0, 8, 256), (2, 1, 2, 1, 2, 64), (4, 0, 3, 1, 1, 32)])
+def test_mixed_page_bytes_match_layout(L, kb, kmix, vb, vmix, H, P):
+    p = tqa.make_params(key_bits=kb, key_mixed=kmix, value_bits=vb, value_mixed=vmix, num_q_heads=H,
+                        num_kv_heads=H, page_tokens=P)
+    assert tqa.tq_page_bytes(p) == pages.Layout(128, kb, 1, vb, H, P, kmix, vmix).page_bytes
+
+
+@pytest.mark.parametrize("bits", [2, 3])
+def test_library_mixed_codebooks_equal_oracle(L, bits):
+    """The b-bit and (b+1)-bit codebooks of a mixed rate, in that order."""
+    from oracle import mixed
+    p = tqa.make_params(key_bits=bits, key_mixed=1, value_bits=bits, value_mixed=1)
+    t = tqa.tq_host_tables(p, tq_inputs.rotation_draws(0, 128), tq_inputs.qjl_draws(0, 128))
+    for kind in ("key", "value"):
+        cb = mixed.MixedCodebook(bits, 128, kind)
+        assert np.array_equal(t[kind + "_centroids"].astype(np.float64), np.concatenate([cb.lo.centroids, cb.hi.centroids]))
+        assert np.array_equal(t[kind + "_boundaries"].astype(np.float64),
+                              np.concatenate([cb.lo.boundaries, cb.hi.boundaries]))

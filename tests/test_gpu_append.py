@@ -52,8 +52,8 @@ def _compare_caches(s, ref, pool_gpu, kwin, vwin, lens_gpu):
             x = ref._src_k[(b, h)][:C]
             xv = ref._src_v[(b, h)][:C]
             assert np.array_equal(kg.norms, kr.norms) and np.array_equal(vng, vnr)
-            gidx = codec.unpack_bits(kg.codes, s.bK, 128)
-            check_codes(x, gidx, codec.unpack_bits(kr.codes, s.bK, 128), s.R, s.kcb)
+            gidx = s.kcb.unpack(kg.codes, 128)
+            check_codes(x, gidx, s.kcb.unpack(kr.codes, 128), s.R, s.kcb)
             check_codes(xv, vig, vir, s.R, s.vcb)
             if s.qjl:
                 check_signs(x, gidx, kg.norms, kg.signs, s.R, s.kcb, s.S)
@@ -75,6 +75,13 @@ CASES = [
     ("hadamard_k2v2_W0", dict(Hq=8, Hkv=1, key_bits=2, value_bits=2, rotation="hadamard", W=0, P=32), [100, 33]),
     ("k4_noqjl_v3", dict(Hq=2, Hkv=2, key_bits=4, key_qjl=0, value_bits=3, W=16, P=32), [77, 16, 15]),
     ("orthoS_shrink", dict(Hq=4, Hkv=2, W=32, P=64, qjl_kind="orthogonal", qjl_shrink=2 / np.pi), [200, 33]),
+    # mixed-channel rates (keys / values at 2.5 or 3.5 bits)
+    ("mixed_k35_v35", dict(Hq=4, Hkv=2, W=32, P=64, key_bits=3, value_bits=3, key_mixed=True, value_mixed=True),
+     [200, 33]),
+    ("mixed_k25_v4_hadamard", dict(Hq=8, Hkv=2, W=16, P=32, key_bits=2, key_mixed=True, value_bits=4,
+                                   rotation="hadamard"), [100, 47]),
+    ("mixed_k3_v25_noqjl", dict(Hq=2, Hkv=2, key_bits=3, key_qjl=0, value_bits=2, value_mixed=True, W=0, P=32),
+     [77, 16]),
 ]
 
 

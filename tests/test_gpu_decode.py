@@ -44,10 +44,33 @@ CASES = [
                                   qjl_kind="orthogonal", qjl_shrink=0.7), [500, 33]),
 ]
 
+# mixed-channel rates (keys / values at 2.5 or 3.5 bits); matrix-core scan only
+MIXED = [
+    ("mixed_k35_v3_gqa4", dict(Hq=8, Hkv=2, key_bits=3, key_mixed=True, value_bits=3, W=64), [700, 129, 1]),
+    ("mixed_k35_v4_wide", dict(Hq=8, Hkv=2, key_bits=3, key_mixed=True, value_bits=4, W=32), [600, 65]),
+    ("mixed_k35_v35", dict(Hq=4, Hkv=4, key_bits=3, key_mixed=True, value_bits=3, value_mixed=True, W=16,
+                           P=64), [333, 64, 17]),
+    ("mixed_k25_v25_hadamard", dict(Hq=8, Hkv=1, key_bits=2, key_mixed=True, value_bits=2, value_mixed=True,
+                                    rotation="hadamard", W=128), [900, 300]),
+    ("mixed_k4_v35_noqjl", dict(Hq=2, Hkv=2, key_bits=4, key_qjl=0, value_bits=3, value_mixed=True, P=32, W=0),
+     [95, 32, 31]),
+    ("mixed_k3_v25_gqa8_orthoS", dict(Hq=16, Hkv=2, key_bits=3, value_bits=2, value_mixed=True, W=32,
+                                      qjl_kind="orthogonal", qjl_shrink=2 / np.pi), [500, 33]),
+]
+
 
 @pytest.mark.parametrize("kernel", ["mfma", "valu"])
 @pytest.mark.parametrize("name,kw,lens", CASES, ids=[c[0] for c in CASES])
 def test_decode_parity_oracle_pages(name, kw, lens, kernel):
+    _decode_parity(name, kw, lens, kernel)
+
+
+@pytest.mark.parametrize("name,kw,lens", MIXED, ids=[c[0] for c in MIXED])
+def test_decode_parity_mixed_rates(name, kw, lens):
+    _decode_parity(name, kw, lens, "mfma")
+
+
+def _decode_parity(name, kw, lens, kernel):
     print(f"case {name} {kernel}", flush=True)
     s = Setup(**kw)
     cache = s.cache(len(lens), max(lens))

@@ -25,10 +25,10 @@ from oracle_cache import Setup, fill
 pytestmark = pytest.mark.gpu
 
 
-def _records(ctx, kind, x16, qjl, bits):
+def _records(ctx, kind, x16, qjl, bits, mixed=False):
     n = x16.shape[0]
     xt = torch.from_numpy(x16.astype(np.float32)).to(torch.float16).cuda()
-    codes = torch.zeros((n, 16 * bits), dtype=torch.uint8, device="cuda")
+    codes = torch.zeros((n, 16 * bits + (8 if mixed else 0)), dtype=torch.uint8, device="cuda")
     norms = torch.zeros(n, dtype=torch.float32, device="cuda")
     signs = torch.zeros((n, 16), dtype=torch.uint8, device="cuda") if qjl else None
     rnorms = torch.zeros(n, dtype=torch.float32, device="cuda") if qjl else None
@@ -111,3 +111,28 @@ def test_quality_report():
     g = res[("gaussian", 1.0)]["logit_rmse"]
     assert res[("orthogonal", 1.0)]["logit_rmse"] < g
     assert res[("orthogonal", 2 / math.pi)]["logit_rmse"] < g
+
+
+@pytest.mark.parametrize("rotation", ["dense", "hadamard"])
+@pytest.mark.parametrize("bits", [2, 3])
+def test_dequant_parity_mixed(rotation, bits):
+    """Mixed-channel records (bits + 1/2) dequantise like the oracle's."""
+    print(f"case dequant mixed {rotation} bits={bits}+", flush=True)
+    s = Setup(key_bits=bits, value_bits=bits, rotation=rotation, key_mixed=True, value_mixed=True)
+    ctx = context_for(s)
+    n = 300
+    x = tq_inputs.keys(3, 128, np.arange(n)).astype(np.float64)
+    x[5] = 0.0
+    x16 = tq_inputs.fp16(x)
+    for kind, cb, qjl in ((tqa.TQ_KIND_KEY, s.kcb, True), (tqa.TQ_KIND_VALUE, s.vcb, False)):
+        codes, norms, signs, rnorms = _records(ctx, kind, x16, qjl, bits, mixed=True)
+        out = torch.full((n, 128), float("nan"), dtype=torch.float32, device="cuda")
+        tqa.tq_decode(ctx, kind, codes, norms, out, signs, rnorms)
+        torch.cuda.synchronize()
+        cpu = lambda t: None if t is None else t.cpu().numpy()
+        ref = codec.dequantize(cpu(codes), cpu(norms), s.R, cb, cpu(signs), cpu(rnorms), s.S if qjl else None,
+                               s.qjl_coef)
+        got = cpu(out)
+        scale = np.maximum(np.linalg.norm(ref, axis=1), 1e-30)
+        assert np.all(np.max(np.abs(got - ref), axis=1) <= 2e-6 * scale + 1e-30)
+        assert np.all(got[5] == 0.0)

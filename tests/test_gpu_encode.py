@@ -25,9 +25,11 @@ def _inputs(n, seed=0):
 
 def _gpu_encode(ctx, kind, x16, qjl, dtype=torch.float16):
     n = x16.shape[0]
-    bits = ctx.params.key_bits if kind == tqa.TQ_KIND_KEY else ctx.params.value_bits
+    key = kind == tqa.TQ_KIND_KEY
+    bits = ctx.params.key_bits if key else ctx.params.value_bits
+    mixed = ctx.params.key_mixed if key else ctx.params.value_mixed
     xt = torch.from_numpy(x16.astype(np.float32)).to(dtype).cuda()
-    codes = torch.zeros((n, 16 * bits), dtype=torch.uint8, device="cuda")
+    codes = torch.zeros((n, 16 * bits + (8 if mixed else 0)), dtype=torch.uint8, device="cuda")
     norms = torch.zeros(n, dtype=torch.float32, device="cuda")
     signs = torch.zeros((n, 16), dtype=torch.uint8, device="cuda") if qjl else None
     rnorms = torch.zeros(n, dtype=torch.float32, device="cuda") if qjl else None
@@ -89,3 +91,32 @@ def test_encode_repeatable():
     b = _gpu_encode(ctx, tqa.TQ_KIND_KEY, x16, True)
     for u, v in zip(a, b):
         assert np.array_equal(u, v)
+
+
+@pytest.mark.parametrize("rotation", ["dense", "hadamard"])
+@pytest.mark.parametrize("bK,kmix,bV,vmix", [(3, 1, 3, 1), (2, 1, 2, 1), (3, 1, 4, 0), (4, 0, 2, 1)])
+@pytest.mark.parametrize("n", [1024, 77])
+def test_encode_parity_mixed(rotation, bK, kmix, bV, vmix, n):
+    """Mixed-channel rates (2.5 / 3.5 bits): records as the oracle packs them
+    (low-rate half first), codes and signs under the guard-band rule."""
+    s = Setup(key_bits=bK, value_bits=bV, rotation=rotation, key_mixed=kmix, value_mixed=vmix)
+    ctx = context_for(s)
+    x16 = _inputs(n, seed=2)
+    x = x16.astype(np.float64)
+    print(f"case mixed rotation={rotation} bK={bK}{'+' if kmix else ''} bV={bV}{'+' if vmix else ''} n={n}", flush=True)
+    codes, norms, signs, rnorms = _gpu_encode(ctx, tqa.TQ_KIND_KEY, x16, True)
+    ref = codec.encode(x, s.R, s.kcb, s.S)
+    assert codes.shape[1] == s.kcb.record_bytes(128)
+    assert np.array_equal(norms, ref.norms)
+    gidx = s.kcb.unpack(codes, 128)
+    nband = check_codes(x, gidx, ref.idx, s.R, s.kcb)
+    check_signs(x, gidx, norms, signs, s.R, s.kcb, s.S)
+    r = codec.residual_from_codes(x, s.R, s.kcb, norms, gidx)
+    assert np.allclose(rnorms, np.linalg.norm(r, axis=1), rtol=1e-5, atol=1e-30)
+    assert nband <= 0.002 * x.size
+    assert np.array_equal(codes[~np.any(gidx != ref.idx, axis=1)], ref.codes[~np.any(gidx != ref.idx, axis=1)])
+    vcodes, vnorms, _, _ = _gpu_encode(ctx, tqa.TQ_KIND_VALUE, x16, False)
+    vref = codec.encode(x, s.R, s.vcb)
+    assert vcodes.shape[1] == s.vcb.record_bytes(128)
+    assert np.array_equal(vnorms, vref.norms)
+    check_codes(x, s.vcb.unpack(vcodes, 128), vref.idx, s.R, s.vcb)
