@@ -43,12 +43,16 @@ def parse():
     ap.add_argument("--T", type=int, default=32768)
     ap.add_argument("--batch", type=int, default=16)
     ap.add_argument("--valu-scan", action="store_true", help="time the vector-ALU scan kernel instead")
+    ap.add_argument("--key-bits", type=int, default=3)
+    ap.add_argument("--value-bits", type=int, default=4)
+    ap.add_argument("--key-mixed", action="store_true", help="keys at key_bits + 1/2 (mixed-channel rate)")
+    ap.add_argument("--value-mixed", action="store_true", help="values at value_bits + 1/2")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy (reference for HBM byte counters)")
     return ap.parse_args()
 
 
-def cpu_baseline(T, W, P, G, Hkv, min_seconds):
+def cpu_baseline(T, W, P, G, Hkv, min_seconds, kbits=3, vbits=4, kmix=0, vmix=0):
     """The oracle's decode (dequantise + float64 softmax attention) on one
     sequence and one KV head (G query heads) at context T, repeated until
     min_seconds of CPU work; converted to sequence-tokens/s at H_kv heads."""
@@ -57,7 +61,8 @@ def cpu_baseline(T, W, P, G, Hkv, min_seconds):
     from oracle import attention as att
     from oracle_cache import Setup, fill
     import tq_inputs
-    s = Setup(Hq=G, Hkv=1, key_bits=3, key_qjl=1, value_bits=4, P=P, W=W)
+    s = Setup(Hq=G, Hkv=1, key_bits=kbits, key_qjl=1, value_bits=vbits, P=P, W=W, key_mixed=bool(kmix),
+              value_mixed=bool(vmix))
     cache = s.cache(1, T)
     fill(s, cache, [T])
     q = tq_inputs.queries(3, (1, G, 128))
@@ -159,9 +164,10 @@ def main():
     Tf = args.T
     nsteps = args.warmup + args.steps
     T0 = Tf - nsteps
-    params = tqa.make_params(key_bits=3, key_qjl=1, value_bits=4, rotation=tqa.TQ_ROT_DENSE, num_q_heads=Hq,
+    kbits, vbits, kmix, vmix = args.key_bits, args.value_bits, int(args.key_mixed), int(args.value_mixed)
+    params = tqa.make_params(key_bits=kbits, key_qjl=1, value_bits=vbits, rotation=tqa.TQ_ROT_DENSE, num_q_heads=Hq,
                              num_kv_heads=Hkv, page_tokens=P, window=W, seed=0,
-                             flags=tqa.TQ_FLAG_VALU_SCAN if args.valu_scan else 0)
+                             flags=tqa.TQ_FLAG_VALU_SCAN if args.valu_scan else 0, key_mixed=kmix, value_mixed=vmix)
     ctx = tqa.Context(params, tq_inputs.rotation_draws(0, d), tq_inputs.qjl_draws(0, d))
     pb = tqa.tq_page_bytes(params)
     max_pages = -(-(Tf - W) // P)
@@ -208,7 +214,8 @@ def main():
     # tokens attended in the timed steps: after step i the length is T0 + i + 1
     lens = [T0 + i + 1 for i in range(args.warmup, nsteps)]
     tokens = B * sum(lens)
-    per_tok_head = (48 + 16 + 4 + 4) + (64 + 4)   # key 3-bit + signs + norm + rnorm, value 4-bit + norm
+    # key codes + signs + norm + rnorm, value codes + norm (a mixed rate adds d/16 code bytes)
+    per_tok_head = (16 * kbits + 8 * kmix + 16 + 4 + 4) + (16 * vbits + 8 * vmix + 4)
     comp_bytes = [B * Hkv * (T - W) * per_tok_head for T in lens]
     win_bytes = B * Hkv * W * d * 2 * 2
     scan_s = scan_ms / 1e3 / max(ncalls, 1)
@@ -219,8 +226,9 @@ def main():
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_step, "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
         "config": {"workload": f"decode step (append 1 token + decode attention), B={B}, Hq={Hq}, Hkv={Hkv}, "
-                               f"d={d}, T={Tf} (last step), W={W} fp16 window, P={P}, keys 3-bit+QJL, values "
-                               f"4-bit, dense rotation, bf16 queries",
+                               f"d={d}, T={Tf} (last step), W={W} fp16 window, P={P}, keys "
+                               f"{kbits + 0.5 * kmix:g}-bit+QJL, values {vbits + 0.5 * vmix:g}-bit, dense rotation, "
+                               f"bf16 queries",
                    "batch": B, "seq_len": Tf, "parallelism": "none (1 GPU)"},
         "hbm_gbps_step": (sum(comp_bytes) / len(comp_bytes) + win_bytes) / (ms_step / 1e3) / 1e9,
         "scan_us": scan_s * 1e6,
@@ -240,10 +248,11 @@ def main():
     res["read_ceiling"] = {"GBps": read_gbps, "bytes": 1 << 30, "kernel": "tq_read_probe (coalesced 16-byte loads)",
                            "frac_of_peak": read_gbps / HBM_PEAK_GBPS}
     res["roofline"]["frac_of_read_ceiling"] = achieved / read_gbps
-    if not args.no_encode:
+    # the encode leg measures the default formats (3-bit+QJL keys, 4-bit values)
+    if not args.no_encode and (kbits, vbits, kmix, vmix) == (3, 4, 0, 0):
         res["encode"] = encode_leg(tqa, tq_inputs, ctx, params)
     if not args.no_cpu_baseline:
-        res["cpu_baseline"] = cpu_baseline(Tf, W, P, G, Hkv, args.cpu_seconds)
+        res["cpu_baseline"] = cpu_baseline(Tf, W, P, G, Hkv, args.cpu_seconds, kbits, vbits, kmix, vmix)
     print(json.dumps(res), flush=True)
 
 

@@ -226,16 +226,28 @@ struct Meta {
 // piece (MFMAs i = 0, 1) and a high-rate piece (i = 2, 3); value MFMA bl
 // reads the low-rate word block for bl < 4 and the high-rate one otherwise,
 // so every operand slice has one compile-time width.
+// Register budget: 128 VGPRs (four waves per SIMD), except where that would
+// spill inside the loop: 3-bit values (two words per value slice), mixed
+// rates (two tables per operand side) and G = 8 (whose LDS already caps a CU
+// at three work-groups) get 168 (three waves).  Measured at B=16, T=32K:
+// keys 3 / values 3 166 -> 132 us, keys 3.5 / values 3 201 -> 136 us.
+template <int G, int BV, bool KMIX, bool VMIX>
+constexpr int scan_waves_per_simd() { return (BV == 3 || KMIX || VMIX || G == 8) ? 3 : 4; }
+
 template <int G, int BK, int BV, bool QJL, bool KMIX, bool VMIX>
-__global__ __launch_bounds__((ScanShape<G, BV, VMIX>::kThreads), 4) void scan_mfma_kernel(DecodeArgs a, DevTables t,
-                                                                                         Codebooks cb, KParams k) {
+__global__ __launch_bounds__((ScanShape<G, BV, VMIX>::kThreads), (scan_waves_per_simd<G, BV, KMIX, VMIX>())) void
+scan_mfma_kernel(DecodeArgs a, DevTables t, Codebooks cb, KParams k) {
   using Sh = ScanShape<G, BV, VMIX>;
   constexpr bool kWide = Sh::kWide;
   constexpr int kThreads = Sh::kThreads, kWaves = Sh::kWaves;
   // One array: the key table (absent when keys and values share a bit width,
   // hence a codebook) first, so that every table address stays within the
   // 16-bit immediate offset of the LDS instructions.
-  constexpr int kKeyWords = BK == BV ? 0 : PairLut<BK>::kWords;
+  // keys read the value table of their width when there is one (the
+  // codebook depends on the width only): BK == BV, or the high-rate half of
+  // mixed values when BK == BV + 1
+  constexpr bool kKeyInVhi = VMIX && BK == BV + 1;
+  constexpr int kKeyWords = (BK == BV || kKeyInVhi) ? 0 : PairLut<BK>::kWords;
   constexpr int kKeyHiWords = KMIX ? PairLut<BK + 1, 1>::kWords : 0;  // mixed keys: high-rate table, one copy
   constexpr int kValHiWords = VMIX ? PairLut<BV + 1>::kWords : 0;     // mixed values: high-rate table
   __shared__ uint32_t luts[kKeyWords + kKeyHiWords + Sh::kLutWords + kValHiWords];
@@ -304,7 +316,7 @@ __global__ __launch_bounds__((ScanShape<G, BV, VMIX>::kThreads), 4) void scan_mf
   } else {
     build_pair_lut<BV, kThreads>(lutV, cvv, tid);
   }
-  if constexpr (BK != BV) build_pair_lut<BK, kThreads>(lutKown, ck, tid);
+  if constexpr (BK != BV && !kKeyInVhi) build_pair_lut<BK, kThreads>(lutKown, ck, tid);
   if constexpr (KMIX) build_pair_lut<BK + 1, kThreads, 1>(lutKhi, ck2, tid);
   if constexpr (VMIX) build_pair_lut<BV + 1, kThreads>(lutVhi, cv2, tid);
   if (!kWide && tid < 16) {
@@ -312,7 +324,7 @@ __global__ __launch_bounds__((ScanShape<G, BV, VMIX>::kThreads), 4) void scan_mf
     lutN[e] = u2{(e & 1 ? 0x3C00u : 0xBC00u) | ((e & 2 ? 0x3C00u : 0xBC00u) << 16),
                  (e & 4 ? 0x3C00u : 0xBC00u) | ((e & 8 ? 0x3C00u : 0xBC00u) << 16)};
   }
-  const uint32_t* lutK = BK == BV ? lutV : lutKown;
+  const uint32_t* lutK = BK == BV ? lutV : kKeyInVhi ? lutVhi : lutKown;
   const uint32_t* lutKl = lutK + (PairLut<BK>::kCopies > 1 ? (tid & 31) : 0);
   const uint32_t* lutVl = lutV + (PairLut<BV>::kCopies > 1 ? (tid & 31) : 0);
   const uint32_t* lutVhil = lutVhi + ((VMIX && PairLut<BV + 1>::kCopies > 1) ? (tid & 31) : 0);
