@@ -25,16 +25,20 @@ constexpr int kSmallThreads = 256;
 
 // y[g][i] = sum_j M[j*kD + i] x[g][j] for the G vectors x (LDS), M a kD x kD
 // row-major table in global memory.  Thread (c, r) owns columns 4c..4c+3 and
-// rows 16r..16r+15: its 16 float4 loads are independent and in flight
-// together; the 8 row-group partials are summed in fixed order.  Called by
-// all kSmallThreads threads; ends with a barrier.
-template <int G>
-__device__ __forceinline__ void matvec_cols(const float* __restrict__ M, const float (*x)[kD],
-                                            float (*part)[G][kD], float (*y)[kD]) {
+// rows 16r..16r+15: its 16 float4 loads (load_cols, issued early by the
+// caller) are independent and in flight together; the 8 row-group partials
+// are summed in fixed order.  Called by all kSmallThreads threads; ends with a
+// barrier.
+__device__ __forceinline__ void load_cols(const float* __restrict__ M, float4 (&m)[16]) {
   const int t = threadIdx.x, c4 = (t & 31) * 4, rg = t >> 5;
-  float4 m[16];
 #pragma unroll
   for (int r = 0; r < 16; ++r) m[r] = *reinterpret_cast<const float4*>(M + (rg * 16 + r) * kD + c4);
+}
+
+template <int G>
+__device__ __forceinline__ void matvec_cols(const float4 (&m)[16], const float (*x)[kD], float (*part)[G][kD],
+                                            float (*y)[kD]) {
+  const int t = threadIdx.x, c4 = (t & 31) * 4, rg = t >> 5;
 #pragma unroll
   for (int g = 0; g < G; ++g) {
     float4 acc = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
@@ -94,14 +98,25 @@ __global__ __launch_bounds__(kSmallThreads) void prep_kernel(DecodeArgs a, DevTa
   const int tid = threadIdx.x, h = blockIdx.x, b = blockIdx.y;
   const int64_t row0 = (static_cast<int64_t>(b) * k.Hq + static_cast<int64_t>(h) * G) * kD;
   const float c2 = a.sm_scale * kLog2e;
-  for (int e = tid; e < G * kD; e += kSmallThreads) {
-    const float q = load_any(a.q, row0 + e, a.q_dtype);
-    a.qwin[row0 + e] = q * c2;
-    qv[e / kD][e % kD] = q;
+  // the query first, then both tables (independent of it), all in flight together
+  float qin[(G * kD + kSmallThreads - 1) / kSmallThreads];
+#pragma unroll
+  for (int u = 0; u * kSmallThreads < G * kD; ++u)
+    if (tid + u * kSmallThreads < G * kD) qin[u] = load_any(a.q, row0 + tid + u * kSmallThreads, a.q_dtype);
+  float4 mr[16], ms[16];
+  if (k.rotation == TQ_ROT_DENSE) load_cols(t.rotT, mr);
+  if (qjl) load_cols(t.ST, ms);
+#pragma unroll
+  for (int u = 0; u * kSmallThreads < G * kD; ++u) {
+    const int e = tid + u * kSmallThreads;
+    if (e < G * kD) {
+      a.qwin[row0 + e] = qin[u] * c2;
+      qv[e / kD][e % kD] = qin[u];
+    }
   }
   __syncthreads();
   if (k.rotation == TQ_ROT_DENSE) {
-    matvec_cols<G>(t.rotT, qv, part, qr);
+    matvec_cols<G>(mr, qv, part, qr);
   } else {
     hadamard_lds<G>(qv, t.rot, nullptr);
     for (int e = tid; e < G * kD; e += kSmallThreads) qr[e / kD][e % kD] = qv[e / kD][e % kD];
@@ -109,7 +124,7 @@ __global__ __launch_bounds__(kSmallThreads) void prep_kernel(DecodeArgs a, DevTa
   }
   for (int e = tid; e < G * kD; e += kSmallThreads) a.qs[row0 + e] = qr[e / kD][e % kD] * c2;
   if (!qjl) return;
-  matvec_cols<G>(t.ST, qr, part, qv);  // qv <- S q_rot
+  matvec_cols<G>(ms, qr, part, qv);  // qv <- S q_rot
   const float sc = k.qjl_scale * c2;
   const int lane = tid & 63, w = tid >> 6;
   for (int g = w; g < G; g += 4) {
@@ -315,9 +330,9 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(DecodeArgs a, DevTab
 // ---------------------------------------------------------------- merge
 // One work-group per (b, kv head) for its G query heads: the window K/V rows,
 // the split partials and Pi are each read once.  The kernel is a short chain
-// of dependent steps, so every independent load (window keys and values of
-// the first 128 slots, the columns of Pi) is issued at the start and lands
-// while the split partials are combined.
+// of dependent steps, so every load is issued at the start, the split
+// partials (needed first) ahead of the window keys and values of the first 128
+// slots and the columns of Pi, which land while the partials are combined.
 template <int G>
 __global__ __launch_bounds__(kSmallThreads) void merge_kernel(DecodeArgs a, DevTables t, KParams k) {
   __shared__ float accr[G][kD], ow[G][kD], qw[G][kD], part[8][G][kD];
@@ -332,7 +347,30 @@ __global__ __launch_bounds__(kSmallThreads) void merge_kernel(DecodeArgs a, DevT
   const int64_t bh = static_cast<int64_t>(b) * k.Hkv + h;
   const bool dense = k.rotation == TQ_ROT_DENSE;
 
-  // ---- prefetch
+  // ---- loads, in the order they are needed (loads complete in order: a
+  // wait for the first ones does not wait for the rest)
+  // split partials: thread (c4, q8) takes query g = q8 % G; for the maximum
+  // it reads (m, l) of the first 16 splits, for the sums the accumulators of
+  // its first 8 splits s = sub, sub + nsub, ... (sub = q8 / G)
+  constexpr int nsub = 8 / G;
+  const int g = q8 % G, sub = q8 / G;
+  float lm[16], mm[16];
+#pragma unroll
+  for (int u = 0; u < 16; ++u) {
+    const int64_t pi = (bh * a.splits + (u < a.splits ? u : 0)) * G + g;
+    lm[u] = u < a.splits ? a.pl[pi] : 0.0f;
+    mm[u] = a.pm[pi];
+  }
+  float4 va[8];
+  float la[8], ma[8];
+#pragma unroll
+  for (int u = 0; u < 8; ++u) {
+    const int s = sub + u * nsub;
+    const int64_t pi = (bh * a.splits + (s < a.splits ? s : 0)) * G + g;
+    va[u] = *reinterpret_cast<const float4*>(a.pacc + pi * kD + c4);
+    la[u] = s < a.splits ? a.pl[pi] : 0.0f;
+    ma[u] = a.pm[pi];
+  }
   // window keys: thread pair (tk, half) holds slot tk = tid / 2, coordinates 64 half ..
   const int tk0 = tid >> 1, half = tid & 1;
   uint4 kv[8];
@@ -355,13 +393,13 @@ __global__ __launch_bounds__(kSmallThreads) void merge_kernel(DecodeArgs a, DevT
   }
   for (int e = tid; e < G * kD; e += kSmallThreads) qw[e / kD][e % kD] = a.qwin[row0 + e];
 
-  // 1. combine the split partials: thread (c4, q8) takes query g = q8 % G and
-  //    splits s = sub, sub + nsub, ... (sub = q8 / G); fixed-order sums.
+  // 1. combine the split partials in fixed order
   {
-    constexpr int nsub = 8 / G;
-    const int g = q8 % G, sub = q8 / G;
     float M = -INFINITY;
-    for (int s0 = 0; s0 < a.splits; s0 += 16) {
+#pragma unroll
+    for (int u = 0; u < 16; ++u)
+      if (lm[u] > 0.0f) M = fmaxf(M, mm[u]);
+    for (int s0 = 16; s0 < a.splits; s0 += 16) {
       float lv[16], mv[16];
 #pragma unroll
       for (int u = 0; u < 16; ++u) {
@@ -375,9 +413,21 @@ __global__ __launch_bounds__(kSmallThreads) void merge_kernel(DecodeArgs a, DevT
     }
     float4 acc = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
     float L = 0.0f;
-    // batches of 8 splits: all loads of a batch are issued before use; an
-    // empty split (l = 0) gets weight 0 and its accumulator is not used
-    for (int s0 = sub; s0 < a.splits; s0 += 8 * nsub) {
+    // an empty split (l = 0) gets weight 0 and its accumulator is not used
+    auto add = [&](const float4& v, float lv, float mv) {
+      if (lv > 0.0f) {
+        const float f = exp2f(mv - M);
+        L = fmaf(f, lv, L);
+        acc.x = fmaf(f, v.x, acc.x);
+        acc.y = fmaf(f, v.y, acc.y);
+        acc.z = fmaf(f, v.z, acc.z);
+        acc.w = fmaf(f, v.w, acc.w);
+      }
+    };
+#pragma unroll
+    for (int u = 0; u < 8; ++u) add(va[u], la[u], ma[u]);
+    // later batches of 8 splits: all loads of a batch are issued before use
+    for (int s0 = sub + 8 * nsub; s0 < a.splits; s0 += 8 * nsub) {
       float4 v[8];
       float lv[8], mv[8];
 #pragma unroll
@@ -389,16 +439,7 @@ __global__ __launch_bounds__(kSmallThreads) void merge_kernel(DecodeArgs a, DevT
         mv[u] = a.pm[pi];
       }
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        if (lv[u] > 0.0f) {
-          const float f = exp2f(mv[u] - M);
-          L = fmaf(f, lv[u], L);
-          acc.x = fmaf(f, v[u].x, acc.x);
-          acc.y = fmaf(f, v[u].y, acc.y);
-          acc.z = fmaf(f, v[u].z, acc.z);
-          acc.w = fmaf(f, v[u].w, acc.w);
-        }
-      }
+      for (int u = 0; u < 8; ++u) add(v[u], lv[u], mv[u]);
     }
     *reinterpret_cast<float4*>(&part[sub][g][c4]) = acc;
     if ((tid & 31) == 0) {

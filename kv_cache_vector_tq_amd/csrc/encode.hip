@@ -57,19 +57,9 @@ __device__ inline CoreParams make_core(const Codebooks& cb, bool key, int bits, 
 // Rotate, quantise and (for keys) sketch the residual of the tile in LDS.
 // Only vectors v0 <= v < v1 of the tile are encoded (the others are not
 // written by the callers).
-template <bool HAD, bool LAT>
+template <bool HAD>
 __device__ void encode_core(Smem& sm, const DevTables& t, const CoreParams& cp, int v0, int v1) {
   const int tid = threadIdx.x;
-  // LAT (appends of a few tokens, a pure latency chain): this thread's whole
-  // rows of Pi and S are requested first, so their loads land during the
-  // rest; otherwise rows are read in halves to keep registers for occupancy
-  float srow[LAT ? kD : 1];
-  if constexpr (LAT) {
-    if (cp.qjl) {
-#pragma unroll
-      for (int j = 0; j < kD; ++j) srow[j] = t.ST[j * kD + tid];
-    }
-  }
   // this thread's coordinate (tid) and its codebook
   const bool hi = cp.hmod != 0 && mixed_hi(tid, cp.hmod);
   const int nb = (1 << (cp.bits + (hi ? 1 : 0))) - 1;
@@ -112,25 +102,7 @@ __device__ void encode_core(Smem& sm, const DevTables& t, const CoreParams& cp, 
     sm.code[v][tid] = static_cast<uint8_t>(c);
     if (cp.qjl) sm.rs[v][tid] = (n > 0.0f) ? fmaf(-n, sm.ctab[(hi ? 16 : 0) + c], accv) : 0.0f;
   };
-  if constexpr (!HAD && LAT) {
-    float pr[kD];
-#pragma unroll
-    for (int j = 0; j < kD; ++j) pr[j] = t.rotT[j * kD + tid];
-#pragma unroll 1
-    for (int v = v0; v < v1; ++v) {
-      float s = 0.0f;
-      const float4* xr = reinterpret_cast<const float4*>(sm.xs[v]);
-#pragma unroll
-      for (int j4 = 0; j4 < kD / 4; ++j4) {
-        const float4 x = xr[j4];
-        s = fmaf(pr[4 * j4 + 0], x.x, s);
-        s = fmaf(pr[4 * j4 + 1], x.y, s);
-        s = fmaf(pr[4 * j4 + 2], x.z, s);
-        s = fmaf(pr[4 * j4 + 3], x.w, s);
-      }
-      finish(v, s);
-    }
-  } else if constexpr (!HAD) {
+  if constexpr (!HAD) {
     // two passes over halves of the rotation row keep the register count
     // low; the first pass parks its partial sums in this thread's rs slots
 #pragma unroll
@@ -198,29 +170,6 @@ __device__ void encode_core(Smem& sm, const DevTables& t, const CoreParams& cp, 
     if (part == 0) sm.rn[v] = static_cast<float>(sqrt(s));
   }
   const int wave = tid >> 6, lane = tid & 63;
-  if constexpr (LAT) {
-    __syncthreads();
-#pragma unroll 1
-    for (int v = v0; v < v1; ++v) {
-      float z = 0.0f;
-      const float4* rr = reinterpret_cast<const float4*>(sm.rs[v]);
-#pragma unroll
-      for (int j4 = 0; j4 < kD / 4; ++j4) {
-        const float4 r = rr[j4];
-        z = fmaf(srow[4 * j4 + 0], r.x, z);
-        z = fmaf(srow[4 * j4 + 1], r.y, z);
-        z = fmaf(srow[4 * j4 + 2], r.z, z);
-        z = fmaf(srow[4 * j4 + 3], r.w, z);
-      }
-      const bool bit = (z >= 0.0f) && (sm.n32[v] > 0.0f);
-      const uint64_t m = __ballot(bit);
-      if (lane == 0) {
-        sm.sgn[v][2 * wave] = static_cast<uint32_t>(m);
-        sm.sgn[v][2 * wave + 1] = static_cast<uint32_t>(m >> 32);
-      }
-    }
-    return;
-  }
   __syncthreads();  // xs is free from here on: it holds the first half of S r
 #pragma unroll
   for (int hp = 0; hp < 2; ++hp) {
@@ -267,7 +216,8 @@ __device__ inline uint32_t stream_word(F code, int n, int w, int bits) {
 // Word w of vector v's record: the d codes LSB-first, or for a mixed rate
 // (hmod != 0) the d/2 low-rate codes at `bits` bits, then the d/2 high-rate
 // codes at bits + 1, each half in ascending coordinate order.
-__device__ inline uint32_t code_word(const Smem& sm, int v, int w, int bits, int hmod) {
+template <class SM>
+__device__ inline uint32_t code_word(const SM& sm, int v, int w, int bits, int hmod) {
   if (hmod == 0) return stream_word([&](int c) { return sm.code[v][c]; }, kD, w, bits);
   const int lo_words = (kD / 2) * bits / 32;
   if (w < lo_words)
@@ -286,7 +236,7 @@ __global__ __launch_bounds__(kThreads) void encode_flat_kernel(EncodeArgs a, Dev
     sm.xs[v][tid] = v < nv ? load_any(a.x, (n0 + v) * a.row_stride + tid, dtype) : 0.0f;
   __syncthreads();
   const CoreParams cp = make_core(cb, kind == TQ_KIND_KEY, bits, qjl != 0, mixed != 0);
-  encode_core<HAD, false>(sm, t, cp, 0, nv);
+  encode_core<HAD>(sm, t, cp, 0, nv);
   __syncthreads();
   if (tid < nv) {
     a.norms[n0 + tid] = sm.n32[tid];
@@ -365,7 +315,7 @@ __device__ inline void ring_owned(const AppendArgs& a, const SeqPlan& sp, int W,
 }
 
 // Encode the evicted tokens of one 32-token group of sequence b, head h.
-template <bool HAD, bool LAT>
+template <bool HAD>
 __device__ void encode_group(Smem& sm, const AppendArgs& a, const DevTables& t, const Codebooks& cb, const Layout& L,
                              int W, const SeqPlan& sp, int b, int h, int kv, int gpos) {
   const int tid = threadIdx.x;
@@ -392,7 +342,7 @@ __device__ void encode_group(Smem& sm, const AppendArgs& a, const DevTables& t, 
     const bool key = kv == 0;
     const CoreParams cp = make_core(cb, key, key ? L.bK : L.bV, key && L.qjl, key ? L.kmix : L.vmix);
     const int vlo = lo - gpos, vhi = hi - gpos;
-    encode_core<HAD, LAT>(sm, t, cp, vlo, vhi);
+    encode_core<HAD>(sm, t, cp, vlo, vhi);
     __syncthreads();
     if (key) {
       float* kn = reinterpret_cast<float*>(hb + L.k_norm);
@@ -442,7 +392,7 @@ __device__ void encode_group(Smem& sm, const AppendArgs& a, const DevTables& t, 
   }
 }
 
-template <bool HAD, bool LAT>
+template <bool HAD>
 __global__ __launch_bounds__(kThreads) void append_encode_kernel(AppendArgs a, DevTables t, Codebooks cb, Layout L,
                                                                 int W, int ring) {
   __shared__ Smem sm;
@@ -454,8 +404,309 @@ __global__ __launch_bounds__(kThreads) void append_encode_kernel(AppendArgs a, D
   const int gr = static_cast<int>(blockIdx.x >> 1);
   const int g = sp.c0 / kVGroup + gr;
   const int gpos = g * kVGroup;
-  if (sp.c1 > sp.c0 && gpos < sp.c1) encode_group<HAD, LAT>(sm, a, t, cb, L, W, sp, b, h, kv, gpos);
+  if (sp.c1 > sp.c0 && gpos < sp.c1) encode_group<HAD>(sm, a, t, cb, L, W, sp, b, h, kv, gpos);
   if (ring) ring_owned(a, sp, W, static_cast<int64_t>(b) * L.H + h, kv, gr, tid);
+}
+
+// ------------------------------------------------------------ few-token append
+// Appends of at most kSmallNew tokens per sequence (decode steps) are a chain
+// of dependent memory round trips, not a throughput problem: sequence length
+// -> window slot and page id -> existing value words.  One work-group of 256
+// threads per (sequence, kv head, keys|values) encodes the (at most
+// kSmallNew) tokens that leave the window.  Threads 0..127 own coordinate i =
+// tid for the rotation and quantiser and hold row i of Pi in registers;
+// threads 128..255 own coordinate i = tid - 128 for the norms and the sign
+// sketch and hold row i of S.  Both rows are requested before the sequence
+// plan, from tables interleaved so that each lane reads 16 contiguous bytes
+// ((j/4, i) -> M[i][4(j/4) .. 4(j/4)+3]), and land while the plan and the
+// window slots are read.  Every sum is taken in the same order as in the bulk
+// kernel above, so one-token and bulk appends write identical bytes.
+constexpr int kSmallNew = 4;
+constexpr int kSmallThreads = 256;
+
+struct SmallSmem {
+  float xs[kSmallNew][kD];   // inputs
+  float rs[kSmallNew][kD];   // key residuals in the rotated basis
+  float hx[kSmallNew][kD];   // Hadamard stride-64 exchange
+  uint8_t code[kSmallNew][kD];
+  float n32[kSmallNew], invn[kSmallNew], rn[kSmallNew];
+  uint32_t sgn[kSmallNew][4];
+  float cbt[64];  // this kind's centroids, boundaries, and the (b+1)-bit ones of a mixed rate
+};
+
+// Double-precision squared norm of row v of `x` as the bulk kernel takes it:
+// four partial sums over 32 consecutive coordinates, combined pairwise.
+// Called by 16 consecutive lanes of one wave (lane l: vector l >> 2, part l & 3).
+__device__ inline double sq_norm_quarters(const float (*x)[kD], int l) {
+  const int v = l >> 2, part = l & 3;
+  double s = 0.0;
+#pragma unroll 8
+  for (int j = 0; j < 32; ++j) {
+    const double e = x[v][part * 32 + j];
+    s = fma(e, e, s);
+  }
+  s += __shfl_xor(s, 1, 64);
+  s += __shfl_xor(s, 2, 64);
+  return s;
+}
+
+template <bool HAD>
+__global__ __launch_bounds__(kSmallThreads) void append_small_kernel(AppendArgs a, DevTables t, Layout L, int W,
+                                                                    int ring) {
+  __shared__ SmallSmem sm;
+  const int tid = threadIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const int i = tid & (kD - 1), lane = tid & 63;
+  const bool lower = tid < kD;
+  const bool key = blockIdx.x == 0;
+  const bool qjl = key && L.qjl;
+
+  // the plan's two words are requested first and the table rows (which do
+  // not depend on it) right after: loads complete in order, so waiting for
+  // the plan does not wait for the tables
+  const int T0 = a.seq_lens[b];
+  int cnt = a.n_new;
+  if (a.counts != nullptr) cnt = a.counts[b];
+  const float cbv = tid < 64 ? t.cbtab[(key ? 0 : 64) + tid] : 0.0f;
+  float4 row[kD / 4];
+  const float4* tab = lower ? (HAD ? nullptr : reinterpret_cast<const float4*>(t.rot4))
+                            : (qjl ? reinterpret_cast<const float4*>(t.S4) : nullptr);
+  if (tab) {
+#pragma unroll
+    for (int j4 = 0; j4 < kD / 4; ++j4) row[j4] = tab[j4 * kD + i];
+  }
+  if (cnt < 0 || cnt > a.n_new || T0 < 0) return;  // reported by the commit kernel
+  const int c0 = T0 - W > 0 ? T0 - W : 0;
+  const int T1 = T0 + cnt;
+  const int c1 = T1 - W > 0 ? T1 - W : 0;
+  const int nv = c1 - c0;  // tokens leaving the window: 0 .. kSmallNew
+  const int64_t bh = static_cast<int64_t>(b) * L.H + h;
+  const uint16_t* win = key ? a.k_win : a.v_win;
+  const uint16_t* src = key ? a.k_new : a.v_new;
+  uint16_t* wdst = key ? a.k_win : a.v_win;
+  // new tokens bound for the ring (the last W of them), loaded now and
+  // stored once this thread has read the slots they overwrite
+  const int j0 = cnt > W ? cnt - W : 0;
+  uint16_t rnew[kSmallNew];
+  if (ring && lower) {
+#pragma unroll
+    for (int j = 0; j < kSmallNew; ++j)
+      if (j0 + j < cnt) rnew[j] = src[(bh * a.n_new + j0 + j) * kD + i];
+  }
+  int pid0 = 0, pid1 = 0;
+  if (nv > 0) {
+    const int pg0 = c0 / L.P, pg1 = (c1 - 1) / L.P;
+    if (pg1 >= a.max_pages) return;
+    pid0 = a.block_table[static_cast<int64_t>(b) * a.max_pages + pg0];
+    pid1 = a.block_table[static_cast<int64_t>(b) * a.max_pages + pg1];
+    if (pid0 < 0 || pid0 >= a.num_pages || pid1 < 0 || pid1 >= a.num_pages) return;
+  }
+  if (nv > 0 && lower) {
+#pragma unroll
+    for (int v = 0; v < kSmallNew; ++v) {
+      float x = 0.0f;
+      if (v < nv) {
+        const int pos = c0 + v;
+        x = half_bits_to_float(pos < T0 ? win[(bh * W + pos % W) * kD + i] : src[(bh * a.n_new + (pos - T0)) * kD + i]);
+      }
+      sm.xs[v][i] = x;
+    }
+  }
+  auto ring_store = [&]() {
+    if (ring && lower) {
+#pragma unroll
+      for (int j = 0; j < kSmallNew; ++j)
+        if (j0 + j < cnt) wdst[(bh * W + (T0 + j0 + j) % W) * kD + i] = rnew[j];
+    }
+  };
+  if (nv == 0) {  // nothing leaves the window: no slot is read
+    ring_store();
+    return;
+  }
+
+  // page addresses of the (at most two) pages and groups the tokens touch
+  auto head_base = [&](int pos) {
+    const int pid = pos / L.P == c0 / L.P ? pid0 : pid1;
+    return a.pool + static_cast<int64_t>(pid) * L.page_bytes + kBodyOffset + static_cast<int64_t>(h) * L.head_bytes;
+  };
+  const int bits = key ? L.bK : L.bV;
+  const int hmod = (key ? L.kmix : L.vmix) ? (key ? kKeyHiMod : kValHiMod) : 0;
+  const bool hi = hmod != 0 && mixed_hi(i, hmod);
+  const int width = bits + (hi ? 1 : 0);
+  // value words are read-modify-write (32 tokens share them): request the
+  // old words of both groups now
+  const int ga = c0 / kVGroup, gb = (c1 - 1) / kVGroup;  // first and last group
+  const int vstride = L.vmix ? kD / 2 : kD;
+  const int vat0 = L.vmix ? (hi ? L.bV * (kD / 2) : 0) + mixed_rank(i, kValHiMod) : i;
+  uint32_t old[2][5];
+  uint32_t* gws[2] = {nullptr, nullptr};
+  if (!key && lower) {
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      if (ga + q > gb) break;
+      const int gpos = (ga + q) * kVGroup;
+      gws[q] = reinterpret_cast<uint32_t*>(head_base(gpos) + L.v_codes) +
+               static_cast<int64_t>((gpos % L.P) / kVGroup) * 8 * L.v_rec;
+#pragma unroll
+      for (int w = 0; w < 5; ++w)
+        if (w < width) old[q][w] = gws[q][vat0 + w * vstride];
+    }
+  }
+  const int nb = (1 << width) - 1;
+  const float* cen = sm.cbt + (hi ? 32 : 0);
+  const float* bnd = sm.cbt + (hi ? 48 : 16);
+  if (tid < 64) sm.cbt[tid] = cbv;
+  __syncthreads();  // (1) inputs in LDS: the slots they came from may be overwritten
+  ring_store();
+
+  // norms (upper wave 0) while the lower threads rotate
+  float acc[kSmallNew];
+  if (!lower) {
+    const int l = tid - kD;
+    if (l < 4 * kSmallNew) {
+      const double sq = sq_norm_quarters(sm.xs, l);
+      const int v = l >> 2;
+      if ((l & 3) == 0 && v < nv) {
+        const double n = sqrt(sq);
+        sm.n32[v] = static_cast<float>(n);
+        sm.invn[v] = n > 0.0 ? static_cast<float>(1.0 / n) : 0.0f;
+      }
+    }
+  } else if constexpr (!HAD) {
+#pragma unroll
+    for (int v = 0; v < kSmallNew; ++v) {
+      float s = 0.0f;
+      if (v < nv) {
+        const float4* xr = reinterpret_cast<const float4*>(sm.xs[v]);
+#pragma unroll
+        for (int j4 = 0; j4 < kD / 4; ++j4) {
+          const float4 x = xr[j4];
+          s = fmaf(row[j4].x, x.x, s);
+          s = fmaf(row[j4].y, x.y, s);
+          s = fmaf(row[j4].z, x.z, s);
+          s = fmaf(row[j4].w, x.w, s);
+        }
+      }
+      acc[v] = s;
+    }
+  } else {
+    // randomised Hadamard: strides 1..32 in the wave, 64 through LDS
+    const float eps = t.rot[i];
+#pragma unroll
+    for (int v = 0; v < kSmallNew; ++v) {
+      if (v >= nv) break;
+      float val = sm.xs[v][i] * eps;
+#pragma unroll
+      for (int st = 1; st < 64; st <<= 1) {
+        const float o = __shfl_xor(val, st, 64);
+        val = (i & st) ? (o - val) : (val + o);
+      }
+      sm.hx[v][i] = val;
+    }
+  }
+  __syncthreads();  // (2) norms (and Hadamard halves) in LDS
+  if (lower) {
+    if constexpr (HAD) {
+      const float inv_sqrt_d = 0.08838834764831845f;  // 1/sqrt(128)
+#pragma unroll
+      for (int v = 0; v < kSmallNew; ++v) {
+        const float p = sm.hx[v][i], q = sm.hx[v][i ^ 64];
+        acc[v] = ((i & 64) ? (q - p) : (p + q)) * inv_sqrt_d;
+      }
+    }
+    // quantise this coordinate of each vector and keep the key residual
+#pragma unroll
+    for (int v = 0; v < kSmallNew; ++v) {
+      if (v >= nv) break;
+      const float n = sm.n32[v];
+      const float y = acc[v] * sm.invn[v];
+      int c = 0;
+#pragma unroll
+      for (int k = 0; k < 15; ++k)
+        if (k < nb) c += (y > bnd[k]) ? 1 : 0;
+      if (!(n > 0.0f)) c = 0;
+      sm.code[v][i] = static_cast<uint8_t>(c);
+      if (qjl) sm.rs[v][i] = (n > 0.0f) ? fmaf(-n, cen[c], acc[v]) : 0.0f;
+    }
+  }
+  __syncthreads();  // (3) codes and residuals in LDS
+
+  if (key) {
+    if (qjl && !lower) {
+      // ||r|| (upper wave 0) and the sign sketch: bit i = [(S r)_i >= 0]
+      const int l = tid - kD, wu = l >> 6;
+      if (l < 4 * kSmallNew) {
+        const double sq = sq_norm_quarters(sm.rs, l);
+        if ((l & 3) == 0 && (l >> 2) < nv) sm.rn[l >> 2] = static_cast<float>(sqrt(sq));
+      }
+#pragma unroll 1
+      for (int v = 0; v < nv; ++v) {
+        float z = 0.0f;
+        const float4* rr = reinterpret_cast<const float4*>(sm.rs[v]);
+#pragma unroll
+        for (int j4 = 0; j4 < kD / 4; ++j4) {
+          const float4 r = rr[j4];
+          z = fmaf(row[j4].x, r.x, z);
+          z = fmaf(row[j4].y, r.y, z);
+          z = fmaf(row[j4].z, r.z, z);
+          z = fmaf(row[j4].w, r.w, z);
+        }
+        const bool bit = (z >= 0.0f) && (sm.n32[v] > 0.0f);
+        const uint64_t m = __ballot(bit);
+        if (lane == 0) {
+          sm.sgn[v][2 * wu] = static_cast<uint32_t>(m);
+          sm.sgn[v][2 * wu + 1] = static_cast<uint32_t>(m >> 32);
+        }
+      }
+    }
+    if (lower) {
+      // records: code words and norms
+      const int wpv = L.k_rec / 4;
+      for (int k = tid; k < nv * wpv; k += kD) {
+        const int v = k / wpv, w = k % wpv;
+        const int pos = c0 + v;
+        reinterpret_cast<uint32_t*>(head_base(pos) + L.k_codes)[(pos % L.P) * wpv + w] =
+            code_word(sm, v, w, L.bK, hmod);
+      }
+      if (tid < nv) reinterpret_cast<float*>(head_base(c0 + tid) + L.k_norm)[(c0 + tid) % L.P] = sm.n32[tid];
+    }
+    if (qjl) {
+      __syncthreads();  // (4) signs and ||r||
+      const int v = tid >> 2;
+      if (v < nv) {
+        const int pos = c0 + v;
+        reinterpret_cast<uint32_t*>(head_base(pos) + L.k_signs)[(pos % L.P) * 4 + (tid & 3)] = sm.sgn[v][tid & 3];
+      }
+      if (tid < nv) reinterpret_cast<float*>(head_base(c0 + tid) + L.k_rnorm)[(c0 + tid) % L.P] = sm.rn[tid];
+    }
+  } else if (lower) {
+    if (tid < nv) reinterpret_cast<float*>(head_base(c0 + tid) + L.v_norm)[(c0 + tid) % L.P] = sm.n32[tid];
+    // group-interleaved value words of coordinate i: token v of a group takes
+    // bits [v width, (v + 1) width) of the stream over words 0 .. width-1
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      if (ga + q > gb) break;
+      const int gpos = (ga + q) * kVGroup;
+      const int lo = c0 > gpos ? c0 : gpos;
+      const int hi_ = c1 < gpos + kVGroup ? c1 : gpos + kVGroup;
+#pragma unroll
+      for (int w = 0; w < 5; ++w) {
+        if (w >= width) break;
+        uint32_t word = old[q][w];
+        for (int pos = lo; pos < hi_; ++pos) {
+          const int v = pos - gpos;
+          const uint32_t c = sm.code[pos - c0][i];
+          for (int k = 0; k < width; ++k) {
+            const int p = v * width + k;
+            if ((p >> 5) == w) {
+              const uint32_t m = 1u << (p & 31);
+              word = (word & ~m) | (((c >> k) & 1u) << (p & 31));
+            }
+          }
+        }
+        gws[q][vat0 + w * vstride] = word;
+      }
+    }
+  }
 }
 
 
@@ -528,24 +779,26 @@ int launch_append(const tq_ctx* c, const AppendArgs& a, void* stream) {
   hipStream_t s = static_cast<hipStream_t>(stream);
   const int W = c->p.window;
   const Layout& L = c->lay;
-  // groups a sequence can touch: ceil(n_new / 32) + 1 (unaligned start)
-  const int gmax = (a.n_new + kVGroup - 1) / kVGroup + 1;
-  dim3 grid(2 * gmax, L.H, a.batch);  // even x: keys, odd x: values
-  // a few new tokens: each work-group encodes at most a handful of vectors
-  // and the kernel is a latency chain (see encode_core's LAT)
-  const bool lat = a.n_new <= 4;
   const bool had = c->p.rotation == TQ_ROT_HADAMARD;
   // the ring update rides along when no slot can be read and written by
   // different work-groups (at most W new tokens)
   const int ring = (W > 0 && a.n_new <= W) ? 1 : 0;
-  if (had && lat)
-    hipLaunchKernelGGL((append_encode_kernel<true, true>), grid, dim3(kThreads), 0, s, a, c->t, c->cb, L, W, ring);
-  else if (had)
-    hipLaunchKernelGGL((append_encode_kernel<true, false>), grid, dim3(kThreads), 0, s, a, c->t, c->cb, L, W, ring);
-  else if (lat)
-    hipLaunchKernelGGL((append_encode_kernel<false, true>), grid, dim3(kThreads), 0, s, a, c->t, c->cb, L, W, ring);
-  else
-    hipLaunchKernelGGL((append_encode_kernel<false, false>), grid, dim3(kThreads), 0, s, a, c->t, c->cb, L, W, ring);
+  if (a.n_new <= kSmallNew) {
+    // decode steps: one work-group per (sequence, kv head, keys|values)
+    const dim3 grid(2, L.H, a.batch);
+    if (had)
+      hipLaunchKernelGGL(append_small_kernel<true>, grid, dim3(kSmallThreads), 0, s, a, c->t, L, W, ring);
+    else
+      hipLaunchKernelGGL(append_small_kernel<false>, grid, dim3(kSmallThreads), 0, s, a, c->t, L, W, ring);
+  } else {
+    // groups a sequence can touch: ceil(n_new / 32) + 1 (unaligned start)
+    const int gmax = (a.n_new + kVGroup - 1) / kVGroup + 1;
+    const dim3 grid(2 * gmax, L.H, a.batch);  // even x: keys, odd x: values
+    if (had)
+      hipLaunchKernelGGL(append_encode_kernel<true>, grid, dim3(kThreads), 0, s, a, c->t, c->cb, L, W, ring);
+    else
+      hipLaunchKernelGGL(append_encode_kernel<false>, grid, dim3(kThreads), 0, s, a, c->t, c->cb, L, W, ring);
+  }
   if (hipGetLastError() != hipSuccess) return 1;
   if (W > 0 && !ring) {
     hipLaunchKernelGGL(append_ring_kernel, dim3(L.H, a.batch), dim3(kThreads), 0, s, a, c->t, L, W);

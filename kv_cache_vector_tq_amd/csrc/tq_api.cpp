@@ -189,10 +189,30 @@ TQ_API int tq_codebook_init(tq_ctx** out, const tq_params* p, const double* rot_
   }
   if (p->rotation == TQ_ROT_DENSE) transpose(rot.data(), rotT.data(), d);
   transpose(S.data(), ST.data(), d);
+  // row-owner layouts for the few-token append: lane i reads M[i][4 j4 .. 4 j4 + 3] as one float4
+  std::vector<float> rot4(d * d, 0.0f), S4(d * d, 0.0f);
+  for (int j4 = 0; j4 < d / 4; ++j4)
+    for (int i = 0; i < d; ++i)
+      for (int q = 0; q < 4; ++q) {
+        if (p->rotation == TQ_ROT_DENSE) rot4[(j4 * d + i) * 4 + q] = rot[i * d + 4 * j4 + q];
+        S4[(j4 * d + i) * 4 + q] = S[i * d + 4 * j4 + q];
+      }
   c->h_rot = rot;
   c->h_S = S;
   const size_t mat = static_cast<size_t>(d) * d * sizeof(float);
-  const size_t total = 4 * mat + 256;
+  // codebooks as a device table (the few-token append reads them into LDS)
+  float cbtab[128] = {};
+  for (int k = 0; k < 16; ++k) {
+    cbtab[k] = c->cb.kc[k];
+    cbtab[16 + k] = c->cb.kb[k];
+    cbtab[32 + k] = c->cb.kc2[k];
+    cbtab[48 + k] = c->cb.kb2[k];
+    cbtab[64 + k] = c->cb.vc[k];
+    cbtab[80 + k] = c->cb.vb[k];
+    cbtab[96 + k] = c->cb.vc2[k];
+    cbtab[112 + k] = c->cb.vb2[k];
+  }
+  const size_t total = 6 * mat + sizeof(cbtab) + 256;
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (hipGetDevice(&c->device) != hipSuccess || hipMalloc(&c->dmem, total) != hipSuccess) {
     delete c;
@@ -203,12 +223,19 @@ TQ_API int tq_codebook_init(tq_ctx** out, const tq_params* p, const double* rot_
   c->t.rotT = reinterpret_cast<float*>(base + mat);
   c->t.S = reinterpret_cast<float*>(base + 2 * mat);
   c->t.ST = reinterpret_cast<float*>(base + 3 * mat);
-  c->t.status = reinterpret_cast<int*>(base + 4 * mat);
+  c->t.rot4 = reinterpret_cast<float*>(base + 4 * mat);
+  c->t.S4 = reinterpret_cast<float*>(base + 5 * mat);
+  c->t.cbtab = reinterpret_cast<float*>(base + 6 * mat);
+  c->t.status = reinterpret_cast<int*>(base + 6 * mat + sizeof(cbtab));
   bool ok = hipMemcpyAsync(base, rot.data(), mat, hipMemcpyHostToDevice, s) == hipSuccess &&
             hipMemcpyAsync(base + mat, rotT.data(), mat, hipMemcpyHostToDevice, s) == hipSuccess &&
             hipMemcpyAsync(base + 2 * mat, S.data(), mat, hipMemcpyHostToDevice, s) == hipSuccess &&
             hipMemcpyAsync(base + 3 * mat, ST.data(), mat, hipMemcpyHostToDevice, s) == hipSuccess &&
-            hipMemsetAsync(base + 4 * mat, 0, 256, s) == hipSuccess && hipStreamSynchronize(s) == hipSuccess;
+            hipMemcpyAsync(base + 4 * mat, rot4.data(), mat, hipMemcpyHostToDevice, s) == hipSuccess &&
+            hipMemcpyAsync(base + 5 * mat, S4.data(), mat, hipMemcpyHostToDevice, s) == hipSuccess &&
+            hipMemcpyAsync(base + 6 * mat, cbtab, sizeof(cbtab), hipMemcpyHostToDevice, s) == hipSuccess &&
+            hipMemsetAsync(base + 6 * mat + sizeof(cbtab), 0, 256, s) == hipSuccess &&
+            hipStreamSynchronize(s) == hipSuccess;
   // resident scan work-groups per device, for the automatic split count
   const bool valu = (p->flags & TQ_FLAG_VALU_SCAN) != 0;
   const void* kf = valu ? tq::scan_valu_kernel_ptr(c) : tq::scan_mfma_kernel_ptr(c);

@@ -78,6 +78,9 @@ struct DevTables {
   const float* rotT;   // DENSE: Pi^T [d][d] row-major
   const float* S;      // QJL matrix [d][d] row-major (sign bit i from row i)
   const float* ST;     // S^T [d][d] row-major
+  const float* rot4;   // DENSE: Pi interleaved by 4 columns: float4 (j4, i) = Pi[i][4 j4 .. 4 j4 + 3]
+  const float* S4;     // S interleaved the same way
+  const float* cbtab;  // [keys, values][64]: centroids[16], boundaries[16], then the (b+1)-bit pair of a mixed rate
   int* status;         // status word (TQ_STATUS_* bits)
 };
 
