@@ -52,7 +52,7 @@ __device__ __forceinline__ void matvec_cols(const float4 (&m)[16], const float (
     }
     *reinterpret_cast<float4*>(&part[rg][g][c4]) = acc;
   }
-  __syncthreads();
+  lds_barrier();
   for (int e = t; e < G * kD; e += kSmallThreads) {
     const int g = e / kD, i = e % kD;
     float v = part[0][g][i];
@@ -60,7 +60,7 @@ __device__ __forceinline__ void matvec_cols(const float4 (&m)[16], const float (
     for (int r = 1; r < 8; ++r) v += part[r][g][i];
     y[g][i] = v;
   }
-  __syncthreads();
+  lds_barrier();
 }
 
 // y[g] = H (eps * x[g]) / sqrt(kD) for the randomised Hadamard rotation; in
@@ -78,17 +78,17 @@ __device__ __forceinline__ void hadamard_lds(float (*x)[kD], const float* __rest
       const float ov = __shfl_xor(val, s2, 64);
       val = (j & s2) ? (ov - val) : (val + ov);
     }
-    __syncthreads();
+    lds_barrier();
     if (act) x[g][j] = val;
-    __syncthreads();
+    lds_barrier();
     if (act) {
       const float a0 = x[g][j], b0 = x[g][j ^ 64];
       val = ((j & 64) ? (b0 - a0) : (a0 + b0)) * 0.08838834764831845f * (post ? post[j] : 1.0f);
     }
-    __syncthreads();
+    lds_barrier();
     if (act) x[g][j] = val;
   }
-  __syncthreads();
+  lds_barrier();
 }
 
 // One work-group per (b, kv head) prepares its G query heads.
@@ -98,14 +98,32 @@ __global__ __launch_bounds__(kSmallThreads) void prep_kernel(DecodeArgs a, DevTa
   const int tid = threadIdx.x, h = blockIdx.x, b = blockIdx.y;
   const int64_t row0 = (static_cast<int64_t>(b) * k.Hq + static_cast<int64_t>(h) * G) * kD;
   const float c2 = a.sm_scale * kLog2e;
-  // the query first, then both tables (independent of it), all in flight together
-  float qin[(G * kD + kSmallThreads - 1) / kSmallThreads];
-#pragma unroll
-  for (int u = 0; u * kSmallThreads < G * kD; ++u)
-    if (tid + u * kSmallThreads < G * kD) qin[u] = load_any(a.q, row0 + tid + u * kSmallThreads, a.q_dtype);
+  // both tables, then the query: all in flight together (the query's loads
+  // sit behind one branch on its dtype, whose join waits for every load issued)
   float4 mr[16], ms[16];
   if (k.rotation == TQ_ROT_DENSE) load_cols(t.rotT, mr);
   if (qjl) load_cols(t.ST, ms);
+  constexpr int kNq = (G * kD + kSmallThreads - 1) / kSmallThreads;
+  float qin[kNq];
+  if (a.q_dtype == TQ_DTYPE_F32) {
+    const float* q32 = static_cast<const float*>(a.q);
+#pragma unroll
+    for (int u = 0; u < kNq; ++u) {
+      const int e = tid + u * kSmallThreads;
+      qin[u] = e < G * kD ? q32[row0 + e] : 0.0f;
+    }
+  } else {
+    const uint16_t* q16 = static_cast<const uint16_t*>(a.q);
+    uint16_t raw[kNq];
+#pragma unroll
+    for (int u = 0; u < kNq; ++u) {
+      const int e = tid + u * kSmallThreads;
+      raw[u] = e < G * kD ? q16[row0 + e] : 0;
+    }
+#pragma unroll
+    for (int u = 0; u < kNq; ++u)
+      qin[u] = a.q_dtype == TQ_DTYPE_F16 ? half_bits_to_float(raw[u]) : bf16_bits_to_float(raw[u]);
+  }
 #pragma unroll
   for (int u = 0; u * kSmallThreads < G * kD; ++u) {
     const int e = tid + u * kSmallThreads;
@@ -114,13 +132,13 @@ __global__ __launch_bounds__(kSmallThreads) void prep_kernel(DecodeArgs a, DevTa
       qv[e / kD][e % kD] = qin[u];
     }
   }
-  __syncthreads();
+  lds_barrier();
   if (k.rotation == TQ_ROT_DENSE) {
     matvec_cols<G>(mr, qv, part, qr);
   } else {
     hadamard_lds<G>(qv, t.rot, nullptr);
     for (int e = tid; e < G * kD; e += kSmallThreads) qr[e / kD][e % kD] = qv[e / kD][e % kD];
-    __syncthreads();
+    lds_barrier();
   }
   for (int e = tid; e < G * kD; e += kSmallThreads) a.qs[row0 + e] = qr[e / kD][e % kD] * c2;
   if (!qjl) return;
@@ -354,13 +372,17 @@ __global__ __launch_bounds__(kSmallThreads) void merge_kernel(DecodeArgs a, DevT
   // its first 8 splits s = sub, sub + nsub, ... (sub = q8 / G)
   constexpr int nsub = 8 / G;
   const int g = q8 % G, sub = q8 / G;
+  // (loads are unconditional, from a clamped split index, and the result is
+  // selected: a load under a branch would make its join wait for all loads)
   float lm[16], mm[16];
 #pragma unroll
   for (int u = 0; u < 16; ++u) {
     const int64_t pi = (bh * a.splits + (u < a.splits ? u : 0)) * G + g;
-    lm[u] = u < a.splits ? a.pl[pi] : 0.0f;
+    lm[u] = a.pl[pi];
     mm[u] = a.pm[pi];
   }
+#pragma unroll
+  for (int u = 0; u < 16; ++u) lm[u] = u < a.splits ? lm[u] : 0.0f;
   float4 va[8];
   float la[8], ma[8];
 #pragma unroll
@@ -368,9 +390,11 @@ __global__ __launch_bounds__(kSmallThreads) void merge_kernel(DecodeArgs a, DevT
     const int s = sub + u * nsub;
     const int64_t pi = (bh * a.splits + (s < a.splits ? s : 0)) * G + g;
     va[u] = *reinterpret_cast<const float4*>(a.pacc + pi * kD + c4);
-    la[u] = s < a.splits ? a.pl[pi] : 0.0f;
+    la[u] = a.pl[pi];
     ma[u] = a.pm[pi];
   }
+#pragma unroll
+  for (int u = 0; u < 8; ++u) la[u] = sub + u * nsub < a.splits ? la[u] : 0.0f;
   // window keys: thread pair (tk, half) holds slot tk = tid / 2, coordinates 64 half ..
   const int tk0 = tid >> 1, half = tid & 1;
   uint4 kv[8];
@@ -391,7 +415,14 @@ __global__ __launch_bounds__(kSmallThreads) void merge_kernel(DecodeArgs a, DevT
 #pragma unroll
     for (int r = 0; r < 16; ++r) rm[r] = *reinterpret_cast<const float4*>(t.rot + (q8 * 16 + r) * kD + c4);
   }
-  for (int e = tid; e < G * kD; e += kSmallThreads) qw[e / kD][e % kD] = a.qwin[row0 + e];
+  // the window query, stored to LDS after the combine (a store now would wait for every load above)
+  constexpr int kNq = (G * kD + kSmallThreads - 1) / kSmallThreads;
+  float qwr[kNq];
+#pragma unroll
+  for (int u = 0; u < kNq; ++u) {
+    const int e = tid + u * kSmallThreads;
+    qwr[u] = a.qwin[row0 + (e < G * kD ? e : 0)];
+  }
 
   // 1. combine the split partials in fixed order
   {
@@ -404,9 +435,11 @@ __global__ __launch_bounds__(kSmallThreads) void merge_kernel(DecodeArgs a, DevT
 #pragma unroll
       for (int u = 0; u < 16; ++u) {
         const int64_t pi = (bh * a.splits + (s0 + u < a.splits ? s0 + u : s0)) * G + g;
-        lv[u] = s0 + u < a.splits ? a.pl[pi] : 0.0f;
+        lv[u] = a.pl[pi];
         mv[u] = a.pm[pi];
       }
+#pragma unroll
+      for (int u = 0; u < 16; ++u) lv[u] = s0 + u < a.splits ? lv[u] : 0.0f;
 #pragma unroll
       for (int u = 0; u < 16; ++u)
         if (lv[u] > 0.0f) M = fmaxf(M, mv[u]);
@@ -435,9 +468,11 @@ __global__ __launch_bounds__(kSmallThreads) void merge_kernel(DecodeArgs a, DevT
         const int s = s0 + u * nsub;
         const int64_t pi = (bh * a.splits + (s < a.splits ? s : s0)) * G + g;
         v[u] = *reinterpret_cast<const float4*>(a.pacc + pi * kD + c4);
-        lv[u] = s < a.splits ? a.pl[pi] : 0.0f;
+        lv[u] = a.pl[pi];
         mv[u] = a.pm[pi];
       }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) lv[u] = s0 + u * nsub < a.splits ? lv[u] : 0.0f;
 #pragma unroll
       for (int u = 0; u < 8; ++u) add(v[u], lv[u], mv[u]);
     }
@@ -447,7 +482,12 @@ __global__ __launch_bounds__(kSmallThreads) void merge_kernel(DecodeArgs a, DevT
       if (sub == 0) sM[g] = M;
     }
   }
-  __syncthreads();
+#pragma unroll
+  for (int u = 0; u < kNq; ++u) {
+    const int e = tid + u * kSmallThreads;
+    if (e < G * kD) qw[e / kD][e % kD] = qwr[u];
+  }
+  lds_barrier();
   for (int e = tid; e < G * kD; e += kSmallThreads) {
     const int g = e / kD, i = e % kD;
     float v = part[0][g][i];
@@ -492,7 +532,7 @@ __global__ __launch_bounds__(kSmallThreads) void merge_kernel(DecodeArgs a, DevT
       }
     }
   }
-  __syncthreads();
+  lds_barrier();
   // 3. per query head (one wave each): window max, weights, their sum
   for (int g = wv; g < G; g += kSmallThreads / 64) {
     float m = sM[g];
@@ -510,7 +550,7 @@ __global__ __launch_bounds__(kSmallThreads) void merge_kernel(DecodeArgs a, DevT
       sLw[g] = lw;
     }
   }
-  __syncthreads();
+  lds_barrier();
   // 4. weighted FP16 window values: thread (c4, q8) takes slots q8, q8+8, ...
   {
     float4 acc[G];
@@ -538,7 +578,7 @@ __global__ __launch_bounds__(kSmallThreads) void merge_kernel(DecodeArgs a, DevT
 #pragma unroll
     for (int g = 0; g < G; ++g) *reinterpret_cast<float4*>(&part[q8][g][c4]) = acc[g];
   }
-  __syncthreads();
+  lds_barrier();
   for (int e = tid; e < G * kD; e += kSmallThreads) {
     const int g = e / kD, i = e % kD;
     float v = part[0][g][i];
@@ -546,7 +586,7 @@ __global__ __launch_bounds__(kSmallThreads) void merge_kernel(DecodeArgs a, DevT
     for (int r = 1; r < 8; ++r) v += part[r][g][i];
     ow[g][i] = v;
   }
-  __syncthreads();
+  lds_barrier();
   // 5. one inverse rotation per query head: o = Pi^T acc_rot
   if (dense) {
     // o[g][j] = sum_i Pi[i][j] accr[g][i]; thread (c4, q8) sums rows 16 q8 ..
@@ -563,7 +603,7 @@ __global__ __launch_bounds__(kSmallThreads) void merge_kernel(DecodeArgs a, DevT
       }
       *reinterpret_cast<float4*>(&part[q8][g][c4]) = o;
     }
-    __syncthreads();
+    lds_barrier();
     for (int e = tid; e < G * kD; e += kSmallThreads) {
       const int g = e / kD, i = e % kD;
       float v = part[0][g][i];
@@ -571,7 +611,7 @@ __global__ __launch_bounds__(kSmallThreads) void merge_kernel(DecodeArgs a, DevT
       for (int r = 1; r < 8; ++r) v += part[r][g][i];
       accr[g][i] = v;
     }
-    __syncthreads();
+    lds_barrier();
   } else {
     hadamard_lds<G>(accr, nullptr, t.rot);
   }

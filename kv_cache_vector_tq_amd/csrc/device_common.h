@@ -27,6 +27,16 @@ __device__ inline float load_any(const void* p, int64_t idx, int dtype) {
   return dtype == TQ_DTYPE_F16 ? half_bits_to_float(v) : bf16_bits_to_float(v);
 }
 
+// Work-group barrier for data exchanged through LDS only.  __syncthreads is
+// a release/acquire fence on all memory and waits for every global load in
+// flight; this one orders LDS alone, so loads issued early keep flying across
+// it.  Only for phases that share no global memory between threads.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 __device__ inline float wave_max(float v) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));

@@ -371,10 +371,14 @@ __device__ void encode_group(Smem& sm, const AppendArgs& a, const DevTables& t, 
       const int width = L.bV + (hi ? 1 : 0);
       const int stride = L.vmix ? kD / 2 : kD;
       const int at0 = L.vmix ? (hi ? L.bV * (kD / 2) : 0) + mixed_rank(tid, kValHiMod) : tid;
+      // bits of tokens not yet written are left zero: the few-token append
+      // ORs later tokens into the word without reading it
 #pragma unroll
       for (int w = 0; w < 5; ++w) {
         if (w >= width) break;
-        uint32_t word = gw[at0 + w * stride];
+        const int keep = vhi * width - 32 * w;  // stream bits of word w below this belong to tokens < vhi
+        uint32_t word = vlo == 0 || keep <= 0 ? 0u : gw[at0 + w * stride];
+        if (keep < 32) word &= keep > 0 ? (1u << keep) - 1u : 0u;
         for (int v = vlo; v < vhi; ++v) {
           const uint32_t c = sm.code[v][tid];
           for (int k = 0; k < width; ++k) {
@@ -460,20 +464,23 @@ __global__ __launch_bounds__(kSmallThreads) void append_small_kernel(AppendArgs 
   const bool key = blockIdx.x == 0;
   const bool qjl = key && L.qjl;
 
-  // the plan's two words are requested first and the table rows (which do
-  // not depend on it) right after: loads complete in order, so waiting for
-  // the plan does not wait for the tables
+  // the plan's two words and this kind's codebook are requested first; the
+  // codebook goes to LDS while nothing else is in flight (loads complete in
+  // order, so a later wait for it would also wait for the tables), then the
+  // table rows, which land while the window slots are read
   const int T0 = a.seq_lens[b];
   int cnt = a.n_new;
   if (a.counts != nullptr) cnt = a.counts[b];
-  const float cbv = tid < 64 ? t.cbtab[(key ? 0 : 64) + tid] : 0.0f;
+  const float cbv = t.cbtab[(key ? 0 : 64) + (tid & 63)];
+  if (tid < 64) sm.cbt[tid] = cbv;
+  // (every thread loads a table, used or not: loads under a branch leave the
+  // compiler's wait counting at later uses conservative, i.e. full drains;
+  // threads without a row of their own read Pi's, which their wave's other
+  // half reads anyway, or a zero table for the Hadamard rotation)
   float4 row[kD / 4];
-  const float4* tab = lower ? (HAD ? nullptr : reinterpret_cast<const float4*>(t.rot4))
-                            : (qjl ? reinterpret_cast<const float4*>(t.S4) : nullptr);
-  if (tab) {
+  const float4* tab = reinterpret_cast<const float4*>(!lower && qjl ? t.S4 : t.rot4);
 #pragma unroll
-    for (int j4 = 0; j4 < kD / 4; ++j4) row[j4] = tab[j4 * kD + i];
-  }
+  for (int j4 = 0; j4 < kD / 4; ++j4) row[j4] = tab[j4 * kD + i];
   if (cnt < 0 || cnt > a.n_new || T0 < 0) return;  // reported by the commit kernel
   const int c0 = T0 - W > 0 ? T0 - W : 0;
   const int T1 = T0 + cnt;
@@ -485,12 +492,13 @@ __global__ __launch_bounds__(kSmallThreads) void append_small_kernel(AppendArgs 
   uint16_t* wdst = key ? a.k_win : a.v_win;
   // new tokens bound for the ring (the last W of them), loaded now and
   // stored once this thread has read the slots they overwrite
+  // (loads in this kernel are unconditional, from clamped indices: a load
+  // under a branch makes the branch's join wait for every load in flight)
   const int j0 = cnt > W ? cnt - W : 0;
   uint16_t rnew[kSmallNew];
-  if (ring && lower) {
+  if (ring && lower && cnt > 0) {
 #pragma unroll
-    for (int j = 0; j < kSmallNew; ++j)
-      if (j0 + j < cnt) rnew[j] = src[(bh * a.n_new + j0 + j) * kD + i];
+    for (int j = 0; j < kSmallNew; ++j) rnew[j] = src[(bh * a.n_new + (j0 + j < cnt ? j0 + j : cnt - 1)) * kD + i];
   }
   int pid0 = 0, pid1 = 0;
   if (nv > 0) {
@@ -501,15 +509,15 @@ __global__ __launch_bounds__(kSmallThreads) void append_small_kernel(AppendArgs 
     if (pid0 < 0 || pid0 >= a.num_pages || pid1 < 0 || pid1 >= a.num_pages) return;
   }
   if (nv > 0 && lower) {
+    uint16_t xr[kSmallNew];
 #pragma unroll
     for (int v = 0; v < kSmallNew; ++v) {
-      float x = 0.0f;
-      if (v < nv) {
-        const int pos = c0 + v;
-        x = half_bits_to_float(pos < T0 ? win[(bh * W + pos % W) * kD + i] : src[(bh * a.n_new + (pos - T0)) * kD + i]);
-      }
-      sm.xs[v][i] = x;
+      const int pos = c0 + (v < nv ? v : nv - 1);
+      const uint16_t* p = pos < T0 ? win + (bh * W + pos % W) * kD : src + (bh * a.n_new + (pos - T0)) * kD;
+      xr[v] = p[i];
     }
+#pragma unroll
+    for (int v = 0; v < kSmallNew; ++v) sm.xs[v][i] = v < nv ? half_bits_to_float(xr[v]) : 0.0f;
   }
   auto ring_store = [&]() {
     if (ring && lower) {
@@ -532,31 +540,16 @@ __global__ __launch_bounds__(kSmallThreads) void append_small_kernel(AppendArgs 
   const int hmod = (key ? L.kmix : L.vmix) ? (key ? kKeyHiMod : kValHiMod) : 0;
   const bool hi = hmod != 0 && mixed_hi(i, hmod);
   const int width = bits + (hi ? 1 : 0);
-  // value words are read-modify-write (32 tokens share them): request the
-  // old words of both groups now
+  // value words hold 32 tokens' codes; the bits of tokens not yet written
+  // are zero (every writer keeps them so), so new codes are stored into a
+  // group's first word outright or ORed in, without reading the word
   const int ga = c0 / kVGroup, gb = (c1 - 1) / kVGroup;  // first and last group
   const int vstride = L.vmix ? kD / 2 : kD;
   const int vat0 = L.vmix ? (hi ? L.bV * (kD / 2) : 0) + mixed_rank(i, kValHiMod) : i;
-  uint32_t old[2][5];
-  uint32_t* gws[2] = {nullptr, nullptr};
-  if (!key && lower) {
-#pragma unroll
-    for (int q = 0; q < 2; ++q) {
-      if (ga + q > gb) break;
-      const int gpos = (ga + q) * kVGroup;
-      gws[q] = reinterpret_cast<uint32_t*>(head_base(gpos) + L.v_codes) +
-               static_cast<int64_t>((gpos % L.P) / kVGroup) * 8 * L.v_rec;
-#pragma unroll
-      for (int w = 0; w < 5; ++w)
-        if (w < width) old[q][w] = gws[q][vat0 + w * vstride];
-    }
-  }
   const int nb = (1 << width) - 1;
   const float* cen = sm.cbt + (hi ? 32 : 0);
   const float* bnd = sm.cbt + (hi ? 48 : 16);
-  if (tid < 64) sm.cbt[tid] = cbv;
-  __syncthreads();  // (1) inputs in LDS: the slots they came from may be overwritten
-  ring_store();
+  lds_barrier();  // (1) inputs in LDS
 
   // norms (upper wave 0) while the lower threads rotate
   float acc[kSmallNew];
@@ -603,7 +596,7 @@ __global__ __launch_bounds__(kSmallThreads) void append_small_kernel(AppendArgs 
       sm.hx[v][i] = val;
     }
   }
-  __syncthreads();  // (2) norms (and Hadamard halves) in LDS
+  lds_barrier();  // (2) norms (and Hadamard halves) in LDS
   if (lower) {
     if constexpr (HAD) {
       const float inv_sqrt_d = 0.08838834764831845f;  // 1/sqrt(128)
@@ -628,7 +621,7 @@ __global__ __launch_bounds__(kSmallThreads) void append_small_kernel(AppendArgs 
       if (qjl) sm.rs[v][i] = (n > 0.0f) ? fmaf(-n, cen[c], acc[v]) : 0.0f;
     }
   }
-  __syncthreads();  // (3) codes and residuals in LDS
+  lds_barrier();  // (3) codes and residuals in LDS
 
   if (key) {
     if (qjl && !lower) {
@@ -670,7 +663,7 @@ __global__ __launch_bounds__(kSmallThreads) void append_small_kernel(AppendArgs 
       if (tid < nv) reinterpret_cast<float*>(head_base(c0 + tid) + L.k_norm)[(c0 + tid) % L.P] = sm.n32[tid];
     }
     if (qjl) {
-      __syncthreads();  // (4) signs and ||r||
+      lds_barrier();  // (4) signs and ||r||
       const int v = tid >> 2;
       if (v < nv) {
         const int pos = c0 + v;
@@ -688,25 +681,30 @@ __global__ __launch_bounds__(kSmallThreads) void append_small_kernel(AppendArgs 
       const int gpos = (ga + q) * kVGroup;
       const int lo = c0 > gpos ? c0 : gpos;
       const int hi_ = c1 < gpos + kVGroup ? c1 : gpos + kVGroup;
+      uint32_t* gw = reinterpret_cast<uint32_t*>(head_base(gpos) + L.v_codes) +
+                     static_cast<int64_t>((gpos % L.P) / kVGroup) * 8 * L.v_rec;
 #pragma unroll
       for (int w = 0; w < 5; ++w) {
         if (w >= width) break;
-        uint32_t word = old[q][w];
+        uint32_t bitsw = 0u;
         for (int pos = lo; pos < hi_; ++pos) {
           const int v = pos - gpos;
           const uint32_t c = sm.code[pos - c0][i];
           for (int k = 0; k < width; ++k) {
             const int p = v * width + k;
-            if ((p >> 5) == w) {
-              const uint32_t m = 1u << (p & 31);
-              word = (word & ~m) | (((c >> k) & 1u) << (p & 31));
-            }
+            if ((p >> 5) == w) bitsw |= ((c >> k) & 1u) << (p & 31);
           }
         }
-        gws[q][vat0 + w * vstride] = word;
+        if (lo == gpos)
+          gw[vat0 + w * vstride] = bitsw;  // the group starts here: later tokens' bits zero
+        else if (bitsw != 0u)
+          atomicOr(&gw[vat0 + w * vstride], bitsw);
       }
     }
   }
+  // the inputs are in LDS, so the slots they came from may be overwritten
+  // (stored last: an earlier store would wait for the value words in flight)
+  ring_store();
 }
 
 
