@@ -371,8 +371,7 @@ __device__ void encode_group(Smem& sm, const AppendArgs& a, const DevTables& t, 
       const int width = L.bV + (hi ? 1 : 0);
       const int stride = L.vmix ? kD / 2 : kD;
       const int at0 = L.vmix ? (hi ? L.bV * (kD / 2) : 0) + mixed_rank(tid, kValHiMod) : tid;
-      // bits of tokens not yet written are left zero: the few-token append
-      // ORs later tokens into the word without reading it
+      // bits of tokens not yet written are left zero
 #pragma unroll
       for (int w = 0; w < 5; ++w) {
         if (w >= width) break;
@@ -540,9 +539,10 @@ __global__ __launch_bounds__(kSmallThreads) void append_small_kernel(AppendArgs 
   const int hmod = (key ? L.kmix : L.vmix) ? (key ? kKeyHiMod : kValHiMod) : 0;
   const bool hi = hmod != 0 && mixed_hi(i, hmod);
   const int width = bits + (hi ? 1 : 0);
-  // value words hold 32 tokens' codes; the bits of tokens not yet written
-  // are zero (every writer keeps them so), so new codes are stored into a
-  // group's first word outright or ORed in, without reading the word
+  // value words hold 32 tokens' codes: the new tokens' bits are stored into
+  // a group's first word outright (later tokens are not valid yet) or
+  // cleared and set with two no-return atomics (same thread, same word: they
+  // take effect in program order), without reading the word
   const int ga = c0 / kVGroup, gb = (c1 - 1) / kVGroup;  // first and last group
   const int vstride = L.vmix ? kD / 2 : kD;
   const int vat0 = L.vmix ? (hi ? L.bV * (kD / 2) : 0) + mixed_rank(i, kValHiMod) : i;
@@ -686,19 +686,25 @@ __global__ __launch_bounds__(kSmallThreads) void append_small_kernel(AppendArgs 
 #pragma unroll
       for (int w = 0; w < 5; ++w) {
         if (w >= width) break;
-        uint32_t bitsw = 0u;
+        uint32_t bitsw = 0u, maskw = 0u;
         for (int pos = lo; pos < hi_; ++pos) {
           const int v = pos - gpos;
           const uint32_t c = sm.code[pos - c0][i];
           for (int k = 0; k < width; ++k) {
             const int p = v * width + k;
-            if ((p >> 5) == w) bitsw |= ((c >> k) & 1u) << (p & 31);
+            if ((p >> 5) == w) {
+              bitsw |= ((c >> k) & 1u) << (p & 31);
+              maskw |= 1u << (p & 31);
+            }
           }
         }
-        if (lo == gpos)
-          gw[vat0 + w * vstride] = bitsw;  // the group starts here: later tokens' bits zero
-        else if (bitsw != 0u)
-          atomicOr(&gw[vat0 + w * vstride], bitsw);
+        uint32_t* wp = &gw[vat0 + w * vstride];
+        if (lo == gpos) {
+          *wp = bitsw;  // the group starts here
+        } else if (maskw != 0u) {
+          atomicAnd(wp, ~maskw);
+          atomicOr(wp, bitsw);
+        }
       }
     }
   }

@@ -161,3 +161,54 @@ def test_invalid_page_leaves_sequence_unchanged():
     pid0 = int(c.block_table[1, 0])
     assert torch.equal(dev["pool"][pid0 * pb:(pid0 + 1) * pb].cpu(), before[pid0 * pb:(pid0 + 1) * pb].cpu())
     assert not dev["k_win"][1].any()
+
+
+@pytest.mark.parametrize("mixed", [False, True])
+def test_one_token_append_over_stale_slots(mixed):
+    """A sequence shortened by the caller (or a recycled page) leaves stale
+    codes in the slots past its length.  One-token appends into those slots
+    must replace every bit of their own codes: the records read back equal
+    those of a cache built in one bulk append from the same tokens."""
+    print(f"case stale-slot one-token append mixed={mixed}", flush=True)
+    kw = dict(Hq=2, Hkv=2, W=8, P=32)
+    if mixed:
+        kw.update(key_bits=3, value_bits=3, key_mixed=True, value_mixed=True)
+    s = Setup(**kw)
+    T, T_cut = 60, 50
+    a_k, a_v = fill(s, s.cache(1, T), [T])
+    b_k, b_v = fill(s, s.cache(1, T), [T], layer=1)
+    # the mixed stream: tokens from T_cut - W on come from a second draw
+    mix_k = a_k.copy(); mix_v = a_v.copy()
+    mix_k[:, :, T_cut - s.W:] = b_k[:, :, T_cut - s.W:]
+    mix_v[:, :, T_cut - s.W:] = b_v[:, :, T_cut - s.W:]
+    ctx = context_for(s)
+    # stale cache: all T tokens of stream a, then cut back to T_cut with the
+    # ring restored to the mixed stream's last W tokens before T_cut
+    d1 = upload_cache(s.cache(1, T))
+    _gpu_append(ctx, d1, a_k, a_v, counts=[T])
+    torch.cuda.synchronize()
+    d1["seq_lens"].fill_(T_cut)
+    for t in range(T_cut - s.W, T_cut):
+        d1["k_win"][0, :, t % s.W] = torch.from_numpy(mix_k[0, :, t].view(np.uint16)).cuda().view(torch.float16)
+        d1["v_win"][0, :, t % s.W] = torch.from_numpy(mix_v[0, :, t].view(np.uint16)).cuda().view(torch.float16)
+    for t in range(T_cut, T):
+        _gpu_append(ctx, d1, np.ascontiguousarray(mix_k[:, :, t:t + 1]), np.ascontiguousarray(mix_v[:, :, t:t + 1]),
+                    counts=[1])
+    # reference: one bulk append of the mixed stream
+    d2 = upload_cache(s.cache(1, T))
+    _gpu_append(ctx, d2, mix_k, mix_v, counts=[T])
+    torch.cuda.synchronize()
+    assert tqa.tq_get_status(ctx) == 0
+    caches = []
+    for dv in (d1, d2):
+        g = s.cache(1, T)
+        g.pool = dv["pool"].cpu().numpy().reshape(g.pool.shape)
+        g.seq_lens = dv["seq_lens"].cpu().numpy()
+        caches.append(g)
+    assert caches[0].seq_lens[0] == T and caches[1].seq_lens[0] == T
+    for h in range(s.Hkv):
+        (k1, vn1, vi1), (k2, vn2, vi2) = caches[0].compressed(0, h), caches[1].compressed(0, h)
+        assert np.array_equal(vi1, vi2) and np.array_equal(vn1, vn2), h
+        assert np.array_equal(k1.codes, k2.codes) and np.array_equal(k1.norms, k2.norms), h
+        assert np.array_equal(k1.signs, k2.signs) and np.array_equal(k1.rnorms, k2.rnorms), h
+    assert torch.equal(d1["k_win"].cpu(), d2["k_win"].cpu()) and torch.equal(d1["v_win"].cpu(), d2["v_win"].cpu())
