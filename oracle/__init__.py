@@ -20,6 +20,7 @@ MacBook" is the blog post on debugging TurboQuant on an Apple M1 Pro,
                    sketch) and dequantisation.
 * ``mixed``      - mixed-channel fractional rates (2.5 and 3.5 bits): half the
                    rotated coordinates at b bits, half at b + 1.
+* ``lognorm``    - u8 log-norm codes for key norms (the low-overhead mode).
 * ``pages``      - fixed-size page format, FP16 recent-token ring, append.
 * ``attention``  - decode attention two ways: dequantise-then-softmax (the
                    plain definition) and the compressed-domain formula.
@@ -30,4 +31,4 @@ against printed values, closed forms, brute force or invariants; none is
 "parity unpinned".
 """
 
-from . import accounting, attention, codebook, codec, mixed, pages, rotation  # noqa: F401
+from . import accounting, attention, codebook, codec, lognorm, mixed, pages, rotation  # noqa: F401

@@ -1,8 +1,9 @@
 """Per-vector TurboQuant encode and dequantise (test oracle only).
 
 Encode of one post-RoPE vector x (float values, taken exactly as float64):
-1. n = ||x||_2, stored as float32; u = x / n ("aither-kvcache" README,
-   "Algorithm" step 1).  A zero vector stores n = 0 and all-zero codes, signs
+1. n = ||x||_2, stored as float32 (or, for keys in the low-overhead mode,
+   as a u8 log-norm code, ``oracle.lognorm``); u = x / n ("aither-kvcache"
+   README, "Algorithm" step 1).  A zero vector stores n = 0 and all-zero codes, signs
    and residual norm, so it decodes to exact zeros ("TurboQuant on a 16GB
    MacBook", "Round 2: the llama.cpp bug hunt", the zero-block fix).
 2. y = Pi u (step 2).
@@ -72,16 +73,20 @@ class Encoded:
     """Flat records for n vectors: codes uint8 [n, d*b/8], norms f32 [n],
     and for keys with QJL signs uint8 [n, d/8] and rnorms f32 [n]."""
 
-    def __init__(self, codes, norms, signs=None, rnorms=None, idx=None):
+    def __init__(self, codes, norms, signs=None, rnorms=None, idx=None, norm_codes=None):
         self.codes = codes
         self.norms = norms
         self.signs = signs
         self.rnorms = rnorms
         self.idx = idx  # unpacked code indices, kept for tests
+        self.norm_codes = norm_codes  # u8 log-norm codes, when the norms are stored that way
 
 
-def encode(x: np.ndarray, rotation, codebook, qjl_S=None) -> Encoded:
-    """Encode row vectors x [n, d]; keys pass the QJL matrix, values pass None."""
+def encode(x: np.ndarray, rotation, codebook, qjl_S=None, norm_u8=False) -> Encoded:
+    """Encode row vectors x [n, d]; keys pass the QJL matrix, values pass None.
+    ``norm_u8``: the norm is stored as a u8 log-norm code (``oracle.lognorm``);
+    the record's float32 norm is then that code's level and the QJL residual
+    is taken against it."""
     x = np.asarray(x, dtype=np.float64)
     n_vec, d = x.shape
     norm = np.sqrt(np.sum(x * x, axis=1))
@@ -92,7 +97,13 @@ def encode(x: np.ndarray, rotation, codebook, qjl_S=None) -> Encoded:
     y32 = y.astype(np.float32).astype(np.float64)
     idx = codebook.quantize(y32)
     idx[~nonzero] = 0
+    ncode = None
+    if norm_u8:
+        from . import lognorm
+        ncode = lognorm.encode(norm32.astype(np.float32))
+        norm32 = lognorm.decode(ncode).astype(np.float32).astype(np.float64)
     rec = Encoded(codebook.pack(idx), norm32.astype(np.float32), idx=idx)
+    rec.norm_codes = ncode
     if qjl_S is not None:
         r = rotation.forward(x) - norm32[:, None] * codebook.values(idx)
         r[~nonzero] = 0.0

@@ -22,9 +22,10 @@ the library implements, stated here independently of its source):
     12 u16 num_kv_heads                   14 u16 page_tokens
     16 u32 valid tokens in this page      20 u32 codebook version (1)
     24 u64 seed                           32 u32 page index within its sequence
-    36..63 zero; bytes [64, 256) zero
+    36 u8 key norm format (0 float32, 1 u8 log-norm)
+    37..63 zero; bytes [64, 256) zero
   body, head h at 256 + h * head_bytes, streams in this order:
-    key norms   f32 [P]
+    key norms   f32 [P], or u8 [P] log-norm codes (``oracle.lognorm``)
     key rnorms  f32 [P]                (QJL only)
     key codes   u8  [P][d*bK/8]        token-major, LSB-first per token
     key signs   u8  [P][d/8]           (QJL only) bit j = sigma_j
@@ -56,17 +57,18 @@ V_GROUP = 32
 
 class Layout:
     def __init__(self, head_dim, key_bits, key_qjl, value_bits, num_kv_heads, page_tokens, key_mixed=False,
-                 value_mixed=False):
+                 value_mixed=False, key_norm_u8=False):
         d, P = head_dim, page_tokens
         if P % V_GROUP:
             raise ValueError("page_tokens must be a multiple of 32")
         self.d, self.bK, self.qjl, self.bV, self.H, self.P = d, key_bits, int(key_qjl), value_bits, num_kv_heads, P
         self.kmix, self.vmix = bool(key_mixed), bool(value_mixed)
+        self.kn8 = bool(key_norm_u8)
         # code bytes of one key record and of one token's value codes
         self.k_rec = d * key_bits // 8 + (d // 16 if self.kmix else 0)
         self.v_rec = d * value_bits // 8 + (d // 16 if self.vmix else 0)
         off = 0
-        self.k_norm = off; off += 4 * P
+        self.k_norm = off; off += (1 if self.kn8 else 4) * P
         if self.qjl:
             self.k_rnorm = off; off += 4 * P
         self.k_codes = off; off += P * self.k_rec
@@ -108,6 +110,7 @@ def write_header(page: np.ndarray, lay: Layout, rotation_kind: int, seed: int, v
     hv[5] = CODEBOOK_VERSION
     hdr[24:32] = np.frombuffer(np.uint64(seed).tobytes(), np.uint8)
     hv[8] = page_index
+    hdr[36] = 1 if lay.kn8 else 0
     page[:HEADER_BYTES] = hdr
 
 
@@ -119,7 +122,10 @@ def write_key_records(page, lay: Layout, h, slots, rec: codec.Encoded):
     """Store key records (flat ``codec.Encoded``) at the given token slots."""
     base = lay.head_base(h)
     cb = lay.k_rec
-    _f32(page, base + lay.k_norm, lay.P)[slots] = rec.norms
+    if lay.kn8:
+        page[base + lay.k_norm: base + lay.k_norm + lay.P][slots] = rec.norm_codes
+    else:
+        _f32(page, base + lay.k_norm, lay.P)[slots] = rec.norms
     codes = page[base + lay.k_codes: base + lay.k_codes + lay.P * cb].reshape(lay.P, cb)
     codes[slots] = rec.codes
     if lay.qjl:
@@ -156,14 +162,20 @@ def write_value_records(page, lay: Layout, h, slots, value_cb, rec: codec.Encode
 def read_key_records(page, lay: Layout, h, n):
     base = lay.head_base(h)
     cb = lay.k_rec
-    norms = _f32(page, base + lay.k_norm, lay.P)[:n].copy()
+    if lay.kn8:
+        from . import lognorm
+        nc = page[base + lay.k_norm: base + lay.k_norm + n].copy()
+        norms = lognorm.decode(nc).astype(np.float32)
+    else:
+        nc = None
+        norms = _f32(page, base + lay.k_norm, lay.P)[:n].copy()
     codes = page[base + lay.k_codes: base + lay.k_codes + lay.P * cb].reshape(lay.P, cb)[:n].copy()
     signs = rnorms = None
     if lay.qjl:
         rnorms = _f32(page, base + lay.k_rnorm, lay.P)[:n].copy()
         sb = lay.d // 8
         signs = page[base + lay.k_signs: base + lay.k_signs + lay.P * sb].reshape(lay.P, sb)[:n].copy()
-    return codec.Encoded(codes, norms, signs, rnorms)
+    return codec.Encoded(codes, norms, signs, rnorms, norm_codes=nc)
 
 
 def read_value_idx(page, lay: Layout, h, n):
@@ -239,7 +251,7 @@ class PagedCache:
 
     def _store(self, b, h, pos, kx, vx):
         lay = self.lay
-        krec = codec.encode(kx, self.rot, self.kcb, self.S if lay.qjl else None)
+        krec = codec.encode(kx, self.rot, self.kcb, self.S if lay.qjl else None, norm_u8=lay.kn8)
         vrec = codec.encode(vx, self.rot, self.vcb, None)
         for pg in np.unique(pos // lay.P):
             sel = np.nonzero(pos // lay.P == pg)[0]
@@ -250,7 +262,8 @@ class PagedCache:
             slots = pos[sel] % lay.P
             sub = lambda r: codec.Encoded(r.codes[sel], r.norms[sel],
                                           None if r.signs is None else r.signs[sel],
-                                          None if r.rnorms is None else r.rnorms[sel])
+                                          None if r.rnorms is None else r.rnorms[sel],
+                                          norm_codes=None if r.norm_codes is None else r.norm_codes[sel])
             write_key_records(page, lay, h, slots, sub(krec))
             write_value_records(page, lay, h, slots, self.vcb, sub(vrec))
 
@@ -279,7 +292,8 @@ class PagedCache:
             return None
         cat = lambda xs: None if xs[0] is None else np.concatenate(xs)
         k = codec.Encoded(cat([r.codes for r in krecs]), cat([r.norms for r in krecs]),
-                          cat([r.signs for r in krecs]), cat([r.rnorms for r in krecs]))
+                          cat([r.signs for r in krecs]), cat([r.rnorms for r in krecs]),
+                          norm_codes=cat([r.norm_codes for r in krecs]))
         return k, np.concatenate(vn), np.concatenate(vidx)
 
     def window_tokens(self, b, h):

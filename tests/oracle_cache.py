@@ -13,9 +13,10 @@ import tq_inputs
 class Setup:
     def __init__(self, d=128, key_bits=3, key_qjl=1, value_bits=4, rotation="dense", seed=0,
                  Hq=1, Hkv=1, P=256, W=128, qjl_kind="gaussian", qjl_shrink=1.0, key_mixed=False,
-                 value_mixed=False):
+                 value_mixed=False, key_norm_u8=False):
         self.d, self.bK, self.qjl, self.bV = d, key_bits, key_qjl, value_bits
         self.kmix, self.vmix = key_mixed, value_mixed
+        self.kn8 = key_norm_u8
         self.qjl_kind, self.qjl_shrink = qjl_kind, qjl_shrink
         self.rotation, self.seed, self.Hq, self.Hkv, self.P, self.W = rotation, seed, Hq, Hkv, P, W
         if rotation == "dense":
@@ -30,7 +31,7 @@ class Setup:
         self.qjl_coef = codec.qjl_scale(d, qjl_kind, qjl_shrink)
         # page-header QJL byte: 0 none, 1 Gaussian S, 2 orthogonal S
         self.lay = pages.Layout(d, key_bits, (1 + (qjl_kind == "orthogonal")) if key_qjl else 0, value_bits, Hkv, P,
-                                key_mixed, value_mixed)
+                                key_mixed, value_mixed, key_norm_u8)
 
     def cache(self, batch, max_tokens):
         max_pages = max(1, -(-max(max_tokens - self.W, 0) // self.P))
