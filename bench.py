@@ -47,12 +47,13 @@ def parse():
     ap.add_argument("--value-bits", type=int, default=4)
     ap.add_argument("--key-mixed", action="store_true", help="keys at key_bits + 1/2 (mixed-channel rate)")
     ap.add_argument("--value-mixed", action="store_true", help="values at value_bits + 1/2")
+    ap.add_argument("--key-norm-u8", action="store_true", help="key norms as u8 log-norm codes")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy (reference for HBM byte counters)")
     return ap.parse_args()
 
 
-def cpu_baseline(T, W, P, G, Hkv, min_seconds, kbits=3, vbits=4, kmix=0, vmix=0):
+def cpu_baseline(T, W, P, G, Hkv, min_seconds, kbits=3, vbits=4, kmix=0, vmix=0, kn8=0):
     """The oracle's decode (dequantise + float64 softmax attention) on one
     sequence and one KV head (G query heads) at context T, repeated until
     min_seconds of CPU work; converted to sequence-tokens/s at H_kv heads."""
@@ -62,7 +63,7 @@ def cpu_baseline(T, W, P, G, Hkv, min_seconds, kbits=3, vbits=4, kmix=0, vmix=0)
     from oracle_cache import Setup, fill
     import tq_inputs
     s = Setup(Hq=G, Hkv=1, key_bits=kbits, key_qjl=1, value_bits=vbits, P=P, W=W, key_mixed=bool(kmix),
-              value_mixed=bool(vmix))
+              value_mixed=bool(vmix), key_norm_u8=bool(kn8))
     cache = s.cache(1, T)
     fill(s, cache, [T])
     q = tq_inputs.queries(3, (1, G, 128))
@@ -165,9 +166,11 @@ def main():
     nsteps = args.warmup + args.steps
     T0 = Tf - nsteps
     kbits, vbits, kmix, vmix = args.key_bits, args.value_bits, int(args.key_mixed), int(args.value_mixed)
+    kn8 = int(args.key_norm_u8)
     params = tqa.make_params(key_bits=kbits, key_qjl=1, value_bits=vbits, rotation=tqa.TQ_ROT_DENSE, num_q_heads=Hq,
                              num_kv_heads=Hkv, page_tokens=P, window=W, seed=0,
-                             flags=tqa.TQ_FLAG_VALU_SCAN if args.valu_scan else 0, key_mixed=kmix, value_mixed=vmix)
+                             flags=tqa.TQ_FLAG_VALU_SCAN if args.valu_scan else 0, key_mixed=kmix, value_mixed=vmix,
+                             key_norm_u8=kn8)
     ctx = tqa.Context(params, tq_inputs.rotation_draws(0, d), tq_inputs.qjl_draws(0, d))
     pb = tqa.tq_page_bytes(params)
     max_pages = -(-(Tf - W) // P)
@@ -215,7 +218,8 @@ def main():
     lens = [T0 + i + 1 for i in range(args.warmup, nsteps)]
     tokens = B * sum(lens)
     # key codes + signs + norm + rnorm, value codes + norm (a mixed rate adds d/16 code bytes)
-    per_tok_head = (16 * kbits + 8 * kmix + 16 + 4 + 4) + (16 * vbits + 8 * vmix + 4)
+    # (a u8 log-norm key norm takes 1 byte instead of 4)
+    per_tok_head = (16 * kbits + 8 * kmix + 16 + 4 + (1 if kn8 else 4)) + (16 * vbits + 8 * vmix + 4)
     comp_bytes = [B * Hkv * (T - W) * per_tok_head for T in lens]
     win_bytes = B * Hkv * W * d * 2 * 2
     scan_s = scan_ms / 1e3 / max(ncalls, 1)
@@ -227,13 +231,15 @@ def main():
         "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
         "config": {"workload": f"decode step (append 1 token + decode attention), B={B}, Hq={Hq}, Hkv={Hkv}, "
                                f"d={d}, T={Tf} (last step), W={W} fp16 window, P={P}, keys "
-                               f"{kbits + 0.5 * kmix:g}-bit+QJL, values {vbits + 0.5 * vmix:g}-bit, dense rotation, "
-                               f"bf16 queries",
+                               f"{kbits + 0.5 * kmix:g}-bit+QJL{' with u8 log-norms' if kn8 else ''}, values "
+                               f"{vbits + 0.5 * vmix:g}-bit, dense rotation, bf16 queries",
                    "batch": B, "seq_len": Tf, "parallelism": "none (1 GPU)"},
         "hbm_gbps_step": (sum(comp_bytes) / len(comp_bytes) + win_bytes) / (ms_step / 1e3) / 1e9,
         "scan_us": scan_s * 1e6,
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBPS, "traffic": scan_traffic(),
+                     "frac": achieved / HBM_PEAK_GBPS,
+                     # the committed counter record covers the default formats only
+                     "traffic": scan_traffic() if (kbits, vbits, kmix, vmix, kn8) == (3, 4, 0, 0, 0) else None,
                      "kernel": "scan_kernel (VALU)" if args.valu_scan else "scan_mfma_kernel",
                      "algorithmic_bytes_per_launch": sum(comp_bytes) / len(comp_bytes)},
     }
@@ -249,10 +255,10 @@ def main():
                            "frac_of_peak": read_gbps / HBM_PEAK_GBPS}
     res["roofline"]["frac_of_read_ceiling"] = achieved / read_gbps
     # the encode leg measures the default formats (3-bit+QJL keys, 4-bit values)
-    if not args.no_encode and (kbits, vbits, kmix, vmix) == (3, 4, 0, 0):
+    if not args.no_encode and (kbits, vbits, kmix, vmix, kn8) == (3, 4, 0, 0, 0):
         res["encode"] = encode_leg(tqa, tq_inputs, ctx, params)
     if not args.no_cpu_baseline:
-        res["cpu_baseline"] = cpu_baseline(Tf, W, P, G, Hkv, args.cpu_seconds, kbits, vbits, kmix, vmix)
+        res["cpu_baseline"] = cpu_baseline(Tf, W, P, G, Hkv, args.cpu_seconds, kbits, vbits, kmix, vmix, kn8)
     print(json.dumps(res), flush=True)
 
 

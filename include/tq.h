@@ -39,8 +39,9 @@
  *   (u32 magic 0x564B5154, u16 version 1, u16 d, u8 key_bits, u8 key QJL
  *   (0 none, 1 Gaussian S, 2 orthogonal S),
  *   u8 value_bits, u8 rotation, u16 H_kv, u16 P, u32 valid tokens, u32
- *   codebook version 1, u64 seed, u32 page index, zeros); head h's body at
- *   256 + h * head_bytes holds, in order: key norms f32[P]; key residual norms
+ *   codebook version 1, u64 seed, u32 page index, u8 key norm format (0 f32,
+ *   1 u8 log-norm), zeros); head h's body at 256 + h * head_bytes holds, in
+ *   order: key norms f32[P] (u8[P] codes with key_norm_u8); key residual norms
  *   f32[P] (QJL only); key codes u8[P][d*bK/8] token-major, LSB-first; key
  *   signs u8[P][d/8] (QJL only); value norms f32[P]; value codes
  *   u32[P/32][bV][d], where for each 32-token group and coordinate j the bV
@@ -118,6 +119,12 @@ typedef struct tq_params {
                            high-rate ones ("TurboQuant Family Design Study", "Packed format and
                            complete bit accounting": 2.5 / 3.5 bits per channel for d = 128) */
   int32_t value_mixed;  /* 1: the same for values, high-rate coordinates j mod 8 >= 4 */
+  int32_t key_norm_u8;  /* 1: key norms stored as u8 log-norm codes, one byte per token-head
+                           ("TurboQuant Family Design Study", "Packed format and complete bit
+                           accounting": the low-overhead modes, 0.0625 bits per channel):
+                           code 0 for a zero norm, else the level 2^(q/16 - 4), q = 1..255,
+                           nearest in log2 (float32 boundaries 2^((q + 1/2)/16 - 4)); the QJL
+                           residual is taken against the stored level */
 } tq_params;
 
 typedef struct tq_ctx tq_ctx;

@@ -46,15 +46,18 @@ class tq_params(ctypes.Structure):
         ("num_kv_heads", ctypes.c_int32), ("page_tokens", ctypes.c_int32), ("window", ctypes.c_int32),
         ("flags", ctypes.c_int32), ("seed", ctypes.c_uint64), ("qjl_kind", ctypes.c_int32),
         ("qjl_shrink", ctypes.c_float), ("key_mixed", ctypes.c_int32), ("value_mixed", ctypes.c_int32),
+        ("key_norm_u8", ctypes.c_int32),
     ]
 
 
 def make_params(head_dim=128, key_bits=3, key_qjl=1, value_bits=4, rotation=TQ_ROT_DENSE, num_q_heads=1,
                 num_kv_heads=1, page_tokens=256, window=128, seed=0, flags=0, qjl_kind=0, qjl_shrink=1.0,
-                key_mixed=0, value_mixed=0):
-    """key_mixed / value_mixed: mixed-channel rate bits + 1/2 (bits 2 or 3)."""
+                key_mixed=0, value_mixed=0, key_norm_u8=0):
+    """key_mixed / value_mixed: mixed-channel rate bits + 1/2 (bits 2 or 3);
+    key_norm_u8: key norms stored as u8 log-norm codes."""
     return tq_params(head_dim, key_bits, key_qjl, value_bits, rotation, num_q_heads, num_kv_heads,
-                     page_tokens, window, flags, seed, qjl_kind, qjl_shrink, key_mixed, value_mixed)
+                     page_tokens, window, flags, seed, qjl_kind, qjl_shrink, key_mixed, value_mixed,
+                     int(key_norm_u8))
 
 
 _lib = None

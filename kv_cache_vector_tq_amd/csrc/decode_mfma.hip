@@ -199,7 +199,8 @@ struct KBuf {
   // words 0-1 the low-rate piece (coordinates 32kg .. +15), 2-3 the high-rate one
   uint32_t kc[2][KMIX ? 4 : BK];
   uint32_t sg[2];      // their sign bits
-  float kn[2], rn[2];
+  uint32_t kn[2];      // key norms: float32 bits, or u8 log-norm codes (decoded when scoring)
+  float rn[2];
   float vn[2];         // value norms of tokens n / 16+n (used when scoring)
 };
 template <int BV, bool VMIX>
@@ -234,7 +235,7 @@ struct Meta {
 template <int G, int BV, bool KMIX, bool VMIX>
 constexpr int scan_waves_per_simd() { return (BV == 3 || KMIX || VMIX || G == 8) ? 3 : 4; }
 
-template <int G, int BK, int BV, bool QJL, bool KMIX, bool VMIX>
+template <int G, int BK, int BV, bool QJL, bool KMIX, bool VMIX, bool N8>
 __global__ __launch_bounds__((ScanShape<G, BV, VMIX>::kThreads), (scan_waves_per_simd<G, BV, KMIX, VMIX>())) void
 scan_mfma_kernel(DecodeArgs a, DevTables t, Codebooks cb, KParams k) {
   using Sh = ScanShape<G, BV, VMIX>;
@@ -424,9 +425,15 @@ scan_mfma_kernel(DecodeArgs a, DevTables t, Codebooks cb, KParams k) {
     m.rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(hb), 0, static_cast<int>(k.head_bytes), kRsrcWord3);
   };
   auto loadK = [&](const Meta& m, KBuf<BK, KMIX>& d) {
-    const int so_kn = static_cast<int>(k.k_norm) + 4 * m.s0;
-    d.kn[0] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(m.rs, o_tok0, so_kn, kStream));
-    d.kn[1] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(m.rs, o_tok1, so_kn, kStream));
+    if constexpr (N8) {
+      const int so_kn = static_cast<int>(k.k_norm) + m.s0;
+      d.kn[0] = __builtin_amdgcn_raw_buffer_load_b8(m.rs, o_tok0 >> 2, so_kn, kStream);
+      d.kn[1] = __builtin_amdgcn_raw_buffer_load_b8(m.rs, o_tok1 >> 2, so_kn, kStream);
+    } else {
+      const int so_kn = static_cast<int>(k.k_norm) + 4 * m.s0;
+      d.kn[0] = __builtin_amdgcn_raw_buffer_load_b32(m.rs, o_tok0, so_kn, kStream);
+      d.kn[1] = __builtin_amdgcn_raw_buffer_load_b32(m.rs, o_tok1, so_kn, kStream);
+    }
     if constexpr (QJL) {
       const int so_rn = static_cast<int>(k.k_rnorm) + 4 * m.s0;
       d.rn[0] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(m.rs, o_tok0, so_rn, kStream));
@@ -522,7 +529,11 @@ scan_mfma_kernel(DecodeArgs a, DevTables t, Codebooks cb, KParams k) {
       const bool live = 16 * tt + n < m.ntok;
 #pragma unroll
       for (int i = 0; i < 2; ++i) {
-        float v = (dm[i] + dm[i + 2]) * d.kn[tt];
+        // u8 log-norm code q: level 2^(q/16 - 4), code 0 a zero norm
+        const float kn = N8 ? (d.kn[tt] ? __builtin_amdgcn_exp2f(static_cast<float>(d.kn[tt]) * 0.0625f - 4.0f)
+                                        : 0.0f)
+                            : __builtin_bit_cast(float, d.kn[tt]);
+        float v = (dm[i] + dm[i + 2]) * kn;
         if constexpr (QJL) v = fmaf(dq[i] + dq[i + 2], d.rn[tt], v);
         sc[i][tt] = live ? v : -INFINITY;
       }
@@ -678,34 +689,37 @@ scan_mfma_kernel(DecodeArgs a, DevTables t, Codebooks cb, KParams k) {
 }
 
 template <int G, int BK, int BV, bool KMIX, bool VMIX>
-const void* pick_bits(bool qjl) {
-  return qjl ? reinterpret_cast<const void*>(&scan_mfma_kernel<G, BK, BV, true, KMIX, VMIX>)
-             : reinterpret_cast<const void*>(&scan_mfma_kernel<G, BK, BV, false, KMIX, VMIX>);
+const void* pick_bits(bool qjl, bool n8) {
+  if (n8)
+    return qjl ? reinterpret_cast<const void*>(&scan_mfma_kernel<G, BK, BV, true, KMIX, VMIX, true>)
+               : reinterpret_cast<const void*>(&scan_mfma_kernel<G, BK, BV, false, KMIX, VMIX, true>);
+  return qjl ? reinterpret_cast<const void*>(&scan_mfma_kernel<G, BK, BV, true, KMIX, VMIX, false>)
+             : reinterpret_cast<const void*>(&scan_mfma_kernel<G, BK, BV, false, KMIX, VMIX, false>);
 }
 
 // mixed-channel rates exist for 2.5 and 3.5 bits (low width 2 or 3)
 template <int G, int BK, bool KMIX>
-const void* pick_bv(int bv, bool vmix, bool qjl) {
+const void* pick_bv(int bv, bool vmix, bool qjl, bool n8) {
   if (vmix) {
-    if (bv == 2) return pick_bits<G, BK, 2, KMIX, true>(qjl);
-    if (bv == 3) return pick_bits<G, BK, 3, KMIX, true>(qjl);
+    if (bv == 2) return pick_bits<G, BK, 2, KMIX, true>(qjl, n8);
+    if (bv == 3) return pick_bits<G, BK, 3, KMIX, true>(qjl, n8);
     return nullptr;
   }
-  if (bv == 2) return pick_bits<G, BK, 2, KMIX, false>(qjl);
-  if (bv == 3) return pick_bits<G, BK, 3, KMIX, false>(qjl);
-  return pick_bits<G, BK, 4, KMIX, false>(qjl);
+  if (bv == 2) return pick_bits<G, BK, 2, KMIX, false>(qjl, n8);
+  if (bv == 3) return pick_bits<G, BK, 3, KMIX, false>(qjl, n8);
+  return pick_bits<G, BK, 4, KMIX, false>(qjl, n8);
 }
 
 template <int G>
-const void* pick_g(int bk, bool kmix, int bv, bool vmix, bool qjl) {
+const void* pick_g(int bk, bool kmix, int bv, bool vmix, bool qjl, bool n8) {
   if (kmix) {
-    if (bk == 2) return pick_bv<G, 2, true>(bv, vmix, qjl);
-    if (bk == 3) return pick_bv<G, 3, true>(bv, vmix, qjl);
+    if (bk == 2) return pick_bv<G, 2, true>(bv, vmix, qjl, n8);
+    if (bk == 3) return pick_bv<G, 3, true>(bv, vmix, qjl, n8);
     return nullptr;
   }
-  if (bk == 2) return pick_bv<G, 2, false>(bv, vmix, qjl);
-  if (bk == 3) return pick_bv<G, 3, false>(bv, vmix, qjl);
-  return pick_bv<G, 4, false>(bv, vmix, qjl);
+  if (bk == 2) return pick_bv<G, 2, false>(bv, vmix, qjl, n8);
+  if (bk == 3) return pick_bv<G, 3, false>(bv, vmix, qjl, n8);
+  return pick_bv<G, 4, false>(bv, vmix, qjl, n8);
 }
 
 }  // namespace
@@ -713,11 +727,12 @@ const void* pick_g(int bk, bool kmix, int bv, bool vmix, bool qjl) {
 const void* scan_mfma_kernel_ptr(const tq_ctx* c) {
   const int G = c->p.num_q_heads / c->p.num_kv_heads, bk = c->p.key_bits, bv = c->p.value_bits;
   const bool qjl = c->p.key_qjl != 0, kmix = c->p.key_mixed != 0, vmix = c->p.value_mixed != 0;
+  const bool n8 = c->p.key_norm_u8 != 0;
   switch (G) {
-    case 1: return pick_g<1>(bk, kmix, bv, vmix, qjl);
-    case 2: return pick_g<2>(bk, kmix, bv, vmix, qjl);
-    case 4: return pick_g<4>(bk, kmix, bv, vmix, qjl);
-    case 8: return pick_g<8>(bk, kmix, bv, vmix, qjl);
+    case 1: return pick_g<1>(bk, kmix, bv, vmix, qjl, n8);
+    case 2: return pick_g<2>(bk, kmix, bv, vmix, qjl, n8);
+    case 4: return pick_g<4>(bk, kmix, bv, vmix, qjl, n8);
+    case 8: return pick_g<8>(bk, kmix, bv, vmix, qjl, n8);
     default: return nullptr;
   }
 }

@@ -25,6 +25,8 @@ struct Smem {
   float rs[kTile][kD];   // residuals / butterfly scratch
   uint8_t code[kTile][kD];
   float n32[kTile], invn[kTile], rn[kTile];
+  float nst[kTile];    // the stored norm: n32, or the u8 log-norm level
+  int nq[kTile];       // u8 log-norm code
   uint32_t sgn[kTile][4];
   float ctab[32];  // centroids; [16, 32): the (b+1)-bit codebook of a mixed rate
 };
@@ -32,6 +34,7 @@ struct Smem {
 struct CoreParams {
   int bits;
   bool qjl;
+  bool n8;         // the norm is stored as a u8 log-norm code (keys)
   int hmod;        // mixed-channel rate: coordinate j takes bits + 1 when j mod hmod >= hmod/2; 0: integer rate
   float bnd[16];   // decision boundaries (uniform values)
   float cen[16];   // centroids
@@ -39,10 +42,12 @@ struct CoreParams {
   float cen2[16];
 };
 
-__device__ inline CoreParams make_core(const Codebooks& cb, bool key, int bits, bool qjl, bool mixed) {
+__device__ inline CoreParams make_core(const Codebooks& cb, bool key, int bits, bool qjl, bool mixed,
+                                       bool n8 = false) {
   CoreParams cp;
   cp.bits = bits;
   cp.qjl = qjl;
+  cp.n8 = n8;
   cp.hmod = mixed ? (key ? kKeyHiMod : kValHiMod) : 0;
 #pragma unroll
   for (int k = 0; k < 16; ++k) {
@@ -85,14 +90,23 @@ __device__ void encode_core(Smem& sm, const DevTables& t, const CoreParams& cp, 
     s += __shfl_xor(s, 2, 64);
     if (part == 0) {
       const double n = sqrt(s);
-      sm.n32[v] = static_cast<float>(n);
+      const float n32 = static_cast<float>(n);
+      sm.n32[v] = n32;
       sm.invn[v] = n > 0.0 ? static_cast<float>(1.0 / n) : 0.0f;
+      float nst = n32;
+      if (cp.n8) {
+        const int q = norm_code(n32, t.ntab + kNormCodes);
+        sm.nq[v] = q;
+        nst = t.ntab[q];
+      }
+      sm.nst[v] = nst;
     }
   }
   __syncthreads();
-  // quantise one vector's coordinate (this thread's) and keep the key residual
+  // quantise one vector's coordinate (this thread's) and keep the key
+  // residual against the stored reconstruction nst c[code]
   auto finish = [&](int v, float accv) {
-    const float n = sm.n32[v];
+    const float n = sm.nst[v];
     const float y = accv * sm.invn[v];
     int c = 0;
 #pragma unroll
@@ -227,7 +241,7 @@ __device__ inline uint32_t code_word(const SM& sm, int v, int w, int bits, int h
 
 template <bool HAD>
 __global__ __launch_bounds__(kThreads) void encode_flat_kernel(EncodeArgs a, DevTables t, Codebooks cb, int kind,
-                                                              int dtype, int bits, int qjl, int mixed) {
+                                                              int dtype, int bits, int qjl, int mixed, int n8) {
   __shared__ Smem sm;
   const int tid = threadIdx.x;
   const int64_t n0 = static_cast<int64_t>(blockIdx.x) * kTile;
@@ -235,11 +249,11 @@ __global__ __launch_bounds__(kThreads) void encode_flat_kernel(EncodeArgs a, Dev
   for (int v = 0; v < kTile; ++v)
     sm.xs[v][tid] = v < nv ? load_any(a.x, (n0 + v) * a.row_stride + tid, dtype) : 0.0f;
   __syncthreads();
-  const CoreParams cp = make_core(cb, kind == TQ_KIND_KEY, bits, qjl != 0, mixed != 0);
+  const CoreParams cp = make_core(cb, kind == TQ_KIND_KEY, bits, qjl != 0, mixed != 0, n8 != 0);
   encode_core<HAD>(sm, t, cp, 0, nv);
   __syncthreads();
   if (tid < nv) {
-    a.norms[n0 + tid] = sm.n32[tid];
+    a.norms[n0 + tid] = sm.nst[tid];
     if (qjl) a.rnorms[n0 + tid] = sm.rn[tid];
   }
   const int wpv = 4 * bits + (mixed ? 2 : 0);  // 32-bit words per record (d = 128)
@@ -340,14 +354,16 @@ __device__ void encode_group(Smem& sm, const AppendArgs& a, const DevTables& t, 
     }
     __syncthreads();
     const bool key = kv == 0;
-    const CoreParams cp = make_core(cb, key, key ? L.bK : L.bV, key && L.qjl, key ? L.kmix : L.vmix);
+    const CoreParams cp = make_core(cb, key, key ? L.bK : L.bV, key && L.qjl, key ? L.kmix : L.vmix, key && L.kn8);
     const int vlo = lo - gpos, vhi = hi - gpos;
     encode_core<HAD>(sm, t, cp, vlo, vhi);
     __syncthreads();
     if (key) {
-      float* kn = reinterpret_cast<float*>(hb + L.k_norm);
       if (tid >= vlo && tid < vhi) {
-        kn[slot0 + tid] = sm.n32[tid];
+        if (L.kn8)
+          (hb + L.k_norm)[slot0 + tid] = static_cast<uint8_t>(sm.nq[tid]);
+        else
+          reinterpret_cast<float*>(hb + L.k_norm)[slot0 + tid] = sm.n32[tid];
         if (L.qjl) reinterpret_cast<float*>(hb + L.k_rnorm)[slot0 + tid] = sm.rn[tid];
       }
       const int wpv = L.k_rec / 4;
@@ -433,8 +449,11 @@ struct SmallSmem {
   float hx[kSmallNew][kD];   // Hadamard stride-64 exchange
   uint8_t code[kSmallNew][kD];
   float n32[kSmallNew], invn[kSmallNew], rn[kSmallNew];
+  float nst[kSmallNew];  // the stored norm: n32, or the u8 log-norm level
+  int nq[kSmallNew];     // u8 log-norm code
   uint32_t sgn[kSmallNew][4];
   float cbt[64];  // this kind's centroids, boundaries, and the (b+1)-bit ones of a mixed rate
+  float ntab[2 * kNormCodes];  // u8 log-norm levels, then boundaries
 };
 
 // Double-precision squared norm of row v of `x` as the bulk kernel takes it:
@@ -471,7 +490,10 @@ __global__ __launch_bounds__(kSmallThreads) void append_small_kernel(AppendArgs 
   int cnt = a.n_new;
   if (a.counts != nullptr) cnt = a.counts[b];
   const float cbv = t.cbtab[(key ? 0 : 64) + (tid & 63)];
+  const float nt0 = t.ntab[tid], nt1 = t.ntab[kNormCodes + tid];
   if (tid < 64) sm.cbt[tid] = cbv;
+  sm.ntab[tid] = nt0;
+  sm.ntab[kNormCodes + tid] = nt1;
   // (every thread loads a table, used or not: loads under a branch leave the
   // compiler's wait counting at later uses conservative, i.e. full drains;
   // threads without a row of their own read Pi's, which their wave's other
@@ -560,8 +582,16 @@ __global__ __launch_bounds__(kSmallThreads) void append_small_kernel(AppendArgs 
       const int v = l >> 2;
       if ((l & 3) == 0 && v < nv) {
         const double n = sqrt(sq);
-        sm.n32[v] = static_cast<float>(n);
+        const float n32 = static_cast<float>(n);
+        sm.n32[v] = n32;
         sm.invn[v] = n > 0.0 ? static_cast<float>(1.0 / n) : 0.0f;
+        float nst = n32;
+        if (key && L.kn8) {
+          const int q = norm_code(n32, sm.ntab + kNormCodes);
+          sm.nq[v] = q;
+          nst = sm.ntab[q];
+        }
+        sm.nst[v] = nst;
       }
     }
   } else if constexpr (!HAD) {
@@ -610,7 +640,7 @@ __global__ __launch_bounds__(kSmallThreads) void append_small_kernel(AppendArgs 
 #pragma unroll
     for (int v = 0; v < kSmallNew; ++v) {
       if (v >= nv) break;
-      const float n = sm.n32[v];
+      const float n = sm.nst[v];  // the residual is taken against the stored norm
       const float y = acc[v] * sm.invn[v];
       int c = 0;
 #pragma unroll
@@ -660,7 +690,12 @@ __global__ __launch_bounds__(kSmallThreads) void append_small_kernel(AppendArgs 
         reinterpret_cast<uint32_t*>(head_base(pos) + L.k_codes)[(pos % L.P) * wpv + w] =
             code_word(sm, v, w, L.bK, hmod);
       }
-      if (tid < nv) reinterpret_cast<float*>(head_base(c0 + tid) + L.k_norm)[(c0 + tid) % L.P] = sm.n32[tid];
+      if (tid < nv) {
+        if (L.kn8)
+          (head_base(c0 + tid) + L.k_norm)[(c0 + tid) % L.P] = static_cast<uint8_t>(sm.nq[tid]);
+        else
+          reinterpret_cast<float*>(head_base(c0 + tid) + L.k_norm)[(c0 + tid) % L.P] = sm.n32[tid];
+      }
     }
     if (qjl) {
       lds_barrier();  // (4) signs and ||r||
@@ -750,7 +785,8 @@ __global__ void append_commit_kernel(AppendArgs a, DevTables t, Layout L, int W,
         hd[6] = static_cast<uint32_t>(seed);
         hd[7] = static_cast<uint32_t>(seed >> 32);
         hd[8] = static_cast<uint32_t>(pg);
-        for (int i = 9; i < 16; ++i) hd[i] = 0u;
+        hd[9] = static_cast<uint32_t>(L.kn8);  // byte 36: key norm format
+        for (int i = 10; i < 16; ++i) hd[i] = 0u;
       }
     }
     a.seq_lens[b] = sp.T0 + sp.cnt;
@@ -767,15 +803,16 @@ int launch_encode(const tq_ctx* c, int kind, int dtype, const EncodeArgs& a, voi
   const int bits = kind == TQ_KIND_KEY ? c->p.key_bits : c->p.value_bits;
   const int qjl = (kind == TQ_KIND_KEY && c->p.key_qjl) ? 1 : 0;
   const int mixed = (kind == TQ_KIND_KEY ? c->p.key_mixed : c->p.value_mixed) ? 1 : 0;
+  const int n8 = (kind == TQ_KIND_KEY && c->p.key_norm_u8) ? 1 : 0;
   const int64_t tiles = (a.n + kTile - 1) / kTile;
   if (tiles > 0x7fffffff) return 1;
   dim3 grid(static_cast<unsigned>(tiles));
   if (c->p.rotation == TQ_ROT_HADAMARD)
     hipLaunchKernelGGL(encode_flat_kernel<true>, grid, dim3(kThreads), 0, s, a, c->t, c->cb, kind, dtype, bits, qjl,
-                       mixed);
+                       mixed, n8);
   else
     hipLaunchKernelGGL(encode_flat_kernel<false>, grid, dim3(kThreads), 0, s, a, c->t, c->cb, kind, dtype, bits, qjl,
-                       mixed);
+                       mixed, n8);
   return hipGetLastError() == hipSuccess ? 0 : 1;
 }
 

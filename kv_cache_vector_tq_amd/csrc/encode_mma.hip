@@ -340,6 +340,8 @@ int launch_encode_mma(const tq_ctx* c, int kind, int dtype, const EncodeArgs& a,
   const bool key = kind == TQ_KIND_KEY;
   // mixed-channel rates take the vector-ALU encoder
   if (key ? c->p.key_mixed : c->p.value_mixed) return 1;
+  // so do keys with u8 log-norms
+  if (key && c->p.key_norm_u8) return 1;
   const bool qjl = key && c->p.key_qjl;
   const bool had = c->p.rotation == TQ_ROT_HADAMARD;
   const int bits = key ? c->p.key_bits : c->p.value_bits;

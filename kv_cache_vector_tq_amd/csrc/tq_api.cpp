@@ -4,6 +4,7 @@
 
 #include <cmath>
 #include <cstring>
+#include <limits>
 #include <new>
 #include <vector>
 
@@ -30,6 +31,7 @@ bool params_ok(const tq_params* p) {
   if (p->value_mixed != 0 && p->value_mixed != 1) return false;
   if (p->key_mixed && (p->key_bits < 2 || p->key_bits > 3 || p->head_dim % 32)) return false;
   if (p->value_mixed && (p->value_bits < 2 || p->value_bits > 3 || p->head_dim % 32)) return false;
+  if (p->key_norm_u8 != 0 && p->key_norm_u8 != 1) return false;
   return true;
 }
 
@@ -37,7 +39,7 @@ bool params_ok(const tq_params* p) {
 bool params_supported(const tq_params* p) {
   const int G = p->num_q_heads / p->num_kv_heads;
   // the vector-ALU scan covers integer rates only
-  if ((p->flags & TQ_FLAG_VALU_SCAN) && (p->key_mixed || p->value_mixed)) return false;
+  if ((p->flags & TQ_FLAG_VALU_SCAN) && (p->key_mixed || p->value_mixed || p->key_norm_u8)) return false;
   return p->head_dim == tq::kD && (G == 1 || G == 2 || G == 4 || G == 8) && p->num_kv_heads <= 65535;
 }
 
@@ -212,7 +214,16 @@ TQ_API int tq_codebook_init(tq_ctx** out, const tq_params* p, const double* rot_
     cbtab[96 + k] = c->cb.vc2[k];
     cbtab[112 + k] = c->cb.vb2[k];
   }
-  const size_t total = 6 * mat + sizeof(cbtab) + 256;
+  // u8 log-norm: levels 2^(q/16 - 4) (level 0 = 0) and the boundaries
+  // between levels q and q + 1 (entry 0: 0, entry 255: +inf), in float32
+  float ntab[2 * tq::kNormCodes];
+  for (int q = 0; q < tq::kNormCodes; ++q) {
+    ntab[q] = q == 0 ? 0.0f : static_cast<float>(std::exp2(q / 16.0 - 4.0));
+    ntab[tq::kNormCodes + q] = q == 0 ? 0.0f
+                               : q == tq::kNormCodes - 1 ? std::numeric_limits<float>::infinity()
+                                                         : static_cast<float>(std::exp2((q + 0.5) / 16.0 - 4.0));
+  }
+  const size_t total = 6 * mat + sizeof(cbtab) + sizeof(ntab) + 256;
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (hipGetDevice(&c->device) != hipSuccess || hipMalloc(&c->dmem, total) != hipSuccess) {
     delete c;
@@ -226,7 +237,8 @@ TQ_API int tq_codebook_init(tq_ctx** out, const tq_params* p, const double* rot_
   c->t.rot4 = reinterpret_cast<float*>(base + 4 * mat);
   c->t.S4 = reinterpret_cast<float*>(base + 5 * mat);
   c->t.cbtab = reinterpret_cast<float*>(base + 6 * mat);
-  c->t.status = reinterpret_cast<int*>(base + 6 * mat + sizeof(cbtab));
+  c->t.ntab = reinterpret_cast<float*>(base + 6 * mat + sizeof(cbtab));
+  c->t.status = reinterpret_cast<int*>(base + 6 * mat + sizeof(cbtab) + sizeof(ntab));
   bool ok = hipMemcpyAsync(base, rot.data(), mat, hipMemcpyHostToDevice, s) == hipSuccess &&
             hipMemcpyAsync(base + mat, rotT.data(), mat, hipMemcpyHostToDevice, s) == hipSuccess &&
             hipMemcpyAsync(base + 2 * mat, S.data(), mat, hipMemcpyHostToDevice, s) == hipSuccess &&
@@ -234,7 +246,8 @@ TQ_API int tq_codebook_init(tq_ctx** out, const tq_params* p, const double* rot_
             hipMemcpyAsync(base + 4 * mat, rot4.data(), mat, hipMemcpyHostToDevice, s) == hipSuccess &&
             hipMemcpyAsync(base + 5 * mat, S4.data(), mat, hipMemcpyHostToDevice, s) == hipSuccess &&
             hipMemcpyAsync(base + 6 * mat, cbtab, sizeof(cbtab), hipMemcpyHostToDevice, s) == hipSuccess &&
-            hipMemsetAsync(base + 6 * mat + sizeof(cbtab), 0, 256, s) == hipSuccess &&
+            hipMemcpyAsync(base + 6 * mat + sizeof(cbtab), ntab, sizeof(ntab), hipMemcpyHostToDevice, s) == hipSuccess &&
+            hipMemsetAsync(base + 6 * mat + sizeof(cbtab) + sizeof(ntab), 0, 256, s) == hipSuccess &&
             hipStreamSynchronize(s) == hipSuccess;
   // resident scan work-groups per device, for the automatic split count
   const bool valu = (p->flags & TQ_FLAG_VALU_SCAN) != 0;

@@ -16,6 +16,20 @@ constexpr int kVGroup = 32;       // value codes are interleaved in 32-token gro
 constexpr uint32_t kMagic = 0x564B5154u;  // "TQKV"
 constexpr int kMaxWindow = 1024;
 constexpr int kMaxPage = 1024;
+constexpr int kNormCodes = 256;   // u8 log-norm codes
+
+// u8 log-norm code of a float32 norm n >= 0 against the boundary table nb
+// (nb[q]: between levels q and q + 1; nb[255] = +inf): 0 for n = 0, else the
+// level nearest in log2.  A first guess from log2 (off by at most one near a
+// boundary) is settled by comparing n with the two boundaries around it.
+__host__ __device__ inline int norm_code(float n, const float* nb) {
+  if (!(n > 0.0f)) return 0;
+  int q = static_cast<int>(floorf(16.0f * (log2f(n) + 4.0f) + 0.5f));
+  q = q < 1 ? 1 : (q > kNormCodes - 1 ? kNormCodes - 1 : q);
+  if (n > nb[q]) ++q;
+  else if (q > 1 && !(n > nb[q - 1])) --q;
+  return q;
+}
 
 // Host table builders (tables.cpp).
 std::vector<double> lloyd_max_normal(int bits);
@@ -26,6 +40,7 @@ void haar_rotation_f32(const double* g, int d, float* out);
 // kmix / vmix: mixed-channel rate b + 1/2 (half the coordinates at b + 1 bits).
 struct Layout {
   int P, bK, bV, qjl, H, d, kmix, vmix;
+  int kn8;           // key norms as u8 log-norm codes
   int k_rec, v_rec;  // code bytes of one key record / one token's value codes
   int64_t k_norm, k_rnorm, k_codes, k_signs, v_norm, v_codes;
   int64_t head_bytes, page_bytes;
@@ -52,11 +67,12 @@ inline Layout make_layout(const tq_params& p) {
   l.d = p.head_dim;
   l.kmix = p.key_mixed ? 1 : 0;
   l.vmix = p.value_mixed ? 1 : 0;
+  l.kn8 = p.key_norm_u8 ? 1 : 0;
   l.k_rec = l.d * l.bK / 8 + (l.kmix ? l.d / 16 : 0);
   l.v_rec = l.d * l.bV / 8 + (l.vmix ? l.d / 16 : 0);
   int64_t off = 0;
   l.k_norm = off;
-  off += 4LL * l.P;
+  off += (l.kn8 ? 1LL : 4LL) * l.P;
   l.k_rnorm = off;
   if (l.qjl) off += 4LL * l.P;
   l.k_codes = off;
@@ -81,6 +97,7 @@ struct DevTables {
   const float* rot4;   // DENSE: Pi interleaved by 4 columns: float4 (j4, i) = Pi[i][4 j4 .. 4 j4 + 3]
   const float* S4;     // S interleaved the same way
   const float* cbtab;  // [keys, values][64]: centroids[16], boundaries[16], then the (b+1)-bit pair of a mixed rate
+  const float* ntab;   // u8 log-norm: levels[kNormCodes], then boundaries[kNormCodes] (entry q: between q and q+1)
   int* status;         // status word (TQ_STATUS_* bits)
 };
 

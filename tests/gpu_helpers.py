@@ -27,7 +27,8 @@ def params_for(setup, flags=0):
         rotation=tqa.TQ_ROT_DENSE if setup.rotation == "dense" else tqa.TQ_ROT_HADAMARD,
         num_q_heads=setup.Hq, num_kv_heads=setup.Hkv, page_tokens=setup.P, window=setup.W, seed=setup.seed,
         qjl_kind=tqa.TQ_QJL_ORTHOGONAL if setup.qjl_kind == "orthogonal" else tqa.TQ_QJL_GAUSSIAN,
-        qjl_shrink=setup.qjl_shrink, key_mixed=int(setup.kmix), value_mixed=int(setup.vmix))
+        qjl_shrink=setup.qjl_shrink, key_mixed=int(setup.kmix), value_mixed=int(setup.vmix),
+        key_norm_u8=int(getattr(setup, "kn8", False)))
 
 
 def context_for(setup, flags=0):

@@ -56,7 +56,7 @@ def test_target_page_size(L):
     ("key_bits", 1), ("key_bits", 5), ("value_bits", 0), ("key_qjl", 2), ("rotation", 7),
     ("num_q_heads", 6), ("num_kv_heads", 0), ("page_tokens", 48), ("page_tokens", 2048), ("window", -1),
     ("head_dim", 0), ("qjl_kind", 2), ("qjl_shrink", 0.0), ("qjl_shrink", 5.0), ("qjl_shrink", float("nan")),
-    ("key_mixed", 2), ("value_mixed", -1),
+    ("key_mixed", 2), ("value_mixed", -1), ("key_norm_u8", 2), ("key_norm_u8", -1),
 ])
 def test_bad_params_rejected(L, field, value):
     p = tqa.make_params(num_q_heads=8, num_kv_heads=4)
@@ -158,6 +158,27 @@ def test_mixed_page_bytes_match_layout(L, kb, kmix, vb, vmix, H, P):
     p = tqa.make_params(key_bits=kb, key_mixed=kmix, value_bits=vb, value_mixed=vmix, num_q_heads=H,
                         num_kv_heads=H, page_tokens=P)
     assert tqa.tq_page_bytes(p) == pages.Layout(128, kb, 1, vb, H, P, kmix, vmix).page_bytes
+
+
+def test_u8_norm_unsupported_on_valu_scan(L):
+    """The vector-ALU scan reads float32 key norms only: rejected at init."""
+    p = tqa.make_params(key_norm_u8=1, flags=tqa.TQ_FLAG_VALU_SCAN)
+    out = ctypes.c_void_p()
+    d = np.zeros(128 * 128)
+    assert L.tq_codebook_init(ctypes.byref(out), ctypes.byref(p), d.ctypes.data, d.ctypes.data, None) == \
+        tqa.TQ_ERR_UNSUPPORTED
+
+
+@pytest.mark.parametrize("kb,kmix,vb,H,P", [(3, 0, 4, 8, 256), (3, 1, 3, 8, 256), (2, 1, 2, 2, 32)])
+def test_u8_norm_page_bytes_match_layout(L, kb, kmix, vb, H, P):
+    """u8 log-norm key norms: P bytes per head instead of 4P."""
+    p = tqa.make_params(key_bits=kb, key_mixed=kmix, value_bits=vb, num_q_heads=H, num_kv_heads=H, page_tokens=P,
+                        key_norm_u8=1)
+    lay = pages.Layout(128, kb, 1, vb, H, P, kmix, False, key_norm_u8=True)
+    assert tqa.tq_page_bytes(p) == lay.page_bytes
+    p0 = tqa.make_params(key_bits=kb, key_mixed=kmix, value_bits=vb, num_q_heads=H, num_kv_heads=H, page_tokens=P)
+    assert pages.Layout(128, kb, 1, vb, H, P, kmix, False).head_bytes - lay.head_bytes == 3 * P
+    assert tqa.tq_page_bytes(p0) >= tqa.tq_page_bytes(p)
 
 
 @pytest.mark.parametrize("bits", [2, 3])

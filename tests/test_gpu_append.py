@@ -82,6 +82,10 @@ CASES = [
                                    rotation="hadamard"), [100, 47]),
     ("mixed_k3_v25_noqjl", dict(Hq=2, Hkv=2, key_bits=3, key_qjl=0, value_bits=2, value_mixed=True, W=0, P=32),
      [77, 16]),
+    # u8 log-norm key norms
+    ("u8norm_k35_v3", dict(Hq=4, Hkv=2, W=32, P=64, key_bits=3, key_mixed=True, value_bits=3, key_norm_u8=True),
+     [200, 33]),
+    ("u8norm_k3_v4_hadamard", dict(Hq=8, Hkv=2, W=16, P=32, rotation="hadamard", key_norm_u8=True), [100, 47]),
 ]
 
 
@@ -111,11 +115,13 @@ def test_bulk_prefill_parity(name, kw, lens):
                 assert rel_close(out[b, hq], ref_o[b, hq]), (b, hq)
 
 
+@pytest.mark.parametrize("kn8", [False, True])
 @pytest.mark.parametrize("late_step", [5, 20, 30])
-def test_streaming_appends_match_bulk(late_step):
+def test_streaming_appends_match_bulk(late_step, kn8):
     """Chunked appends (1 token, then late_step tokens: up to and beyond the
     window, evictions spanning two 32-token groups) equal one bulk append."""
-    s = Setup(Hq=4, Hkv=2, W=24, P=32)
+    print(f"case streaming late_step={late_step} u8 key norms={kn8}", flush=True)
+    s = Setup(Hq=4, Hkv=2, W=24, P=32, key_norm_u8=kn8)
     lens = [90, 30]
     ref = s.cache(2, 90)
     k, v = fill(s, ref, lens)

@@ -56,6 +56,13 @@ MIXED = [
      [95, 32, 31]),
     ("mixed_k3_v25_gqa8_orthoS", dict(Hq=16, Hkv=2, key_bits=3, value_bits=2, value_mixed=True, W=32,
                                       qjl_kind="orthogonal", qjl_shrink=2 / np.pi), [500, 33]),
+    # u8 log-norm key norms (the design study's recommended first mode: keys 3.5 + u8 log-norm, values 3)
+    ("u8norm_k35_v3_gqa4", dict(Hq=8, Hkv=2, key_bits=3, key_mixed=True, value_bits=3, W=64, key_norm_u8=True),
+     [700, 129, 1]),
+    ("u8norm_k3_v4_noqjl_gqa1", dict(Hq=2, Hkv=2, key_bits=3, key_qjl=0, value_bits=4, W=16, P=64,
+                                     key_norm_u8=True), [300, 64]),
+    ("u8norm_k2_v2_hadamard_gqa8", dict(Hq=16, Hkv=2, key_bits=2, value_bits=2, rotation="hadamard", W=32,
+                                        key_norm_u8=True), [400, 33]),
 ]
 
 

@@ -120,3 +120,33 @@ def test_encode_parity_mixed(rotation, bK, kmix, bV, vmix, n):
     assert vcodes.shape[1] == s.vcb.record_bytes(128)
     assert np.array_equal(vnorms, vref.norms)
     check_codes(x, s.vcb.unpack(vcodes, 128), vref.idx, s.R, s.vcb)
+
+
+@pytest.mark.parametrize("rotation", ["dense", "hadamard"])
+@pytest.mark.parametrize("bK,kmix,qjl", [(3, 0, True), (3, 1, True), (4, 0, False)])
+@pytest.mark.parametrize("dtype", [torch.float16, torch.float32])
+def test_encode_parity_u8_key_norm(rotation, bK, kmix, qjl, dtype):
+    """u8 log-norm key norms: the record's norm is the level of the oracle's
+    code (exactly, as float32), codes and signs under the guard-band rule with
+    the residual against that level; values keep float32 norms."""
+    print(f"case u8 key norm rotation={rotation} bK={bK}{'+' if kmix else ''} qjl={qjl} {dtype}", flush=True)
+    s = Setup(key_bits=bK, key_qjl=int(qjl), value_bits=3, rotation=rotation, key_mixed=bool(kmix),
+              key_norm_u8=True)
+    ctx = context_for(s)
+    x16 = _inputs(700, seed=4)
+    x16[11] = 0
+    x = x16.astype(np.float64)
+    codes, norms, signs, rnorms = _gpu_encode(ctx, tqa.TQ_KIND_KEY, x16, qjl, dtype)
+    ref = codec.encode(x, s.R, s.kcb, s.S if qjl else None, norm_u8=True)
+    assert np.array_equal(norms, ref.norms)
+    assert norms[11] == 0
+    gidx = s.kcb.unpack(codes, 128)
+    nband = check_codes(x, gidx, ref.idx, s.R, s.kcb)
+    assert nband <= 0.002 * x.size
+    if qjl:
+        check_signs(x, gidx, norms, signs, s.R, s.kcb, s.S)
+        r = codec.residual_from_codes(x, s.R, s.kcb, norms, gidx)
+        assert np.allclose(rnorms, np.linalg.norm(r, axis=1), rtol=1e-5, atol=1e-30)
+    vcodes, vnorms, _, _ = _gpu_encode(ctx, tqa.TQ_KIND_VALUE, x16, False, dtype)
+    vref = codec.encode(x, s.R, s.vcb)
+    assert np.array_equal(vnorms, vref.norms)
