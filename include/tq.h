@@ -176,7 +176,8 @@ TQ_API int tq_decode(const tq_ctx* ctx, int kind, const uint8_t* codes, const ui
  *   x: [n][row_stride] elements of dtype (F16, BF16 or F32), first d used;
  *   codes: [n][d*b/8] u8 LSB-first, b = key_bits or value_bits by kind
  *   ([n][d*b/8 + d/16] for a mixed-channel rate, layout as in the page);
- *   norms: [n] f32 L2 norms;
+ *   norms: [n] f32 L2 norms (keys with key_norm_u8: the u8 log-norm level each norm is
+ *   stored as, 2^(q/16 - 4) or 0, against which the key's QJL residual is taken);
  *   signs: [n][d/8] u8 and rnorms: [n] f32, required iff kind == KEY and key_qjl.
  * A vector with zero norm gets all-zero codes, signs and rnorm. */
 TQ_API int tq_encode(const tq_ctx* ctx, int kind, const void* x, int dtype, int64_t n, int64_t row_stride,
