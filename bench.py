@@ -14,7 +14,9 @@ Prints one JSON line: tokens/s (sum of context lengths attended per second),
 the step time, the scan kernel's roofline (algorithmic bytes per launch /
 its HIP-event time vs the 8 TB/s HBM peak, and vs the device's measured
 streaming-read rate) and a CPU baseline (the float64 oracle on a bounded
-sample of the same workload).
+sample of the same workload).  The scan's HIP events are recorded over a
+second run of as many steps right after the timed ones: each event record
+adds a few microseconds of queue time, which the timed steps do not carry.
 """
 
 import argparse
@@ -163,8 +165,12 @@ def main():
     B, Hq, Hkv, d, P, W = args.batch, 32, 8, 128, 256, 128
     G = Hq // Hkv
     Tf = args.T
-    nsteps = args.warmup + args.steps
-    T0 = Tf - nsteps
+    # warm-up steps, then the timed steps (the last at T = Tf), then as many
+    # steps again with HIP events around each scan launch (the roofline's
+    # kernel time; each event record adds queue time, so they are not timed)
+    nsteps = args.warmup + 2 * args.steps
+    T0 = Tf - args.warmup - args.steps
+    Tend = T0 + nsteps
     kbits, vbits, kmix, vmix = args.key_bits, args.value_bits, int(args.key_mixed), int(args.value_mixed)
     kn8 = int(args.key_norm_u8)
     params = tqa.make_params(key_bits=kbits, key_qjl=1, value_bits=vbits, rotation=tqa.TQ_ROT_DENSE, num_q_heads=Hq,
@@ -173,7 +179,7 @@ def main():
                              key_norm_u8=kn8)
     ctx = tqa.Context(params, tq_inputs.rotation_draws(0, d), tq_inputs.qjl_draws(0, d))
     pb = tqa.tq_page_bytes(params)
-    max_pages = -(-(Tf - W) // P)
+    max_pages = -(-(Tend - W) // P)
     npages = B * max_pages
     pool = torch.zeros(npages * pb, dtype=torch.uint8, device=dev)
     # pages of a sequence are scattered over the pool
@@ -182,7 +188,7 @@ def main():
     seq_lens = torch.zeros(B, dtype=torch.int32, device=dev)
     k_win = torch.zeros((B, Hkv, W, d), dtype=torch.float16, device=dev)
     v_win = torch.zeros_like(k_win)
-    k_all, v_all = tq_inputs.torch_kv(0, B, Hkv, Tf, d, dev)
+    k_all, v_all = tq_inputs.torch_kv(0, B, Hkv, Tend, d, dev)
     kpre = k_all[:, :, :T0].contiguous()
     vpre = v_all[:, :, :T0].contiguous()
     tqa.tq_append_page(ctx, pool, block_table, seq_lens, kpre, vpre, k_win, v_win, num_pages=npages)
@@ -204,23 +210,32 @@ def main():
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
-    tqa.tq_profile_begin(ctx, args.steps)
+    # timed region: the steps as a caller runs them
     t0 = time.perf_counter()
-    for i in range(args.warmup, nsteps):
+    for i in range(args.warmup, args.warmup + args.steps):
         step(i)
     torch.cuda.synchronize()
     el = time.perf_counter() - t0
+    # the scan kernel's time: HIP events recorded by the library on the launch
+    # stream around each scan launch of the next steps
+    tqa.tq_profile_begin(ctx, args.steps)
+    t1 = time.perf_counter()
+    for i in range(args.warmup + args.steps, nsteps):
+        step(i)
+    torch.cuda.synchronize()
+    el_prof = time.perf_counter() - t1
     scan_ms, ncalls = tqa.tq_profile_end(ctx)
     status = tqa.tq_get_status(ctx)
     if status != 0 or not torch.isfinite(out).all():
         raise SystemExit(f"bench: bad status {status} or non-finite output")
     # tokens attended in the timed steps: after step i the length is T0 + i + 1
-    lens = [T0 + i + 1 for i in range(args.warmup, nsteps)]
+    lens = [T0 + i + 1 for i in range(args.warmup, args.warmup + args.steps)]
+    lens_prof = [T0 + i + 1 for i in range(args.warmup + args.steps, nsteps)]
     tokens = B * sum(lens)
     # key codes + signs + norm + rnorm, value codes + norm (a mixed rate adds d/16 code bytes)
     # (a u8 log-norm key norm takes 1 byte instead of 4)
     per_tok_head = (16 * kbits + 8 * kmix + 16 + 4 + (1 if kn8 else 4)) + (16 * vbits + 8 * vmix + 4)
-    comp_bytes = [B * Hkv * (T - W) * per_tok_head for T in lens]
+    comp_bytes = [B * Hkv * (T - W) * per_tok_head for T in lens_prof]
     win_bytes = B * Hkv * W * d * 2 * 2
     scan_s = scan_ms / 1e3 / max(ncalls, 1)
     achieved = (sum(comp_bytes) / len(comp_bytes)) / scan_s / 1e9
@@ -234,8 +249,10 @@ def main():
                                f"{kbits + 0.5 * kmix:g}-bit+QJL{' with u8 log-norms' if kn8 else ''}, values "
                                f"{vbits + 0.5 * vmix:g}-bit, dense rotation, bf16 queries",
                    "batch": B, "seq_len": Tf, "parallelism": "none (1 GPU)"},
-        "hbm_gbps_step": (sum(comp_bytes) / len(comp_bytes) + win_bytes) / (ms_step / 1e3) / 1e9,
+        "hbm_gbps_step": (sum(B * Hkv * (T - W) * per_tok_head for T in lens) / len(lens) + win_bytes)
+                         / (ms_step / 1e3) / 1e9,
         "scan_us": scan_s * 1e6,
+        "ms_per_step_with_scan_events": el_prof / args.steps * 1e3,
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBPS,
                      # the committed counter record covers the default formats only

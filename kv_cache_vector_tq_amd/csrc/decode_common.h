@@ -43,6 +43,7 @@ inline KParams make_kparams(const tq_ctx* c) {
 constexpr int kScanThreads = 256;
 
 // MFMA-based compressed-page scan (decode_mfma.hip).
-int launch_scan_mfma(const tq_ctx* c, const DecodeArgs& a, const KParams& k, void* stream);
+// ev0 / ev1 (may be null): HIP events updated with the scan kernel's own start and stop times
+int launch_scan_mfma(const tq_ctx* c, const DecodeArgs& a, const KParams& k, void* stream, void* ev0, void* ev1);
 
 }  // namespace tq

@@ -19,6 +19,8 @@
 // Each wave streams 32-token chunks (one value group) with its own online
 // softmax state; the waves of a work-group (four, or eight with the wide
 // table below) merge at the end.
+#include <hip/hip_ext.h>
+
 #include "decode_common.h"
 #include "device_common.h"
 
@@ -741,7 +743,7 @@ int scan_mfma_threads(const tq_ctx* c) {
   return scan_threads(wide_scan(c->p.num_q_heads / c->p.num_kv_heads, c->p.value_bits, c->p.value_mixed != 0));
 }
 
-int launch_scan_mfma(const tq_ctx* c, const DecodeArgs& a, const KParams& k, void* stream) {
+int launch_scan_mfma(const tq_ctx* c, const DecodeArgs& a, const KParams& k, void* stream, void* ev0, void* ev1) {
   const void* f = scan_mfma_kernel_ptr(c);
   if (!f) return 1;
   DecodeArgs aa = a;
@@ -750,7 +752,8 @@ int launch_scan_mfma(const tq_ctx* c, const DecodeArgs& a, const KParams& k, voi
   KParams kk = k;
   void* args[] = {&aa, &tt, &cc, &kk};
   const dim3 grid(a.splits, k.Hkv, a.batch);
-  return hipLaunchKernel(f, grid, dim3(scan_mfma_threads(c)), args, 0, static_cast<hipStream_t>(stream)) == hipSuccess
+  return hipExtLaunchKernel(f, grid, dim3(scan_mfma_threads(c)), args, 0, static_cast<hipStream_t>(stream),
+                            static_cast<hipEvent_t>(ev0), static_cast<hipEvent_t>(ev1), 0) == hipSuccess
              ? 0
              : 1;
 }

@@ -767,11 +767,36 @@ __global__ __launch_bounds__(kThreads) void append_ring_kernel(AppendArgs a, Dev
 __global__ void append_commit_kernel(AppendArgs a, DevTables t, Layout L, int W, int rotation, int qjl_code,
                                      uint64_t seed) {
   for (int b = blockIdx.x * blockDim.x + threadIdx.x; b < a.batch; b += gridDim.x * blockDim.x) {
-    const SeqPlan sp = plan_seq(a, L, W, b, t.status, true);
-    if (!sp.ok) continue;
+    // the plan as plan_seq takes it, with its loads issued together: both
+    // per-sequence words, then the ids of the first two pages (a decode step
+    // touches one page, at most two)
+    SeqPlan sp;
+    sp.T0 = a.seq_lens[b];
+    const int craw = (a.counts ? a.counts : a.seq_lens)[b];
+    sp.cnt = a.counts ? craw : a.n_new;
+    if (sp.cnt < 0 || sp.cnt > a.n_new || sp.T0 < 0) {
+      atomicOr(t.status, TQ_STATUS_BAD_COUNT);
+      continue;
+    }
+    const int T1 = sp.T0 + sp.cnt;
+    sp.c0 = sp.T0 - W > 0 ? sp.T0 - W : 0;
+    sp.c1 = T1 - W > 0 ? T1 - W : 0;
+    const int pg0 = sp.c0 / L.P, pg1 = sp.c1 > sp.c0 ? (sp.c1 - 1) / L.P : pg0 - 1;
+    const int32_t* bt = a.block_table + static_cast<int64_t>(b) * a.max_pages;
+    const int pa = pg0 < a.max_pages ? bt[pg0] : -1;
+    const int pb = pg0 + 1 < a.max_pages ? bt[pg0 + 1] : -1;
+    bool ok = sp.c1 <= sp.c0 || pg1 < a.max_pages;
+    for (int pg = pg0; ok && pg <= pg1; ++pg) {
+      const int pid = pg == pg0 ? pa : pg == pg0 + 1 ? pb : bt[pg];
+      if (pid < 0 || pid >= a.num_pages) ok = false;
+    }
+    if (!ok) {
+      atomicOr(t.status, TQ_STATUS_BAD_PAGE);
+      continue;
+    }
     if (sp.c1 > sp.c0) {
-      for (int pg = sp.c0 / L.P; pg <= (sp.c1 - 1) / L.P; ++pg) {
-        const int pid = a.block_table[static_cast<int64_t>(b) * a.max_pages + pg];
+      for (int pg = pg0; pg <= pg1; ++pg) {
+        const int pid = pg == pg0 ? pa : pg == pg0 + 1 ? pb : bt[pg];
         uint32_t* hd = reinterpret_cast<uint32_t*>(a.pool + static_cast<int64_t>(pid) * L.page_bytes);
         const int valid = sp.c1 - pg * L.P < L.P ? sp.c1 - pg * L.P : L.P;
         hd[0] = kMagic;
