@@ -182,3 +182,43 @@ def test_garbage_beyond_live_tokens(kernel):
     out, dbg = run_decode(ctx, qt, dev, 1 / np.sqrt(128), logits_len=max(lens) + 1)
     _check(cache, q.astype(np.float32).astype(np.float64), out, dbg)
     assert tqa.tq_get_status(ctx) == 0
+
+
+@pytest.mark.parametrize("kernel", ["mfma", "valu"])
+def test_largest_page_and_window(kernel):
+    """The largest page (P = 1024 tokens) and FP16 window (W = 1024) the
+    library takes, with contexts shorter than, equal to and longer than the
+    window and spanning two pages."""
+    _decode_parity("P1024_W1024", dict(Hq=8, Hkv=2, P=1024, W=1024), [3100, 1024, 1025, 700], kernel)
+
+
+def test_zero_size_calls_are_no_ops():
+    """Empty batches, zero vectors and zero new tokens return OK and write nothing."""
+    s = Setup(Hq=4, Hkv=2, W=16, P=32)
+    ctx = context_for(s)
+    cache = s.cache(2, 100)
+    fill(s, cache, [100, 50])
+    dev = upload_cache(cache)
+    before = {k: v.clone() for k, v in dev.items() if isinstance(v, torch.Tensor)}
+    empty16 = torch.zeros((0, 128), dtype=torch.float16, device="cuda")
+    codes = torch.zeros((0, 48), dtype=torch.uint8, device="cuda")
+    norms = torch.zeros(0, dtype=torch.float32, device="cuda")
+    signs = torch.zeros((0, 16), dtype=torch.uint8, device="cuda")
+    tqa.tq_encode(ctx, tqa.TQ_KIND_KEY, empty16, codes, norms, signs, norms)
+    tqa.tq_decode(ctx, tqa.TQ_KIND_KEY, codes, norms, torch.zeros((0, 128), device="cuda"), signs, norms)
+    kn = torch.zeros((2, 2, 0, 128), dtype=torch.float16, device="cuda")
+    tqa.tq_append_page(ctx, dev["pool"], dev["block_table"], dev["seq_lens"], kn, kn.clone(), dev["k_win"],
+                       dev["v_win"], num_pages=dev["num_pages"])
+    kb0 = torch.zeros((0, 2, 1, 128), dtype=torch.float16, device="cuda")
+    tqa.tq_append_page(ctx, dev["pool"], dev["block_table"][:0], dev["seq_lens"][:0], kb0, kb0.clone(),
+                       dev["k_win"][:0], dev["v_win"][:0], num_pages=dev["num_pages"])
+    q0 = torch.zeros((0, 4, 128), dtype=torch.float32, device="cuda")
+    ws = torch.empty(max(tqa.tq_decode_workspace_bytes(ctx, 0, dev["block_table"].shape[1]), 1), dtype=torch.uint8,
+                     device="cuda")
+    tqa.tq_decode_attn(ctx, q0, dev["pool"], dev["block_table"][:0], dev["seq_lens"][:0], dev["k_win"][:0],
+                       dev["v_win"][:0], torch.zeros((0, 4, 128), device="cuda"), ws, 1 / np.sqrt(128),
+                       num_pages=dev["num_pages"])
+    torch.cuda.synchronize()
+    assert tqa.tq_get_status(ctx) == 0
+    for k, v in before.items():
+        assert torch.equal(dev[k], v), k
