@@ -253,7 +253,7 @@ scan_mfma_kernel(DecodeArgs a, DevTables t, Codebooks cb, KParams k) {
   constexpr int kKeyWords = (BK == BV || kKeyInVhi) ? 0 : PairLut<BK>::kWords;
   constexpr int kKeyHiWords = KMIX ? PairLut<BK + 1, 1>::kWords : 0;  // mixed keys: high-rate table, one copy
   constexpr int kValHiWords = VMIX ? PairLut<BV + 1>::kWords : 0;     // mixed values: high-rate table
-  __shared__ uint32_t luts[kKeyWords + kKeyHiWords + Sh::kLutWords + kValHiWords];
+  __shared__ __align__(16) uint32_t luts[kKeyWords + kKeyHiWords + Sh::kLutWords + kValHiWords];
   uint32_t* const lutKown = luts;
   uint32_t* const lutKhi = luts + kKeyWords;
   uint32_t* const lutV = luts + kKeyWords + kKeyHiWords;
@@ -269,10 +269,39 @@ scan_mfma_kernel(DecodeArgs a, DevTables t, Codebooks cb, KParams k) {
   // and buffer descriptors in scalar registers
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l = tid & 63, n = l & 15, kg = l >> 4;
+  // Loads that do not depend on the sequence length are issued first, so
+  // that they land while the length is read and the tables are built: the
+  // query operands (A operands of the key products: lane group kg covers
+  // coordinates 32kg .. 32kg+31, MFMA i the 8 starting at 32kg + 8i) and the
+  // split's page ids (64 per register, lane j: page pb + j, read with
+  // v_readlane; no scalar load, whose out-of-order return would make every
+  // later LDS wait a full drain).
+  const int64_t qrow = (static_cast<int64_t>(b) * k.Hq + static_cast<int64_t>(h) * G) * kD;
+  const int ag = 2 * (n >> 2) + (n & 1), apart = (n >> 1) & 1;
+  const uint32_t amask = apart ? 0xffffe000u : 0u;
+  const int agc = ag < G ? ag : 0;
+  float4 qin[4][2], pin[4][2];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float4* q4 = reinterpret_cast<const float4*>(a.qs + qrow + agc * kD + 32 * kg + 8 * i);
+    qin[i][0] = q4[0];
+    qin[i][1] = q4[1];
+    if constexpr (QJL) {
+      const float4* p4 = reinterpret_cast<const float4*>(a.ps + qrow + agc * kD + 32 * kg + 8 * i);
+      pin[i][0] = p4[0];
+      pin[i][1] = p4[1];
+    }
+  }
+  const int pb = split * a.pages_per_split;
+  auto load_pids = [&](int base) {
+    const int j = base + l;
+    return a.block_table[static_cast<int64_t>(b) * a.max_pages + (j < a.max_pages ? j : 0)];
+  };
+  int pbase = pb;
+  int pids = load_pids(pb);
   const int T = a.seq_lens[b];
   const int C = T - k.W > 0 ? T - k.W : 0;
   const int npages = (C + k.P - 1) / k.P;
-  const int pb = split * a.pages_per_split;
   int pe = npages < pb + a.pages_per_split ? npages : pb + a.pages_per_split;
   const int64_t pidx = ((static_cast<int64_t>(b) * k.Hkv + h) * a.splits + split) * G;
   if (pe > a.max_pages) {
@@ -305,16 +334,22 @@ scan_mfma_kernel(DecodeArgs a, DevTables t, Codebooks cb, KParams k) {
   }
   __syncthreads();
   if constexpr (kWide) {
-    for (int w = tid; w < Sh::kLutWords; w += kThreads) {
-      const int e = w >> 6, c = w & 63;
-      uint32_t v;
-      if (c < 32) {
-        v = h_bits(cvv[e & 15]) | (h_bits(cvv[e >> 4]) << 16);
-      } else {  // word j of sign byte e: bits 2j (low half) and 2j + 1
-        const int j = c & 3;
-        v = ((e >> (2 * j)) & 1 ? 0x3C00u : 0xBC00u) | (((e >> (2 * j + 1)) & 1 ? 0x3C00u : 0xBC00u) << 16);
+    // row e: words 0..31 the value pair of byte e (32 copies), words 32..63
+    // the four sign words of byte e (8 copies); written four words at a time
+    auto sgn_word = [](int e, int j) {  // word j of sign byte e: bits 2j (low half) and 2j + 1
+      return ((e >> (2 * j)) & 1 ? 0x3C00u : 0xBC00u) | (((e >> (2 * j + 1)) & 1 ? 0x3C00u : 0xBC00u) << 16);
+    };
+    u4* lut4 = reinterpret_cast<u4*>(lutV);
+    for (int w4 = tid; w4 < Sh::kLutWords / 4; w4 += kThreads) {
+      const int e = w4 >> 4;
+      u4 v;
+      if ((w4 & 15) < 8) {
+        const uint32_t x = h_bits(cvv[e & 15]) | (h_bits(cvv[e >> 4]) << 16);
+        v = u4{x, x, x, x};
+      } else {
+        v = u4{sgn_word(e, 0), sgn_word(e, 1), sgn_word(e, 2), sgn_word(e, 3)};
       }
-      lutV[w] = v;
+      lut4[w4] = v;
     }
   } else {
     build_pair_lut<BV, kThreads>(lutV, cvv, tid);
@@ -332,27 +367,23 @@ scan_mfma_kernel(DecodeArgs a, DevTables t, Codebooks cb, KParams k) {
   const uint32_t* lutVl = lutV + (PairLut<BV>::kCopies > 1 ? (tid & 31) : 0);
   const uint32_t* lutVhil = lutVhi + ((VMIX && PairLut<BV + 1>::kCopies > 1) ? (tid & 31) : 0);
   const uint32_t vbase = static_cast<uint32_t>(tid & 31) * 4u, sbase = 128u + static_cast<uint32_t>(tid & 7) * 16u;
-  // A operands of the key products: lane group kg covers coordinates
-  // 32kg .. 32kg+31, MFMA i the 8 starting at 32kg + 8i.
-  const int64_t qrow = (static_cast<int64_t>(b) * k.Hq + static_cast<int64_t>(h) * G) * kD;
-  const int ag = 2 * (n >> 2) + (n & 1), apart = (n >> 1) & 1;
-  const uint32_t amask = apart ? 0xffffe000u : 0u;
+  // the query operands, fp16 hi part or remainder per lane (zero for rows
+  // past the G queries)
   u4 aq[4], ap[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    aq[i] = u4{0u, 0u, 0u, 0u};
+    const float4 q0 = qin[i][0], q1 = qin[i][1];
+    aq[i] = u4{pack_part(q0.x, q0.y, apart), pack_part(q0.z, q0.w, apart), pack_part(q1.x, q1.y, apart),
+               pack_part(q1.z, q1.w, apart)};
     ap[i] = u4{0u, 0u, 0u, 0u};
-    if (ag < G) {
-      const float4* q4 = reinterpret_cast<const float4*>(a.qs + qrow + ag * kD + 32 * kg + 8 * i);
-      const float4 q0 = q4[0], q1 = q4[1];
-      aq[i] = u4{pack_part(q0.x, q0.y, apart), pack_part(q0.z, q0.w, apart), pack_part(q1.x, q1.y, apart),
-                 pack_part(q1.z, q1.w, apart)};
-      if constexpr (QJL) {
-        const float4* p4 = reinterpret_cast<const float4*>(a.ps + qrow + ag * kD + 32 * kg + 8 * i);
-        const float4 p0 = p4[0], p1 = p4[1];
-        ap[i] = u4{pack_part(p0.x, p0.y, apart), pack_part(p0.z, p0.w, apart), pack_part(p1.x, p1.y, apart),
-                   pack_part(p1.z, p1.w, apart)};
-      }
+    if constexpr (QJL) {
+      const float4 p0 = pin[i][0], p1 = pin[i][1];
+      ap[i] = u4{pack_part(p0.x, p0.y, apart), pack_part(p0.z, p0.w, apart), pack_part(p1.x, p1.y, apart),
+                 pack_part(p1.z, p1.w, apart)};
+    }
+    if (ag >= G) {
+      aq[i] = u4{0u, 0u, 0u, 0u};
+      ap[i] = u4{0u, 0u, 0u, 0u};
     }
   }
   __syncthreads();
@@ -397,15 +428,6 @@ scan_mfma_kernel(DecodeArgs a, DevTables t, Codebooks cb, KParams k) {
   const uint32_t o_vw = static_cast<uint32_t>((vw0 * kD + 8 * n) * 4);
   const uint32_t o_vw2 = static_cast<uint32_t>(((vtwo ? vw0 + 1 : vw0) * kD + 8 * n) * 4);
 
-  // page ids of this split held in one register, 64 at a time: lane j has
-  // the id of page pbase + j, read with v_readlane (no scalar load, whose
-  // out-of-order return would make every later LDS wait a full drain)
-  int pbase = pb;
-  auto load_pids = [&](int base) {
-    const int j = base + l;
-    return j < pe ? a.block_table[static_cast<int64_t>(b) * a.max_pages + j] : 0;
-  };
-  int pids = load_pids(pb);
   auto meta = [&](int i, Meta& m) {
     const int c = wave + i * kWaves;
     const int tok0 = c * kChunk;
@@ -660,23 +682,47 @@ scan_mfma_kernel(DecodeArgs a, DevTables t, Codebooks cb, KParams k) {
     for (int w = 0; w < kWaves; ++w) M = fmaxf(M, wm[w][g]);
     fac[i2] = (M == -INFINITY || wm[wave][g] == -INFINITY) ? 0.0f : exp2f(wm[wave][g] - M);
   }
-  for (int w = 0; w < kWaves; ++w) {
-    if (wave == w) {
+  constexpr bool kWaveSlots = sizeof(luts) >= sizeof(float) * kWaves * G * kD;
+  if constexpr (kWaveSlots) {
+    // every wave stores its scaled accumulators in a slot of its own (the
+    // tables are not read any more: all waves have passed the barrier above),
+    // then each element is summed over the waves in order 0 .. kWaves-1
+    float* slot = reinterpret_cast<float*>(luts);
 #pragma unroll
-      for (int i2 = 0; i2 < 2; ++i2) {
-        const int g = 2 * kg + i2;
-        if (g < G) {
+    for (int i2 = 0; i2 < 2; ++i2) {
+      const int g = 2 * kg + i2;
+      if (g < G) {
 #pragma unroll
-          for (int bl = 0; bl < 8; ++bl) {
-            const float v = (acc[bl][i2] + acc[bl][i2 + 2]) * fac[i2];
-            red[g][8 * n + bl] = (w == 0) ? v : red[g][8 * n + bl] + v;
-          }
-        }
+        for (int bl = 0; bl < 8; ++bl)
+          slot[(wave * G + g) * kD + 8 * n + bl] = (acc[bl][i2] + acc[bl][i2 + 2]) * fac[i2];
       }
     }
     __syncthreads();
+    for (int e = tid; e < G * kD; e += kThreads) {
+      float v = slot[e];
+#pragma unroll
+      for (int w = 1; w < kWaves; ++w) v += slot[w * G * kD + e];
+      a.pacc[pidx * kD + e] = v;
+    }
+  } else {
+    for (int w = 0; w < kWaves; ++w) {
+      if (wave == w) {
+#pragma unroll
+        for (int i2 = 0; i2 < 2; ++i2) {
+          const int g = 2 * kg + i2;
+          if (g < G) {
+#pragma unroll
+            for (int bl = 0; bl < 8; ++bl) {
+              const float v = (acc[bl][i2] + acc[bl][i2 + 2]) * fac[i2];
+              red[g][8 * n + bl] = (w == 0) ? v : red[g][8 * n + bl] + v;
+            }
+          }
+        }
+      }
+      __syncthreads();
+    }
+    for (int i2 = tid; i2 < G * kD; i2 += kThreads) a.pacc[pidx * kD + i2] = red[i2 / kD][i2 % kD];
   }
-  for (int i2 = tid; i2 < G * kD; i2 += kThreads) a.pacc[pidx * kD + i2] = red[i2 / kD][i2 % kD];
   if (tid < G) {
     float M = -INFINITY;
 #pragma unroll
