@@ -24,6 +24,7 @@ namespace {
 
 // ---------------------------------------------------------------- prep
 constexpr int kSmallThreads = 256;
+constexpr int kMergeGroups = 128;  // fewest merge work-groups before heads are spread out
 
 // y[g][i] = sum_j M[j*kD + i] x[g][j] for the G vectors x (LDS), M a kD x kD
 // row-major table in global memory.  Thread (c, r) owns columns 4c..4c+3 and
@@ -93,26 +94,29 @@ __device__ __forceinline__ void hadamard_lds(float (*x)[kD], const float* __rest
   lds_barrier();
 }
 
-// One work-group per (b, kv head) prepares its G query heads.
-template <int G>
+// One work-group per (b, kv head) prepares its G query heads (or GW of them,
+// when one per kv head would make too few work-groups).
+template <int GW>
 __global__ __launch_bounds__(kSmallThreads) void prep_kernel(DecodeArgs a, DevTables t, KParams k, int qjl) {
-  __shared__ float qv[G][kD], qr[G][kD], part[8][G][kD];
-  const int tid = threadIdx.x, h = blockIdx.x, b = blockIdx.y;
-  const int64_t row0 = (static_cast<int64_t>(b) * k.Hq + static_cast<int64_t>(h) * G) * kD;
+  __shared__ float qv[GW][kD], qr[GW][kD], part[8][GW][kD];
+  // work-group (kv head h, query heads g0 .. g0+GW-1 of its group of k.G)
+  const int nhs = k.G / GW;
+  const int tid = threadIdx.x, h = blockIdx.x / nhs, g0 = (blockIdx.x % nhs) * GW, b = blockIdx.y;
+  const int64_t row0 = (static_cast<int64_t>(b) * k.Hq + static_cast<int64_t>(h) * k.G + g0) * kD;
   const float c2 = a.sm_scale * kLog2e;
   // both tables, then the query: all in flight together (the query's loads
   // sit behind one branch on its dtype, whose join waits for every load issued)
   float4 mr[16], ms[16];
   if (k.rotation == TQ_ROT_DENSE) load_cols(t.rotT, mr);
   if (qjl) load_cols(t.ST, ms);
-  constexpr int kNq = (G * kD + kSmallThreads - 1) / kSmallThreads;
+  constexpr int kNq = (GW * kD + kSmallThreads - 1) / kSmallThreads;
   float qin[kNq];
   if (a.q_dtype == TQ_DTYPE_F32) {
     const float* q32 = static_cast<const float*>(a.q);
 #pragma unroll
     for (int u = 0; u < kNq; ++u) {
       const int e = tid + u * kSmallThreads;
-      qin[u] = e < G * kD ? q32[row0 + e] : 0.0f;
+      qin[u] = e < GW * kD ? q32[row0 + e] : 0.0f;
     }
   } else {
     const uint16_t* q16 = static_cast<const uint16_t*>(a.q);
@@ -120,34 +124,34 @@ __global__ __launch_bounds__(kSmallThreads) void prep_kernel(DecodeArgs a, DevTa
 #pragma unroll
     for (int u = 0; u < kNq; ++u) {
       const int e = tid + u * kSmallThreads;
-      raw[u] = e < G * kD ? q16[row0 + e] : 0;
+      raw[u] = e < GW * kD ? q16[row0 + e] : 0;
     }
 #pragma unroll
     for (int u = 0; u < kNq; ++u)
       qin[u] = a.q_dtype == TQ_DTYPE_F16 ? half_bits_to_float(raw[u]) : bf16_bits_to_float(raw[u]);
   }
 #pragma unroll
-  for (int u = 0; u * kSmallThreads < G * kD; ++u) {
+  for (int u = 0; u * kSmallThreads < GW * kD; ++u) {
     const int e = tid + u * kSmallThreads;
-    if (e < G * kD) {
+    if (e < GW * kD) {
       a.qwin[row0 + e] = qin[u] * c2;
       qv[e / kD][e % kD] = qin[u];
     }
   }
   lds_barrier();
   if (k.rotation == TQ_ROT_DENSE) {
-    matvec_cols<G>(mr, qv, part, qr);
+    matvec_cols<GW>(mr, qv, part, qr);
   } else {
-    hadamard_lds<G>(qv, t.rot, nullptr);
-    for (int e = tid; e < G * kD; e += kSmallThreads) qr[e / kD][e % kD] = qv[e / kD][e % kD];
+    hadamard_lds<GW>(qv, t.rot, nullptr);
+    for (int e = tid; e < GW * kD; e += kSmallThreads) qr[e / kD][e % kD] = qv[e / kD][e % kD];
     lds_barrier();
   }
-  for (int e = tid; e < G * kD; e += kSmallThreads) a.qs[row0 + e] = qr[e / kD][e % kD] * c2;
+  for (int e = tid; e < GW * kD; e += kSmallThreads) a.qs[row0 + e] = qr[e / kD][e % kD] * c2;
   if (!qjl) return;
-  matvec_cols<G>(ms, qr, part, qv);  // qv <- S q_rot
+  matvec_cols<GW>(ms, qr, part, qv);  // qv <- S q_rot
   const float sc = k.qjl_scale * c2;
   const int lane = tid & 63, w = tid >> 6;
-  for (int g = w; g < G; g += 4) {
+  for (int g = w; g < GW; g += 4) {
     float s2 = 0.0f;
     for (int i = lane; i < kD; i += 64) {
       const float ps = qv[g][i] * sc;
@@ -155,7 +159,7 @@ __global__ __launch_bounds__(kSmallThreads) void prep_kernel(DecodeArgs a, DevTa
       s2 += ps;
     }
     s2 = wave_sum(s2);
-    if (lane == 0) a.psum[static_cast<int64_t>(b) * k.Hq + h * G + g] = s2;
+    if (lane == 0) a.psum[static_cast<int64_t>(b) * k.Hq + h * k.G + g0 + g] = s2;
   }
 }
 
@@ -348,38 +352,41 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(DecodeArgs a, DevTab
 }
 
 // ---------------------------------------------------------------- merge
-// One work-group per (b, kv head) for its G query heads: the window K/V rows,
-// the split partials and Pi are each read once.  The kernel is a short chain
+// One work-group per (b, kv head) for its G query heads (or, when that makes
+// too few work-groups, for GW of them): the window K/V rows, the split
+// partials and Pi are each read once per work-group.  The kernel is a short chain
 // of dependent steps, so every load is issued at the start, the split
 // partials (needed first) ahead of the window keys and values of the first 128
 // slots and the columns of Pi, which land while the partials are combined.
-template <int G>
+template <int GW>
 __global__ __launch_bounds__(kSmallThreads) void merge_kernel(DecodeArgs a, DevTables t, KParams k) {
-  __shared__ float accr[G][kD], ow[G][kD], qw[G][kD], part[8][G][kD];
-  __shared__ float ls[G][kMaxWindow];
-  __shared__ float sM[G], sL[8][G], sM2[G], sLw[G];
+  __shared__ float accr[GW][kD], ow[GW][kD], qw[GW][kD], part[8][GW][kD];
+  __shared__ float ls[GW][kMaxWindow];
+  __shared__ float sM[GW], sL[8][GW], sM2[GW], sLw[GW];
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int c4 = (tid & 31) * 4, q8 = tid >> 5;
-  const int h = blockIdx.x, b = blockIdx.y;
+  // work-group (kv head h, heads g0 .. g0+GW-1 of its group of k.G)
+  const int nhs = k.G / GW;
+  const int h = blockIdx.x / nhs, g0 = (blockIdx.x % nhs) * GW, b = blockIdx.y;
   const int T = a.seq_lens[b];
   const int nwin = T < k.W ? T : k.W;
-  const int64_t row0 = (static_cast<int64_t>(b) * k.Hq + static_cast<int64_t>(h) * G) * kD;
+  const int64_t row0 = (static_cast<int64_t>(b) * k.Hq + static_cast<int64_t>(h) * k.G + g0) * kD;
   const int64_t bh = static_cast<int64_t>(b) * k.Hkv + h;
   const bool dense = k.rotation == TQ_ROT_DENSE;
 
   // ---- loads, in the order they are needed (loads complete in order: a
   // wait for the first ones does not wait for the rest)
-  // split partials: thread (c4, q8) takes query g = q8 % G; for the maximum
+  // split partials: thread (c4, q8) takes query g = q8 % GW; for the maximum
   // it reads (m, l) of the first 16 splits, for the sums the accumulators of
-  // its first 8 splits s = sub, sub + nsub, ... (sub = q8 / G)
-  constexpr int nsub = 8 / G;
-  const int g = q8 % G, sub = q8 / G;
+  // its first 8 splits s = sub, sub + nsub, ... (sub = q8 / GW)
+  constexpr int nsub = 8 / GW;
+  const int g = q8 % GW, sub = q8 / GW;
   // (loads are unconditional, from a clamped split index, and the result is
   // selected: a load under a branch would make its join wait for all loads)
   float lm[16], mm[16];
 #pragma unroll
   for (int u = 0; u < 16; ++u) {
-    const int64_t pi = (bh * a.splits + (u < a.splits ? u : 0)) * G + g;
+    const int64_t pi = (bh * a.splits + (u < a.splits ? u : 0)) * k.G + g0 + g;
     lm[u] = a.pl[pi];
     mm[u] = a.pm[pi];
   }
@@ -390,7 +397,7 @@ __global__ __launch_bounds__(kSmallThreads) void merge_kernel(DecodeArgs a, DevT
 #pragma unroll
   for (int u = 0; u < 8; ++u) {
     const int s = sub + u * nsub;
-    const int64_t pi = (bh * a.splits + (s < a.splits ? s : 0)) * G + g;
+    const int64_t pi = (bh * a.splits + (s < a.splits ? s : 0)) * k.G + g0 + g;
     va[u] = *reinterpret_cast<const float4*>(a.pacc + pi * kD + c4);
     la[u] = a.pl[pi];
     ma[u] = a.pm[pi];
@@ -418,12 +425,12 @@ __global__ __launch_bounds__(kSmallThreads) void merge_kernel(DecodeArgs a, DevT
     for (int r = 0; r < 16; ++r) rm[r] = *reinterpret_cast<const float4*>(t.rot + (q8 * 16 + r) * kD + c4);
   }
   // the window query, stored to LDS after the combine (a store now would wait for every load above)
-  constexpr int kNq = (G * kD + kSmallThreads - 1) / kSmallThreads;
+  constexpr int kNq = (GW * kD + kSmallThreads - 1) / kSmallThreads;
   float qwr[kNq];
 #pragma unroll
   for (int u = 0; u < kNq; ++u) {
     const int e = tid + u * kSmallThreads;
-    qwr[u] = a.qwin[row0 + (e < G * kD ? e : 0)];
+    qwr[u] = a.qwin[row0 + (e < GW * kD ? e : 0)];
   }
 
   // 1. combine the split partials in fixed order
@@ -436,7 +443,7 @@ __global__ __launch_bounds__(kSmallThreads) void merge_kernel(DecodeArgs a, DevT
       float lv[16], mv[16];
 #pragma unroll
       for (int u = 0; u < 16; ++u) {
-        const int64_t pi = (bh * a.splits + (s0 + u < a.splits ? s0 + u : s0)) * G + g;
+        const int64_t pi = (bh * a.splits + (s0 + u < a.splits ? s0 + u : s0)) * k.G + g0 + g;
         lv[u] = a.pl[pi];
         mv[u] = a.pm[pi];
       }
@@ -468,7 +475,7 @@ __global__ __launch_bounds__(kSmallThreads) void merge_kernel(DecodeArgs a, DevT
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
         const int s = s0 + u * nsub;
-        const int64_t pi = (bh * a.splits + (s < a.splits ? s : s0)) * G + g;
+        const int64_t pi = (bh * a.splits + (s < a.splits ? s : s0)) * k.G + g0 + g;
         v[u] = *reinterpret_cast<const float4*>(a.pacc + pi * kD + c4);
         lv[u] = a.pl[pi];
         mv[u] = a.pm[pi];
@@ -487,14 +494,14 @@ __global__ __launch_bounds__(kSmallThreads) void merge_kernel(DecodeArgs a, DevT
 #pragma unroll
   for (int u = 0; u < kNq; ++u) {
     const int e = tid + u * kSmallThreads;
-    if (e < G * kD) qw[e / kD][e % kD] = qwr[u];
+    if (e < GW * kD) qw[e / kD][e % kD] = qwr[u];
   }
   lds_barrier();
-  for (int e = tid; e < G * kD; e += kSmallThreads) {
+  for (int e = tid; e < GW * kD; e += kSmallThreads) {
     const int g = e / kD, i = e % kD;
     float v = part[0][g][i];
 #pragma unroll
-    for (int r = 1; r < 8 / G; ++r) v += part[r][g][i];
+    for (int r = 1; r < 8 / GW; ++r) v += part[r][g][i];
     accr[g][i] = v;
   }
 
@@ -507,9 +514,9 @@ __global__ __launch_bounds__(kSmallThreads) void merge_kernel(DecodeArgs a, DevT
 #pragma unroll
       for (int c = 0; c < 8; ++c) kv[c] = kr[c];
     }
-    float sg[G];
+    float sg[GW];
 #pragma unroll
-    for (int g = 0; g < G; ++g) sg[g] = 0.0f;
+    for (int g = 0; g < GW; ++g) sg[g] = 0.0f;
 #pragma unroll
     for (int c = 0; c < 8; ++c) {
       const uint32_t u4v[4] = {kv[c].x, kv[c].y, kv[c].z, kv[c].w};
@@ -519,24 +526,24 @@ __global__ __launch_bounds__(kSmallThreads) void merge_kernel(DecodeArgs a, DevT
         const float k0 = half_bits_to_float(static_cast<uint16_t>(u4v[e2] & 0xffffu));
         const float k1 = half_bits_to_float(static_cast<uint16_t>(u4v[e2] >> 16));
 #pragma unroll
-        for (int g = 0; g < G; ++g) sg[g] = fmaf(qw[g][i + 1], k1, fmaf(qw[g][i], k0, sg[g]));
+        for (int g = 0; g < GW; ++g) sg[g] = fmaf(qw[g][i + 1], k1, fmaf(qw[g][i], k0, sg[g]));
       }
     }
 #pragma unroll
-    for (int g = 0; g < G; ++g) sg[g] += __shfl_xor(sg[g], 1, 64);
+    for (int g = 0; g < GW; ++g) sg[g] += __shfl_xor(sg[g], 1, 64);
     if (half == 0) {
       // slot tk holds the largest position p < T with p = tk (mod W)
       const int pos = tk + k.W * ((T - 1 - tk) / k.W);
 #pragma unroll
-      for (int g = 0; g < G; ++g) {
+      for (int g = 0; g < GW; ++g) {
         ls[g][tk] = sg[g];
-        if (a.dbg_logits) a.dbg_logits[(static_cast<int64_t>(b) * k.Hq + h * G + g) * a.logits_stride + pos] = sg[g] * kLn2;
+        if (a.dbg_logits) a.dbg_logits[(static_cast<int64_t>(b) * k.Hq + h * k.G + g0 + g) * a.logits_stride + pos] = sg[g] * kLn2;
       }
     }
   }
   lds_barrier();
   // 3. per query head (one wave each): window max, weights, their sum
-  for (int g = wv; g < G; g += kSmallThreads / 64) {
+  for (int g = wv; g < GW; g += kSmallThreads / 64) {
     float m = sM[g];
     for (int tk = lane; tk < nwin; tk += 64) m = fmaxf(m, ls[g][tk]);
     m = wave_max(m);
@@ -555,16 +562,16 @@ __global__ __launch_bounds__(kSmallThreads) void merge_kernel(DecodeArgs a, DevT
   lds_barrier();
   // 4. weighted FP16 window values: thread (c4, q8) takes slots q8, q8+8, ...
   {
-    float4 acc[G];
+    float4 acc[GW];
 #pragma unroll
-    for (int g = 0; g < G; ++g) acc[g] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+    for (int g = 0; g < GW; ++g) acc[g] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
     auto add = [&](int tk, uint2 u) {
       const float v0 = half_bits_to_float(static_cast<uint16_t>(u.x & 0xffffu));
       const float v1 = half_bits_to_float(static_cast<uint16_t>(u.x >> 16));
       const float v2 = half_bits_to_float(static_cast<uint16_t>(u.y & 0xffffu));
       const float v3 = half_bits_to_float(static_cast<uint16_t>(u.y >> 16));
 #pragma unroll
-      for (int g = 0; g < G; ++g) {
+      for (int g = 0; g < GW; ++g) {
         const float w = ls[g][tk];
         acc[g].x = fmaf(w, v0, acc[g].x);
         acc[g].y = fmaf(w, v1, acc[g].y);
@@ -578,10 +585,10 @@ __global__ __launch_bounds__(kSmallThreads) void merge_kernel(DecodeArgs a, DevT
     for (int tk = q8 + 128; tk < nwin; tk += 8)
       add(tk, *reinterpret_cast<const uint2*>(vbase + static_cast<int64_t>(tk) * kD));
 #pragma unroll
-    for (int g = 0; g < G; ++g) *reinterpret_cast<float4*>(&part[q8][g][c4]) = acc[g];
+    for (int g = 0; g < GW; ++g) *reinterpret_cast<float4*>(&part[q8][g][c4]) = acc[g];
   }
   lds_barrier();
-  for (int e = tid; e < G * kD; e += kSmallThreads) {
+  for (int e = tid; e < GW * kD; e += kSmallThreads) {
     const int g = e / kD, i = e % kD;
     float v = part[0][g][i];
 #pragma unroll
@@ -593,7 +600,7 @@ __global__ __launch_bounds__(kSmallThreads) void merge_kernel(DecodeArgs a, DevT
   if (dense) {
     // o[g][j] = sum_i Pi[i][j] accr[g][i]; thread (c4, q8) sums rows 16 q8 ..
 #pragma unroll
-    for (int g = 0; g < G; ++g) {
+    for (int g = 0; g < GW; ++g) {
       float4 o = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
@@ -606,7 +613,7 @@ __global__ __launch_bounds__(kSmallThreads) void merge_kernel(DecodeArgs a, DevT
       *reinterpret_cast<float4*>(&part[q8][g][c4]) = o;
     }
     lds_barrier();
-    for (int e = tid; e < G * kD; e += kSmallThreads) {
+    for (int e = tid; e < GW * kD; e += kSmallThreads) {
       const int g = e / kD, i = e % kD;
       float v = part[0][g][i];
 #pragma unroll
@@ -615,14 +622,14 @@ __global__ __launch_bounds__(kSmallThreads) void merge_kernel(DecodeArgs a, DevT
     }
     lds_barrier();
   } else {
-    hadamard_lds<G>(accr, nullptr, t.rot);
+    hadamard_lds<GW>(accr, nullptr, t.rot);
   }
-  for (int e = tid; e < G * kD; e += kSmallThreads) {
+  for (int e = tid; e < GW * kD; e += kSmallThreads) {
     const int g = e / kD, i = e % kD;
     const float M = sM[g], M2 = sM2[g];
     const float corr = (M == -INFINITY) ? 0.0f : exp2f(M - M2);
     float L = 0.0f;
-    for (int r = 0; r < 8 / G; ++r) L += sL[r][g];
+    for (int r = 0; r < 8 / GW; ++r) L += sL[r][g];
     const float Ltot = fmaf(L, corr, sLw[g]);
     a.out[row0 + e] = Ltot > 0.0f ? fmaf(accr[g][i], corr, ow[g][i]) / Ltot : 0.0f;
   }
@@ -685,12 +692,17 @@ int launch_decode(const tq_ctx* c, const DecodeArgs& a, void* stream) {
   hipStream_t s = static_cast<hipStream_t>(stream);
   const KParams k = make_kparams(c);
   const int qjl = c->p.key_qjl;
-  const dim3 ghb(k.Hkv, a.batch);
-  switch (k.G) {
-    case 1: hipLaunchKernelGGL(prep_kernel<1>, ghb, dim3(kSmallThreads), 0, s, a, c->t, k, qjl); break;
-    case 2: hipLaunchKernelGGL(prep_kernel<2>, ghb, dim3(kSmallThreads), 0, s, a, c->t, k, qjl); break;
-    case 4: hipLaunchKernelGGL(prep_kernel<4>, ghb, dim3(kSmallThreads), 0, s, a, c->t, k, qjl); break;
-    case 8: hipLaunchKernelGGL(prep_kernel<8>, ghb, dim3(kSmallThreads), 0, s, a, c->t, k, qjl); break;
+  // prep and merge: one work-group per (sequence, kv head) for all G query
+  // heads, unless that leaves fewer than kMergeGroups work-groups; then the
+  // heads of a group are spread over more work-groups (GW heads each)
+  int GW = k.G;
+  while (GW > 1 && static_cast<long long>(a.batch) * k.Hkv * (k.G / GW) < kMergeGroups) GW /= 2;
+  const dim3 gm(k.Hkv * (k.G / GW), a.batch);
+  switch (GW) {
+    case 1: hipLaunchKernelGGL(prep_kernel<1>, gm, dim3(kSmallThreads), 0, s, a, c->t, k, qjl); break;
+    case 2: hipLaunchKernelGGL(prep_kernel<2>, gm, dim3(kSmallThreads), 0, s, a, c->t, k, qjl); break;
+    case 4: hipLaunchKernelGGL(prep_kernel<4>, gm, dim3(kSmallThreads), 0, s, a, c->t, k, qjl); break;
+    case 8: hipLaunchKernelGGL(prep_kernel<8>, gm, dim3(kSmallThreads), 0, s, a, c->t, k, qjl); break;
     default: return 1;
   }
   if (hipGetLastError() != hipSuccess) return 1;
@@ -701,11 +713,11 @@ int launch_decode(const tq_ctx* c, const DecodeArgs& a, void* stream) {
   const int rc = (c->p.flags & TQ_FLAG_VALU_SCAN) ? launch_scan_valu(c, a, k, s, ev0, ev1)
                                                   : launch_scan_mfma(c, a, k, stream, ev0, ev1);
   if (rc != 0) return 1;
-  switch (k.G) {
-    case 1: hipLaunchKernelGGL(merge_kernel<1>, ghb, dim3(kSmallThreads), 0, s, a, c->t, k); break;
-    case 2: hipLaunchKernelGGL(merge_kernel<2>, ghb, dim3(kSmallThreads), 0, s, a, c->t, k); break;
-    case 4: hipLaunchKernelGGL(merge_kernel<4>, ghb, dim3(kSmallThreads), 0, s, a, c->t, k); break;
-    case 8: hipLaunchKernelGGL(merge_kernel<8>, ghb, dim3(kSmallThreads), 0, s, a, c->t, k); break;
+  switch (GW) {
+    case 1: hipLaunchKernelGGL(merge_kernel<1>, gm, dim3(kSmallThreads), 0, s, a, c->t, k); break;
+    case 2: hipLaunchKernelGGL(merge_kernel<2>, gm, dim3(kSmallThreads), 0, s, a, c->t, k); break;
+    case 4: hipLaunchKernelGGL(merge_kernel<4>, gm, dim3(kSmallThreads), 0, s, a, c->t, k); break;
+    case 8: hipLaunchKernelGGL(merge_kernel<8>, gm, dim3(kSmallThreads), 0, s, a, c->t, k); break;
     default: return 1;
   }
   return hipGetLastError() == hipSuccess ? 0 : 1;
