@@ -119,6 +119,30 @@ def test_split_invariance_and_repeatability():
     assert np.array_equal(again, outs[2])
 
 
+def test_ragged_batch_split_invariance():
+    """One long sequence among short and empty ones (most work-groups of the
+    long sequence's splits, the short ones' splits mostly empty): parity with
+    the oracle at the automatic split, and with splits of 1 and 7 pages
+    within 1e-5."""
+    print("case ragged split invariance", flush=True)
+    s = Setup(Hq=8, Hkv=2, W=16, P=32)
+    lens = [4000] + [40] * 12 + [0, 17, 1]
+    cache = s.cache(len(lens), max(lens))
+    fill(s, cache, lens)
+    ctx = context_for(s)
+    dev = upload_cache(cache)
+    q = tq_inputs.queries(8, (len(lens), s.Hq, 128))
+    qt = torch.from_numpy(q.astype(np.float32)).cuda()
+    out, dbg = run_decode(ctx, qt, dev, 1 / np.sqrt(128), logits_len=max(lens) + 1)
+    _check(cache, q.astype(np.float32).astype(np.float64), out, dbg)
+    for pps in (1, 7):
+        o = run_decode(ctx, qt, dev, 1 / np.sqrt(128), pages_per_split=pps)[0]
+        assert np.max(np.abs(o - out)) <= 1e-5 * np.max(np.abs(out)), pps
+    again = run_decode(ctx, qt, dev, 1 / np.sqrt(128))[0]
+    assert np.array_equal(again, out)
+    assert tqa.tq_get_status(ctx) == 0
+
+
 def test_bad_page_sets_status():
     s = Setup(Hq=2, Hkv=1, W=16, P=32)
     cache = s.cache(1, 200)
