@@ -25,6 +25,7 @@ namespace {
 // ---------------------------------------------------------------- prep
 constexpr int kSmallThreads = 256;
 constexpr int kMergeGroups = 128;  // fewest merge work-groups before heads are spread out
+constexpr int kMergeMaxHeads = 4;  // most query heads per prep / merge work-group
 
 // y[g][i] = sum_j M[j*kD + i] x[g][j] for the G vectors x (LDS), M a kD x kD
 // row-major table in global memory.  Thread (c, r) owns columns 4c..4c+3 and
@@ -692,17 +693,18 @@ int launch_decode(const tq_ctx* c, const DecodeArgs& a, void* stream) {
   hipStream_t s = static_cast<hipStream_t>(stream);
   const KParams k = make_kparams(c);
   const int qjl = c->p.key_qjl;
-  // prep and merge: one work-group per (sequence, kv head) for all G query
-  // heads, unless that leaves fewer than kMergeGroups work-groups; then the
-  // heads of a group are spread over more work-groups (GW heads each)
-  int GW = k.G;
+  // prep and merge: one work-group per (sequence, kv head) for up to
+  // kMergeMaxHeads query heads (eight heads made one work-group's chain of
+  // window, combine and inverse rotation the longest step), and fewer when
+  // that leaves fewer than kMergeGroups work-groups: the heads of a group
+  // are spread over G / GW work-groups (GW heads each)
+  int GW = k.G < kMergeMaxHeads ? k.G : kMergeMaxHeads;
   while (GW > 1 && static_cast<long long>(a.batch) * k.Hkv * (k.G / GW) < kMergeGroups) GW /= 2;
   const dim3 gm(k.Hkv * (k.G / GW), a.batch);
   switch (GW) {
     case 1: hipLaunchKernelGGL(prep_kernel<1>, gm, dim3(kSmallThreads), 0, s, a, c->t, k, qjl); break;
     case 2: hipLaunchKernelGGL(prep_kernel<2>, gm, dim3(kSmallThreads), 0, s, a, c->t, k, qjl); break;
     case 4: hipLaunchKernelGGL(prep_kernel<4>, gm, dim3(kSmallThreads), 0, s, a, c->t, k, qjl); break;
-    case 8: hipLaunchKernelGGL(prep_kernel<8>, gm, dim3(kSmallThreads), 0, s, a, c->t, k, qjl); break;
     default: return 1;
   }
   if (hipGetLastError() != hipSuccess) return 1;
@@ -717,7 +719,6 @@ int launch_decode(const tq_ctx* c, const DecodeArgs& a, void* stream) {
     case 1: hipLaunchKernelGGL(merge_kernel<1>, gm, dim3(kSmallThreads), 0, s, a, c->t, k); break;
     case 2: hipLaunchKernelGGL(merge_kernel<2>, gm, dim3(kSmallThreads), 0, s, a, c->t, k); break;
     case 4: hipLaunchKernelGGL(merge_kernel<4>, gm, dim3(kSmallThreads), 0, s, a, c->t, k); break;
-    case 8: hipLaunchKernelGGL(merge_kernel<8>, gm, dim3(kSmallThreads), 0, s, a, c->t, k); break;
     default: return 1;
   }
   return hipGetLastError() == hipSuccess ? 0 : 1;
