@@ -363,7 +363,7 @@ template <int GW>
 __global__ __launch_bounds__(kSmallThreads) void merge_kernel(DecodeArgs a, DevTables t, KParams k) {
   __shared__ float accr[GW][kD], ow[GW][kD], qw[GW][kD], part[8][GW][kD];
   __shared__ float ls[GW][kMaxWindow];
-  __shared__ float sM[GW], sL[8][GW], sM2[GW], sLw[GW];
+  __shared__ float sM[GW], sL[8][GW], sM2[GW], sLw[GW], sMx[8][GW];
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int c4 = (tid & 31) * 4, q8 = tid >> 5;
   // work-group (kv head h, heads g0 .. g0+GW-1 of its group of k.G)
@@ -377,22 +377,14 @@ __global__ __launch_bounds__(kSmallThreads) void merge_kernel(DecodeArgs a, DevT
 
   // ---- loads, in the order they are needed (loads complete in order: a
   // wait for the first ones does not wait for the rest)
-  // split partials: thread (c4, q8) takes query g = q8 % GW; for the maximum
-  // it reads (m, l) of the first 16 splits, for the sums the accumulators of
-  // its first 8 splits s = sub, sub + nsub, ... (sub = q8 / GW)
+  // split partials: thread (c4, q8) takes query g = q8 % GW and reads the
+  // accumulators of its first 8 splits s = sub, sub + nsub, ... (sub =
+  // q8 / GW); together the nsub threads of a query cover the first 8 nsub
+  // splits, whose maximum they combine through LDS
   constexpr int nsub = 8 / GW;
   const int g = q8 % GW, sub = q8 / GW;
   // (loads are unconditional, from a clamped split index, and the result is
   // selected: a load under a branch would make its join wait for all loads)
-  float lm[16], mm[16];
-#pragma unroll
-  for (int u = 0; u < 16; ++u) {
-    const int64_t pi = (bh * a.splits + (u < a.splits ? u : 0)) * k.G + g0 + g;
-    lm[u] = a.pl[pi];
-    mm[u] = a.pm[pi];
-  }
-#pragma unroll
-  for (int u = 0; u < 16; ++u) lm[u] = u < a.splits ? lm[u] : 0.0f;
   float4 va[8];
   float la[8], ma[8];
 #pragma unroll
@@ -434,13 +426,15 @@ __global__ __launch_bounds__(kSmallThreads) void merge_kernel(DecodeArgs a, DevT
     qwr[u] = a.qwin[row0 + (e < GW * kD ? e : 0)];
   }
 
-  // 1. combine the split partials in fixed order
+  // 1. combine the split partials in fixed order; the maximum M over the
+  //    non-empty splits (l > 0) is exact in any order
   {
     float M = -INFINITY;
 #pragma unroll
-    for (int u = 0; u < 16; ++u)
-      if (lm[u] > 0.0f) M = fmaxf(M, mm[u]);
-    for (int s0 = 16; s0 < a.splits; s0 += 16) {
+    for (int u = 0; u < 8; ++u)
+      if (la[u] > 0.0f) M = fmaxf(M, ma[u]);
+    // splits past the first 8 nsub: every thread of the query reads them all
+    for (int s0 = 8 * nsub; s0 < a.splits; s0 += 16) {
       float lv[16], mv[16];
 #pragma unroll
       for (int u = 0; u < 16; ++u) {
@@ -454,6 +448,10 @@ __global__ __launch_bounds__(kSmallThreads) void merge_kernel(DecodeArgs a, DevT
       for (int u = 0; u < 16; ++u)
         if (lv[u] > 0.0f) M = fmaxf(M, mv[u]);
     }
+    if ((tid & 31) == 0) sMx[sub][g] = M;
+    lds_barrier();
+#pragma unroll
+    for (int r = 0; r < nsub; ++r) M = fmaxf(M, sMx[r][g]);
     float4 acc = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
     float L = 0.0f;
     // an empty split (l = 0) gets weight 0 and its accumulator is not used
