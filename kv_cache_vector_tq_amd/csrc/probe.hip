@@ -36,7 +36,9 @@ TQ_API int tq_read_probe(const void* buf, int64_t bytes, uint32_t* sink, int rep
   if (reinterpret_cast<uintptr_t>(buf) % 16 != 0) return TQ_ERR_INVALID_ARG;
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipEvent_t a = nullptr, b = nullptr;
-  if (hipEventCreate(&a) != hipSuccess || hipEventCreate(&b) != hipSuccess) {
+  // timing-only events, as for the scan's: no system-scope fence when recorded
+  if (hipEventCreateWithFlags(&a, hipEventDisableSystemFence) != hipSuccess ||
+      hipEventCreateWithFlags(&b, hipEventDisableSystemFence) != hipSuccess) {
     if (a) (void)hipEventDestroy(a);
     return TQ_ERR_HIP;
   }

@@ -283,7 +283,9 @@ TQ_API int tq_profile_begin(tq_ctx* c, int max_calls) {
   c->prof_next = 0;
   for (int i = 0; i < 2 * max_calls; ++i) {
     hipEvent_t e;
-    if (hipEventCreate(&e) != hipSuccess) return TQ_ERR_HIP;
+    // timing-only events: no system-scope fence (cache writeback and
+    // invalidate) when they are recorded, which would lengthen the interval
+    if (hipEventCreateWithFlags(&e, hipEventDisableSystemFence) != hipSuccess) return TQ_ERR_HIP;
     c->prof_events.push_back(e);
   }
   return rc;
