@@ -378,17 +378,20 @@ __global__ __launch_bounds__(kSmallThreads) void merge_kernel(DecodeArgs a, DevT
   // ---- loads, in the order they are needed (loads complete in order: a
   // wait for the first ones does not wait for the rest)
   // split partials: thread (c4, q8) takes query g = q8 % GW and reads the
-  // accumulators of its first 8 splits s = sub, sub + nsub, ... (sub =
-  // q8 / GW); together the nsub threads of a query cover the first 8 nsub
-  // splits, whose maximum they combine through LDS
+  // accumulators of its first kFirst splits s = sub, sub + nsub, ... (sub =
+  // q8 / GW); together the nsub threads of a query cover the first
+  // kFirst nsub splits, whose maximum they combine through LDS
   constexpr int nsub = 8 / GW;
+  // (16 for one query head per work-group: the launch shape with few work-
+  // groups and many splits per head; 8 otherwise, which keeps two waves per SIMD)
+  constexpr int kFirst = GW == 1 ? 16 : 8;
   const int g = q8 % GW, sub = q8 / GW;
   // (loads are unconditional, from a clamped split index, and the result is
   // selected: a load under a branch would make its join wait for all loads)
-  float4 va[8];
-  float la[8], ma[8];
+  float4 va[kFirst];
+  float la[kFirst], ma[kFirst];
 #pragma unroll
-  for (int u = 0; u < 8; ++u) {
+  for (int u = 0; u < kFirst; ++u) {
     const int s = sub + u * nsub;
     const int64_t pi = (bh * a.splits + (s < a.splits ? s : 0)) * k.G + g0 + g;
     va[u] = *reinterpret_cast<const float4*>(a.pacc + pi * kD + c4);
@@ -396,7 +399,7 @@ __global__ __launch_bounds__(kSmallThreads) void merge_kernel(DecodeArgs a, DevT
     ma[u] = a.pm[pi];
   }
 #pragma unroll
-  for (int u = 0; u < 8; ++u) la[u] = sub + u * nsub < a.splits ? la[u] : 0.0f;
+  for (int u = 0; u < kFirst; ++u) la[u] = sub + u * nsub < a.splits ? la[u] : 0.0f;
   // window keys: thread pair (tk, half) holds slot tk = tid / 2, coordinates 64 half ..
   const int tk0 = tid >> 1, half = tid & 1;
   uint4 kv[8];
@@ -431,10 +434,10 @@ __global__ __launch_bounds__(kSmallThreads) void merge_kernel(DecodeArgs a, DevT
   {
     float M = -INFINITY;
 #pragma unroll
-    for (int u = 0; u < 8; ++u)
+    for (int u = 0; u < kFirst; ++u)
       if (la[u] > 0.0f) M = fmaxf(M, ma[u]);
-    // splits past the first 8 nsub: every thread of the query reads them all
-    for (int s0 = 8 * nsub; s0 < a.splits; s0 += 16) {
+    // splits past the first kFirst nsub: every thread of the query reads them all
+    for (int s0 = kFirst * nsub; s0 < a.splits; s0 += 16) {
       float lv[16], mv[16];
 #pragma unroll
       for (int u = 0; u < 16; ++u) {
@@ -466,9 +469,9 @@ __global__ __launch_bounds__(kSmallThreads) void merge_kernel(DecodeArgs a, DevT
       }
     };
 #pragma unroll
-    for (int u = 0; u < 8; ++u) add(va[u], la[u], ma[u]);
+    for (int u = 0; u < kFirst; ++u) add(va[u], la[u], ma[u]);
     // later batches of 8 splits: all loads of a batch are issued before use
-    for (int s0 = sub + 8 * nsub; s0 < a.splits; s0 += 8 * nsub) {
+    for (int s0 = sub + kFirst * nsub; s0 < a.splits; s0 += 8 * nsub) {
       float4 v[8];
       float lv[8], mv[8];
 #pragma unroll
