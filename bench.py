@@ -1,25 +1,35 @@
 """Benchmark of the TurboQuant KV-cache hot path on one MI355X.
 
-Workload (one decode step per layer call): B=16 sequences, H_q=32 query heads
-over H_kv=8 KV heads (GQA 4:1), head_dim 128, a 32K-token context per
-sequence (the last 128 tokens in the FP16 window, the rest in 256-token
-pages of 3-bit+QJL keys and 4-bit values, dense rotation), bf16 queries.
-A step appends one new token to every sequence (tq_append_page: the token
+Headline workload (one decode step per layer call): B=16 sequences, H_q=32
+query heads over H_kv=8 KV heads (GQA 4:1), head_dim 128, a 32K-token context
+per sequence (the last 128 tokens in the FP16 window, the rest in 256-token
+pages of 3-bit+QJL keys and 4-bit values, dense rotation), bf16 queries.  A
+step appends one new token to every sequence (tq_append_page: the token
 leaving the window is encoded into its page) and runs tq_decode_attn over
 the whole context.  The context is prefilled so that the last timed step
-decodes at exactly T = 32768.  Inputs are seeded synthetic data with the
-key recipe of tq_inputs (heavy-tailed channels, RoPE) drawn on the GPU.
+decodes at exactly T = 32768.  Inputs are seeded synthetic data with the key
+recipe of tq_inputs (heavy-tailed channels, RoPE) drawn on the GPU.
 
-Prints one JSON line: tokens/s (sum of context lengths attended per second),
-the step time, the scan kernel's roofline (algorithmic bytes per launch /
-its HIP-event time vs the 8 TB/s HBM peak, and vs the device's measured
-streaming-read rate) and a CPU baseline (the float64 oracle on a bounded
-sample of the same workload).  The scan's HIP events are recorded over a
-second run of as many steps right after the timed ones: each event record
-adds a few microseconds of queue time, which the timed steps do not carry.
+The JSON line carries, besides the step rate:
+  roofline      the scan kernel (the one that streams the packed cache):
+                algorithmic bytes per launch / its duration.  The duration
+                comes from HIP events the library records on the launch
+                stream around each scan launch, over a replay of the timed
+                steps (lengths and rings restored to where the timed region
+                started, so the same tokens at the same context lengths);
+                each event adds its own latency, so this fraction is a
+                conservative one;
+  decode_call   back-to-back tq_decode_attn calls at the final length,
+                host-timed: prep + scan + merge per call, against the bytes
+                one call must read (pages and FP16 window);
+  read_ceiling  the device's streaming-read rate (tq_read_probe, 1 GiB);
+  workloads     the two other decode workloads (below), same fields;
+  encode        tq_encode of 4M fp16 vectors at 2, 3 and 4 bits, dense and
+                randomized-Hadamard rotations, keys with QJL and values;
+  cpu_baseline  the float64 oracle on a bounded slice of the headline
+                workload, on the host cores.
 
-Two more decode workloads are available with --workload (the default is
-"batch", the workload above):
+Other decode workloads (--workload selects one of them alone):
   long    B=1, H_q=64, H_kv=8, T=131,072, keys 2-bit+QJL, values 2-bit,
           Hadamard rotation.  One layer's cache is 97 MB, less than the
           256 MB last-level cache, so three replicas of it take turns (step i
@@ -34,6 +44,7 @@ Two more decode workloads are available with --workload (the default is
 import argparse
 import json
 import os
+import platform
 import sys
 import time
 
@@ -51,6 +62,7 @@ WORKLOADS = {
     "layers": dict(B=64, Hq=16, Hkv=2, T=(1024, 16384), kbits=3, vbits=4, rotation="dense", replicas=1, layers=36),
 }
 METRIC = "decode-attn compressed-KV tokens/s & HBM GB/s vs peak; encode vectors/s"
+DTYPE = "fp32 accumulate; fp16 MFMA operands (query side split hi+lo, ~22 bits)"
 
 
 def parse():
@@ -59,9 +71,11 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-encode", action="store_true", help="skip the tq_encode leg")
+    ap.add_argument("--no-encode", action="store_true", help="skip the tq_encode legs")
+    ap.add_argument("--no-extra", action="store_true", help="skip the other decode workloads")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
-    ap.add_argument("--workload", choices=sorted(WORKLOADS), default="batch")
+    ap.add_argument("--workload", choices=sorted(WORKLOADS), default=None,
+                    help="time this decode workload alone (default: the headline line with all legs)")
     ap.add_argument("--T", type=int, default=None, help="context length (batch and long workloads)")
     ap.add_argument("--batch", type=int, default=None)
     ap.add_argument("--valu-scan", action="store_true", help="time the vector-ALU scan kernel instead")
@@ -76,10 +90,25 @@ def parse():
     return ap.parse_args()
 
 
-def cpu_baseline(T, W, P, G, Hkv, min_seconds, kbits=3, vbits=4, kmix=0, vmix=0, kn8=0, rotation="dense"):
+def host_info():
+    model = platform.processor() or "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return model, len(os.sched_getaffinity(0))
+
+
+def cpu_baseline(T, W, P, G, Hkv, B, min_seconds, kbits=3, vbits=4, kmix=0, vmix=0, kn8=0, rotation="dense"):
     """The oracle's decode (dequantise + float64 softmax attention) on one
-    sequence and one KV head (G query heads) at context T, repeated until
-    min_seconds of CPU work; converted to sequence-tokens/s at H_kv heads."""
+    (sequence, KV head) slice of a layer call: G query heads over a T-token
+    context.  Repeated until min_seconds of CPU work.  A layer call is B x Hkv
+    such slices, so the rate in the workload's unit (sequence tokens attended
+    per second) is calls * T / (time * Hkv)."""
     from threadpoolctl import threadpool_info
     sys.path.insert(0, os.path.join(ROOT, "tests"))
     from oracle import attention as att
@@ -97,10 +126,13 @@ def cpu_baseline(T, W, P, G, Hkv, min_seconds, kbits=3, vbits=4, kmix=0, vmix=0,
         el = time.perf_counter() - t0
         if el >= min_seconds:
             break
-    threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
-    return {"value": calls * T / Hkv / el, "unit": "tokens/s", "cores": threads, "kind": "oracle",
-            "sample": f"{calls} oracle decode call(s) of 1 sequence x 1 KV head ({G} query heads) at T={T}, "
-                      f"{el:.1f} s; rate scaled to {Hkv} KV heads"}
+    model, cores = host_info()
+    blas = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    return {"value": calls * T / Hkv / el, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "cpu_model": model, "blas_threads": blas,
+            "sample": f"{calls} oracle decode call(s) of one (sequence, KV head) slice ({G} query heads, "
+                      f"T={T}) of the {B} x {Hkv}-slice layer call, {el:.1f} s; tokens/s = calls x T / "
+                      f"(seconds x {Hkv} KV heads)"}
 
 
 SCAN_SOURCES = ["decode_mfma.hip", "decode_common.h", "device_common.h", "tq_internal.h"]
@@ -123,12 +155,12 @@ def scan_traffic():
     return rec.get("hbm_bytes_per_launch")
 
 
-def encode_leg(tqa, tq_inputs, ctx, params, reps=10):
+def encode_legs(tqa, tq_inputs, reps=10):
     """tq_encode of 4M fp16 vectors (4,096 sequences x 1,024 positions of the
-    key recipe, and as many N(0,1) values) with the decode workload's formats:
-    keys 3-bit + QJL, values 4-bit, dense rotation.  HIP-event time per call;
-    MFMA work as executed (rotation in two fp16 passes, QJL projection in
-    three) and as the two d x d products count it (4 d^2 flop per key)."""
+    key recipe, and as many N(0,1) values) at 2, 3 and 4 bits, dense and
+    Hadamard rotations; keys with the QJL sketch.  HIP-event time per call.
+    Dense rotation: algorithmic flops 4 d^2 per key, 2 d^2 per value; MFMA
+    flops as executed (fp16 passes: rotation 2, QJL projection 3)."""
     import torch
     n, d = 4096 * 1024, 128
     k, v = tq_inputs.torch_kv(5, 4096, 1, 1024, d, "cuda")
@@ -137,75 +169,58 @@ def encode_leg(tqa, tq_inputs, ctx, params, reps=10):
     norms = torch.empty(n, dtype=torch.float32, device="cuda")
     signs = torch.empty((n, 16), dtype=torch.uint8, device="cuda")
     rnorms = torch.empty(n, dtype=torch.float32, device="cuda")
-    out = {}
-    for name, kind, x, qjl in (("keys_3bit_qjl", tqa.TQ_KIND_KEY, k, True), ("values_4bit", tqa.TQ_KIND_VALUE, v, False)):
-        def call():
-            tqa.tq_encode(ctx, kind, x, codes, norms, signs if qjl else None, rnorms if qjl else None)
-        call()
-        torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        for _ in range(reps):
-            call()
-        e1.record()
-        torch.cuda.synchronize()
-        ms = e0.elapsed_time(e1) / reps
-        algo = (4 if qjl else 2) * d * d * n
-        executed = (5 if qjl else 2) * 2 * d * d * n
-        in_bytes = n * d * 2
-        out_bytes = n * ((48 + 16 + 8) if qjl else (64 + 4))
-        out[name] = {"ms": ms, "vectors_per_s": n / (ms / 1e3), "algorithmic_tflops": algo / (ms / 1e3) / 1e12,
-                     "mfma_tflops_executed": executed / (ms / 1e3) / 1e12,
-                     "hbm_gbps": (in_bytes + out_bytes) / (ms / 1e3) / 1e9}
-    out["workload"] = "tq_encode of 4,194,304 fp16 vectors d=128 (4,096 x 1,024 positions), dense rotation"
+    out = {"workload": "tq_encode of 4,194,304 fp16 vectors d=128 (4,096 x 1,024 positions) into flat records"}
+    for rotation in ("dense", "hadamard"):
+        for bits in (2, 3, 4):
+            params = tqa.make_params(key_bits=bits, key_qjl=1, value_bits=bits,
+                                     rotation=tqa.TQ_ROT_DENSE if rotation == "dense" else tqa.TQ_ROT_HADAMARD)
+            rd = tq_inputs.rotation_draws(0, d) if rotation == "dense" else tq_inputs.hadamard_draws(0, d)
+            ctx = tqa.Context(params, rd, tq_inputs.qjl_draws(0, d))
+            for name, kind, x, qjl in ((f"{rotation}_keys_{bits}bit_qjl", tqa.TQ_KIND_KEY, k, True),
+                                       (f"{rotation}_values_{bits}bit", tqa.TQ_KIND_VALUE, v, False)):
+                def call():
+                    tqa.tq_encode(ctx, kind, x, codes, norms, signs if qjl else None, rnorms if qjl else None)
+                call()
+                torch.cuda.synchronize()
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record()
+                for _ in range(reps):
+                    call()
+                e1.record()
+                torch.cuda.synchronize()
+                ms = e0.elapsed_time(e1) / reps
+                rec_bytes = 16 * bits + 4 + (16 + 4 if qjl else 0)
+                hbm = (n * d * 2 + n * rec_bytes) / (ms / 1e3) / 1e9
+                r = {"ms": ms, "vectors_per_s": n / (ms / 1e3), "hbm_gbps": hbm, "hbm_frac": hbm / HBM_PEAK_GBPS}
+                if rotation == "dense":
+                    r["algorithmic_tflops"] = (4 if qjl else 2) * d * d * n / (ms / 1e3) / 1e12
+                    r["mfma_tflops_executed"] = (5 if qjl else 2) * 2 * d * d * n / (ms / 1e3) / 1e12
+                out[name] = r
+            ctx.close()
     del k, v, codes, norms, signs, rnorms
     return out
 
 
-def main():
-    args = parse()
-    if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU; --gpus above 1 is not supported",
-                          "n_gpus": args.gpus}))
-        sys.exit(2)
+def decode_workload(tqa, tq_inputs, wname, args, fmt_over=None):
+    """Prefill, warm up, time args.steps decode steps of one workload; then
+    replay the timed steps with scan events; then time back-to-back decode
+    calls at the final lengths.  Returns the JSON fields of the workload."""
     import torch
-    if args.copy_calibration:
-        src = torch.ones(1 << 30, dtype=torch.uint8, device="cuda")
-        dst = torch.empty_like(src)
-        for _ in range(3):
-            dst.copy_(src)
-        torch.cuda.synchronize()
-        print(json.dumps({"copy_bytes_read": 1 << 30, "copy_bytes_written": 1 << 30, "launches": 3}))
-        return
-    import kv_cache_vector_tq_amd as tqa
-    import tq_inputs
-    if not os.path.exists(tqa.LIB_PATH):
-        from kv_cache_vector_tq_amd import build
-        build.build()
     dev = "cuda"
-    wl = WORKLOADS[args.workload]
-    default_run = args.workload == "batch"
-    B = args.batch if args.batch is not None else wl["B"]
+    wl = WORKLOADS[wname]
+    fo = fmt_over or {}
+    B = fo.get("B", wl["B"])
     Hq, Hkv, d, P, W = wl["Hq"], wl["Hkv"], 128, 256, 128
     G = Hq // Hkv
     R, L = wl["replicas"], wl["layers"]
     ncache = R * L
-    kbits = args.key_bits if args.key_bits is not None else wl["kbits"]
-    vbits = args.value_bits if args.value_bits is not None else wl["vbits"]
-    kmix, vmix = int(args.key_mixed), int(args.value_mixed)
-    kn8 = int(args.key_norm_u8)
+    kbits, vbits = fo.get("kbits", wl["kbits"]), fo.get("vbits", wl["vbits"])
+    kmix, vmix, kn8 = fo.get("kmix", 0), fo.get("vmix", 0), fo.get("kn8", 0)
     rotation = wl["rotation"]
-    # target length of each sequence at the last step (a drawn length per
-    # sequence for a range)
     if isinstance(wl["T"], tuple):
         Tf = tq_inputs.ragged_lengths(0, B, *wl["T"]).astype(np.int64)
     else:
-        Tf = np.full(B, args.T if args.T is not None else wl["T"], dtype=np.int64)
-    # warm-up steps, then the timed steps, then as many steps again with HIP
-    # events around each scan launch (the roofline's kernel time; each event
-    # record adds queue time, so they are not timed).  Step i appends one
-    # token to, and decodes, every layer's cache, or replica i mod R.
-    nsteps = args.warmup + 2 * args.steps
+        Tf = np.full(B, fo.get("T", wl["T"]), dtype=np.int64)
     ntimed = args.warmup + args.steps
 
     def appends(c, n):  # appends cache c receives in steps 0 .. n-1
@@ -213,13 +228,12 @@ def main():
     params = tqa.make_params(key_bits=kbits, key_qjl=1, value_bits=vbits,
                              rotation=tqa.TQ_ROT_DENSE if rotation == "dense" else tqa.TQ_ROT_HADAMARD,
                              num_q_heads=Hq, num_kv_heads=Hkv, page_tokens=P, window=W, seed=0,
-                             flags=tqa.TQ_FLAG_VALU_SCAN if args.valu_scan else 0, key_mixed=kmix, value_mixed=vmix,
+                             flags=tqa.TQ_FLAG_VALU_SCAN if fo.get("valu") else 0, key_mixed=kmix, value_mixed=vmix,
                              key_norm_u8=kn8)
     rdraws = tq_inputs.rotation_draws(0, d) if rotation == "dense" else tq_inputs.hadamard_draws(0, d)
     ctx = tqa.Context(params, rdraws, tq_inputs.qjl_draws(0, d))
     pb = tqa.tq_page_bytes(params)
-    # lengths reach Tf at the last timed step; the evented steps go past it
-    max_pages = -(-(int(Tf.max()) + max(appends(c, nsteps) - appends(c, ntimed) for c in range(ncache)) - W) // P)
+    max_pages = -(-(int(Tf.max()) - W) // P)
     npages = B * max_pages
     caches = []
     for c in range(ncache):
@@ -240,13 +254,12 @@ def main():
         del k, v
         cache["lens"] = lens0.copy()
         caches.append(cache)
-    # new tokens and queries of the steps (the same for every layer's cache)
-    k_new, v_new = tq_inputs.torch_kv(0, B, Hkv, nsteps, d, dev, layer=L, start=int(Tf.max()))
-    ksteps = [k_new[:, :, i:i + 1].contiguous() for i in range(nsteps)]
-    vsteps = [v_new[:, :, i:i + 1].contiguous() for i in range(nsteps)]
+    k_new, v_new = tq_inputs.torch_kv(0, B, Hkv, ntimed, d, dev, layer=L, start=int(Tf.max()))
+    ksteps = [k_new[:, :, i:i + 1].contiguous() for i in range(ntimed)]
+    vsteps = [v_new[:, :, i:i + 1].contiguous() for i in range(ntimed)]
     del k_new, v_new
-    qsteps = [tq_inputs.torch_queries(0, (B, Hq, d), dev, torch.bfloat16, step=i) for i in range(nsteps)]
-    pps = args.pages_per_split
+    qsteps = [tq_inputs.torch_queries(0, (B, Hq, d), dev, torch.bfloat16, step=i) for i in range(ntimed)]
+    pps = fo.get("pps", 0)
     ws = torch.empty(tqa.tq_decode_workspace_bytes(ctx, B, max_pages, pps), dtype=torch.uint8, device=dev)
     out = torch.empty((B, Hq, d), dtype=torch.float32, device=dev)
     sm = 1.0 / np.sqrt(d)
@@ -256,16 +269,19 @@ def main():
     def step_caches(i):
         return [caches[i % R]] if R > 1 else caches
 
+    def decode(c, i):
+        tqa.tq_decode_attn(ctx, qsteps[i], c["pool"], c["block_table"], c["seq_lens"], c["k_win"], c["v_win"],
+                           out, ws, sm, pages_per_split=pps, num_pages=npages)
+
     def step(i):
         for c in step_caches(i):
             tqa.tq_append_page(ctx, c["pool"], c["block_table"], c["seq_lens"], ksteps[i], vsteps[i], c["k_win"],
                                c["v_win"], num_pages=npages)
-            tqa.tq_decode_attn(ctx, qsteps[i], c["pool"], c["block_table"], c["seq_lens"], c["k_win"], c["v_win"],
-                               out, ws, sm, pages_per_split=pps, num_pages=npages)
+            decode(c, i)
 
     # context lengths each decode call attends (host bookkeeping of the appends)
     attended = []
-    for i in range(nsteps):
+    for i in range(ntimed):
         lens_i = []
         for c in step_caches(i):
             c["lens"] = c["lens"] + 1
@@ -274,28 +290,44 @@ def main():
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
+    # where the timed region starts: lengths and rings, restored for the replay
+    snap = [(c["seq_lens"].clone(), c["k_win"].clone(), c["v_win"].clone()) for c in caches]
     # timed region: the steps as a caller runs them
     t0 = time.perf_counter()
-    for i in range(args.warmup, args.warmup + args.steps):
+    for i in range(args.warmup, ntimed):
         step(i)
     torch.cuda.synchronize()
     el = time.perf_counter() - t0
-    # the scan kernel's time: HIP events recorded by the library on the launch
-    # stream around each scan launch of the next steps
-    nprof = sum(len(step_caches(i)) for i in range(args.warmup + args.steps, nsteps))
+    final = [c["seq_lens"].clone() for c in caches]
+    # replay of the timed steps with HIP events around each scan launch
+    for c, (sl, kw, vw) in zip(caches, snap):
+        c["seq_lens"].copy_(sl)
+        c["k_win"].copy_(kw)
+        c["v_win"].copy_(vw)
+    torch.cuda.synchronize()
+    nprof = sum(len(step_caches(i)) for i in range(args.warmup, ntimed))
     tqa.tq_profile_begin(ctx, nprof)
-    t1 = time.perf_counter()
-    for i in range(args.warmup + args.steps, nsteps):
+    for i in range(args.warmup, ntimed):
         step(i)
     torch.cuda.synchronize()
-    el_prof = time.perf_counter() - t1
     scan_ms, ncalls = tqa.tq_profile_end(ctx)
+    for c, f in zip(caches, final):
+        assert torch.equal(c["seq_lens"], f), "the replay did not end at the timed region's lengths"
+    # back-to-back decode calls at the final lengths (no appends): prep + scan + merge
+    ncall = max(args.steps, 10)
+    torch.cuda.synchronize()
+    t2 = time.perf_counter()
+    for j in range(ncall):
+        for c in step_caches(ntimed - 1 - (j % R)):
+            decode(c, ntimed - 1)
+    torch.cuda.synchronize()
+    el_call = (time.perf_counter() - t2) / (ncall * (L if R == 1 else 1))
     status = tqa.tq_get_status(ctx)
     if status != 0 or not torch.isfinite(out).all():
         raise SystemExit(f"bench: bad status {status} or non-finite output")
     for c in caches:
         assert np.array_equal(c["seq_lens"].cpu().numpy(), c["lens"]), "sequence lengths drifted from the bookkeeping"
-    timed = range(args.warmup, args.warmup + args.steps)
+    timed = range(args.warmup, ntimed)
     tokens = sum(int(x.sum()) for i in timed for x in attended[i])
     # key codes + signs + norm + rnorm, value codes + norm (a mixed rate adds d/16 code bytes)
     # (a u8 log-norm key norm takes 1 byte instead of 4)
@@ -303,18 +335,19 @@ def main():
 
     def comp_bytes(lens):  # compressed bytes one scan launch reads
         return Hkv * int(np.maximum(lens - W, 0).sum()) * per_tok_head
-
-    prof_bytes = [comp_bytes(x) for i in range(args.warmup + args.steps, nsteps) for x in attended[i]]
     win_bytes = B * Hkv * W * d * 2 * 2
+    prof_bytes = [comp_bytes(x) for i in timed for x in attended[i]]
     scan_s = scan_ms / 1e3 / max(ncalls, 1)
     achieved = (sum(prof_bytes) / len(prof_bytes)) / scan_s / 1e9
     ms_step = el / args.steps * 1e3
+    call_bytes = comp_bytes(attended[ntimed - 1][-1]) + win_bytes
+    lo_T, hi_T = int(min(x.max() for i in timed for x in attended[i])), int(Tf.max())
     fmt = (f"keys {kbits + 0.5 * kmix:g}-bit+QJL{' with u8 log-norms' if kn8 else ''}, values "
            f"{vbits + 0.5 * vmix:g}-bit, {rotation} rotation, bf16 queries")
-    if args.workload == "batch":
+    if wname == "batch":
         desc = (f"decode step (append 1 token + decode attention), B={B}, Hq={Hq}, Hkv={Hkv}, d={d}, "
                 f"T={int(Tf[0])} (last step), W={W} fp16 window, P={P}, {fmt}")
-    elif args.workload == "long":
+    elif wname == "long":
         desc = (f"long-context decode step (append 1 token + decode attention), B={B}, Hq={Hq}, Hkv={Hkv}, d={d}, "
                 f"T={int(Tf[0])} (last step), W={W}, P={P}, {fmt}; {R} cache replicas take turns so that "
                 f"each decode reads from HBM")
@@ -323,42 +356,92 @@ def main():
                 f"lengths U{{{wl['T'][0]}..{wl['T'][1]}}} (mean {Tf.mean():.0f} at the last step), Hq={Hq}, "
                 f"Hkv={Hkv}, d={d}, W={W}, P={P}, {fmt}")
     res = {
-        "metric": METRIC, "value": tokens / el, "unit": "tokens/s", "n_gpus": 1,
-        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_step, "higher_is_better": True,
-        "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "value": tokens / el, "unit": "tokens/s", "ms_per_step": ms_step,
         "config": {"workload": desc, "batch": B, "seq_len": int(Tf.max()), "parallelism": "none (1 GPU)"},
         "hbm_gbps_step": (sum(comp_bytes(x) for i in timed for x in attended[i]) / args.steps
                           + len(step_caches(0)) * win_bytes) / (ms_step / 1e3) / 1e9,
-        "scan_us": scan_s * 1e6,
-        "ms_per_step_with_scan_events": el_prof / args.steps * 1e3,
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBPS,
-                     # the committed counter record covers the default workload and formats only
-                     "traffic": scan_traffic() if default_run and (kbits, vbits, kmix, vmix, kn8) == (3, 4, 0, 0, 0)
-                     else None,
-                     "kernel": "scan_kernel (VALU)" if args.valu_scan else "scan_mfma_kernel",
-                     "algorithmic_bytes_per_launch": sum(prof_bytes) / len(prof_bytes)},
+                     "frac": achieved / HBM_PEAK_GBPS, "traffic": None,
+                     "kernel": "scan_kernel (VALU)" if fo.get("valu") else "scan_mfma_kernel",
+                     "algorithmic_bytes_per_launch": sum(prof_bytes) / len(prof_bytes),
+                     "launch_us": scan_s * 1e6,
+                     "launches": f"{ncalls} scan launches by HIP events, a replay of the timed steps "
+                                 f"(longest context {lo_T}..{hi_T})"},
+        "decode_call": {"us": el_call * 1e6, "bytes": call_bytes,
+                        "gbps": call_bytes / el_call / 1e9, "frac": call_bytes / el_call / 1e9 / HBM_PEAK_GBPS,
+                        "what": f"tq_decode_attn (prep + scan + merge) at longest context {hi_T}, mean of "
+                                f"{ncall} back-to-back host-timed calls; bytes = packed pages + FP16 window"},
     }
     if L > 1:
         res["layer_calls_per_s"] = L * args.steps / el
-    del caches, ksteps, vsteps, ws
+    del caches, ksteps, vsteps, ws, out
+    ctx.close()
+    torch.cuda.empty_cache()
+    return res
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU; --gpus above 1 is not supported",
+                          "n_gpus": args.gpus}))
+        sys.exit(2)
+    import torch
+    if args.copy_calibration:
+        src = torch.ones(1 << 30, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_read": 1 << 30, "copy_bytes_written": 1 << 30, "launches": 3}))
+        return
+    import kv_cache_vector_tq_amd as tqa
+    import tq_inputs
+    if not os.path.exists(tqa.LIB_PATH):
+        raise SystemExit(f"{tqa.LIB_PATH} is missing: build the library first (python -m kv_cache_vector_tq_amd.build)")
+    wname = args.workload or "batch"
+    headline = args.workload is None
+    fo = {}
+    for key, val in (("kbits", args.key_bits), ("vbits", args.value_bits), ("B", args.batch), ("T", args.T)):
+        if val is not None:
+            fo[key] = val
+    fo.update(kmix=int(args.key_mixed), vmix=int(args.value_mixed), kn8=int(args.key_norm_u8),
+              valu=bool(args.valu_scan), pps=args.pages_per_split)
+    default_fmt = not any(k in fo for k in ("kbits", "vbits", "B", "T")) and not (
+        args.key_mixed or args.value_mixed or args.key_norm_u8 or args.valu_scan or args.pages_per_split)
+    w = decode_workload(tqa, tq_inputs, wname, args, fo)
+    res = {"metric": METRIC, "value": w.pop("value"), "unit": w.pop("unit"), "n_gpus": 1,
+           "steps": args.steps, "warmup": args.warmup, "ms_per_step": w.pop("ms_per_step"),
+           "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": DTYPE,
+           "data": "synthetic"}
+    res.update(w)
+    if wname == "batch" and default_fmt:
+        # the committed counter record covers the headline workload and formats only
+        res["roofline"]["traffic"] = scan_traffic()
     # measured ceiling: a plain coalesced streaming read of 1 GiB (beyond the
     # 256 MB last-level cache), fastest of 5 launches
-    rbuf = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    rbuf = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
     rbuf.fill_(1)
-    sink = torch.zeros(1, dtype=torch.int32, device=dev)
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
     read_gbps = rbuf.numel() / (tqa.tq_read_probe(rbuf, sink, reps=5) / 1e3) / 1e9
     del rbuf
     res["read_ceiling"] = {"GBps": read_gbps, "bytes": 1 << 30, "kernel": "tq_read_probe (coalesced 16-byte loads)",
                            "frac_of_peak": read_gbps / HBM_PEAK_GBPS}
-    res["roofline"]["frac_of_read_ceiling"] = achieved / read_gbps
-    # the encode leg measures the default formats (3-bit+QJL keys, 4-bit values)
-    if default_run and not args.no_encode and (kbits, vbits, kmix, vmix, kn8) == (3, 4, 0, 0, 0):
-        res["encode"] = encode_leg(tqa, tq_inputs, ctx, params)
+    res["roofline"]["frac_of_read_ceiling"] = res["roofline"]["achieved"] / read_gbps
+    if headline and default_fmt and not args.no_extra:
+        extra = {}
+        for other in ("long", "layers"):
+            ow = decode_workload(tqa, tq_inputs, other, args)
+            extra[other] = ow
+        res["workloads"] = extra
+    if headline and default_fmt and not args.no_encode:
+        res["encode"] = encode_legs(tqa, tq_inputs)
     if not args.no_cpu_baseline:
-        # one sequence at the workload's longest context
-        res["cpu_baseline"] = cpu_baseline(int(Tf.max()), W, P, G, Hkv, args.cpu_seconds, kbits, vbits, kmix, vmix,
-                                           kn8, rotation)
+        wl = WORKLOADS[wname]
+        res["cpu_baseline"] = cpu_baseline(int(res["config"]["seq_len"]), 128, 256, wl["Hq"] // wl["Hkv"], wl["Hkv"],
+                                           res["config"]["batch"], args.cpu_seconds,
+                                           fo.get("kbits", wl["kbits"]), fo.get("vbits", wl["vbits"]),
+                                           fo["kmix"], fo["vmix"], fo["kn8"], wl["rotation"])
     print(json.dumps(res), flush=True)
 
 

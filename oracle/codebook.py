@@ -108,12 +108,16 @@ class Codebook:
     held as float64 so that every later step uses them as exact numbers.
     """
 
-    def __init__(self, bits: int, head_dim: int):
+    def __init__(self, bits: int, head_dim: int, storage: str = "half"):
+        """``storage``: precision the scaled levels are rounded to, "half"
+        (the reading used throughout) or "single" (float32; kept only so a
+        test can show the choice does not move results at the parity bar)."""
         self.bits = bits
         self.head_dim = head_dim
         unit = lloyd_max_normal(bits)
         scale = 1.0 / math.sqrt(head_dim)
-        self.centroids = np.array([np.float16(c * scale) for c in unit], dtype=np.float64)
+        rnd = {"half": np.float16, "single": np.float32}[storage]
+        self.centroids = np.array([rnd(c * scale) for c in unit], dtype=np.float64)
         c = self.centroids
         self.boundaries = np.array(
             [np.float32((c[k] + c[k + 1]) * 0.5) for k in range(len(c) - 1)], dtype=np.float64

@@ -77,6 +77,47 @@ def rel_close(got, want, tol=1e-3):
     return np.linalg.norm(got - want) <= tol * max(np.linalg.norm(want), 1e-30)
 
 
+def out_errors(got, want):
+    """(L2 relative error, largest coordinate error / largest |coordinate|) of
+    one output vector."""
+    got = np.asarray(got, np.float64)
+    want = np.asarray(want, np.float64)
+    d = np.abs(got - want)
+    return (float(np.linalg.norm(d) / max(np.linalg.norm(want), 1e-30)),
+            float(np.max(d) / max(np.max(np.abs(want)), 1e-30)))
+
+
+def assert_out_close(got, want, tol=1e-3, what=""):
+    """The output bar, per (b, q-head): ||got - want||_2 <= tol ||want||_2 and,
+    coordinate by coordinate, |got_j - want_j| <= tol max_j |want_j|.
+    Returns the two errors."""
+    l2, co = out_errors(got, want)
+    assert np.all(np.isfinite(got)), f"non-finite output {what}"
+    assert l2 <= tol, f"L2 error {l2:.3g} > {tol} {what}"
+    assert co <= tol, f"coordinate error {co:.3g} (of max |o|) > {tol} {what}"
+    return l2, co
+
+
+class ErrStats:
+    """Largest logit / output errors seen by a test (printed at the end, so a
+    run shows how far inside the bar the results are)."""
+
+    def __init__(self, name):
+        self.name, self.logit, self.l2, self.co, self.n = name, None, 0.0, 0.0, 0
+
+    def add(self, logit=None, out=None):
+        if logit is not None:
+            self.logit = logit if self.logit is None else max(self.logit, logit)
+        if out is not None:
+            self.l2, self.co = max(self.l2, out[0]), max(self.co, out[1])
+            self.n += 1
+
+    def report(self):
+        lg = "not captured" if self.logit is None else f"{self.logit:.3g}"
+        print(f"{self.name}: {self.n} outputs checked; max logit err {lg}, max L2 err {self.l2:.3g}, "
+              f"max coordinate err {self.co:.3g} (bar 1e-3)", flush=True)
+
+
 def to_dev(a, dtype=None):
     t = torch.from_numpy(np.ascontiguousarray(a))
     if dtype is not None:

@@ -23,7 +23,7 @@ import kv_cache_vector_tq_amd as tqa
 from oracle import attention as att
 from oracle import codec, pages
 import tq_inputs
-from gpu_helpers import check_codes, check_signs, context_for, rel_close
+from gpu_helpers import ErrStats, assert_out_close, check_codes, check_signs, context_for
 from oracle_cache import Setup
 
 pytestmark = [pytest.mark.gpu, pytest.mark.slow]
@@ -111,18 +111,25 @@ def check_window(s, cache, k, v, pairs):
                               v[b, h].index_select(0, pt).cpu().numpy().view(np.uint16))
 
 
-def check_decode(s, cache, q, out, dbg, pairs):
+def check_decode(s, cache, q, out, dbg, pairs, name="decode"):
+    """Every query head of the sampled (b, kv head) pairs: logits within 1e-3
+    of max|logit| (when captured), outputs within 1e-3 (L2 and per coordinate)."""
     qh = q.float().cpu().numpy().astype(np.float64)
     ref_o, ref_l = att.attention_plain(cache, qh, 1 / np.sqrt(s.d), pairs=pairs)
     out = out.cpu().numpy()
-    dbg = dbg.cpu().numpy()
+    dbg = None if dbg is None else dbg.cpu().numpy()
     G = s.Hq // s.Hkv
+    st = ErrStats(name)
     for b, h in pairs:
         T = int(cache.seq_lens[b])
         for g in range(h * G, (h + 1) * G):
-            l = ref_l[b][g]
-            assert np.max(np.abs(dbg[b, g, :T] - l)) <= 1e-3 * np.max(np.abs(l)), (b, g)
-            assert rel_close(out[b, g], ref_o[b, g], 1e-3), (b, g)
+            if dbg is not None:
+                l = ref_l[b][g]
+                le = np.max(np.abs(dbg[b, g, :T] - l)) / np.max(np.abs(l))
+                assert le <= 1e-3, (b, g, le)
+                st.add(logit=le)
+            st.add(out=assert_out_close(out[b, g], ref_o[b, g], 1e-3, (b, g)))
+    st.report()
 
 
 def test_decode_step_B16_Hq32_Hkv8_T32K():
@@ -141,11 +148,13 @@ def test_decode_step_B16_Hq32_Hkv8_T32K():
     assert tqa.tq_get_status(gc.ctx) == 0
     cache = gc.host()
     assert np.all(cache.seq_lens == T)
-    pairs = [(0, 0), (7, 3), (15, 7)]
+    # 16 (sequence, KV head) pairs: every sequence once, every KV head twice
+    pairs = [(b, (3 * b) % Hkv) for b in range(B)]
+    assert len(set(h for _, h in pairs)) == Hkv
     rng = np.random.default_rng(5)
-    check_records(s, cache, k, v, pairs, rng, extra=(T - s.W - 2, T - s.W - 1))
+    check_records(s, cache, k, v, pairs[::4], rng, extra=(T - s.W - 2, T - s.W - 1))
     check_window(s, cache, k, v, pairs)
-    check_decode(s, cache, q, out, dbg, pairs)
+    check_decode(s, cache, q, out, dbg, pairs, "B16 T32K")
 
 
 def test_long_context_B1_Hq64_T128K_hadamard_2bit():
@@ -165,10 +174,10 @@ def test_long_context_B1_Hq64_T128K_hadamard_2bit():
     assert torch.equal(out, out2)
     assert tqa.tq_get_status(gc.ctx) == 0
     cache = gc.host()
-    pairs = [(0, 0), (0, 5)]
-    check_records(s, cache, k, v, pairs, np.random.default_rng(6), extra=range(T0 - s.W, T - s.W))
+    pairs = [(0, h) for h in range(Hkv)]
+    check_records(s, cache, k, v, pairs[::3], np.random.default_rng(6), extra=range(T0 - s.W, T - s.W))
     check_window(s, cache, k, v, pairs)
-    check_decode(s, cache, q, out, dbg, pairs)
+    check_decode(s, cache, q, out, dbg, pairs, "B1 T128K")
 
 
 def test_ragged_layer_B64_Hq16_Hkv2():
@@ -190,11 +199,12 @@ def test_ragged_layer_B64_Hq16_Hkv2():
     assert tqa.tq_get_status(gc.ctx) == 0
     cache = gc.host()
     assert np.array_equal(cache.seq_lens, lens)
+    # 16 pairs spread over the length distribution, both KV heads
     order = np.argsort(lens)
-    pairs = [(int(order[0]), 0), (int(order[B // 2]), 1), (int(order[-1]), 0)]
-    check_records(s, cache, k, v, pairs, np.random.default_rng(7))
+    pairs = [(int(order[i]), i % Hkv) for i in np.linspace(0, B - 1, 16).astype(int)]
+    check_records(s, cache, k, v, pairs[::4], np.random.default_rng(7))
     check_window(s, cache, k, v, pairs)
-    check_decode(s, cache, q, out, dbg, pairs)
+    check_decode(s, cache, q, out, dbg, pairs, "ragged B64")
 
 
 @pytest.mark.parametrize("rotation", ["dense", "hadamard"])
@@ -231,3 +241,60 @@ def test_encode_4M_vectors(rotation):
         assert np.array_equal(g(norms), vref.norms)
         check_codes(xv, codec.unpack_bits(g(codes), bits, 128), vref.idx, s.R, s.vcb)
     torch.cuda.synchronize()
+
+
+def test_streaming_layers_B64_Hq16_Hkv2():
+    """Full-model streaming at the 36-layer workload's shape, cut to 3 layers
+    and 16 steps: every layer (its own cache and K/V draws) is prefilled with
+    a ragged batch (64 sequences, lengths U[1K, 16K]), then each step appends
+    one token per sequence to every layer and decodes every layer.  Checked
+    at the end: lengths and rings exactly, the records of the tokens the steps
+    evicted into pages (and a sample of the prefill's) under the guard-band
+    rule, and the decode outputs of steps 0, 7 and 15 for 4 (sequence, KV
+    head) pairs per layer against the oracle over the cache as it stood at
+    that step (the pages are append-only; the ring of step i is refilled from
+    the FP16 sources)."""
+    print("case streaming 3 layers x 16 steps, B64 Hq16 Hkv2", flush=True)
+    B, Hq, Hkv, nl, steps = 64, 16, 2, 3, 16
+    lens = tq_inputs.ragged_lengths(0, B, 1024, 16384).astype(np.int64)
+    Tm = int(lens.max())
+    s = Setup(Hq=Hq, Hkv=Hkv, key_bits=3, key_qjl=1, value_bits=4, P=256, W=128)
+    order = np.argsort(lens)
+    pairs = [(int(order[i]), i % Hkv) for i in (0, B // 3, 2 * B // 3, B - 1)]
+    checked_steps = (0, 7, steps - 1)
+    layers = []
+    for li in range(nl):
+        gc = GpuCache(s, B, Tm + steps, seed=10 + li)
+        k, v = tq_inputs.torch_kv(20 + li, B, Hkv, Tm + steps, s.d, "cuda", layer=li)
+        gc.append(k[:, :, :Tm], v[:, :, :Tm], counts=lens)
+        layers.append(dict(gc=gc, k=k, v=v, outs={}))
+    torch.cuda.synchronize()
+    for i in range(steps):
+        idx = torch.from_numpy(lens + i).cuda().view(B, 1, 1, 1).expand(B, Hkv, 1, s.d)
+        for li, L in enumerate(layers):
+            L["gc"].append(torch.gather(L["k"], 2, idx), torch.gather(L["v"], 2, idx))
+            q = tq_inputs.torch_queries(30 + li, (B, Hq, s.d), "cuda", torch.bfloat16, step=i)
+            out, _ = L["gc"].decode(q)
+            if i in checked_steps:
+                L["outs"][i] = (q, out)
+    for li, L in enumerate(layers):
+        gc = L["gc"]
+        assert tqa.tq_get_status(gc.ctx) == 0
+        cache = gc.host()
+        assert np.array_equal(cache.seq_lens, lens + steps), li
+        k, v = L["k"], L["v"]
+        check_window(s, cache, k, v, pairs)
+        # the tokens evicted during the steps, and a sample of the prefill
+        for b, h in pairs:
+            ev = range(int(lens[b]) - s.W, int(lens[b]) + steps - s.W)
+            check_records(s, cache, k, v, [(b, h)], np.random.default_rng(40 + li), nsamp=64, extra=ev)
+        for i in checked_steps:
+            q, out = L["outs"][i]
+            c = gc.host()
+            c.seq_lens = lens + i + 1
+            for b, h in pairs:  # the ring as it stood after step i
+                p = np.arange(int(c.seq_lens[b]) - s.W, int(c.seq_lens[b]))
+                pt = torch.from_numpy(p).cuda()
+                c.k_win[b, h, p % s.W] = k[b, h].index_select(0, pt).cpu().numpy()
+                c.v_win[b, h, p % s.W] = v[b, h].index_select(0, pt).cpu().numpy()
+            check_decode(s, c, q, out, None, pairs, f"layer {li} step {i}")

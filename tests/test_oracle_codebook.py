@@ -14,6 +14,7 @@ import pytest
 from scipy import integrate
 
 from oracle import codebook as cbm
+from oracle import codec
 from oracle import rotation as rot
 import tq_inputs
 
@@ -144,3 +145,50 @@ def test_unit_vector_mse_50k(golden, bits):
     uh = codec.dequantize(enc.codes, enc.norms, R, cb)
     mse = np.mean(np.sum((u - uh) ** 2, axis=1))
     assert abs(mse - printed) / printed < 0.03
+
+
+def test_half_storage_keeps_the_printed_distortion():
+    """The stored levels are rounded to half precision (a format choice the
+    pages leave open).  Against levels kept in float32, the Gaussian
+    distortion moves by under 1e-5 relative and still rounds to the README's
+    printed "Validated MSE" values."""
+    for bits, printed in ((2, 0.1175), (3, 0.0345), (4, 0.0095)):
+        dh = cbm.gaussian_distortion(cbm.Codebook(bits, 128, "half").centroids * math.sqrt(128))
+        ds = cbm.gaussian_distortion(cbm.Codebook(bits, 128, "single").centroids * math.sqrt(128))
+        assert abs(dh - ds) <= 1e-5 * ds, bits
+        assert round(dh, 4) == printed and round(ds, 4) == printed, bits
+
+
+def test_half_storage_quality_matches_single_storage():
+    """Same quality either way, at the config-0 shape (T = 1024, keys 3-bit +
+    QJL, values 4-bit, dense rotation, 256 queries): reconstruction MSE of
+    keys and values, logit RMSE and mean output error against exact FP
+    attention agree within 0.5% between half- and float32-stored levels.
+    (Exact outputs do differ beyond 1e-3: a level moved by its half-precision
+    rounding changes a few codes and, through the residual, the QJL signs,
+    and each sign flip moves the Gaussian-S correction by a large amount.)"""
+    d, T = 128, 1024
+    R = rot.Rotation("dense", tq_inputs.rotation_draws(0, d), d)
+    S = rot.qjl_matrix(tq_inputs.qjl_draws(0, d), d, "gaussian")
+    k = tq_inputs.fp16(tq_inputs.keys(0, d, np.arange(T))).astype(np.float64)
+    v = tq_inputs.fp16(tq_inputs.values(0, d, T)).astype(np.float64)
+    q = tq_inputs.queries(0, (256, d))
+
+    def attn(K, V):
+        l = (K @ q.T).T / math.sqrt(d)
+        w = np.exp(l - l.max(1, keepdims=True))
+        return l, (w @ V) / w.sum(1, keepdims=True)
+
+    le, oe = attn(k, v)
+    res = {}
+    for st in ("half", "single"):
+        kc, vc = cbm.Codebook(3, d, st), cbm.Codebook(4, d, st)
+        ek, ev = codec.encode(k, R, kc, S), codec.encode(v, R, vc)
+        K = codec.dequantize(ek.codes, ek.norms, R, kc, ek.signs, ek.rnorms, S, codec.qjl_scale(d))
+        V = codec.dequantize(ev.codes, ev.norms, R, vc)
+        l, o = attn(K, V)
+        res[st] = np.array([np.mean(np.sum((K - k) ** 2, 1) / np.sum(k ** 2, 1)),
+                            np.mean(np.sum((V - v) ** 2, 1) / np.sum(v ** 2, 1)),
+                            np.sqrt(np.mean((l - le) ** 2)),
+                            np.mean(np.linalg.norm(o - oe, axis=1) / np.linalg.norm(oe, axis=1))])
+    assert np.all(np.abs(res["half"] - res["single"]) <= 5e-3 * res["single"]), res

@@ -164,3 +164,30 @@ def test_attention_routes_agree(kmix, vmix, kb, vb):
     for b in range(2):
         for g in range(4):
             assert np.max(np.abs(l1[b][g] - l2[b][g])) <= 1e-12 * np.max(np.abs(l1[b][g]))
+
+
+@pytest.mark.parametrize("bits", [2, 3])
+@pytest.mark.parametrize("kind", ["key", "value"])
+def test_channel_choice_does_not_change_the_error(bits, kind):
+    """The page fixes only the counts (d/2 channels at each width).  Which
+    half takes the extra bit is this library's choice (the sets the
+    matrix-core scan reads as whole operand slices); after the rotation every
+    coordinate has the same distribution, so any fixed half gives the same
+    expected error.  Pinned: the library's set and the plain contiguous split
+    (coordinates d/2 .. d-1 high-rate) reach the same relative MSE within
+    Monte Carlo error on the same 20K rotated unit vectors."""
+    d = 128
+    x = np.random.default_rng(21).standard_normal((20_000, d))
+    u = x / np.linalg.norm(x, axis=1, keepdims=True)
+    R = rot.Rotation("dense", tq_inputs.rotation_draws(0, d), d)
+    errs = []
+    for contiguous in (False, True):
+        cb = mixed.MixedCodebook(bits, d, kind)
+        if contiguous:
+            cb.hi_mask = np.arange(d) >= d // 2
+            cb.lo_idx, cb.hi_idx = np.nonzero(~cb.hi_mask)[0], np.nonzero(cb.hi_mask)[0]
+        enc = codec.encode(u, R, cb)
+        uh = codec.dequantize(enc.codes, enc.norms, R, cb)
+        errs.append(np.sum((u - uh) ** 2, axis=1))
+    diff = errs[0] - errs[1]
+    assert abs(diff.mean()) < 4 * diff.std(ddof=1) / math.sqrt(len(diff)) + 1e-3 * errs[1].mean()
