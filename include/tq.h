@@ -86,6 +86,10 @@ enum { TQ_KIND_KEY = 0, TQ_KIND_VALUE = 1 };
  * instead of the matrix-core one (same results to the stated tolerance; kept
  * for measurement and cross-checking). */
 enum { TQ_FLAG_VALU_SCAN = 1 };
+/* Streams of the library's seeded generator (tq_seed_draws): the Gaussian
+ * matrix the dense rotation is built from, the QJL draws, and the draws whose
+ * signs are the Hadamard variant's Rademacher stage. */
+enum { TQ_DRAWS_ROTATION = 1, TQ_DRAWS_QJL = 2, TQ_DRAWS_HADAMARD = 3 };
 
 /* Bits of the device status word (tq_get_status). */
 enum {
@@ -105,7 +109,8 @@ typedef struct tq_params {
   int32_t page_tokens;  /* P, a multiple of 32, at most 1024 */
   int32_t window;       /* W, FP16 recent tokens per sequence, 0..1024 */
   int32_t flags;        /* TQ_FLAG_* bits, 0 for the default kernels */
-  uint64_t seed;        /* recorded in page headers (cache identity); draws come from the caller */
+  uint64_t seed;        /* recorded in page headers (cache identity); keys the library's generator
+                           when the caller gives no draws or tables */
   int32_t qjl_kind;     /* TQ_QJL_GAUSSIAN (the paper's S, coefficient sqrt(pi/2)/d) or
                            TQ_QJL_ORTHOGONAL (S = Haar orthogonal matrix from the same draws,
                            matched coefficient sqrt(pi/2)/sqrt(d)): "TurboQuant on a 16GB
@@ -129,35 +134,93 @@ typedef struct tq_params {
 
 typedef struct tq_ctx tq_ctx;
 
+/* Seeded draws ("aither-kvcache" README, "API Reference": a quantiser is
+ * built from head_dim, bits and a seed; "Algorithm" step 2: a fixed random
+ * orthogonal matrix; "TurboQuant on a 16GB MacBook", "The QJL detective
+ * story": a Gaussian QJL matrix).  Writes n N(0,1) values (host double[n]) of
+ * one stream (TQ_DRAWS_*) of the generator the library uses when a caller
+ * gives it only a seed: Philox4x32-10 (Salmon, Moraes, Dror and Shaw,
+ * "Parallel Random Numbers: As Easy as 1, 2, 3", SC 2011) with key (seed mod
+ * 2^32, seed / 2^32); draws 2j and 2j+1 come from the block with counter
+ * (j mod 2^32, j / 2^32, stream, 0), whose words w0..w3 give the uniforms
+ * u1 = ((w0 >> 5) 2^26 + (w1 >> 6)) 2^-53 and u2 likewise from w2, w3, and
+ * Box-Muller gives sqrt(-2 ln(1 - u1)) cos(2 pi u2), then ... sin(2 pi u2).
+ * Host only.  TQ_ERR_INVALID_ARG for a null out, n < 0 or an unknown stream. */
+TQ_API int tq_seed_draws(uint64_t seed, int stream, int64_t n, double* out);
+
 /* Host-only: compute the constant tables exactly as tq_codebook_init stores
- * them, without touching a GPU.  rot_draws: DENSE: d*d i.i.d. N(0,1) values
- * (row-major) whose QR Q factor, with the signs of diag(R) folded in, is the
- * rotation Pi (y = Pi x); HADAMARD: d values whose signs (x < 0 -> -1, else +1)
- * are the Rademacher stage.  qjl_draws: d*d N(0,1) values: the QJL matrix S
- * itself (TQ_QJL_GAUSSIAN; row i gives sign bit i) or the draws its Haar
- * orthogonal S is built from, like the dense rotation (TQ_QJL_ORTHOGONAL);
- * may be NULL when key_qjl == 0.
+ * them, without touching a GPU ("aither-kvcache" README, "Algorithm":
+ * rotation and precomputed Lloyd-Max codebooks; "TurboQuant Family Design
+ * Study", "Dense and structured transform comparison": the Rademacher-sign
+ * stage of the Hadamard variant; "TurboQuant on a 16GB MacBook", "The QJL
+ * detective story": Gaussian S, or the orthogonal S built by QR).
+ * rot_draws: DENSE: d*d i.i.d. N(0,1) values (row-major) whose QR Q factor,
+ * with the signs of diag(R) folded in, is the rotation Pi (y = Pi x);
+ * HADAMARD: d values whose signs (x < 0 -> -1, else +1) are the Rademacher
+ * stage.  qjl_draws: d*d N(0,1) values: the QJL matrix S itself
+ * (TQ_QJL_GAUSSIAN; row i gives sign bit i) or the draws its Haar orthogonal S
+ * is built from, like the dense rotation (TQ_QJL_ORTHOGONAL).  Either draw
+ * pointer may be NULL: the draws then come from the seeded generator
+ * (tq_seed_draws with params->seed; streams TQ_DRAWS_ROTATION or
+ * TQ_DRAWS_HADAMARD, and TQ_DRAWS_QJL).
  * Outputs (each nullable): rotation d*d f32 (DENSE: Pi row-major; HADAMARD:
  * the d signs), qjl d*d f32, key/value centroids 2^b f32 (Lloyd-Max levels of
  * N(0,1) times 1/sqrt(d), rounded to half-precision values), key/value
  * boundaries 2^b - 1 f32 (midpoints of the stored levels); with a
  * mixed-channel rate the b-bit arrays are followed by the (b+1)-bit ones
  * (2^b + 2^(b+1) centroids, 2^b - 1 + 2^(b+1) - 1 boundaries).
- * Returns TQ_ERR_INVALID_ARG for bad params or missing draws. */
+ * Returns TQ_ERR_INVALID_ARG for bad params. */
 TQ_API int tq_host_tables(const tq_params* params, const double* rot_draws, const double* qjl_draws,
                           float* rotation, float* qjl, float* key_centroids, float* key_boundaries,
                           float* value_centroids, float* value_boundaries);
 
-/* Build a context on the current HIP device: computes the tables above (host,
- * double precision, rounded to f32) and uploads them.  *out receives the
- * context, to be released with tq_destroy.  Host pointers; the stream is used
- * for the upload and synchronised before return. */
+/* Build a context on the current HIP device ("aither-kvcache" README, "API
+ * Reference": TurboQuant(head_dim, bits, seed) builds the quantiser once and
+ * is shared by encode and decode; "TurboQuant Family Design Study", "Paging,
+ * lifecycle, and cache identity": the seed and codebook version identify a
+ * cache): computes the tables of tq_host_tables (host, double precision,
+ * rounded to f32) from the given draws, or from params->seed where a draw
+ * pointer is NULL, and uploads them.  *out receives the context, to be
+ * released with tq_destroy.  Host pointers; the stream is used for the
+ * upload and synchronised before return.  TQ_ERR_INVALID_ARG for bad
+ * params, TQ_ERR_UNSUPPORTED for a parameter set without kernels, TQ_ERR_HIP
+ * if the device allocation or upload fails (nothing is left allocated). */
 TQ_API int tq_codebook_init(tq_ctx** out, const tq_params* params, const double* rot_draws,
                             const double* qjl_draws, void* stream);
 
+/* Finished tables given as data (host f32 arrays, read during the call). */
+typedef struct tq_tables {
+  const float* rotation;        /* DENSE: Pi, d*d row-major (y = Pi x); HADAMARD: d signs, each +1 or -1 */
+  const float* qjl;             /* S as used, d*d row-major (sign bit i from row i); ignored without QJL */
+  const float* key_centroids;   /* 2^bK ascending levels (2^bK then 2^(bK+1) for a mixed key rate) */
+  const float* value_centroids; /* likewise for values */
+} tq_tables;
+
+/* Build a context from tables given as data ("aither-kvcache" README, "API
+ * Reference" and "Algorithm": the quantiser is a rotation, a QJL matrix and
+ * precomputed codebooks; a caller that already holds them, for instance to
+ * decode a cache written elsewhere ("TurboQuant Family Design Study",
+ * "Paging, lifecycle, and cache identity"), passes them in).  Every member of
+ * *tables, and tables itself, may be NULL: what is missing is built from
+ * params->seed as tq_codebook_init does without draws.  Levels are stored
+ * rounded to half precision and the decision boundaries are the midpoints
+ * of the stored levels; the rotation and S are used as given (their
+ * orthogonality is the caller's responsibility).  TQ_ERR_INVALID_ARG for bad
+ * params, a non-finite table entry, a Hadamard sign other than +-1 or levels
+ * that are not strictly increasing once rounded; otherwise as
+ * tq_codebook_init. */
+TQ_API int tq_codebook_init_tables(tq_ctx** out, const tq_params* params, const tq_tables* tables, void* stream);
+
+/* Release a context and its device tables ("aither-kvcache" README, "API
+ * Reference": the quantiser object's lifetime).  TQ_ERR_INVALID_ARG for
+ * NULL, TQ_ERR_HIP if freeing the device memory fails (the context is
+ * released either way). */
 TQ_API int tq_destroy(tq_ctx* ctx);
 
-/* Bytes of one page for these params (see the page format above); <0 on bad params. */
+/* Bytes of one page for these params ("TurboQuant Family Design Study",
+ * "Packed format and complete bit accounting": fixed-size pages with a
+ * 64-byte header, 16-byte aligned streams; the layout is given at the top of
+ * this file); TQ_ERR_INVALID_ARG on bad params. */
 TQ_API int64_t tq_page_bytes(const tq_params* params);
 
 /* Dequantise n flat records (device pointers) back to vectors ("aither-
@@ -172,18 +235,28 @@ TQ_API int64_t tq_page_bytes(const tq_params* params);
 TQ_API int tq_decode(const tq_ctx* ctx, int kind, const uint8_t* codes, const uint8_t* signs, const float* norms,
                      const float* rnorms, int64_t n, float* out, void* stream);
 
-/* Encode n vectors (device pointers) into flat records:
+/* Encode n vectors (device pointers) into flat records ("aither-kvcache"
+ * README, "Algorithm": norm, rotation, Lloyd-Max codes, LSB-first packing;
+ * "TurboQuant on a 16GB MacBook", "Why this caught my eye": the keys' 1-bit
+ * QJL sketch of the residual, with the residual's norm):
  *   x: [n][row_stride] elements of dtype (F16, BF16 or F32), first d used;
  *   codes: [n][d*b/8] u8 LSB-first, b = key_bits or value_bits by kind
  *   ([n][d*b/8 + d/16] for a mixed-channel rate, layout as in the page);
  *   norms: [n] f32 L2 norms (keys with key_norm_u8: the u8 log-norm level each norm is
  *   stored as, 2^(q/16 - 4) or 0, against which the key's QJL residual is taken);
  *   signs: [n][d/8] u8 and rnorms: [n] f32, required iff kind == KEY and key_qjl.
- * A vector with zero norm gets all-zero codes, signs and rnorm. */
+ * A vector with zero norm gets all-zero codes, signs and rnorm ("TurboQuant
+ * on a 16GB MacBook", "Round 2: the llama.cpp bug hunt": the zero-block fix).
+ * TQ_ERR_INVALID_ARG for null or misaligned pointers (x to its element size,
+ * the outputs to 4 bytes) or row_stride < d; TQ_ERR_HIP if a launch fails. */
 TQ_API int tq_encode(const tq_ctx* ctx, int kind, const void* x, int dtype, int64_t n, int64_t row_stride,
                      uint8_t* codes, uint8_t* signs, float* norms, float* rnorms, void* stream);
 
-/* Append new tokens to every sequence of one layer's cache (device pointers).
+/* Append new tokens to every sequence of one layer's cache (device
+ * pointers; "TurboQuant Family Design Study", "Paging, lifecycle, and cache
+ * identity": token-order append into fixed pages reserved by the caller,
+ * rollback of an append that fails; "Packed format and complete bit
+ * accounting": the recent-token FP16 window).
  *   page_pool: num_pages * tq_page_bytes bytes; block_table: [batch][max_pages] page ids;
  *   seq_lens: [batch] tokens held so far, advanced by this call;
  *   k_new, v_new: [batch][H_kv][n_new][d] fp16 (bit patterns as uint16);
@@ -194,16 +267,27 @@ TQ_API int tq_encode(const tq_ctx* ctx, int kind, const void* x, int dtype, int6
  * tokens still inside the window go to the ring, and seq_lens[b] grows by its
  * count.  The caller reserves pages: every page a token lands in must be a valid
  * id in block_table.  A sequence whose pages or count are invalid is left
- * unchanged and raises a status bit (tq_get_status). */
+ * unchanged and raises a status bit (tq_get_status).  TQ_ERR_INVALID_ARG
+ * for null or misaligned pointers (pool 256 bytes, token rows and rings 16
+ * bytes) or negative sizes; TQ_ERR_HIP if a launch fails. */
 TQ_API int tq_append_page(const tq_ctx* ctx, uint8_t* page_pool, int64_t num_pages, const int32_t* block_table,
                           int max_pages, int batch, int32_t* seq_lens, const uint16_t* k_new,
                           const uint16_t* v_new, int n_new, const int32_t* new_counts, uint16_t* k_win,
                           uint16_t* v_win, void* stream);
 
-/* Workspace bytes tq_decode_attn needs for this batch and block-table width. */
+/* Workspace bytes tq_decode_attn needs for this batch, block-table width
+ * and split size (rotated queries and the split partials of the online
+ * softmax, "TurboQuant Family Design Study", "CPU and WASM kernel design");
+ * TQ_ERR_INVALID_ARG for negative sizes. */
 TQ_API int64_t tq_decode_workspace_bytes(const tq_ctx* ctx, int batch, int max_pages, int pages_per_split);
 
-/* Decode attention for one query token per sequence (device pointers).
+/* Decode attention for one query token per sequence (device pointers;
+ * "TurboQuant Family Design Study", "Placement relative to RoPE and
+ * attention": the query goes through the same transform so q.k = (Tq).(Tk),
+ * and "CPU and WASM kernel design": packed keys scored in the compressed
+ * domain, values accumulated in the rotated basis, one inverse transform per
+ * head; "TurboQuant on a 16GB MacBook", "The QJL detective story": the QJL
+ * correction at scale sqrt(pi/2)/d).
  *   q: [batch][H_q][d] post-RoPE queries, dtype F16, BF16 or F32;
  *   cache arguments as in tq_append_page (seq_lens[b] tokens, at most
  *   max_pages * P + W);
@@ -216,7 +300,11 @@ TQ_API int64_t tq_decode_workspace_bytes(const tq_ctx* ctx, int batch, int max_p
  *   device holds at once (the fewest rounds of resident work-groups, each
  *   work-group as long as possible);
  *   dbg_logits: NULL, or [batch][H_q][logits_stride] f32 receiving each token's
- *   logit q.k*sm_scale at its position index (for tests). */
+ *   logit q.k*sm_scale at its position index (for tests).
+ * TQ_ERR_INVALID_ARG for null or misaligned pointers (pool and workspace 256
+ * bytes, out 16, q 8 or 16) or a non-finite sm_scale, TQ_ERR_WORKSPACE for a
+ * workspace below tq_decode_workspace_bytes, TQ_ERR_HIP if a launch fails;
+ * invalid page ids met on the device set a status bit (tq_get_status). */
 TQ_API int tq_decode_attn(const tq_ctx* ctx, const void* q, int q_dtype, const uint8_t* page_pool, int64_t num_pages,
                           const int32_t* block_table, int max_pages, int batch, const int32_t* seq_lens,
                           const uint16_t* k_win, const uint16_t* v_win, float sm_scale, float* out,
@@ -245,10 +333,14 @@ TQ_API int tq_profile_end(tq_ctx* ctx, double* scan_ms_total, int* calls);
  * arguments, TQ_ERR_HIP if a launch or an event fails. */
 TQ_API int tq_read_probe(const void* buf, int64_t bytes, uint32_t* sink, int reps, double* best_ms, void* stream);
 
-/* Read and clear the device status word (synchronises the context's device). */
+/* Read and clear the device status word (synchronises the context's device):
+ * the device-side error report of appends and decodes ("TurboQuant Family
+ * Design Study", "Paging, lifecycle, and cache identity": an append that
+ * cannot complete leaves its sequence unchanged).  TQ_ERR_HIP if the read
+ * fails. */
 TQ_API int tq_get_status(tq_ctx* ctx, int* code);
 
-/* Text for a TQ_ERR_* code. */
+/* Text for a TQ_ERR_* code (the library's own error convention). */
 TQ_API const char* tq_strerror(int err);
 
 #ifdef __cplusplus

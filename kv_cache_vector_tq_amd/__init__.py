@@ -25,11 +25,13 @@ TQ_DTYPE_F16, TQ_DTYPE_BF16, TQ_DTYPE_F32 = 0, 1, 2
 TQ_KIND_KEY, TQ_KIND_VALUE = 0, 1
 TQ_STATUS_BAD_PAGE, TQ_STATUS_BAD_COUNT = 1, 2
 TQ_FLAG_VALU_SCAN = 1
+TQ_DRAWS_ROTATION, TQ_DRAWS_QJL, TQ_DRAWS_HADAMARD = 1, 2, 3
 
 EXPORTED = [
     "tq_host_tables", "tq_codebook_init", "tq_destroy", "tq_page_bytes", "tq_encode",
     "tq_append_page", "tq_decode_workspace_bytes", "tq_decode_attn", "tq_get_status", "tq_strerror",
-    "tq_profile_begin", "tq_profile_end", "tq_decode", "tq_read_probe",
+    "tq_profile_begin", "tq_profile_end", "tq_decode", "tq_read_probe", "tq_seed_draws",
+    "tq_codebook_init_tables",
 ]
 
 
@@ -48,6 +50,11 @@ class tq_params(ctypes.Structure):
         ("qjl_shrink", ctypes.c_float), ("key_mixed", ctypes.c_int32), ("value_mixed", ctypes.c_int32),
         ("key_norm_u8", ctypes.c_int32),
     ]
+
+
+class tq_tables(ctypes.Structure):
+    _fields_ = [("rotation", ctypes.c_void_p), ("qjl", ctypes.c_void_p), ("key_centroids", ctypes.c_void_p),
+                ("value_centroids", ctypes.c_void_p)]
 
 
 def make_params(head_dim=128, key_bits=3, key_qjl=1, value_bits=4, rotation=TQ_ROT_DENSE, num_q_heads=1,
@@ -91,6 +98,8 @@ def lib():
         "tq_profile_begin": (i32, [P, i32]),
         "tq_profile_end": (i32, [P, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int)]),
         "tq_read_probe": (i32, [P, i64, P, i32, ctypes.POINTER(ctypes.c_double), P]),
+        "tq_seed_draws": (i32, [ctypes.c_uint64, i32, i64, P]),
+        "tq_codebook_init_tables": (i32, [ctypes.POINTER(P), pp, ctypes.POINTER(tq_tables), P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(L, name)
@@ -138,11 +147,20 @@ def _dtype_code(t):
     return _DT[t.dtype]
 
 
-def tq_host_tables(params, rot_draws, qjl_draws=None):
-    """Library-side tables computed on the host (no GPU): dict of numpy arrays."""
+def tq_seed_draws(seed, stream, n):
+    """n N(0,1) draws of one stream of the library's seeded generator (host)."""
+    out = np.zeros(n, np.float64)
+    _check(lib().tq_seed_draws(int(seed), int(stream), int(n), _ptr(out)), "tq_seed_draws")
+    return out
+
+
+def tq_host_tables(params, rot_draws=None, qjl_draws=None, qjl=True):
+    """Library-side tables computed on the host (no GPU): dict of numpy arrays.
+    Draws left as None come from the library's seeded generator (the QJL
+    matrix only when ``qjl``)."""
     d = params.head_dim
     rot = np.zeros(d * d if params.rotation == TQ_ROT_DENSE else d, np.float32)
-    S = np.zeros(d * d, np.float32) if qjl_draws is not None else None
+    S = np.zeros(d * d, np.float32) if (qjl_draws is not None or qjl) else None
     # a mixed-channel rate appends the (b+1)-bit codebook to the b-bit one
     nk = (1 << params.key_bits) * (3 if params.key_mixed else 1)
     nv = (1 << params.value_bits) * (3 if params.value_mixed else 1)
@@ -150,7 +168,7 @@ def tq_host_tables(params, rot_draws, qjl_draws=None):
     kb = np.zeros(nk - (2 if params.key_mixed else 1), np.float32)
     vc = np.zeros(nv, np.float32)
     vb = np.zeros(nv - (2 if params.value_mixed else 1), np.float32)
-    rd = np.ascontiguousarray(rot_draws, dtype=np.float64)
+    rd = None if rot_draws is None else np.ascontiguousarray(rot_draws, dtype=np.float64)
     qd = None if qjl_draws is None else np.ascontiguousarray(qjl_draws, dtype=np.float64)
     rc = lib().tq_host_tables(ctypes.byref(params), _ptr(rd), _ptr(qd), _ptr(rot), _ptr(S),
                               _ptr(kc), _ptr(kb), _ptr(vc), _ptr(vb))
@@ -168,15 +186,26 @@ def tq_page_bytes(params):
 
 
 class Context:
-    """Owns a tq_ctx (constant tables on the current device)."""
+    """Owns a tq_ctx (constant tables on the current device).  Built from
+    draws (None: the library's seeded generator) or, with ``tables``, from
+    finished tables given as data (a dict with any of "rotation", "qjl",
+    "key_centroids", "value_centroids"; missing ones come from the seed)."""
 
-    def __init__(self, params, rot_draws, qjl_draws=None, stream=None):
+    def __init__(self, params, rot_draws=None, qjl_draws=None, stream=None, tables=None):
         self.params = params
         self._h = ctypes.c_void_p()
-        rd = np.ascontiguousarray(rot_draws, dtype=np.float64)
-        qd = None if qjl_draws is None else np.ascontiguousarray(qjl_draws, dtype=np.float64)
-        rc = lib().tq_codebook_init(ctypes.byref(self._h), ctypes.byref(params), _ptr(rd), _ptr(qd), _stream(stream))
-        _check(rc, "tq_codebook_init")
+        if tables is None:
+            rd = None if rot_draws is None else np.ascontiguousarray(rot_draws, dtype=np.float64)
+            qd = None if qjl_draws is None else np.ascontiguousarray(qjl_draws, dtype=np.float64)
+            rc = lib().tq_codebook_init(ctypes.byref(self._h), ctypes.byref(params), _ptr(rd), _ptr(qd),
+                                        _stream(stream))
+            _check(rc, "tq_codebook_init")
+            return
+        keep = {k: np.ascontiguousarray(v, dtype=np.float32) for k, v in tables.items() if v is not None}
+        t = tq_tables(*[_ptr(keep.get(k)) for k in ("rotation", "qjl", "key_centroids", "value_centroids")])
+        rc = lib().tq_codebook_init_tables(ctypes.byref(self._h), ctypes.byref(params), ctypes.byref(t),
+                                           _stream(stream))
+        _check(rc, "tq_codebook_init_tables")
 
     @property
     def handle(self):
@@ -194,8 +223,12 @@ class Context:
             pass
 
 
-def tq_codebook_init(params, rot_draws, qjl_draws=None, stream=None):
+def tq_codebook_init(params, rot_draws=None, qjl_draws=None, stream=None):
     return Context(params, rot_draws, qjl_draws, stream)
+
+
+def tq_codebook_init_tables(params, tables=None, stream=None):
+    return Context(params, stream=stream, tables=tables or {})
 
 
 def tq_encode(ctx, kind, x, codes, norms, signs=None, rnorms=None, stream=None):

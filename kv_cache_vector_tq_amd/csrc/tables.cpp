@@ -13,6 +13,10 @@
 // Rotation: a fixed random orthogonal matrix (README "Algorithm" step 2); the
 // Q factor of a Gaussian matrix with the signs of diag(R) folded in is Haar
 // distributed.
+// Seeded draws: when the caller passes no draws, the Gaussian matrices come
+// from the counter-based generator Philox4x32-10 (Salmon, Moraes, Dror and
+// Shaw, "Parallel Random Numbers: As Easy as 1, 2, 3", SC 2011) keyed by the
+// seed, turned into normals by the Box-Muller transform.
 #include <cmath>
 #include <cstring>
 #include <vector>
@@ -64,6 +68,57 @@ std::vector<double> lloyd_max_normal(int bits) {
     out[half - 1 - k] = -pos[k];
   }
   return out;
+}
+
+namespace {
+
+// One Philox4x32 round: two 32x32 -> 64-bit products, the counter words
+// permuted and mixed with the key.
+inline void philox_round(uint32_t c[4], const uint32_t k[2]) {
+  const uint64_t p0 = static_cast<uint64_t>(0xD2511F53u) * c[0];
+  const uint64_t p1 = static_cast<uint64_t>(0xCD9E8D57u) * c[2];
+  const uint32_t hi0 = static_cast<uint32_t>(p0 >> 32), lo0 = static_cast<uint32_t>(p0);
+  const uint32_t hi1 = static_cast<uint32_t>(p1 >> 32), lo1 = static_cast<uint32_t>(p1);
+  const uint32_t n0 = hi1 ^ c[1] ^ k[0], n2 = hi0 ^ c[3] ^ k[1];
+  c[0] = n0;
+  c[1] = lo1;
+  c[2] = n2;
+  c[3] = lo0;
+}
+
+}  // namespace
+
+void philox4x32_10(uint32_t ctr[4], const uint32_t key[2]) {
+  uint32_t k[2] = {key[0], key[1]};
+  for (int r = 0; r < 10; ++r) {
+    if (r > 0) {  // key schedule: Weyl increments (golden ratio, sqrt(3) - 1)
+      k[0] += 0x9E3779B9u;
+      k[1] += 0xBB67AE85u;
+    }
+    philox_round(ctr, k);
+  }
+}
+
+// Draws 2j and 2j+1 of stream `stream` come from Philox block j: counter
+// (j mod 2^32, j / 2^32, stream, 0), key (seed mod 2^32, seed / 2^32).  Its
+// words give two 53-bit uniforms u1 = (w0 >> 5, w1 >> 6), u2 = (w2 >> 5,
+// w3 >> 6) in [0, 1), and Box-Muller gives sqrt(-2 ln(1 - u1)) cos(2 pi u2)
+// and sqrt(-2 ln(1 - u1)) sin(2 pi u2).
+void seed_normals(uint64_t seed, int stream, int64_t n, double* out) {
+  const uint32_t key[2] = {static_cast<uint32_t>(seed), static_cast<uint32_t>(seed >> 32)};
+  const double two_pi = 6.283185307179586;
+  for (int64_t j = 0; 2 * j < n; ++j) {
+    uint32_t c[4] = {static_cast<uint32_t>(j), static_cast<uint32_t>(static_cast<uint64_t>(j) >> 32),
+                     static_cast<uint32_t>(stream), 0u};
+    philox4x32_10(c, key);
+    const double u1 = (static_cast<double>(c[0] >> 5) * 67108864.0 + static_cast<double>(c[1] >> 6)) *
+                      (1.0 / 9007199254740992.0);
+    const double u2 = (static_cast<double>(c[2] >> 5) * 67108864.0 + static_cast<double>(c[3] >> 6)) *
+                      (1.0 / 9007199254740992.0);
+    const double rad = std::sqrt(-2.0 * std::log(1.0 - u1));
+    out[2 * j] = rad * std::cos(two_pi * u2);
+    if (2 * j + 1 < n) out[2 * j + 1] = rad * std::sin(two_pi * u2);
+  }
 }
 
 void codebook_f32(int bits, int d, float* centroids, float* boundaries) {

@@ -123,12 +123,32 @@ TQ_API int64_t tq_page_bytes(const tq_params* p) {
   return tq::make_layout(*p).page_bytes;
 }
 
+TQ_API int tq_seed_draws(uint64_t seed, int stream, int64_t n, double* out) {
+  if (!out || n < 0 || n > (int64_t(1) << 40)) return TQ_ERR_INVALID_ARG;
+  if (stream != TQ_DRAWS_ROTATION && stream != TQ_DRAWS_QJL && stream != TQ_DRAWS_HADAMARD)
+    return TQ_ERR_INVALID_ARG;
+  tq::seed_normals(seed, stream, n, out);
+  return TQ_OK;
+}
+
 TQ_API int tq_host_tables(const tq_params* p, const double* rot_draws, const double* qjl_draws, float* rotation,
                           float* qjl, float* key_centroids, float* key_boundaries, float* value_centroids,
                           float* value_boundaries) {
-  if (!params_ok(p) || !rot_draws) return TQ_ERR_INVALID_ARG;
-  if (p->key_qjl && !qjl_draws && qjl) return TQ_ERR_INVALID_ARG;
+  if (!params_ok(p)) return TQ_ERR_INVALID_ARG;
   const int d = p->head_dim;
+  // draws not given: the seeded generator's streams
+  std::vector<double> gen_rot, gen_qjl;
+  if (!rot_draws && rotation) {
+    gen_rot.resize(p->rotation == TQ_ROT_DENSE ? static_cast<size_t>(d) * d : d);
+    tq::seed_normals(p->seed, p->rotation == TQ_ROT_DENSE ? TQ_DRAWS_ROTATION : TQ_DRAWS_HADAMARD,
+                     static_cast<int64_t>(gen_rot.size()), gen_rot.data());
+    rot_draws = gen_rot.data();
+  }
+  if (!qjl_draws && qjl) {
+    gen_qjl.resize(static_cast<size_t>(d) * d);
+    tq::seed_normals(p->seed, TQ_DRAWS_QJL, static_cast<int64_t>(gen_qjl.size()), gen_qjl.data());
+    qjl_draws = gen_qjl.data();
+  }
   if (rotation) {
     if (p->rotation == TQ_ROT_DENSE) {
       tq::haar_rotation_f32(rot_draws, d, rotation);
@@ -137,7 +157,6 @@ TQ_API int tq_host_tables(const tq_params* p, const double* rot_draws, const dou
     }
   }
   if (qjl) {
-    if (!qjl_draws) return TQ_ERR_INVALID_ARG;
     if (p->qjl_kind == TQ_QJL_ORTHOGONAL)
       tq::haar_rotation_f32(qjl_draws, d, qjl);  // Haar orthogonal S from the draws
     else
@@ -156,11 +175,37 @@ TQ_API int tq_host_tables(const tq_params* p, const double* rot_draws, const dou
   return TQ_OK;
 }
 
-TQ_API int tq_codebook_init(tq_ctx** out, const tq_params* p, const double* rot_draws, const double* qjl_draws,
-                            void* stream) {
-  if (!out || !params_ok(p) || !rot_draws) return TQ_ERR_INVALID_ARG;
-  if (p->key_qjl && !qjl_draws) return TQ_ERR_INVALID_ARG;
-  if (!params_supported(p)) return TQ_ERR_UNSUPPORTED;
+}  // extern "C"
+
+namespace {
+
+// Caller-given levels of one kind, rounded to the stored half-precision
+// values, with the boundaries between them (midpoints, float32); 2^b levels,
+// or 2^b then 2^(b+1) for a mixed rate (two ascending runs).  False for a
+// non-finite level or a run that is not strictly increasing once rounded.
+bool caller_codebook(const float* cen, int bits, bool mixed, float* c, float* bnd) {
+  int off = 0, boff = 0;
+  for (int part = 0; part < (mixed ? 2 : 1); ++part) {
+    const int L = 1 << (bits + part);
+    for (int k = 0; k < L; ++k) {
+      if (!std::isfinite(cen[off + k])) return false;
+      c[off + k] = static_cast<float>(static_cast<_Float16>(cen[off + k]));
+      if (k > 0 && !(c[off + k] > c[off + k - 1])) return false;
+    }
+    for (int k = 0; k + 1 < L; ++k)
+      bnd[boff + k] =
+          static_cast<float>(0.5 * (static_cast<double>(c[off + k]) + static_cast<double>(c[off + k + 1])));
+    off += L;
+    boff += L - 1;
+  }
+  return true;
+}
+
+// A context from finished tables: the rotation (Pi row-major, or the
+// Hadamard signs), the QJL matrix S as used (ignored without QJL) and the
+// codebooks with their boundaries, laid out as tq_host_tables writes them.
+int init_ctx(tq_ctx** out, const tq_params* p, const float* rot_in, const float* S_in, const float* kc,
+             const float* kb, const float* vc, const float* vb, void* stream) {
   *out = nullptr;
   const int d = p->head_dim;
   tq_ctx* c = new (std::nothrow) tq_ctx();
@@ -168,14 +213,9 @@ TQ_API int tq_codebook_init(tq_ctx** out, const tq_params* p, const double* rot_
   c->p = *p;
   c->lay = tq::make_layout(*p);
   std::vector<float> rot(d * d, 0.0f), rotT(d * d, 0.0f), S(d * d, 0.0f), ST(d * d, 0.0f);
+  std::memcpy(rot.data(), rot_in, (p->rotation == TQ_ROT_DENSE ? d * d : d) * sizeof(float));
+  if (p->key_qjl) std::memcpy(S.data(), S_in, d * d * sizeof(float));
   std::memset(&c->cb, 0, sizeof(c->cb));
-  float kc[48] = {}, kb[48] = {}, vc[48] = {}, vb[48] = {};
-  int rc = tq_host_tables(p, rot_draws, p->key_qjl ? qjl_draws : nullptr, rot.data(),
-                          p->key_qjl ? S.data() : nullptr, kc, kb, vc, vb);
-  if (rc != TQ_OK) {
-    delete c;
-    return rc;
-  }
   const int nk = 1 << p->key_bits, nv = 1 << p->value_bits;
   std::memcpy(c->cb.kc, kc, nk * sizeof(float));
   std::memcpy(c->cb.kb, kb, (nk - 1) * sizeof(float));
@@ -264,6 +304,59 @@ TQ_API int tq_codebook_init(tq_ctx** out, const tq_params* p, const double* rot_
   c->scan_slots = (per_cu > 0 ? per_cu : 1) * (cus > 0 ? cus : 1);
   *out = c;
   return TQ_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+TQ_API int tq_codebook_init(tq_ctx** out, const tq_params* p, const double* rot_draws, const double* qjl_draws,
+                            void* stream) {
+  if (!out || !params_ok(p)) return TQ_ERR_INVALID_ARG;
+  if (!params_supported(p)) return TQ_ERR_UNSUPPORTED;
+  *out = nullptr;
+  const int d = p->head_dim;
+  std::vector<float> rot(d * d, 0.0f), S(d * d, 0.0f);
+  float kc[48] = {}, kb[48] = {}, vc[48] = {}, vb[48] = {};
+  const int rc =
+      tq_host_tables(p, rot_draws, qjl_draws, rot.data(), p->key_qjl ? S.data() : nullptr, kc, kb, vc, vb);
+  if (rc != TQ_OK) return rc;
+  return init_ctx(out, p, rot.data(), S.data(), kc, kb, vc, vb, stream);
+}
+
+TQ_API int tq_codebook_init_tables(tq_ctx** out, const tq_params* p, const tq_tables* tables, void* stream) {
+  if (!out || !params_ok(p)) return TQ_ERR_INVALID_ARG;
+  if (!params_supported(p)) return TQ_ERR_UNSUPPORTED;
+  *out = nullptr;
+  const int d = p->head_dim;
+  const tq_tables none = {nullptr, nullptr, nullptr, nullptr};
+  const tq_tables& t = tables ? *tables : none;
+  // the seeded tables for whatever the caller leaves out
+  std::vector<float> rot(d * d, 0.0f), S(d * d, 0.0f);
+  float kc[48] = {}, kb[48] = {}, vc[48] = {}, vb[48] = {};
+  const int rc = tq_host_tables(p, nullptr, nullptr, t.rotation ? nullptr : rot.data(),
+                                (p->key_qjl && !t.qjl) ? S.data() : nullptr, kc, kb, vc, vb);
+  if (rc != TQ_OK) return rc;
+  if (t.rotation) {
+    const int n = p->rotation == TQ_ROT_DENSE ? d * d : d;
+    for (int i = 0; i < n; ++i) {
+      const float v = t.rotation[i];
+      if (!std::isfinite(v) || (p->rotation == TQ_ROT_HADAMARD && v != 1.0f && v != -1.0f))
+        return TQ_ERR_INVALID_ARG;
+      rot[i] = v;
+    }
+  }
+  if (p->key_qjl && t.qjl) {
+    for (int i = 0; i < d * d; ++i) {
+      if (!std::isfinite(t.qjl[i])) return TQ_ERR_INVALID_ARG;
+      S[i] = t.qjl[i];
+    }
+  }
+  if (t.key_centroids && !caller_codebook(t.key_centroids, p->key_bits, p->key_mixed != 0, kc, kb))
+    return TQ_ERR_INVALID_ARG;
+  if (t.value_centroids && !caller_codebook(t.value_centroids, p->value_bits, p->value_mixed != 0, vc, vb))
+    return TQ_ERR_INVALID_ARG;
+  return init_ctx(out, p, rot.data(), S.data(), kc, kb, vc, vb, stream);
 }
 
 TQ_API int tq_destroy(tq_ctx* c) {

@@ -35,6 +35,10 @@ __host__ __device__ inline int norm_code(float n, const float* nb) {
 std::vector<double> lloyd_max_normal(int bits);
 void codebook_f32(int bits, int d, float* centroids, float* boundaries);
 void haar_rotation_f32(const double* g, int d, float* out);
+// Philox4x32-10 block function (in place on the counter) and the seeded
+// N(0,1) draws built on it (stream: TQ_DRAWS_*).
+void philox4x32_10(uint32_t ctr[4], const uint32_t key[2]);
+void seed_normals(uint64_t seed, int stream, int64_t n, double* out);
 
 // Byte offsets of one head's streams inside its head block, and page sizes.
 // kmix / vmix: mixed-channel rate b + 1/2 (half the coordinates at b + 1 bits).

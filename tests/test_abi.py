@@ -76,9 +76,7 @@ def test_null_context_and_pointers(L):
         tqa.TQ_ERR_INVALID_ARG
     assert L.tq_destroy(None) == tqa.TQ_ERR_INVALID_ARG
     assert L.tq_decode_workspace_bytes(None, 1, 1, 0) == tqa.TQ_ERR_INVALID_ARG
-    p = tqa.make_params()
-    assert L.tq_host_tables(ctypes.byref(p), None, None, None, None, None, None, None, None) == \
-        tqa.TQ_ERR_INVALID_ARG
+    assert L.tq_host_tables(None, None, None, None, None, None, None, None, None) == tqa.TQ_ERR_INVALID_ARG
     assert L.tq_strerror(tqa.TQ_ERR_WORKSPACE) == b"workspace too small"
 
 
