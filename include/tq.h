@@ -90,6 +90,9 @@ enum { TQ_FLAG_VALU_SCAN = 1 };
  * matrix the dense rotation is built from, the QJL draws, and the draws whose
  * signs are the Hadamard variant's Rademacher stage. */
 enum { TQ_DRAWS_ROTATION = 1, TQ_DRAWS_QJL = 2, TQ_DRAWS_HADAMARD = 3 };
+/* Size of the static device scratch tq_decode_attn_noalloc works in (32 MiB
+ * per device). */
+#define TQ_NOALLOC_SCRATCH_BYTES (32u << 20)
 
 /* Bits of the device status word (tq_get_status). */
 enum {
@@ -310,6 +313,23 @@ TQ_API int tq_decode_attn(const tq_ctx* ctx, const void* q, int q_dtype, const u
                           const uint16_t* k_win, const uint16_t* v_win, float sm_scale, float* out,
                           void* workspace, size_t workspace_bytes, int pages_per_split, float* dbg_logits,
                           int64_t logits_stride, void* stream);
+
+/* tq_decode_attn for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid allocation):
+ * the same computation and kernels, with the workspace taken from a static
+ * device array of TQ_NOALLOC_SCRATCH_BYTES that the library holds on each
+ * device it runs on until the process ends (its address is looked up once
+ * per device, at tq_codebook_init).  The caller passes inputs and outputs as
+ * for tq_decode_attn; no logits are captured.  Allocates nothing.  Calls on
+ * one device share the array and keep nothing from one call to the next
+ * (every word a call reads, it has written): calls that overlap on one device,
+ * from different streams or threads, race and must not be made.
+ * TQ_ERR_WORKSPACE when tq_decode_workspace_bytes for these sizes exceeds
+ * TQ_NOALLOC_SCRATCH_BYTES; otherwise the errors of tq_decode_attn. */
+TQ_API int tq_decode_attn_noalloc(const tq_ctx* ctx, const void* q, int q_dtype, const uint8_t* page_pool,
+                                  int64_t num_pages, const int32_t* block_table, int max_pages, int batch,
+                                  const int32_t* seq_lens, const uint16_t* k_win, const uint16_t* v_win,
+                                  float sm_scale, float* out, int pages_per_split, void* stream);
 
 /* Kernel timing for measurement.  tq_profile_begin(ctx, n) arms the context:
  * the next n tq_decode_attn calls record a pair of HIP events on their stream

@@ -26,12 +26,13 @@ TQ_KIND_KEY, TQ_KIND_VALUE = 0, 1
 TQ_STATUS_BAD_PAGE, TQ_STATUS_BAD_COUNT = 1, 2
 TQ_FLAG_VALU_SCAN = 1
 TQ_DRAWS_ROTATION, TQ_DRAWS_QJL, TQ_DRAWS_HADAMARD = 1, 2, 3
+TQ_NOALLOC_SCRATCH_BYTES = 32 << 20
 
 EXPORTED = [
     "tq_host_tables", "tq_codebook_init", "tq_destroy", "tq_page_bytes", "tq_encode",
     "tq_append_page", "tq_decode_workspace_bytes", "tq_decode_attn", "tq_get_status", "tq_strerror",
     "tq_profile_begin", "tq_profile_end", "tq_decode", "tq_read_probe", "tq_seed_draws",
-    "tq_codebook_init_tables",
+    "tq_codebook_init_tables", "tq_decode_attn_noalloc",
 ]
 
 
@@ -100,6 +101,7 @@ def lib():
         "tq_read_probe": (i32, [P, i64, P, i32, ctypes.POINTER(ctypes.c_double), P]),
         "tq_seed_draws": (i32, [ctypes.c_uint64, i32, i64, P]),
         "tq_codebook_init_tables": (i32, [ctypes.POINTER(P), pp, ctypes.POINTER(tq_tables), P]),
+        "tq_decode_attn_noalloc": (i32, [P, P, i32, P, i64, P, i32, i32, P, P, P, f32, P, i32, P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(L, name)
@@ -279,6 +281,18 @@ def tq_decode_attn(ctx, q, page_pool, block_table, seq_lens, k_win, v_win, out, 
                               _ptr(out), _ptr(workspace), workspace.numel() * workspace.element_size(),
                               pages_per_split, _ptr(dbg_logits), stride, _stream(stream))
     _check(rc, "tq_decode_attn")
+
+
+def tq_decode_attn_noalloc(ctx, q, page_pool, block_table, seq_lens, k_win, v_win, out, sm_scale,
+                           pages_per_split=0, num_pages=None, stream=None):
+    """tq_decode_attn with the library's static device scratch as workspace
+    (no allocation)."""
+    B = q.shape[0]
+    npg = num_pages if num_pages is not None else page_pool.numel() // tq_page_bytes(ctx.params)
+    rc = lib().tq_decode_attn_noalloc(ctx.handle, _ptr(q), _dtype_code(q), _ptr(page_pool), npg, _ptr(block_table),
+                                      block_table.shape[1], B, _ptr(seq_lens), _ptr(k_win), _ptr(v_win),
+                                      float(sm_scale), _ptr(out), pages_per_split, _stream(stream))
+    _check(rc, "tq_decode_attn_noalloc")
 
 
 def tq_get_status(ctx):

@@ -15,9 +15,17 @@
 //     rotated accumulator once and normalise.
 #include <hip/hip_ext.h>
 
+#include <mutex>
+
 #include "decode_common.h"
 #include "device_common.h"
 #include "tq_internal.h"
+
+// Workspace of tq_decode_attn_noalloc (rotated queries and split partials),
+// for callers that cannot allocate.  One copy per device, held until the
+// process ends; host code reaches it only through the address
+// hipGetSymbolAddress returns for the device (static_scratch_init).
+static __device__ __align__(256) unsigned char scratch[TQ_NOALLOC_SCRATCH_BYTES];
 
 namespace tq {
 namespace {
@@ -689,6 +697,30 @@ int launch_scan_valu(const tq_ctx* c, const DecodeArgs& a, const KParams& k, hip
 }
 
 }  // namespace
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+}  // namespace
+
+// Records the device address of `scratch` on `device`, which must be the
+// current device; once per device.  0 on success.
+int static_scratch_init(int device) {
+  if (device < 0 || device >= kMaxDevices) return 1;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[device]) return 0;
+  void* ptr = nullptr;
+  if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || ptr == nullptr) return 1;
+  g_scratch_ptr[device] = ptr;
+  return 0;
+}
+
+void* static_scratch_ptr(int device) {
+  if (device < 0 || device >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  return g_scratch_ptr[device];
+}
 
 int launch_decode(const tq_ctx* c, const DecodeArgs& a, void* stream) {
   hipStream_t s = static_cast<hipStream_t>(stream);

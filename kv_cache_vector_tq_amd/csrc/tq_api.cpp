@@ -302,6 +302,12 @@ int init_ctx(tq_ctx** out, const tq_params* p, const float* rot_in, const float*
     return TQ_ERR_HIP;
   }
   c->scan_slots = (per_cu > 0 ? per_cu : 1) * (cus > 0 ? cus : 1);
+  // the static scratch of the allocation-free decode: its address on this device
+  if (tq::static_scratch_init(c->device) != 0) {
+    (void)hipFree(c->dmem);
+    delete c;
+    return TQ_ERR_HIP;
+  }
   *out = c;
   return TQ_OK;
 }
@@ -513,6 +519,21 @@ TQ_API int tq_decode_attn(const tq_ctx* c, const void* q, int q_dtype, const uin
   a.pl = reinterpret_cast<float*>(base + w.pl);
   a.pacc = reinterpret_cast<float*>(base + w.pacc);
   return tq::launch_decode(c, a, stream) == 0 ? TQ_OK : TQ_ERR_HIP;
+}
+
+TQ_API int tq_decode_attn_noalloc(const tq_ctx* c, const void* q, int q_dtype, const uint8_t* pool,
+                                  int64_t num_pages, const int32_t* block_table, int max_pages, int batch,
+                                  const int32_t* seq_lens, const uint16_t* k_win, const uint16_t* v_win,
+                                  float sm_scale, float* out, int pages_per_split, void* stream) {
+  if (!c || batch < 0 || max_pages < 0 || pages_per_split < 0) return TQ_ERR_INVALID_ARG;
+  const int64_t need = tq_decode_workspace_bytes(c, batch, max_pages, pages_per_split);
+  if (need < 0) return static_cast<int>(need);
+  if (need > static_cast<int64_t>(TQ_NOALLOC_SCRATCH_BYTES)) return TQ_ERR_WORKSPACE;
+  void* ws = tq::static_scratch_ptr(c->device);
+  if (!ws) return TQ_ERR_HIP;
+  return tq_decode_attn(c, q, q_dtype, pool, num_pages, block_table, max_pages, batch, seq_lens, k_win, v_win,
+                        sm_scale, out, ws, static_cast<size_t>(TQ_NOALLOC_SCRATCH_BYTES), pages_per_split, nullptr, 0,
+                        stream);
 }
 
 }  // extern "C"

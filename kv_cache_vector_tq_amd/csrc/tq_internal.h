@@ -182,6 +182,11 @@ const void* scan_valu_kernel_ptr(const tq_ctx* ctx);
 int scan_mfma_threads(const tq_ctx* ctx);
 // Events to record around the scan kernel of this call (nullptr when not profiling).
 void* profile_slot(const tq_ctx* ctx, int which);
+// Device address of the allocation-free decode's static scratch
+// (decode.hip): static_scratch_init records it for the current device
+// (0 on success), static_scratch_ptr returns it (nullptr before init).
+int static_scratch_init(int device);
+void* static_scratch_ptr(int device);
 
 }  // namespace tq
 

@@ -77,6 +77,8 @@ def test_null_context_and_pointers(L):
     assert L.tq_destroy(None) == tqa.TQ_ERR_INVALID_ARG
     assert L.tq_decode_workspace_bytes(None, 1, 1, 0) == tqa.TQ_ERR_INVALID_ARG
     assert L.tq_host_tables(None, None, None, None, None, None, None, None, None) == tqa.TQ_ERR_INVALID_ARG
+    assert L.tq_decode_attn_noalloc(None, None, 0, None, 0, None, 0, 1, None, None, None, 0.1, None, 0, None) == \
+        tqa.TQ_ERR_INVALID_ARG
     assert L.tq_strerror(tqa.TQ_ERR_WORKSPACE) == b"workspace too small"
 
 
