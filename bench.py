@@ -197,7 +197,34 @@ def encode_legs(tqa, tq_inputs, reps=10):
                     r["mfma_tflops_executed"] = (5 if qjl else 2) * 2 * d * d * n / (ms / 1e3) / 1e12
                 out[name] = r
             ctx.close()
-    del k, v, codes, norms, signs, rnorms
+    del codes, norms, signs, rnorms
+    # the same vectors written into 256-token pages by one bulk tq_append_page
+    # (4,096 sequences x 1,024 tokens, no FP16 window): keys 3-bit + QJL and
+    # values 4-bit, dense rotation
+    params = tqa.make_params(key_bits=3, key_qjl=1, value_bits=4, page_tokens=256, window=0)
+    ctx = tqa.Context(params, tq_inputs.rotation_draws(0, d), tq_inputs.qjl_draws(0, d))
+    pb = tqa.tq_page_bytes(params)
+    npg = 4096 * 4
+    pool = torch.zeros(npg * pb, dtype=torch.uint8, device="cuda")
+    bt = torch.arange(npg, dtype=torch.int32, device="cuda").view(4096, 4)
+    sl = torch.zeros(4096, dtype=torch.int32, device="cuda")
+    kp, vp = k.view(4096, 1, 1024, d), v.view(4096, 1, 1024, d)
+    times = []
+    for _ in range(3):
+        sl.zero_()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        tqa.tq_append_page(ctx, pool, bt, sl, kp, vp, None, None, num_pages=npg)
+        e1.record()
+        torch.cuda.synchronize()
+        times.append(e0.elapsed_time(e1))
+    ms = min(times)
+    out["pages_dense_k3qjl_v4"] = {"ms": ms, "vectors_per_s": 2 * n / (ms / 1e3),
+                                   "hbm_gbps": (2 * n * d * 2 + n * (72 + 68)) / (ms / 1e3) / 1e9,
+                                   "what": "tq_append_page of 4,096 sequences x 1,024 tokens (keys and values, "
+                                           "8,388,608 vectors) into 256-token pages, W=0; fastest of 3"}
+    ctx.close()
+    del k, v, kp, vp, pool
     return out
 
 
@@ -236,6 +263,7 @@ def decode_workload(tqa, tq_inputs, wname, args, fmt_over=None):
     max_pages = -(-(int(Tf.max()) - W) // P)
     npages = B * max_pages
     caches = []
+    prefill = None
     for c in range(ncache):
         pool = torch.zeros(npages * pb, dtype=torch.uint8, device=dev)
         # pages of a sequence are scattered over the pool
@@ -249,8 +277,18 @@ def decode_workload(tqa, tq_inputs, wname, args, fmt_over=None):
         T0 = int(lens0.max())
         k, v = tq_inputs.torch_kv(0, B, Hkv, T0, d, dev, layer=c % L)
         counts = None if np.all(lens0 == T0) else torch.from_numpy(lens0.astype(np.int32)).to(dev)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
         tqa.tq_append_page(ctx, pool, cache["block_table"], cache["seq_lens"], k, v, cache["k_win"], cache["v_win"],
                            new_counts=counts, num_pages=npages)
+        e1.record()
+        if c == 0:  # the bulk prefill of the first cache: every token leaving the window is encoded
+            torch.cuda.synchronize()
+            ms = e0.elapsed_time(e1)
+            nvec = 2 * Hkv * int(np.maximum(lens0 - W, 0).sum())
+            prefill = {"ms": ms, "vectors": nvec, "vectors_per_s": nvec / (ms / 1e3),
+                       "what": "one tq_append_page of the whole prompt (keys and values of every KV head; "
+                               "HIP events), the cache's first prefill"}
         del k, v
         cache["lens"] = lens0.copy()
         caches.append(cache)
@@ -372,6 +410,7 @@ def decode_workload(tqa, tq_inputs, wname, args, fmt_over=None):
                         "what": f"tq_decode_attn (prep + scan + merge) at longest context {hi_T}, mean of "
                                 f"{ncall} back-to-back host-timed calls; bytes = packed pages + FP16 window"},
     }
+    res["prefill"] = prefill
     if L > 1:
         res["layer_calls_per_s"] = L * args.steps / el
     del caches, ksteps, vsteps, ws, out

@@ -83,9 +83,10 @@ enum { TQ_QJL_GAUSSIAN = 0, TQ_QJL_ORTHOGONAL = 1 };
 enum { TQ_DTYPE_F16 = 0, TQ_DTYPE_BF16 = 1, TQ_DTYPE_F32 = 2 };
 enum { TQ_KIND_KEY = 0, TQ_KIND_VALUE = 1 };
 /* tq_params.flags: TQ_FLAG_VALU_SCAN selects the vector-ALU decode scan
- * instead of the matrix-core one (same results to the stated tolerance; kept
- * for measurement and cross-checking). */
-enum { TQ_FLAG_VALU_SCAN = 1 };
+ * instead of the matrix-core one, TQ_FLAG_VALU_APPEND the vector-ALU encoder
+ * for bulk appends instead of the matrix-core one (same results to the stated
+ * tolerance and guard band; kept for measurement and cross-checking). */
+enum { TQ_FLAG_VALU_SCAN = 1, TQ_FLAG_VALU_APPEND = 2 };
 /* Streams of the library's seeded generator (tq_seed_draws): the Gaussian
  * matrix the dense rotation is built from, the QJL draws, and the draws whose
  * signs are the Hadamard variant's Rademacher stage. */

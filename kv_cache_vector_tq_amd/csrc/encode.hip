@@ -411,9 +411,10 @@ __device__ void encode_group(Smem& sm, const AppendArgs& a, const DevTables& t, 
   }
 }
 
+// kinds: bit 0 keys, bit 1 values (the kinds the matrix-core append does not take)
 template <bool HAD>
 __global__ __launch_bounds__(kThreads) void append_encode_kernel(AppendArgs a, DevTables t, Codebooks cb, Layout L,
-                                                                int W, int ring) {
+                                                                int W, int ring, int kinds) {
   __shared__ Smem sm;
   const int tid = threadIdx.x, h = blockIdx.y, b = blockIdx.z;
   // every work-group of b evaluates the same plan; the commit kernel reports
@@ -423,7 +424,7 @@ __global__ __launch_bounds__(kThreads) void append_encode_kernel(AppendArgs a, D
   const int gr = static_cast<int>(blockIdx.x >> 1);
   const int g = sp.c0 / kVGroup + gr;
   const int gpos = g * kVGroup;
-  if (sp.c1 > sp.c0 && gpos < sp.c1) encode_group<HAD>(sm, a, t, cb, L, W, sp, b, h, kv, gpos);
+  if (sp.c1 > sp.c0 && gpos < sp.c1 && ((kinds >> kv) & 1)) encode_group<HAD>(sm, a, t, cb, L, W, sp, b, h, kv, gpos);
   if (ring) ring_owned(a, sp, W, static_cast<int64_t>(b) * L.H + h, kv, gr, tid);
 }
 
@@ -848,7 +849,7 @@ int launch_append(const tq_ctx* c, const AppendArgs& a, void* stream) {
   const bool had = c->p.rotation == TQ_ROT_HADAMARD;
   // the ring update rides along when no slot can be read and written by
   // different work-groups (at most W new tokens)
-  const int ring = (W > 0 && a.n_new <= W) ? 1 : 0;
+  int ring = (W > 0 && a.n_new <= W) ? 1 : 0;
   if (a.n_new <= kSmallNew) {
     // decode steps: one work-group per (sequence, kv head, keys|values)
     const dim3 grid(2, L.H, a.batch);
@@ -857,13 +858,25 @@ int launch_append(const tq_ctx* c, const AppendArgs& a, void* stream) {
     else
       hipLaunchKernelGGL(append_small_kernel<false>, grid, dim3(kSmallThreads), 0, s, a, c->t, L, W, ring);
   } else {
-    // groups a sequence can touch: ceil(n_new / 32) + 1 (unaligned start)
-    const int gmax = (a.n_new + kVGroup - 1) / kVGroup + 1;
-    const dim3 grid(2 * gmax, L.H, a.batch);  // even x: keys, odd x: values
-    if (had)
-      hipLaunchKernelGGL(append_encode_kernel<true>, grid, dim3(kThreads), 0, s, a, c->t, c->cb, L, W, ring);
-    else
-      hipLaunchKernelGGL(append_encode_kernel<false>, grid, dim3(kThreads), 0, s, a, c->t, c->cb, L, W, ring);
+    // bulk: the matrix-core append for the kinds it takes (integer rates),
+    // the vector-ALU one for the rest; the ring is then updated by its own
+    // kernel, after every encoded token has been read
+    int kinds = 0;
+    for (int kind = 0; kind < 2; ++kind) {
+      const int rc = (c->p.flags & TQ_FLAG_VALU_APPEND) ? 1 : launch_append_mma(c, kind, a, stream);
+      if (rc < 0) return 1;
+      if (rc > 0) kinds |= 1 << kind;
+    }
+    if (kinds != 3) ring = 0;
+    if (kinds != 0) {
+      // groups a sequence can touch: ceil(n_new / 32) + 1 (unaligned start)
+      const int gmax = (a.n_new + kVGroup - 1) / kVGroup + 1;
+      const dim3 grid(2 * gmax, L.H, a.batch);  // even x: keys, odd x: values
+      if (had)
+        hipLaunchKernelGGL(append_encode_kernel<true>, grid, dim3(kThreads), 0, s, a, c->t, c->cb, L, W, ring, kinds);
+      else
+        hipLaunchKernelGGL(append_encode_kernel<false>, grid, dim3(kThreads), 0, s, a, c->t, c->cb, L, W, ring, kinds);
+    }
   }
   if (hipGetLastError() != hipSuccess) return 1;
   if (W > 0 && !ring) {

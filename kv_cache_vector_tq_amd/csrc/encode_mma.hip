@@ -1,4 +1,5 @@
-// Bulk encode of fp16 vectors on the matrix cores (tq_encode, gfx950).
+// Bulk encode of fp16 vectors on the matrix cores (gfx950): tq_encode's flat
+// records and tq_append_page's bulk appends into pages.
 //
 // Same per-vector steps as the vector-ALU encoder in encode.hip ("aither-
 // kvcache" README, section "Algorithm"; keys' residual sketch from "TurboQuant
@@ -19,6 +20,14 @@
 // 32kg + 8s + i), so every operand a lane feeds is its own data.
 // The Hadamard variant rotates with butterflies (five stages inside a lane,
 // two across the lane groups) and keeps the dense QJL product.
+//
+// Bulk append ("TurboQuant Family Design Study", sections "Packed format and
+// complete bit accounting" and "Paging, lifecycle, and cache identity"): one
+// wave encodes one 32-token value group of one (sequence, KV head) at a time,
+// taking its tokens from the FP16 ring (tokens already cached) or from the new
+// rows, and writes key records token by token, or the group's value words
+// (for each coordinate, the 32 tokens' codes as one bit string), which the
+// wave gathers from its lanes in LDS.
 #include "device_common.h"
 #include "tq_internal.h"
 
@@ -105,14 +114,203 @@ __device__ inline double sum4(double v) {
   return v;
 }
 
-// Two work-groups per CU need <= 128 VGPRs; the dense key variant holds both
-// matrices (128 KB of LDS) and fits only one anyway.
-template <bool QJL, bool HAD, int BITS>
-__global__ __launch_bounds__(kEncThreads) __attribute__((amdgpu_waves_per_eu((QJL && !HAD) ? 2 : 4)))
-void encode_mma_kernel(EncodeArgs a, DevTables t, EncCodebook cbk) {
-  __shared__ u4 fragP[HAD ? 1 : 8 * 4 * 2 * 64];  // 64 KB
-  __shared__ u4 fragS[QJL ? 8 * 4 * 2 * 64 : 1];  // 64 KB
-  __shared__ float ctab[16];
+// Encodes the COLS x 16 vectors whose fp16 coordinates the lanes hold in xb
+// (zeros for dead vectors: they come out as the zero vector's record); lane
+// (n, kg) of column block c holds vector 16c + n, coordinates 32kg .. 32kg+31.
+// Results go to two callbacks, each called for c = 0 .. COLS-1 as soon as
+// they exist (so they need not stay in registers):
+//   codes(c, words, nst, nq): the lane's BITS words of the vector's LSB-first
+//     code stream, the stored norm (f32 norm, or the u8 log-norm level) and
+//     the u8 log-norm code (N8);
+//   signs(c, rn, sw): ||r|| and the sign bits of coordinates 32kg .. 32kg+31 (QJL).
+// frag*: the LDS fragments; ctab: the centroids in LDS; emask: the lane's
+// Hadamard signs as fp16 sign-bit masks over its input words (bit 15 or 31
+// set where the sign is -1); ntab: the u8 log-norm levels then boundaries (N8).
+template <bool QJL, bool HAD, int BITS, bool N8, int COLS, class CodesFn, class SignsFn>
+__device__ __forceinline__ void encode_tile(const u4* fragP, const u4* fragS, const float* ctab, const u4* emask,
+                                            const EncCodebook& cbk, const float* ntab, const u4 (&xb)[COLS][4],
+                                            CodesFn&& codes_out, SignsFn&& signs_out) {
+  const int l = threadIdx.x & 63;
+  // ---- norms (double accumulation, as the vector-ALU path)
+  float n32[COLS], invn[COLS], nstv[COLS];
+  int nqv[COLS];
+#pragma unroll
+  for (int c = 0; c < COLS; ++c) {
+    double ss = 0.0;
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const double e0 = hval(xb[c][s][w] & 0xffffu), e1 = hval(xb[c][s][w] >> 16);
+        ss = fma(e0, e0, ss);
+        ss = fma(e1, e1, ss);
+      }
+    ss = sum4(ss);
+    const double nn = sqrt(ss);
+    n32[c] = static_cast<float>(nn);
+    invn[c] = nn > 0.0 ? static_cast<float>(1.0 / nn) : 0.0f;
+    nstv[c] = n32[c];
+    nqv[c] = 0;
+    if constexpr (N8) {
+      const int q = norm_code(n32[c], ntab + kNormCodes);
+      nqv[c] = q;
+      nstv[c] = ntab[q];
+    }
+  }
+  // ---- y (unnormalised, fp32): lane holds coordinate 32kg + 4tt + r in acc[c][tt][r]
+  f4 acc[COLS][8];
+  if constexpr (!HAD) {
+#pragma unroll
+    for (int c = 0; c < COLS; ++c)
+#pragma unroll
+      for (int tt = 0; tt < 8; ++tt) acc[c][tt] = f4{0.0f, 0.0f, 0.0f, 0.0f};
+    // one output tile at a time: the scheduling barrier keeps later tiles'
+    // fragment reads from being hoisted (they would all be live at once;
+    // reading the next tile ahead measured no faster)
+    u4 fa[8];
+    auto ldP = [&](int tt, u4* f) {
+#pragma unroll
+      for (int q = 0; q < 8; ++q) f[q] = fragP[(tt * 8 + q) * 64 + l];
+    };
+    ldP(0, fa);
+#pragma unroll
+    for (int tt = 0; tt < 8; ++tt) {
+      u4* cur = fa;
+      if (tt > 0) ldP(tt, cur);
+#pragma unroll
+      for (int s = 0; s < 4; ++s)
+#pragma unroll
+        for (int c = 0; c < COLS; ++c) {
+          acc[c][tt] = mfma(cur[2 * s], xb[c][s], acc[c][tt]);
+          acc[c][tt] = mfma(cur[2 * s + 1], xb[c][s], acc[c][tt]);
+        }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+#pragma unroll
+    for (int c = 0; c < COLS; ++c)
+#pragma unroll
+      for (int tt = 0; tt < 8; ++tt) acc[c][tt] *= 0.0625f;
+  } else {
+    // y = H (eps . x) / sqrt(d), natural (Sylvester) order
+#pragma unroll
+    for (int c = 0; c < COLS; ++c) {
+      float v[32];
+#pragma unroll
+      for (int j = 0; j < 32; ++j) {
+        const uint32_t w = xb[c][j >> 3][(j >> 1) & 3] ^ emask[j >> 3][(j >> 1) & 3];
+        v[j] = hval((j & 1) ? (w >> 16) : (w & 0xffffu));
+      }
+#pragma unroll
+      for (int h = 1; h < 32; h <<= 1)
+#pragma unroll
+        for (int j = 0; j < 32; ++j)
+          if (!(j & h)) {
+            const float p = v[j], q = v[j + h];
+            v[j] = p + q;
+            v[j + h] = p - q;
+          }
+#pragma unroll
+      for (int h = 16; h <= 32; h <<= 1)
+#pragma unroll
+        for (int j = 0; j < 32; ++j) {
+          const float ov = __shfl_xor(v[j], h, 64);
+          v[j] = (l & h) ? (ov - v[j]) : (v[j] + ov);
+        }
+#pragma unroll
+      for (int j = 0; j < 32; ++j) acc[c][j >> 2][j & 3] = v[j] * 0.08838834764831845f;
+    }
+  }
+  // ---- quantise, pack, residual
+  u4 rb[COLS][4][2];  // B operands of the residual product (hi / lo)
+  float rnv[COLS];
+#pragma unroll
+  for (int c = 0; c < COLS; ++c) {
+    uint32_t words[BITS];
+#pragma unroll
+    for (int w = 0; w < BITS; ++w) words[w] = 0u;
+    float rv[32];
+    float rs = 0.0f;
+    const float nst = nstv[c];
+#pragma unroll
+    for (int j = 0; j < 32; ++j) {
+      const float accv = acc[c][j >> 2][j & 3];
+      const float y = accv * invn[c];
+      uint32_t code = 0;
+      if constexpr (BITS == 3 && !QJL) {
+        code = quantize_sym<BITS>(y, cbk);
+      } else {
+        // a linear count measured faster for 2 and 4 bits and for keys
+#pragma unroll
+        for (int k = 0; k < (1 << BITS) - 1; ++k) code += (y > cbk.bnd[k]) ? 1u : 0u;
+      }
+      if (!(n32[c] > 0.0f)) code = 0;
+      const int pos = j * BITS;
+      words[pos >> 5] |= code << (pos & 31);
+      if ((pos & 31) + BITS > 32) words[(pos >> 5) + 1] |= code >> (32 - (pos & 31));
+      if constexpr (QJL) {
+        // the residual against the stored reconstruction nst c[code]
+        const float r = (n32[c] > 0.0f) ? fmaf(-nst, ctab[code], accv) : 0.0f;
+        rs = fmaf(r, r, rs);
+        rv[j] = r * (64.0f * invn[c]);
+      }
+    }
+    codes_out(c, words, nstv[c], nqv[c]);
+    if constexpr (QJL) {
+      rs += __shfl_xor(rs, 16, 64);
+      rs += __shfl_xor(rs, 32, 64);
+      rnv[c] = sqrtf(rs);
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        uint32_t hi[4], lo[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          // hi truncated to fp16, lo = the exact fp32 remainder truncated again
+          const float r0 = rv[8 * s + 2 * i], r1 = rv[8 * s + 2 * i + 1];
+          const auto hp = __builtin_amdgcn_cvt_pkrtz(r0, r1);
+          hi[i] = __builtin_bit_cast(uint32_t, hp);
+          lo[i] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(r0 - static_cast<float>(hp[0]),
+                                                                          r1 - static_cast<float>(hp[1])));
+        }
+        rb[c][s][0] = u4{hi[0], hi[1], hi[2], hi[3]};
+        rb[c][s][1] = u4{lo[0], lo[1], lo[2], lo[3]};
+      }
+    }
+  }
+  if constexpr (QJL) {
+    // ---- z = S r (scaled), one sign word per lane: bit 4tt + r of word kg
+    uint32_t sw[COLS] = {};
+#pragma unroll
+    for (int tt = 0; tt < 8; ++tt) {
+      f4 z[COLS];
+#pragma unroll
+      for (int c = 0; c < COLS; ++c) z[c] = f4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        const u4 sh = fragS[((tt * 4 + s) * 2 + 0) * 64 + l];
+        const u4 sl = fragS[((tt * 4 + s) * 2 + 1) * 64 + l];
+#pragma unroll
+        for (int c = 0; c < COLS; ++c) {
+          z[c] = mfma(sh, rb[c][s][0], z[c]);
+          z[c] = mfma(sh, rb[c][s][1], z[c]);
+          z[c] = mfma(sl, rb[c][s][0], z[c]);
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int c = 0; c < COLS; ++c)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) sw[c] |= (z[c][r] >= 0.0f ? 1u : 0u) << (4 * tt + r);
+    }
+#pragma unroll
+    for (int c = 0; c < COLS; ++c) signs_out(c, rnv[c], (n32[c] > 0.0f) ? sw[c] : 0u);
+  }
+}
+
+// Builds the work-group's LDS tables (all threads) and the lane's Hadamard
+// sign masks (for coordinates 32kg + 8s + 2i, 2i+1: bits 15, 31 of word i of emask[s]).
+template <bool QJL, bool HAD>
+__device__ __forceinline__ void setup_tables(u4* fragP, u4* fragS, float* ctab, const DevTables& t,
+                                             const EncCodebook& cbk, u4* emask) {
   const int tid = threadIdx.x;
   if (!HAD) build_frags(fragP, t.rot, 16.0f, tid);
   if (QJL) build_frags(fragS, t.S, 1.0f, tid);
@@ -123,16 +321,34 @@ void encode_mma_kernel(EncodeArgs a, DevTables t, EncCodebook cbk) {
       if (k == tid) cv = cbk.cen[k];
     ctab[tid] = cv;
   }
+  if constexpr (HAD) {
+    const int kg = (tid & 63) >> 4;
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float e0 = t.rot[32 * kg + 8 * s + 2 * i], e1 = t.rot[32 * kg + 8 * s + 2 * i + 1];
+        emask[s][i] = (e0 < 0.0f ? 0x8000u : 0u) | (e1 < 0.0f ? 0x80000000u : 0u);
+      }
+  }
   __syncthreads();
+}
+
+// Two work-groups per CU need <= 128 VGPRs; the dense key variant holds both
+// matrices (128 KB of LDS) and fits only one anyway.
+template <bool QJL, bool HAD, int BITS, bool N8>
+__global__ __launch_bounds__(kEncThreads) __attribute__((amdgpu_waves_per_eu((QJL && !HAD) ? 2 : 4)))
+void encode_mma_kernel(EncodeArgs a, DevTables t, EncCodebook cbk) {
+  __shared__ u4 fragP[HAD ? 1 : 8 * 4 * 2 * 64];  // 64 KB
+  __shared__ u4 fragS[QJL ? 8 * 4 * 2 * 64 : 1];  // 64 KB
+  __shared__ float ctab[16];
+  u4 emask[4];  // Hadamard signs of this lane's coordinates
+  setup_tables<QJL, HAD>(fragP, fragS, ctab, t, cbk, emask);
 
   constexpr int kCols = cols_for(HAD), kTileVec = 16 * kCols;
+  const int tid = threadIdx.x;
   const int l = tid & 63, n = l & 15, kg = l >> 4;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  float eps[32];  // Hadamard signs of this lane's coordinates
-  if constexpr (HAD) {
-#pragma unroll
-    for (int j = 0; j < 32; ++j) eps[j] = t.rot[32 * kg + j];
-  }
   const int64_t ntiles = (a.n + kTileVec - 1) / kTileVec;
   const int64_t stride = static_cast<int64_t>(gridDim.x) * kEncWaves;
   const _Float16* X = static_cast<const _Float16*>(a.x);
@@ -150,226 +366,270 @@ void encode_mma_kernel(EncodeArgs a, DevTables t, EncCodebook cbk) {
 #pragma unroll
       for (int s = 0; s < 4; ++s) xb[c][s] = live[c] ? src[s] : u4{0u, 0u, 0u, 0u};
     }
-    // ---- norms (double accumulation, as the vector-ALU path)
-    float n32[kCols], invn[kCols];
+    // stores: this lane's BITS words of the code stream, the norm, ||r||, the sign word
+    encode_tile<QJL, HAD, BITS, N8, kCols>(
+        fragP, fragS, ctab, emask, cbk, t.ntab, xb,
+        [&](int c, const uint32_t* words, float nst, int) {
+          if (!live[c]) return;
+          uint32_t* cw = reinterpret_cast<uint32_t*>(a.codes + vid[c] * (16 * BITS)) + BITS * kg;
 #pragma unroll
-    for (int c = 0; c < kCols; ++c) {
-      double ss = 0.0;
-#pragma unroll
-      for (int s = 0; s < 4; ++s)
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {
-          const double e0 = hval(xb[c][s][w] & 0xffffu), e1 = hval(xb[c][s][w] >> 16);
-          ss = fma(e0, e0, ss);
-          ss = fma(e1, e1, ss);
-        }
-      ss = sum4(ss);
-      const double nn = sqrt(ss);
-      n32[c] = static_cast<float>(nn);
-      invn[c] = nn > 0.0 ? static_cast<float>(1.0 / nn) : 0.0f;
+          for (int w = 0; w < BITS; ++w) cw[w] = words[w];
+          if (kg == 0) a.norms[vid[c]] = nst;
+        },
+        [&](int c, float rn, uint32_t sw) {
+          if (!live[c]) return;
+          if (kg == 0) a.rnorms[vid[c]] = rn;
+          reinterpret_cast<uint32_t*>(a.signs + vid[c] * 16)[kg] = sw;
+        });
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Bulk append of one kind (keys or values) of every sequence.  Work item
+// (tile) = ((b * H + h) * gmax + gr): the gr-th 32-token value group among
+// those whose tokens leave the window in this append, for sequence b and KV
+// head h; a wave takes tiles wave, wave + waves in the grid, ...  For each
+// sequence: T0 = seq_lens[b], T1 = T0 + count; the tokens at positions
+// [max(T0-W, 0), max(T1-W, 0)) are encoded from their FP16 values (the ring
+// for positions below T0, else the new rows).  A sequence with an invalid
+// count or page id is skipped (left unchanged; the commit kernel reports it).
+template <bool KEY, bool QJL, bool HAD, int BITS, bool N8>
+__global__ __launch_bounds__(kEncThreads) __attribute__((amdgpu_waves_per_eu((QJL && !HAD) ? 2 : 4)))
+void append_mma_kernel(AppendArgs a, DevTables t, EncCodebook cbk, Layout L, int W, int gmax) {
+  __shared__ u4 fragP[HAD ? 1 : 8 * 4 * 2 * 64];  // 64 KB
+  __shared__ u4 fragS[QJL ? 8 * 4 * 2 * 64 : 1];  // 64 KB
+  __shared__ float ctab[16];
+  __shared__ uint32_t vbuf[KEY ? 1 : kEncWaves][KEY ? 1 : BITS * kD];  // a wave's value words of one group
+  u4 emask[4];
+  setup_tables<QJL, HAD>(fragP, fragS, ctab, t, cbk, emask);
+
+  constexpr int kCols = cols_for(HAD);
+  constexpr int kSub = 2 / kCols;  // encode_tile calls per 32-token group
+  const int tid = threadIdx.x;
+  const int l = tid & 63, n = l & 15, kg = l >> 4;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int64_t ntiles = static_cast<int64_t>(a.batch) * L.H * gmax;
+  const int64_t stride = static_cast<int64_t>(gridDim.x) * kEncWaves;
+  const uint16_t* win = KEY ? a.k_win : a.v_win;
+  const uint16_t* src = KEY ? a.k_new : a.v_new;
+
+  for (int64_t tile = static_cast<int64_t>(blockIdx.x) * kEncWaves + wave; tile < ntiles; tile += stride) {
+    const int gr = static_cast<int>(tile % gmax);
+    const int64_t bh = tile / gmax;
+    const int h = static_cast<int>(bh % L.H), b = static_cast<int>(bh / L.H);
+    // ---- the sequence's plan (wave-uniform)
+    const int T0 = a.seq_lens[b];
+    const int cnt = a.counts ? a.counts[b] : a.n_new;
+    if (cnt < 0 || cnt > a.n_new || T0 < 0) continue;
+    const int c0 = T0 - W > 0 ? T0 - W : 0;
+    const int c1 = T0 + cnt - W > 0 ? T0 + cnt - W : 0;
+    const int gpos = (c0 / kVGroup + gr) * kVGroup;
+    if (c1 <= c0 || gpos >= c1) continue;
+    const int pg0 = c0 / L.P, pg1 = (c1 - 1) / L.P;
+    if (pg1 >= a.max_pages) continue;
+    // every page the append touches must be valid, or the sequence stays as it is
+    bool bad = false;
+    for (int pg = pg0 + l; pg <= pg1; pg += 64) {
+      const int pid = a.block_table[static_cast<int64_t>(b) * a.max_pages + pg];
+      bad = bad || pid < 0 || pid >= a.num_pages;
     }
-    // ---- y (unnormalised, fp32): lane holds coordinate 32kg + 4tt + r in acc[c][tt][r]
-    f4 acc[kCols][8];
-    if constexpr (!HAD) {
+    if (__ballot(bad)) continue;
+    const int lo = c0 > gpos ? c0 : gpos;
+    const int hi = c1 < gpos + kVGroup ? c1 : gpos + kVGroup;
+    const int pid = a.block_table[static_cast<int64_t>(b) * a.max_pages + gpos / L.P];
+    uint8_t* hb = a.pool + static_cast<int64_t>(pid) * L.page_bytes + kBodyOffset + static_cast<int64_t>(h) * L.head_bytes;
+    const int slot0 = gpos % L.P;
+    if constexpr (!KEY) {
 #pragma unroll
-      for (int c = 0; c < kCols; ++c)
+      for (int e = l; e < BITS * kD; e += 64) vbuf[wave][e] = 0u;
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
+    }
 #pragma unroll
-        for (int tt = 0; tt < 8; ++tt) acc[c][tt] = f4{0.0f, 0.0f, 0.0f, 0.0f};
-      // one output tile at a time: the scheduling barrier keeps later tiles'
-      // fragment reads from being hoisted (they would all be live at once;
-      // reading the next tile ahead measured no faster)
-      u4 fa[8];
-      auto ldP = [&](int tt, u4* f) {
-#pragma unroll
-        for (int q = 0; q < 8; ++q) f[q] = fragP[(tt * 8 + q) * 64 + l];
-      };
-      ldP(0, fa);
-#pragma unroll
-      for (int tt = 0; tt < 8; ++tt) {
-        u4* cur = fa;
-        if (tt > 0) ldP(tt, cur);
-#pragma unroll
-        for (int s = 0; s < 4; ++s)
-#pragma unroll
-          for (int c = 0; c < kCols; ++c) {
-            acc[c][tt] = mfma(cur[2 * s], xb[c][s], acc[c][tt]);
-            acc[c][tt] = mfma(cur[2 * s + 1], xb[c][s], acc[c][tt]);
-          }
-        __builtin_amdgcn_sched_barrier(0);
-      }
-#pragma unroll
-      for (int c = 0; c < kCols; ++c)
-#pragma unroll
-        for (int tt = 0; tt < 8; ++tt) acc[c][tt] *= 0.0625f;
-    } else {
-      // y = H (eps . x) / sqrt(d), natural (Sylvester) order
+    for (int sb = 0; sb < kSub; ++sb) {
+      // ---- load: lane (n, kg) of block c takes token 16 (kCols sb + c) + n of the group
+      u4 xb[kCols][4];
+      int tk[kCols];
+      bool live[kCols];
 #pragma unroll
       for (int c = 0; c < kCols; ++c) {
-        float v[32];
+        tk[c] = 16 * (kCols * sb + c) + n;
+        const int p = gpos + tk[c];
+        live[c] = p >= lo && p < hi;
+        // (a dead lane reads row 0 of the new rows, which always exist, and discards it)
+        const bool ring = live[c] && p < T0;
+        const int64_t row = !live[c] ? 0 : ring ? (bh * W + p % W) : (bh * a.n_new + (p - T0));
+        const u4* rp = reinterpret_cast<const u4*>((ring ? win : src) + row * kD + 32 * kg);
 #pragma unroll
-        for (int j = 0; j < 32; ++j) {
-          const uint32_t w = xb[c][j >> 3][(j >> 1) & 3];
-          v[j] = hval((j & 1) ? (w >> 16) : (w & 0xffffu)) * eps[j];
-        }
+        for (int s = 0; s < 4; ++s) xb[c][s] = live[c] ? rp[s] : u4{0u, 0u, 0u, 0u};
+      }
+      encode_tile<QJL, HAD, BITS, N8, kCols>(
+          fragP, fragS, ctab, emask, cbk, t.ntab, xb,
+          [&](int c, const uint32_t* words, float nst, int nq) {
+            if (!live[c]) return;
+            const int slot = slot0 + tk[c];
+            if constexpr (KEY) {
+              uint32_t* cw =
+                  reinterpret_cast<uint32_t*>(hb + L.k_codes + static_cast<int64_t>(slot) * L.k_rec) + BITS * kg;
 #pragma unroll
-        for (int h = 1; h < 32; h <<= 1)
+              for (int w = 0; w < BITS; ++w) cw[w] = words[w];
+              if (kg == 0) {
+                if constexpr (N8)
+                  (hb + L.k_norm)[slot] = static_cast<uint8_t>(nq);
+                else
+                  reinterpret_cast<float*>(hb + L.k_norm)[slot] = nst;
+              }
+            } else {
+              if (kg == 0) reinterpret_cast<float*>(hb + L.v_norm)[slot] = nst;
+              // token tk's code of coordinate j goes to bits [tk BITS, (tk+1) BITS) of j's string
+              const int bit = tk[c] * BITS, w0 = bit >> 5, sh = bit & 31;
 #pragma unroll
-          for (int j = 0; j < 32; ++j)
-            if (!(j & h)) {
-              const float p = v[j], q = v[j + h];
-              v[j] = p + q;
-              v[j + h] = p - q;
+              for (int jj = 0; jj < 32; ++jj) {
+                const int pos = jj * BITS;
+                uint32_t code = words[pos >> 5] >> (pos & 31);
+                if ((pos & 31) + BITS > 32) code |= words[(pos >> 5) + 1] << (32 - (pos & 31));
+                code &= (1u << BITS) - 1u;
+                const int j = 32 * kg + jj;
+                atomicOr(&vbuf[wave][w0 * kD + j], code << sh);
+                if (sh + BITS > 32) atomicOr(&vbuf[wave][(w0 + 1) * kD + j], code >> (32 - sh));
+              }
             }
-#pragma unroll
-        for (int h = 16; h <= 32; h <<= 1)
-#pragma unroll
-          for (int j = 0; j < 32; ++j) {
-            const float o = __shfl_xor(v[j], h, 64);
-            v[j] = (l & h) ? (o - v[j]) : (v[j] + o);
-          }
-#pragma unroll
-        for (int j = 0; j < 32; ++j) acc[c][j >> 2][j & 3] = v[j] * 0.08838834764831845f;
-      }
+          },
+          [&](int c, float rn, uint32_t sw) {
+            if (!live[c]) return;
+            const int slot = slot0 + tk[c];
+            if (kg == 0) reinterpret_cast<float*>(hb + L.k_rnorm)[slot] = rn;
+            reinterpret_cast<uint32_t*>(hb + L.k_signs + static_cast<int64_t>(slot) * (kD / 8))[kg] = sw;
+          });
     }
-    // ---- quantise, pack, residual
-    uint32_t words[kCols][BITS];
-    u4 rb[kCols][4][2];  // B operands of the residual product (hi / lo)
+    if constexpr (!KEY) {
+      // the group's words; bits of tokens before lo (earlier appends) are kept,
+      // those from hi on are zero
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
+      uint32_t* gw = reinterpret_cast<uint32_t*>(hb + L.v_codes) + static_cast<int64_t>(slot0 / kVGroup) * BITS * kD;
+      const int keep_bits = (lo - gpos) * BITS;
 #pragma unroll
-    for (int c = 0; c < kCols; ++c) {
-#pragma unroll
-      for (int w = 0; w < BITS; ++w) words[c][w] = 0u;
-      float rv[32];
-      float rs = 0.0f;
-#pragma unroll
-      for (int j = 0; j < 32; ++j) {
-        const float accv = acc[c][j >> 2][j & 3];
-        const float y = accv * invn[c];
-        uint32_t code = 0;
-        if constexpr (BITS == 3 && !QJL) {
-          code = quantize_sym<BITS>(y, cbk);
-        } else {
-          // a linear count measured faster for 2 and 4 bits and for keys
-#pragma unroll
-          for (int k = 0; k < (1 << BITS) - 1; ++k) code += (y > cbk.bnd[k]) ? 1u : 0u;
-        }
-        if (!(n32[c] > 0.0f)) code = 0;
-        const int pos = j * BITS;
-        words[c][pos >> 5] |= code << (pos & 31);
-        if ((pos & 31) + BITS > 32) words[c][(pos >> 5) + 1] |= code >> (32 - (pos & 31));
-        if constexpr (QJL) {
-          const float r = (n32[c] > 0.0f) ? fmaf(-n32[c], ctab[code], accv) : 0.0f;
-          rs = fmaf(r, r, rs);
-          rv[j] = r * (64.0f * invn[c]);
-        }
+      for (int e = l; e < BITS * kD; e += 64) {
+        uint32_t v = vbuf[wave][e];
+        const int kb = keep_bits - 32 * (e / kD);
+        if (kb > 0) v |= gw[e] & (kb >= 32 ? 0xffffffffu : ((1u << kb) - 1u));
+        gw[e] = v;
       }
-      // stores: this lane's BITS words of the code stream, and the norm
-      if (live[c]) {
-        uint32_t* cw = reinterpret_cast<uint32_t*>(a.codes + vid[c] * (16 * BITS)) + BITS * kg;
-#pragma unroll
-        for (int w = 0; w < BITS; ++w) cw[w] = words[c][w];
-        if (kg == 0) a.norms[vid[c]] = n32[c];
-      }
-      if constexpr (QJL) {
-        rs += __shfl_xor(rs, 16, 64);
-        rs += __shfl_xor(rs, 32, 64);
-        if (live[c] && kg == 0) a.rnorms[vid[c]] = sqrtf(rs);
-#pragma unroll
-        for (int s = 0; s < 4; ++s) {
-          uint32_t hi[4], lo[4];
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            // hi truncated to fp16, lo = the exact fp32 remainder truncated again
-            const float r0 = rv[8 * s + 2 * i], r1 = rv[8 * s + 2 * i + 1];
-            const auto hp = __builtin_amdgcn_cvt_pkrtz(r0, r1);
-            hi[i] = __builtin_bit_cast(uint32_t, hp);
-            lo[i] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(r0 - static_cast<float>(hp[0]),
-                                                                            r1 - static_cast<float>(hp[1])));
-          }
-          rb[c][s][0] = u4{hi[0], hi[1], hi[2], hi[3]};
-          rb[c][s][1] = u4{lo[0], lo[1], lo[2], lo[3]};
-        }
-      }
-    }
-    if constexpr (QJL) {
-      // ---- z = S r (scaled), one sign word per lane: bit 4tt + r of word kg
-      uint32_t sw[kCols] = {};
-#pragma unroll
-      for (int tt = 0; tt < 8; ++tt) {
-        f4 z[kCols];
-#pragma unroll
-        for (int c = 0; c < kCols; ++c) z[c] = f4{0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-        for (int s = 0; s < 4; ++s) {
-          const u4 sh = fragS[((tt * 4 + s) * 2 + 0) * 64 + l];
-          const u4 sl = fragS[((tt * 4 + s) * 2 + 1) * 64 + l];
-#pragma unroll
-          for (int c = 0; c < kCols; ++c) {
-            z[c] = mfma(sh, rb[c][s][0], z[c]);
-            z[c] = mfma(sh, rb[c][s][1], z[c]);
-            z[c] = mfma(sl, rb[c][s][0], z[c]);
-          }
-        }
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int c = 0; c < kCols; ++c)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) sw[c] |= (z[c][r] >= 0.0f ? 1u : 0u) << (4 * tt + r);
-      }
-#pragma unroll
-      for (int c = 0; c < kCols; ++c)
-        if (live[c]) reinterpret_cast<uint32_t*>(a.signs + vid[c] * 16)[kg] = (n32[c] > 0.0f) ? sw[c] : 0u;
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
+      __builtin_amdgcn_wave_barrier();
     }
   }
 }
 
-template <bool QJL, bool HAD>
+template <bool QJL, bool HAD, bool N8>
 const void* pick_bits(int bits) {
-  if (bits == 2) return reinterpret_cast<const void*>(&encode_mma_kernel<QJL, HAD, 2>);
-  if (bits == 3) return reinterpret_cast<const void*>(&encode_mma_kernel<QJL, HAD, 3>);
-  return reinterpret_cast<const void*>(&encode_mma_kernel<QJL, HAD, 4>);
+  if (bits == 2) return reinterpret_cast<const void*>(&encode_mma_kernel<QJL, HAD, 2, N8>);
+  if (bits == 3) return reinterpret_cast<const void*>(&encode_mma_kernel<QJL, HAD, 3, N8>);
+  return reinterpret_cast<const void*>(&encode_mma_kernel<QJL, HAD, 4, N8>);
 }
 
-}  // namespace
+template <bool KEY, bool QJL, bool HAD, bool N8>
+const void* pick_append_bits(int bits) {
+  if (bits == 2) return reinterpret_cast<const void*>(&append_mma_kernel<KEY, QJL, HAD, 2, N8>);
+  if (bits == 3) return reinterpret_cast<const void*>(&append_mma_kernel<KEY, QJL, HAD, 3, N8>);
+  return reinterpret_cast<const void*>(&append_mma_kernel<KEY, QJL, HAD, 4, N8>);
+}
 
-// Returns 1 when this path does not apply (input not fp16 or not 16-byte
-// rows); the caller then uses the vector-ALU encoder.
-int launch_encode_mma(const tq_ctx* c, int kind, int dtype, const EncodeArgs& a, void* stream) {
-  if (dtype != TQ_DTYPE_F16 || c->p.head_dim != kD || (a.row_stride % 8) != 0 ||
-      (reinterpret_cast<uintptr_t>(a.x) % 16) != 0)
-    return 1;
-  const bool key = kind == TQ_KIND_KEY;
-  // mixed-channel rates take the vector-ALU encoder
-  if (key ? c->p.key_mixed : c->p.value_mixed) return 1;
-  // so do keys with u8 log-norms
-  if (key && c->p.key_norm_u8) return 1;
-  const bool qjl = key && c->p.key_qjl;
-  const bool had = c->p.rotation == TQ_ROT_HADAMARD;
+template <bool QJL, bool HAD>
+const void* pick_append_key(int bits, bool n8) {
+  return n8 ? pick_append_bits<true, QJL, HAD, true>(bits) : pick_append_bits<true, QJL, HAD, false>(bits);
+}
+
+// This kind's codebook, if the matrix-core path takes it: an integer rate
+// with a symmetric codebook (the binary-search quantiser relies on it).
+bool mma_codebook(const tq_ctx* c, bool key, EncCodebook& cbk) {
+  if (c->p.head_dim != kD || (key ? c->p.key_mixed : c->p.value_mixed)) return false;
   const int bits = key ? c->p.key_bits : c->p.value_bits;
-  const void* f = qjl ? (had ? pick_bits<true, true>(bits) : pick_bits<true, false>(bits))
-                      : (had ? pick_bits<false, true>(bits) : pick_bits<false, false>(bits));
-  EncCodebook cbk;
   for (int k = 0; k < 16; ++k) {
     cbk.cen[k] = key ? c->cb.kc[k] : c->cb.vc[k];
     cbk.bnd[k] = key ? c->cb.kb[k] : c->cb.vb[k];
   }
-  // the quantiser relies on a symmetric codebook with a boundary at 0
   const int L = 1 << bits;
-  if (cbk.bnd[L / 2 - 1] != 0.0f) return 1;
+  if (cbk.bnd[L / 2 - 1] != 0.0f) return false;
   for (int k = 0; k + 1 < L; ++k)
-    if (cbk.bnd[k] != -cbk.bnd[L - 2 - k]) return 1;
+    if (cbk.bnd[k] != -cbk.bnd[L - 2 - k]) return false;
+  return true;
+}
+
+// Work-groups for a persistent grid over `items` wave-sized items.
+int persistent_blocks(const void* f, int64_t items, int64_t* blocks) {
   int dev = 0, cus = 0, per_cu = 0;
   if (hipGetDevice(&dev) != hipSuccess ||
       hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
       hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, f, kEncThreads, 0) != hipSuccess)
     return -1;
-  const int tv = 16 * cols_for(had);
-  const int64_t ntiles = (a.n + tv - 1) / tv;
-  int64_t blocks = (ntiles + kEncWaves - 1) / kEncWaves;
+  int64_t bl = (items + kEncWaves - 1) / kEncWaves;
   const int64_t cap = static_cast<int64_t>(cus > 0 ? cus : 1) * (per_cu > 0 ? per_cu : 1);
-  if (blocks > cap) blocks = cap;
+  if (bl > cap) bl = cap;
+  *blocks = bl < 1 ? 1 : bl;
+  return 0;
+}
+
+}  // namespace
+
+// Returns 1 when this path does not apply (input not fp16 or not 16-byte
+// rows, mixed-channel rate); the caller then uses the vector-ALU encoder.
+int launch_encode_mma(const tq_ctx* c, int kind, int dtype, const EncodeArgs& a, void* stream) {
+  if (dtype != TQ_DTYPE_F16 || (a.row_stride % 8) != 0 || (reinterpret_cast<uintptr_t>(a.x) % 16) != 0) return 1;
+  const bool key = kind == TQ_KIND_KEY;
+  EncCodebook cbk;
+  if (!mma_codebook(c, key, cbk)) return 1;
+  const bool qjl = key && c->p.key_qjl;
+  const bool had = c->p.rotation == TQ_ROT_HADAMARD;
+  const bool n8 = key && c->p.key_norm_u8;
+  const int bits = key ? c->p.key_bits : c->p.value_bits;
+  const void* f;
+  if (n8)
+    f = qjl ? (had ? pick_bits<true, true, true>(bits) : pick_bits<true, false, true>(bits))
+            : (had ? pick_bits<false, true, true>(bits) : pick_bits<false, false, true>(bits));
+  else
+    f = qjl ? (had ? pick_bits<true, true, false>(bits) : pick_bits<true, false, false>(bits))
+            : (had ? pick_bits<false, true, false>(bits) : pick_bits<false, false, false>(bits));
+  const int tv = 16 * cols_for(had);
+  int64_t blocks = 0;
+  if (persistent_blocks(f, (a.n + tv - 1) / tv, &blocks) != 0) return -1;
   EncodeArgs aa = a;
   DevTables tt = c->t;
   void* args[] = {&aa, &tt, &cbk};
+  return hipLaunchKernel(f, dim3(static_cast<unsigned>(blocks)), dim3(kEncThreads), args, 0,
+                         static_cast<hipStream_t>(stream)) == hipSuccess
+             ? 0
+             : -1;
+}
+
+// Bulk append of one kind on the matrix cores.  Returns 1 when this path does
+// not apply (mixed-channel rate); -1 on a launch error.
+int launch_append_mma(const tq_ctx* c, int kind, const AppendArgs& a, void* stream) {
+  const bool key = kind == TQ_KIND_KEY;
+  EncCodebook cbk;
+  if (!mma_codebook(c, key, cbk)) return 1;
+  const bool had = c->p.rotation == TQ_ROT_HADAMARD;
+  const bool n8 = key && c->p.key_norm_u8;
+  const bool qjl = key && c->p.key_qjl;
+  const int bits = key ? c->p.key_bits : c->p.value_bits;
+  const void* f;
+  if (key)
+    f = qjl ? (had ? pick_append_key<true, true>(bits, n8) : pick_append_key<true, false>(bits, n8))
+            : (had ? pick_append_key<false, true>(bits, n8) : pick_append_key<false, false>(bits, n8));
+  else
+    f = had ? pick_append_bits<false, false, true, false>(bits) : pick_append_bits<false, false, false, false>(bits);
+  // value groups a sequence can touch: ceil(n_new / 32) + 1 (unaligned start)
+  const int gmax = (a.n_new + kVGroup - 1) / kVGroup + 1;
+  int64_t blocks = 0;
+  if (persistent_blocks(f, static_cast<int64_t>(a.batch) * c->lay.H * gmax, &blocks) != 0) return -1;
+  AppendArgs aa = a;
+  DevTables tt = c->t;
+  Layout L = c->lay;
+  int W = c->p.window, gm = gmax;
+  void* args[] = {&aa, &tt, &cbk, &L, &W, &gm};
   return hipLaunchKernel(f, dim3(static_cast<unsigned>(blocks)), dim3(kEncThreads), args, 0,
                          static_cast<hipStream_t>(stream)) == hipSuccess
              ? 0

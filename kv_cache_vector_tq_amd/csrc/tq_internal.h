@@ -171,6 +171,9 @@ int launch_encode(const tq_ctx* ctx, int kind, int dtype, const EncodeArgs& a, v
 // applicable (the caller falls back to the vector-ALU encoder), -1 error.
 int launch_encode_mma(const tq_ctx* ctx, int kind, int dtype, const EncodeArgs& a, void* stream);
 int launch_append(const tq_ctx* ctx, const AppendArgs& a, void* stream);
+// Matrix-core bulk append of one kind (encode_mma.hip): 0 launched, 1 not
+// applicable (mixed-channel rate), -1 error.
+int launch_append_mma(const tq_ctx* ctx, int kind, const AppendArgs& a, void* stream);
 int launch_decode(const tq_ctx* ctx, const DecodeArgs& a, void* stream);
 int launch_dequant(const tq_ctx* ctx, int kind, const uint8_t* codes, const uint8_t* signs, const float* norms,
                    const float* rnorms, int64_t n, float* out, void* stream);

@@ -61,6 +61,43 @@ def _compare_caches(s, ref, pool_gpu, kwin, vwin, lens_gpu):
     return gcache
 
 
+def _records_match(s, caches, k, v, lens):
+    """Two GPU-built caches of the same tokens hold the same records: norms
+    exactly, codes exactly outside the guard band (either neighbour inside
+    it), each cache's sign bits those of the oracle for its own codes, the
+    residual norms to 2e-5.  (Bulk appends run on the matrix cores, appends
+    of a few tokens on the vector ALU: their sums differ in rounding.)"""
+    a, b2 = caches
+    for b in range(len(lens)):
+        for h in range(s.Hkv):
+            ca, cb = a.compressed(b, h), b2.compressed(b, h)
+            if ca is None:
+                assert cb is None
+                continue
+            (ka, vna, via), (kb, vnb, vib) = ca, cb
+            C = ka.norms.shape[0]
+            x = k[b, h, :C].astype(np.float64)
+            xv = v[b, h, :C].astype(np.float64)
+            assert np.array_equal(ka.norms, kb.norms) and np.array_equal(vna, vnb), (b, h)
+            ia, ib = s.kcb.unpack(ka.codes, 128), s.kcb.unpack(kb.codes, 128)
+            check_codes(x, ia, ib, s.R, s.kcb)
+            check_codes(xv, via, vib, s.R, s.vcb)
+            if s.qjl:
+                check_signs(x, ia, ka.norms, ka.signs, s.R, s.kcb, s.S)
+                check_signs(x, ib, kb.norms, kb.signs, s.R, s.kcb, s.S)
+                assert np.allclose(ka.rnorms, kb.rnorms, rtol=2e-5, atol=1e-30)
+
+
+def _host_cache(s, dv, B, T):
+    g = s.cache(B, T)
+    g.pool = dv["pool"].cpu().numpy().reshape(g.pool.shape)
+    g.seq_lens = dv["seq_lens"].cpu().numpy()
+    g.block_table = dv["block_table"].cpu().numpy()
+    g.k_win = dv["k_win"].cpu().numpy()
+    g.v_win = dv["v_win"].cpu().numpy()
+    return g
+
+
 def _track_sources(s, cache, k, v, lens):
     cache._src_k, cache._src_v = {}, {}
     for b in range(len(lens)):
@@ -144,8 +181,14 @@ def test_streaming_appends_match_bulk(late_step, kn8):
         t += step
     torch.cuda.synchronize()
     assert tqa.tq_get_status(ctx) == 0
-    for key in ("pool", "k_win", "v_win", "seq_lens"):
+    for key in ("k_win", "v_win", "seq_lens"):
         assert torch.equal(d1[key].cpu(), d2[key].cpu()), key
+    g1, g2 = _host_cache(s, d1, 2, 90), _host_cache(s, d2, 2, 90)
+    for b in range(2):
+        for pg in range(-(-max(lens[b] - s.W, 0) // s.P)):
+            pid = int(g1.block_table[b, pg])
+            assert np.array_equal(g1.pool[pid, :64], g2.pool[pid, :64]), (b, pg)  # headers
+    _records_match(s, (g1, g2), k, v, lens)
 
 
 def test_invalid_page_leaves_sequence_unchanged():
@@ -205,16 +248,56 @@ def test_one_token_append_over_stale_slots(mixed):
     _gpu_append(ctx, d2, mix_k, mix_v, counts=[T])
     torch.cuda.synchronize()
     assert tqa.tq_get_status(ctx) == 0
-    caches = []
-    for dv in (d1, d2):
-        g = s.cache(1, T)
-        g.pool = dv["pool"].cpu().numpy().reshape(g.pool.shape)
-        g.seq_lens = dv["seq_lens"].cpu().numpy()
-        caches.append(g)
+    caches = [_host_cache(s, dv, 1, T) for dv in (d1, d2)]
     assert caches[0].seq_lens[0] == T and caches[1].seq_lens[0] == T
-    for h in range(s.Hkv):
-        (k1, vn1, vi1), (k2, vn2, vi2) = caches[0].compressed(0, h), caches[1].compressed(0, h)
-        assert np.array_equal(vi1, vi2) and np.array_equal(vn1, vn2), h
-        assert np.array_equal(k1.codes, k2.codes) and np.array_equal(k1.norms, k2.norms), h
-        assert np.array_equal(k1.signs, k2.signs) and np.array_equal(k1.rnorms, k2.rnorms), h
+    _records_match(s, caches, mix_k, mix_v, [T])
     assert torch.equal(d1["k_win"].cpu(), d2["k_win"].cpu()) and torch.equal(d1["v_win"].cpu(), d2["v_win"].cpu())
+
+
+MMA_CASES = [
+    # name, setup kwargs, prefill lengths, second append (tokens per sequence)
+    ("k3qjl_v4_dense", dict(Hq=8, Hkv=2, W=40, P=64), [300, 41, 40, 7, 0, 129], 37),
+    ("k2qjl_v2_hadamard", dict(Hq=8, Hkv=2, key_bits=2, value_bits=2, rotation="hadamard", W=16, P=32), [200, 77], 50),
+    ("k4_noqjl_v3", dict(Hq=4, Hkv=2, key_bits=4, key_qjl=0, value_bits=3, W=8, P=64), [333, 64, 17], 9),
+    ("k3qjl_u8norm_v4", dict(Hq=4, Hkv=1, W=0, P=32, key_norm_u8=True), [150, 31], 20),
+    ("orthoS_k3_v2", dict(Hq=4, Hkv=2, value_bits=2, W=24, P=64, qjl_kind="orthogonal", qjl_shrink=0.7), [90, 260], 33),
+]
+
+
+@pytest.mark.parametrize("name,kw,lens,extra", MMA_CASES, ids=[c[0] for c in MMA_CASES])
+def test_matrix_core_append_matches_vector_alu_append(name, kw, lens, extra):
+    """The bulk append on the matrix cores writes the records of the
+    vector-ALU append (flag TQ_FLAG_VALU_APPEND) for the same tokens, under
+    the guard-band rule, including a second append that starts inside a
+    value group (earlier tokens' bits kept) and takes tokens from the ring;
+    both equal the oracle's records."""
+    print(f"case mma append {name}", flush=True)
+    s = Setup(**kw)
+    B = len(lens)
+    total = [n + extra for n in lens]
+    ref = s.cache(B, max(total))
+    k, v = fill(s, ref, total)
+    _track_sources(s, ref, k, v, total)
+    devs = []
+    for flags in (0, tqa.TQ_FLAG_VALU_APPEND):
+        ctx = context_for(s, flags)
+        dv = upload_cache(s.cache(B, max(total)))
+        _gpu_append(ctx, dv, np.ascontiguousarray(k[:, :, :max(lens)]), np.ascontiguousarray(v[:, :, :max(lens)]),
+                    counts=lens)
+        # the next `extra` tokens of every sequence, as one more bulk append
+        kk = np.zeros((B, s.Hkv, extra, 128), np.float16)
+        vv = np.zeros_like(kk)
+        for b in range(B):
+            kk[b] = k[b, :, lens[b]:lens[b] + extra]
+            vv[b] = v[b, :, lens[b]:lens[b] + extra]
+        _gpu_append(ctx, dv, kk, vv)
+        torch.cuda.synchronize()
+        assert tqa.tq_get_status(ctx) == 0
+        devs.append(dv)
+    g = [_host_cache(s, dv, B, max(total)) for dv in devs]
+    for key in ("k_win", "v_win", "seq_lens"):
+        assert torch.equal(devs[0][key].cpu(), devs[1][key].cpu()), key
+    assert np.array_equal(g[0].seq_lens, np.asarray(total))
+    _records_match(s, g, k, v, total)
+    _compare_caches(s, ref, devs[0]["pool"].cpu().numpy(), devs[0]["k_win"].cpu().view(torch.int16).numpy().view(np.uint16),
+                    devs[0]["v_win"].cpu().view(torch.int16).numpy().view(np.uint16), devs[0]["seq_lens"].cpu().numpy())
