@@ -83,28 +83,42 @@ struct EncCodebook {
   float bnd[16];
 };
 
-// Code of y for a symmetric codebook of 2^B levels (boundaries b_j = -b_{L-2-j},
-// middle boundary 0): the number of boundaries strictly below y.  With
-// m = |y| and the positive boundaries p_1 < .. < p_P (P = L/2 - 1): y > 0
-// gives L/2 + #{p_k < m}; y <= 0 gives L/2 - 1 - #{p_k <= m}.  Both counts
-// are #{p_k < m'} with m' = m or its float successor, found by binary search.
-template <int B>
-__device__ inline uint32_t quantize_sym(float y, const EncCodebook& cbk) {
-  constexpr int H = 1 << (B - 1);  // L/2
-  const float* p = cbk.bnd + (H - 1);  // p[k] = k-th positive boundary, p[0] = 0
-  const bool pos = y > 0.0f;
-  const uint32_t mb = __builtin_bit_cast(uint32_t, y) & 0x7fffffffu;
-  const float m = __builtin_bit_cast(float, pos ? mb : mb + 1u);
+// Code of y: the number of decision boundaries strictly below it.  The
+// codebook is symmetric with boundaries 0, +-p_1 < .. < p_{H-1}.  With s the
+// sign bit of y and m' the bit pattern of |y| plus s (the next float up for
+// y < 0; non-negative floats order like their bit patterns): y > 0 gives
+// H + #{p_k < m'}, y < 0 gives H - 1 - #{p_k <= |y|} = H - 1 - #{p_k < m'},
+// and both are cnt XOR (H - s).  (y = +0 takes code H rather than H - 1: a
+// value on the boundary 0, inside the guard band.)  The count comes from a
+// branch-free binary search over the positive boundaries (bit patterns
+// pb[1..H-1], uniform): each step compares m' with one boundary through the
+// sign of the difference and picks the next boundary with a bit select, so
+// no lane masks and no table are involved.
+template <int BITS>
+__device__ __forceinline__ uint32_t quantize_search(float y, const uint32_t* pb) {
+  constexpr uint32_t H = 1u << (BITS - 1);
+  const uint32_t bits = __builtin_bit_cast(uint32_t, y);
+  const uint32_t sgn = bits >> 31;
+  const uint32_t m = (bits & 0x7fffffffu) + sgn;
+  // all-ones where m' > p (both below 2^31: the difference cannot wrap)
+  auto gt = [&](uint32_t p) { return static_cast<uint32_t>(static_cast<int32_t>(p - m) >> 31); };
+  // mask ? a : b, bit by bit (v_bitop3 with truth table 0xCA for operands
+  // mask, a, b); written as the instruction so that the compiler keeps the
+  // mask arithmetic instead of turning it into compares and lane masks
+  auto pick = [](uint32_t mask, uint32_t a, uint32_t b) { return __builtin_amdgcn_bitop3_b32(mask, a, b, 0xCA); };
   uint32_t cnt;
-  if constexpr (B == 2) {
-    cnt = m > p[1] ? 1u : 0u;
+  if constexpr (BITS == 2) {
+    cnt = (pb[1] - m) >> 31;
+  } else if constexpr (BITS == 3) {
+    const uint32_t g2 = gt(pb[2]);
+    cnt = ((pick(g2, pb[3], pb[1]) - m) >> 31) - 2u * g2;
   } else {
-    static_assert(B == 3, "binary search written for 2 and 3 bits");
-    const bool g2 = m > p[2];
-    const bool g1 = m > (g2 ? p[3] : p[1]);
-    cnt = (g2 ? 2u : 0u) + (g1 ? 1u : 0u);
+    const uint32_t g4 = gt(pb[4]);
+    const uint32_t g2 = gt(pick(g4, pb[6], pb[2]));
+    const uint32_t t1 = pick(g4, pick(g2, pb[7], pb[5]), pick(g2, pb[3], pb[1]));
+    cnt = ((t1 - m) >> 31) - 2u * (2u * g4 + g2);
   }
-  return pos ? H + cnt : H - 1 - cnt;
+  return cnt ^ (H - sgn);
 }
 
 // 32-lane-group sum of a double over the four lanes holding one vector
@@ -128,9 +142,16 @@ __device__ inline double sum4(double v) {
 // set where the sign is -1); ntab: the u8 log-norm levels then boundaries (N8).
 template <bool QJL, bool HAD, int BITS, bool N8, int COLS, class CodesFn, class SignsFn>
 __device__ __forceinline__ void encode_tile(const u4* fragP, const u4* fragS, const float* ctab, const u4* emask,
-                                            const EncCodebook& cbk, const float* ntab, const u4 (&xb)[COLS][4],
-                                            CodesFn&& codes_out, SignsFn&& signs_out) {
+                                            const EncCodebook& cbk, const float* ntab,
+                                            const u4 (&xb)[COLS][4], CodesFn&& codes_out, SignsFn&& signs_out) {
   const int l = threadIdx.x & 63;
+  // the dense product comes out scaled by 16 (Pi's fragments are): y, the
+  // residual and its norm take that factor out where they are formed
+  constexpr float kScale = HAD ? 1.0f : 16.0f, kInv = HAD ? 1.0f : 0.0625f;
+  // positive boundaries as bit patterns: pbits[k] = p_k, k = 1 .. H-1
+  uint32_t pbits[1 << (BITS - 1)];
+#pragma unroll
+  for (int k = 0; k < (1 << (BITS - 1)); ++k) pbits[k] = __builtin_bit_cast(uint32_t, cbk.bnd[(1 << (BITS - 1)) - 1 + k]);
   // ---- norms (double accumulation, as the vector-ALU path)
   float n32[COLS], invn[COLS], nstv[COLS];
   int nqv[COLS];
@@ -186,10 +207,6 @@ __device__ __forceinline__ void encode_tile(const u4* fragP, const u4* fragS, co
         }
       __builtin_amdgcn_sched_barrier(0);
     }
-#pragma unroll
-    for (int c = 0; c < COLS; ++c)
-#pragma unroll
-      for (int tt = 0; tt < 8; ++tt) acc[c][tt] *= 0.0625f;
   } else {
     // y = H (eps . x) / sqrt(d), natural (Sylvester) order
 #pragma unroll
@@ -230,35 +247,29 @@ __device__ __forceinline__ void encode_tile(const u4* fragP, const u4* fragS, co
     for (int w = 0; w < BITS; ++w) words[w] = 0u;
     float rv[32];
     float rs = 0.0f;
-    const float nst = nstv[c];
+    // y = acc / (kScale n); residual r kScale = acc - kScale nst c[code]
+    const float ys = invn[c] * kInv, nsts = -nstv[c] * kScale, rvs = 64.0f * kInv * invn[c];
+    const uint32_t live = n32[c] > 0.0f ? 0xffffffffu : 0u;  // a zero vector keeps all-zero codes
 #pragma unroll
     for (int j = 0; j < 32; ++j) {
       const float accv = acc[c][j >> 2][j & 3];
-      const float y = accv * invn[c];
-      uint32_t code = 0;
-      if constexpr (BITS == 3 && !QJL) {
-        code = quantize_sym<BITS>(y, cbk);
-      } else {
-        // a linear count measured faster for 2 and 4 bits and for keys
-#pragma unroll
-        for (int k = 0; k < (1 << BITS) - 1; ++k) code += (y > cbk.bnd[k]) ? 1u : 0u;
-      }
-      if (!(n32[c] > 0.0f)) code = 0;
+      const uint32_t code = quantize_search<BITS>(accv * ys, pbits) & live;
       const int pos = j * BITS;
       words[pos >> 5] |= code << (pos & 31);
       if ((pos & 31) + BITS > 32) words[(pos >> 5) + 1] |= code >> (32 - (pos & 31));
       if constexpr (QJL) {
         // the residual against the stored reconstruction nst c[code]
-        const float r = (n32[c] > 0.0f) ? fmaf(-nst, ctab[code], accv) : 0.0f;
+        // (a zero vector has accv = 0 and nst = 0: r = 0 without a branch)
+        const float r = fmaf(nsts, ctab[code], accv);
         rs = fmaf(r, r, rs);
-        rv[j] = r * (64.0f * invn[c]);
+        rv[j] = r * rvs;
       }
     }
     codes_out(c, words, nstv[c], nqv[c]);
     if constexpr (QJL) {
       rs += __shfl_xor(rs, 16, 64);
       rs += __shfl_xor(rs, 32, 64);
-      rnv[c] = sqrtf(rs);
+      rnv[c] = sqrtf(rs) * kInv;
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
         uint32_t hi[4], lo[4];
@@ -278,6 +289,8 @@ __device__ __forceinline__ void encode_tile(const u4* fragP, const u4* fragS, co
   }
   if constexpr (QJL) {
     // ---- z = S r (scaled), one sign word per lane: bit 4tt + r of word kg
+    // is set for z >= 0; collected as the sign bits of z, complemented at the
+    // end (z = -0 counts as negative: a value on the decision, in the band)
     uint32_t sw[COLS] = {};
 #pragma unroll
     for (int tt = 0; tt < 8; ++tt) {
@@ -299,10 +312,13 @@ __device__ __forceinline__ void encode_tile(const u4* fragP, const u4* fragS, co
 #pragma unroll
       for (int c = 0; c < COLS; ++c)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) sw[c] |= (z[c][r] >= 0.0f ? 1u : 0u) << (4 * tt + r);
+        for (int r = 0; r < 4; ++r) {
+          const float zr = z[c][r];  // (a scalar first: bit-casting the vector element reads element 0)
+          sw[c] |= (__builtin_bit_cast(uint32_t, zr) >> 31) << (4 * tt + r);
+        }
     }
 #pragma unroll
-    for (int c = 0; c < COLS; ++c) signs_out(c, rnv[c], (n32[c] > 0.0f) ? sw[c] : 0u);
+    for (int c = 0; c < COLS; ++c) signs_out(c, rnv[c], (n32[c] > 0.0f) ? ~sw[c] : 0u);
   }
 }
 
@@ -408,15 +424,17 @@ void append_mma_kernel(AppendArgs a, DevTables t, EncCodebook cbk, Layout L, int
   const int tid = threadIdx.x;
   const int l = tid & 63, n = l & 15, kg = l >> 4;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int64_t ntiles = static_cast<int64_t>(a.batch) * L.H * gmax;
-  const int64_t stride = static_cast<int64_t>(gridDim.x) * kEncWaves;
+  // (32-bit tile arithmetic: the launcher keeps batch * H * gmax below 2^31)
+  const uint32_t ntiles = static_cast<uint32_t>(a.batch) * static_cast<uint32_t>(L.H) * static_cast<uint32_t>(gmax);
+  const uint32_t stride = gridDim.x * kEncWaves;
   const uint16_t* win = KEY ? a.k_win : a.v_win;
   const uint16_t* src = KEY ? a.k_new : a.v_new;
 
-  for (int64_t tile = static_cast<int64_t>(blockIdx.x) * kEncWaves + wave; tile < ntiles; tile += stride) {
-    const int gr = static_cast<int>(tile % gmax);
-    const int64_t bh = tile / gmax;
-    const int h = static_cast<int>(bh % L.H), b = static_cast<int>(bh / L.H);
+  for (uint32_t tile = blockIdx.x * kEncWaves + wave; tile < ntiles; tile += stride) {
+    const uint32_t bh32 = tile / static_cast<uint32_t>(gmax);
+    const int gr = static_cast<int>(tile - bh32 * static_cast<uint32_t>(gmax));
+    const int64_t bh = bh32;
+    const int b = static_cast<int>(bh32 / static_cast<uint32_t>(L.H)), h = static_cast<int>(bh32 - b * L.H);
     // ---- the sequence's plan (wave-uniform)
     const int T0 = a.seq_lens[b];
     const int cnt = a.counts ? a.counts[b] : a.n_new;
@@ -623,6 +641,7 @@ int launch_append_mma(const tq_ctx* c, int kind, const AppendArgs& a, void* stre
     f = had ? pick_append_bits<false, false, true, false>(bits) : pick_append_bits<false, false, false, false>(bits);
   // value groups a sequence can touch: ceil(n_new / 32) + 1 (unaligned start)
   const int gmax = (a.n_new + kVGroup - 1) / kVGroup + 1;
+  if (static_cast<int64_t>(a.batch) * c->lay.H * gmax >= (int64_t(1) << 31)) return 1;
   int64_t blocks = 0;
   if (persistent_blocks(f, static_cast<int64_t>(a.batch) * c->lay.H * gmax, &blocks) != 0) return -1;
   AppendArgs aa = a;
