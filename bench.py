@@ -19,9 +19,10 @@ The JSON line carries, besides the step rate:
                 started, so the same tokens at the same context lengths);
                 each event adds its own latency, so this fraction is a
                 conservative one;
-  decode_call   back-to-back tq_decode_attn calls at the final length,
-                host-timed: prep + scan + merge per call, against the bytes
-                one call must read (pages and FP16 window);
+  decode_call   back-to-back tq_decode_attn calls at the final length
+                between HIP events: prep + scan + merge per call, against the
+                bytes one call must read (pages and FP16 window);
+  prefill       the first cache's bulk tq_append_page (HIP events);
   read_ceiling  the device's streaming-read rate (tq_read_probe, 1 GiB);
   workloads     the two other decode workloads (below), same fields;
   encode        tq_encode of 4M fp16 vectors at 2, 3 and 4 bits, dense and
@@ -351,15 +352,18 @@ def decode_workload(tqa, tq_inputs, wname, args, fmt_over=None):
     scan_ms, ncalls = tqa.tq_profile_end(ctx)
     for c, f in zip(caches, final):
         assert torch.equal(c["seq_lens"], f), "the replay did not end at the timed region's lengths"
-    # back-to-back decode calls at the final lengths (no appends): prep + scan + merge
+    # back-to-back decode calls at the final lengths (no appends): prep + scan
+    # + merge, between two events on the stream the calls are launched on
     ncall = max(args.steps, 10)
     torch.cuda.synchronize()
-    t2 = time.perf_counter()
+    e2, e3 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e2.record()
     for j in range(ncall):
         for c in step_caches(ntimed - 1 - (j % R)):
             decode(c, ntimed - 1)
+    e3.record()
     torch.cuda.synchronize()
-    el_call = (time.perf_counter() - t2) / (ncall * (L if R == 1 else 1))
+    el_call = e2.elapsed_time(e3) / 1e3 / (ncall * (L if R == 1 else 1))
     status = tqa.tq_get_status(ctx)
     if status != 0 or not torch.isfinite(out).all():
         raise SystemExit(f"bench: bad status {status} or non-finite output")
@@ -408,7 +412,7 @@ def decode_workload(tqa, tq_inputs, wname, args, fmt_over=None):
         "decode_call": {"us": el_call * 1e6, "bytes": call_bytes,
                         "gbps": call_bytes / el_call / 1e9, "frac": call_bytes / el_call / 1e9 / HBM_PEAK_GBPS,
                         "what": f"tq_decode_attn (prep + scan + merge) at longest context {hi_T}, mean of "
-                                f"{ncall} back-to-back host-timed calls; bytes = packed pages + FP16 window"},
+                                f"{ncall} back-to-back calls between HIP events; bytes = packed pages + FP16 window"},
     }
     res["prefill"] = prefill
     if L > 1:

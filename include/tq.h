@@ -299,7 +299,8 @@ TQ_API int64_t tq_decode_workspace_bytes(const tq_ctx* ctx, int batch, int max_p
  *   out: [batch][H_q][d] f32, softmax(q.k * sm_scale) weighted sum of values
  *   over all seq_lens[b] tokens (zeros for an empty sequence);
  *   workspace: >= tq_decode_workspace_bytes(ctx, batch, max_pages, pages_per_split);
- *   pages_per_split: compressed pages per work-group; 0 lets the library choose
+ *   pages_per_split: compressed pages per work-group (at most 64; larger values
+ *   are taken as 64); 0 lets the library choose
  *   from the batch, the block-table width and how many scan work-groups the
  *   device holds at once (the fewest rounds of resident work-groups, each
  *   work-group as long as possible);

@@ -292,13 +292,9 @@ scan_mfma_kernel(DecodeArgs a, DevTables t, Codebooks cb, KParams k) {
       pin[i][1] = p4[1];
     }
   }
+  // the split's page ids (at most kMaxSplitPages = 64: lane j holds page pb + j)
   const int pb = split * a.pages_per_split;
-  auto load_pids = [&](int base) {
-    const int j = base + l;
-    return a.block_table[static_cast<int64_t>(b) * a.max_pages + (j < a.max_pages ? j : 0)];
-  };
-  int pbase = pb;
-  int pids = load_pids(pb);
+  const int pids = a.block_table[static_cast<int64_t>(b) * a.max_pages + (pb + l < a.max_pages ? pb + l : 0)];
   const int T = a.seq_lens[b];
   const int C = T - k.W > 0 ? T - k.W : 0;
   const int npages = (C + k.P - 1) / k.P;
@@ -436,11 +432,7 @@ scan_mfma_kernel(DecodeArgs a, DevTables t, Codebooks cb, KParams k) {
     m.s0 = m.gi * kChunk;
     const int rem = tot - tok0;
     m.pos0 = pg * k.P + m.s0;
-    if (pg - pbase >= 64) {
-      pbase += (pg - pbase) / 64 * 64;
-      pids = load_pids(pbase);
-    }
-    const int pid0 = __builtin_amdgcn_readlane(pids, pg - pbase);
+    const int pid0 = __builtin_amdgcn_readlane(pids, pg - pb);
     const bool bad = pid0 < 0 || pid0 >= a.num_pages;  // flagged, then page 0 is read and the chunk masked
     if (bad && l == 0) atomicOr(t.status, TQ_STATUS_BAD_PAGE);
     m.ntok = __builtin_amdgcn_readfirstlane(bad ? 0 : (rem < kChunk ? rem : kChunk));
@@ -584,9 +576,11 @@ scan_mfma_kernel(DecodeArgs a, DevTables t, Codebooks cb, KParams k) {
       }
       corr[i] = move ? __builtin_amdgcn_exp2f(mrun[i] - mn) : 1.0f;
       mrun[i] = mn;
-      // a dead token has score -inf: weight 0, also while mn is still -inf
-      const float w0 = sc[i][0] == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(sc[i][0] - mn);
-      const float w1 = sc[i][1] == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(sc[i][1] - mn);
+      // a dead token has score -inf and weight exp2(-inf) = 0; while mn is
+      // still -inf every score is, and the reference 0 keeps them at 0
+      const float mref = mn == -INFINITY ? 0.0f : mn;
+      const float w0 = __builtin_amdgcn_exp2f(sc[i][0] - mref);
+      const float w1 = __builtin_amdgcn_exp2f(sc[i][1] - mref);
       lrun[i] = fmaf(lrun[i], corr[i], w0 + w1);
       const int g = 2 * kg + i;
       if (g < G) {

@@ -64,6 +64,7 @@ int decode_splits(int batch, int hkv, int max_pages, int pages_per_split, int sl
     pps = max_pages > 0 ? max_pages : 1;
     for (int s = 1; s <= (max_pages > 0 ? max_pages : 1); ++s) {
       const long long per = (max_pages + s - 1) / s;
+      if (per > tq::kMaxSplitPages) continue;  // a split reads at most kMaxSplitPages pages
       if (s > 1 && per == (max_pages + s - 2) / (s - 1)) continue;  // same pages per split as s - 1
       const long long rounds = (bh * s + sl - 1) / sl;
       const long long cost = rounds * (per + 2);
@@ -74,6 +75,7 @@ int decode_splits(int batch, int hkv, int max_pages, int pages_per_split, int sl
     }
   }
   if (pps > max_pages) pps = max_pages;
+  if (pps > tq::kMaxSplitPages) pps = tq::kMaxSplitPages;
   if (pps < 1) pps = 1;
   if (pps_out) *pps_out = pps;
   const int splits = (max_pages + pps - 1) / pps;

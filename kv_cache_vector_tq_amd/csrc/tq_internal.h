@@ -16,6 +16,7 @@ constexpr int kVGroup = 32;       // value codes are interleaved in 32-token gro
 constexpr uint32_t kMagic = 0x564B5154u;  // "TQKV"
 constexpr int kMaxWindow = 1024;
 constexpr int kMaxPage = 1024;
+constexpr int kMaxSplitPages = 64;  // pages one decode split reads (its page ids fill one wave's lanes)
 constexpr int kNormCodes = 256;   // u8 log-norm codes
 
 // u8 log-norm code of a float32 norm n >= 0 against the boundary table nb
