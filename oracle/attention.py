@@ -71,7 +71,7 @@ def attention_compressed(cache, q, sm_scale):
     q = np.asarray(q, dtype=np.float64)
     B, Hq, d = q.shape
     lay = cache.lay
-    H = lay.H
+    H, D = lay.H, lay.D
     G = Hq // H
     alpha = cache.qjl_coef
     out = np.zeros((B, Hq, d))
@@ -86,11 +86,11 @@ def attention_compressed(cache, q, sm_scale):
                 parts = []
                 if comp is not None:
                     krec, vn, vidx = comp
-                    kidx = cache.kcb.unpack(krec.codes, d)
+                    kidx = cache.kcb.unpack(krec.codes, D)
                     s = krec.norms.astype(np.float64) * (cache.kcb.values(kidx) @ q_rot)
                     if lay.qjl:
                         p = cache.S @ q_rot
-                        pm = 2.0 * codec.unpack_bits(krec.signs, 1, d) - 1.0
+                        pm = 2.0 * codec.unpack_bits(krec.signs, 1, D) - 1.0
                         s = s + alpha * krec.rnorms.astype(np.float64) * (pm @ p)
                     parts.append(s * sm_scale)
                 parts.append((kw @ qg) * sm_scale)
@@ -101,7 +101,7 @@ def attention_compressed(cache, q, sm_scale):
                 m = np.max(l)
                 w = np.exp(l - m)
                 nc = 0 if comp is None else comp[0].norms.shape[0]
-                acc_rot = np.zeros(d)
+                acc_rot = np.zeros(D)
                 if nc:
                     acc_rot = (w[:nc] * vn.astype(np.float64)) @ cache.vcb.values(vidx)
                 acc_win = w[nc:] @ vw

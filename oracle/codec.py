@@ -84,6 +84,8 @@ class Encoded:
 
 def encode(x: np.ndarray, rotation, codebook, qjl_S=None, norm_u8=False) -> Encoded:
     """Encode row vectors x [n, d]; keys pass the QJL matrix, values pass None.
+    The records hold the D = rotation.D transform coordinates (d zero-padded
+    to D when d is not a power of two); codebook and S are built for D.
     ``norm_u8``: the norm is stored as a u8 log-norm code (``oracle.lognorm``);
     the record's float32 norm is then that code's level and the QJL residual
     is taken against it."""
@@ -138,9 +140,10 @@ def dequantize_rotated(codes, norms, codebook, d, signs=None, rnorms=None, qjl_S
 
 
 def dequantize(codes, norms, rotation, codebook, signs=None, rnorms=None, qjl_S=None, qjl_coef=None):
-    """k_hat / v_hat in the original basis."""
-    d = rotation.d
-    return rotation.inverse(dequantize_rotated(codes, norms, codebook, d, signs, rnorms, qjl_S, qjl_coef))
+    """k_hat / v_hat in the original basis (d coordinates; the records hold
+    the D = rotation.D transform coordinates)."""
+    D = rotation.D
+    return rotation.inverse(dequantize_rotated(codes, norms, codebook, D, signs, rnorms, qjl_S, qjl_coef))
 
 
 def qjl_reconstruct(r: np.ndarray, S: np.ndarray, coef: float) -> np.ndarray:

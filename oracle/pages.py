@@ -27,17 +27,20 @@ the library implements, stated here independently of its source):
   body, head h at 256 + h * head_bytes, streams in this order:
     key norms   f32 [P], or u8 [P] log-norm codes (``oracle.lognorm``)
     key rnorms  f32 [P]                (QJL only)
-    key codes   u8  [P][d*bK/8]        token-major, LSB-first per token
-    key signs   u8  [P][d/8]           (QJL only) bit j = sigma_j
+    key codes   u8  [P][D*bK/8]        token-major, LSB-first per token
+    key signs   u8  [P][D/8]           (QJL only) bit j = sigma_j
     value norms f32 [P]
-    value codes u32 [P/32][bV][d]      for each 32-token group and coordinate j
+    value codes u32 [P/32][bV][D]      for each 32-token group and coordinate j
                 the bV words w=0..bV-1 (word w at index [group][w][j]) form a
                 32*bV-bit little-endian string; token i of the group has its
                 code at bits [i*bV, (i+1)*bV).
+  D is the transform size, the next power of two >= head_dim d (records of a
+  head size that is not a power of two hold all D transform coordinates, see
+  ``oracle.rotation``); the header stores d.
   Mixed-channel rates b + 1/2 (``oracle.mixed``): the header bits byte holds
-  b + 16; a key record holds (d/2) b + (d/2)(b+1) bits (low-rate coordinates
-  first); a value group holds a low-rate block u32 [bV][d/2] followed by a
-  high-rate block u32 [bV+1][d/2], coordinates of each half in ascending
+  b + 16; a key record holds (D/2) b + (D/2)(b+1) bits (low-rate coordinates
+  first); a value group holds a low-rate block u32 [bV][D/2] followed by a
+  high-rate block u32 [bV+1][D/2], coordinates of each half in ascending
   order, each coordinate's words forming its 32-token string as above.
   FP16 ring: k_win, v_win [B, H_kv, W, d]; token at position t lives in slot
   t mod W while it is one of the last W tokens.
@@ -46,6 +49,7 @@ the library implements, stated here independently of its source):
 import numpy as np
 
 from . import codec
+from .rotation import transform_dim
 
 MAGIC = 0x564B5154
 FORMAT_VERSION = 1
@@ -58,10 +62,11 @@ V_GROUP = 32
 class Layout:
     def __init__(self, head_dim, key_bits, key_qjl, value_bits, num_kv_heads, page_tokens, key_mixed=False,
                  value_mixed=False, key_norm_u8=False):
-        d, P = head_dim, page_tokens
+        d, P = transform_dim(head_dim), page_tokens
         if P % V_GROUP:
             raise ValueError("page_tokens must be a multiple of 32")
-        self.d, self.bK, self.qjl, self.bV, self.H, self.P = d, key_bits, int(key_qjl), value_bits, num_kv_heads, P
+        self.d, self.D = head_dim, d
+        self.bK, self.qjl, self.bV, self.H, self.P = key_bits, int(key_qjl), value_bits, num_kv_heads, P
         self.kmix, self.vmix = bool(key_mixed), bool(value_mixed)
         self.kn8 = bool(key_norm_u8)
         # code bytes of one key record and of one token's value codes
@@ -130,7 +135,7 @@ def write_key_records(page, lay: Layout, h, slots, rec: codec.Encoded):
     codes[slots] = rec.codes
     if lay.qjl:
         _f32(page, base + lay.k_rnorm, lay.P)[slots] = rec.rnorms
-        sb = lay.d // 8
+        sb = lay.D // 8
         signs = page[base + lay.k_signs: base + lay.k_signs + lay.P * sb].reshape(lay.P, sb)
         signs[slots] = rec.signs
 
@@ -147,7 +152,7 @@ def write_value_records(page, lay: Layout, h, slots, value_cb, rec: codec.Encode
     base = lay.head_base(h)
     _f32(page, base + lay.v_norm, lay.P)[slots] = rec.norms
     words = _v_words(page, lay, h)
-    idx = value_cb.unpack(rec.codes, lay.d)
+    idx = value_cb.unpack(rec.codes, lay.D)
     for s, code_row in zip(np.asarray(slots), idx):
         g, i = divmod(int(s), V_GROUP)
         for wd in np.unique(lay.v_width):
@@ -173,20 +178,20 @@ def read_key_records(page, lay: Layout, h, n):
     signs = rnorms = None
     if lay.qjl:
         rnorms = _f32(page, base + lay.k_rnorm, lay.P)[:n].copy()
-        sb = lay.d // 8
+        sb = lay.D // 8
         signs = page[base + lay.k_signs: base + lay.k_signs + lay.P * sb].reshape(lay.P, sb)[:n].copy()
     return codec.Encoded(codes, norms, signs, rnorms, norm_codes=nc)
 
 
 def read_value_idx(page, lay: Layout, h, n):
-    """Value norms [n] and code indices [n, d] of the first n slots."""
+    """Value norms [n] and code indices [n, D] of the first n slots."""
     base = lay.head_base(h)
     norms = _f32(page, base + lay.v_norm, lay.P)[:n].copy()
     words = _v_words(page, lay, h).astype(np.int64)
-    idx = np.zeros((lay.P, lay.d), dtype=np.int64)
+    idx = np.zeros((lay.P, lay.D), dtype=np.int64)
     for s in range(n):
         g, i = divmod(s, V_GROUP)
-        code = np.zeros(lay.d, dtype=np.int64)
+        code = np.zeros(lay.D, dtype=np.int64)
         for k in range(int(lay.v_width.max())):
             live = k < lay.v_width
             w, pos = np.divmod(i * lay.v_width + k, 32)
@@ -210,7 +215,7 @@ class PagedCache:
     def __init__(self, lay: Layout, rotation, key_cb, value_cb, qjl_S, window, num_pages, batch,
                  max_pages, rotation_kind=0, seed=0, qjl_coef=None):
         self.lay, self.rot, self.kcb, self.vcb, self.S = lay, rotation, key_cb, value_cb, qjl_S
-        self.qjl_coef = codec.qjl_scale(lay.d) if qjl_coef is None else qjl_coef
+        self.qjl_coef = codec.qjl_scale(lay.D) if qjl_coef is None else qjl_coef
         self.W = window
         self.pool = np.zeros((num_pages, lay.page_bytes), dtype=np.uint8)
         self.block_table = np.full((batch, max_pages), -1, dtype=np.int32)

@@ -14,6 +14,19 @@
   the same section replaces it by an orthogonal matrix obtained by QR, here
   the Haar construction of the dense rotation applied to the S draws.
 
+Head sizes that are not a power of two ("TurboQuant Family Design Study",
+same section: zero-pad temporarily during append and the query transform):
+the transform acts on D = the next power of two >= d coordinates; a vector is
+padded with zeros to D, transformed, and all D transform coordinates are
+quantised and stored.  (The page asks not to store padded payload unless a
+kernel proves it worthwhile; keeping only d of the D coordinates would make
+the transform non-invertible and break q.k = (Tq).(Tk), so this reading
+stores them: the padding is what stays temporary, the FP16 vectors and the
+outputs keep d coordinates.)  The dense rotation is padded the same way, a
+Haar D x D matrix applied to the padded vector, i.e. its first d columns, an
+isometry of R^d into R^D.  The inverse transform returns the first d
+coordinates.
+
 The random draws are inputs (they come from ``tq_inputs``); this module only
 does the arithmetic that turns them into the stored matrices.
 """
@@ -67,37 +80,61 @@ def fwht(x: np.ndarray) -> np.ndarray:
     return y
 
 
-class Rotation:
-    """The orthogonal transform Pi used for keys, values and queries.
+def transform_dim(head_dim: int) -> int:
+    """D: the next power of two >= head_dim (the transform's size)."""
+    D = 1
+    while D < head_dim:
+        D *= 2
+    return D
 
-    kind "dense": explicit matrix.  kind "hadamard": y = H_d (eps * x) / sqrt(d),
-    inverse x = eps * (H_d y) / sqrt(d).
+
+class Rotation:
+    """The orthogonal transform Pi used for keys, values and queries, on
+    D = transform_dim(d) coordinates (inputs zero-padded from d to D).
+
+    kind "dense": explicit D x D matrix (draws D x D).  kind "hadamard":
+    y = H_D (eps * x) / sqrt(D) (draws: D values), inverse
+    x = eps * (H_D y) / sqrt(D).
     """
 
     def __init__(self, kind: str, draws: np.ndarray, head_dim: int):
         self.kind = kind
         self.d = head_dim
+        self.D = D = transform_dim(head_dim)
         if kind == "dense":
-            self.matrix = dense_rotation(np.asarray(draws).reshape(head_dim, head_dim))
+            self.matrix = dense_rotation(np.asarray(draws).reshape(D, D))
         elif kind == "hadamard":
-            self.eps = rademacher_signs(np.asarray(draws).reshape(head_dim))
-            self.matrix = sylvester_hadamard(head_dim) * self.eps[None, :] / np.sqrt(head_dim)
+            self.eps = rademacher_signs(np.asarray(draws).reshape(D))
+            self.matrix = sylvester_hadamard(D) * self.eps[None, :] / np.sqrt(D)
         else:
             raise ValueError(kind)
 
-    def forward(self, x: np.ndarray) -> np.ndarray:
-        """Rotate row vectors: returns x @ Pi^T (i.e. Pi x for each row)."""
+    def pad(self, x: np.ndarray) -> np.ndarray:
+        """Row vectors of d coordinates, zero-padded to D."""
         x = np.asarray(x, dtype=np.float64)
+        if x.shape[-1] == self.D:
+            return x
+        out = np.zeros(x.shape[:-1] + (self.D,))
+        out[..., :x.shape[-1]] = x
+        return out
+
+    def forward(self, x: np.ndarray) -> np.ndarray:
+        """Rotate row vectors of d coordinates: returns the D coordinates of
+        Pi [x; 0] for each row."""
+        x = self.pad(x)
         if self.kind == "dense":
             return x @ self.matrix.T
-        return fwht(x * self.eps) / np.sqrt(self.d)
+        return fwht(x * self.eps) / np.sqrt(self.D)
 
     def inverse(self, y: np.ndarray) -> np.ndarray:
-        """Undo ``forward`` on row vectors: returns y @ Pi."""
+        """Undo ``forward`` on row vectors of D coordinates: the first d
+        coordinates of Pi^T y."""
         y = np.asarray(y, dtype=np.float64)
         if self.kind == "dense":
-            return y @ self.matrix
-        return fwht(y) * self.eps / np.sqrt(self.d)
+            full = y @ self.matrix
+        else:
+            full = fwht(y) * self.eps / np.sqrt(self.D)
+        return full[..., :self.d]
 
 
 def qjl_matrix(gauss_draws: np.ndarray, head_dim: int, kind: str = "gaussian") -> np.ndarray:

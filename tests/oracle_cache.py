@@ -19,16 +19,19 @@ class Setup:
         self.kn8 = key_norm_u8
         self.qjl_kind, self.qjl_shrink = qjl_kind, qjl_shrink
         self.rotation, self.seed, self.Hq, self.Hkv, self.P, self.W = rotation, seed, Hq, Hkv, P, W
+        # the transform, codebooks and S act on D = next power of two >= d
+        # coordinates (inputs zero-padded); D = d for the power-of-two sizes
+        self.D = D = rot.transform_dim(d)
         if rotation == "dense":
-            self.rot_draws = tq_inputs.rotation_draws(seed, d)
+            self.rot_draws = tq_inputs.rotation_draws(seed, D)
         else:
-            self.rot_draws = tq_inputs.hadamard_draws(seed, d)
-        self.qjl_draws = tq_inputs.qjl_draws(seed, d)
+            self.rot_draws = tq_inputs.hadamard_draws(seed, D)
+        self.qjl_draws = tq_inputs.qjl_draws(seed, D)
         self.R = rot.Rotation(rotation, self.rot_draws, d)
-        self.kcb = mixed.make_codebook(key_bits, d, "key", key_mixed)
-        self.vcb = mixed.make_codebook(value_bits, d, "value", value_mixed)
-        self.S = rot.qjl_matrix(self.qjl_draws, d, qjl_kind) if key_qjl else None
-        self.qjl_coef = codec.qjl_scale(d, qjl_kind, qjl_shrink)
+        self.kcb = mixed.make_codebook(key_bits, D, "key", key_mixed)
+        self.vcb = mixed.make_codebook(value_bits, D, "value", value_mixed)
+        self.S = rot.qjl_matrix(self.qjl_draws, D, qjl_kind) if key_qjl else None
+        self.qjl_coef = codec.qjl_scale(D, qjl_kind, qjl_shrink)
         # page-header QJL byte: 0 none, 1 Gaussian S, 2 orthogonal S
         self.lay = pages.Layout(d, key_bits, (1 + (qjl_kind == "orthogonal")) if key_qjl else 0, value_bits, Hkv, P,
                                 key_mixed, value_mixed, key_norm_u8)
