@@ -32,26 +32,35 @@
  *    allocated in hot calls.  A tq_ctx is immutable after init apart from its
  *    status word and its profiling slots (tq_profile_begin), so calls on
  *    different streams may share it while profiling is off.
- *  - head_dim d = 128 is the size the kernels are built for.
+ *  - Head size d and transform size D: D is the next power of two >= d.  A
+ *    head size that is not a power of two is zero-padded to D for the
+ *    rotation and the QJL sketch, and its records hold all D transform
+ *    coordinates ("TurboQuant Family Design Study", "Dense and structured
+ *    transform comparison": temporary zero-padding during append and the
+ *    query transform; storing all D coordinates keeps the transform
+ *    invertible, so q.k = (Tq).(Tk) still holds).  FP16 rows, queries and
+ *    outputs hold d coordinates.  The kernels are built for D = 128: head
+ *    sizes 72..128 in steps of 8; tq_codebook_init returns
+ *    TQ_ERR_UNSUPPORTED for other sizes, which the host-only calls accept.
  *
  * Page format (one page = one layer x one sequence x P tokens x all H_kv heads):
  *   page_bytes = roundup(256 + H_kv * head_bytes, 256); 64-byte header at 0
- *   (u32 magic 0x564B5154, u16 version 1, u16 d, u8 key_bits, u8 key QJL
+ *   (u32 magic 0x564B5154, u16 version 1, u16 d (the head size), u8 key_bits, u8 key QJL
  *   (0 none, 1 Gaussian S, 2 orthogonal S),
  *   u8 value_bits, u8 rotation, u16 H_kv, u16 P, u32 valid tokens, u32
  *   codebook version 1, u64 seed, u32 page index, u8 key norm format (0 f32,
  *   1 u8 log-norm), zeros); head h's body at 256 + h * head_bytes holds, in
  *   order: key norms f32[P] (u8[P] codes with key_norm_u8); key residual norms
- *   f32[P] (QJL only); key codes u8[P][d*bK/8] token-major, LSB-first; key
- *   signs u8[P][d/8] (QJL only); value norms f32[P]; value codes
- *   u32[P/32][bV][d], where for each 32-token group and coordinate j the bV
+ *   f32[P] (QJL only); key codes u8[P][D*bK/8] token-major, LSB-first; key
+ *   signs u8[P][D/8] (QJL only); value norms f32[P]; value codes
+ *   u32[P/32][bV][D], where for each 32-token group and coordinate j the bV
  *   words w = 0..bV-1 form a little-endian 32*bV-bit string holding token i's
  *   code at bits [i*bV, (i+1)*bV).
  *   Mixed-channel rates (key_mixed / value_mixed): the header bits byte holds
- *   b + 16; a key record is d*b/8 + d/16 bytes (the d/2 low-rate codes at b
- *   bits, then the d/2 high-rate codes at b + 1 bits, each half in ascending
- *   coordinate order); a value group is a low-rate block u32[bV][d/2] then a
- *   high-rate block u32[bV+1][d/2], coordinates of each half in ascending
+ *   b + 16; a key record is D*b/8 + D/16 bytes (the D/2 low-rate codes at b
+ *   bits, then the D/2 high-rate codes at b + 1 bits, each half in ascending
+ *   coordinate order); a value group is a low-rate block u32[bV][D/2] then a
+ *   high-rate block u32[bV+1][D/2], coordinates of each half in ascending
  *   order, each coordinate's words forming its 32-token string as above.
  * FP16 window: k_win, v_win [B][H_kv][W][d] fp16; the token at position t
  *   lives in slot t mod W while it is among the last W tokens of its sequence.
@@ -103,7 +112,7 @@ enum {
 };
 
 typedef struct tq_params {
-  int32_t head_dim;     /* d; 128 */
+  int32_t head_dim;     /* d, a multiple of 8 (kernels: 72..128) */
   int32_t key_bits;     /* MSE bits per key coordinate, 2..4 */
   int32_t key_qjl;      /* 1: keys carry the QJL sign sketch and residual norm */
   int32_t value_bits;   /* bits per value coordinate, 2..4 */
@@ -115,9 +124,9 @@ typedef struct tq_params {
   int32_t flags;        /* TQ_FLAG_* bits, 0 for the default kernels */
   uint64_t seed;        /* recorded in page headers (cache identity); keys the library's generator
                            when the caller gives no draws or tables */
-  int32_t qjl_kind;     /* TQ_QJL_GAUSSIAN (the paper's S, coefficient sqrt(pi/2)/d) or
+  int32_t qjl_kind;     /* TQ_QJL_GAUSSIAN (the paper's S, coefficient sqrt(pi/2)/D) or
                            TQ_QJL_ORTHOGONAL (S = Haar orthogonal matrix from the same draws,
-                           matched coefficient sqrt(pi/2)/sqrt(d)): "TurboQuant on a 16GB
+                           matched coefficient sqrt(pi/2)/sqrt(D)): "TurboQuant on a 16GB
                            MacBook", "The QJL detective story" */
   float qjl_shrink;     /* factor on the QJL correction term in decode, (0, 4]; 1 = unbiased,
                            2/pi = the MMSE shrinkage for orthogonal S (same section, the 0.7
@@ -158,18 +167,19 @@ TQ_API int tq_seed_draws(uint64_t seed, int stream, int64_t n, double* out);
  * Study", "Dense and structured transform comparison": the Rademacher-sign
  * stage of the Hadamard variant; "TurboQuant on a 16GB MacBook", "The QJL
  * detective story": Gaussian S, or the orthogonal S built by QR).
- * rot_draws: DENSE: d*d i.i.d. N(0,1) values (row-major) whose QR Q factor,
+ * Every table acts on the D = next power of two >= d transform coordinates.
+ * rot_draws: DENSE: D*D i.i.d. N(0,1) values (row-major) whose QR Q factor,
  * with the signs of diag(R) folded in, is the rotation Pi (y = Pi x);
- * HADAMARD: d values whose signs (x < 0 -> -1, else +1) are the Rademacher
- * stage.  qjl_draws: d*d N(0,1) values: the QJL matrix S itself
+ * HADAMARD: D values whose signs (x < 0 -> -1, else +1) are the Rademacher
+ * stage.  qjl_draws: D*D N(0,1) values: the QJL matrix S itself
  * (TQ_QJL_GAUSSIAN; row i gives sign bit i) or the draws its Haar orthogonal S
  * is built from, like the dense rotation (TQ_QJL_ORTHOGONAL).  Either draw
  * pointer may be NULL: the draws then come from the seeded generator
  * (tq_seed_draws with params->seed; streams TQ_DRAWS_ROTATION or
  * TQ_DRAWS_HADAMARD, and TQ_DRAWS_QJL).
- * Outputs (each nullable): rotation d*d f32 (DENSE: Pi row-major; HADAMARD:
- * the d signs), qjl d*d f32, key/value centroids 2^b f32 (Lloyd-Max levels of
- * N(0,1) times 1/sqrt(d), rounded to half-precision values), key/value
+ * Outputs (each nullable): rotation D*D f32 (DENSE: Pi row-major; HADAMARD:
+ * the D signs), qjl D*D f32, key/value centroids 2^b f32 (Lloyd-Max levels of
+ * N(0,1) times 1/sqrt(D), rounded to half-precision values), key/value
  * boundaries 2^b - 1 f32 (midpoints of the stored levels); with a
  * mixed-channel rate the b-bit arrays are followed by the (b+1)-bit ones
  * (2^b + 2^(b+1) centroids, 2^b - 1 + 2^(b+1) - 1 boundaries).
@@ -194,8 +204,8 @@ TQ_API int tq_codebook_init(tq_ctx** out, const tq_params* params, const double*
 
 /* Finished tables given as data (host f32 arrays, read during the call). */
 typedef struct tq_tables {
-  const float* rotation;        /* DENSE: Pi, d*d row-major (y = Pi x); HADAMARD: d signs, each +1 or -1 */
-  const float* qjl;             /* S as used, d*d row-major (sign bit i from row i); ignored without QJL */
+  const float* rotation;        /* DENSE: Pi, D*D row-major (y = Pi x); HADAMARD: D signs, each +1 or -1 */
+  const float* qjl;             /* S as used, D*D row-major (sign bit i from row i); ignored without QJL */
   const float* key_centroids;   /* 2^bK ascending levels (2^bK then 2^(bK+1) for a mixed key rate) */
   const float* value_centroids; /* likewise for values */
 } tq_tables;
@@ -232,9 +242,10 @@ TQ_API int64_t tq_page_bytes(const tq_params* params);
  * "The QJL detective story" for the key correction):
  *   out[i] = Pi^T ( norms[i] c[codes[i]] + a rnorms[i] S^T (2 sigma_i - 1) )
  * with the correction only for keys with key_qjl and a the context's QJL
- * coefficient: qjl_shrink * sqrt(pi/2)/d for Gaussian S, qjl_shrink *
- * sqrt(pi/2)/sqrt(d) for orthogonal S.  Record layouts as in
- * tq_encode; out: [n][d] f32.  For quality measurements against exact
+ * coefficient: qjl_shrink * sqrt(pi/2)/D for Gaussian S, qjl_shrink *
+ * sqrt(pi/2)/sqrt(D) for orthogonal S.  Record layouts as in
+ * tq_encode; out: [n][d] f32, the first d of the D coordinates of
+ * Pi^T (...).  For quality measurements against exact
  * attention; the decode path never dequantises. */
 TQ_API int tq_decode(const tq_ctx* ctx, int kind, const uint8_t* codes, const uint8_t* signs, const float* norms,
                      const float* rnorms, int64_t n, float* out, void* stream);
@@ -243,12 +254,13 @@ TQ_API int tq_decode(const tq_ctx* ctx, int kind, const uint8_t* codes, const ui
  * README, "Algorithm": norm, rotation, Lloyd-Max codes, LSB-first packing;
  * "TurboQuant on a 16GB MacBook", "Why this caught my eye": the keys' 1-bit
  * QJL sketch of the residual, with the residual's norm):
- *   x: [n][row_stride] elements of dtype (F16, BF16 or F32), first d used;
- *   codes: [n][d*b/8] u8 LSB-first, b = key_bits or value_bits by kind
- *   ([n][d*b/8 + d/16] for a mixed-channel rate, layout as in the page);
+ *   x: [n][row_stride] elements of dtype (F16, BF16 or F32), first d used
+ *   (zero-padded to D);
+ *   codes: [n][D*b/8] u8 LSB-first, b = key_bits or value_bits by kind
+ *   ([n][D*b/8 + D/16] for a mixed-channel rate, layout as in the page);
  *   norms: [n] f32 L2 norms (keys with key_norm_u8: the u8 log-norm level each norm is
  *   stored as, 2^(q/16 - 4) or 0, against which the key's QJL residual is taken);
- *   signs: [n][d/8] u8 and rnorms: [n] f32, required iff kind == KEY and key_qjl.
+ *   signs: [n][D/8] u8 and rnorms: [n] f32, required iff kind == KEY and key_qjl.
  * A vector with zero norm gets all-zero codes, signs and rnorm ("TurboQuant
  * on a 16GB MacBook", "Round 2: the llama.cpp bug hunt": the zero-block fix).
  * TQ_ERR_INVALID_ARG for null or misaligned pointers (x to its element size,
@@ -291,7 +303,7 @@ TQ_API int64_t tq_decode_workspace_bytes(const tq_ctx* ctx, int batch, int max_p
  * and "CPU and WASM kernel design": packed keys scored in the compressed
  * domain, values accumulated in the rotated basis, one inverse transform per
  * head; "TurboQuant on a 16GB MacBook", "The QJL detective story": the QJL
- * correction at scale sqrt(pi/2)/d).
+ * correction at scale sqrt(pi/2)/D).
  *   q: [batch][H_q][d] post-RoPE queries, dtype F16, BF16 or F32;
  *   cache arguments as in tq_append_page (seq_lens[b] tokens, at most
  *   max_pages * P + W);

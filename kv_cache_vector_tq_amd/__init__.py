@@ -157,11 +157,20 @@ def tq_seed_draws(seed, stream, n):
     return out
 
 
+def transform_dim(head_dim):
+    """D: the next power of two >= head_dim (records and tables hold D coordinates)."""
+    D = 1
+    while D < head_dim:
+        D *= 2
+    return D
+
+
 def tq_host_tables(params, rot_draws=None, qjl_draws=None, qjl=True):
     """Library-side tables computed on the host (no GPU): dict of numpy arrays.
     Draws left as None come from the library's seeded generator (the QJL
-    matrix only when ``qjl``)."""
-    d = params.head_dim
+    matrix only when ``qjl``).  The tables act on D = transform_dim(head_dim)
+    coordinates."""
+    d = transform_dim(params.head_dim)
     rot = np.zeros(d * d if params.rotation == TQ_ROT_DENSE else d, np.float32)
     S = np.zeros(d * d, np.float32) if (qjl_draws is not None or qjl) else None
     # a mixed-channel rate appends the (b+1)-bit codebook to the b-bit one

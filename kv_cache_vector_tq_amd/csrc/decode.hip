@@ -112,6 +112,8 @@ __global__ __launch_bounds__(kSmallThreads) void prep_kernel(DecodeArgs a, DevTa
   const int nhs = k.G / GW;
   const int tid = threadIdx.x, h = blockIdx.x / nhs, g0 = (blockIdx.x % nhs) * GW, b = blockIdx.y;
   const int64_t row0 = (static_cast<int64_t>(b) * k.Hq + static_cast<int64_t>(h) * k.G + g0) * kD;
+  // the caller's query rows hold d coordinates; they are zero-padded to kD here
+  const int64_t qin0 = (static_cast<int64_t>(b) * k.Hq + static_cast<int64_t>(h) * k.G + g0) * k.d;
   const float c2 = a.sm_scale * kLog2e;
   // both tables, then the query: all in flight together (the query's loads
   // sit behind one branch on its dtype, whose join waits for every load issued)
@@ -125,7 +127,7 @@ __global__ __launch_bounds__(kSmallThreads) void prep_kernel(DecodeArgs a, DevTa
 #pragma unroll
     for (int u = 0; u < kNq; ++u) {
       const int e = tid + u * kSmallThreads;
-      qin[u] = e < GW * kD ? q32[row0 + e] : 0.0f;
+      qin[u] = (e < GW * kD && e % kD < k.d) ? q32[qin0 + (e / kD) * k.d + e % kD] : 0.0f;
     }
   } else {
     const uint16_t* q16 = static_cast<const uint16_t*>(a.q);
@@ -133,7 +135,7 @@ __global__ __launch_bounds__(kSmallThreads) void prep_kernel(DecodeArgs a, DevTa
 #pragma unroll
     for (int u = 0; u < kNq; ++u) {
       const int e = tid + u * kSmallThreads;
-      raw[u] = e < GW * kD ? q16[row0 + e] : 0;
+      raw[u] = (e < GW * kD && e % kD < k.d) ? q16[qin0 + (e / kD) * k.d + e % kD] : 0;
     }
 #pragma unroll
     for (int u = 0; u < kNq; ++u)
@@ -380,6 +382,8 @@ __global__ __launch_bounds__(kSmallThreads) void merge_kernel(DecodeArgs a, DevT
   const int T = a.seq_lens[b];
   const int nwin = T < k.W ? T : k.W;
   const int64_t row0 = (static_cast<int64_t>(b) * k.Hq + static_cast<int64_t>(h) * k.G + g0) * kD;
+  // output rows and FP16 window rows hold d coordinates (d <= kD, a multiple of 8)
+  const int64_t orow0 = (static_cast<int64_t>(b) * k.Hq + static_cast<int64_t>(h) * k.G + g0) * k.d;
   const int64_t bh = static_cast<int64_t>(b) * k.Hkv + h;
   const bool dense = k.rotation == TQ_ROT_DENSE;
 
@@ -410,18 +414,21 @@ __global__ __launch_bounds__(kSmallThreads) void merge_kernel(DecodeArgs a, DevT
   for (int u = 0; u < kFirst; ++u) la[u] = sub + u * nsub < a.splits ? la[u] : 0.0f;
   // window keys: thread pair (tk, half) holds slot tk = tid / 2, coordinates 64 half ..
   const int tk0 = tid >> 1, half = tid & 1;
+  // (coordinates past d read as zero)
   uint4 kv[8];
   if (tk0 < nwin) {
-    const uint4* kr = reinterpret_cast<const uint4*>(a.k_win + (bh * k.W + tk0) * kD + 64 * half);
+    const uint4* kr = reinterpret_cast<const uint4*>(a.k_win + (bh * k.W + tk0) * k.d + 64 * half);
 #pragma unroll
-    for (int c = 0; c < 8; ++c) kv[c] = kr[c];
+    for (int c = 0; c < 8; ++c) kv[c] = 64 * half + 8 * c < k.d ? kr[c] : make_uint4(0u, 0u, 0u, 0u);
   }
   // window values: thread (c4, q8) holds slots q8, q8 + 8, ... (first 16), coordinates c4 .. c4+3
-  const uint16_t* vbase = a.v_win + bh * k.W * kD + c4;
+  // (threads with c4 >= d read slot 0's first coordinates and discard them)
+  const bool vlive = c4 < k.d;
+  const uint16_t* vbase = a.v_win + bh * k.W * k.d + (vlive ? c4 : 0);
   uint2 vv[16];
 #pragma unroll
   for (int u = 0; u < 16; ++u)
-    if (q8 + 8 * u < nwin) vv[u] = *reinterpret_cast<const uint2*>(vbase + static_cast<int64_t>(q8 + 8 * u) * kD);
+    if (q8 + 8 * u < nwin) vv[u] = *reinterpret_cast<const uint2*>(vbase + static_cast<int64_t>(q8 + 8 * u) * k.d);
   // columns c4 .. c4+3 of Pi, rows 16 q8 .. 16 q8 + 15 (dense rotation)
   float4 rm[16];
   if (dense) {
@@ -520,9 +527,9 @@ __global__ __launch_bounds__(kSmallThreads) void merge_kernel(DecodeArgs a, DevT
   for (int e = tid; e < 2 * nwin; e += kSmallThreads) {
     const int tk = e >> 1;
     if (e >= kSmallThreads) {
-      const uint4* kr = reinterpret_cast<const uint4*>(a.k_win + (bh * k.W + tk) * kD + 64 * half);
+      const uint4* kr = reinterpret_cast<const uint4*>(a.k_win + (bh * k.W + tk) * k.d + 64 * half);
 #pragma unroll
-      for (int c = 0; c < 8; ++c) kv[c] = kr[c];
+      for (int c = 0; c < 8; ++c) kv[c] = 64 * half + 8 * c < k.d ? kr[c] : make_uint4(0u, 0u, 0u, 0u);
     }
     float sg[GW];
 #pragma unroll
@@ -593,9 +600,10 @@ __global__ __launch_bounds__(kSmallThreads) void merge_kernel(DecodeArgs a, DevT
     for (int u = 0; u < 16; ++u)
       if (q8 + 8 * u < nwin) add(q8 + 8 * u, vv[u]);
     for (int tk = q8 + 128; tk < nwin; tk += 8)
-      add(tk, *reinterpret_cast<const uint2*>(vbase + static_cast<int64_t>(tk) * kD));
+      add(tk, *reinterpret_cast<const uint2*>(vbase + static_cast<int64_t>(tk) * k.d));
 #pragma unroll
-    for (int g = 0; g < GW; ++g) *reinterpret_cast<float4*>(&part[q8][g][c4]) = acc[g];
+    for (int g = 0; g < GW; ++g)
+      *reinterpret_cast<float4*>(&part[q8][g][c4]) = vlive ? acc[g] : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
   }
   lds_barrier();
   for (int e = tid; e < GW * kD; e += kSmallThreads) {
@@ -641,7 +649,7 @@ __global__ __launch_bounds__(kSmallThreads) void merge_kernel(DecodeArgs a, DevT
     float L = 0.0f;
     for (int r = 0; r < 8 / GW; ++r) L += sL[r][g];
     const float Ltot = fmaf(L, corr, sLw[g]);
-    a.out[row0 + e] = Ltot > 0.0f ? fmaf(accr[g][i], corr, ow[g][i]) / Ltot : 0.0f;
+    if (i < k.d) a.out[orow0 + g * k.d + i] = Ltot > 0.0f ? fmaf(accr[g][i], corr, ow[g][i]) / Ltot : 0.0f;
   }
 }
 

@@ -9,6 +9,7 @@ namespace tq {
 
 struct KParams {
   int Hq, Hkv, G, P, W;
+  int d;  // head size: coordinates of q, out and the FP16 window rows (the rest use D)
   int64_t page_bytes, head_bytes, k_norm, k_rnorm, k_codes, k_signs, v_norm, v_codes;
   int rotation;
   float qjl_scale;
@@ -21,6 +22,7 @@ inline KParams make_kparams(const tq_ctx* c) {
   k.G = k.Hq / k.Hkv;
   k.P = c->p.page_tokens;
   k.W = c->p.window;
+  k.d = c->p.head_dim;
   k.page_bytes = c->lay.page_bytes;
   k.head_bytes = c->lay.head_bytes;
   k.k_norm = c->lay.k_norm;
@@ -30,9 +32,9 @@ inline KParams make_kparams(const tq_ctx* c) {
   k.v_norm = c->lay.v_norm;
   k.v_codes = c->lay.v_codes;
   k.rotation = c->p.rotation;
-  // QJL coefficient: sqrt(pi/2)/d for Gaussian S, sqrt(pi/2)/sqrt(d) for
-  // orthogonal S, times the shrinkage factor
-  const double dd = static_cast<double>(c->p.head_dim);
+  // QJL coefficient: sqrt(pi/2)/D for Gaussian S, sqrt(pi/2)/sqrt(D) for
+  // orthogonal S (S has D rows), times the shrinkage factor
+  const double dd = static_cast<double>(c->lay.D);
   const double base = c->p.qjl_kind == TQ_QJL_ORTHOGONAL ? 1.2533141373155003 / std::sqrt(dd)
                                                           : 1.2533141373155003 / dd;
   k.qjl_scale = static_cast<float>(base * static_cast<double>(c->p.qjl_shrink));

@@ -24,7 +24,8 @@ struct DequantArgs {
   const float* norms;
   const float* rnorms;
   int64_t n;
-  float* out;
+  float* out;  // rows of d coordinates (the first d of the D the records hold)
+  int d;
   int bits;
   int qjl;
   int hmod;  // mixed-channel rate: coordinate j has bits + 1 when j mod hmod >= hmod/2; 0: integer rate
@@ -109,7 +110,7 @@ __global__ __launch_bounds__(kThreads) void dequant_kernel(DequantArgs a, DevTab
         x = fmaf(prow[4 * j4 + 2], u.z, x);
         x = fmaf(prow[4 * j4 + 3], u.w, x);
       }
-      a.out[(v0 + v) * kD + tid] = x;
+      if (tid < a.d) a.out[(v0 + v) * a.d + tid] = x;
     }
   } else {
     // x_hat = eps . H u / sqrt(d): butterflies 1..32 in the wave, 64 through LDS
@@ -125,7 +126,7 @@ __global__ __launch_bounds__(kThreads) void dequant_kernel(DequantArgs a, DevTab
       us[v][tid] = val;
       __syncthreads();
       const float p = us[v][tid], q = us[v][tid ^ 64];
-      a.out[(v0 + v) * kD + tid] = ((tid & 64) ? (q - p) : (p + q)) * 0.08838834764831845f * eps;
+      if (tid < a.d) a.out[(v0 + v) * a.d + tid] = ((tid & 64) ? (q - p) : (p + q)) * 0.08838834764831845f * eps;
     }
   }
 }
@@ -142,6 +143,7 @@ int launch_dequant(const tq_ctx* c, int kind, const uint8_t* codes, const uint8_
   a.rnorms = rnorms;
   a.n = n;
   a.out = out;
+  a.d = c->p.head_dim;
   a.bits = key ? c->p.key_bits : c->p.value_bits;
   a.qjl = (key && c->p.key_qjl) ? 1 : 0;
   a.coef = make_kparams(c).qjl_scale;

@@ -246,8 +246,9 @@ __global__ __launch_bounds__(kThreads) void encode_flat_kernel(EncodeArgs a, Dev
   const int tid = threadIdx.x;
   const int64_t n0 = static_cast<int64_t>(blockIdx.x) * kTile;
   const int nv = static_cast<int>(a.n - n0 < kTile ? a.n - n0 : kTile);
+  // rows of d coordinates, zero-padded to kD
   for (int v = 0; v < kTile; ++v)
-    sm.xs[v][tid] = v < nv ? load_any(a.x, (n0 + v) * a.row_stride + tid, dtype) : 0.0f;
+    sm.xs[v][tid] = (v < nv && tid < a.d) ? load_any(a.x, (n0 + v) * a.row_stride + tid, dtype) : 0.0f;
   __syncthreads();
   const CoreParams cp = make_core(cb, kind == TQ_KIND_KEY, bits, qjl != 0, mixed != 0, n8 != 0);
   encode_core<HAD>(sm, t, cp, 0, nv);
@@ -314,17 +315,18 @@ __device__ inline SeqPlan plan_seq(const AppendArgs& a, const Layout& L, int W, 
 // the work-group that encodes q - W (after that one has read the slot), or
 // evicts nothing and is written by the first work-group; no slot is read by
 // one work-group and written by another.
-__device__ inline void ring_owned(const AppendArgs& a, const SeqPlan& sp, int W, int64_t bh, int kv, int gr,
+__device__ inline void ring_owned(const AppendArgs& a, const SeqPlan& sp, int W, int d, int64_t bh, int kv, int gr,
                                   int tid) {
   const int j0 = sp.cnt > W ? sp.cnt - W : 0;
   const int g0 = sp.c0 / kVGroup;
+  if (tid >= d) return;  // rows hold d coordinates
   for (int j = j0; j < sp.cnt; ++j) {
     const int q = sp.T0 + j;
     if ((q >= W ? (q - W) / kVGroup - g0 : 0) != gr) continue;
     if (kv == 0)
-      a.k_win[(bh * W + q % W) * kD + tid] = a.k_new[(bh * a.n_new + j) * kD + tid];
+      a.k_win[(bh * W + q % W) * d + tid] = a.k_new[(bh * a.n_new + j) * d + tid];
     else
-      a.v_win[(bh * W + q % W) * kD + tid] = a.v_new[(bh * a.n_new + j) * kD + tid];
+      a.v_win[(bh * W + q % W) * d + tid] = a.v_new[(bh * a.n_new + j) * d + tid];
   }
 }
 
@@ -344,10 +346,10 @@ __device__ void encode_group(Smem& sm, const AppendArgs& a, const DevTables& t, 
     const uint16_t* src = kv == 0 ? a.k_new : a.v_new;
     for (int v = 0; v < kTile; ++v) {
       const int pos = gpos + v;
-      float x = 0.0f;
-      if (pos >= lo && pos < hi) {
-        const uint16_t bits = pos < sp.T0 ? win[(bh * W + pos % W) * kD + tid]
-                                          : src[(bh * a.n_new + (pos - sp.T0)) * kD + tid];
+      float x = 0.0f;  // (coordinates past d: zero padding)
+      if (pos >= lo && pos < hi && tid < L.d) {
+        const uint16_t bits = pos < sp.T0 ? win[(bh * W + pos % W) * L.d + tid]
+                                          : src[(bh * a.n_new + (pos - sp.T0)) * L.d + tid];
         x = half_bits_to_float(bits);
       }
       sm.xs[v][tid] = x;
@@ -425,7 +427,7 @@ __global__ __launch_bounds__(kThreads) void append_encode_kernel(AppendArgs a, D
   const int g = sp.c0 / kVGroup + gr;
   const int gpos = g * kVGroup;
   if (sp.c1 > sp.c0 && gpos < sp.c1 && ((kinds >> kv) & 1)) encode_group<HAD>(sm, a, t, cb, L, W, sp, b, h, kv, gpos);
-  if (ring) ring_owned(a, sp, W, static_cast<int64_t>(b) * L.H + h, kv, gr, tid);
+  if (ring) ring_owned(a, sp, W, L.d, static_cast<int64_t>(b) * L.H + h, kv, gr, tid);
 }
 
 // ------------------------------------------------------------ few-token append
@@ -517,10 +519,15 @@ __global__ __launch_bounds__(kSmallThreads) void append_small_kernel(AppendArgs 
   // (loads in this kernel are unconditional, from clamped indices: a load
   // under a branch makes the branch's join wait for every load in flight)
   const int j0 = cnt > W ? cnt - W : 0;
+  // FP16 rows hold d coordinates: threads of coordinates past d read
+  // coordinate 0 (discarded) and take zero padding
+  const int d = L.d;
+  const bool live = i < d;
+  const int ic = live ? i : 0;
   uint16_t rnew[kSmallNew];
   if (ring && lower && cnt > 0) {
 #pragma unroll
-    for (int j = 0; j < kSmallNew; ++j) rnew[j] = src[(bh * a.n_new + (j0 + j < cnt ? j0 + j : cnt - 1)) * kD + i];
+    for (int j = 0; j < kSmallNew; ++j) rnew[j] = src[(bh * a.n_new + (j0 + j < cnt ? j0 + j : cnt - 1)) * d + ic];
   }
   int pid0 = 0, pid1 = 0;
   if (nv > 0) {
@@ -535,17 +542,17 @@ __global__ __launch_bounds__(kSmallThreads) void append_small_kernel(AppendArgs 
 #pragma unroll
     for (int v = 0; v < kSmallNew; ++v) {
       const int pos = c0 + (v < nv ? v : nv - 1);
-      const uint16_t* p = pos < T0 ? win + (bh * W + pos % W) * kD : src + (bh * a.n_new + (pos - T0)) * kD;
-      xr[v] = p[i];
+      const uint16_t* p = pos < T0 ? win + (bh * W + pos % W) * d : src + (bh * a.n_new + (pos - T0)) * d;
+      xr[v] = p[ic];
     }
 #pragma unroll
-    for (int v = 0; v < kSmallNew; ++v) sm.xs[v][i] = v < nv ? half_bits_to_float(xr[v]) : 0.0f;
+    for (int v = 0; v < kSmallNew; ++v) sm.xs[v][i] = (v < nv && live) ? half_bits_to_float(xr[v]) : 0.0f;
   }
   auto ring_store = [&]() {
-    if (ring && lower) {
+    if (ring && lower && live) {
 #pragma unroll
       for (int j = 0; j < kSmallNew; ++j)
-        if (j0 + j < cnt) wdst[(bh * W + (T0 + j0 + j) % W) * kD + i] = rnew[j];
+        if (j0 + j < cnt) wdst[(bh * W + (T0 + j0 + j) % W) * d + i] = rnew[j];
     }
   };
   if (nv == 0) {  // nothing leaves the window: no slot is read
@@ -757,10 +764,12 @@ __global__ __launch_bounds__(kThreads) void append_ring_kernel(AppendArgs a, Dev
   if (!sp.ok) return;
   const int64_t bh = static_cast<int64_t>(b) * L.H + h;
   const int j0 = sp.cnt > W ? sp.cnt - W : 0;
+  const int d = L.d;  // rows hold d coordinates
+  if (tid >= d) return;
   for (int j = j0; j < sp.cnt; ++j) {
     const int pos = sp.T0 + j;
-    a.k_win[(bh * W + pos % W) * kD + tid] = a.k_new[(bh * a.n_new + j) * kD + tid];
-    a.v_win[(bh * W + pos % W) * kD + tid] = a.v_new[(bh * a.n_new + j) * kD + tid];
+    a.k_win[(bh * W + pos % W) * d + tid] = a.k_new[(bh * a.n_new + j) * d + tid];
+    a.v_win[(bh * W + pos % W) * d + tid] = a.v_new[(bh * a.n_new + j) * d + tid];
   }
 }
 

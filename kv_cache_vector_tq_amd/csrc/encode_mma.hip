@@ -378,9 +378,10 @@ void encode_mma_kernel(EncodeArgs a, DevTables t, EncCodebook cbk) {
     for (int c = 0; c < kCols; ++c) {
       vid[c] = tile * kTileVec + 16 * c + n;
       live[c] = vid[c] < a.n;
+      // (rows of d coordinates: the 8-coordinate chunks past d are zero padding)
       const u4* src = reinterpret_cast<const u4*>(X + (live[c] ? vid[c] : 0) * a.row_stride + 32 * kg);
 #pragma unroll
-      for (int s = 0; s < 4; ++s) xb[c][s] = live[c] ? src[s] : u4{0u, 0u, 0u, 0u};
+      for (int s = 0; s < 4; ++s) xb[c][s] = (live[c] && 32 * kg + 8 * s < a.d) ? src[s] : u4{0u, 0u, 0u, 0u};
     }
     // stores: this lane's BITS words of the code stream, the norm, ||r||, the sign word
     encode_tile<QJL, HAD, BITS, N8, kCols>(
@@ -478,9 +479,10 @@ void append_mma_kernel(AppendArgs a, DevTables t, EncCodebook cbk, Layout L, int
         // (a dead lane reads row 0 of the new rows, which always exist, and discards it)
         const bool ring = live[c] && p < T0;
         const int64_t row = !live[c] ? 0 : ring ? (bh * W + p % W) : (bh * a.n_new + (p - T0));
-        const u4* rp = reinterpret_cast<const u4*>((ring ? win : src) + row * kD + 32 * kg);
+        // (rows of d coordinates: the 8-coordinate chunks past d are zero padding)
+        const u4* rp = reinterpret_cast<const u4*>((ring ? win : src) + row * L.d + 32 * kg);
 #pragma unroll
-        for (int s = 0; s < 4; ++s) xb[c][s] = live[c] ? rp[s] : u4{0u, 0u, 0u, 0u};
+        for (int s = 0; s < 4; ++s) xb[c][s] = (live[c] && 32 * kg + 8 * s < L.d) ? rp[s] : u4{0u, 0u, 0u, 0u};
       }
       encode_tile<QJL, HAD, BITS, N8, kCols>(
           fragP, fragS, ctab, emask, cbk, t.ntab, xb,
@@ -564,7 +566,7 @@ const void* pick_append_key(int bits, bool n8) {
 // This kind's codebook, if the matrix-core path takes it: an integer rate
 // with a symmetric codebook (the binary-search quantiser relies on it).
 bool mma_codebook(const tq_ctx* c, bool key, EncCodebook& cbk) {
-  if (c->p.head_dim != kD || (key ? c->p.key_mixed : c->p.value_mixed)) return false;
+  if (c->lay.D != kD || (key ? c->p.key_mixed : c->p.value_mixed)) return false;
   const int bits = key ? c->p.key_bits : c->p.value_bits;
   for (int k = 0; k < 16; ++k) {
     cbk.cen[k] = key ? c->cb.kc[k] : c->cb.vc[k];

@@ -15,22 +15,22 @@ namespace {
 
 bool params_ok(const tq_params* p) {
   if (!p) return false;
-  if (p->head_dim <= 0 || p->head_dim % 8) return false;
+  if (p->head_dim <= 0 || p->head_dim % 8 || p->head_dim > 4096) return false;
   if (p->key_bits < 2 || p->key_bits > 4 || p->value_bits < 2 || p->value_bits > 4) return false;
   if (p->key_qjl != 0 && p->key_qjl != 1) return false;
   if (p->rotation != TQ_ROT_DENSE && p->rotation != TQ_ROT_HADAMARD) return false;
-  if (p->rotation == TQ_ROT_HADAMARD && (p->head_dim & (p->head_dim - 1))) return false;
   if (p->num_q_heads <= 0 || p->num_kv_heads <= 0 || p->num_q_heads % p->num_kv_heads) return false;
   if (p->page_tokens <= 0 || p->page_tokens % tq::kVGroup || p->page_tokens > tq::kMaxPage) return false;
   if (p->window < 0 || p->window > tq::kMaxWindow) return false;
   if (p->flags & ~(TQ_FLAG_VALU_SCAN | TQ_FLAG_VALU_APPEND)) return false;
   if (p->qjl_kind != TQ_QJL_GAUSSIAN && p->qjl_kind != TQ_QJL_ORTHOGONAL) return false;
   if (!(p->qjl_shrink > 0.0f && p->qjl_shrink <= 4.0f)) return false;  // also rejects NaN
-  // mixed-channel rates: 2.5 and 3.5 bits, halves of a multiple of 32 coordinates
+  // mixed-channel rates: 2.5 and 3.5 bits, halves of a multiple of 32 transform coordinates
   if (p->key_mixed != 0 && p->key_mixed != 1) return false;
   if (p->value_mixed != 0 && p->value_mixed != 1) return false;
-  if (p->key_mixed && (p->key_bits < 2 || p->key_bits > 3 || p->head_dim % 32)) return false;
-  if (p->value_mixed && (p->value_bits < 2 || p->value_bits > 3 || p->head_dim % 32)) return false;
+  const int D = tq::transform_dim(p->head_dim);
+  if (p->key_mixed && (p->key_bits < 2 || p->key_bits > 3 || D % 32)) return false;
+  if (p->value_mixed && (p->value_bits < 2 || p->value_bits > 3 || D % 32)) return false;
   if (p->key_norm_u8 != 0 && p->key_norm_u8 != 1) return false;
   return true;
 }
@@ -40,7 +40,9 @@ bool params_supported(const tq_params* p) {
   const int G = p->num_q_heads / p->num_kv_heads;
   // the vector-ALU scan covers integer rates only
   if ((p->flags & TQ_FLAG_VALU_SCAN) && (p->key_mixed || p->value_mixed || p->key_norm_u8)) return false;
-  return p->head_dim == tq::kD && (G == 1 || G == 2 || G == 4 || G == 8) && p->num_kv_heads <= 65535;
+  // head sizes 72 .. 128 (transform size 128)
+  return tq::transform_dim(p->head_dim) == tq::kD && (G == 1 || G == 2 || G == 4 || G == 8) &&
+         p->num_kv_heads <= 65535;
 }
 
 bool aligned(const void* ptr, size_t a) { return (reinterpret_cast<uintptr_t>(ptr) % a) == 0; }
@@ -88,7 +90,7 @@ struct WsLayout {
 
 WsLayout ws_layout(const tq_params& p, int batch, int splits) {
   const int G = p.num_q_heads / p.num_kv_heads;
-  const size_t d = p.head_dim;
+  const size_t d = tq::transform_dim(p.head_dim);  // workspace rows hold D coordinates
   const size_t bq = static_cast<size_t>(batch) * p.num_q_heads;
   const size_t nb = static_cast<size_t>(batch) * p.num_kv_heads * splits * G;
   auto up = [](size_t x) { return (x + 255) / 256 * 256; };
@@ -137,7 +139,8 @@ TQ_API int tq_host_tables(const tq_params* p, const double* rot_draws, const dou
                           float* qjl, float* key_centroids, float* key_boundaries, float* value_centroids,
                           float* value_boundaries) {
   if (!params_ok(p)) return TQ_ERR_INVALID_ARG;
-  const int d = p->head_dim;
+  // tables act on the transform size D (rows zero-padded from head_dim)
+  const int d = tq::transform_dim(p->head_dim);
   // draws not given: the seeded generator's streams
   std::vector<double> gen_rot, gen_qjl;
   if (!rot_draws && rotation) {
@@ -209,7 +212,7 @@ bool caller_codebook(const float* cen, int bits, bool mixed, float* c, float* bn
 int init_ctx(tq_ctx** out, const tq_params* p, const float* rot_in, const float* S_in, const float* kc,
              const float* kb, const float* vc, const float* vb, void* stream) {
   *out = nullptr;
-  const int d = p->head_dim;
+  const int d = tq::transform_dim(p->head_dim);  // table size D
   tq_ctx* c = new (std::nothrow) tq_ctx();
   if (!c) return TQ_ERR_HIP;
   c->p = *p;
@@ -323,7 +326,7 @@ TQ_API int tq_codebook_init(tq_ctx** out, const tq_params* p, const double* rot_
   if (!out || !params_ok(p)) return TQ_ERR_INVALID_ARG;
   if (!params_supported(p)) return TQ_ERR_UNSUPPORTED;
   *out = nullptr;
-  const int d = p->head_dim;
+  const int d = tq::transform_dim(p->head_dim);  // table size D
   std::vector<float> rot(d * d, 0.0f), S(d * d, 0.0f);
   float kc[48] = {}, kb[48] = {}, vc[48] = {}, vb[48] = {};
   const int rc =
@@ -336,7 +339,7 @@ TQ_API int tq_codebook_init_tables(tq_ctx** out, const tq_params* p, const tq_ta
   if (!out || !params_ok(p)) return TQ_ERR_INVALID_ARG;
   if (!params_supported(p)) return TQ_ERR_UNSUPPORTED;
   *out = nullptr;
-  const int d = p->head_dim;
+  const int d = tq::transform_dim(p->head_dim);  // table size D
   const tq_tables none = {nullptr, nullptr, nullptr, nullptr};
   const tq_tables& t = tables ? *tables : none;
   // the seeded tables for whatever the caller leaves out
@@ -435,7 +438,7 @@ TQ_API int tq_encode(const tq_ctx* c, int kind, const void* x, int dtype, int64_
   if (!aligned(x, esz) || !aligned(codes, 4) || !aligned(norms, 4) || (qjl && (!aligned(signs, 4) || !aligned(rnorms, 4))))
     return TQ_ERR_INVALID_ARG;
   if (n > (int64_t(1) << 40)) return TQ_ERR_INVALID_ARG;
-  tq::EncodeArgs a{x, n, row_stride, codes, qjl ? signs : nullptr, norms, qjl ? rnorms : nullptr};
+  tq::EncodeArgs a{x, n, row_stride, c->p.head_dim, codes, qjl ? signs : nullptr, norms, qjl ? rnorms : nullptr};
   return tq::launch_encode(c, kind, dtype, a, stream) == 0 ? TQ_OK : TQ_ERR_HIP;
 }
 

@@ -10,7 +10,7 @@
 
 namespace tq {
 
-constexpr int kD = 128;           // head_dim the kernels are built for
+constexpr int kD = 128;           // transform size D the kernels are built for (head_dim 72..128)
 constexpr int kBodyOffset = 256;  // page body starts after the 64-byte header and padding
 constexpr int kVGroup = 32;       // value codes are interleaved in 32-token groups
 constexpr uint32_t kMagic = 0x564B5154u;  // "TQKV"
@@ -32,6 +32,18 @@ __host__ __device__ inline int norm_code(float n, const float* nb) {
   return q;
 }
 
+// Transform size D for head size d: the next power of two >= d.  A head
+// size that is not a power of two is zero-padded to D for the rotation and
+// its records hold all D transform coordinates ("TurboQuant Family Design
+// Study", section "Dense and structured transform comparison": temporary
+// zero-padding during append and the query transform); FP16 rows, queries
+// and outputs keep d coordinates.
+__host__ __device__ inline int transform_dim(int d) {
+  int D = 1;
+  while (D < d) D *= 2;
+  return D;
+}
+
 // Host table builders (tables.cpp).
 std::vector<double> lloyd_max_normal(int bits);
 void codebook_f32(int bits, int d, float* centroids, float* boundaries);
@@ -44,7 +56,9 @@ void seed_normals(uint64_t seed, int stream, int64_t n, double* out);
 // Byte offsets of one head's streams inside its head block, and page sizes.
 // kmix / vmix: mixed-channel rate b + 1/2 (half the coordinates at b + 1 bits).
 struct Layout {
-  int P, bK, bV, qjl, H, d, kmix, vmix;
+  int P, bK, bV, qjl, H, kmix, vmix;
+  int d;             // head size: FP16 rows (new tokens, ring) hold d coordinates
+  int D;             // transform size: records hold D coordinates
   int kn8;           // key norms as u8 log-norm codes
   int k_rec, v_rec;  // code bytes of one key record / one token's value codes
   int64_t k_norm, k_rnorm, k_codes, k_signs, v_norm, v_codes;
@@ -70,11 +84,12 @@ inline Layout make_layout(const tq_params& p) {
   l.qjl = p.key_qjl ? 1 : 0;
   l.H = p.num_kv_heads;
   l.d = p.head_dim;
+  l.D = transform_dim(p.head_dim);
   l.kmix = p.key_mixed ? 1 : 0;
   l.vmix = p.value_mixed ? 1 : 0;
   l.kn8 = p.key_norm_u8 ? 1 : 0;
-  l.k_rec = l.d * l.bK / 8 + (l.kmix ? l.d / 16 : 0);
-  l.v_rec = l.d * l.bV / 8 + (l.vmix ? l.d / 16 : 0);
+  l.k_rec = l.D * l.bK / 8 + (l.kmix ? l.D / 16 : 0);
+  l.v_rec = l.D * l.bV / 8 + (l.vmix ? l.D / 16 : 0);
   int64_t off = 0;
   l.k_norm = off;
   off += (l.kn8 ? 1LL : 4LL) * l.P;
@@ -83,7 +98,7 @@ inline Layout make_layout(const tq_params& p) {
   l.k_codes = off;
   off += int64_t(l.P) * l.k_rec;
   l.k_signs = off;
-  if (l.qjl) off += int64_t(l.P) * l.d / 8;
+  if (l.qjl) off += int64_t(l.P) * l.D / 8;
   l.v_norm = off;
   off += 4LL * l.P;
   l.v_codes = off;
@@ -95,10 +110,10 @@ inline Layout make_layout(const tq_params& p) {
 
 // Device-resident constant tables (one allocation owned by the context).
 struct DevTables {
-  const float* rot;    // DENSE: Pi [d][d] row-major; HADAMARD: signs [d]
-  const float* rotT;   // DENSE: Pi^T [d][d] row-major
-  const float* S;      // QJL matrix [d][d] row-major (sign bit i from row i)
-  const float* ST;     // S^T [d][d] row-major
+  const float* rot;    // DENSE: Pi [D][D] row-major; HADAMARD: signs [D]
+  const float* rotT;   // DENSE: Pi^T [D][D] row-major
+  const float* S;      // QJL matrix [D][D] row-major (sign bit i from row i)
+  const float* ST;     // S^T [D][D] row-major
   const float* rot4;   // DENSE: Pi interleaved by 4 columns: float4 (j4, i) = Pi[i][4 j4 .. 4 j4 + 3]
   const float* S4;     // S interleaved the same way
   const float* cbtab;  // [keys, values][64]: centroids[16], boundaries[16], then the (b+1)-bit pair of a mixed rate
@@ -116,6 +131,7 @@ struct Codebooks {
 struct EncodeArgs {
   const void* x;
   int64_t n, row_stride;
+  int d;  // coordinates per input row (zero-padded to D)
   uint8_t* codes;
   uint8_t* signs;
   float* norms;
@@ -155,13 +171,14 @@ struct DecodeArgs {
   int pages_per_split;
   int splits;
   // workspace carve-up
-  float* qs;      // [B][Hq][d] rotated query * sm_scale * log2(e)
-  float* ps;      // [B][Hq][d] S q_rot * qjl_scale * sm_scale * log2(e)
+  // (rows of D coordinates; q and out rows hold d)
+  float* qs;      // [B][Hq][D] rotated query * sm_scale * log2(e)
+  float* ps;      // [B][Hq][D] S q_rot * qjl_scale * sm_scale * log2(e)
   float* psum;    // [B][Hq] sum of ps
-  float* qwin;    // [B][Hq][d] query * sm_scale * log2(e)
+  float* qwin;    // [B][Hq][D] query * sm_scale * log2(e), zero past d
   float* pm;      // [B][Hkv][splits][G] running max (log2 units)
   float* pl;      // [B][Hkv][splits][G] running sum
-  float* pacc;    // [B][Hkv][splits][G][d] rotated-basis accumulator
+  float* pacc;    // [B][Hkv][splits][G][D] rotated-basis accumulator
 };
 
 struct Ctx;  // tq_ctx

@@ -9,7 +9,8 @@ off by at most gamma_128 * sum|Pi_ij x_j|/n <= 128 * 2^-24 * 1 ~ 2^-17.  So a
 code must match exactly wherever y lies more than 2^-16 from every boundary
 (unit-vector units), and may differ by one level inside that band.  Sign bits
 are checked against the oracle recomputed from the GPU's own codes and norms,
-exactly wherever |(S r)_j| > 2^-16 * sqrt(d) * ||r||.
+exactly wherever |(S r)_j| > 2^-16 * sqrt(D) * ||r|| (D = 128 transform
+coordinates, also for head sizes below 128, which are zero-padded to D).
 """
 
 import numpy as np
@@ -58,7 +59,7 @@ def check_codes(x, gpu_idx, ref_idx, R, cb):
 
 
 def check_signs(x, gpu_idx, gpu_norms, gpu_signs, R, cb, S):
-    d = x.shape[1]
+    d = gpu_idx.shape[1]  # the transform size D (the input rows may hold fewer)
     r = codec.residual_from_codes(x, R, cb, gpu_norms.astype(np.float64), gpu_idx)
     z = r @ S.T
     rn = np.linalg.norm(r, axis=1)

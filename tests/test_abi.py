@@ -192,3 +192,40 @@ def test_library_mixed_codebooks_equal_oracle(L, bits):
         assert np.array_equal(t[kind + "_centroids"].astype(np.float64), np.concatenate([cb.lo.centroids, cb.hi.centroids]))
         assert np.array_equal(t[kind + "_boundaries"].astype(np.float64),
                               np.concatenate([cb.lo.boundaries, cb.hi.boundaries]))
+
+
+@pytest.mark.parametrize("d", [96, 72, 120])
+@pytest.mark.parametrize("rotation", [tqa.TQ_ROT_DENSE, tqa.TQ_ROT_HADAMARD])
+def test_head_sizes_below_the_transform_size(L, d, rotation):
+    """Head sizes 72..128 that are not a power of two take the transform size
+    D = 128: page bytes as the oracle's layout, tables of D (the rotation and
+    S from D x D draws, codebooks at scale 1/sqrt(D))."""
+    p = tqa.make_params(head_dim=d, rotation=rotation, num_q_heads=4, num_kv_heads=2, page_tokens=64)
+    assert tqa.tq_page_bytes(p) == pages.Layout(d, 3, 1, 4, 2, 64).page_bytes
+    assert tqa.tq_page_bytes(p) == tqa.tq_page_bytes(tqa.make_params(head_dim=128, num_q_heads=4, num_kv_heads=2,
+                                                                       page_tokens=64))
+    seed = 4
+    draws = tq_inputs.rotation_draws(seed, 128) if rotation == tqa.TQ_ROT_DENSE else tq_inputs.hadamard_draws(seed, 128)
+    t = tqa.tq_host_tables(p, draws, tq_inputs.qjl_draws(seed, 128))
+    R = rot.Rotation("dense" if rotation == tqa.TQ_ROT_DENSE else "hadamard", draws, d)
+    if rotation == tqa.TQ_ROT_DENSE:
+        assert t["rotation"].shape == (128, 128)
+        assert np.max(np.abs(t["rotation"].astype(np.float64) - R.matrix)) <= 2.0 ** -30
+    else:
+        assert np.array_equal(t["rotation"].astype(np.float64), R.eps)
+    assert np.array_equal(t["qjl"].astype(np.float64), rot.qjl_matrix(tq_inputs.qjl_draws(seed, 128), 128))
+    assert np.array_equal(t["key_centroids"].astype(np.float64), cbm.Codebook(3, 128).centroids)
+
+
+@pytest.mark.parametrize("d,want", [(64, tqa.TQ_ERR_UNSUPPORTED), (136, tqa.TQ_ERR_UNSUPPORTED),
+                                    (256, tqa.TQ_ERR_UNSUPPORTED), (100, tqa.TQ_ERR_INVALID_ARG),
+                                    (0, tqa.TQ_ERR_INVALID_ARG)])
+def test_head_sizes_without_kernels(L, d, want):
+    """Kernels exist for D = 128 (head sizes 72..128 in steps of 8); other
+    multiples of 8 are valid parameters (page bytes) but have no kernels, and
+    are refused at init before any HIP call."""
+    p = tqa.make_params(head_dim=d)
+    if want == tqa.TQ_ERR_UNSUPPORTED:
+        assert L.tq_page_bytes(ctypes.byref(p)) > 0
+    out = ctypes.c_void_p()
+    assert L.tq_codebook_init(ctypes.byref(out), ctypes.byref(p), None, None, None) == want

@@ -52,8 +52,8 @@ def _compare_caches(s, ref, pool_gpu, kwin, vwin, lens_gpu):
             x = ref._src_k[(b, h)][:C]
             xv = ref._src_v[(b, h)][:C]
             assert np.array_equal(kg.norms, kr.norms) and np.array_equal(vng, vnr)
-            gidx = s.kcb.unpack(kg.codes, 128)
-            check_codes(x, gidx, s.kcb.unpack(kr.codes, 128), s.R, s.kcb)
+            gidx = s.kcb.unpack(kg.codes, s.D)
+            check_codes(x, gidx, s.kcb.unpack(kr.codes, s.D), s.R, s.kcb)
             check_codes(xv, vig, vir, s.R, s.vcb)
             if s.qjl:
                 check_signs(x, gidx, kg.norms, kg.signs, s.R, s.kcb, s.S)
@@ -79,7 +79,7 @@ def _records_match(s, caches, k, v, lens):
             x = k[b, h, :C].astype(np.float64)
             xv = v[b, h, :C].astype(np.float64)
             assert np.array_equal(ka.norms, kb.norms) and np.array_equal(vna, vnb), (b, h)
-            ia, ib = s.kcb.unpack(ka.codes, 128), s.kcb.unpack(kb.codes, 128)
+            ia, ib = s.kcb.unpack(ka.codes, s.D), s.kcb.unpack(kb.codes, s.D)
             check_codes(x, ia, ib, s.R, s.kcb)
             check_codes(xv, via, vib, s.R, s.vcb)
             if s.qjl:
@@ -123,6 +123,13 @@ CASES = [
     ("u8norm_k35_v3", dict(Hq=4, Hkv=2, W=32, P=64, key_bits=3, key_mixed=True, value_bits=3, key_norm_u8=True),
      [200, 33]),
     ("u8norm_k3_v4_hadamard", dict(Hq=8, Hkv=2, W=16, P=32, rotation="hadamard", key_norm_u8=True), [100, 47]),
+    # head sizes below the transform size (zero-padded to D = 128)
+    ("d96_k3qjl_v4", dict(d=96, Hq=8, Hkv=2, W=40, P=64), [300, 41, 40, 7, 0, 129]),
+    ("d96_k2qjl_v2_hadamard", dict(d=96, Hq=4, Hkv=2, key_bits=2, value_bits=2, rotation="hadamard", W=16, P=32),
+     [100, 33]),
+    ("d72_k35_v3_u8norm", dict(d=72, Hq=4, Hkv=2, W=32, P=64, key_bits=3, key_mixed=True, value_bits=3,
+                               key_norm_u8=True), [200, 33]),
+    ("d120_k4_noqjl_v3", dict(d=120, Hq=2, Hkv=2, key_bits=4, key_qjl=0, value_bits=3, W=16, P=32), [77, 16, 15]),
 ]
 
 
@@ -142,23 +149,24 @@ def test_bulk_prefill_parity(name, kw, lens):
     g = _compare_caches(s, ref, dev["pool"].cpu().numpy(), dev["k_win"].cpu().view(torch.int16).numpy().view(np.uint16),
                         dev["v_win"].cpu().view(torch.int16).numpy().view(np.uint16), dev["seq_lens"].cpu().numpy())
     # decode over the GPU-built cache against the oracle's attention over the same bytes
-    q = tq_inputs.queries(8, (len(lens), s.Hq, 128))
-    out, dbg = run_decode(ctx, torch.from_numpy(q.astype(np.float32)).cuda(), dev, 1 / np.sqrt(128),
+    q = tq_inputs.queries(8, (len(lens), s.Hq, s.d))
+    out, dbg = run_decode(ctx, torch.from_numpy(q.astype(np.float32)).cuda(), dev, 1 / np.sqrt(s.d),
                           logits_len=max(lens) + 1)
-    ref_o, _ = att.attention_plain(g, q.astype(np.float32).astype(np.float64), 1 / np.sqrt(128))
+    ref_o, _ = att.attention_plain(g, q.astype(np.float32).astype(np.float64), 1 / np.sqrt(s.d))
     for b in range(len(lens)):
         for hq in range(s.Hq):
             if lens[b]:
                 assert_out_close(out[b, hq], ref_o[b, hq], 1e-3, (b, hq))
 
 
+@pytest.mark.parametrize("d", [128, 96])
 @pytest.mark.parametrize("kn8", [False, True])
 @pytest.mark.parametrize("late_step", [5, 20, 30])
-def test_streaming_appends_match_bulk(late_step, kn8):
+def test_streaming_appends_match_bulk(late_step, kn8, d):
     """Chunked appends (1 token, then late_step tokens: up to and beyond the
     window, evictions spanning two 32-token groups) equal one bulk append."""
-    print(f"case streaming late_step={late_step} u8 key norms={kn8}", flush=True)
-    s = Setup(Hq=4, Hkv=2, W=24, P=32, key_norm_u8=kn8)
+    print(f"case streaming late_step={late_step} u8 key norms={kn8} d={d}", flush=True)
+    s = Setup(d=d, Hq=4, Hkv=2, W=24, P=32, key_norm_u8=kn8)
     lens = [90, 30]
     ref = s.cache(2, 90)
     k, v = fill(s, ref, lens)
@@ -175,8 +183,8 @@ def test_streaming_appends_match_bulk(late_step, kn8):
         vv = np.ascontiguousarray(v[:, :, t:t + step])
         if kk.shape[2] < step:
             pad = step - kk.shape[2]
-            kk = np.concatenate([kk, np.zeros(kk.shape[:2] + (pad, 128), np.float16)], 2)
-            vv = np.concatenate([vv, np.zeros(vv.shape[:2] + (pad, 128), np.float16)], 2)
+            kk = np.concatenate([kk, np.zeros(kk.shape[:2] + (pad, s.d), np.float16)], 2)
+            vv = np.concatenate([vv, np.zeros(vv.shape[:2] + (pad, s.d), np.float16)], 2)
         _gpu_append(ctx, d2, kk, vv, counts=cnt)
         t += step
     torch.cuda.synchronize()
@@ -261,6 +269,9 @@ MMA_CASES = [
     ("k4_noqjl_v3", dict(Hq=4, Hkv=2, key_bits=4, key_qjl=0, value_bits=3, W=8, P=64), [333, 64, 17], 9),
     ("k3qjl_u8norm_v4", dict(Hq=4, Hkv=1, W=0, P=32, key_norm_u8=True), [150, 31], 20),
     ("orthoS_k3_v2", dict(Hq=4, Hkv=2, value_bits=2, W=24, P=64, qjl_kind="orthogonal", qjl_shrink=0.7), [90, 260], 33),
+    ("d96_k3qjl_v4", dict(d=96, Hq=8, Hkv=2, W=40, P=64), [300, 41, 40, 7, 0, 129], 37),
+    ("d80_k2qjl_v3_hadamard", dict(d=80, Hq=4, Hkv=2, key_bits=2, value_bits=3, rotation="hadamard", W=16, P=32),
+     [200, 77], 50),
 ]
 
 
@@ -285,7 +296,7 @@ def test_matrix_core_append_matches_vector_alu_append(name, kw, lens, extra):
         _gpu_append(ctx, dv, np.ascontiguousarray(k[:, :, :max(lens)]), np.ascontiguousarray(v[:, :, :max(lens)]),
                     counts=lens)
         # the next `extra` tokens of every sequence, as one more bulk append
-        kk = np.zeros((B, s.Hkv, extra, 128), np.float16)
+        kk = np.zeros((B, s.Hkv, extra, s.d), np.float16)
         vv = np.zeros_like(kk)
         for b in range(B):
             kk[b] = k[b, :, lens[b]:lens[b] + extra]

@@ -21,7 +21,7 @@ pytestmark = pytest.mark.gpu
 
 
 def _check(cache, q, out, dbg, tol=1e-3, name="decode"):
-    ref_o, ref_l = att.attention_plain(cache, q, 1 / np.sqrt(128))
+    ref_o, ref_l = att.attention_plain(cache, q, 1 / np.sqrt(q.shape[-1]))
     B, Hq, _ = q.shape
     st = ErrStats(name)
     for b in range(B):
@@ -51,6 +51,14 @@ CASES = [
     ("gqa4_orthoS_shrink", dict(Hq=8, Hkv=2, W=64, qjl_kind="orthogonal", qjl_shrink=2 / np.pi), [600, 70, 1]),
     ("gqa8_orthoS_hadamard", dict(Hq=16, Hkv=2, key_bits=2, value_bits=2, rotation="hadamard", W=32,
                                   qjl_kind="orthogonal", qjl_shrink=0.7), [500, 33]),
+    # head sizes below the transform size (zero-padded to D = 128); windows
+    # past 128 slots take the merge kernel's second batch of window loads
+    ("d96_gqa4_ragged", dict(d=96, Hq=8, Hkv=2, W=200), [700, 129, 201, 40, 1, 0, 1000]),
+    ("d96_gqa1_hadamard_k2v2", dict(d=96, Hq=2, Hkv=2, key_bits=2, value_bits=2, rotation="hadamard", W=16,
+                                    P=64), [333, 64, 17]),
+    ("d72_gqa8_k4_noqjl_v3", dict(d=72, Hq=16, Hkv=2, key_bits=4, key_qjl=0, value_bits=3, W=64), [600, 70]),
+    ("d112_gqa2_orthoS", dict(d=112, Hq=4, Hkv=2, W=32, P=32, qjl_kind="orthogonal", qjl_shrink=2 / np.pi),
+     [300, 33]),
 ]
 
 # mixed-channel rates (keys / values at 2.5 or 3.5 bits); matrix-core scan only
@@ -72,6 +80,8 @@ MIXED = [
                                      key_norm_u8=True), [300, 64]),
     ("u8norm_k2_v2_hadamard_gqa8", dict(Hq=16, Hkv=2, key_bits=2, value_bits=2, rotation="hadamard", W=32,
                                         key_norm_u8=True), [400, 33]),
+    ("d96_u8norm_k35_v35", dict(d=96, Hq=8, Hkv=2, key_bits=3, key_mixed=True, value_bits=3, value_mixed=True,
+                                W=64, key_norm_u8=True), [700, 129, 1]),
 ]
 
 
@@ -93,23 +103,24 @@ def _decode_parity(name, kw, lens, kernel):
     fill(s, cache, lens)
     ctx = context_for(s, tqa.TQ_FLAG_VALU_SCAN if kernel == "valu" else 0)
     dev = upload_cache(cache)
-    q = tq_inputs.queries(5, (len(lens), s.Hq, 128))
+    q = tq_inputs.queries(5, (len(lens), s.Hq, s.d))
     qt = torch.from_numpy(q.astype(np.float32)).cuda()
-    out, dbg = run_decode(ctx, qt, dev, 1 / np.sqrt(128), logits_len=max(lens) + 1)
+    out, dbg = run_decode(ctx, qt, dev, 1 / np.sqrt(s.d), logits_len=max(lens) + 1)
     _check(cache, q.astype(np.float32).astype(np.float64), out, dbg, name=f"{name} {kernel}")
     assert tqa.tq_get_status(ctx) == 0
 
 
+@pytest.mark.parametrize("d", [128, 96])
 @pytest.mark.parametrize("qdtype", [torch.bfloat16, torch.float16])
-def test_decode_query_dtypes(qdtype):
-    s = Setup(Hq=4, Hkv=1, W=128)
+def test_decode_query_dtypes(qdtype, d):
+    s = Setup(d=d, Hq=4, Hkv=1, W=128)
     lens = [800]
     cache = s.cache(1, 800)
     fill(s, cache, lens)
     ctx = context_for(s)
     dev = upload_cache(cache)
-    qt = torch.from_numpy(tq_inputs.queries(6, (1, 4, 128)).astype(np.float32)).to(qdtype).cuda()
-    out, dbg = run_decode(ctx, qt, dev, 1 / np.sqrt(128), logits_len=801)
+    qt = torch.from_numpy(tq_inputs.queries(6, (1, 4, d)).astype(np.float32)).to(qdtype).cuda()
+    out, dbg = run_decode(ctx, qt, dev, 1 / np.sqrt(d), logits_len=801)
     _check(cache, qt.float().cpu().numpy().astype(np.float64), out, dbg)
 
 

@@ -136,3 +136,33 @@ def test_dequant_parity_mixed(rotation, bits):
         scale = np.maximum(np.linalg.norm(ref, axis=1), 1e-30)
         assert np.all(np.max(np.abs(got - ref), axis=1) <= 2e-6 * scale + 1e-30)
         assert np.all(got[5] == 0.0)
+
+
+@pytest.mark.parametrize("d", [96, 72])
+@pytest.mark.parametrize("rotation", ["dense", "hadamard"])
+def test_dequant_parity_head_sizes(d, rotation):
+    """Head sizes below the transform size: the records hold D = 128
+    coordinates and the output rows the first d of Pi^T(...)."""
+    print(f"case dequant d={d} {rotation}", flush=True)
+    s = Setup(d=d, key_bits=3, value_bits=4, rotation=rotation)
+    ctx = context_for(s)
+    n = 200
+    x = tq_inputs.keys(4, d, np.arange(n)).astype(np.float64)
+    x[5] = 0.0
+    x16 = tq_inputs.fp16(x)
+    for kind, bits, cb, qjl in ((tqa.TQ_KIND_KEY, 3, s.kcb, True), (tqa.TQ_KIND_VALUE, 4, s.vcb, False)):
+        codes, norms, signs, rnorms = _records(ctx, kind, x16, qjl, bits)
+        out = torch.full((n, d + 1), float("nan"), dtype=torch.float32, device="cuda")
+        tqa.tq_decode(ctx, kind, codes, norms, out, signs, rnorms)
+        torch.cuda.synchronize()
+        cpu = lambda t: None if t is None else t.cpu().numpy()
+        ref = codec.dequantize(cpu(codes), cpu(norms), s.R, cb, cpu(signs), cpu(rnorms),
+                               s.S if qjl else None, s.qjl_coef)
+        assert ref.shape == (n, d)
+        # n rows of d: the output ends at n * d floats (the rest stays untouched)
+        flat = cpu(out).reshape(-1)
+        got = flat[:n * d].reshape(n, d)
+        assert np.all(np.isnan(flat[n * d:]))
+        scale = np.maximum(np.linalg.norm(ref, axis=1), 1e-30)
+        assert np.all(np.max(np.abs(got - ref), axis=1) <= 2e-6 * scale + 1e-30)
+        assert np.all(got[5] == 0.0)

@@ -150,3 +150,46 @@ def test_encode_parity_u8_key_norm(rotation, bK, kmix, qjl, dtype):
     vcodes, vnorms, _, _ = _gpu_encode(ctx, tqa.TQ_KIND_VALUE, x16, False, dtype)
     vref = codec.encode(x, s.R, s.vcb)
     assert np.array_equal(vnorms, vref.norms)
+
+
+@pytest.mark.parametrize("d", [96, 72, 120])
+@pytest.mark.parametrize("rotation", ["dense", "hadamard"])
+@pytest.mark.parametrize("dtype", [torch.float16, torch.float32])
+def test_encode_parity_head_sizes(d, rotation, dtype):
+    """Head sizes below the transform size D = 128: rows of d coordinates
+    (here inside wider rows, row_stride = d + 8) are zero-padded to D; the
+    records hold D codes and D sign bits.  fp16 rows take the matrix-core
+    encoder, f32 rows the vector-ALU one."""
+    print(f"case head size d={d} rotation={rotation} dtype={dtype}", flush=True)
+    s = Setup(d=d, rotation=rotation)
+    ctx = context_for(s)
+    n = 300
+    x = tq_inputs.keys(6, d, np.arange(n)).astype(np.float64)
+    x[3] = 0.0
+    x[7, :] = 0.0
+    x[7, d - 1] = 1.5
+    x16 = tq_inputs.fp16(x)
+    wide = np.zeros((n, d + 8), np.float32)
+    wide[:, :d] = x16.astype(np.float32)
+    wide[:, d:] = 1e4  # past the row: must not be read
+    xt = torch.from_numpy(wide).to(dtype).cuda()[:, :d]
+    x = x16.astype(np.float64)
+    for kind, cb, qjl in ((tqa.TQ_KIND_KEY, s.kcb, True), (tqa.TQ_KIND_VALUE, s.vcb, False)):
+        codes = torch.zeros((n, cb.record_bytes(128)), dtype=torch.uint8, device="cuda")
+        norms = torch.zeros(n, dtype=torch.float32, device="cuda")
+        signs = torch.zeros((n, 16), dtype=torch.uint8, device="cuda") if qjl else None
+        rnorms = torch.zeros(n, dtype=torch.float32, device="cuda") if qjl else None
+        tqa.tq_encode(ctx, kind, xt, codes, norms, signs, rnorms)
+        torch.cuda.synchronize()
+        codes, norms = codes.cpu().numpy(), norms.cpu().numpy()
+        ref = codec.encode(x, s.R, cb, s.S if qjl else None)
+        assert np.array_equal(norms, ref.norms)
+        gidx = cb.unpack(codes, 128)
+        assert check_codes(x, gidx, ref.idx, s.R, cb) <= 0.002 * n * 128
+        if qjl:
+            signs, rnorms = signs.cpu().numpy(), rnorms.cpu().numpy()
+            check_signs(x, gidx, norms, signs, s.R, cb, s.S)
+            r = codec.residual_from_codes(x, s.R, cb, norms, gidx)
+            assert np.allclose(rnorms, np.linalg.norm(r, axis=1), rtol=1e-5, atol=1e-30)
+            assert rnorms[3] == 0 and not signs[3].any()
+        assert norms[3] == 0 and not codes[3].any()
