@@ -94,8 +94,15 @@ enum { TQ_KIND_KEY = 0, TQ_KIND_VALUE = 1 };
 /* tq_params.flags: TQ_FLAG_VALU_SCAN selects the vector-ALU decode scan
  * instead of the matrix-core one, TQ_FLAG_VALU_APPEND the vector-ALU encoder
  * for bulk appends instead of the matrix-core one (same results to the stated
- * tolerance and guard band; kept for measurement and cross-checking). */
-enum { TQ_FLAG_VALU_SCAN = 1, TQ_FLAG_VALU_APPEND = 2 };
+ * tolerance and guard band; kept for measurement and cross-checking).
+ * TQ_FLAG_DETERMINISTIC makes tq_decode_attn bit-reproducible: by default
+ * the waves of a matrix-core scan work-group claim the tokens of their page
+ * split as they free up, which balances the waves but lets the grouping of
+ * the floating-point sums, hence the last bits of the output, vary from call
+ * to call (within about 1e-6 relative); with the flag every wave takes a
+ * fixed share and repeated calls on the same inputs give identical bits.
+ * The vector-ALU scan is always bit-reproducible. */
+enum { TQ_FLAG_VALU_SCAN = 1, TQ_FLAG_VALU_APPEND = 2, TQ_FLAG_DETERMINISTIC = 4 };
 /* Streams of the library's seeded generator (tq_seed_draws): the Gaussian
  * matrix the dense rotation is built from, the QJL draws, and the draws whose
  * signs are the Hadamard variant's Rademacher stage. */
@@ -121,7 +128,7 @@ typedef struct tq_params {
   int32_t num_kv_heads; /* H_kv; H_q % H_kv == 0, query head g reads kv head g / (H_q/H_kv) */
   int32_t page_tokens;  /* P, a multiple of 32, at most 1024 */
   int32_t window;       /* W, FP16 recent tokens per sequence, 0..1024 */
-  int32_t flags;        /* TQ_FLAG_* bits, 0 for the default kernels */
+  int32_t flags;        /* TQ_FLAG_* bits, 0 for the default kernels and schedule */
   uint64_t seed;        /* recorded in page headers (cache identity); keys the library's generator
                            when the caller gives no draws or tables */
   int32_t qjl_kind;     /* TQ_QJL_GAUSSIAN (the paper's S, coefficient sqrt(pi/2)/D) or

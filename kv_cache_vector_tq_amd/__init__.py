@@ -26,6 +26,7 @@ TQ_KIND_KEY, TQ_KIND_VALUE = 0, 1
 TQ_STATUS_BAD_PAGE, TQ_STATUS_BAD_COUNT = 1, 2
 TQ_FLAG_VALU_SCAN = 1
 TQ_FLAG_VALU_APPEND = 2
+TQ_FLAG_DETERMINISTIC = 4
 TQ_DRAWS_ROTATION, TQ_DRAWS_QJL, TQ_DRAWS_HADAMARD = 1, 2, 3
 TQ_NOALLOC_SCRATCH_BYTES = 32 << 20
 

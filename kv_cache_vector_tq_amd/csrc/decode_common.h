@@ -13,6 +13,7 @@ struct KParams {
   int64_t page_bytes, head_bytes, k_norm, k_rnorm, k_codes, k_signs, v_norm, v_codes;
   int rotation;
   float qjl_scale;
+  int det;  // fixed (bit-reproducible) share of chunks per scan wave
 };
 
 inline KParams make_kparams(const tq_ctx* c) {
@@ -32,6 +33,7 @@ inline KParams make_kparams(const tq_ctx* c) {
   k.v_norm = c->lay.v_norm;
   k.v_codes = c->lay.v_codes;
   k.rotation = c->p.rotation;
+  k.det = (c->p.flags & TQ_FLAG_DETERMINISTIC) ? 1 : 0;
   // QJL coefficient: sqrt(pi/2)/D for Gaussian S, sqrt(pi/2)/sqrt(D) for
   // orthogonal S (S has D rows), times the shrinkage factor
   const double dd = static_cast<double>(c->lay.D);

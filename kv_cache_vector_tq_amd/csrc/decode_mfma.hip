@@ -263,6 +263,7 @@ scan_mfma_kernel(DecodeArgs a, DevTables t, Codebooks cb, KParams k) {
   __shared__ float wm[kWaves][G], wl[kWaves][G];
   __shared__ float red[G][kD];
   __shared__ float ck[16], cvv[16], ck2[16], cv2[16];
+  __shared__ int next_chunk;  // the split's next unclaimed chunk
 
   const int tid = threadIdx.x, split = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   // the wave index is uniform within a wave; saying so keeps page addresses
@@ -313,6 +314,7 @@ scan_mfma_kernel(DecodeArgs a, DevTables t, Codebooks cb, KParams k) {
     return;
   }
   // codebooks to LDS (no dynamic indexing of kernel arguments), then the tables
+  if (tid == 0) next_chunk = kWaves;  // wave w starts with chunk w
   if (tid < 16) {
     float kv = 0.0f, vv = 0.0f, kv2 = 0.0f, vv2 = 0.0f;
 #pragma unroll
@@ -392,8 +394,6 @@ scan_mfma_kernel(DecodeArgs a, DevTables t, Codebooks cb, KParams k) {
 
   const int tot = (C < pe * k.P ? C : pe * k.P) - pb * k.P;
   const int nchunks = (tot + kChunk - 1) / kChunk;
-  // this wave takes chunks wave, wave + kWaves, ...
-  const int nmine = nchunks > wave ? (nchunks - wave + kWaves - 1) / kWaves : 0;
   // value words: the lane's 8 tokens of coordinate 8n + bl are bits [8*kg*BV, +8*BV)
   const int vbit = 8 * kg * BV;
   const int vw0 = vbit >> 5, vsh = vbit & 31;
@@ -424,8 +424,7 @@ scan_mfma_kernel(DecodeArgs a, DevTables t, Codebooks cb, KParams k) {
   const uint32_t o_vw = static_cast<uint32_t>((vw0 * kD + 8 * n) * 4);
   const uint32_t o_vw2 = static_cast<uint32_t>(((vtwo ? vw0 + 1 : vw0) * kD + 8 * n) * 4);
 
-  auto meta = [&](int i, Meta& m) {
-    const int c = wave + i * kWaves;
+  auto meta = [&](int c, Meta& m) {
     const int tok0 = c * kChunk;
     const int pg = pb + tok0 / k.P;
     m.gi = (tok0 % k.P) / kChunk;
@@ -630,26 +629,39 @@ scan_mfma_kernel(DecodeArgs a, DevTables t, Codebooks cb, KParams k) {
     }
   };
 
-  // Software pipeline over this wave's chunks 0 .. nmine-1: step i
-  // accumulates the values of chunk i and scores chunk i+1.  Each buffer is
-  // refilled as soon as it is consumed: keys (with the value norms) of chunk
-  // i+1 load while chunk i's values are accumulated, values of chunk i+1
-  // while chunk i+1 is scored.  The weights alternate between two pv slots.
+  // Software pipeline over this wave's chunks: each step accumulates the
+  // values of the current chunk and scores the next one.  Each buffer is
+  // refilled as soon as it is consumed: keys (with the value norms) of the
+  // next chunk load while the current chunk's values are accumulated, its
+  // values while it is scored.  The weights alternate between two pv slots.
+  // Wave w starts with chunk w and then claims the split's next unclaimed
+  // chunk (an LDS counter, claimed one step ahead of its loads), so the
+  // waves of a work-group finish within about one chunk of each other; the
+  // grouping of the sums then varies between calls.  With k.det every wave
+  // takes the fixed share w, w + kWaves, ... (bit-reproducible results).
+  auto claim = [&]() {
+    int c = 0;
+    if (l == 0) c = atomicAdd(&next_chunk, 1);
+    return __builtin_amdgcn_readfirstlane(c);
+  };
   Meta m;
   KBuf<BK, KMIX> kb;
   VBuf<BV, VMIX> vb;
-  if (nmine > 0) {
-    meta(0, m);
+  if (wave < nchunks) {
+    meta(wave, m);
     loadK(m, kb);
     loadV(m, vb);
+    int cn = k.det ? wave + kWaves : claim();
     keyphase(m, kb, 0);
     int i = 0;
-    for (; i + 1 < nmine; ++i) {
-      meta(i + 1, m);
+    for (; cn < nchunks; ++i) {
+      meta(cn, m);
       loadK(m, kb);
+      const int cnn = k.det ? cn + kWaves : claim();
       valuephase(vb, i & 1);
       loadV(m, vb);
       keyphase(m, kb, (i + 1) & 1);
+      cn = cnn;
     }
     valuephase(vb, i & 1);
   }

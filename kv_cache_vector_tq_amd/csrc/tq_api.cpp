@@ -22,7 +22,7 @@ bool params_ok(const tq_params* p) {
   if (p->num_q_heads <= 0 || p->num_kv_heads <= 0 || p->num_q_heads % p->num_kv_heads) return false;
   if (p->page_tokens <= 0 || p->page_tokens % tq::kVGroup || p->page_tokens > tq::kMaxPage) return false;
   if (p->window < 0 || p->window > tq::kMaxWindow) return false;
-  if (p->flags & ~(TQ_FLAG_VALU_SCAN | TQ_FLAG_VALU_APPEND)) return false;
+  if (p->flags & ~(TQ_FLAG_VALU_SCAN | TQ_FLAG_VALU_APPEND | TQ_FLAG_DETERMINISTIC)) return false;
   if (p->qjl_kind != TQ_QJL_GAUSSIAN && p->qjl_kind != TQ_QJL_ORTHOGONAL) return false;
   if (!(p->qjl_shrink > 0.0f && p->qjl_shrink <= 4.0f)) return false;  // also rejects NaN
   // mixed-channel rates: 2.5 and 3.5 bits, halves of a multiple of 32 transform coordinates

@@ -9,7 +9,9 @@ time from the GPU's own pages:
     norms exactly, residual norms to 2e-5; the FP16 ring slots exactly;
   * decode: logits of the sampled heads within 1e-3 of max|logit| and their
     outputs within 1e-3 (L2) of the oracle's dequantise-then-softmax
-    attention; the output without logit capture is bit-identical.
+    attention; the output without logit capture is the same up to the
+    grouping of the sums (within 1e-5 of max|o|; bit-identical under the
+    deterministic schedule, checked at the B=16 shape).
 Shapes: B=16 Hq=32 Hkv=8 T=32K (3-bit+QJL keys, 4-bit values, dense);
 B=1 Hq=64 Hkv=8 T=128K (2-bit+QJL, 2-bit, Hadamard, 4 decode steps);
 one layer of 64 ragged sequences, lengths U[1K, 16K], Hq=16 Hkv=2;
@@ -27,6 +29,13 @@ from gpu_helpers import ErrStats, assert_out_close, check_codes, check_signs, co
 from oracle_cache import Setup
 
 pytestmark = [pytest.mark.gpu, pytest.mark.slow]
+
+
+def _same_sums(a, b):
+    """Two decodes of the same inputs under the default schedule: equal up to
+    the grouping of the floating-point sums."""
+    a, b = a.cpu().numpy(), b.cpu().numpy()
+    assert np.max(np.abs(a - b)) <= 1e-5 * np.max(np.abs(b))
 
 
 class GpuCache:
@@ -50,14 +59,14 @@ class GpuCache:
         tqa.tq_append_page(self.ctx, self.pool, self.bt, self.sl, k.contiguous(), v.contiguous(), self.kw, self.vw,
                            c, num_pages=self.npages)
 
-    def decode(self, q, dbg_len=None):
+    def decode(self, q, dbg_len=None, ctx=None):
         ws = torch.empty(tqa.tq_decode_workspace_bytes(self.ctx, self.B, self.max_pages, 0), dtype=torch.uint8,
                          device="cuda")
         out = torch.full((self.B, q.shape[1], self.s.d), float("nan"), dtype=torch.float32, device="cuda")
         dbg = None
         if dbg_len is not None:
             dbg = torch.full((self.B, q.shape[1], dbg_len), float("nan"), dtype=torch.float32, device="cuda")
-        tqa.tq_decode_attn(self.ctx, q, self.pool, self.bt, self.sl, self.kw, self.vw, out, ws,
+        tqa.tq_decode_attn(ctx or self.ctx, q, self.pool, self.bt, self.sl, self.kw, self.vw, out, ws,
                            1 / np.sqrt(self.s.d), dbg_logits=dbg, num_pages=self.npages)
         torch.cuda.synchronize()
         return out, dbg
@@ -144,7 +153,11 @@ def test_decode_step_B16_Hq32_Hkv8_T32K():
     q = tq_inputs.torch_queries(0, (B, Hq, s.d), "cuda", torch.bfloat16)
     out, _ = gc.decode(q)
     out2, dbg = gc.decode(q, dbg_len=T)
-    assert torch.equal(out, out2)
+    _same_sums(out, out2)
+    ctx_d = context_for(s, tqa.TQ_FLAG_DETERMINISTIC)
+    od = [gc.decode(q, ctx=ctx_d)[0] for _ in range(2)]
+    assert torch.equal(od[0], od[1])
+    _same_sums(od[0], out)
     assert tqa.tq_get_status(gc.ctx) == 0
     cache = gc.host()
     assert np.all(cache.seq_lens == T)
@@ -171,7 +184,7 @@ def test_long_context_B1_Hq64_T128K_hadamard_2bit():
         q = tq_inputs.torch_queries(3, (B, Hq, s.d), "cuda", torch.bfloat16, step=i)
         out, _ = gc.decode(q)
     out2, dbg = gc.decode(q, dbg_len=T)
-    assert torch.equal(out, out2)
+    _same_sums(out, out2)
     assert tqa.tq_get_status(gc.ctx) == 0
     cache = gc.host()
     pairs = [(0, h) for h in range(Hkv)]
@@ -195,7 +208,7 @@ def test_ragged_layer_B64_Hq16_Hkv2():
     q = tq_inputs.torch_queries(4, (B, Hq, s.d), "cuda", torch.bfloat16)
     out, _ = gc.decode(q)
     out2, dbg = gc.decode(q, dbg_len=Tm)
-    assert torch.equal(out, out2)
+    _same_sums(out, out2)
     assert tqa.tq_get_status(gc.ctx) == 0
     cache = gc.host()
     assert np.array_equal(cache.seq_lens, lens)
