@@ -17,7 +17,7 @@
 //  * packed codes are expanded to fp16 B operands through LDS lookup tables
 //    (a 6- or 8-bit slice of the code stream yields 2 or 4 fp16 values).
 // Each wave streams 32-token chunks (one value group) with its own online
-// softmax state; the waves of a work-group (four, or eight with the wide
+// softmax state; the waves of a work-group (four, or sixteen with the wide
 // table below) merge at the end.
 #include <hip/hip_ext.h>
 
@@ -143,10 +143,13 @@ __device__ inline u4 dec_signs8(uint32_t x, const u2* lutN) {
 // second half, the eight +-1 fp16 values of sign byte e in 8 copies of 16
 // bytes (lane reads copy lane % 8, one 16-byte read per 8 signs).  One v_perm
 // forms each address (byte e into bits 8..15, the lane's copy offset into
-// bits 0..7) where the narrow tables take a shift and a mask-or.  Eight waves
-// share the table so that two work-groups still fit in a CU.
+// bits 0..7) where the narrow tables take a shift and a mask-or.  Sixteen
+// waves (a whole CU at four waves per SIMD) share one table and one chunk
+// counter: the waves of a CU finish together, where two eight-wave
+// work-groups per CU ended 15 us apart (the younger one's waves lose issue
+// arbitration to the older one's and then run on at half occupancy).
 constexpr bool wide_scan(int G, int BV, bool vmix) { return BV == 4 && G <= 4 && !vmix; }
-constexpr int scan_threads(bool wide) { return wide ? 512 : 256; }
+constexpr int scan_threads(bool wide) { return wide ? 1024 : 256; }
 
 template <int G, int BV, bool VMIX = false>
 struct ScanShape {
