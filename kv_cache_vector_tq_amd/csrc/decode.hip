@@ -5,19 +5,23 @@
 // "aither-kvcache" README, "Zero-buffer fused attention"):
 //  1. prep:  per (b, query head) q_rot = Pi q and p = S q_rot, pre-scaled by
 //     sm_scale*log2(e) (and sqrt(pi/2)/d for p) so scores come out in log2
-//     units; the plain query is kept for the FP16 window.
+//     units.
 //  2. scan:  per (b, kv head, page split) stream the packed pages once:
 //     score_t = n_t <q_rot, c_K[idx_t]> + ||r_t|| (2 <p, sigma_t> - sum p)
 //     for the G query heads of the group, online softmax (exp2), and
 //     acc += w_t n^V_t c_V[idx^V_t] in the rotated basis; write (m, l, acc).
-//  3. merge: per (b, query head) combine the split partials in fixed order,
-//     score the FP16 window exactly in the original basis, apply Pi^T to the
-//     rotated accumulator once and normalise.
+//     Work-groups of the same launch score the FP16 window exactly in the
+//     original basis (its softmax partial m_w, l_w, acc_w).
+//  3. finalize: per (b, kv head) combine the split partials and the window's
+//     in fixed order, apply Pi^T to the rotated accumulator once and
+//     normalise (decode_finalize.h): in the matrix-core scan's last
+//     work-group of the kv head, after the vector-ALU scan in a kernel.
 #include <hip/hip_ext.h>
 
 #include <mutex>
 
 #include "decode_common.h"
+#include "decode_finalize.h"
 #include "device_common.h"
 #include "tq_internal.h"
 
@@ -32,8 +36,8 @@ namespace {
 
 // ---------------------------------------------------------------- prep
 constexpr int kSmallThreads = 256;
-constexpr int kMergeGroups = 128;  // fewest merge work-groups before heads are spread out
-constexpr int kMergeMaxHeads = 4;  // most query heads per prep / merge work-group
+constexpr int kPrepGroups = 128;  // fewest prep work-groups (of each kind) before heads are spread out
+constexpr int kPrepMaxHeads = 4;  // most query heads per prep work-group
 
 // y[g][i] = sum_j M[j*kD + i] x[g][j] for the G vectors x (LDS), M a kD x kD
 // row-major table in global memory.  Thread (c, r) owns columns 4c..4c+3 and
@@ -103,14 +107,12 @@ __device__ __forceinline__ void hadamard_lds(float (*x)[kD], const float* __rest
   lds_barrier();
 }
 
-// One work-group per (b, kv head) prepares its G query heads (or GW of them,
-// when one per kv head would make too few work-groups).
+// Rotated queries: q_rot = Pi q and p = S q_rot for GW query heads of kv
+// head h (their rows g0 .. g0+GW-1 of the group of k.G).
 template <int GW>
-__global__ __launch_bounds__(kSmallThreads) void prep_kernel(DecodeArgs a, DevTables t, KParams k, int qjl) {
-  __shared__ float qv[GW][kD], qr[GW][kD], part[8][GW][kD];
-  // work-group (kv head h, query heads g0 .. g0+GW-1 of its group of k.G)
-  const int nhs = k.G / GW;
-  const int tid = threadIdx.x, h = blockIdx.x / nhs, g0 = (blockIdx.x % nhs) * GW, b = blockIdx.y;
+__device__ void rotate_queries(const DecodeArgs& a, const DevTables& t, const KParams& k, int qjl, int b, int h,
+                               int g0, float (*qv)[kD], float (*qr)[kD], float (*part)[GW][kD]) {
+  const int tid = threadIdx.x;
   const int64_t row0 = (static_cast<int64_t>(b) * k.Hq + static_cast<int64_t>(h) * k.G + g0) * kD;
   // the caller's query rows hold d coordinates; they are zero-padded to kD here
   const int64_t qin0 = (static_cast<int64_t>(b) * k.Hq + static_cast<int64_t>(h) * k.G + g0) * k.d;
@@ -144,10 +146,7 @@ __global__ __launch_bounds__(kSmallThreads) void prep_kernel(DecodeArgs a, DevTa
 #pragma unroll
   for (int u = 0; u * kSmallThreads < GW * kD; ++u) {
     const int e = tid + u * kSmallThreads;
-    if (e < GW * kD) {
-      a.qwin[row0 + e] = qin[u] * c2;
-      qv[e / kD][e % kD] = qin[u];
-    }
+    if (e < GW * kD) qv[e / kD][e % kD] = qin[u];
   }
   lds_barrier();
   if (k.rotation == TQ_ROT_DENSE) {
@@ -172,6 +171,163 @@ __global__ __launch_bounds__(kSmallThreads) void prep_kernel(DecodeArgs a, DevTa
     s2 = wave_sum(s2);
     if (lane == 0) a.psum[static_cast<int64_t>(b) * k.Hq + h * k.G + g0 + g] = s2;
   }
+}
+
+// The FP16 window's partial for GW query heads of kv head h: scores in the
+// original basis (log2 units), m_w = their maximum, l_w = sum 2^(s - m_w),
+// acc_w = sum 2^(s - m_w) v (original basis; zero past d).  An empty window
+// gives m_w = -inf, l_w = 0, acc_w = 0.  It depends on the query and the
+// ring only, so it is taken here, before the scan, and the final combine
+// just adds it.  Also clears the kv head's arrival counter for the scan.
+template <int GW>
+__device__ void window_partial(const DecodeArgs& a, const KParams& k, int b, int h, int g0, float (*qw)[kD],
+                               float (*ls)[kMaxWindow], float (*part)[GW][kD], float* sMw, float* sLw) {
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int c4 = (tid & 31) * 4, q8 = tid >> 5;
+  const int T = a.seq_lens[b];
+  const int nwin = T < k.W ? T : k.W;
+  const int64_t bh = static_cast<int64_t>(b) * k.Hkv + h;
+  const int64_t qr0 = static_cast<int64_t>(b) * k.Hq + static_cast<int64_t>(h) * k.G + g0;  // first query row
+  if (g0 == 0 && tid == 0) a.ctr[bh] = 0;
+  const float c2 = a.sm_scale * kLog2e;
+  // window keys: thread pair (tk, half) holds slot tk = tid / 2, coordinates
+  // 64 half .. 64 half + 63 (past d: zero); rows hold d coordinates
+  const int tk0 = tid >> 1, half = tid & 1;
+  uint4 kv[8];
+  if (tk0 < nwin) {
+    const uint4* kr = reinterpret_cast<const uint4*>(a.k_win + (bh * k.W + tk0) * k.d + 64 * half);
+#pragma unroll
+    for (int c = 0; c < 8; ++c) kv[c] = 64 * half + 8 * c < k.d ? kr[c] : make_uint4(0u, 0u, 0u, 0u);
+  }
+  // window values: thread (c4, q8) holds slots q8, q8 + 8, ... (first 16), coordinates c4 .. c4+3
+  // (threads with c4 >= d read slot 0's first coordinates and discard them)
+  const bool vlive = c4 < k.d;
+  const uint16_t* vbase = a.v_win + bh * k.W * k.d + (vlive ? c4 : 0);
+  uint2 vv[16];
+#pragma unroll
+  for (int u = 0; u < 16; ++u)
+    if (q8 + 8 * u < nwin) vv[u] = *reinterpret_cast<const uint2*>(vbase + static_cast<int64_t>(q8 + 8 * u) * k.d);
+  // the query rows (d coordinates, scaled to log2 units; zero past d)
+  for (int e = tid; e < GW * kD; e += kSmallThreads) {
+    const int g = e / kD, i = e % kD;
+    qw[g][i] = i < k.d ? load_any(a.q, (qr0 + g) * k.d + i, a.q_dtype) * c2 : 0.0f;
+  }
+  lds_barrier();
+  // scores: two threads per slot, 64 coordinates each; slots past the first
+  // 128 are loaded here
+  for (int e = tid; e < 2 * nwin; e += kSmallThreads) {
+    const int tk = e >> 1;
+    if (e >= kSmallThreads) {
+      const uint4* kr = reinterpret_cast<const uint4*>(a.k_win + (bh * k.W + tk) * k.d + 64 * half);
+#pragma unroll
+      for (int c = 0; c < 8; ++c) kv[c] = 64 * half + 8 * c < k.d ? kr[c] : make_uint4(0u, 0u, 0u, 0u);
+    }
+    float sg[GW];
+#pragma unroll
+    for (int g = 0; g < GW; ++g) sg[g] = 0.0f;
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      const uint32_t u4v[4] = {kv[c].x, kv[c].y, kv[c].z, kv[c].w};
+#pragma unroll
+      for (int e2 = 0; e2 < 4; ++e2) {
+        const int i = 64 * half + 8 * c + 2 * e2;
+        const float k0 = half_bits_to_float(static_cast<uint16_t>(u4v[e2] & 0xffffu));
+        const float k1 = half_bits_to_float(static_cast<uint16_t>(u4v[e2] >> 16));
+#pragma unroll
+        for (int g = 0; g < GW; ++g) sg[g] = fmaf(qw[g][i + 1], k1, fmaf(qw[g][i], k0, sg[g]));
+      }
+    }
+#pragma unroll
+    for (int g = 0; g < GW; ++g) sg[g] += __shfl_xor(sg[g], 1, 64);
+    if (half == 0) {
+      // slot tk holds the largest position p < T with p = tk (mod W)
+      const int pos = tk + k.W * ((T - 1 - tk) / k.W);
+#pragma unroll
+      for (int g = 0; g < GW; ++g) {
+        ls[g][tk] = sg[g];
+        if (a.dbg_logits) a.dbg_logits[(qr0 + g) * a.logits_stride + pos] = sg[g] * kLn2;
+      }
+    }
+  }
+  lds_barrier();
+  // per query head (one wave each): maximum, weights, their sum
+  for (int g = wv; g < GW; g += kSmallThreads / 64) {
+    float m = -INFINITY;
+    for (int tk = lane; tk < nwin; tk += 64) m = fmaxf(m, ls[g][tk]);
+    m = wave_max(m);
+    float lw = 0.0f;
+    for (int tk = lane; tk < nwin; tk += 64) {
+      const float w = exp2f(ls[g][tk] - m);
+      ls[g][tk] = w;
+      lw += w;
+    }
+    lw = wave_sum(lw);
+    if (lane == 0) {
+      sMw[g] = m;
+      sLw[g] = lw;
+    }
+  }
+  lds_barrier();
+  // weighted values: thread (c4, q8) takes slots q8, q8+8, ...
+  {
+    float4 acc[GW];
+#pragma unroll
+    for (int g = 0; g < GW; ++g) acc[g] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+    auto add = [&](int tk, uint2 u) {
+      const float v0 = half_bits_to_float(static_cast<uint16_t>(u.x & 0xffffu));
+      const float v1 = half_bits_to_float(static_cast<uint16_t>(u.x >> 16));
+      const float v2 = half_bits_to_float(static_cast<uint16_t>(u.y & 0xffffu));
+      const float v3 = half_bits_to_float(static_cast<uint16_t>(u.y >> 16));
+#pragma unroll
+      for (int g = 0; g < GW; ++g) {
+        const float w = ls[g][tk];
+        acc[g].x = fmaf(w, v0, acc[g].x);
+        acc[g].y = fmaf(w, v1, acc[g].y);
+        acc[g].z = fmaf(w, v2, acc[g].z);
+        acc[g].w = fmaf(w, v3, acc[g].w);
+      }
+    };
+#pragma unroll
+    for (int u = 0; u < 16; ++u)
+      if (q8 + 8 * u < nwin) add(q8 + 8 * u, vv[u]);
+    for (int tk = q8 + 128; tk < nwin; tk += 8)
+      add(tk, *reinterpret_cast<const uint2*>(vbase + static_cast<int64_t>(tk) * k.d));
+#pragma unroll
+    for (int g = 0; g < GW; ++g)
+      *reinterpret_cast<float4*>(&part[q8][g][c4]) = vlive ? acc[g] : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+  }
+  lds_barrier();
+  for (int e = tid; e < GW * kD; e += kSmallThreads) {
+    const int g = e / kD, i = e % kD;
+    float v = part[0][g][i];
+#pragma unroll
+    for (int r = 1; r < 8; ++r) v += part[r][g][i];
+    a.wacc[(qr0 + g) * kD + i] = v;
+  }
+  if (tid < GW) {
+    a.wm[qr0 + tid] = sMw[tid];
+    a.wl[qr0 + tid] = sLw[tid];
+  }
+}
+
+// Work-groups 0 .. nrot-1 rotate the queries of (kv head h, query heads g0
+// .. g0+GW-1); work-groups nrot .. 2 nrot-1 take the FP16 window of the same
+// heads.  The two run side by side (each is a short chain of memory round
+// trips).
+template <int GW>
+__global__ __launch_bounds__(kSmallThreads) void prep_kernel(DecodeArgs a, DevTables t, KParams k, int qjl) {
+  __shared__ float qv[GW][kD], qr[GW][kD], part[8][GW][kD];
+  __shared__ float ls[GW][kMaxWindow];
+  __shared__ float sMw[GW], sLw[GW];
+  const int nhs = k.G / GW;
+  const int nrot = k.Hkv * nhs;
+  const bool rot = static_cast<int>(blockIdx.x) < nrot;
+  const int x = rot ? blockIdx.x : blockIdx.x - nrot;
+  const int h = x / nhs, g0 = (x % nhs) * GW, b = blockIdx.y;
+  if (rot)
+    rotate_queries<GW>(a, t, k, qjl, b, h, g0, qv, qr, part);
+  else
+    window_partial<GW>(a, k, b, h, g0, qv, ls, part, sMw, sLw);
 }
 
 // ---------------------------------------------------------------- scan
@@ -362,295 +518,16 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(DecodeArgs a, DevTab
   }
 }
 
-// ---------------------------------------------------------------- merge
-// One work-group per (b, kv head) for its G query heads (or, when that makes
-// too few work-groups, for GW of them): the window K/V rows, the split
-// partials and Pi are each read once per work-group.  The kernel is a short chain
-// of dependent steps, so every load is issued at the start, the split
-// partials (needed first) ahead of the window keys and values of the first 128
-// slots and the columns of Pi, which land while the partials are combined.
-template <int GW>
-__global__ __launch_bounds__(kSmallThreads) void merge_kernel(DecodeArgs a, DevTables t, KParams k) {
-  __shared__ float accr[GW][kD], ow[GW][kD], qw[GW][kD], part[8][GW][kD];
-  __shared__ float ls[GW][kMaxWindow];
-  __shared__ float sM[GW], sL[8][GW], sM2[GW], sLw[GW], sMx[8][GW];
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-  const int c4 = (tid & 31) * 4, q8 = tid >> 5;
-  // work-group (kv head h, heads g0 .. g0+GW-1 of its group of k.G)
-  const int nhs = k.G / GW;
-  const int h = blockIdx.x / nhs, g0 = (blockIdx.x % nhs) * GW, b = blockIdx.y;
-  const int T = a.seq_lens[b];
-  const int nwin = T < k.W ? T : k.W;
-  const int64_t row0 = (static_cast<int64_t>(b) * k.Hq + static_cast<int64_t>(h) * k.G + g0) * kD;
-  // output rows and FP16 window rows hold d coordinates (d <= kD, a multiple of 8)
-  const int64_t orow0 = (static_cast<int64_t>(b) * k.Hq + static_cast<int64_t>(h) * k.G + g0) * k.d;
-  const int64_t bh = static_cast<int64_t>(b) * k.Hkv + h;
-  const bool dense = k.rotation == TQ_ROT_DENSE;
-
-  // ---- loads, in the order they are needed (loads complete in order: a
-  // wait for the first ones does not wait for the rest)
-  // split partials: thread (c4, q8) takes query g = q8 % GW and reads the
-  // accumulators of its first kFirst splits s = sub, sub + nsub, ... (sub =
-  // q8 / GW); together the nsub threads of a query cover the first
-  // kFirst nsub splits, whose maximum they combine through LDS
-  constexpr int nsub = 8 / GW;
-  // (16 for one query head per work-group: the launch shape with few work-
-  // groups and many splits per head; 8 otherwise, which keeps two waves per SIMD)
-  constexpr int kFirst = GW == 1 ? 16 : 8;
-  const int g = q8 % GW, sub = q8 / GW;
-  // (loads are unconditional, from a clamped split index, and the result is
-  // selected: a load under a branch would make its join wait for all loads)
-  float4 va[kFirst];
-  float la[kFirst], ma[kFirst];
-#pragma unroll
-  for (int u = 0; u < kFirst; ++u) {
-    const int s = sub + u * nsub;
-    const int64_t pi = (bh * a.splits + (s < a.splits ? s : 0)) * k.G + g0 + g;
-    va[u] = *reinterpret_cast<const float4*>(a.pacc + pi * kD + c4);
-    la[u] = a.pl[pi];
-    ma[u] = a.pm[pi];
-  }
-#pragma unroll
-  for (int u = 0; u < kFirst; ++u) la[u] = sub + u * nsub < a.splits ? la[u] : 0.0f;
-  // window keys: thread pair (tk, half) holds slot tk = tid / 2, coordinates 64 half ..
-  const int tk0 = tid >> 1, half = tid & 1;
-  // (coordinates past d read as zero)
-  uint4 kv[8];
-  if (tk0 < nwin) {
-    const uint4* kr = reinterpret_cast<const uint4*>(a.k_win + (bh * k.W + tk0) * k.d + 64 * half);
-#pragma unroll
-    for (int c = 0; c < 8; ++c) kv[c] = 64 * half + 8 * c < k.d ? kr[c] : make_uint4(0u, 0u, 0u, 0u);
-  }
-  // window values: thread (c4, q8) holds slots q8, q8 + 8, ... (first 16), coordinates c4 .. c4+3
-  // (threads with c4 >= d read slot 0's first coordinates and discard them)
-  const bool vlive = c4 < k.d;
-  const uint16_t* vbase = a.v_win + bh * k.W * k.d + (vlive ? c4 : 0);
-  uint2 vv[16];
-#pragma unroll
-  for (int u = 0; u < 16; ++u)
-    if (q8 + 8 * u < nwin) vv[u] = *reinterpret_cast<const uint2*>(vbase + static_cast<int64_t>(q8 + 8 * u) * k.d);
-  // columns c4 .. c4+3 of Pi, rows 16 q8 .. 16 q8 + 15 (dense rotation)
-  float4 rm[16];
-  if (dense) {
-#pragma unroll
-    for (int r = 0; r < 16; ++r) rm[r] = *reinterpret_cast<const float4*>(t.rot + (q8 * 16 + r) * kD + c4);
-  }
-  // the window query, stored to LDS after the combine (a store now would wait for every load above)
-  constexpr int kNq = (GW * kD + kSmallThreads - 1) / kSmallThreads;
-  float qwr[kNq];
-#pragma unroll
-  for (int u = 0; u < kNq; ++u) {
-    const int e = tid + u * kSmallThreads;
-    qwr[u] = a.qwin[row0 + (e < GW * kD ? e : 0)];
-  }
-
-  // 1. combine the split partials in fixed order; the maximum M over the
-  //    non-empty splits (l > 0) is exact in any order
-  {
-    float M = -INFINITY;
-#pragma unroll
-    for (int u = 0; u < kFirst; ++u)
-      if (la[u] > 0.0f) M = fmaxf(M, ma[u]);
-    // splits past the first kFirst nsub: every thread of the query reads them all
-    for (int s0 = kFirst * nsub; s0 < a.splits; s0 += 16) {
-      float lv[16], mv[16];
-#pragma unroll
-      for (int u = 0; u < 16; ++u) {
-        const int64_t pi = (bh * a.splits + (s0 + u < a.splits ? s0 + u : s0)) * k.G + g0 + g;
-        lv[u] = a.pl[pi];
-        mv[u] = a.pm[pi];
-      }
-#pragma unroll
-      for (int u = 0; u < 16; ++u) lv[u] = s0 + u < a.splits ? lv[u] : 0.0f;
-#pragma unroll
-      for (int u = 0; u < 16; ++u)
-        if (lv[u] > 0.0f) M = fmaxf(M, mv[u]);
-    }
-    if ((tid & 31) == 0) sMx[sub][g] = M;
-    lds_barrier();
-#pragma unroll
-    for (int r = 0; r < nsub; ++r) M = fmaxf(M, sMx[r][g]);
-    float4 acc = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-    float L = 0.0f;
-    // an empty split (l = 0) gets weight 0 and its accumulator is not used
-    auto add = [&](const float4& v, float lv, float mv) {
-      if (lv > 0.0f) {
-        const float f = exp2f(mv - M);
-        L = fmaf(f, lv, L);
-        acc.x = fmaf(f, v.x, acc.x);
-        acc.y = fmaf(f, v.y, acc.y);
-        acc.z = fmaf(f, v.z, acc.z);
-        acc.w = fmaf(f, v.w, acc.w);
-      }
-    };
-#pragma unroll
-    for (int u = 0; u < kFirst; ++u) add(va[u], la[u], ma[u]);
-    // later batches of 8 splits: all loads of a batch are issued before use
-    for (int s0 = sub + kFirst * nsub; s0 < a.splits; s0 += 8 * nsub) {
-      float4 v[8];
-      float lv[8], mv[8];
-#pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const int s = s0 + u * nsub;
-        const int64_t pi = (bh * a.splits + (s < a.splits ? s : s0)) * k.G + g0 + g;
-        v[u] = *reinterpret_cast<const float4*>(a.pacc + pi * kD + c4);
-        lv[u] = a.pl[pi];
-        mv[u] = a.pm[pi];
-      }
-#pragma unroll
-      for (int u = 0; u < 8; ++u) lv[u] = s0 + u * nsub < a.splits ? lv[u] : 0.0f;
-#pragma unroll
-      for (int u = 0; u < 8; ++u) add(v[u], lv[u], mv[u]);
-    }
-    *reinterpret_cast<float4*>(&part[sub][g][c4]) = acc;
-    if ((tid & 31) == 0) {
-      sL[sub][g] = L;
-      if (sub == 0) sM[g] = M;
-    }
-  }
-#pragma unroll
-  for (int u = 0; u < kNq; ++u) {
-    const int e = tid + u * kSmallThreads;
-    if (e < GW * kD) qw[e / kD][e % kD] = qwr[u];
-  }
-  lds_barrier();
-  for (int e = tid; e < GW * kD; e += kSmallThreads) {
-    const int g = e / kD, i = e % kD;
-    float v = part[0][g][i];
-#pragma unroll
-    for (int r = 1; r < 8 / GW; ++r) v += part[r][g][i];
-    accr[g][i] = v;
-  }
-
-  // 2. window scores (original basis, FP16 keys, log2 units): two threads per
-  //    slot, 64 coordinates each; slots past the first 128 are loaded here.
-  for (int e = tid; e < 2 * nwin; e += kSmallThreads) {
-    const int tk = e >> 1;
-    if (e >= kSmallThreads) {
-      const uint4* kr = reinterpret_cast<const uint4*>(a.k_win + (bh * k.W + tk) * k.d + 64 * half);
-#pragma unroll
-      for (int c = 0; c < 8; ++c) kv[c] = 64 * half + 8 * c < k.d ? kr[c] : make_uint4(0u, 0u, 0u, 0u);
-    }
-    float sg[GW];
-#pragma unroll
-    for (int g = 0; g < GW; ++g) sg[g] = 0.0f;
-#pragma unroll
-    for (int c = 0; c < 8; ++c) {
-      const uint32_t u4v[4] = {kv[c].x, kv[c].y, kv[c].z, kv[c].w};
-#pragma unroll
-      for (int e2 = 0; e2 < 4; ++e2) {
-        const int i = 64 * half + 8 * c + 2 * e2;
-        const float k0 = half_bits_to_float(static_cast<uint16_t>(u4v[e2] & 0xffffu));
-        const float k1 = half_bits_to_float(static_cast<uint16_t>(u4v[e2] >> 16));
-#pragma unroll
-        for (int g = 0; g < GW; ++g) sg[g] = fmaf(qw[g][i + 1], k1, fmaf(qw[g][i], k0, sg[g]));
-      }
-    }
-#pragma unroll
-    for (int g = 0; g < GW; ++g) sg[g] += __shfl_xor(sg[g], 1, 64);
-    if (half == 0) {
-      // slot tk holds the largest position p < T with p = tk (mod W)
-      const int pos = tk + k.W * ((T - 1 - tk) / k.W);
-#pragma unroll
-      for (int g = 0; g < GW; ++g) {
-        ls[g][tk] = sg[g];
-        if (a.dbg_logits) a.dbg_logits[(static_cast<int64_t>(b) * k.Hq + h * k.G + g0 + g) * a.logits_stride + pos] = sg[g] * kLn2;
-      }
-    }
-  }
-  lds_barrier();
-  // 3. per query head (one wave each): window max, weights, their sum
-  for (int g = wv; g < GW; g += kSmallThreads / 64) {
-    float m = sM[g];
-    for (int tk = lane; tk < nwin; tk += 64) m = fmaxf(m, ls[g][tk]);
-    m = wave_max(m);
-    float lw = 0.0f;
-    for (int tk = lane; tk < nwin; tk += 64) {
-      const float w = exp2f(ls[g][tk] - m);
-      ls[g][tk] = w;
-      lw += w;
-    }
-    lw = wave_sum(lw);
-    if (lane == 0) {
-      sM2[g] = m;
-      sLw[g] = lw;
-    }
-  }
-  lds_barrier();
-  // 4. weighted FP16 window values: thread (c4, q8) takes slots q8, q8+8, ...
-  {
-    float4 acc[GW];
-#pragma unroll
-    for (int g = 0; g < GW; ++g) acc[g] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-    auto add = [&](int tk, uint2 u) {
-      const float v0 = half_bits_to_float(static_cast<uint16_t>(u.x & 0xffffu));
-      const float v1 = half_bits_to_float(static_cast<uint16_t>(u.x >> 16));
-      const float v2 = half_bits_to_float(static_cast<uint16_t>(u.y & 0xffffu));
-      const float v3 = half_bits_to_float(static_cast<uint16_t>(u.y >> 16));
-#pragma unroll
-      for (int g = 0; g < GW; ++g) {
-        const float w = ls[g][tk];
-        acc[g].x = fmaf(w, v0, acc[g].x);
-        acc[g].y = fmaf(w, v1, acc[g].y);
-        acc[g].z = fmaf(w, v2, acc[g].z);
-        acc[g].w = fmaf(w, v3, acc[g].w);
-      }
-    };
-#pragma unroll
-    for (int u = 0; u < 16; ++u)
-      if (q8 + 8 * u < nwin) add(q8 + 8 * u, vv[u]);
-    for (int tk = q8 + 128; tk < nwin; tk += 8)
-      add(tk, *reinterpret_cast<const uint2*>(vbase + static_cast<int64_t>(tk) * k.d));
-#pragma unroll
-    for (int g = 0; g < GW; ++g)
-      *reinterpret_cast<float4*>(&part[q8][g][c4]) = vlive ? acc[g] : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-  }
-  lds_barrier();
-  for (int e = tid; e < GW * kD; e += kSmallThreads) {
-    const int g = e / kD, i = e % kD;
-    float v = part[0][g][i];
-#pragma unroll
-    for (int r = 1; r < 8; ++r) v += part[r][g][i];
-    ow[g][i] = v;
-  }
-  lds_barrier();
-  // 5. one inverse rotation per query head: o = Pi^T acc_rot
-  if (dense) {
-    // o[g][j] = sum_i Pi[i][j] accr[g][i]; thread (c4, q8) sums rows 16 q8 ..
-#pragma unroll
-    for (int g = 0; g < GW; ++g) {
-      float4 o = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float xv = accr[g][q8 * 16 + r];
-        o.x = fmaf(rm[r].x, xv, o.x);
-        o.y = fmaf(rm[r].y, xv, o.y);
-        o.z = fmaf(rm[r].z, xv, o.z);
-        o.w = fmaf(rm[r].w, xv, o.w);
-      }
-      *reinterpret_cast<float4*>(&part[q8][g][c4]) = o;
-    }
-    lds_barrier();
-    for (int e = tid; e < GW * kD; e += kSmallThreads) {
-      const int g = e / kD, i = e % kD;
-      float v = part[0][g][i];
-#pragma unroll
-      for (int r = 1; r < 8; ++r) v += part[r][g][i];
-      accr[g][i] = v;
-    }
-    lds_barrier();
-  } else {
-    hadamard_lds<GW>(accr, nullptr, t.rot);
-  }
-  for (int e = tid; e < GW * kD; e += kSmallThreads) {
-    const int g = e / kD, i = e % kD;
-    const float M = sM[g], M2 = sM2[g];
-    const float corr = (M == -INFINITY) ? 0.0f : exp2f(M - M2);
-    float L = 0.0f;
-    for (int r = 0; r < 8 / GW; ++r) L += sL[r][g];
-    const float Ltot = fmaf(L, corr, sLw[g]);
-    if (i < k.d) a.out[orow0 + g * k.d + i] = Ltot > 0.0f ? fmaf(accr[g][i], corr, ow[g][i]) / Ltot : 0.0f;
-  }
+// ---------------------------------------------------------------- finalize
+// After the vector-ALU scan: one work-group per (b, kv head) combines the
+// split partials with the window's (the matrix-core scan does this in its
+// last work-group of each kv head).
+template <int G>
+__global__ __launch_bounds__(kSmallThreads) void finalize_kernel(DecodeArgs a, DevTables t, KParams k) {
+  __shared__ float acc[G][kD];
+  __shared__ float fin[finalize_scratch_floats<kSmallThreads, G>()];
+  __shared__ float sM[G], sL[G], sW[G];
+  finalize_bh<kSmallThreads, G>(a, t, k, blockIdx.y, blockIdx.x, acc, fin, sM, sL, sW);
 }
 
 template <int G, int BK, int BV>
@@ -734,18 +611,16 @@ int launch_decode(const tq_ctx* c, const DecodeArgs& a, void* stream) {
   hipStream_t s = static_cast<hipStream_t>(stream);
   const KParams k = make_kparams(c);
   const int qjl = c->p.key_qjl;
-  // prep and merge: one work-group per (sequence, kv head) for up to
-  // kMergeMaxHeads query heads (eight heads made one work-group's chain of
-  // window, combine and inverse rotation the longest step), and fewer when
-  // that leaves fewer than kMergeGroups work-groups: the heads of a group
-  // are spread over G / GW work-groups (GW heads each)
-  int GW = k.G < kMergeMaxHeads ? k.G : kMergeMaxHeads;
-  while (GW > 1 && static_cast<long long>(a.batch) * k.Hkv * (k.G / GW) < kMergeGroups) GW /= 2;
-  const dim3 gm(k.Hkv * (k.G / GW), a.batch);
+  // prep: per (sequence, kv head) one work-group rotating up to
+  // kPrepMaxHeads query heads and one taking their FP16 window; fewer heads
+  // per work-group (GW) when that leaves fewer than kPrepGroups of each
+  int GW = k.G < kPrepMaxHeads ? k.G : kPrepMaxHeads;
+  while (GW > 1 && static_cast<long long>(a.batch) * k.Hkv * (k.G / GW) < kPrepGroups) GW /= 2;
+  const dim3 gp(2 * k.Hkv * (k.G / GW), a.batch);
   switch (GW) {
-    case 1: hipLaunchKernelGGL(prep_kernel<1>, gm, dim3(kSmallThreads), 0, s, a, c->t, k, qjl); break;
-    case 2: hipLaunchKernelGGL(prep_kernel<2>, gm, dim3(kSmallThreads), 0, s, a, c->t, k, qjl); break;
-    case 4: hipLaunchKernelGGL(prep_kernel<4>, gm, dim3(kSmallThreads), 0, s, a, c->t, k, qjl); break;
+    case 1: hipLaunchKernelGGL(prep_kernel<1>, gp, dim3(kSmallThreads), 0, s, a, c->t, k, qjl); break;
+    case 2: hipLaunchKernelGGL(prep_kernel<2>, gp, dim3(kSmallThreads), 0, s, a, c->t, k, qjl); break;
+    case 4: hipLaunchKernelGGL(prep_kernel<4>, gp, dim3(kSmallThreads), 0, s, a, c->t, k, qjl); break;
     default: return 1;
   }
   if (hipGetLastError() != hipSuccess) return 1;
@@ -753,13 +628,15 @@ int launch_decode(const tq_ctx* c, const DecodeArgs& a, void* stream) {
   // (taken by the launch itself, so no marker is queued around the kernel)
   void* ev0 = profile_slot(c, 0);
   void* ev1 = ev0 ? profile_slot(c, 1) : nullptr;
-  const int rc = (c->p.flags & TQ_FLAG_VALU_SCAN) ? launch_scan_valu(c, a, k, s, ev0, ev1)
-                                                  : launch_scan_mfma(c, a, k, stream, ev0, ev1);
-  if (rc != 0) return 1;
-  switch (GW) {
-    case 1: hipLaunchKernelGGL(merge_kernel<1>, gm, dim3(kSmallThreads), 0, s, a, c->t, k); break;
-    case 2: hipLaunchKernelGGL(merge_kernel<2>, gm, dim3(kSmallThreads), 0, s, a, c->t, k); break;
-    case 4: hipLaunchKernelGGL(merge_kernel<4>, gm, dim3(kSmallThreads), 0, s, a, c->t, k); break;
+  if (!(c->p.flags & TQ_FLAG_VALU_SCAN))  // the matrix-core scan finalizes in its last work-group per kv head
+    return launch_scan_mfma(c, a, k, stream, ev0, ev1) == 0 ? 0 : 1;
+  if (launch_scan_valu(c, a, k, s, ev0, ev1) != 0) return 1;
+  const dim3 gf(k.Hkv, a.batch);
+  switch (k.G) {
+    case 1: hipLaunchKernelGGL(finalize_kernel<1>, gf, dim3(kSmallThreads), 0, s, a, c->t, k); break;
+    case 2: hipLaunchKernelGGL(finalize_kernel<2>, gf, dim3(kSmallThreads), 0, s, a, c->t, k); break;
+    case 4: hipLaunchKernelGGL(finalize_kernel<4>, gf, dim3(kSmallThreads), 0, s, a, c->t, k); break;
+    case 8: hipLaunchKernelGGL(finalize_kernel<8>, gf, dim3(kSmallThreads), 0, s, a, c->t, k); break;
     default: return 1;
   }
   return hipGetLastError() == hipSuccess ? 0 : 1;

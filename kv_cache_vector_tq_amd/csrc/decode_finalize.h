@@ -1,0 +1,186 @@
+// Final step of tq_decode_attn for one (sequence b, kv head h), run by the
+// last scan work-group of the pair to finish (or by a finalize kernel after
+// the vector-ALU scan): combine the split partials (m_s, l_s, acc_s, rotated
+// basis, s = 0 .. splits-1 in order) with the FP16 window's partial (m_w,
+// l_w, acc_w, original basis), apply Pi^T once and normalise
+// ("TurboQuant Family Design Study", section "CPU and WASM kernel design":
+// values accumulated in the rotated basis, one inverse transform per head):
+//   M = max(m_s, m_w),  L = sum_s 2^(m_s - M) l_s + 2^(m_w - M) l_w,
+//   o = (Pi^T sum_s 2^(m_s - M) acc_s + 2^(m_w - M) acc_w) / L.
+// Every sum is taken in a fixed order, so the result does not depend on
+// which work-group finalizes.
+#pragma once
+
+#include "decode_common.h"
+#include "device_common.h"
+
+namespace tq {
+
+// LDS floats the finalize needs besides acc[G][kD]: NT * max(G, 4).
+template <int NT, int G>
+constexpr int finalize_scratch_floats() { return NT * (G > 4 ? G : 4); }
+
+// Called after this work-group's partial is in global memory; every thread
+// calls it.  Returns true in the work-group that arrives last among the
+// splits of (b, h), which then sees every split's partial.  Each wave waits
+// for its own stores to be acknowledged; one thread then counts the arrival
+// with an agent-scope acquire-release add (its release writes back this
+// XCD's L2 so that the partial reaches a finalizer on another XCD; its
+// acquire invalidates the caches the finalizer reads through).  One such
+// pair per work-group: a device fence in every wave measured twice the scan
+// time.
+template <int NT>
+__device__ inline bool arrive_last(int* ctr, int splits, int* flag) {
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's partial stores are done
+  __syncthreads();
+  if (threadIdx.x == 0)
+    *flag = __hip_atomic_fetch_add(ctr, 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT) == splits - 1;
+  __syncthreads();
+  return *flag != 0;
+}
+
+template <int NT, int G>
+__device__ void finalize_bh(const DecodeArgs& a, const DevTables& t, const KParams& k, int b, int h,
+                            float (*acc)[kD], float* fin, float* sM, float* sL, float* sW) {
+  (void)sM;
+  const int tid = threadIdx.x;
+  const int64_t bh = static_cast<int64_t>(b) * k.Hkv + h;
+  const int64_t q0 = static_cast<int64_t>(b) * k.Hq + static_cast<int64_t>(h) * G;  // first query row
+  const int S = a.splits;
+  const bool dense = k.rotation == TQ_ROT_DENSE;
+  // Global loads go out together, before any of them is used: this runs
+  // after the arrival's cache invalidation, so each round trip is a full
+  // memory latency.
+  // (a) this thread's slice of a row of Pi^T (dense): thread (j, part)
+  constexpr int P = NT / kD;
+  constexpr int kSlice = kD / P;
+  const int j = tid % kD, p = tid / kD;
+  float4 rrow[kSlice / 4];
+  if (dense) {
+    const float4* row = reinterpret_cast<const float4*>(t.rotT + j * kD + p * kSlice);
+#pragma unroll
+    for (int i4 = 0; i4 < kSlice / 4; ++i4) rrow[i4] = row[i4];
+  }
+  // (b) the window accumulator elements this thread finishes in step 3
+  constexpr int kOut = (G * kD + NT - 1) / NT;
+  float wa[kOut];
+#pragma unroll
+  for (int r = 0; r < kOut; ++r) {
+    const int e = tid + r * NT;
+    wa[r] = e < G * kD ? a.wacc[(q0 + e / kD) * kD + e % kD] : 0.0f;
+  }
+  // (c) combine item: query g, coordinates c4 .. c4+3, splits grp, grp + NG, ...
+  constexpr int kItems = G * (kD / 4);
+  constexpr int NG = NT / kItems > 0 ? NT / kItems : 1;
+  constexpr int kRounds = (kItems * NG + NT - 1) / NT;
+  // 1. per query: M over the non-empty partials, the window factor, L;
+  //    every thread takes its queries' values from all splits itself
+  float4 v[kRounds];
+#pragma unroll
+  for (int r = 0; r < kRounds; ++r) {
+    const int e = tid + r * NT;
+    v[r] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+    if (e >= kItems * NG) continue;
+    const int item = e % kItems, grp = e / kItems;
+    const int g = item / (kD / 4), c4 = 4 * (item % (kD / 4));
+    const float wl = a.wl[q0 + g], wmv = a.wm[q0 + g];
+    float M = wl > 0.0f ? wmv : -INFINITY;
+#pragma unroll 8
+    for (int s2 = 0; s2 < S; ++s2) {
+      const int64_t pi = (bh * S + s2) * G + g;
+      const float ls = a.pl[pi], ms = a.pm[pi];
+      if (ls > 0.0f) M = fmaxf(M, ms);
+    }
+    float L = 0.0f;
+#pragma unroll 4
+    for (int s2 = grp; s2 < S; s2 += NG) {
+      const int64_t pi = (bh * S + s2) * G + g;
+      const float ls = a.pl[pi];
+      if (ls > 0.0f) {
+        const float f = exp2f(a.pm[pi] - M);
+        const float4 pa = *reinterpret_cast<const float4*>(a.pacc + pi * kD + c4);
+        v[r].x = fmaf(f, pa.x, v[r].x);
+        v[r].y = fmaf(f, pa.y, v[r].y);
+        v[r].z = fmaf(f, pa.z, v[r].z);
+        v[r].w = fmaf(f, pa.w, v[r].w);
+      }
+    }
+    if (grp == 0 && c4 == 0) {
+      for (int s2 = 0; s2 < S; ++s2) {
+        const int64_t pi = (bh * S + s2) * G + g;
+        const float ls = a.pl[pi];
+        if (ls > 0.0f) L += exp2f(a.pm[pi] - M) * ls;
+      }
+      const float fw = wl > 0.0f ? exp2f(wmv - M) : 0.0f;
+      sW[g] = fw;
+      sL[g] = fmaf(fw, wl, L);
+    }
+    *reinterpret_cast<float4*>(fin + (grp * G + g) * kD + c4) = v[r];
+  }
+  __syncthreads();
+  for (int e = tid; e < G * kD; e += NT) {
+    const int g = e / kD, i = e % kD;
+    float x = fin[g * kD + i];
+    for (int r = 1; r < NG; ++r) x += fin[(r * G + g) * kD + i];
+    acc[g][i] = x;
+  }
+  __syncthreads();
+  // 2. back to the original basis
+  if (dense) {
+    // o[g][j] = sum_i Pi[i][j] acc[g][i] = sum_i PiT[j][i] acc[g][i]
+    float o[G];
+#pragma unroll
+    for (int g = 0; g < G; ++g) o[g] = 0.0f;
+#pragma unroll
+    for (int i4 = 0; i4 < kSlice / 4; ++i4) {
+      const float4 r = rrow[i4];
+      const int i = p * kSlice + 4 * i4;
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+        o[g] = fmaf(r.x, acc[g][i], o[g]);
+        o[g] = fmaf(r.y, acc[g][i + 1], o[g]);
+        o[g] = fmaf(r.z, acc[g][i + 2], o[g]);
+        o[g] = fmaf(r.w, acc[g][i + 3], o[g]);
+      }
+    }
+#pragma unroll
+    for (int g = 0; g < G; ++g) fin[(p * G + g) * kD + j] = o[g];
+    __syncthreads();
+    for (int e = tid; e < G * kD; e += NT) {
+      const int g = e / kD, jj = e % kD;
+      float x = fin[g * kD + jj];
+      for (int r = 1; r < P; ++r) x += fin[(r * G + g) * kD + jj];
+      acc[g][jj] = x;
+    }
+    __syncthreads();
+  } else {
+    // x = eps . H y / sqrt(kD): butterflies at strides 1 .. 64 in LDS
+    for (int hs = 1; hs < kD; hs <<= 1) {
+      for (int e = tid; e < G * (kD / 2); e += NT) {
+        const int g = e / (kD / 2), r = e % (kD / 2);
+        const int i0 = (r / hs) * 2 * hs + r % hs, i1 = i0 + hs;
+        const float x0 = acc[g][i0], x1 = acc[g][i1];
+        acc[g][i0] = x0 + x1;
+        acc[g][i1] = x0 - x1;
+      }
+      __syncthreads();
+    }
+    for (int e = tid; e < G * kD; e += NT) {
+      const int g = e / kD, i = e % kD;
+      acc[g][i] *= t.rot[i] * 0.08838834764831845f;  // 1/sqrt(128)
+    }
+    __syncthreads();
+  }
+  // 3. plus the window's share, normalised; rows of d coordinates
+#pragma unroll
+  for (int r = 0; r < kOut; ++r) {
+    const int e = tid + r * NT;
+    const int g = e / kD, jj = e % kD;
+    if (e >= G * kD || jj >= k.d) continue;
+    const float L = sL[g];
+    const float x = fmaf(sW[g], wa[r], acc[g][jj]);
+    a.out[(q0 + g) * k.d + jj] = L > 0.0f ? x / L : 0.0f;
+  }
+}
+
+}  // namespace tq

@@ -22,6 +22,7 @@
 #include <hip/hip_ext.h>
 
 #include "decode_common.h"
+#include "decode_finalize.h"
 #include "device_common.h"
 
 namespace tq {
@@ -266,6 +267,13 @@ scan_mfma_kernel(DecodeArgs a, DevTables t, Codebooks cb, KParams k) {
   __shared__ float wm[kWaves][G], wl[kWaves][G];
   __shared__ float red[G][kD];
   __shared__ float ck[16], cvv[16], ck2[16], cv2[16];
+  // the final combine (last work-group of the kv head): its scratch is the
+  // table memory when that is large enough
+  constexpr int kFin = finalize_scratch_floats<kThreads, G>();
+  constexpr bool kFinInLuts = sizeof(luts) >= sizeof(float) * kFin;
+  __shared__ __align__(16) float fin_own[kFinInLuts ? 1 : kFin];
+  __shared__ float fsm[3][G];
+  __shared__ int fflag;
   __shared__ int next_chunk;  // the split's next unclaimed chunk
 
   const int tid = threadIdx.x, split = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
@@ -314,6 +322,9 @@ scan_mfma_kernel(DecodeArgs a, DevTables t, Codebooks cb, KParams k) {
       a.pl[pidx + tid] = 0.0f;
     }
     for (int i = tid; i < G * kD; i += kThreads) a.pacc[pidx * kD + i] = 0.0f;
+    if (arrive_last<kThreads>(a.ctr + static_cast<int64_t>(b) * k.Hkv + h, a.splits, &fflag))
+      finalize_bh<kThreads, G>(a, t, k, b, h, red, kFinInLuts ? reinterpret_cast<float*>(luts) : fin_own, fsm[0],
+                               fsm[1], fsm[2]);
     return;
   }
   // codebooks to LDS (no dynamic indexing of kernel arguments), then the tables
@@ -604,12 +615,21 @@ scan_mfma_kernel(DecodeArgs a, DevTables t, Codebooks cb, KParams k) {
   };
   // ---- value product of one chunk with the weights in pv[slot]
   auto valuephase = [&](const VBuf<BV, VMIX>& d, int slot) {
+    // the lane's weight row (query ag, part amask, tokens 8kg ..), derived
+    // afresh from the lane id each step: an opaque read of the id keeps these
+    // values out of the registers held across the loop (a spill there would
+    // make every step wait for all loads in flight)
+    int ln;
+    asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(ln));
+    const int wn = ln & 15, wkg = ln >> 4;
+    const int wag = 2 * (wn >> 2) + (wn & 1);
+    const uint32_t wmask = ((wn >> 1) & 1) ? 0xffffe000u : 0u;
     u4 aw = u4{0u, 0u, 0u, 0u};
-    if (ag < G) {
-      const float4* pw = reinterpret_cast<const float4*>(pvw + slot * (G * kChunk) + ag * kChunk + 8 * kg);
+    if (wag < G) {
+      const float4* pw = reinterpret_cast<const float4*>(pvw + slot * (G * kChunk) + wag * kChunk + 8 * wkg);
       const float4 w0 = pw[0], w1 = pw[1];
-      aw = u4{pk_rtz(part_of(w0.x, amask), part_of(w0.y, amask)), pk_rtz(part_of(w0.z, amask), part_of(w0.w, amask)),
-              pk_rtz(part_of(w1.x, amask), part_of(w1.y, amask)), pk_rtz(part_of(w1.z, amask), part_of(w1.w, amask))};
+      aw = u4{pk_rtz(part_of(w0.x, wmask), part_of(w0.y, wmask)), pk_rtz(part_of(w0.z, wmask), part_of(w0.w, wmask)),
+              pk_rtz(part_of(w1.x, wmask), part_of(w1.y, wmask)), pk_rtz(part_of(w1.z, wmask), part_of(w1.w, wmask))};
     }
     if constexpr (VMIX) {
 #pragma unroll
@@ -743,6 +763,11 @@ scan_mfma_kernel(DecodeArgs a, DevTables t, Codebooks cb, KParams k) {
     a.pm[pidx + tid] = M;
     a.pl[pidx + tid] = L;
   }
+  // the last work-group of this kv head to finish combines every split's
+  // partial with the window's and writes the output rows
+  if (arrive_last<kThreads>(a.ctr + static_cast<int64_t>(b) * k.Hkv + h, a.splits, &fflag))
+    finalize_bh<kThreads, G>(a, t, k, b, h, red, kFinInLuts ? reinterpret_cast<float*>(luts) : fin_own, fsm[0],
+                             fsm[1], fsm[2]);
 }
 
 template <int G, int BK, int BV, bool KMIX, bool VMIX>

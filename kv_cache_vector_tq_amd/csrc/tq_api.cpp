@@ -85,7 +85,7 @@ int decode_splits(int batch, int hkv, int max_pages, int pages_per_split, int sl
 }
 
 struct WsLayout {
-  size_t qs, ps, psum, qwin, pm, pl, pacc, total;
+  size_t qs, ps, psum, wm, wl, wacc, pm, pl, pacc, ctr, total;
 };
 
 WsLayout ws_layout(const tq_params& p, int batch, int splits) {
@@ -99,10 +99,13 @@ WsLayout ws_layout(const tq_params& p, int batch, int splits) {
   w.qs = off; off += up(bq * d * 4);
   w.ps = off; off += up(bq * d * 4);
   w.psum = off; off += up(bq * 4);
-  w.qwin = off; off += up(bq * d * 4);
+  w.wm = off; off += up(bq * 4);
+  w.wl = off; off += up(bq * 4);
+  w.wacc = off; off += up(bq * d * 4);
   w.pm = off; off += up(nb * 4);
   w.pl = off; off += up(nb * 4);
   w.pacc = off; off += up(nb * d * 4);
+  w.ctr = off; off += up(static_cast<size_t>(batch) * p.num_kv_heads * 4);
   w.total = off;
   return w;
 }
@@ -519,7 +522,10 @@ TQ_API int tq_decode_attn(const tq_ctx* c, const void* q, int q_dtype, const uin
   a.qs = reinterpret_cast<float*>(base + w.qs);
   a.ps = reinterpret_cast<float*>(base + w.ps);
   a.psum = reinterpret_cast<float*>(base + w.psum);
-  a.qwin = reinterpret_cast<float*>(base + w.qwin);
+  a.wm = reinterpret_cast<float*>(base + w.wm);
+  a.wl = reinterpret_cast<float*>(base + w.wl);
+  a.wacc = reinterpret_cast<float*>(base + w.wacc);
+  a.ctr = reinterpret_cast<int*>(base + w.ctr);
   a.pm = reinterpret_cast<float*>(base + w.pm);
   a.pl = reinterpret_cast<float*>(base + w.pl);
   a.pacc = reinterpret_cast<float*>(base + w.pacc);

@@ -175,10 +175,13 @@ struct DecodeArgs {
   float* qs;      // [B][Hq][D] rotated query * sm_scale * log2(e)
   float* ps;      // [B][Hq][D] S q_rot * qjl_scale * sm_scale * log2(e)
   float* psum;    // [B][Hq] sum of ps
-  float* qwin;    // [B][Hq][D] query * sm_scale * log2(e), zero past d
+  float* wm;      // [B][Hq] FP16 window: max score (log2 units)
+  float* wl;      // [B][Hq] FP16 window: sum of 2^(s - wm)
+  float* wacc;    // [B][Hq][D] FP16 window: weighted values, original basis
   float* pm;      // [B][Hkv][splits][G] running max (log2 units)
   float* pl;      // [B][Hkv][splits][G] running sum
   float* pacc;    // [B][Hkv][splits][G][D] rotated-basis accumulator
+  int* ctr;       // [B][Hkv] scan work-groups finished (cleared by prep)
 };
 
 struct Ctx;  // tq_ctx
