@@ -27,7 +27,7 @@
 // taking its tokens from the FP16 ring (tokens already cached) or from the new
 // rows, and writes key records token by token, or the group's value words
 // (for each coordinate, the 32 tokens' codes as one bit string), which the
-// wave gathers from its lanes in LDS.
+// wave forms with a transpose of the code fields across its lanes.
 #include "device_common.h"
 #include "tq_internal.h"
 
@@ -126,6 +126,39 @@ __device__ inline double sum4(double v) {
   v += __shfl_xor(v, 16, 64);
   v += __shfl_xor(v, 32, 64);
   return v;
+}
+
+// One stage of a transpose of small fields across lanes: lanes that differ
+// in lane bit XOR swap blocks of S bits (mask M selects the blocks a lane
+// keeps in place).  Three stages transpose an 8 x 8 matrix of 4-bit fields
+// held as one word per lane over 8 lanes, four a 16 x 16 matrix of 2-bit
+// fields over 16 lanes: field i of lane r becomes field r of lane i.
+template <int XOR, uint32_t M, int S>
+__device__ __forceinline__ uint32_t xchg_fields(uint32_t x, int lane) {
+  const uint32_t p = static_cast<uint32_t>(__shfl_xor(static_cast<int>(x), XOR, 64));
+  return (lane & XOR) ? (((p >> S) & M) | (x & ~M)) : ((x & M) | ((p & M) << S));
+}
+__device__ __forceinline__ uint32_t transpose_nibbles8(uint32_t x, int lane) {
+  x = xchg_fields<1, 0x0F0F0F0Fu, 4>(x, lane);
+  x = xchg_fields<2, 0x00FF00FFu, 8>(x, lane);
+  return xchg_fields<4, 0x0000FFFFu, 16>(x, lane);
+}
+__device__ __forceinline__ uint32_t transpose_crumbs16(uint32_t x, int lane) {
+  x = xchg_fields<1, 0x33333333u, 2>(x, lane);
+  x = xchg_fields<2, 0x0F0F0F0Fu, 4>(x, lane);
+  x = xchg_fields<4, 0x00FF00FFu, 8>(x, lane);
+  return xchg_fields<8, 0x0000FFFFu, 16>(x, lane);
+}
+// 8 fields of 3 bits (24 bits) <-> 8 nibbles (the high bit of each zero)
+__device__ __forceinline__ uint32_t spread3to4(uint32_t x) {
+  x = ((x & 0xFFF000u) << 4) | (x & 0xFFFu);
+  x = ((x & 0x0FC00FC0u) << 2) | (x & 0x003F003Fu);
+  return ((x & 0x38383838u) << 1) | (x & 0x07070707u);
+}
+__device__ __forceinline__ uint32_t pack4to3(uint32_t x) {
+  x = (x & 0x07070707u) | ((x & 0x70707070u) >> 1);
+  x = (x & 0x003F003Fu) | ((x & 0x3F003F00u) >> 2);
+  return (x & 0x00000FFFu) | ((x & 0x0FFF0000u) >> 4);
 }
 
 // Encodes the COLS x 16 vectors whose fp16 coordinates the lanes hold in xb
@@ -416,7 +449,6 @@ void append_mma_kernel(AppendArgs a, DevTables t, EncCodebook cbk, Layout L, int
   __shared__ u4 fragP[HAD ? 1 : 8 * 4 * 2 * 64];  // 64 KB
   __shared__ u4 fragS[QJL ? 8 * 4 * 2 * 64 : 1];  // 64 KB
   __shared__ float ctab[16];
-  __shared__ uint32_t vbuf[KEY ? 1 : kEncWaves][KEY ? 1 : BITS * kD];  // a wave's value words of one group
   u4 emask[4];
   setup_tables<QJL, HAD>(fragP, fragS, ctab, t, cbk, emask);
 
@@ -458,13 +490,17 @@ void append_mma_kernel(AppendArgs a, DevTables t, EncCodebook cbk, Layout L, int
     const int pid = a.block_table[static_cast<int64_t>(b) * a.max_pages + gpos / L.P];
     uint8_t* hb = a.pool + static_cast<int64_t>(pid) * L.page_bytes + kBodyOffset + static_cast<int64_t>(h) * L.head_bytes;
     const int slot0 = gpos % L.P;
-    if constexpr (!KEY) {
-#pragma unroll
-      for (int e = l; e < BITS * kD; e += 64) vbuf[wave][e] = 0u;
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
-      __builtin_amdgcn_wave_barrier();
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
-    }
+    // value words of the group: word w of coordinate j at gw[w kD + j]; bits
+    // of tokens before lo (earlier appends) are kept, those from hi on are zero
+    uint32_t* gw = reinterpret_cast<uint32_t*>(hb + L.v_codes) + static_cast<int64_t>(slot0 / kVGroup) * BITS * kD;
+    const int keep_bits = (lo - gpos) * BITS;
+    auto put_word = [&](int w, int j, uint32_t v) {
+      const int kb = keep_bits - 32 * w;
+      if (kb > 0) v |= gw[w * kD + j] & (kb >= 32 ? 0xffffffffu : ((1u << kb) - 1u));
+      gw[w * kD + j] = v;
+    };
+    uint32_t ch3[2][4];  // 3-bit values: the lane's 24-bit chunks per 16-token block
+    (void)ch3;
 #pragma unroll
     for (int sb = 0; sb < kSub; ++sb) {
       // ---- load: lane (n, kg) of block c takes token 16 (kCols sb + c) + n of the group
@@ -487,9 +523,9 @@ void append_mma_kernel(AppendArgs a, DevTables t, EncCodebook cbk, Layout L, int
       encode_tile<QJL, HAD, BITS, N8, kCols>(
           fragP, fragS, ctab, emask, cbk, t.ntab, xb,
           [&](int c, const uint32_t* words, float nst, int nq) {
-            if (!live[c]) return;
             const int slot = slot0 + tk[c];
             if constexpr (KEY) {
+              if (!live[c]) return;
               uint32_t* cw =
                   reinterpret_cast<uint32_t*>(hb + L.k_codes + static_cast<int64_t>(slot) * L.k_rec) + BITS * kg;
 #pragma unroll
@@ -501,18 +537,34 @@ void append_mma_kernel(AppendArgs a, DevTables t, EncCodebook cbk, Layout L, int
                   reinterpret_cast<float*>(hb + L.k_norm)[slot] = nst;
               }
             } else {
-              if (kg == 0) reinterpret_cast<float*>(hb + L.v_norm)[slot] = nst;
-              // token tk's code of coordinate j goes to bits [tk BITS, (tk+1) BITS) of j's string
-              const int bit = tk[c] * BITS, w0 = bit >> 5, sh = bit & 31;
+              if (live[c] && kg == 0) reinterpret_cast<float*>(hb + L.v_norm)[slot] = nst;
+              // Token t's code of coordinate j goes to bits [t BITS, (t+1) BITS)
+              // of j's string.  The lanes of this 16-token block (tb) hold one
+              // token each and 32 coordinates: a transpose of the code fields
+              // across lanes gives each lane whole words of the strings (dead
+              // tokens carry zero codes).  All lanes take part in the shuffles.
+              const int tb = kCols * sb + c;
+              if constexpr (BITS == 4) {
+                // words[q]: codes of coordinates 32kg + 8q .. +7 -> word 2tb + n/8
+                // of coordinate 32kg + 8q + n%8 (tokens 16tb + 8(n/8) .. +7)
 #pragma unroll
-              for (int jj = 0; jj < 32; ++jj) {
-                const int pos = jj * BITS;
-                uint32_t code = words[pos >> 5] >> (pos & 31);
-                if ((pos & 31) + BITS > 32) code |= words[(pos >> 5) + 1] << (32 - (pos & 31));
-                code &= (1u << BITS) - 1u;
-                const int j = 32 * kg + jj;
-                atomicOr(&vbuf[wave][w0 * kD + j], code << sh);
-                if (sh + BITS > 32) atomicOr(&vbuf[wave][(w0 + 1) * kD + j], code >> (32 - sh));
+                for (int q = 0; q < 4; ++q)
+                  put_word(2 * tb + (n >> 3), 32 * kg + 8 * q + (n & 7), transpose_nibbles8(words[q], l));
+              } else if constexpr (BITS == 2) {
+                // words[q]: coordinates 32kg + 16q .. +15 -> word tb of coordinate 32kg + 16q + n
+#pragma unroll
+                for (int q = 0; q < 2; ++q) put_word(tb, 32 * kg + 16 * q + n, transpose_crumbs16(words[q], l));
+              } else {
+                // 8 codes (24 bits) at a time as nibbles, transposed, packed
+                // back: the 24-bit chunk of tokens 16tb + 8(n/8) .. +7 of
+                // coordinate 32kg + 8q + n%8; the chunks are joined below
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                  const int b0 = 24 * q, wi = b0 >> 5, sh = b0 & 31;
+                  uint32_t v = words[wi] >> sh;
+                  if (sh > 8) v |= words[wi + 1] << (32 - sh);
+                  ch3[tb][q] = pack4to3(transpose_nibbles8(spread3to4(v & 0xFFFFFFu), l));
+                }
               }
             }
           },
@@ -523,23 +575,26 @@ void append_mma_kernel(AppendArgs a, DevTables t, EncCodebook cbk, Layout L, int
             reinterpret_cast<uint32_t*>(hb + L.k_signs + static_cast<int64_t>(slot) * (kD / 8))[kg] = sw;
           });
     }
-    if constexpr (!KEY) {
-      // the group's words; bits of tokens before lo (earlier appends) are kept,
-      // those from hi on are zero
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
-      __builtin_amdgcn_wave_barrier();
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
-      uint32_t* gw = reinterpret_cast<uint32_t*>(hb + L.v_codes) + static_cast<int64_t>(slot0 / kVGroup) * BITS * kD;
-      const int keep_bits = (lo - gpos) * BITS;
+    if constexpr (!KEY && BITS == 3) {
+      // coordinate j's 96-bit string is chunks 0..3 (tokens 8w .. 8w+7) at
+      // bits 24w: lane n < 8 holds chunks 0 and 2, lane n + 8 chunks 1 and 3;
+      // each takes the other two from its partner and writes words 0, 1
+      // (n < 8) or word 2
+      const bool hi8 = (n & 8) != 0;
 #pragma unroll
-      for (int e = l; e < BITS * kD; e += 64) {
-        uint32_t v = vbuf[wave][e];
-        const int kb = keep_bits - 32 * (e / kD);
-        if (kb > 0) v |= gw[e] & (kb >= 32 ? 0xffffffffu : ((1u << kb) - 1u));
-        gw[e] = v;
+      for (int q = 0; q < 4; ++q) {
+        const uint32_t o0 = static_cast<uint32_t>(__shfl_xor(static_cast<int>(ch3[0][q]), 8, 64));
+        const uint32_t o1 = static_cast<uint32_t>(__shfl_xor(static_cast<int>(ch3[1][q]), 8, 64));
+        const uint32_t c0 = hi8 ? o0 : ch3[0][q], c1 = hi8 ? ch3[0][q] : o0;
+        const uint32_t c2 = hi8 ? o1 : ch3[1][q], c3 = hi8 ? ch3[1][q] : o1;
+        const int j = 32 * kg + 8 * q + (n & 7);
+        if (!hi8) {
+          put_word(0, j, c0 | (c1 << 24));
+          put_word(1, j, (c1 >> 8) | (c2 << 16));
+        } else {
+          put_word(2, j, (c2 >> 16) | (c3 << 8));
+        }
       }
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
-      __builtin_amdgcn_wave_barrier();
     }
   }
 }
