@@ -15,7 +15,8 @@
 //  3. finalize: per (b, kv head) combine the split partials and the window's
 //     in fixed order, apply Pi^T to the rotated accumulator once and
 //     normalise (decode_finalize.h): in the matrix-core scan's last
-//     work-group of the kv head, after the vector-ALU scan in a kernel.
+//     work-group of the kv head when it has at most kFuseMaxSplits splits,
+//     otherwise in a kernel of its own.
 #include <hip/hip_ext.h>
 
 #include <mutex>
@@ -179,16 +180,19 @@ __device__ void rotate_queries(const DecodeArgs& a, const DevTables& t, const KP
 // gives m_w = -inf, l_w = 0, acc_w = 0.  It depends on the query and the
 // ring only, so it is taken here, before the scan, and the final combine
 // just adds it.  Also clears the kv head's arrival counter for the scan.
-template <int GW>
+// TO_GLOBAL: written to the workspace for the scan's fused finalize (and the
+// kv head's arrival counter cleared); else left in LDS: sMw, sLw, wacc.
+template <int GW, bool TO_GLOBAL>
 __device__ void window_partial(const DecodeArgs& a, const KParams& k, int b, int h, int g0, float (*qw)[kD],
-                               float (*ls)[kMaxWindow], float (*part)[GW][kD], float* sMw, float* sLw) {
+                               float (*ls)[kMaxWindow], float (*part)[GW][kD], float* sMw, float* sLw,
+                               float (*wacc)[kD]) {
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int c4 = (tid & 31) * 4, q8 = tid >> 5;
   const int T = a.seq_lens[b];
   const int nwin = T < k.W ? T : k.W;
   const int64_t bh = static_cast<int64_t>(b) * k.Hkv + h;
   const int64_t qr0 = static_cast<int64_t>(b) * k.Hq + static_cast<int64_t>(h) * k.G + g0;  // first query row
-  if (g0 == 0 && tid == 0) a.ctr[bh] = 0;
+  if (TO_GLOBAL && g0 == 0 && tid == 0) a.ctr[bh] = 0;
   const float c2 = a.sm_scale * kLog2e;
   // window keys: thread pair (tk, half) holds slot tk = tid / 2, coordinates
   // 64 half .. 64 half + 63 (past d: zero); rows hold d coordinates
@@ -302,18 +306,22 @@ __device__ void window_partial(const DecodeArgs& a, const KParams& k, int b, int
     float v = part[0][g][i];
 #pragma unroll
     for (int r = 1; r < 8; ++r) v += part[r][g][i];
-    a.wacc[(qr0 + g) * kD + i] = v;
+    if (TO_GLOBAL)
+      a.wacc[(qr0 + g) * kD + i] = v;
+    else
+      wacc[g][i] = v;
   }
-  if (tid < GW) {
+  if (TO_GLOBAL && tid < GW) {
     a.wm[qr0 + tid] = sMw[tid];
     a.wl[qr0 + tid] = sLw[tid];
   }
+  if (!TO_GLOBAL) lds_barrier();
 }
 
 // Work-groups 0 .. nrot-1 rotate the queries of (kv head h, query heads g0
-// .. g0+GW-1); work-groups nrot .. 2 nrot-1 take the FP16 window of the same
-// heads.  The two run side by side (each is a short chain of memory round
-// trips).
+// .. g0+GW-1); when the scan finalizes (a.fuse), work-groups nrot .. 2 nrot-1
+// take the FP16 window of the same heads.  The two run side by side (each is
+// a short chain of memory round trips).
 template <int GW>
 __global__ __launch_bounds__(kSmallThreads) void prep_kernel(DecodeArgs a, DevTables t, KParams k, int qjl) {
   __shared__ float qv[GW][kD], qr[GW][kD], part[8][GW][kD];
@@ -327,7 +335,7 @@ __global__ __launch_bounds__(kSmallThreads) void prep_kernel(DecodeArgs a, DevTa
   if (rot)
     rotate_queries<GW>(a, t, k, qjl, b, h, g0, qv, qr, part);
   else
-    window_partial<GW>(a, k, b, h, g0, qv, ls, part, sMw, sLw);
+    window_partial<GW, true>(a, k, b, h, g0, qv, ls, part, sMw, sLw, nullptr);
 }
 
 // ---------------------------------------------------------------- scan
@@ -519,15 +527,20 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(DecodeArgs a, DevTab
 }
 
 // ---------------------------------------------------------------- finalize
-// After the vector-ALU scan: one work-group per (b, kv head) combines the
-// split partials with the window's (the matrix-core scan does this in its
-// last work-group of each kv head).
-template <int G>
+// One work-group per (b, kv head, GW of its query heads) combines the split
+// partials with the window's: after the vector-ALU scan, and after the
+// matrix-core scan when it has more than kFuseMaxSplits splits.
+template <int GW>
 __global__ __launch_bounds__(kSmallThreads) void finalize_kernel(DecodeArgs a, DevTables t, KParams k) {
-  __shared__ float acc[G][kD];
-  __shared__ float fin[finalize_scratch_floats<kSmallThreads, G>()];
-  __shared__ float sM[G], sL[G], sW[G];
-  finalize_bh<kSmallThreads, G>(a, t, k, blockIdx.y, blockIdx.x, acc, fin, sM, sL, sW);
+  __shared__ float acc[GW][kD], qw[GW][kD], wacc[GW][kD], part[8][GW][kD];
+  __shared__ float ls[GW][kMaxWindow];
+  __shared__ float fin[finalize_scratch_floats<kSmallThreads, GW>()];
+  __shared__ float sL[GW], sW[GW], sMw[GW], sLw[GW];
+  const int nhs = k.G / GW;
+  const int h = blockIdx.x / nhs, g0 = (blockIdx.x % nhs) * GW, b = blockIdx.y;
+  // the FP16 window first (its partial stays in LDS), then the combine
+  window_partial<GW, false>(a, k, b, h, g0, qw, ls, part, sMw, sLw, wacc);
+  finalize_bh<kSmallThreads, GW>(a, t, k, b, h, g0, acc, fin, sL, sW, sMw, sLw, wacc);
 }
 
 template <int G, int BK, int BV>
@@ -616,11 +629,15 @@ int launch_decode(const tq_ctx* c, const DecodeArgs& a, void* stream) {
   // per work-group (GW) when that leaves fewer than kPrepGroups of each
   int GW = k.G < kPrepMaxHeads ? k.G : kPrepMaxHeads;
   while (GW > 1 && static_cast<long long>(a.batch) * k.Hkv * (k.G / GW) < kPrepGroups) GW /= 2;
-  const dim3 gp(2 * k.Hkv * (k.G / GW), a.batch);
+  const bool valu = (c->p.flags & TQ_FLAG_VALU_SCAN) != 0;
+  DecodeArgs as = a;
+  as.fuse = (!valu && a.splits <= kFuseMaxSplits) ? 1 : 0;
+  // (window work-groups only when the scan finalizes)
+  const dim3 gp((as.fuse ? 2 : 1) * k.Hkv * (k.G / GW), a.batch);
   switch (GW) {
-    case 1: hipLaunchKernelGGL(prep_kernel<1>, gp, dim3(kSmallThreads), 0, s, a, c->t, k, qjl); break;
-    case 2: hipLaunchKernelGGL(prep_kernel<2>, gp, dim3(kSmallThreads), 0, s, a, c->t, k, qjl); break;
-    case 4: hipLaunchKernelGGL(prep_kernel<4>, gp, dim3(kSmallThreads), 0, s, a, c->t, k, qjl); break;
+    case 1: hipLaunchKernelGGL(prep_kernel<1>, gp, dim3(kSmallThreads), 0, s, as, c->t, k, qjl); break;
+    case 2: hipLaunchKernelGGL(prep_kernel<2>, gp, dim3(kSmallThreads), 0, s, as, c->t, k, qjl); break;
+    case 4: hipLaunchKernelGGL(prep_kernel<4>, gp, dim3(kSmallThreads), 0, s, as, c->t, k, qjl); break;
     default: return 1;
   }
   if (hipGetLastError() != hipSuccess) return 1;
@@ -628,15 +645,15 @@ int launch_decode(const tq_ctx* c, const DecodeArgs& a, void* stream) {
   // (taken by the launch itself, so no marker is queued around the kernel)
   void* ev0 = profile_slot(c, 0);
   void* ev1 = ev0 ? profile_slot(c, 1) : nullptr;
-  if (!(c->p.flags & TQ_FLAG_VALU_SCAN))  // the matrix-core scan finalizes in its last work-group per kv head
-    return launch_scan_mfma(c, a, k, stream, ev0, ev1) == 0 ? 0 : 1;
-  if (launch_scan_valu(c, a, k, s, ev0, ev1) != 0) return 1;
-  const dim3 gf(k.Hkv, a.batch);
-  switch (k.G) {
-    case 1: hipLaunchKernelGGL(finalize_kernel<1>, gf, dim3(kSmallThreads), 0, s, a, c->t, k); break;
-    case 2: hipLaunchKernelGGL(finalize_kernel<2>, gf, dim3(kSmallThreads), 0, s, a, c->t, k); break;
-    case 4: hipLaunchKernelGGL(finalize_kernel<4>, gf, dim3(kSmallThreads), 0, s, a, c->t, k); break;
-    case 8: hipLaunchKernelGGL(finalize_kernel<8>, gf, dim3(kSmallThreads), 0, s, a, c->t, k); break;
+  const int rc = valu ? launch_scan_valu(c, as, k, s, ev0, ev1) : launch_scan_mfma(c, as, k, stream, ev0, ev1);
+  if (rc != 0) return 1;
+  if (as.fuse) return 0;
+  // the same heads per work-group as prep
+  const dim3 gf(k.Hkv * (k.G / GW), a.batch);
+  switch (GW) {
+    case 1: hipLaunchKernelGGL(finalize_kernel<1>, gf, dim3(kSmallThreads), 0, s, as, c->t, k); break;
+    case 2: hipLaunchKernelGGL(finalize_kernel<2>, gf, dim3(kSmallThreads), 0, s, as, c->t, k); break;
+    case 4: hipLaunchKernelGGL(finalize_kernel<4>, gf, dim3(kSmallThreads), 0, s, as, c->t, k); break;
     default: return 1;
   }
   return hipGetLastError() == hipSuccess ? 0 : 1;

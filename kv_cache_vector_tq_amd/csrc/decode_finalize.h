@@ -16,9 +16,15 @@
 
 namespace tq {
 
-// LDS floats the finalize needs besides acc[G][kD]: NT * max(G, 4).
-template <int NT, int G>
-constexpr int finalize_scratch_floats() { return NT * (G > 4 ? G : 4); }
+// LDS floats the finalize needs besides acc[GW][kD]: NT * max(GW, 4) for the
+// partial sums, and the per-group maxima and normalisers.
+template <int NT, int GW>
+constexpr int finalize_scratch_floats() { return NT * (GW > 4 ? GW : 4) + 2 * NT; }
+
+// Splits up to which the matrix-core scan's last work-group of a kv head
+// finalizes it; with more (long contexts, few sequences) a finalize kernel
+// spreads the heads over more work-groups.
+constexpr int kFuseMaxSplits = 4;
 
 // Called after this work-group's partial is in global memory; every thread
 // calls it.  Returns true in the work-group that arrives last among the
@@ -39,18 +45,24 @@ __device__ inline bool arrive_last(int* ctr, int splits, int* flag) {
   return *flag != 0;
 }
 
-template <int NT, int G>
-__device__ void finalize_bh(const DecodeArgs& a, const DevTables& t, const KParams& k, int b, int h,
-                            float (*acc)[kD], float* fin, float* sM, float* sL, float* sW) {
-  (void)sM;
+// Combines query heads g0 .. g0+GW-1 of kv head h of sequence b (GW of the
+// group's k.G heads; acc: LDS [GW][kD]; fin: LDS, finalize_scratch_floats;
+// sL, sW: LDS [GW]).  The window's partial comes from global memory (prep
+// wrote it), or with lw_m non-null from LDS (lw_m, lw_l [GW], lw_acc
+// [GW][kD]: the finalize kernel took the window itself).  Every load of a
+// step is issued before any is used: empty splits hold zero accumulators
+// and get factor 0, so they are read like the others.
+template <int NT, int GW>
+__device__ void finalize_bh(const DecodeArgs& a, const DevTables& t, const KParams& k, int b, int h, int g0,
+                            float (*acc)[kD], float* fin, float* sL, float* sW, const float* lw_m = nullptr,
+                            const float* lw_l = nullptr, const float (*lw_acc)[kD] = nullptr) {
   const int tid = threadIdx.x;
   const int64_t bh = static_cast<int64_t>(b) * k.Hkv + h;
-  const int64_t q0 = static_cast<int64_t>(b) * k.Hq + static_cast<int64_t>(h) * G;  // first query row
-  const int S = a.splits;
+  const int64_t q0 = static_cast<int64_t>(b) * k.Hq + static_cast<int64_t>(h) * k.G + g0;  // first query row
+  const int S = a.splits, G = k.G;
   const bool dense = k.rotation == TQ_ROT_DENSE;
-  // Global loads go out together, before any of them is used: this runs
-  // after the arrival's cache invalidation, so each round trip is a full
-  // memory latency.
+  auto win_m = [&](int g) { return lw_m ? lw_m[g] : a.wm[q0 + g]; };
+  auto win_l = [&](int g) { return lw_l ? lw_l[g] : a.wl[q0 + g]; };
   // (a) this thread's slice of a row of Pi^T (dense): thread (j, part)
   constexpr int P = NT / kD;
   constexpr int kSlice = kD / P;
@@ -62,81 +74,89 @@ __device__ void finalize_bh(const DecodeArgs& a, const DevTables& t, const KPara
     for (int i4 = 0; i4 < kSlice / 4; ++i4) rrow[i4] = row[i4];
   }
   // (b) the window accumulator elements this thread finishes in step 3
-  constexpr int kOut = (G * kD + NT - 1) / NT;
+  constexpr int kOut = (GW * kD + NT - 1) / NT;
   float wa[kOut];
 #pragma unroll
   for (int r = 0; r < kOut; ++r) {
     const int e = tid + r * NT;
-    wa[r] = e < G * kD ? a.wacc[(q0 + e / kD) * kD + e % kD] : 0.0f;
+    const int g = e / kD, i = e % kD;
+    wa[r] = e >= GW * kD ? 0.0f : lw_acc ? lw_acc[g][i] : a.wacc[(q0 + g) * kD + i];
   }
-  // (c) combine item: query g, coordinates c4 .. c4+3, splits grp, grp + NG, ...
-  constexpr int kItems = G * (kD / 4);
+  // 1. thread (item = query g, coordinates c4 .. c4+3; group grp) merges
+  //    splits grp, grp + NG, ... online (running maximum m, rescaled sums);
+  //    the groups are merged in order below
+  constexpr int kItems = GW * (kD / 4);
   constexpr int NG = NT / kItems > 0 ? NT / kItems : 1;
   constexpr int kRounds = (kItems * NG + NT - 1) / NT;
-  // 1. per query: M over the non-empty partials, the window factor, L;
-  //    every thread takes its queries' values from all splits itself
-  float4 v[kRounds];
+  float* gm = fin + NG * GW * kD;  // [NG][GW] group maxima
+  float* gl = gm + NG * GW;        // [NG][GW] group sums of l
 #pragma unroll
   for (int r = 0; r < kRounds; ++r) {
     const int e = tid + r * NT;
-    v[r] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
     if (e >= kItems * NG) continue;
     const int item = e % kItems, grp = e / kItems;
     const int g = item / (kD / 4), c4 = 4 * (item % (kD / 4));
-    const float wl = a.wl[q0 + g], wmv = a.wm[q0 + g];
-    float M = wl > 0.0f ? wmv : -INFINITY;
+    float m = -INFINITY, L = 0.0f;
+    float4 v = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
 #pragma unroll 8
-    for (int s2 = 0; s2 < S; ++s2) {
-      const int64_t pi = (bh * S + s2) * G + g;
-      const float ls = a.pl[pi], ms = a.pm[pi];
-      if (ls > 0.0f) M = fmaxf(M, ms);
-    }
-    float L = 0.0f;
-#pragma unroll 4
     for (int s2 = grp; s2 < S; s2 += NG) {
-      const int64_t pi = (bh * S + s2) * G + g;
-      const float ls = a.pl[pi];
-      if (ls > 0.0f) {
-        const float f = exp2f(a.pm[pi] - M);
-        const float4 pa = *reinterpret_cast<const float4*>(a.pacc + pi * kD + c4);
-        v[r].x = fmaf(f, pa.x, v[r].x);
-        v[r].y = fmaf(f, pa.y, v[r].y);
-        v[r].z = fmaf(f, pa.z, v[r].z);
-        v[r].w = fmaf(f, pa.w, v[r].w);
-      }
+      const int64_t pi = (bh * S + s2) * G + g0 + g;
+      const float ls = a.pl[pi], ms = a.pm[pi];
+      const float4 pa = *reinterpret_cast<const float4*>(a.pacc + pi * kD + c4);
+      const bool ok = ls > 0.0f;
+      const float mn = ok ? fmaxf(m, ms) : m;
+      const float cf = m == mn ? 1.0f : exp2f(m - mn);
+      const float f = ok ? exp2f(ms - mn) : 0.0f;
+      v.x = fmaf(f, pa.x, v.x * cf);
+      v.y = fmaf(f, pa.y, v.y * cf);
+      v.z = fmaf(f, pa.z, v.z * cf);
+      v.w = fmaf(f, pa.w, v.w * cf);
+      L = fmaf(f, ls, L * cf);
+      m = mn;
     }
-    if (grp == 0 && c4 == 0) {
-      for (int s2 = 0; s2 < S; ++s2) {
-        const int64_t pi = (bh * S + s2) * G + g;
-        const float ls = a.pl[pi];
-        if (ls > 0.0f) L += exp2f(a.pm[pi] - M) * ls;
-      }
-      const float fw = wl > 0.0f ? exp2f(wmv - M) : 0.0f;
-      sW[g] = fw;
-      sL[g] = fmaf(fw, wl, L);
+    *reinterpret_cast<float4*>(fin + (grp * GW + g) * kD + c4) = v;
+    if (c4 == 0) {
+      gm[grp * GW + g] = m;
+      gl[grp * GW + g] = L;
     }
-    *reinterpret_cast<float4*>(fin + (grp * G + g) * kD + c4) = v[r];
   }
   __syncthreads();
-  for (int e = tid; e < G * kD; e += NT) {
+  // per query: M over the groups and the window, the factors, L
+  if (tid < GW) {
+    const float wl = win_l(tid), wmv = win_m(tid);
+    float M = wl > 0.0f ? wmv : -INFINITY;
+    for (int r = 0; r < NG; ++r) M = fmaxf(M, gm[r * GW + tid]);
+    float L = 0.0f;
+    for (int r = 0; r < NG; ++r) {
+      const float mr = gm[r * GW + tid];
+      const float f = mr == -INFINITY ? 0.0f : exp2f(mr - M);
+      gm[r * GW + tid] = f;  // the group's factor from here on
+      L = fmaf(f, gl[r * GW + tid], L);
+    }
+    const float fw = wl > 0.0f ? exp2f(wmv - M) : 0.0f;
+    sW[tid] = fw;
+    sL[tid] = fmaf(fw, wl, L);
+  }
+  __syncthreads();
+  for (int e = tid; e < GW * kD; e += NT) {
     const int g = e / kD, i = e % kD;
-    float x = fin[g * kD + i];
-    for (int r = 1; r < NG; ++r) x += fin[(r * G + g) * kD + i];
+    float x = 0.0f;
+    for (int r = 0; r < NG; ++r) x = fmaf(gm[r * GW + g], fin[(r * GW + g) * kD + i], x);
     acc[g][i] = x;
   }
   __syncthreads();
   // 2. back to the original basis
   if (dense) {
     // o[g][j] = sum_i Pi[i][j] acc[g][i] = sum_i PiT[j][i] acc[g][i]
-    float o[G];
+    float o[GW];
 #pragma unroll
-    for (int g = 0; g < G; ++g) o[g] = 0.0f;
+    for (int g = 0; g < GW; ++g) o[g] = 0.0f;
 #pragma unroll
     for (int i4 = 0; i4 < kSlice / 4; ++i4) {
       const float4 r = rrow[i4];
       const int i = p * kSlice + 4 * i4;
 #pragma unroll
-      for (int g = 0; g < G; ++g) {
+      for (int g = 0; g < GW; ++g) {
         o[g] = fmaf(r.x, acc[g][i], o[g]);
         o[g] = fmaf(r.y, acc[g][i + 1], o[g]);
         o[g] = fmaf(r.z, acc[g][i + 2], o[g]);
@@ -144,19 +164,19 @@ __device__ void finalize_bh(const DecodeArgs& a, const DevTables& t, const KPara
       }
     }
 #pragma unroll
-    for (int g = 0; g < G; ++g) fin[(p * G + g) * kD + j] = o[g];
+    for (int g = 0; g < GW; ++g) fin[(p * GW + g) * kD + j] = o[g];
     __syncthreads();
-    for (int e = tid; e < G * kD; e += NT) {
+    for (int e = tid; e < GW * kD; e += NT) {
       const int g = e / kD, jj = e % kD;
       float x = fin[g * kD + jj];
-      for (int r = 1; r < P; ++r) x += fin[(r * G + g) * kD + jj];
+      for (int r = 1; r < P; ++r) x += fin[(r * GW + g) * kD + jj];
       acc[g][jj] = x;
     }
     __syncthreads();
   } else {
     // x = eps . H y / sqrt(kD): butterflies at strides 1 .. 64 in LDS
     for (int hs = 1; hs < kD; hs <<= 1) {
-      for (int e = tid; e < G * (kD / 2); e += NT) {
+      for (int e = tid; e < GW * (kD / 2); e += NT) {
         const int g = e / (kD / 2), r = e % (kD / 2);
         const int i0 = (r / hs) * 2 * hs + r % hs, i1 = i0 + hs;
         const float x0 = acc[g][i0], x1 = acc[g][i1];
@@ -165,7 +185,7 @@ __device__ void finalize_bh(const DecodeArgs& a, const DevTables& t, const KPara
       }
       __syncthreads();
     }
-    for (int e = tid; e < G * kD; e += NT) {
+    for (int e = tid; e < GW * kD; e += NT) {
       const int g = e / kD, i = e % kD;
       acc[g][i] *= t.rot[i] * 0.08838834764831845f;  // 1/sqrt(128)
     }
@@ -176,7 +196,7 @@ __device__ void finalize_bh(const DecodeArgs& a, const DevTables& t, const KPara
   for (int r = 0; r < kOut; ++r) {
     const int e = tid + r * NT;
     const int g = e / kD, jj = e % kD;
-    if (e >= G * kD || jj >= k.d) continue;
+    if (e >= GW * kD || jj >= k.d) continue;
     const float L = sL[g];
     const float x = fmaf(sW[g], wa[r], acc[g][jj]);
     a.out[(q0 + g) * k.d + jj] = L > 0.0f ? x / L : 0.0f;

@@ -272,7 +272,7 @@ scan_mfma_kernel(DecodeArgs a, DevTables t, Codebooks cb, KParams k) {
   constexpr int kFin = finalize_scratch_floats<kThreads, G>();
   constexpr bool kFinInLuts = sizeof(luts) >= sizeof(float) * kFin;
   __shared__ __align__(16) float fin_own[kFinInLuts ? 1 : kFin];
-  __shared__ float fsm[3][G];
+  __shared__ float fsm[2][G];
   __shared__ int fflag;
   __shared__ int next_chunk;  // the split's next unclaimed chunk
 
@@ -322,9 +322,9 @@ scan_mfma_kernel(DecodeArgs a, DevTables t, Codebooks cb, KParams k) {
       a.pl[pidx + tid] = 0.0f;
     }
     for (int i = tid; i < G * kD; i += kThreads) a.pacc[pidx * kD + i] = 0.0f;
-    if (arrive_last<kThreads>(a.ctr + static_cast<int64_t>(b) * k.Hkv + h, a.splits, &fflag))
-      finalize_bh<kThreads, G>(a, t, k, b, h, red, kFinInLuts ? reinterpret_cast<float*>(luts) : fin_own, fsm[0],
-                               fsm[1], fsm[2]);
+    if (a.fuse && arrive_last<kThreads>(a.ctr + static_cast<int64_t>(b) * k.Hkv + h, a.splits, &fflag))
+      finalize_bh<kThreads, G>(a, t, k, b, h, 0, red, kFinInLuts ? reinterpret_cast<float*>(luts) : fin_own, fsm[0],
+                               fsm[1]);
     return;
   }
   // codebooks to LDS (no dynamic indexing of kernel arguments), then the tables
@@ -763,11 +763,12 @@ scan_mfma_kernel(DecodeArgs a, DevTables t, Codebooks cb, KParams k) {
     a.pm[pidx + tid] = M;
     a.pl[pidx + tid] = L;
   }
-  // the last work-group of this kv head to finish combines every split's
-  // partial with the window's and writes the output rows
-  if (arrive_last<kThreads>(a.ctr + static_cast<int64_t>(b) * k.Hkv + h, a.splits, &fflag))
-    finalize_bh<kThreads, G>(a, t, k, b, h, red, kFinInLuts ? reinterpret_cast<float*>(luts) : fin_own, fsm[0],
-                             fsm[1], fsm[2]);
+  // with few splits (a.fuse) the last work-group of this kv head to finish
+  // combines every split's partial with the window's and writes the output
+  // rows; otherwise the finalize kernel does
+  if (a.fuse && arrive_last<kThreads>(a.ctr + static_cast<int64_t>(b) * k.Hkv + h, a.splits, &fflag))
+    finalize_bh<kThreads, G>(a, t, k, b, h, 0, red, kFinInLuts ? reinterpret_cast<float*>(luts) : fin_own, fsm[0],
+                             fsm[1]);
 }
 
 template <int G, int BK, int BV, bool KMIX, bool VMIX>

@@ -170,6 +170,7 @@ struct DecodeArgs {
   int64_t logits_stride;
   int pages_per_split;
   int splits;
+  int fuse;       // the matrix-core scan's last work-group per kv head finalizes it
   // workspace carve-up
   // (rows of D coordinates; q and out rows hold d)
   float* qs;      // [B][Hq][D] rotated query * sm_scale * log2(e)
