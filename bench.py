@@ -11,7 +11,9 @@ decodes at exactly T = 32768.  Inputs are seeded synthetic data with the key
 recipe of tq_inputs (heavy-tailed channels, RoPE) drawn on the GPU.
 
 The JSON line carries, besides the step rate:
-  roofline      the scan kernel (the one that streams the packed cache):
+  roofline      the scan kernel (the one that streams the packed cache; with
+                at most 4 page splits per KV head its last work-group of a
+                head also combines the splits, so the tail is included):
                 algorithmic bytes per launch / its duration.  The duration
                 comes from HIP events the library records on the launch
                 stream around each scan launch, over a replay of the timed
@@ -20,7 +22,7 @@ The JSON line carries, besides the step rate:
                 each event adds its own latency, so this fraction is a
                 conservative one;
   decode_call   back-to-back tq_decode_attn calls at the final length
-                between HIP events: prep + scan + merge per call, against the
+                between HIP events: prep + scan + finalize per call, against the
                 bytes one call must read (pages and FP16 window);
   prefill       the first cache's bulk tq_append_page (HIP events);
   read_ceiling  the device's streaming-read rate (tq_read_probe, 1 GiB);
@@ -136,7 +138,7 @@ def cpu_baseline(T, W, P, G, Hkv, B, min_seconds, kbits=3, vbits=4, kmix=0, vmix
                       f"(seconds x {Hkv} KV heads)"}
 
 
-SCAN_SOURCES = ["decode_mfma.hip", "decode_common.h", "device_common.h", "tq_internal.h"]
+SCAN_SOURCES = ["decode_mfma.hip", "decode_finalize.h", "decode_common.h", "device_common.h", "tq_internal.h"]
 
 
 def scan_traffic():
@@ -353,7 +355,7 @@ def decode_workload(tqa, tq_inputs, wname, args, fmt_over=None):
     for c, f in zip(caches, final):
         assert torch.equal(c["seq_lens"], f), "the replay did not end at the timed region's lengths"
     # back-to-back decode calls at the final lengths (no appends): prep + scan
-    # + merge, between two events on the stream the calls are launched on
+    # (+ finalize), between two events on the stream the calls are launched on
     ncall = max(args.steps, 10)
     torch.cuda.synchronize()
     e2, e3 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -404,14 +406,16 @@ def decode_workload(tqa, tq_inputs, wname, args, fmt_over=None):
                           + len(step_caches(0)) * win_bytes) / (ms_step / 1e3) / 1e9,
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBPS, "traffic": None,
-                     "kernel": "scan_kernel (VALU)" if fo.get("valu") else "scan_mfma_kernel",
+                     "kernel": "scan_kernel (VALU)" if fo.get("valu") else (
+                         "scan_mfma_kernel (its last work-group per KV head also combines the splits and the "
+                         "window when there are at most 4 splits)"),
                      "algorithmic_bytes_per_launch": sum(prof_bytes) / len(prof_bytes),
                      "launch_us": scan_s * 1e6,
                      "launches": f"{ncalls} scan launches by HIP events, a replay of the timed steps "
                                  f"(longest context {lo_T}..{hi_T})"},
         "decode_call": {"us": el_call * 1e6, "bytes": call_bytes,
                         "gbps": call_bytes / el_call / 1e9, "frac": call_bytes / el_call / 1e9 / HBM_PEAK_GBPS,
-                        "what": f"tq_decode_attn (prep + scan + merge) at longest context {hi_T}, mean of "
+                        "what": f"tq_decode_attn (prep + scan + finalize) at longest context {hi_T}, mean of "
                                 f"{ncall} back-to-back calls between HIP events; bytes = packed pages + FP16 window"},
     }
     res["prefill"] = prefill
