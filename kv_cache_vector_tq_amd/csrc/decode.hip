@@ -318,6 +318,129 @@ __device__ void window_partial(const DecodeArgs& a, const KParams& k, int b, int
   if (!TO_GLOBAL) lds_barrier();
 }
 
+// ---------------------------------------------------------------- plan
+// Balanced splits for the matrix-core scan (automatic split size).  The kv
+// heads of a sequence with n chunks of 32 compressed tokens get
+// max(1, ceil(n / U)) splits of U chunks each, U a whole number of pages and
+// at most kMaxSplitPages pages: the smallest such U whose splits fit the
+// work-groups resident at once (a.slots), else the largest.  A ragged batch
+// then gives every scan work-group about the same number of chunks, where a
+// split size fixed by the longest sequence leaves the short sequences'
+// work-groups mostly idle; a batch of equal lengths gets the splits of the
+// fixed rule.  Plan entry j (scan work-group j, partial slot j) names the kv
+// head, the split, the kv head's split count and the pages per split; kv
+// head bh's entries start at sbase[bh], in split order, and sbase[B * Hkv]
+// counts the entries in use.  Run by one work-group of kSmallThreads threads.
+constexpr int kPlanStage = 2048;  // chunk counts kept in LDS (later sequences: read again)
+
+__device__ void make_plan(const DecodeArgs& a, const KParams& k) {
+  __shared__ int nch_s[kPlanStage];
+  __shared__ long long red_s[kSmallThreads / 64];
+  __shared__ int scan_s[kSmallThreads / 64];
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int B = a.batch, Hkv = k.Hkv, cpp = k.P / 32;
+  // chunks of sequence b, at most the block table's pages (the scan stops there too)
+  auto nch_of = [&](int b) {
+    const int T = a.seq_lens[b];
+    const long long C = T - k.W > 0 ? T - k.W : 0;
+    const long long n = (C + 31) / 32, cap = static_cast<long long>(a.max_pages) * cpp;
+    return static_cast<int>(n < cap ? n : cap);
+  };
+  for (int b = tid; b < B && b < kPlanStage; b += kSmallThreads) nch_s[b] = nch_of(b);
+  __syncthreads();
+  auto nch = [&](int b) { return b < kPlanStage ? nch_s[b] : nch_of(b); };
+  auto block_sum = [&](long long v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+    if (lane == 0) red_s[wv] = v;
+    __syncthreads();
+    long long t = 0;
+#pragma unroll
+    for (int w = 0; w < kSmallThreads / 64; ++w) t += red_s[w];
+    __syncthreads();
+    return t;
+  };
+  // splits at U chunks per split, all kv heads
+  auto count = [&](int U) {
+    long long c = 0;
+    for (int b = tid; b < B; b += kSmallThreads) {
+      const int n = nch(b);
+      c += n > U ? (n + U - 1) / U : 1;
+    }
+    return block_sum(c) * Hkv;
+  };
+  long long N = 0;
+  for (int b = tid; b < B; b += kSmallThreads) N += nch(b);
+  N = block_sum(N) * Hkv;
+  const long long S = a.slots;
+  const int hi = kMaxSplitPages * cpp;
+  long long lo0 = (N + S - 1) / S;
+  lo0 = (lo0 + cpp - 1) / cpp * cpp;
+  const int lo = static_cast<int>(lo0 < cpp ? cpp : lo0 > hi ? hi : lo0);
+  int U = hi;
+  if (count(lo) <= S) {
+    U = lo;
+  } else if (count(hi) <= S) {
+    // count(lp * cpp) > S >= count(hp * cpp): bisect in whole pages
+    int lp = lo / cpp, hp = hi / cpp;
+    while (hp - lp > 1) {
+      const int mp = (lp + hp) / 2;
+      if (count(mp * cpp) <= S) hp = mp;
+      else lp = mp;
+    }
+    U = hp * cpp;
+  }
+  // entries, kSmallThreads sequences per round: each thread finds its
+  // sequence's first entry (a prefix sum of the split counts), then the
+  // round's entries are written by all threads, each locating its sequence
+  // by bisection over the round's first entries
+  __shared__ int first_s[kSmallThreads], sp_s[kSmallThreads];
+  int carry = 0;
+  for (int b0 = 0; b0 < B; b0 += kSmallThreads) {
+    const int b = b0 + tid;
+    const int n = b < B ? nch(b) : 0;
+    const int sp = b < B ? (n > U ? (n + U - 1) / U : 1) : 0;
+    int x = sp;  // inclusive prefix within the wave
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int y = __shfl_up(x, o, 64);
+      if (lane >= o) x += y;
+    }
+    if (lane == 63) scan_s[wv] = x;
+    __syncthreads();
+    int before = 0, round = 0;
+#pragma unroll
+    for (int w = 0; w < kSmallThreads / 64; ++w) {
+      before += w < wv ? scan_s[w] : 0;
+      round += scan_s[w];
+    }
+    const int first = Hkv * (carry + before + x - sp);  // entries of the earlier sequences
+    first_s[tid] = first;
+    sp_s[tid] = sp;
+    if (b < B)
+      for (int h = 0; h < Hkv; ++h) a.sbase[b * Hkv + h] = first + h * sp;
+    __syncthreads();
+    const int nb = B - b0 < kSmallThreads ? B - b0 : kSmallThreads;  // sequences in this round (each >= 1 split)
+    const int e1 = Hkv * (carry + round);
+    for (int j = Hkv * carry + tid; j < e1 && j < a.nwg; j += kSmallThreads) {
+      int lo2 = 0, hi2 = nb - 1;  // last sequence i of the round with first_s[i] <= j
+      while (lo2 < hi2) {
+        const int mid = (lo2 + hi2 + 1) / 2;
+        if (first_s[mid] <= j) lo2 = mid;
+        else hi2 = mid - 1;
+      }
+      const int off = j - first_s[lo2], spi = sp_s[lo2];
+      const int hh = off / spi;
+      a.plan[j] = make_int4((b0 + lo2) * Hkv + hh, off - hh * spi, spi, U / cpp);
+    }
+    carry += round;
+    __syncthreads();
+  }
+  const int total = Hkv * carry;
+  if (tid == 0) a.sbase[B * Hkv] = total;
+  for (int j = total + tid; j < a.nwg; j += kSmallThreads) a.plan[j] = make_int4(-1, 0, 0, 0);
+}
+
 // Work-groups 0 .. nrot-1 rotate the queries of (kv head h, query heads g0
 // .. g0+GW-1); when the scan finalizes (a.fuse), work-groups nrot .. 2 nrot-1
 // take the FP16 window of the same heads.  The two run side by side (each is
@@ -327,6 +450,10 @@ __global__ __launch_bounds__(kSmallThreads) void prep_kernel(DecodeArgs a, DevTa
   __shared__ float qv[GW][kD], qr[GW][kD], part[8][GW][kD];
   __shared__ float ls[GW][kMaxWindow];
   __shared__ float sMw[GW], sLw[GW];
+  if (a.plan && blockIdx.x == gridDim.x - 1) {  // the balanced split plan (one work-group)
+    if (blockIdx.y == 0) make_plan(a, k);
+    return;
+  }
   const int nhs = k.G / GW;
   const int nrot = k.Hkv * nhs;
   const bool rot = static_cast<int>(blockIdx.x) < nrot;
@@ -631,9 +758,12 @@ int launch_decode(const tq_ctx* c, const DecodeArgs& a, void* stream) {
   while (GW > 1 && static_cast<long long>(a.batch) * k.Hkv * (k.G / GW) < kPrepGroups) GW /= 2;
   const bool valu = (c->p.flags & TQ_FLAG_VALU_SCAN) != 0;
   DecodeArgs as = a;
-  as.fuse = (!valu && a.splits <= kFuseMaxSplits) ? 1 : 0;
-  // (window work-groups only when the scan finalizes)
-  const dim3 gp((as.fuse ? 2 : 1) * k.Hkv * (k.G / GW), a.batch);
+  // with balanced splits the fused finalize is taken for G <= 4 (the split
+  // count per kv head is only known on the device); G = 8 keeps the
+  // finalize kernel, whose work-groups take the FP16 window themselves
+  as.fuse = valu ? 0 : a.plan ? (k.G <= 4 ? 1 : 0) : (a.splits <= kFuseMaxSplits ? 1 : 0);
+  // (window work-groups only when the scan finalizes; one more for the plan)
+  const dim3 gp((as.fuse ? 2 : 1) * k.Hkv * (k.G / GW) + (a.plan ? 1 : 0), a.batch);
   switch (GW) {
     case 1: hipLaunchKernelGGL(prep_kernel<1>, gp, dim3(kSmallThreads), 0, s, as, c->t, k, qjl); break;
     case 2: hipLaunchKernelGGL(prep_kernel<2>, gp, dim3(kSmallThreads), 0, s, as, c->t, k, qjl); break;

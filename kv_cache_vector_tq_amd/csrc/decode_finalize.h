@@ -59,16 +59,19 @@ __device__ void finalize_bh(const DecodeArgs& a, const DevTables& t, const KPara
   const int tid = threadIdx.x;
   const int64_t bh = static_cast<int64_t>(b) * k.Hkv + h;
   const int64_t q0 = static_cast<int64_t>(b) * k.Hq + static_cast<int64_t>(h) * k.G + g0;  // first query row
-  const int S = a.splits, G = k.G;
+  // this kv head's partial slots: base .. base + S - 1, in split order
+  const int S = a.sbase ? a.sbase[bh + 1] - a.sbase[bh] : a.splits, G = k.G;
+  const int64_t base = a.sbase ? a.sbase[bh] : bh * a.splits;
   const bool dense = k.rotation == TQ_ROT_DENSE;
   auto win_m = [&](int g) { return lw_m ? lw_m[g] : a.wm[q0 + g]; };
   auto win_l = [&](int g) { return lw_l ? lw_l[g] : a.wl[q0 + g]; };
-  // (a) this thread's slice of a row of Pi^T (dense): thread (j, part)
-  constexpr int P = NT / kD;
+  // (a) this thread's slice of a row of Pi^T (dense): thread (j, part p),
+  //     P parts (a power of two; threads past P * kD take no part)
+  constexpr int P = (NT / kD) >= 8 ? 8 : (NT / kD) >= 4 ? 4 : (NT / kD) >= 2 ? 2 : 1;
   constexpr int kSlice = kD / P;
   const int j = tid % kD, p = tid / kD;
   float4 rrow[kSlice / 4];
-  if (dense) {
+  if (dense && p < P) {
     const float4* row = reinterpret_cast<const float4*>(t.rotT + j * kD + p * kSlice);
 #pragma unroll
     for (int i4 = 0; i4 < kSlice / 4; ++i4) rrow[i4] = row[i4];
@@ -100,7 +103,7 @@ __device__ void finalize_bh(const DecodeArgs& a, const DevTables& t, const KPara
     float4 v = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
 #pragma unroll 8
     for (int s2 = grp; s2 < S; s2 += NG) {
-      const int64_t pi = (bh * S + s2) * G + g0 + g;
+      const int64_t pi = (base + s2) * G + g0 + g;
       const float ls = a.pl[pi], ms = a.pm[pi];
       const float4 pa = *reinterpret_cast<const float4*>(a.pacc + pi * kD + c4);
       const bool ok = ls > 0.0f;
@@ -148,23 +151,25 @@ __device__ void finalize_bh(const DecodeArgs& a, const DevTables& t, const KPara
   // 2. back to the original basis
   if (dense) {
     // o[g][j] = sum_i Pi[i][j] acc[g][i] = sum_i PiT[j][i] acc[g][i]
-    float o[GW];
+    if (p < P) {
+      float o[GW];
 #pragma unroll
-    for (int g = 0; g < GW; ++g) o[g] = 0.0f;
+      for (int g = 0; g < GW; ++g) o[g] = 0.0f;
 #pragma unroll
-    for (int i4 = 0; i4 < kSlice / 4; ++i4) {
-      const float4 r = rrow[i4];
-      const int i = p * kSlice + 4 * i4;
+      for (int i4 = 0; i4 < kSlice / 4; ++i4) {
+        const float4 r = rrow[i4];
+        const int i = p * kSlice + 4 * i4;
 #pragma unroll
-      for (int g = 0; g < GW; ++g) {
-        o[g] = fmaf(r.x, acc[g][i], o[g]);
-        o[g] = fmaf(r.y, acc[g][i + 1], o[g]);
-        o[g] = fmaf(r.z, acc[g][i + 2], o[g]);
-        o[g] = fmaf(r.w, acc[g][i + 3], o[g]);
+        for (int g = 0; g < GW; ++g) {
+          o[g] = fmaf(r.x, acc[g][i], o[g]);
+          o[g] = fmaf(r.y, acc[g][i + 1], o[g]);
+          o[g] = fmaf(r.z, acc[g][i + 2], o[g]);
+          o[g] = fmaf(r.w, acc[g][i + 3], o[g]);
+        }
       }
-    }
 #pragma unroll
-    for (int g = 0; g < GW; ++g) fin[(p * GW + g) * kD + j] = o[g];
+      for (int g = 0; g < GW; ++g) fin[(p * GW + g) * kD + j] = o[g];
+    }
     __syncthreads();
     for (int e = tid; e < GW * kD; e += NT) {
       const int g = e / kD, jj = e % kD;

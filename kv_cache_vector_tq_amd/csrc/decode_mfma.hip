@@ -136,26 +136,34 @@ __device__ inline u4 dec_signs8(uint32_t x, const u2* lutN) {
   return u4{a.x, a.y, c.x, c.y};
 }
 
-// Work-group shape.  With 4-bit values (and at most four query heads per KV
-// head, for the LDS budget) one 64 KB "wide" table serves both the value
-// codes and the sign bits, addressed straight from a byte of the code word:
-// row e (256 bytes) holds the value pair e in 32 copies (words 64e + c, lane
-// reads copy lane % 32: a half-wave touches 32 distinct banks) and, in its
-// second half, the eight +-1 fp16 values of sign byte e in 8 copies of 16
-// bytes (lane reads copy lane % 8, one 16-byte read per 8 signs).  One v_perm
-// forms each address (byte e into bits 8..15, the lane's copy offset into
-// bits 0..7) where the narrow tables take a shift and a mask-or.  Sixteen
-// waves (a whole CU at four waves per SIMD) share one table and one chunk
-// counter: the waves of a CU finish together, where two eight-wave
-// work-groups per CU ended 15 us apart (the younger one's waves lose issue
-// arbitration to the older one's and then run on at half occupancy).
-constexpr bool wide_scan(int G, int BV, bool vmix) { return BV == 4 && G <= 4 && !vmix; }
-constexpr int scan_threads(bool wide) { return wide ? 1024 : 256; }
+// Work-group shape.  One work-group fills a CU (four SIMDs at the waves per
+// SIMD the register budget below allows: 16 or 12 waves); its waves share
+// the tables and one chunk counter, so the waves of a CU finish together
+// (two eight-wave work-groups per CU ended 15 us apart: the younger one's
+// waves lose issue arbitration to the older one's and then run on at half
+// occupancy).
+// With 4-bit values (and at most four query heads per KV head, for the LDS
+// budget) one 64 KB "wide" table serves both the value codes and the sign
+// bits, addressed straight from a byte of the code word: row e (256 bytes)
+// holds the value pair e in 32 copies (words 64e + c, lane reads copy
+// lane % 32: a half-wave touches 32 distinct banks) and, in its second half,
+// the eight +-1 fp16 values of sign byte e in 8 copies of 16 bytes (lane
+// reads copy lane % 8, one 16-byte read per 8 signs).  One v_perm forms each
+// address (byte e into bits 8..15, the lane's copy offset into bits 0..7)
+// where the narrow tables take a shift and a mask-or.
+// Register budget: 128 VGPRs (four waves per SIMD), except where that would
+// spill inside the loop: 3-bit values (two words per value slice) and mixed
+// rates (two tables per operand side) get 168 (three waves).  Measured at
+// B=16, T=32K with four-wave work-groups: keys 3 / values 3 166 -> 132 us,
+// keys 3.5 / values 3 201 -> 136 us.
+constexpr bool wide_table(int G, int BV, bool vmix) { return BV == 4 && G <= 4 && !vmix; }
+constexpr int scan_waves_per_simd(int BV, bool kmix, bool vmix) { return (BV == 3 || kmix || vmix) ? 3 : 4; }
+constexpr int scan_threads(int BV, bool kmix, bool vmix) { return 256 * scan_waves_per_simd(BV, kmix, vmix); }
 
-template <int G, int BV, bool VMIX = false>
+template <int G, int BV, bool KMIX, bool VMIX>
 struct ScanShape {
-  static constexpr bool kWide = wide_scan(G, BV, VMIX);
-  static constexpr int kThreads = scan_threads(kWide);
+  static constexpr bool kWide = wide_table(G, BV, VMIX);
+  static constexpr int kThreads = scan_threads(BV, KMIX, VMIX);
   static constexpr int kWaves = kThreads / 64;
   static constexpr int kLutWords = kWide ? 256 * 64 : PairLut<BV>::kWords;
 };
@@ -233,18 +241,10 @@ struct Meta {
 // piece (MFMAs i = 0, 1) and a high-rate piece (i = 2, 3); value MFMA bl
 // reads the low-rate word block for bl < 4 and the high-rate one otherwise,
 // so every operand slice has one compile-time width.
-// Register budget: 128 VGPRs (four waves per SIMD), except where that would
-// spill inside the loop: 3-bit values (two words per value slice), mixed
-// rates (two tables per operand side) and G = 8 (whose LDS already caps a CU
-// at three work-groups) get 168 (three waves).  Measured at B=16, T=32K:
-// keys 3 / values 3 166 -> 132 us, keys 3.5 / values 3 201 -> 136 us.
-template <int G, int BV, bool KMIX, bool VMIX>
-constexpr int scan_waves_per_simd() { return (BV == 3 || KMIX || VMIX || G == 8) ? 3 : 4; }
-
 template <int G, int BK, int BV, bool QJL, bool KMIX, bool VMIX, bool N8>
-__global__ __launch_bounds__((ScanShape<G, BV, VMIX>::kThreads), (scan_waves_per_simd<G, BV, KMIX, VMIX>())) void
+__global__ __launch_bounds__((ScanShape<G, BV, KMIX, VMIX>::kThreads), (scan_waves_per_simd(BV, KMIX, VMIX))) void
 scan_mfma_kernel(DecodeArgs a, DevTables t, Codebooks cb, KParams k) {
-  using Sh = ScanShape<G, BV, VMIX>;
+  using Sh = ScanShape<G, BV, KMIX, VMIX>;
   constexpr bool kWide = Sh::kWide;
   constexpr int kThreads = Sh::kThreads, kWaves = Sh::kWaves;
   // One array: the key table (absent when keys and values share a bit width,
@@ -267,16 +267,35 @@ scan_mfma_kernel(DecodeArgs a, DevTables t, Codebooks cb, KParams k) {
   __shared__ float wm[kWaves][G], wl[kWaves][G];
   __shared__ float red[G][kD];
   __shared__ float ck[16], cvv[16], ck2[16], cv2[16];
-  // the final combine (last work-group of the kv head): its scratch is the
-  // table memory when that is large enough
+  // scratch of the end phases: the waves' scaled accumulators (one slot of
+  // G x kD floats per wave), then the final combine (last work-group of the
+  // kv head); the table memory when that is large enough
   constexpr int kFin = finalize_scratch_floats<kThreads, G>();
-  constexpr bool kFinInLuts = sizeof(luts) >= sizeof(float) * kFin;
-  __shared__ __align__(16) float fin_own[kFinInLuts ? 1 : kFin];
+  constexpr int kEnd = kFin > kWaves * G * kD ? kFin : kWaves * G * kD;
+  constexpr bool kEndInLuts = sizeof(luts) >= sizeof(float) * kEnd;
+  __shared__ __align__(16) float end_own[kEndInLuts ? 1 : kEnd];
+  float* const endbuf = kEndInLuts ? reinterpret_cast<float*>(luts) : end_own;
   __shared__ float fsm[2][G];
   __shared__ int fflag;
   __shared__ int next_chunk;  // the split's next unclaimed chunk
+  __shared__ int page_ids[kMaxSplitPages];
 
-  const int tid = threadIdx.x, split = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const int tid = threadIdx.x;
+  // (b, kv head h, split): the grid position, or with balanced splits plan
+  // entry blockIdx.x (whose partial slot it is); idle entries leave at once
+  int split = blockIdx.x, h = blockIdx.y, b = blockIdx.z, pps = a.pages_per_split, nsplit = a.splits;
+  int64_t slot = (static_cast<int64_t>(b) * k.Hkv + h) * a.splits + split;
+  if (a.plan) {
+    const int4 e = a.plan[blockIdx.x];
+    const int bh = __builtin_amdgcn_readfirstlane(e.x);
+    if (bh < 0) return;
+    b = bh / k.Hkv;
+    h = bh - b * k.Hkv;
+    split = __builtin_amdgcn_readfirstlane(e.y);
+    nsplit = __builtin_amdgcn_readfirstlane(e.z);
+    pps = __builtin_amdgcn_readfirstlane(e.w);
+    slot = blockIdx.x;
+  }
   // the wave index is uniform within a wave; saying so keeps page addresses
   // and buffer descriptors in scalar registers
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -285,12 +304,10 @@ scan_mfma_kernel(DecodeArgs a, DevTables t, Codebooks cb, KParams k) {
   // that they land while the length is read and the tables are built: the
   // query operands (A operands of the key products: lane group kg covers
   // coordinates 32kg .. 32kg+31, MFMA i the 8 starting at 32kg + 8i) and the
-  // split's page ids (64 per register, lane j: page pb + j, read with
-  // v_readlane; no scalar load, whose out-of-order return would make every
-  // later LDS wait a full drain).
+  // split's page ids (vector loads: a scalar load's out-of-order return would
+  // make every later LDS wait a full drain).
   const int64_t qrow = (static_cast<int64_t>(b) * k.Hq + static_cast<int64_t>(h) * G) * kD;
   const int ag = 2 * (n >> 2) + (n & 1), apart = (n >> 1) & 1;
-  const uint32_t amask = apart ? 0xffffe000u : 0u;
   const int agc = ag < G ? ag : 0;
   float4 qin[4][2], pin[4][2];
 #pragma unroll
@@ -304,14 +321,19 @@ scan_mfma_kernel(DecodeArgs a, DevTables t, Codebooks cb, KParams k) {
       pin[i][1] = p4[1];
     }
   }
-  // the split's page ids (at most kMaxSplitPages = 64: lane j holds page pb + j)
-  const int pb = split * a.pages_per_split;
-  const int pids = a.block_table[static_cast<int64_t>(b) * a.max_pages + (pb + l < a.max_pages ? pb + l : 0)];
+  // the split's page ids (at most kMaxSplitPages), to LDS by the first
+  // threads: a chunk reads its page id from there (held in a register, it
+  // was spilled, and its reload at the top of every step waited for all
+  // loads in flight)
+  const int pb = split * pps;
+  int pid_in = 0;
+  if (tid < kMaxSplitPages)
+    pid_in = a.block_table[static_cast<int64_t>(b) * a.max_pages + (pb + tid < a.max_pages ? pb + tid : 0)];
   const int T = a.seq_lens[b];
   const int C = T - k.W > 0 ? T - k.W : 0;
   const int npages = (C + k.P - 1) / k.P;
-  int pe = npages < pb + a.pages_per_split ? npages : pb + a.pages_per_split;
-  const int64_t pidx = ((static_cast<int64_t>(b) * k.Hkv + h) * a.splits + split) * G;
+  int pe = npages < pb + pps ? npages : pb + pps;
+  const int64_t pidx = slot * G;
   if (pe > a.max_pages) {
     if (tid == 0) atomicOr(t.status, TQ_STATUS_BAD_PAGE);
     pe = a.max_pages;
@@ -322,13 +344,14 @@ scan_mfma_kernel(DecodeArgs a, DevTables t, Codebooks cb, KParams k) {
       a.pl[pidx + tid] = 0.0f;
     }
     for (int i = tid; i < G * kD; i += kThreads) a.pacc[pidx * kD + i] = 0.0f;
-    if (a.fuse && arrive_last<kThreads>(a.ctr + static_cast<int64_t>(b) * k.Hkv + h, a.splits, &fflag))
-      finalize_bh<kThreads, G>(a, t, k, b, h, 0, red, kFinInLuts ? reinterpret_cast<float*>(luts) : fin_own, fsm[0],
+    if (a.fuse && arrive_last<kThreads>(a.ctr + static_cast<int64_t>(b) * k.Hkv + h, nsplit, &fflag))
+      finalize_bh<kThreads, G>(a, t, k, b, h, 0, red, endbuf, fsm[0],
                                fsm[1]);
     return;
   }
   // codebooks to LDS (no dynamic indexing of kernel arguments), then the tables
   if (tid == 0) next_chunk = kWaves;  // wave w starts with chunk w
+  if (tid < kMaxSplitPages) page_ids[tid] = pid_in;
   if (tid < 16) {
     float kv = 0.0f, vv = 0.0f, kv2 = 0.0f, vv2 = 0.0f;
 #pragma unroll
@@ -445,7 +468,7 @@ scan_mfma_kernel(DecodeArgs a, DevTables t, Codebooks cb, KParams k) {
     m.s0 = m.gi * kChunk;
     const int rem = tot - tok0;
     m.pos0 = pg * k.P + m.s0;
-    const int pid0 = __builtin_amdgcn_readlane(pids, pg - pb);
+    const int pid0 = __builtin_amdgcn_readfirstlane(page_ids[pg - pb]);
     const bool bad = pid0 < 0 || pid0 >= a.num_pages;  // flagged, then page 0 is read and the chunk masked
     if (bad && l == 0) atomicOr(t.status, TQ_STATUS_BAD_PAGE);
     m.ntok = __builtin_amdgcn_readfirstlane(bad ? 0 : (rem < kChunk ? rem : kChunk));
@@ -615,7 +638,7 @@ scan_mfma_kernel(DecodeArgs a, DevTables t, Codebooks cb, KParams k) {
   };
   // ---- value product of one chunk with the weights in pv[slot]
   auto valuephase = [&](const VBuf<BV, VMIX>& d, int slot) {
-    // the lane's weight row (query ag, part amask, tokens 8kg ..), derived
+    // the lane's weight row (query ag, hi or remainder part, tokens 8kg ..), derived
     // afresh from the lane id each step: an opaque read of the id keeps these
     // values out of the registers held across the loop (a spill there would
     // make every step wait for all loads in flight)
@@ -711,12 +734,12 @@ scan_mfma_kernel(DecodeArgs a, DevTables t, Codebooks cb, KParams k) {
     for (int w = 0; w < kWaves; ++w) M = fmaxf(M, wm[w][g]);
     fac[i2] = (M == -INFINITY || wm[wave][g] == -INFINITY) ? 0.0f : exp2f(wm[wave][g] - M);
   }
-  constexpr bool kWaveSlots = sizeof(luts) >= sizeof(float) * kWaves * G * kD;
-  if constexpr (kWaveSlots) {
-    // every wave stores its scaled accumulators in a slot of its own (the
-    // tables are not read any more: all waves have passed the barrier above),
-    // then each element is summed over the waves in order 0 .. kWaves-1
-    float* slot = reinterpret_cast<float*>(luts);
+  {
+    // every wave stores its scaled accumulators in a slot of its own (when
+    // the slots are the table memory, the tables are not read any more: all
+    // waves have passed the barrier above), then each element is summed over
+    // the waves in order 0 .. kWaves-1
+    float* slot = endbuf;
 #pragma unroll
     for (int i2 = 0; i2 < 2; ++i2) {
       const int g = 2 * kg + i2;
@@ -733,24 +756,6 @@ scan_mfma_kernel(DecodeArgs a, DevTables t, Codebooks cb, KParams k) {
       for (int w = 1; w < kWaves; ++w) v += slot[w * G * kD + e];
       a.pacc[pidx * kD + e] = v;
     }
-  } else {
-    for (int w = 0; w < kWaves; ++w) {
-      if (wave == w) {
-#pragma unroll
-        for (int i2 = 0; i2 < 2; ++i2) {
-          const int g = 2 * kg + i2;
-          if (g < G) {
-#pragma unroll
-            for (int bl = 0; bl < 8; ++bl) {
-              const float v = (acc[bl][i2] + acc[bl][i2 + 2]) * fac[i2];
-              red[g][8 * n + bl] = (w == 0) ? v : red[g][8 * n + bl] + v;
-            }
-          }
-        }
-      }
-      __syncthreads();
-    }
-    for (int i2 = tid; i2 < G * kD; i2 += kThreads) a.pacc[pidx * kD + i2] = red[i2 / kD][i2 % kD];
   }
   if (tid < G) {
     float M = -INFINITY;
@@ -766,8 +771,8 @@ scan_mfma_kernel(DecodeArgs a, DevTables t, Codebooks cb, KParams k) {
   // with few splits (a.fuse) the last work-group of this kv head to finish
   // combines every split's partial with the window's and writes the output
   // rows; otherwise the finalize kernel does
-  if (a.fuse && arrive_last<kThreads>(a.ctr + static_cast<int64_t>(b) * k.Hkv + h, a.splits, &fflag))
-    finalize_bh<kThreads, G>(a, t, k, b, h, 0, red, kFinInLuts ? reinterpret_cast<float*>(luts) : fin_own, fsm[0],
+  if (a.fuse && arrive_last<kThreads>(a.ctr + static_cast<int64_t>(b) * k.Hkv + h, nsplit, &fflag))
+    finalize_bh<kThreads, G>(a, t, k, b, h, 0, red, endbuf, fsm[0],
                              fsm[1]);
 }
 
@@ -821,7 +826,7 @@ const void* scan_mfma_kernel_ptr(const tq_ctx* c) {
 }
 
 int scan_mfma_threads(const tq_ctx* c) {
-  return scan_threads(wide_scan(c->p.num_q_heads / c->p.num_kv_heads, c->p.value_bits, c->p.value_mixed != 0));
+  return scan_threads(c->p.value_bits, c->p.key_mixed != 0, c->p.value_mixed != 0);
 }
 
 int launch_scan_mfma(const tq_ctx* c, const DecodeArgs& a, const KParams& k, void* stream, void* ev0, void* ev1) {
@@ -832,7 +837,7 @@ int launch_scan_mfma(const tq_ctx* c, const DecodeArgs& a, const KParams& k, voi
   Codebooks cc = c->cb;
   KParams kk = k;
   void* args[] = {&aa, &tt, &cc, &kk};
-  const dim3 grid(a.splits, k.Hkv, a.batch);
+  const dim3 grid = a.plan ? dim3(a.nwg) : dim3(a.splits, k.Hkv, a.batch);
   return hipExtLaunchKernel(f, grid, dim3(scan_mfma_threads(c)), args, 0, static_cast<hipStream_t>(stream),
                             static_cast<hipEvent_t>(ev0), static_cast<hipEvent_t>(ev1), 0) == hipSuccess
              ? 0

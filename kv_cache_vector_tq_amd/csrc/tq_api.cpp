@@ -2,6 +2,7 @@
 // sizing and kernel launches.  See include/tq.h for the contract.
 #include <hip/hip_runtime_api.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstring>
 #include <limits>
@@ -85,14 +86,44 @@ int decode_splits(int batch, int hkv, int max_pages, int pages_per_split, int sl
 }
 
 struct WsLayout {
-  size_t qs, ps, psum, wm, wl, wacc, pm, pl, pacc, ctr, total;
+  size_t qs, ps, psum, wm, wl, wacc, pm, pl, pacc, ctr, plan, sbase, total;
 };
 
-WsLayout ws_layout(const tq_params& p, int batch, int splits) {
+// Splits of one tq_decode_attn call.  Automatic split size with the
+// matrix-core scan: balanced splits, planned on the device from the
+// sequence lengths (nwg work-groups, one partial slot each); otherwise a
+// fixed number of splits per kv head (nparts = batch * hkv * splits).
+struct SplitPlan {
+  bool balanced;
+  int pps, splits;  // fixed splits
+  int nwg;          // balanced: work-groups launched
+  size_t nparts;    // partial slots
+};
+
+SplitPlan split_plan(const tq_ctx* c, int batch, int max_pages, int pages_per_split) {
+  SplitPlan sp{};
+  const long long bh = static_cast<long long>(batch) * c->p.num_kv_heads;
+  sp.balanced = pages_per_split == 0 && max_pages > 0 && (c->p.flags & TQ_FLAG_VALU_SCAN) == 0;
+  sp.splits = decode_splits(batch, c->p.num_kv_heads, max_pages, pages_per_split, c->scan_slots, &sp.pps);
+  if (sp.balanced) {
+    // every kv head gets at least one split and a split at most
+    // kMaxSplitPages pages, so bh * ceil(max_pages / kMaxSplitPages) bounds the plan
+    const long long per = (max_pages + tq::kMaxSplitPages - 1) / tq::kMaxSplitPages;
+    const long long n = std::max<long long>(c->scan_slots > 0 ? c->scan_slots : 1, bh * std::max<long long>(per, 1));
+    sp.nwg = static_cast<int>(std::min<long long>(n, 1LL << 30));
+    sp.nparts = static_cast<size_t>(sp.nwg);
+  } else {
+    sp.nparts = static_cast<size_t>(bh) * sp.splits;
+  }
+  return sp;
+}
+
+WsLayout ws_layout(const tq_params& p, int batch, const SplitPlan& sp) {
   const int G = p.num_q_heads / p.num_kv_heads;
   const size_t d = tq::transform_dim(p.head_dim);  // workspace rows hold D coordinates
   const size_t bq = static_cast<size_t>(batch) * p.num_q_heads;
-  const size_t nb = static_cast<size_t>(batch) * p.num_kv_heads * splits * G;
+  const size_t nbh = static_cast<size_t>(batch) * p.num_kv_heads;
+  const size_t nb = sp.nparts * G;
   auto up = [](size_t x) { return (x + 255) / 256 * 256; };
   WsLayout w{};
   size_t off = 0;
@@ -105,7 +136,9 @@ WsLayout ws_layout(const tq_params& p, int batch, int splits) {
   w.pm = off; off += up(nb * 4);
   w.pl = off; off += up(nb * 4);
   w.pacc = off; off += up(nb * d * 4);
-  w.ctr = off; off += up(static_cast<size_t>(batch) * p.num_kv_heads * 4);
+  w.ctr = off; off += up(nbh * 4);
+  w.plan = off; off += sp.balanced ? up(static_cast<size_t>(sp.nwg) * 16) : 0;
+  w.sbase = off; off += sp.balanced ? up((nbh + 1) * 4) : 0;
   w.total = off;
   return w;
 }
@@ -476,8 +509,7 @@ TQ_API int tq_append_page(const tq_ctx* c, uint8_t* pool, int64_t num_pages, con
 
 TQ_API int64_t tq_decode_workspace_bytes(const tq_ctx* c, int batch, int max_pages, int pages_per_split) {
   if (!c || batch < 0 || max_pages < 0 || pages_per_split < 0) return TQ_ERR_INVALID_ARG;
-  const int splits = decode_splits(batch, c->p.num_kv_heads, max_pages, pages_per_split, c->scan_slots, nullptr);
-  return static_cast<int64_t>(ws_layout(c->p, batch, splits).total);
+  return static_cast<int64_t>(ws_layout(c->p, batch, split_plan(c, batch, max_pages, pages_per_split)).total);
 }
 
 TQ_API int tq_decode_attn(const tq_ctx* c, const void* q, int q_dtype, const uint8_t* pool, int64_t num_pages,
@@ -497,9 +529,8 @@ TQ_API int tq_decode_attn(const tq_ctx* c, const void* q, int q_dtype, const uin
   if ((pool && !aligned(pool, 256)) || !aligned(out, 16) || !aligned(workspace, 256) ||
       !aligned(q, q_dtype == TQ_DTYPE_F32 ? 16 : 8))
     return TQ_ERR_INVALID_ARG;
-  int pps = 1;
-  const int splits = decode_splits(batch, c->p.num_kv_heads, max_pages, pages_per_split, c->scan_slots, &pps);
-  const WsLayout w = ws_layout(c->p, batch, splits);
+  const SplitPlan sp = split_plan(c, batch, max_pages, pages_per_split);
+  const WsLayout w = ws_layout(c->p, batch, sp);
   if (workspace_bytes < w.total) return TQ_ERR_WORKSPACE;
   char* base = static_cast<char*>(workspace);
   tq::DecodeArgs a{};
@@ -517,8 +548,14 @@ TQ_API int tq_decode_attn(const tq_ctx* c, const void* q, int q_dtype, const uin
   a.out = out;
   a.dbg_logits = dbg_logits;
   a.logits_stride = logits_stride;
-  a.pages_per_split = pps;
-  a.splits = splits;
+  a.pages_per_split = sp.pps;
+  a.splits = sp.splits;
+  a.slots = c->scan_slots > 0 ? c->scan_slots : 1;
+  if (sp.balanced) {
+    a.nwg = sp.nwg;
+    a.plan = reinterpret_cast<int4*>(base + w.plan);
+    a.sbase = reinterpret_cast<int*>(base + w.sbase);
+  }
   a.qs = reinterpret_cast<float*>(base + w.qs);
   a.ps = reinterpret_cast<float*>(base + w.ps);
   a.psum = reinterpret_cast<float*>(base + w.psum);

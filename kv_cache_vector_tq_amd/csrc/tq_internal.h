@@ -169,8 +169,14 @@ struct DecodeArgs {
   float* dbg_logits;
   int64_t logits_stride;
   int pages_per_split;
-  int splits;
+  int splits;     // fixed splits per kv head (plan == nullptr)
   int fuse;       // the matrix-core scan's last work-group per kv head finalizes it
+  // balanced splits (matrix-core scan, automatic split size): prep sizes the
+  // splits from the sequence lengths; scan work-group j takes plan entry j
+  int4* plan;     // [nwg] {b * Hkv + h, split, splits of that kv head, pages per split}; b * Hkv + h < 0: idle
+  int* sbase;     // [B * Hkv + 1] first plan entry (= partial slot) of each kv head; last: entries in use
+  int nwg;        // scan work-groups launched (plan entries)
+  int slots;      // scan work-groups resident at once
   // workspace carve-up
   // (rows of D coordinates; q and out rows hold d)
   float* qs;      // [B][Hq][D] rotated query * sm_scale * log2(e)
@@ -179,9 +185,10 @@ struct DecodeArgs {
   float* wm;      // [B][Hq] FP16 window: max score (log2 units)
   float* wl;      // [B][Hq] FP16 window: sum of 2^(s - wm)
   float* wacc;    // [B][Hq][D] FP16 window: weighted values, original basis
-  float* pm;      // [B][Hkv][splits][G] running max (log2 units)
-  float* pl;      // [B][Hkv][splits][G] running sum
-  float* pacc;    // [B][Hkv][splits][G][D] rotated-basis accumulator
+  // split partials: slot (b * Hkv + h) * splits + split, or the plan entry
+  float* pm;      // [slots][G] running max (log2 units)
+  float* pl;      // [slots][G] running sum
+  float* pacc;    // [slots][G][D] rotated-basis accumulator
   int* ctr;       // [B][Hkv] scan work-groups finished (cleared by prep)
 };
 

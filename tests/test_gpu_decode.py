@@ -179,6 +179,29 @@ def test_ragged_batch_split_invariance():
     assert tqa.tq_get_status(ctx) == 0
 
 
+@pytest.mark.parametrize("Hq", [8, 16], ids=["G4_fused", "G8_finalize_kernel"])
+def test_balanced_splits_many_sequences(Hq):
+    """More sequences than one round of the split planner (270), ragged
+    lengths from empty to a few pages, some inside the window only: parity
+    with the oracle at the automatic (length-balanced) split, and with a
+    fixed split of 2 pages within 1e-5."""
+    print(f"case balanced splits many sequences Hq={Hq}", flush=True)
+    s = Setup(Hq=Hq, Hkv=2, W=16, P=32)
+    lens = [int(x) for x in np.random.default_rng(11).integers(0, 300, 270)]
+    lens[5], lens[6] = 0, 16
+    cache = s.cache(len(lens), max(lens))
+    fill(s, cache, lens)
+    ctx = context_for(s)
+    dev = upload_cache(cache)
+    q = tq_inputs.queries(9, (len(lens), s.Hq, 128))
+    qt = torch.from_numpy(q.astype(np.float32)).cuda()
+    out, dbg = run_decode(ctx, qt, dev, 1 / np.sqrt(128), logits_len=max(lens) + 1)
+    _check(cache, q.astype(np.float32).astype(np.float64), out, dbg)
+    o = run_decode(ctx, qt, dev, 1 / np.sqrt(128), pages_per_split=2)[0]
+    assert np.max(np.abs(o - out)) <= 1e-5 * np.max(np.abs(out))
+    assert tqa.tq_get_status(ctx) == 0
+
+
 def test_bad_page_sets_status():
     s = Setup(Hq=2, Hkv=1, W=16, P=32)
     cache = s.cache(1, 200)
