@@ -12,7 +12,7 @@ recipe of tq_inputs (heavy-tailed channels, RoPE) drawn on the GPU.
 
 The JSON line carries, besides the step rate:
   roofline      the scan kernel (the one that streams the packed cache; with
-                at most 4 page splits per KV head its last work-group of a
+                at most 4 query heads per KV head its last work-group of a
                 head also combines the splits, so the tail is included):
                 algorithmic bytes per launch / its duration.  The duration
                 comes from HIP events the library records on the launch
@@ -138,7 +138,8 @@ def cpu_baseline(T, W, P, G, Hkv, B, min_seconds, kbits=3, vbits=4, kmix=0, vmix
                       f"(seconds x {Hkv} KV heads)"}
 
 
-SCAN_SOURCES = ["decode_mfma.hip", "decode_finalize.h", "decode_common.h", "device_common.h", "tq_internal.h"]
+SCAN_SOURCES = ["decode_mfma.hip", "decode_finalize.h", "decode_common.h", "device_common.h", "tq_internal.h",
+                "decode.hip"]
 
 
 def scan_traffic():
@@ -407,8 +408,8 @@ def decode_workload(tqa, tq_inputs, wname, args, fmt_over=None):
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBPS, "traffic": None,
                      "kernel": "scan_kernel (VALU)" if fo.get("valu") else (
-                         "scan_mfma_kernel (its last work-group per KV head also combines the splits and the "
-                         "window when there are at most 4 splits)"),
+                         "scan_mfma_kernel (with at most 4 query heads per KV head its last work-group per "
+                         "KV head also combines the splits and the window)"),
                      "algorithmic_bytes_per_launch": sum(prof_bytes) / len(prof_bytes),
                      "launch_us": scan_s * 1e6,
                      "launches": f"{ncalls} scan launches by HIP events, a replay of the timed steps "
