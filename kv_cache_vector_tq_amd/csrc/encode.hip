@@ -867,9 +867,10 @@ int launch_append(const tq_ctx* c, const AppendArgs& a, void* stream) {
     else
       hipLaunchKernelGGL(append_small_kernel<false>, grid, dim3(kSmallThreads), 0, s, a, c->t, L, W, ring);
   } else {
-    // bulk: the matrix-core append for the kinds it takes (integer rates),
-    // the vector-ALU one for the rest; the ring is then updated by its own
-    // kernel, after every encoded token has been read
+    // bulk: the matrix-core append for the kinds it takes (every rate with a
+    // symmetric codebook), the vector-ALU one for the rest and under
+    // TQ_FLAG_VALU_APPEND; the ring is then updated by its own kernel, after
+    // every encoded token has been read
     int kinds = 0;
     for (int kind = 0; kind < 2; ++kind) {
       const int rc = (c->p.flags & TQ_FLAG_VALU_APPEND) ? 1 : launch_append_mma(c, kind, a, stream);

@@ -28,6 +28,8 @@
 // rows, and writes key records token by token, or the group's value words
 // (for each coordinate, the 32 tokens' codes as one bit string), which the
 // wave forms with a transpose of the code fields across its lanes.
+#include <type_traits>
+
 #include "device_common.h"
 #include "tq_internal.h"
 
@@ -81,6 +83,8 @@ __device__ void build_frags(u4* frag, const float* M, float scale, int tid) {
 struct EncCodebook {
   float cen[16];
   float bnd[16];
+  float cen2[16];  // mixed-channel rate: the (b+1)-bit codebook of the high-rate half
+  float bnd2[16];
 };
 
 // Code of y: the number of decision boundaries strictly below it.  The
@@ -166,14 +170,19 @@ __device__ __forceinline__ uint32_t pack4to3(uint32_t x) {
 // (n, kg) of column block c holds vector 16c + n, coordinates 32kg .. 32kg+31.
 // Results go to two callbacks, each called for c = 0 .. COLS-1 as soon as
 // they exist (so they need not stay in registers):
-//   codes(c, words, nst, nq): the lane's BITS words of the vector's LSB-first
-//     code stream, the stored norm (f32 norm, or the u8 log-norm level) and
-//     the u8 log-norm code (N8);
+//   codes(c, words, words2, nst, nq): the lane's BITS words of the vector's
+//     LSB-first code stream, the stored norm (f32 norm, or the u8 log-norm
+//     level) and the u8 log-norm code (N8).  With a mixed-channel rate
+//     (MIXMOD = M > 0: coordinate j takes BITS + 1 bits and the second
+//     codebook when j mod M >= M/2) words holds the low-rate codes and words2
+//     the high-rate ones, each in rank order (rank of the lane's coordinate j
+//     within its half: (j / M)(M/2) + j mod M/2), 16 codes each;
 //   signs(c, rn, sw): ||r|| and the sign bits of coordinates 32kg .. 32kg+31 (QJL).
-// frag*: the LDS fragments; ctab: the centroids in LDS; emask: the lane's
+// frag*: the LDS fragments; ctab: the centroids in LDS (then those of the
+// (b+1)-bit codebook, mixed rates); emask: the lane's
 // Hadamard signs as fp16 sign-bit masks over its input words (bit 15 or 31
 // set where the sign is -1); ntab: the u8 log-norm levels then boundaries (N8).
-template <bool QJL, bool HAD, int BITS, bool N8, int COLS, class CodesFn, class SignsFn>
+template <bool QJL, bool HAD, int BITS, bool N8, int COLS, int MIXMOD, class CodesFn, class SignsFn>
 __device__ __forceinline__ void encode_tile(const u4* fragP, const u4* fragS, const float* ctab, const u4* emask,
                                             const EncCodebook& cbk, const float* ntab,
                                             const u4 (&xb)[COLS][4], CodesFn&& codes_out, SignsFn&& signs_out) {
@@ -185,6 +194,11 @@ __device__ __forceinline__ void encode_tile(const u4* fragP, const u4* fragS, co
   uint32_t pbits[1 << (BITS - 1)];
 #pragma unroll
   for (int k = 0; k < (1 << (BITS - 1)); ++k) pbits[k] = __builtin_bit_cast(uint32_t, cbk.bnd[(1 << (BITS - 1)) - 1 + k]);
+  uint32_t pbits2[MIXMOD ? (1 << BITS) : 1];
+  if constexpr (MIXMOD > 0) {
+#pragma unroll
+    for (int k = 0; k < (1 << BITS); ++k) pbits2[k] = __builtin_bit_cast(uint32_t, cbk.bnd2[(1 << BITS) - 1 + k]);
+  }
   // ---- norms (double accumulation, as the vector-ALU path)
   float n32[COLS], invn[COLS], nstv[COLS];
   int nqv[COLS];
@@ -275,9 +289,11 @@ __device__ __forceinline__ void encode_tile(const u4* fragP, const u4* fragS, co
   float rnv[COLS];
 #pragma unroll
   for (int c = 0; c < COLS; ++c) {
-    uint32_t words[BITS];
+    uint32_t words[BITS], words2[MIXMOD ? 2 : 1];
 #pragma unroll
     for (int w = 0; w < BITS; ++w) words[w] = 0u;
+    words2[0] = 0u;
+    if constexpr (MIXMOD > 0) words2[1] = 0u;
     float rv[32];
     float rs = 0.0f;
     // y = acc / (kScale n); residual r kScale = acc - kScale nst c[code]
@@ -286,19 +302,33 @@ __device__ __forceinline__ void encode_tile(const u4* fragP, const u4* fragS, co
 #pragma unroll
     for (int j = 0; j < 32; ++j) {
       const float accv = acc[c][j >> 2][j & 3];
-      const uint32_t code = quantize_search<BITS>(accv * ys, pbits) & live;
-      const int pos = j * BITS;
-      words[pos >> 5] |= code << (pos & 31);
-      if ((pos & 31) + BITS > 32) words[(pos >> 5) + 1] |= code >> (32 - (pos & 31));
+      const bool hi = MIXMOD > 0 && (j % (MIXMOD > 0 ? MIXMOD : 1)) >= MIXMOD / 2;
+      uint32_t code;
+      if constexpr (MIXMOD > 0)
+        code = hi ? quantize_search<BITS + 1>(accv * ys, pbits2) : quantize_search<BITS>(accv * ys, pbits);
+      else
+        code = quantize_search<BITS>(accv * ys, pbits);
+      code &= live;
+      if constexpr (MIXMOD > 0) {
+        const int rank = (j / MIXMOD) * (MIXMOD / 2) + (j % MIXMOD) % (MIXMOD / 2);
+        const int wd = hi ? BITS + 1 : BITS, pos = rank * wd;
+        uint32_t* ws = hi ? words2 : words;
+        ws[pos >> 5] |= code << (pos & 31);
+        if ((pos & 31) + wd > 32) ws[(pos >> 5) + 1] |= code >> (32 - (pos & 31));
+      } else {
+        const int pos = j * BITS;
+        words[pos >> 5] |= code << (pos & 31);
+        if ((pos & 31) + BITS > 32) words[(pos >> 5) + 1] |= code >> (32 - (pos & 31));
+      }
       if constexpr (QJL) {
         // the residual against the stored reconstruction nst c[code]
         // (a zero vector has accv = 0 and nst = 0: r = 0 without a branch)
-        const float r = fmaf(nsts, ctab[code], accv);
+        const float r = fmaf(nsts, ctab[(hi ? 16 : 0) + code], accv);
         rs = fmaf(r, r, rs);
         rv[j] = r * rvs;
       }
     }
-    codes_out(c, words, nstv[c], nqv[c]);
+    codes_out(c, words, words2, nstv[c], nqv[c]);
     if constexpr (QJL) {
       rs += __shfl_xor(rs, 16, 64);
       rs += __shfl_xor(rs, 32, 64);
@@ -363,11 +393,13 @@ __device__ __forceinline__ void setup_tables(u4* fragP, u4* fragS, float* ctab, 
   const int tid = threadIdx.x;
   if (!HAD) build_frags(fragP, t.rot, 16.0f, tid);
   if (QJL) build_frags(fragS, t.S, 1.0f, tid);
-  if (tid < 16) {
+  if (tid < 32) {
     float cv = 0.0f;
 #pragma unroll
-    for (int k = 0; k < 16; ++k)
+    for (int k = 0; k < 16; ++k) {
       if (k == tid) cv = cbk.cen[k];
+      if (k + 16 == tid) cv = cbk.cen2[k];
+    }
     ctab[tid] = cv;
   }
   if constexpr (HAD) {
@@ -390,7 +422,7 @@ __global__ __launch_bounds__(kEncThreads) __attribute__((amdgpu_waves_per_eu((QJ
 void encode_mma_kernel(EncodeArgs a, DevTables t, EncCodebook cbk) {
   __shared__ u4 fragP[HAD ? 1 : 8 * 4 * 2 * 64];  // 64 KB
   __shared__ u4 fragS[QJL ? 8 * 4 * 2 * 64 : 1];  // 64 KB
-  __shared__ float ctab[16];
+  __shared__ float ctab[32];
   u4 emask[4];  // Hadamard signs of this lane's coordinates
   setup_tables<QJL, HAD>(fragP, fragS, ctab, t, cbk, emask);
 
@@ -417,9 +449,9 @@ void encode_mma_kernel(EncodeArgs a, DevTables t, EncCodebook cbk) {
       for (int s = 0; s < 4; ++s) xb[c][s] = (live[c] && 32 * kg + 8 * s < a.d) ? src[s] : u4{0u, 0u, 0u, 0u};
     }
     // stores: this lane's BITS words of the code stream, the norm, ||r||, the sign word
-    encode_tile<QJL, HAD, BITS, N8, kCols>(
+    encode_tile<QJL, HAD, BITS, N8, kCols, 0>(
         fragP, fragS, ctab, emask, cbk, t.ntab, xb,
-        [&](int c, const uint32_t* words, float nst, int) {
+        [&](int c, const uint32_t* words, const uint32_t*, float nst, int) {
           if (!live[c]) return;
           uint32_t* cw = reinterpret_cast<uint32_t*>(a.codes + vid[c] * (16 * BITS)) + BITS * kg;
 #pragma unroll
@@ -443,12 +475,16 @@ void encode_mma_kernel(EncodeArgs a, DevTables t, EncCodebook cbk) {
 // [max(T0-W, 0), max(T1-W, 0)) are encoded from their FP16 values (the ring
 // for positions below T0, else the new rows).  A sequence with an invalid
 // count or page id is skipped (left unchanged; the commit kernel reports it).
-template <bool KEY, bool QJL, bool HAD, int BITS, bool N8>
+// MIX: the mixed-channel rate BITS + 1/2 (keys: coordinates j mod 32 >= 16,
+// values: j mod 8 >= 4 at BITS + 1 bits); a key record holds the low-rate
+// codes then the high-rate ones, a value group a BITS-bit word block for the
+// low-rate half then a (BITS+1)-bit block, each indexed by rank.
+template <bool KEY, bool QJL, bool HAD, int BITS, bool N8, bool MIX>
 __global__ __launch_bounds__(kEncThreads) __attribute__((amdgpu_waves_per_eu((QJL && !HAD) ? 2 : 4)))
 void append_mma_kernel(AppendArgs a, DevTables t, EncCodebook cbk, Layout L, int W, int gmax) {
   __shared__ u4 fragP[HAD ? 1 : 8 * 4 * 2 * 64];  // 64 KB
   __shared__ u4 fragS[QJL ? 8 * 4 * 2 * 64 : 1];  // 64 KB
-  __shared__ float ctab[16];
+  __shared__ float ctab[32];
   u4 emask[4];
   setup_tables<QJL, HAD>(fragP, fragS, ctab, t, cbk, emask);
 
@@ -490,16 +526,23 @@ void append_mma_kernel(AppendArgs a, DevTables t, EncCodebook cbk, Layout L, int
     const int pid = a.block_table[static_cast<int64_t>(b) * a.max_pages + gpos / L.P];
     uint8_t* hb = a.pool + static_cast<int64_t>(pid) * L.page_bytes + kBodyOffset + static_cast<int64_t>(h) * L.head_bytes;
     const int slot0 = gpos % L.P;
-    // value words of the group: word w of coordinate j at gw[w kD + j]; bits
-    // of tokens before lo (earlier appends) are kept, those from hi on are zero
-    uint32_t* gw = reinterpret_cast<uint32_t*>(hb + L.v_codes) + static_cast<int64_t>(slot0 / kVGroup) * BITS * kD;
-    const int keep_bits = (lo - gpos) * BITS;
-    auto put_word = [&](int w, int j, uint32_t v) {
-      const int kb = keep_bits - 32 * w;
-      if (kb > 0) v |= gw[w * kD + j] & (kb >= 32 ? 0xffffffffu : ((1u << kb) - 1u));
-      gw[w * kD + j] = v;
+    // value words of the group: word w of coordinate j at gw[w kD + j] (mixed
+    // rate: of rank j in the block at word off, gw[off + 64 w + j]); bits of
+    // tokens before lo (earlier appends) are kept, those from hi on are zero
+    constexpr int kVStride = MIX ? kD / 2 : kD;
+    uint32_t* gw = reinterpret_cast<uint32_t*>(hb + L.v_codes) +
+                   static_cast<int64_t>(slot0 / kVGroup) * (MIX ? (2 * BITS + 1) * (kD / 2) : BITS * kD);
+    auto put_word = [&](int off, int wd, int w, int j, uint32_t v) {
+      const int kb = (lo - gpos) * wd - 32 * w;
+      uint32_t* pw = gw + off + w * kVStride + j;
+      if (kb > 0) v |= *pw & (kb >= 32 ? 0xffffffffu : ((1u << kb) - 1u));
+      *pw = v;
     };
-    uint32_t ch3[2][4];  // 3-bit values: the lane's 24-bit chunks per 16-token block
+    // the 3-bit block's 24-bit chunks per 16-token block (3-bit values, or
+    // the 3-bit half of a mixed rate), joined after the loop
+    constexpr int kQ3 = MIX ? 2 : 4;                                // chunks of 8 codes per lane
+    constexpr int kOff3 = (MIX && BITS == 2) ? (kD / 2) * BITS : 0;  // word offset of the 3-bit block
+    uint32_t ch3[2][4];
     (void)ch3;
 #pragma unroll
     for (int sb = 0; sb < kSub; ++sb) {
@@ -520,16 +563,29 @@ void append_mma_kernel(AppendArgs a, DevTables t, EncCodebook cbk, Layout L, int
 #pragma unroll
         for (int s = 0; s < 4; ++s) xb[c][s] = (live[c] && 32 * kg + 8 * s < L.d) ? rp[s] : u4{0u, 0u, 0u, 0u};
       }
-      encode_tile<QJL, HAD, BITS, N8, kCols>(
+      encode_tile<QJL, HAD, BITS, N8, kCols, MIX ? (KEY ? kKeyHiMod : kValHiMod) : 0>(
           fragP, fragS, ctab, emask, cbk, t.ntab, xb,
-          [&](int c, const uint32_t* words, float nst, int nq) {
+          [&](int c, const uint32_t* words, const uint32_t* words2, float nst, int nq) {
             const int slot = slot0 + tk[c];
             if constexpr (KEY) {
               if (!live[c]) return;
-              uint32_t* cw =
-                  reinterpret_cast<uint32_t*>(hb + L.k_codes + static_cast<int64_t>(slot) * L.k_rec) + BITS * kg;
+              if constexpr (MIX) {
+                // low-rate piece: 2 BITS bytes at 2 BITS kg; high-rate piece:
+                // 2 (BITS+1) bytes at 8 BITS + 2 (BITS+1) kg (16-bit stores)
+                uint16_t* rl = reinterpret_cast<uint16_t*>(hb + L.k_codes + static_cast<int64_t>(slot) * L.k_rec +
+                                                           2 * BITS * kg);
+                uint16_t* rh = reinterpret_cast<uint16_t*>(hb + L.k_codes + static_cast<int64_t>(slot) * L.k_rec +
+                                                           8 * BITS + 2 * (BITS + 1) * kg);
 #pragma unroll
-              for (int w = 0; w < BITS; ++w) cw[w] = words[w];
+                for (int i = 0; i < BITS; ++i) rl[i] = static_cast<uint16_t>(words[i >> 1] >> (16 * (i & 1)));
+#pragma unroll
+                for (int i = 0; i < BITS + 1; ++i) rh[i] = static_cast<uint16_t>(words2[i >> 1] >> (16 * (i & 1)));
+              } else {
+                uint32_t* cw =
+                    reinterpret_cast<uint32_t*>(hb + L.k_codes + static_cast<int64_t>(slot) * L.k_rec) + BITS * kg;
+#pragma unroll
+                for (int w = 0; w < BITS; ++w) cw[w] = words[w];
+              }
               if (kg == 0) {
                 if constexpr (N8)
                   (hb + L.k_norm)[slot] = static_cast<uint8_t>(nq);
@@ -544,27 +600,40 @@ void append_mma_kernel(AppendArgs a, DevTables t, EncCodebook cbk, Layout L, int
               // across lanes gives each lane whole words of the strings (dead
               // tokens carry zero codes).  All lanes take part in the shuffles.
               const int tb = kCols * sb + c;
-              if constexpr (BITS == 4) {
-                // words[q]: codes of coordinates 32kg + 8q .. +7 -> word 2tb + n/8
-                // of coordinate 32kg + 8q + n%8 (tokens 16tb + 8(n/8) .. +7)
+              // One block of NC codes of width WD per lane (the lane's codes of
+              // indices J0 .. J0 + NC - 1 of the block at word OFF):
+              //  WD = 4: word q holds indices J0 + 8q .. +7 -> word 2tb + n/8 of
+              //          index J0 + 8q + n%8 (tokens 16tb + 8(n/8) .. +7);
+              //  WD = 2: word q holds indices J0 + 16q .. +15 -> word tb of index J0 + 16q + n;
+              //  WD = 3: 8 codes (24 bits) at a time as nibbles, transposed and
+              //          packed back: the 24-bit chunk of tokens 16tb + 8(n/8)
+              //          .. +7 of index J0 + 8q + n%8; joined below.
+              auto block = [&](auto wd_c, auto nc_c, int off, int j0, const uint32_t* ws) {
+                constexpr int WD = decltype(wd_c)::value, NC = decltype(nc_c)::value;
+                if constexpr (WD == 4) {
 #pragma unroll
-                for (int q = 0; q < 4; ++q)
-                  put_word(2 * tb + (n >> 3), 32 * kg + 8 * q + (n & 7), transpose_nibbles8(words[q], l));
-              } else if constexpr (BITS == 2) {
-                // words[q]: coordinates 32kg + 16q .. +15 -> word tb of coordinate 32kg + 16q + n
+                  for (int q = 0; q < NC / 8; ++q)
+                    put_word(off, 4, 2 * tb + (n >> 3), j0 + 8 * q + (n & 7), transpose_nibbles8(ws[q], l));
+                } else if constexpr (WD == 2) {
 #pragma unroll
-                for (int q = 0; q < 2; ++q) put_word(tb, 32 * kg + 16 * q + n, transpose_crumbs16(words[q], l));
-              } else {
-                // 8 codes (24 bits) at a time as nibbles, transposed, packed
-                // back: the 24-bit chunk of tokens 16tb + 8(n/8) .. +7 of
-                // coordinate 32kg + 8q + n%8; the chunks are joined below
+                  for (int q = 0; q < NC / 16; ++q) put_word(off, 2, tb, j0 + 16 * q + n, transpose_crumbs16(ws[q], l));
+                } else {
 #pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                  const int b0 = 24 * q, wi = b0 >> 5, sh = b0 & 31;
-                  uint32_t v = words[wi] >> sh;
-                  if (sh > 8) v |= words[wi + 1] << (32 - sh);
-                  ch3[tb][q] = pack4to3(transpose_nibbles8(spread3to4(v & 0xFFFFFFu), l));
+                  for (int q = 0; q < NC / 8; ++q) {
+                    const int b0 = 24 * q, wi = b0 >> 5, sh = b0 & 31;
+                    uint32_t v = ws[wi] >> sh;
+                    if (sh > 8) v |= ws[wi + 1] << (32 - sh);
+                    ch3[tb][q] = pack4to3(transpose_nibbles8(spread3to4(v & 0xFFFFFFu), l));
+                  }
                 }
+              };
+              if constexpr (MIX) {
+                // ranks 16kg .. 16kg+15 of each half
+                block(std::integral_constant<int, BITS>{}, std::integral_constant<int, 16>{}, 0, 16 * kg, words);
+                block(std::integral_constant<int, BITS + 1>{}, std::integral_constant<int, 16>{}, (kD / 2) * BITS,
+                      16 * kg, words2);
+              } else {
+                block(std::integral_constant<int, BITS>{}, std::integral_constant<int, 32>{}, 0, 32 * kg, words);
               }
             }
           },
@@ -575,24 +644,24 @@ void append_mma_kernel(AppendArgs a, DevTables t, EncCodebook cbk, Layout L, int
             reinterpret_cast<uint32_t*>(hb + L.k_signs + static_cast<int64_t>(slot) * (kD / 8))[kg] = sw;
           });
     }
-    if constexpr (!KEY && BITS == 3) {
-      // coordinate j's 96-bit string is chunks 0..3 (tokens 8w .. 8w+7) at
-      // bits 24w: lane n < 8 holds chunks 0 and 2, lane n + 8 chunks 1 and 3;
-      // each takes the other two from its partner and writes words 0, 1
-      // (n < 8) or word 2
+    if constexpr (!KEY && (BITS == 3 || MIX)) {
+      // index j's 96-bit string is chunks 0..3 (tokens 8w .. 8w+7) at bits
+      // 24w: lane n < 8 holds chunks 0 and 2, lane n + 8 chunks 1 and 3; each
+      // takes the other two from its partner and writes words 0, 1 (n < 8)
+      // or word 2
       const bool hi8 = (n & 8) != 0;
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
+      for (int q = 0; q < kQ3; ++q) {
         const uint32_t o0 = static_cast<uint32_t>(__shfl_xor(static_cast<int>(ch3[0][q]), 8, 64));
         const uint32_t o1 = static_cast<uint32_t>(__shfl_xor(static_cast<int>(ch3[1][q]), 8, 64));
         const uint32_t c0 = hi8 ? o0 : ch3[0][q], c1 = hi8 ? ch3[0][q] : o0;
         const uint32_t c2 = hi8 ? o1 : ch3[1][q], c3 = hi8 ? ch3[1][q] : o1;
-        const int j = 32 * kg + 8 * q + (n & 7);
+        const int j = (MIX ? 16 : 32) * kg + 8 * q + (n & 7);
         if (!hi8) {
-          put_word(0, j, c0 | (c1 << 24));
-          put_word(1, j, (c1 >> 8) | (c2 << 16));
+          put_word(kOff3, 3, 0, j, c0 | (c1 << 24));
+          put_word(kOff3, 3, 1, j, (c1 >> 8) | (c2 << 16));
         } else {
-          put_word(2, j, (c2 >> 16) | (c3 << 8));
+          put_word(kOff3, 3, 2, j, (c2 >> 16) | (c3 << 8));
         }
       }
     }
@@ -607,30 +676,43 @@ const void* pick_bits(int bits) {
 }
 
 template <bool KEY, bool QJL, bool HAD, bool N8>
-const void* pick_append_bits(int bits) {
-  if (bits == 2) return reinterpret_cast<const void*>(&append_mma_kernel<KEY, QJL, HAD, 2, N8>);
-  if (bits == 3) return reinterpret_cast<const void*>(&append_mma_kernel<KEY, QJL, HAD, 3, N8>);
-  return reinterpret_cast<const void*>(&append_mma_kernel<KEY, QJL, HAD, 4, N8>);
+const void* pick_append_bits(int bits, bool mix) {
+  if (mix) {  // mixed rates exist at 2.5 and 3.5 bits
+    if (bits == 2) return reinterpret_cast<const void*>(&append_mma_kernel<KEY, QJL, HAD, 2, N8, true>);
+    if (bits == 3) return reinterpret_cast<const void*>(&append_mma_kernel<KEY, QJL, HAD, 3, N8, true>);
+    return nullptr;
+  }
+  if (bits == 2) return reinterpret_cast<const void*>(&append_mma_kernel<KEY, QJL, HAD, 2, N8, false>);
+  if (bits == 3) return reinterpret_cast<const void*>(&append_mma_kernel<KEY, QJL, HAD, 3, N8, false>);
+  return reinterpret_cast<const void*>(&append_mma_kernel<KEY, QJL, HAD, 4, N8, false>);
 }
 
 template <bool QJL, bool HAD>
-const void* pick_append_key(int bits, bool n8) {
-  return n8 ? pick_append_bits<true, QJL, HAD, true>(bits) : pick_append_bits<true, QJL, HAD, false>(bits);
+const void* pick_append_key(int bits, bool n8, bool mix) {
+  return n8 ? pick_append_bits<true, QJL, HAD, true>(bits, mix) : pick_append_bits<true, QJL, HAD, false>(bits, mix);
 }
 
-// This kind's codebook, if the matrix-core path takes it: an integer rate
-// with a symmetric codebook (the binary-search quantiser relies on it).
-bool mma_codebook(const tq_ctx* c, bool key, EncCodebook& cbk) {
-  if (c->lay.D != kD || (key ? c->p.key_mixed : c->p.value_mixed)) return false;
+// This kind's codebook(s), if the matrix-core path takes them: symmetric
+// codebooks (the binary-search quantiser relies on it); a mixed-channel rate
+// only where allowed (the bulk append), with its (b+1)-bit codebook too.
+bool mma_codebook(const tq_ctx* c, bool key, EncCodebook& cbk, bool allow_mixed) {
+  const bool mix = key ? c->p.key_mixed : c->p.value_mixed;
+  if (c->lay.D != kD || (mix && !allow_mixed)) return false;
   const int bits = key ? c->p.key_bits : c->p.value_bits;
   for (int k = 0; k < 16; ++k) {
     cbk.cen[k] = key ? c->cb.kc[k] : c->cb.vc[k];
     cbk.bnd[k] = key ? c->cb.kb[k] : c->cb.vb[k];
+    cbk.cen2[k] = key ? c->cb.kc2[k] : c->cb.vc2[k];
+    cbk.bnd2[k] = key ? c->cb.kb2[k] : c->cb.vb2[k];
   }
-  const int L = 1 << bits;
-  if (cbk.bnd[L / 2 - 1] != 0.0f) return false;
-  for (int k = 0; k + 1 < L; ++k)
-    if (cbk.bnd[k] != -cbk.bnd[L - 2 - k]) return false;
+  auto symmetric = [](const float* bnd, int levels) {
+    if (bnd[levels / 2 - 1] != 0.0f) return false;
+    for (int k = 0; k + 1 < levels; ++k)
+      if (bnd[k] != -bnd[levels - 2 - k]) return false;
+    return true;
+  };
+  if (!symmetric(cbk.bnd, 1 << bits)) return false;
+  if (mix && (bits + 1 > 4 || !symmetric(cbk.bnd2, 1 << (bits + 1)))) return false;
   return true;
 }
 
@@ -656,7 +738,7 @@ int launch_encode_mma(const tq_ctx* c, int kind, int dtype, const EncodeArgs& a,
   if (dtype != TQ_DTYPE_F16 || (a.row_stride % 8) != 0 || (reinterpret_cast<uintptr_t>(a.x) % 16) != 0) return 1;
   const bool key = kind == TQ_KIND_KEY;
   EncCodebook cbk;
-  if (!mma_codebook(c, key, cbk)) return 1;
+  if (!mma_codebook(c, key, cbk, false)) return 1;
   const bool qjl = key && c->p.key_qjl;
   const bool had = c->p.rotation == TQ_ROT_HADAMARD;
   const bool n8 = key && c->p.key_norm_u8;
@@ -681,21 +763,25 @@ int launch_encode_mma(const tq_ctx* c, int kind, int dtype, const EncodeArgs& a,
 }
 
 // Bulk append of one kind on the matrix cores.  Returns 1 when this path does
-// not apply (mixed-channel rate); -1 on a launch error.
+// not apply (a codebook the binary-search quantiser cannot take); -1 on a
+// launch error.
 int launch_append_mma(const tq_ctx* c, int kind, const AppendArgs& a, void* stream) {
   const bool key = kind == TQ_KIND_KEY;
   EncCodebook cbk;
-  if (!mma_codebook(c, key, cbk)) return 1;
+  if (!mma_codebook(c, key, cbk, true)) return 1;
   const bool had = c->p.rotation == TQ_ROT_HADAMARD;
   const bool n8 = key && c->p.key_norm_u8;
   const bool qjl = key && c->p.key_qjl;
+  const bool mix = key ? c->p.key_mixed : c->p.value_mixed;
   const int bits = key ? c->p.key_bits : c->p.value_bits;
   const void* f;
   if (key)
-    f = qjl ? (had ? pick_append_key<true, true>(bits, n8) : pick_append_key<true, false>(bits, n8))
-            : (had ? pick_append_key<false, true>(bits, n8) : pick_append_key<false, false>(bits, n8));
+    f = qjl ? (had ? pick_append_key<true, true>(bits, n8, mix) : pick_append_key<true, false>(bits, n8, mix))
+            : (had ? pick_append_key<false, true>(bits, n8, mix) : pick_append_key<false, false>(bits, n8, mix));
   else
-    f = had ? pick_append_bits<false, false, true, false>(bits) : pick_append_bits<false, false, false, false>(bits);
+    f = had ? pick_append_bits<false, false, true, false>(bits, mix)
+            : pick_append_bits<false, false, false, false>(bits, mix);
+  if (!f) return 1;
   // value groups a sequence can touch: ceil(n_new / 32) + 1 (unaligned start)
   const int gmax = (a.n_new + kVGroup - 1) / kVGroup + 1;
   if (static_cast<int64_t>(a.batch) * c->lay.H * gmax >= (int64_t(1) << 31)) return 1;

@@ -272,6 +272,17 @@ MMA_CASES = [
     ("d96_k3qjl_v4", dict(d=96, Hq=8, Hkv=2, W=40, P=64), [300, 41, 40, 7, 0, 129], 37),
     ("d80_k2qjl_v3_hadamard", dict(d=80, Hq=4, Hkv=2, key_bits=2, value_bits=3, rotation="hadamard", W=16, P=32),
      [200, 77], 50),
+    # mixed-channel rates (keys and values at 2.5 or 3.5 bits)
+    ("mixed_k35qjl_v35", dict(Hq=8, Hkv=2, W=40, P=64, key_bits=3, key_mixed=True, value_bits=3, value_mixed=True),
+     [300, 41, 40, 7, 0, 129], 37),
+    ("mixed_k25qjl_v25_hadamard", dict(Hq=8, Hkv=2, W=16, P=32, key_bits=2, key_mixed=True, value_bits=2,
+                                       value_mixed=True, rotation="hadamard"), [200, 77], 50),
+    ("mixed_k35qjl_u8norm_v3", dict(Hq=4, Hkv=2, W=24, P=64, key_bits=3, key_mixed=True, value_bits=3,
+                                    key_norm_u8=True), [150, 31, 64], 20),
+    ("mixed_k3_noqjl_v25", dict(Hq=4, Hkv=2, key_bits=3, key_qjl=0, value_bits=2, value_mixed=True, W=8, P=32),
+     [333, 64, 17], 9),
+    ("mixed_d96_k35qjl_v35", dict(d=96, Hq=4, Hkv=2, W=40, P=64, key_bits=3, key_mixed=True, value_bits=3,
+                                  value_mixed=True), [300, 41], 37),
 ]
 
 
