@@ -417,7 +417,10 @@ __device__ __forceinline__ void setup_tables(u4* fragP, u4* fragS, float* ctab, 
 
 // Two work-groups per CU need <= 128 VGPRs; the dense key variant holds both
 // matrices (128 KB of LDS) and fits only one anyway.
-template <bool QJL, bool HAD, int BITS, bool N8>
+// MIXMOD > 0: mixed-channel rate (coordinate j at BITS + 1 bits when
+// j mod MIXMOD >= MIXMOD/2); a record holds the low-rate codes, then the
+// high-rate ones, each in rank order.
+template <bool QJL, bool HAD, int BITS, bool N8, int MIXMOD>
 __global__ __launch_bounds__(kEncThreads) __attribute__((amdgpu_waves_per_eu((QJL && !HAD) ? 2 : 4)))
 void encode_mma_kernel(EncodeArgs a, DevTables t, EncCodebook cbk) {
   __shared__ u4 fragP[HAD ? 1 : 8 * 4 * 2 * 64];  // 64 KB
@@ -449,13 +452,26 @@ void encode_mma_kernel(EncodeArgs a, DevTables t, EncCodebook cbk) {
       for (int s = 0; s < 4; ++s) xb[c][s] = (live[c] && 32 * kg + 8 * s < a.d) ? src[s] : u4{0u, 0u, 0u, 0u};
     }
     // stores: this lane's BITS words of the code stream, the norm, ||r||, the sign word
-    encode_tile<QJL, HAD, BITS, N8, kCols, 0>(
+    encode_tile<QJL, HAD, BITS, N8, kCols, MIXMOD>(
         fragP, fragS, ctab, emask, cbk, t.ntab, xb,
-        [&](int c, const uint32_t* words, const uint32_t*, float nst, int) {
+        [&](int c, const uint32_t* words, const uint32_t* words2, float nst, int) {
           if (!live[c]) return;
-          uint32_t* cw = reinterpret_cast<uint32_t*>(a.codes + vid[c] * (16 * BITS)) + BITS * kg;
+          if constexpr (MIXMOD > 0) {
+            // record of 16 BITS + 8 bytes: the lane's low-rate piece (2 BITS
+            // bytes at 2 BITS kg) and high-rate piece (2 (BITS+1) bytes at
+            // 8 BITS + 2 (BITS+1) kg), 16-bit stores
+            uint8_t* rec = a.codes + vid[c] * (16 * BITS + 8);
+            uint16_t* rl = reinterpret_cast<uint16_t*>(rec + 2 * BITS * kg);
+            uint16_t* rh = reinterpret_cast<uint16_t*>(rec + 8 * BITS + 2 * (BITS + 1) * kg);
 #pragma unroll
-          for (int w = 0; w < BITS; ++w) cw[w] = words[w];
+            for (int i = 0; i < BITS; ++i) rl[i] = static_cast<uint16_t>(words[i >> 1] >> (16 * (i & 1)));
+#pragma unroll
+            for (int i = 0; i < BITS + 1; ++i) rh[i] = static_cast<uint16_t>(words2[i >> 1] >> (16 * (i & 1)));
+          } else {
+            uint32_t* cw = reinterpret_cast<uint32_t*>(a.codes + vid[c] * (16 * BITS)) + BITS * kg;
+#pragma unroll
+            for (int w = 0; w < BITS; ++w) cw[w] = words[w];
+          }
           if (kg == 0) a.norms[vid[c]] = nst;
         },
         [&](int c, float rn, uint32_t sw) {
@@ -669,10 +685,20 @@ void append_mma_kernel(AppendArgs a, DevTables t, EncCodebook cbk, Layout L, int
 }
 
 template <bool QJL, bool HAD, bool N8>
-const void* pick_bits(int bits) {
-  if (bits == 2) return reinterpret_cast<const void*>(&encode_mma_kernel<QJL, HAD, 2, N8>);
-  if (bits == 3) return reinterpret_cast<const void*>(&encode_mma_kernel<QJL, HAD, 3, N8>);
-  return reinterpret_cast<const void*>(&encode_mma_kernel<QJL, HAD, 4, N8>);
+const void* pick_bits(int bits, int mixmod) {
+  if (mixmod == kKeyHiMod) {  // mixed rates exist at 2.5 and 3.5 bits
+    if (bits == 2) return reinterpret_cast<const void*>(&encode_mma_kernel<QJL, HAD, 2, N8, kKeyHiMod>);
+    if (bits == 3) return reinterpret_cast<const void*>(&encode_mma_kernel<QJL, HAD, 3, N8, kKeyHiMod>);
+    return nullptr;
+  }
+  if (mixmod == kValHiMod) {
+    if (bits == 2) return reinterpret_cast<const void*>(&encode_mma_kernel<QJL, HAD, 2, N8, kValHiMod>);
+    if (bits == 3) return reinterpret_cast<const void*>(&encode_mma_kernel<QJL, HAD, 3, N8, kValHiMod>);
+    return nullptr;
+  }
+  if (bits == 2) return reinterpret_cast<const void*>(&encode_mma_kernel<QJL, HAD, 2, N8, 0>);
+  if (bits == 3) return reinterpret_cast<const void*>(&encode_mma_kernel<QJL, HAD, 3, N8, 0>);
+  return reinterpret_cast<const void*>(&encode_mma_kernel<QJL, HAD, 4, N8, 0>);
 }
 
 template <bool KEY, bool QJL, bool HAD, bool N8>
@@ -733,23 +759,26 @@ int persistent_blocks(const void* f, int64_t items, int64_t* blocks) {
 }  // namespace
 
 // Returns 1 when this path does not apply (input not fp16 or not 16-byte
-// rows, mixed-channel rate); the caller then uses the vector-ALU encoder.
+// rows, or a codebook the binary-search quantiser cannot take); the caller
+// then uses the vector-ALU encoder.
 int launch_encode_mma(const tq_ctx* c, int kind, int dtype, const EncodeArgs& a, void* stream) {
   if (dtype != TQ_DTYPE_F16 || (a.row_stride % 8) != 0 || (reinterpret_cast<uintptr_t>(a.x) % 16) != 0) return 1;
   const bool key = kind == TQ_KIND_KEY;
   EncCodebook cbk;
-  if (!mma_codebook(c, key, cbk, false)) return 1;
+  if (!mma_codebook(c, key, cbk, true)) return 1;
   const bool qjl = key && c->p.key_qjl;
   const bool had = c->p.rotation == TQ_ROT_HADAMARD;
   const bool n8 = key && c->p.key_norm_u8;
   const int bits = key ? c->p.key_bits : c->p.value_bits;
+  const int mm = (key ? c->p.key_mixed : c->p.value_mixed) ? (key ? kKeyHiMod : kValHiMod) : 0;
   const void* f;
   if (n8)
-    f = qjl ? (had ? pick_bits<true, true, true>(bits) : pick_bits<true, false, true>(bits))
-            : (had ? pick_bits<false, true, true>(bits) : pick_bits<false, false, true>(bits));
+    f = qjl ? (had ? pick_bits<true, true, true>(bits, mm) : pick_bits<true, false, true>(bits, mm))
+            : (had ? pick_bits<false, true, true>(bits, mm) : pick_bits<false, false, true>(bits, mm));
   else
-    f = qjl ? (had ? pick_bits<true, true, false>(bits) : pick_bits<true, false, false>(bits))
-            : (had ? pick_bits<false, true, false>(bits) : pick_bits<false, false, false>(bits));
+    f = qjl ? (had ? pick_bits<true, true, false>(bits, mm) : pick_bits<true, false, false>(bits, mm))
+            : (had ? pick_bits<false, true, false>(bits, mm) : pick_bits<false, false, false>(bits, mm));
+  if (!f) return 1;
   const int tv = 16 * cols_for(had);
   int64_t blocks = 0;
   if (persistent_blocks(f, (a.n + tv - 1) / tv, &blocks) != 0) return -1;
