@@ -156,7 +156,7 @@ __device__ inline u4 dec_signs8(uint32_t x, const u2* lutN) {
 // rates (two tables per operand side) get 168 (three waves).  Measured at
 // B=16, T=32K with four-wave work-groups: keys 3 / values 3 166 -> 132 us,
 // keys 3.5 / values 3 201 -> 136 us.
-constexpr bool wide_table(int G, int BV, bool vmix) { return BV == 4 && G <= 4 && !vmix; }
+constexpr bool wide_table(int G, int BV, bool vmix) { return BV == 4 && G <= 8 && !vmix; }
 constexpr int scan_waves_per_simd(int BV, bool kmix, bool vmix) { return (BV == 3 || kmix || vmix) ? 3 : 4; }
 constexpr int scan_threads(int BV, bool kmix, bool vmix) { return 256 * scan_waves_per_simd(BV, kmix, vmix); }
 
