@@ -151,21 +151,29 @@ __device__ inline u4 dec_signs8(uint32_t x, const u2* lutN) {
 // reads copy lane % 8, one 16-byte read per 8 signs).  One v_perm forms each
 // address (byte e into bits 8..15, the lane's copy offset into bits 0..7)
 // where the narrow tables take a shift and a mask-or.
+// With 2-bit keys and values a "quad" table of the same shape serves both:
+// row e holds the four fp16 centroids of code byte e (four 2-bit codes) in
+// 16 copies of 8 bytes (lane reads copy lane % 16) and the same sign half,
+// so 8 codes take two v_perm addresses and two 8-byte reads, where the
+// 16-entry pair table takes a shift and a mask per pair.
 // Register budget: 128 VGPRs (four waves per SIMD), except where that would
 // spill inside the loop: 3-bit values (two words per value slice) and mixed
 // rates (two tables per operand side) get 168 (three waves).  Measured at
 // B=16, T=32K with four-wave work-groups: keys 3 / values 3 166 -> 132 us,
 // keys 3.5 / values 3 201 -> 136 us.
 constexpr bool wide_table(int G, int BV, bool vmix) { return BV == 4 && G <= 8 && !vmix; }
+constexpr bool quad_table(int BK, int BV, bool kmix, bool vmix) { return BK == 2 && BV == 2 && !kmix && !vmix; }
 constexpr int scan_waves_per_simd(int BV, bool kmix, bool vmix) { return (BV == 3 || kmix || vmix) ? 3 : 4; }
 constexpr int scan_threads(int BV, bool kmix, bool vmix) { return 256 * scan_waves_per_simd(BV, kmix, vmix); }
 
-template <int G, int BV, bool KMIX, bool VMIX>
+template <int G, int BK, int BV, bool KMIX, bool VMIX>
 struct ScanShape {
   static constexpr bool kWide = wide_table(G, BV, VMIX);
+  static constexpr bool kQuad = quad_table(BK, BV, KMIX, VMIX);
+  static constexpr bool kRows = kWide || kQuad;  // 256-byte rows with the sign half
   static constexpr int kThreads = scan_threads(BV, KMIX, VMIX);
   static constexpr int kWaves = kThreads / 64;
-  static constexpr int kLutWords = kWide ? 256 * 64 : PairLut<BV>::kWords;
+  static constexpr int kLutWords = kRows ? 256 * 64 : PairLut<BV>::kWords;
 };
 
 // address of byte K of x in a 256-byte-row table, plus the lane's copy offset
@@ -180,6 +188,16 @@ __device__ inline uint32_t lds_word(const uint32_t* t, uint32_t byte_addr) {
 __device__ inline u4 dec8_wide(uint32_t x, const uint32_t* t, uint32_t vbase) {
   return u4{lds_word(t, row_addr<0>(x, vbase)), lds_word(t, row_addr<1>(x, vbase)),
             lds_word(t, row_addr<2>(x, vbase)), lds_word(t, row_addr<3>(x, vbase))};
+}
+// selector of v_perm placing byte K of its first operand in bits 8..15 and
+// byte 0 of the second in bits 0..7
+constexpr uint32_t row_sel(int K) { return 0x0C0C0000u | ((4u + K) << 8); }
+// 8 consecutive 2-bit codes (bytes of x picked by sel0, sel1) -> 8 fp16
+// values from the quad table
+__device__ inline u4 dec8_quad(uint32_t x, const uint32_t* t, uint32_t qbase, uint32_t sel0, uint32_t sel1) {
+  const u2 a = *reinterpret_cast<const u2*>(reinterpret_cast<const char*>(t) + __builtin_amdgcn_perm(x, qbase, sel0));
+  const u2 b = *reinterpret_cast<const u2*>(reinterpret_cast<const char*>(t) + __builtin_amdgcn_perm(x, qbase, sel1));
+  return u4{a.x, a.y, b.x, b.y};
 }
 // sign byte K of x -> 8 fp16 +-1 from the wide table
 template <int K>
@@ -242,10 +260,10 @@ struct Meta {
 // reads the low-rate word block for bl < 4 and the high-rate one otherwise,
 // so every operand slice has one compile-time width.
 template <int G, int BK, int BV, bool QJL, bool KMIX, bool VMIX, bool N8>
-__global__ __launch_bounds__((ScanShape<G, BV, KMIX, VMIX>::kThreads), (scan_waves_per_simd(BV, KMIX, VMIX))) void
+__global__ __launch_bounds__((ScanShape<G, BK, BV, KMIX, VMIX>::kThreads), (scan_waves_per_simd(BV, KMIX, VMIX))) void
 scan_mfma_kernel(DecodeArgs a, DevTables t, Codebooks cb, KParams k) {
-  using Sh = ScanShape<G, BV, KMIX, VMIX>;
-  constexpr bool kWide = Sh::kWide;
+  using Sh = ScanShape<G, BK, BV, KMIX, VMIX>;
+  constexpr bool kWide = Sh::kWide, kQuad = Sh::kQuad, kRows = Sh::kRows;
   constexpr int kThreads = Sh::kThreads, kWaves = Sh::kWaves;
   // One array: the key table (absent when keys and values share a bit width,
   // hence a codebook) first, so that every table address stays within the
@@ -262,7 +280,7 @@ scan_mfma_kernel(DecodeArgs a, DevTables t, Codebooks cb, KParams k) {
   uint32_t* const lutKhi = luts + kKeyWords;
   uint32_t* const lutV = luts + kKeyWords + kKeyHiWords;
   uint32_t* const lutVhi = lutV + Sh::kLutWords;
-  __shared__ u2 lutN[kWide ? 1 : 16];
+  __shared__ u2 lutN[kRows ? 1 : 16];
   __shared__ float pv[kWaves][2][G][kChunk];  // softmax weights x value norms, two chunks in flight
   __shared__ float wm[kWaves][G], wl[kWaves][G];
   __shared__ float red[G][kD];
@@ -368,9 +386,10 @@ scan_mfma_kernel(DecodeArgs a, DevTables t, Codebooks cb, KParams k) {
     cv2[tid] = vv2;
   }
   __syncthreads();
-  if constexpr (kWide) {
-    // row e: words 0..31 the value pair of byte e (32 copies), words 32..63
-    // the four sign words of byte e (8 copies); written four words at a time
+  if constexpr (kRows) {
+    // row e: words 0..31 the value pair of byte e (32 copies; quad table:
+    // the four values of byte e, 16 copies of two words), words 32..63 the
+    // four sign words of byte e (8 copies); written four words at a time
     auto sgn_word = [](int e, int j) {  // word j of sign byte e: bits 2j (low half) and 2j + 1
       return ((e >> (2 * j)) & 1 ? 0x3C00u : 0xBC00u) | (((e >> (2 * j + 1)) & 1 ? 0x3C00u : 0xBC00u) << 16);
     };
@@ -379,8 +398,14 @@ scan_mfma_kernel(DecodeArgs a, DevTables t, Codebooks cb, KParams k) {
       const int e = w4 >> 4;
       u4 v;
       if ((w4 & 15) < 8) {
-        const uint32_t x = h_bits(cvv[e & 15]) | (h_bits(cvv[e >> 4]) << 16);
-        v = u4{x, x, x, x};
+        if constexpr (kQuad) {
+          const uint32_t x0 = h_bits(cvv[e & 3]) | (h_bits(cvv[(e >> 2) & 3]) << 16);
+          const uint32_t x1 = h_bits(cvv[(e >> 4) & 3]) | (h_bits(cvv[e >> 6]) << 16);
+          v = u4{x0, x1, x0, x1};
+        } else {
+          const uint32_t x = h_bits(cvv[e & 15]) | (h_bits(cvv[e >> 4]) << 16);
+          v = u4{x, x, x, x};
+        }
       } else {
         v = u4{sgn_word(e, 0), sgn_word(e, 1), sgn_word(e, 2), sgn_word(e, 3)};
       }
@@ -392,7 +417,7 @@ scan_mfma_kernel(DecodeArgs a, DevTables t, Codebooks cb, KParams k) {
   if constexpr (BK != BV && !kKeyInVhi) build_pair_lut<BK, kThreads>(lutKown, ck, tid);
   if constexpr (KMIX) build_pair_lut<BK + 1, kThreads, 1>(lutKhi, ck2, tid);
   if constexpr (VMIX) build_pair_lut<BV + 1, kThreads>(lutVhi, cv2, tid);
-  if (!kWide && tid < 16) {
+  if (!kRows && tid < 16) {
     const int e = tid;
     lutN[e] = u2{(e & 1 ? 0x3C00u : 0xBC00u) | ((e & 2 ? 0x3C00u : 0xBC00u) << 16),
                  (e & 4 ? 0x3C00u : 0xBC00u) | ((e & 8 ? 0x3C00u : 0xBC00u) << 16)};
@@ -402,6 +427,7 @@ scan_mfma_kernel(DecodeArgs a, DevTables t, Codebooks cb, KParams k) {
   const uint32_t* lutVl = lutV + (PairLut<BV>::kCopies > 1 ? (tid & 31) : 0);
   const uint32_t* lutVhil = lutVhi + ((VMIX && PairLut<BV + 1>::kCopies > 1) ? (tid & 31) : 0);
   const uint32_t vbase = static_cast<uint32_t>(tid & 31) * 4u, sbase = 128u + static_cast<uint32_t>(tid & 7) * 16u;
+  const uint32_t qbase = static_cast<uint32_t>(tid & 15) * 8u;  // quad table: the lane's copy
   // the query operands, fp16 hi part or remainder per lane (zero for rows
   // past the G queries)
   u4 aq[4], ap[4];
@@ -564,10 +590,13 @@ scan_mfma_kernel(DecodeArgs a, DevTables t, Codebooks cb, KParams k) {
           else dm = mfma(aq[i], dec8<BK + 1, 1>(key_slice<BK + 1>(&d.kc[tt][2], i - 2), lutKhi), dm);
         } else if constexpr (kWide && BK == 4) {
           dm = mfma(aq[i], dec8_wide(d.kc[tt][i], lutV, vbase), dm);
+        } else if constexpr (kQuad) {
+          // codes 8i .. 8i+7: bytes 2(i%2), 2(i%2)+1 of word i/2
+          dm = mfma(aq[i], dec8_quad(d.kc[tt][i >> 1], lutV, qbase, row_sel(2 * (i & 1)), row_sel(2 * (i & 1) + 1)), dm);
         } else {
           dm = mfma(aq[i], dec8<BK>(key_slice<BK>(d.kc[tt], i), lutKl), dm);
         }
-        if constexpr (QJL && kWide) {
+        if constexpr (QJL && kRows) {
           const uint32_t sgw = d.sg[tt];
           const u4 sb = i == 0 ? dec_signs_wide<0>(sgw, lutV, sbase)
                         : i == 1 ? dec_signs_wide<1>(sgw, lutV, sbase)
@@ -662,6 +691,13 @@ scan_mfma_kernel(DecodeArgs a, DevTables t, Codebooks cb, KParams k) {
         else
           acc[bl] = mfma(aw, dec8<BV + 1>(vslice<BV + 1>(d.vw[bl], d.vw2[bl], vshH, vtwoH), lutVhil), acc[bl]);
       }
+      return;
+    }
+    if constexpr (kQuad) {
+      // the lane's 8 codes are bytes 2(kg%2), 2(kg%2)+1 of each value word
+      const uint32_t qs0 = 0x0C0C0400u + ((2u * (static_cast<uint32_t>(wkg) & 1u)) << 8), qs1 = qs0 + 0x100u;
+#pragma unroll
+      for (int bl = 0; bl < 8; ++bl) acc[bl] = mfma(aw, dec8_quad(d.vw[bl], lutV, qbase, qs0, qs1), acc[bl]);
       return;
     }
 #pragma unroll
