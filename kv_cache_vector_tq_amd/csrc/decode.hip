@@ -335,7 +335,7 @@ constexpr int kPlanStage = 2048;  // chunk counts kept in LDS (later sequences: 
 
 __device__ void make_plan(const DecodeArgs& a, const KParams& k) {
   __shared__ int nch_s[kPlanStage];
-  __shared__ long long red_s[kSmallThreads / 64];
+  __shared__ unsigned long long sum_s[16];  // one zeroed slot per block sum (at most 9 are taken)
   __shared__ int scan_s[kSmallThreads / 64];
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int B = a.batch, Hkv = k.Hkv, cpp = k.P / 32;
@@ -346,19 +346,20 @@ __device__ void make_plan(const DecodeArgs& a, const KParams& k) {
     const long long n = (C + 31) / 32, cap = static_cast<long long>(a.max_pages) * cpp;
     return static_cast<int>(n < cap ? n : cap);
   };
+  if (tid < 16) sum_s[tid] = 0;
   for (int b = tid; b < B && b < kPlanStage; b += kSmallThreads) nch_s[b] = nch_of(b);
   __syncthreads();
   auto nch = [&](int b) { return b < kPlanStage ? nch_s[b] : nch_of(b); };
+  // sum over the work-group of non-negative v: one LDS add per wave into a
+  // slot of its own, one barrier (the plan is a chain of barriers: each one
+  // saved shortens prep)
+  int nsum = 0;
   auto block_sum = [&](long long v) {
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
-    if (lane == 0) red_s[wv] = v;
+    if (lane == 0) atomicAdd(&sum_s[nsum], static_cast<unsigned long long>(v));
     __syncthreads();
-    long long t = 0;
-#pragma unroll
-    for (int w = 0; w < kSmallThreads / 64; ++w) t += red_s[w];
-    __syncthreads();
-    return t;
+    return static_cast<long long>(sum_s[nsum++]);
   };
   // splits at U chunks per split, all kv heads
   auto count = [&](int U) {
@@ -397,6 +398,7 @@ __device__ void make_plan(const DecodeArgs& a, const KParams& k) {
   __shared__ int first_s[kSmallThreads], sp_s[kSmallThreads];
   int carry = 0;
   for (int b0 = 0; b0 < B; b0 += kSmallThreads) {
+    if (b0 > 0) __syncthreads();  // the previous round is done with first_s, sp_s, scan_s
     const int b = b0 + tid;
     const int n = b < B ? nch(b) : 0;
     const int sp = b < B ? (n > U ? (n + U - 1) / U : 1) : 0;
@@ -434,7 +436,6 @@ __device__ void make_plan(const DecodeArgs& a, const KParams& k) {
       a.plan[j] = make_int4((b0 + lo2) * Hkv + hh, off - hh * spi, spi, U / cpp);
     }
     carry += round;
-    __syncthreads();
   }
   const int total = Hkv * carry;
   if (tid == 0) a.sbase[B * Hkv] = total;
