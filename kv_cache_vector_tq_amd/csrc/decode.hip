@@ -451,8 +451,12 @@ __global__ __launch_bounds__(kSmallThreads) void prep_kernel(DecodeArgs a, DevTa
   __shared__ float qv[GW][kD], qr[GW][kD], part[8][GW][kD];
   __shared__ float ls[GW][kMaxWindow];
   __shared__ float sMw[GW], sLw[GW];
-  if (a.plan && blockIdx.x == gridDim.x - 1) {  // the balanced split plan (one work-group)
-    if (blockIdx.y == 0) make_plan(a, k);
+  // with balanced splits the grid has one more row, the last: its first
+  // work-group computes the plan, the others return at once (sequence b
+  // keeps row b; the plan's work-group, dispatched last, ended prep 3.5 us
+  // sooner at B=16 H_kv=8 than one dispatched among the first)
+  if (a.plan && blockIdx.y == gridDim.y - 1) {
+    if (blockIdx.x == 0) make_plan(a, k);
     return;
   }
   const int nhs = k.G / GW;
@@ -763,8 +767,8 @@ int launch_decode(const tq_ctx* c, const DecodeArgs& a, void* stream) {
   // count per kv head is only known on the device); G = 8 keeps the
   // finalize kernel, whose work-groups take the FP16 window themselves
   as.fuse = valu ? 0 : a.plan ? (k.G <= 4 ? 1 : 0) : (a.splits <= kFuseMaxSplits ? 1 : 0);
-  // (window work-groups only when the scan finalizes; one more for the plan)
-  const dim3 gp((as.fuse ? 2 : 1) * k.Hkv * (k.G / GW) + (a.plan ? 1 : 0), a.batch);
+  // (window work-groups only when the scan finalizes; one more row for the plan)
+  const dim3 gp((as.fuse ? 2 : 1) * k.Hkv * (k.G / GW), a.batch + (a.plan ? 1 : 0));
   switch (GW) {
     case 1: hipLaunchKernelGGL(prep_kernel<1>, gp, dim3(kSmallThreads), 0, s, as, c->t, k, qjl); break;
     case 2: hipLaunchKernelGGL(prep_kernel<2>, gp, dim3(kSmallThreads), 0, s, as, c->t, k, qjl); break;

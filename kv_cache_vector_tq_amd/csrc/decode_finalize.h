@@ -60,8 +60,11 @@ __device__ void finalize_bh(const DecodeArgs& a, const DevTables& t, const KPara
   const int64_t bh = static_cast<int64_t>(b) * k.Hkv + h;
   const int64_t q0 = static_cast<int64_t>(b) * k.Hq + static_cast<int64_t>(h) * k.G + g0;  // first query row
   // this kv head's partial slots: base .. base + S - 1, in split order
-  const int S = a.sbase ? a.sbase[bh + 1] - a.sbase[bh] : a.splits, G = k.G;
+  // (slots outside the plan's are never read)
   const int64_t base = a.sbase ? a.sbase[bh] : bh * a.splits;
+  int S = a.sbase ? a.sbase[bh + 1] - a.sbase[bh] : a.splits;
+  if (a.sbase && (base < 0 || S < 0 || base + S > a.nwg)) S = 0;
+  const int G = k.G;
   const bool dense = k.rotation == TQ_ROT_DENSE;
   auto win_m = [&](int g) { return lw_m ? lw_m[g] : a.wm[q0 + g]; };
   auto win_l = [&](int g) { return lw_l ? lw_l[g] : a.wl[q0 + g]; };

@@ -313,6 +313,8 @@ scan_mfma_kernel(DecodeArgs a, DevTables t, Codebooks cb, KParams k) {
     nsplit = __builtin_amdgcn_readfirstlane(e.z);
     pps = __builtin_amdgcn_readfirstlane(e.w);
     slot = blockIdx.x;
+    // an entry out of range (a plan prep did not write) touches nothing
+    if (b >= a.batch || split < 0 || split >= nsplit || pps < 1 || pps > kMaxSplitPages) return;
   }
   // the wave index is uniform within a wave; saying so keeps page addresses
   // and buffer descriptors in scalar registers

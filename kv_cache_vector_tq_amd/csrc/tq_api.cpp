@@ -103,7 +103,8 @@ struct SplitPlan {
 SplitPlan split_plan(const tq_ctx* c, int batch, int max_pages, int pages_per_split) {
   SplitPlan sp{};
   const long long bh = static_cast<long long>(batch) * c->p.num_kv_heads;
-  sp.balanced = pages_per_split == 0 && max_pages > 0 && (c->p.flags & TQ_FLAG_VALU_SCAN) == 0;
+  // (prep gives the plan a grid row of its own: batch + 1 rows)
+  sp.balanced = pages_per_split == 0 && max_pages > 0 && (c->p.flags & TQ_FLAG_VALU_SCAN) == 0 && batch < 65535;
   sp.splits = decode_splits(batch, c->p.num_kv_heads, max_pages, pages_per_split, c->scan_slots, &sp.pps);
   if (sp.balanced) {
     // every kv head gets at least one split and a split at most
