@@ -333,63 +333,61 @@ __device__ void window_partial(const DecodeArgs& a, const KParams& k, int b, int
 // counts the entries in use.  Run by one work-group of kSmallThreads threads.
 constexpr int kPlanStage = 2048;  // chunk counts kept in LDS (later sequences: read again)
 
+static_assert(kMaxSplitPages == 64, "the plan gives each candidate split size one lane of a wave");
+
 __device__ void make_plan(const DecodeArgs& a, const KParams& k) {
-  __shared__ int nch_s[kPlanStage];
-  __shared__ unsigned long long sum_s[16];  // one zeroed slot per block sum (at most 9 are taken)
+  __shared__ int pg_s[kPlanStage];
+  __shared__ unsigned cnt_s[kSmallThreads / 64][64];
   __shared__ int scan_s[kSmallThreads / 64];
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int B = a.batch, Hkv = k.Hkv, cpp = k.P / 32;
-  // chunks of sequence b, at most the block table's pages (the scan stops there too)
-  auto nch_of = [&](int b) {
+  // pages of 32-token chunks of sequence b, at most the block table's pages
+  // (the scan stops there too).  A split of p pages covers p * cpp chunks, and
+  // ceil(ceil(n / cpp) / p) = ceil(n / (p * cpp)), so split counts follow
+  // from the page counts alone.
+  auto pg_of = [&](int b) {
     const int T = a.seq_lens[b];
     const long long C = T - k.W > 0 ? T - k.W : 0;
     const long long n = (C + 31) / 32, cap = static_cast<long long>(a.max_pages) * cpp;
-    return static_cast<int>(n < cap ? n : cap);
+    return static_cast<int>(((n < cap ? n : cap) + cpp - 1) / cpp);
   };
-  if (tid < 16) sum_s[tid] = 0;
-  for (int b = tid; b < B && b < kPlanStage; b += kSmallThreads) nch_s[b] = nch_of(b);
+  for (int b = tid; b < B && b < kPlanStage; b += kSmallThreads) pg_s[b] = pg_of(b);
   __syncthreads();
-  auto nch = [&](int b) { return b < kPlanStage ? nch_s[b] : nch_of(b); };
-  // sum over the work-group of non-negative v: one LDS add per wave into a
-  // slot of its own, one barrier (the plan is a chain of barriers: each one
-  // saved shortens prep)
-  int nsum = 0;
-  auto block_sum = [&](long long v) {
+  auto pg = [&](int b) { return b < kPlanStage ? pg_s[b] : pg_of(b); };
+  // Every candidate at once: lane l tries splits of p = l + 1 pages, wave w
+  // counts the splits of sequences w, w + 4, ... (one kv head each); one
+  // barrier merges the four waves, and every wave then takes the smallest p
+  // whose splits over all kv heads fit the resident work-groups (a.slots),
+  // else 64 pages.  The count never rises with p, and count(p) >= N / (p *
+  // cpp) for N chunks in all, so this is the smallest fitting split size in
+  // whole pages.  q = ceil(g / p) comes from the fp64 product (g + p - 1) *
+  // (1 / p), whose error is far below 1 / p, with one upward correction for
+  // an exact multiple that lands just under its quotient.
+  {
+    const unsigned p = static_cast<unsigned>(lane) + 1u;
+    const double inv = 1.0 / static_cast<double>(p);
+    constexpr unsigned kSat = 1u << 30;  // counts past any slot count saturate here
+    unsigned c = 0;
+#pragma unroll 4
+    for (int b = wv; b < B; b += kSmallThreads / 64) {
+      const unsigned x = static_cast<unsigned>(pg(b)) + p - 1u;
+      unsigned q = static_cast<unsigned>(static_cast<double>(x) * inv);
+      q += (q + 1u) * p <= x ? 1u : 0u;
+      q = q > 1u ? q : 1u;  // an empty sequence still takes one split
+      c += q < kSat ? q : kSat;
+      c = c < kSat ? c : kSat;
+    }
+    cnt_s[wv][lane] = c;
+  }
+  __syncthreads();
+  int U;
+  {
+    unsigned long long tot = 0;
 #pragma unroll
-    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
-    if (lane == 0) atomicAdd(&sum_s[nsum], static_cast<unsigned long long>(v));
-    __syncthreads();
-    return static_cast<long long>(sum_s[nsum++]);
-  };
-  // splits at U chunks per split, all kv heads
-  auto count = [&](int U) {
-    long long c = 0;
-    for (int b = tid; b < B; b += kSmallThreads) {
-      const int n = nch(b);
-      c += n > U ? (n + U - 1) / U : 1;
-    }
-    return block_sum(c) * Hkv;
-  };
-  long long N = 0;
-  for (int b = tid; b < B; b += kSmallThreads) N += nch(b);
-  N = block_sum(N) * Hkv;
-  const long long S = a.slots;
-  const int hi = kMaxSplitPages * cpp;
-  long long lo0 = (N + S - 1) / S;
-  lo0 = (lo0 + cpp - 1) / cpp * cpp;
-  const int lo = static_cast<int>(lo0 < cpp ? cpp : lo0 > hi ? hi : lo0);
-  int U = hi;
-  if (count(lo) <= S) {
-    U = lo;
-  } else if (count(hi) <= S) {
-    // count(lp * cpp) > S >= count(hp * cpp): bisect in whole pages
-    int lp = lo / cpp, hp = hi / cpp;
-    while (hp - lp > 1) {
-      const int mp = (lp + hp) / 2;
-      if (count(mp * cpp) <= S) hp = mp;
-      else lp = mp;
-    }
-    U = hp * cpp;
+    for (int w = 0; w < kSmallThreads / 64; ++w) tot += cnt_s[w][lane];
+    const unsigned long long fit = __ballot(tot * static_cast<unsigned long long>(Hkv) <=
+                                            static_cast<unsigned long long>(a.slots));
+    U = (fit ? __builtin_ctzll(fit) + 1 : kMaxSplitPages) * cpp;
   }
   // entries, kSmallThreads sequences per round: each thread finds its
   // sequence's first entry (a prefix sum of the split counts), then the
@@ -399,9 +397,9 @@ __device__ void make_plan(const DecodeArgs& a, const KParams& k) {
   int carry = 0;
   for (int b0 = 0; b0 < B; b0 += kSmallThreads) {
     if (b0 > 0) __syncthreads();  // the previous round is done with first_s, sp_s, scan_s
-    const int b = b0 + tid;
-    const int n = b < B ? nch(b) : 0;
-    const int sp = b < B ? (n > U ? (n + U - 1) / U : 1) : 0;
+    const int b = b0 + tid, up = U / cpp;
+    const int g = b < B ? pg(b) : 0;
+    const int sp = b < B ? (g > up ? (g + up - 1) / up : 1) : 0;
     int x = sp;  // inclusive prefix within the wave
 #pragma unroll
     for (int o = 1; o < 64; o <<= 1) {
