@@ -195,10 +195,13 @@ __device__ void window_partial(const DecodeArgs& a, const KParams& k, int b, int
   if (TO_GLOBAL && g0 == 0 && tid == 0) a.ctr[bh] = 0;
   const float c2 = a.sm_scale * kLog2e;
   // window keys: thread pair (tk, half) holds slot tk = tid / 2, coordinates
-  // 64 half .. 64 half + 63 (past d: zero); rows hold d coordinates
+  // 64 half .. 64 half + 63 (past d: zero); rows hold d coordinates.  The
+  // ring has W slots whatever the length, so the loads are bounded by W and
+  // issued at once, beside the length's own load; slots at or past the
+  // length are loaded but never used.
   const int tk0 = tid >> 1, half = tid & 1;
   uint4 kv[8];
-  if (tk0 < nwin) {
+  if (tk0 < k.W) {
     const uint4* kr = reinterpret_cast<const uint4*>(a.k_win + (bh * k.W + tk0) * k.d + 64 * half);
 #pragma unroll
     for (int c = 0; c < 8; ++c) kv[c] = 64 * half + 8 * c < k.d ? kr[c] : make_uint4(0u, 0u, 0u, 0u);
@@ -210,7 +213,7 @@ __device__ void window_partial(const DecodeArgs& a, const KParams& k, int b, int
   uint2 vv[16];
 #pragma unroll
   for (int u = 0; u < 16; ++u)
-    if (q8 + 8 * u < nwin) vv[u] = *reinterpret_cast<const uint2*>(vbase + static_cast<int64_t>(q8 + 8 * u) * k.d);
+    if (q8 + 8 * u < k.W) vv[u] = *reinterpret_cast<const uint2*>(vbase + static_cast<int64_t>(q8 + 8 * u) * k.d);
   // the query rows (d coordinates, scaled to log2 units; zero past d)
   for (int e = tid; e < GW * kD; e += kSmallThreads) {
     const int g = e / kD, i = e % kD;
