@@ -30,8 +30,10 @@
  *    except tq_codebook_init (uploads tables, then synchronises the stream)
  *    and tq_get_status (reads the status word back).  No device memory is
  *    allocated in hot calls.  A tq_ctx is immutable after init apart from its
- *    status word and its profiling slots (tq_profile_begin), so calls on
- *    different streams may share it while profiling is off.
+ *    status word, its profiling slots (tq_profile_begin) and the arrival
+ *    counts of decode-step appends (8 sets, taken in turn, each back at zero
+ *    when its call ends), so calls on different streams may share it while
+ *    profiling is off, with at most 8 appends in flight at once.
  *  - Head size d and transform size D: D is the next power of two >= d.  A
  *    head size that is not a power of two is zero-padded to D for the
  *    rotation and the QJL sketch, and its records hold all D transform
@@ -292,7 +294,12 @@ TQ_API int tq_encode(const tq_ctx* ctx, int kind, const void* x, int dtype, int6
  * id in block_table.  A sequence whose pages or count are invalid is left
  * unchanged and raises a status bit (tq_get_status).  TQ_ERR_INVALID_ARG
  * for null or misaligned pointers (pool 256 bytes, token rows and rings 16
- * bytes) or negative sizes; TQ_ERR_HIP if a launch fails. */
+ * bytes) or negative sizes; TQ_ERR_HIP if a launch fails.  A decode-step
+ * append (n_new <= 4, n_new <= W or W == 0) is one kernel: the last of a
+ * sequence's work-groups commits it, counting arrivals in one of 8 sets of
+ * counters in the context, taken in turn by successive calls; at most 8
+ * append calls on one context may therefore be in flight at once (calls on
+ * one stream never overlap). */
 TQ_API int tq_append_page(const tq_ctx* ctx, uint8_t* page_pool, int64_t num_pages, const int32_t* block_table,
                           int max_pages, int batch, int32_t* seq_lens, const uint16_t* k_new,
                           const uint16_t* v_new, int n_new, const int32_t* new_counts, uint16_t* k_win,

@@ -475,10 +475,18 @@ __device__ inline double sq_norm_quarters(const float (*x)[kD], int l) {
   return s;
 }
 
+// What the commit of sequence b reads: the plan as plan_seq takes it (both
+// per-sequence words, then the ids of the first two pages: a decode step
+// touches one page, at most two).
+struct CommitLoads {
+  int T0, craw, pa, pb;
+};
+
+// The append of one (keys | values, kv head, sequence); cl receives the words
+// a commit of the sequence reads, as this work-group read them.
 template <bool HAD>
-__global__ __launch_bounds__(kSmallThreads) void append_small_kernel(AppendArgs a, DevTables t, Layout L, int W,
-                                                                    int ring) {
-  __shared__ SmallSmem sm;
+__device__ __forceinline__ void append_small_body(const AppendArgs& a, const DevTables& t, const Layout& L, int W,
+                                                  int ring, SmallSmem& sm, CommitLoads& cl) {
   const int tid = threadIdx.x, h = blockIdx.y, b = blockIdx.z;
   const int i = tid & (kD - 1), lane = tid & 63;
   const bool lower = tid < kD;
@@ -492,6 +500,9 @@ __global__ __launch_bounds__(kSmallThreads) void append_small_kernel(AppendArgs 
   const int T0 = a.seq_lens[b];
   int cnt = a.n_new;
   if (a.counts != nullptr) cnt = a.counts[b];
+  cl.T0 = T0;
+  cl.craw = cnt;
+  cl.pa = cl.pb = -1;
   const float cbv = t.cbtab[(key ? 0 : 64) + (tid & 63)];
   const float nt0 = t.ntab[tid], nt1 = t.ntab[kNormCodes + tid];
   if (tid < 64) sm.cbt[tid] = cbv;
@@ -535,6 +546,8 @@ __global__ __launch_bounds__(kSmallThreads) void append_small_kernel(AppendArgs 
     if (pg1 >= a.max_pages) return;
     pid0 = a.block_table[static_cast<int64_t>(b) * a.max_pages + pg0];
     pid1 = a.block_table[static_cast<int64_t>(b) * a.max_pages + pg1];
+    cl.pa = pid0;
+    cl.pb = pid1;  // (the commit takes it only when pg1 = pg0 + 1)
     if (pid0 < 0 || pid0 >= a.num_pages || pid1 < 0 || pid1 >= a.num_pages) return;
   }
   if (nv > 0 && lower) {
@@ -756,6 +769,108 @@ __global__ __launch_bounds__(kSmallThreads) void append_small_kernel(AppendArgs 
   ring_store();
 }
 
+// What the commit writes into page headers besides the layout.
+struct CommitInfo {
+  int rotation;
+  int qjl_code;  // 0 no QJL, 1 Gaussian S, 2 orthogonal S
+  uint64_t seed;
+};
+
+__device__ inline CommitLoads commit_load(const AppendArgs& a, const Layout& L, int W, int b) {
+  CommitLoads cl;
+  cl.T0 = a.seq_lens[b];
+  cl.craw = (a.counts ? a.counts : a.seq_lens)[b];
+  const int c0 = cl.T0 - W > 0 ? cl.T0 - W : 0;
+  const int pg0 = c0 > 0 ? c0 / L.P : 0;
+  const int32_t* bt = a.block_table + static_cast<int64_t>(b) * a.max_pages;
+  cl.pa = pg0 < a.max_pages ? bt[pg0] : -1;
+  cl.pb = pg0 + 1 < a.max_pages ? bt[pg0 + 1] : -1;
+  return cl;
+}
+
+// Commit of sequence b after its tokens are stored (cl: commit_load's words,
+// read before any of them can change): check the count and the page ids as
+// the append took them, rewrite the headers of the pages the append touched
+// and advance seq_lens[b].  A bad count or page raises a status bit and
+// leaves the sequence as it was.  One thread per sequence.
+__device__ inline void commit_store(const AppendArgs& a, const DevTables& t, const Layout& L, int W, CommitInfo ci,
+                                    int b, const CommitLoads& cl) {
+  SeqPlan sp;
+  sp.T0 = cl.T0;
+  sp.cnt = a.counts ? cl.craw : a.n_new;
+  if (sp.cnt < 0 || sp.cnt > a.n_new || sp.T0 < 0) {
+    atomicOr(t.status, TQ_STATUS_BAD_COUNT);
+    return;
+  }
+  const int T1 = sp.T0 + sp.cnt;
+  sp.c0 = sp.T0 - W > 0 ? sp.T0 - W : 0;
+  sp.c1 = T1 - W > 0 ? T1 - W : 0;
+  const int pg0 = sp.c0 / L.P, pg1 = sp.c1 > sp.c0 ? (sp.c1 - 1) / L.P : pg0 - 1;
+  const int32_t* bt = a.block_table + static_cast<int64_t>(b) * a.max_pages;
+  const int pa = cl.pa, pb = cl.pb;
+  bool ok = sp.c1 <= sp.c0 || pg1 < a.max_pages;
+  for (int pg = pg0; ok && pg <= pg1; ++pg) {
+    const int pid = pg == pg0 ? pa : pg == pg0 + 1 ? pb : bt[pg];
+    if (pid < 0 || pid >= a.num_pages) ok = false;
+  }
+  if (!ok) {
+    atomicOr(t.status, TQ_STATUS_BAD_PAGE);
+    return;
+  }
+  if (sp.c1 > sp.c0) {
+    for (int pg = pg0; pg <= pg1; ++pg) {
+      const int pid = pg == pg0 ? pa : pg == pg0 + 1 ? pb : bt[pg];
+      uint32_t* hd = reinterpret_cast<uint32_t*>(a.pool + static_cast<int64_t>(pid) * L.page_bytes);
+      const int valid = sp.c1 - pg * L.P < L.P ? sp.c1 - pg * L.P : L.P;
+      hd[0] = kMagic;
+      hd[1] = 1u | (static_cast<uint32_t>(L.d) << 16);
+      // bits bytes: b, or b + 16 for a mixed-channel rate b + 1/2
+      hd[2] = static_cast<uint32_t>(L.bK + 16 * L.kmix) | (static_cast<uint32_t>(ci.qjl_code) << 8) |
+              (static_cast<uint32_t>(L.bV + 16 * L.vmix) << 16) | (static_cast<uint32_t>(ci.rotation) << 24);
+      hd[3] = static_cast<uint32_t>(L.H) | (static_cast<uint32_t>(L.P) << 16);
+      hd[4] = static_cast<uint32_t>(valid);
+      hd[5] = 1u;
+      hd[6] = static_cast<uint32_t>(ci.seed);
+      hd[7] = static_cast<uint32_t>(ci.seed >> 32);
+      hd[8] = static_cast<uint32_t>(pg);
+      hd[9] = static_cast<uint32_t>(L.kn8);  // byte 36: key norm format
+      for (int i = 10; i < 16; ++i) hd[i] = 0u;
+    }
+  }
+  a.seq_lens[b] = sp.T0 + sp.cnt;
+}
+
+__device__ inline void commit_seq(const AppendArgs& a, const DevTables& t, const Layout& L, int W, CommitInfo ci,
+                                  int b) {
+  commit_store(a, t, L, W, ci, b, commit_load(a, L, W, b));
+}
+
+// One work-group per (keys | values, kv head, sequence) appends at most
+// kSmallNew tokens.  With a.ctr, the last of sequence b's 2 H work-groups to
+// finish also commits it: every work-group counts its arrival once all its
+// threads have read seq_lens[b], so the length is advanced only after its
+// last reader (the count is cleared for the next call).  Without a.ctr a
+// commit kernel follows.
+template <bool HAD>
+__global__ __launch_bounds__(kSmallThreads) void append_small_kernel(AppendArgs a, DevTables t, Layout L, int W,
+                                                                    int ring, CommitInfo ci) {
+  __shared__ SmallSmem sm;
+  const int b = blockIdx.z;
+  // the words the commit reads come from the append's own loads (taken
+  // before any of them can change)
+  CommitLoads cl;
+  append_small_body<HAD>(a, t, L, W, ring, sm, cl);
+  if (a.ctr == nullptr) return;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const int n = 2 * static_cast<int>(gridDim.y);
+    if (__hip_atomic_fetch_add(a.ctr + b, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == n - 1) {
+      __hip_atomic_store(a.ctr + b, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      commit_store(a, t, L, W, ci, b, cl);
+    }
+  }
+}
+
 
 // New tokens that remain among the last W go to the FP16 ring.
 __global__ __launch_bounds__(kThreads) void append_ring_kernel(AppendArgs a, DevTables t, Layout L, int W) {
@@ -774,58 +889,9 @@ __global__ __launch_bounds__(kThreads) void append_ring_kernel(AppendArgs a, Dev
 }
 
 // Advance seq_lens and rewrite the headers of the pages the append touched.
-__global__ void append_commit_kernel(AppendArgs a, DevTables t, Layout L, int W, int rotation, int qjl_code,
-                                     uint64_t seed) {
-  for (int b = blockIdx.x * blockDim.x + threadIdx.x; b < a.batch; b += gridDim.x * blockDim.x) {
-    // the plan as plan_seq takes it, with its loads issued together: both
-    // per-sequence words, then the ids of the first two pages (a decode step
-    // touches one page, at most two)
-    SeqPlan sp;
-    sp.T0 = a.seq_lens[b];
-    const int craw = (a.counts ? a.counts : a.seq_lens)[b];
-    sp.cnt = a.counts ? craw : a.n_new;
-    if (sp.cnt < 0 || sp.cnt > a.n_new || sp.T0 < 0) {
-      atomicOr(t.status, TQ_STATUS_BAD_COUNT);
-      continue;
-    }
-    const int T1 = sp.T0 + sp.cnt;
-    sp.c0 = sp.T0 - W > 0 ? sp.T0 - W : 0;
-    sp.c1 = T1 - W > 0 ? T1 - W : 0;
-    const int pg0 = sp.c0 / L.P, pg1 = sp.c1 > sp.c0 ? (sp.c1 - 1) / L.P : pg0 - 1;
-    const int32_t* bt = a.block_table + static_cast<int64_t>(b) * a.max_pages;
-    const int pa = pg0 < a.max_pages ? bt[pg0] : -1;
-    const int pb = pg0 + 1 < a.max_pages ? bt[pg0 + 1] : -1;
-    bool ok = sp.c1 <= sp.c0 || pg1 < a.max_pages;
-    for (int pg = pg0; ok && pg <= pg1; ++pg) {
-      const int pid = pg == pg0 ? pa : pg == pg0 + 1 ? pb : bt[pg];
-      if (pid < 0 || pid >= a.num_pages) ok = false;
-    }
-    if (!ok) {
-      atomicOr(t.status, TQ_STATUS_BAD_PAGE);
-      continue;
-    }
-    if (sp.c1 > sp.c0) {
-      for (int pg = pg0; pg <= pg1; ++pg) {
-        const int pid = pg == pg0 ? pa : pg == pg0 + 1 ? pb : bt[pg];
-        uint32_t* hd = reinterpret_cast<uint32_t*>(a.pool + static_cast<int64_t>(pid) * L.page_bytes);
-        const int valid = sp.c1 - pg * L.P < L.P ? sp.c1 - pg * L.P : L.P;
-        hd[0] = kMagic;
-        hd[1] = 1u | (static_cast<uint32_t>(L.d) << 16);
-        // bits bytes: b, or b + 16 for a mixed-channel rate b + 1/2
-        hd[2] = static_cast<uint32_t>(L.bK + 16 * L.kmix) | (static_cast<uint32_t>(qjl_code) << 8) |
-                (static_cast<uint32_t>(L.bV + 16 * L.vmix) << 16) | (static_cast<uint32_t>(rotation) << 24);
-        hd[3] = static_cast<uint32_t>(L.H) | (static_cast<uint32_t>(L.P) << 16);
-        hd[4] = static_cast<uint32_t>(valid);
-        hd[5] = 1u;
-        hd[6] = static_cast<uint32_t>(seed);
-        hd[7] = static_cast<uint32_t>(seed >> 32);
-        hd[8] = static_cast<uint32_t>(pg);
-        hd[9] = static_cast<uint32_t>(L.kn8);  // byte 36: key norm format
-        for (int i = 10; i < 16; ++i) hd[i] = 0u;
-      }
-    }
-    a.seq_lens[b] = sp.T0 + sp.cnt;
-  }
+__global__ void append_commit_kernel(AppendArgs a, DevTables t, Layout L, int W, CommitInfo ci) {
+  for (int b = blockIdx.x * blockDim.x + threadIdx.x; b < a.batch; b += gridDim.x * blockDim.x)
+    commit_seq(a, t, L, W, ci, b);
 }
 
 }  // namespace
@@ -859,13 +925,24 @@ int launch_append(const tq_ctx* c, const AppendArgs& a, void* stream) {
   // the ring update rides along when no slot can be read and written by
   // different work-groups (at most W new tokens)
   int ring = (W > 0 && a.n_new <= W) ? 1 : 0;
+  // header byte: 0 no QJL, 1 Gaussian S, 2 orthogonal S
+  const CommitInfo ci{c->p.rotation, c->p.key_qjl ? 1 + c->p.qjl_kind : 0, c->p.seed};
   if (a.n_new <= kSmallNew) {
-    // decode steps: one work-group per (sequence, kv head, keys|values)
+    // decode steps: one work-group per (sequence, kv head, keys|values); with
+    // the ring updated here too (or no ring), the last work-group of each
+    // sequence commits it, with the next set of arrival counts
+    AppendArgs as = a;
+    if ((ring || W == 0) && a.batch <= kAppendMaxBatch && c->append_ctr) {
+      const unsigned slot = c->append_calls.fetch_add(1u, std::memory_order_relaxed) % kAppendSlots;
+      as.ctr = c->append_ctr + static_cast<int64_t>(slot) * kAppendMaxBatch;
+    }
     const dim3 grid(2, L.H, a.batch);
     if (had)
-      hipLaunchKernelGGL(append_small_kernel<true>, grid, dim3(kSmallThreads), 0, s, a, c->t, L, W, ring);
+      hipLaunchKernelGGL(append_small_kernel<true>, grid, dim3(kSmallThreads), 0, s, as, c->t, L, W, ring, ci);
     else
-      hipLaunchKernelGGL(append_small_kernel<false>, grid, dim3(kSmallThreads), 0, s, a, c->t, L, W, ring);
+      hipLaunchKernelGGL(append_small_kernel<false>, grid, dim3(kSmallThreads), 0, s, as, c->t, L, W, ring, ci);
+    if (hipGetLastError() != hipSuccess) return 1;
+    if (as.ctr) return 0;
   } else {
     // bulk: the matrix-core append for the kinds it takes (every rate with a
     // symmetric codebook), the vector-ALU one for the rest and under
@@ -894,10 +971,7 @@ int launch_append(const tq_ctx* c, const AppendArgs& a, void* stream) {
     if (hipGetLastError() != hipSuccess) return 1;
   }
   const int cb = (a.batch + 255) / 256;
-  // header byte: 0 no QJL, 1 Gaussian S, 2 orthogonal S
-  const int qjl_code = c->p.key_qjl ? 1 + c->p.qjl_kind : 0;
-  hipLaunchKernelGGL(append_commit_kernel, dim3(cb), dim3(256), 0, s, a, c->t, L, W, c->p.rotation, qjl_code,
-                     c->p.seed);
+  hipLaunchKernelGGL(append_commit_kernel, dim3(cb), dim3(256), 0, s, a, c->t, L, W, ci);
   return hipGetLastError() == hipSuccess ? 0 : 1;
 }
 

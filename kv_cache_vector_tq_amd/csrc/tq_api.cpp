@@ -305,7 +305,8 @@ int init_ctx(tq_ctx** out, const tq_params* p, const float* rot_in, const float*
                                : q == tq::kNormCodes - 1 ? std::numeric_limits<float>::infinity()
                                                          : static_cast<float>(std::exp2((q + 0.5) / 16.0 - 4.0));
   }
-  const size_t total = 6 * mat + sizeof(cbtab) + sizeof(ntab) + 256;
+  const size_t ctr_bytes = sizeof(int) * static_cast<size_t>(tq::kAppendSlots) * tq::kAppendMaxBatch;
+  const size_t total = 6 * mat + sizeof(cbtab) + sizeof(ntab) + 256 + ctr_bytes;
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (hipGetDevice(&c->device) != hipSuccess || hipMalloc(&c->dmem, total) != hipSuccess) {
     delete c;
@@ -321,6 +322,7 @@ int init_ctx(tq_ctx** out, const tq_params* p, const float* rot_in, const float*
   c->t.cbtab = reinterpret_cast<float*>(base + 6 * mat);
   c->t.ntab = reinterpret_cast<float*>(base + 6 * mat + sizeof(cbtab));
   c->t.status = reinterpret_cast<int*>(base + 6 * mat + sizeof(cbtab) + sizeof(ntab));
+  c->append_ctr = reinterpret_cast<int*>(base + 6 * mat + sizeof(cbtab) + sizeof(ntab) + 256);
   bool ok = hipMemcpyAsync(base, rot.data(), mat, hipMemcpyHostToDevice, s) == hipSuccess &&
             hipMemcpyAsync(base + mat, rotT.data(), mat, hipMemcpyHostToDevice, s) == hipSuccess &&
             hipMemcpyAsync(base + 2 * mat, S.data(), mat, hipMemcpyHostToDevice, s) == hipSuccess &&
@@ -329,7 +331,7 @@ int init_ctx(tq_ctx** out, const tq_params* p, const float* rot_in, const float*
             hipMemcpyAsync(base + 5 * mat, S4.data(), mat, hipMemcpyHostToDevice, s) == hipSuccess &&
             hipMemcpyAsync(base + 6 * mat, cbtab, sizeof(cbtab), hipMemcpyHostToDevice, s) == hipSuccess &&
             hipMemcpyAsync(base + 6 * mat + sizeof(cbtab), ntab, sizeof(ntab), hipMemcpyHostToDevice, s) == hipSuccess &&
-            hipMemsetAsync(base + 6 * mat + sizeof(cbtab) + sizeof(ntab), 0, 256, s) == hipSuccess &&
+            hipMemsetAsync(base + 6 * mat + sizeof(cbtab) + sizeof(ntab), 0, 256 + ctr_bytes, s) == hipSuccess &&
             hipStreamSynchronize(s) == hipSuccess;
   // resident scan work-groups per device, for the automatic split count
   const bool valu = (p->flags & TQ_FLAG_VALU_SCAN) != 0;

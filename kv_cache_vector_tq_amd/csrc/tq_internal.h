@@ -3,6 +3,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <cstdint>
 #include <vector>
 
@@ -151,7 +152,16 @@ struct AppendArgs {
   const int32_t* counts;
   uint16_t* k_win;
   uint16_t* v_win;
+  // per-sequence arrival counts of the one-token append that commits itself
+  // (null: a commit kernel follows)
+  int* ctr = nullptr;
 };
+
+// Arrival counts of the self-committing append: kAppendSlots sets of one
+// count per sequence (batch <= 65535), taken in turn by successive calls,
+// each count back at zero once its sequence is committed.
+constexpr int kAppendSlots = 8;
+constexpr int kAppendMaxBatch = 65536;
 
 struct DecodeArgs {
   const void* q;
@@ -236,4 +246,8 @@ struct tq_ctx {
   // scan work-groups resident at once on the device (compute units x
   // work-groups per unit); the automatic split count fills one such round
   int scan_slots = 0;
+  // the self-committing append's counts (kAppendSlots x kAppendMaxBatch, in
+  // dmem) and the call counter that picks their set
+  int* append_ctr = nullptr;
+  mutable std::atomic<unsigned> append_calls{0};
 };

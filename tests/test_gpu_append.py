@@ -323,3 +323,49 @@ def test_matrix_core_append_matches_vector_alu_append(name, kw, lens, extra):
     _records_match(s, g, k, v, total)
     _compare_caches(s, ref, devs[0]["pool"].cpu().numpy(), devs[0]["k_win"].cpu().view(torch.int16).numpy().view(np.uint16),
                     devs[0]["v_win"].cpu().view(torch.int16).numpy().view(np.uint16), devs[0]["seq_lens"].cpu().numpy())
+
+
+@pytest.mark.parametrize("W", [0, 8])
+def test_one_token_appends_commit_themselves(W):
+    """Decode-step appends commit themselves (the last work-group of each
+    sequence advances its length and rewrites its page headers), over more
+    calls than there are sets of arrival counts, and equal one bulk append
+    of the same tokens.  A sequence whose next page is invalid stops there
+    with a status bit while the others go on; a count of 0 leaves a
+    sequence as it was."""
+    print(f"case self-committing one-token appends W={W}", flush=True)
+    s = Setup(Hq=2, Hkv=2, W=W, P=32)
+    B, T = 3, 60
+    k, v = fill(s, s.cache(B, T), [T] * B)
+    ctx = context_for(s)
+    dev = upload_cache(s.cache(B, T))
+    dev["block_table"][1, 1] = -1  # sequence 1 cannot store past its first page
+    stop1 = s.P + W  # its length once the next token would leave the window into page 1
+    taken = [0] * B
+    for t in range(T):
+        cnt = [1, 1, 0 if t % 3 == 2 else 1]
+        kk = np.zeros((B, s.Hkv, 1, s.d), np.float16)
+        vv = np.zeros((B, s.Hkv, 1, s.d), np.float16)
+        for b in range(B):
+            kk[b, :, 0] = k[b, :, min(taken[b], T - 1)]
+            vv[b, :, 0] = v[b, :, min(taken[b], T - 1)]
+        _gpu_append(ctx, dev, kk, vv, counts=cnt)
+        for b in range(B):
+            if cnt[b] and not (b == 1 and taken[1] >= stop1):
+                taken[b] += 1
+    torch.cuda.synchronize()
+    lens = [int(x) for x in dev["seq_lens"].cpu().numpy()]
+    assert lens == [T, stop1, taken[2]] and taken[2] < T
+    assert tqa.tq_get_status(ctx) == tqa.TQ_STATUS_BAD_PAGE
+    # the same tokens in one bulk append (its own commit kernel)
+    ref = upload_cache(s.cache(B, T))
+    _gpu_append(ctx, ref, k, v, counts=lens)
+    torch.cuda.synchronize()
+    for key in ("k_win", "v_win", "seq_lens"):
+        assert torch.equal(dev[key].cpu(), ref[key].cpu()), key
+    g1, g2 = _host_cache(s, dev, B, T), _host_cache(s, ref, B, T)
+    for b in range(B):
+        for pg in range(-(-max(lens[b] - W, 0) // s.P)):
+            pid = int(g2.block_table[b, pg])
+            assert np.array_equal(g1.pool[pid, :64], g2.pool[pid, :64]), (b, pg)  # headers
+    _records_match(s, (g1, g2), k, v, lens)
