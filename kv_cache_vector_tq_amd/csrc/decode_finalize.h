@@ -51,18 +51,21 @@ __device__ inline bool arrive_last(int* ctr, int splits, int* flag) {
 // wrote it), or with lw_m non-null from LDS (lw_m, lw_l [GW], lw_acc
 // [GW][kD]: the finalize kernel took the window itself).  Every load of a
 // step is issued before any is used: empty splits hold zero accumulators
-// and get factor 0, so they are read like the others.
+// and get factor 0, so they are read like the others.  base_in >= 0 gives
+// the kv head's first partial slot and S_in its split count (a scan
+// work-group knows both from its own plan entry); else they are read.
 template <int NT, int GW>
 __device__ void finalize_bh(const DecodeArgs& a, const DevTables& t, const KParams& k, int b, int h, int g0,
                             float (*acc)[kD], float* fin, float* sL, float* sW, const float* lw_m = nullptr,
-                            const float* lw_l = nullptr, const float (*lw_acc)[kD] = nullptr) {
+                            const float* lw_l = nullptr, const float (*lw_acc)[kD] = nullptr,
+                            int64_t base_in = -1, int S_in = 0) {
   const int tid = threadIdx.x;
   const int64_t bh = static_cast<int64_t>(b) * k.Hkv + h;
   const int64_t q0 = static_cast<int64_t>(b) * k.Hq + static_cast<int64_t>(h) * k.G + g0;  // first query row
   // this kv head's partial slots: base .. base + S - 1, in split order
   // (slots outside the plan's are never read)
-  const int64_t base = a.sbase ? a.sbase[bh] : bh * a.splits;
-  int S = a.sbase ? a.sbase[bh + 1] - a.sbase[bh] : a.splits;
+  const int64_t base = base_in >= 0 ? base_in : a.sbase ? a.sbase[bh] : bh * a.splits;
+  int S = base_in >= 0 ? S_in : a.sbase ? a.sbase[bh + 1] - a.sbase[bh] : a.splits;
   if (a.sbase && (base < 0 || S < 0 || base + S > a.nwg)) S = 0;
   const int G = k.G;
   const bool dense = k.rotation == TQ_ROT_DENSE;

@@ -365,8 +365,8 @@ scan_mfma_kernel(DecodeArgs a, DevTables t, Codebooks cb, KParams k) {
     }
     for (int i = tid; i < G * kD; i += kThreads) a.pacc[pidx * kD + i] = 0.0f;
     if (a.fuse && arrive_last<kThreads>(a.ctr + static_cast<int64_t>(b) * k.Hkv + h, nsplit, &fflag))
-      finalize_bh<kThreads, G>(a, t, k, b, h, 0, red, endbuf, fsm[0],
-                               fsm[1]);
+      finalize_bh<kThreads, G>(a, t, k, b, h, 0, red, endbuf, fsm[0], fsm[1], nullptr, nullptr, nullptr,
+                               slot - split, nsplit);
     return;
   }
   // codebooks to LDS (no dynamic indexing of kernel arguments), then the tables
@@ -777,21 +777,21 @@ scan_mfma_kernel(DecodeArgs a, DevTables t, Codebooks cb, KParams k) {
     // the slots are the table memory, the tables are not read any more: all
     // waves have passed the barrier above), then each element is summed over
     // the waves in order 0 .. kWaves-1
-    float* slot = endbuf;
+    float* wslot = endbuf;
 #pragma unroll
     for (int i2 = 0; i2 < 2; ++i2) {
       const int g = 2 * kg + i2;
       if (g < G) {
 #pragma unroll
         for (int bl = 0; bl < 8; ++bl)
-          slot[(wave * G + g) * kD + 8 * n + bl] = (acc[bl][i2] + acc[bl][i2 + 2]) * fac[i2];
+          wslot[(wave * G + g) * kD + 8 * n + bl] = (acc[bl][i2] + acc[bl][i2 + 2]) * fac[i2];
       }
     }
     __syncthreads();
     for (int e = tid; e < G * kD; e += kThreads) {
-      float v = slot[e];
+      float v = wslot[e];
 #pragma unroll
-      for (int w = 1; w < kWaves; ++w) v += slot[w * G * kD + e];
+      for (int w = 1; w < kWaves; ++w) v += wslot[w * G * kD + e];
       a.pacc[pidx * kD + e] = v;
     }
   }
@@ -810,8 +810,8 @@ scan_mfma_kernel(DecodeArgs a, DevTables t, Codebooks cb, KParams k) {
   // combines every split's partial with the window's and writes the output
   // rows; otherwise the finalize kernel does
   if (a.fuse && arrive_last<kThreads>(a.ctr + static_cast<int64_t>(b) * k.Hkv + h, nsplit, &fflag))
-    finalize_bh<kThreads, G>(a, t, k, b, h, 0, red, endbuf, fsm[0],
-                             fsm[1]);
+    finalize_bh<kThreads, G>(a, t, k, b, h, 0, red, endbuf, fsm[0], fsm[1], nullptr, nullptr, nullptr,
+                             slot - split, nsplit);
 }
 
 template <int G, int BK, int BV, bool KMIX, bool VMIX>
