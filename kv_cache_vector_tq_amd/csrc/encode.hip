@@ -776,20 +776,28 @@ struct CommitInfo {
   uint64_t seed;
 };
 
-__device__ inline CommitLoads commit_load(const AppendArgs& a, const Layout& L, int W, int b) {
-  CommitLoads cl;
-  cl.T0 = a.seq_lens[b];
-  cl.craw = (a.counts ? a.counts : a.seq_lens)[b];
-  const int c0 = cl.T0 - W > 0 ? cl.T0 - W : 0;
-  const int pg0 = c0 > 0 ? c0 / L.P : 0;
-  const int32_t* bt = a.block_table + static_cast<int64_t>(b) * a.max_pages;
-  cl.pa = pg0 < a.max_pages ? bt[pg0] : -1;
-  cl.pb = pg0 + 1 < a.max_pages ? bt[pg0 + 1] : -1;
-  return cl;
+// Words 4j .. 4j+3 of the 64-byte header of page pg (valid tokens `valid`).
+__device__ inline uint4 header_words(const Layout& L, CommitInfo ci, int pg, int valid, int j) {
+  switch (j) {
+    case 0:
+      // bits bytes: b, or b + 16 for a mixed-channel rate b + 1/2
+      return make_uint4(kMagic, 1u | (static_cast<uint32_t>(L.d) << 16),
+                        static_cast<uint32_t>(L.bK + 16 * L.kmix) | (static_cast<uint32_t>(ci.qjl_code) << 8) |
+                            (static_cast<uint32_t>(L.bV + 16 * L.vmix) << 16) |
+                            (static_cast<uint32_t>(ci.rotation) << 24),
+                        static_cast<uint32_t>(L.H) | (static_cast<uint32_t>(L.P) << 16));
+    case 1:
+      return make_uint4(static_cast<uint32_t>(valid), 1u, static_cast<uint32_t>(ci.seed),
+                        static_cast<uint32_t>(ci.seed >> 32));
+    case 2:
+      return make_uint4(static_cast<uint32_t>(pg), static_cast<uint32_t>(L.kn8), 0u, 0u);  // byte 36: key norm format
+    default:
+      return make_uint4(0u, 0u, 0u, 0u);
+  }
 }
 
-// Commit of sequence b after its tokens are stored (cl: commit_load's words,
-// read before any of them can change): check the count and the page ids as
+// Commit of sequence b after its tokens are stored (cl: the words the append
+// read, before any of them can change): check the count and the page ids as
 // the append took them, rewrite the headers of the pages the append touched
 // and advance seq_lens[b].  A bad count or page raises a status bit and
 // leaves the sequence as it was.  One thread per sequence.
@@ -820,29 +828,13 @@ __device__ inline void commit_store(const AppendArgs& a, const DevTables& t, con
   if (sp.c1 > sp.c0) {
     for (int pg = pg0; pg <= pg1; ++pg) {
       const int pid = pg == pg0 ? pa : pg == pg0 + 1 ? pb : bt[pg];
-      uint32_t* hd = reinterpret_cast<uint32_t*>(a.pool + static_cast<int64_t>(pid) * L.page_bytes);
+      uint4* hd = reinterpret_cast<uint4*>(a.pool + static_cast<int64_t>(pid) * L.page_bytes);
       const int valid = sp.c1 - pg * L.P < L.P ? sp.c1 - pg * L.P : L.P;
-      hd[0] = kMagic;
-      hd[1] = 1u | (static_cast<uint32_t>(L.d) << 16);
-      // bits bytes: b, or b + 16 for a mixed-channel rate b + 1/2
-      hd[2] = static_cast<uint32_t>(L.bK + 16 * L.kmix) | (static_cast<uint32_t>(ci.qjl_code) << 8) |
-              (static_cast<uint32_t>(L.bV + 16 * L.vmix) << 16) | (static_cast<uint32_t>(ci.rotation) << 24);
-      hd[3] = static_cast<uint32_t>(L.H) | (static_cast<uint32_t>(L.P) << 16);
-      hd[4] = static_cast<uint32_t>(valid);
-      hd[5] = 1u;
-      hd[6] = static_cast<uint32_t>(ci.seed);
-      hd[7] = static_cast<uint32_t>(ci.seed >> 32);
-      hd[8] = static_cast<uint32_t>(pg);
-      hd[9] = static_cast<uint32_t>(L.kn8);  // byte 36: key norm format
-      for (int i = 10; i < 16; ++i) hd[i] = 0u;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) hd[j] = header_words(L, ci, pg, valid, j);
     }
   }
   a.seq_lens[b] = sp.T0 + sp.cnt;
-}
-
-__device__ inline void commit_seq(const AppendArgs& a, const DevTables& t, const Layout& L, int W, CommitInfo ci,
-                                  int b) {
-  commit_store(a, t, L, W, ci, b, commit_load(a, L, W, b));
 }
 
 // One work-group per (keys | values, kv head, sequence) appends at most
@@ -872,26 +864,78 @@ __global__ __launch_bounds__(kSmallThreads) void append_small_kernel(AppendArgs 
 }
 
 
-// New tokens that remain among the last W go to the FP16 ring.
+// New tokens that remain among the last W go to the FP16 ring, when the
+// append of the sequence is valid (its count, and every page it touched:
+// checked by all threads at once).  Rows of d fp16 values (d a multiple of
+// 8) move as 16-byte pieces spread over the threads.
 __global__ __launch_bounds__(kThreads) void append_ring_kernel(AppendArgs a, DevTables t, Layout L, int W) {
   const int tid = threadIdx.x, h = blockIdx.x, b = blockIdx.y;
-  const SeqPlan sp = plan_seq(a, L, W, b, t.status, false);
-  if (!sp.ok) return;
+  const int T0 = a.seq_lens[b];
+  const int cnt = a.counts ? a.counts[b] : a.n_new;
+  bool ok = !(cnt < 0 || cnt > a.n_new || T0 < 0);
+  const int c0 = T0 - W > 0 ? T0 - W : 0;
+  const int c1 = T0 + cnt - W > 0 ? T0 + cnt - W : 0;
+  if (ok && c1 > c0) {
+    const int pg0 = c0 / L.P, pg1 = (c1 - 1) / L.P;
+    ok = pg1 < a.max_pages;
+    for (int pg = pg0 + tid; ok && pg <= pg1; pg += kThreads) {
+      const int pid = a.block_table[static_cast<int64_t>(b) * a.max_pages + pg];
+      if (pid < 0 || pid >= a.num_pages) ok = false;
+    }
+  }
+  if (!__syncthreads_and(ok)) return;
   const int64_t bh = static_cast<int64_t>(b) * L.H + h;
-  const int j0 = sp.cnt > W ? sp.cnt - W : 0;
-  const int d = L.d;  // rows hold d coordinates
-  if (tid >= d) return;
-  for (int j = j0; j < sp.cnt; ++j) {
-    const int pos = sp.T0 + j;
-    a.k_win[(bh * W + pos % W) * d + tid] = a.k_new[(bh * a.n_new + j) * d + tid];
-    a.v_win[(bh * W + pos % W) * d + tid] = a.v_new[(bh * a.n_new + j) * d + tid];
+  const int j0 = cnt > W ? cnt - W : 0;
+  const int r16 = L.d / 8;  // 16-byte pieces per row
+  const uint4* kn = reinterpret_cast<const uint4*>(a.k_new);
+  const uint4* vn = reinterpret_cast<const uint4*>(a.v_new);
+  uint4* kw = reinterpret_cast<uint4*>(a.k_win);
+  uint4* vw = reinterpret_cast<uint4*>(a.v_win);
+  for (int e = tid; e < (cnt - j0) * r16; e += kThreads) {
+    const int j = j0 + e / r16, c = e % r16;
+    const int64_t dst = (bh * W + (T0 + j) % W) * r16 + c, src = (bh * a.n_new + j) * r16 + c;
+    kw[dst] = kn[src];
+    vw[dst] = vn[src];
   }
 }
 
-// Advance seq_lens and rewrite the headers of the pages the append touched.
-__global__ void append_commit_kernel(AppendArgs a, DevTables t, Layout L, int W, CommitInfo ci) {
-  for (int b = blockIdx.x * blockDim.x + threadIdx.x; b < a.batch; b += gridDim.x * blockDim.x)
-    commit_seq(a, t, L, W, ci, b);
+// Commit after a bulk append, one work-group per sequence b: check the
+// count and every page id the append took, then rewrite the headers of those
+// pages (four 16-byte stores each, spread over the threads) and advance
+// seq_lens[b].  A bad count or page raises a status bit and leaves the
+// sequence as it was.
+constexpr int kCommitThreads = 256;
+
+__global__ __launch_bounds__(kCommitThreads) void append_commit_kernel(AppendArgs a, DevTables t, Layout L, int W,
+                                                                      CommitInfo ci) {
+  const int b = blockIdx.x, tid = threadIdx.x;
+  const int T0 = a.seq_lens[b];
+  const int cnt = a.counts ? a.counts[b] : a.n_new;
+  const bool bad_count = cnt < 0 || cnt > a.n_new || T0 < 0;
+  const int T1 = T0 + cnt;
+  const int c0 = T0 - W > 0 ? T0 - W : 0;
+  const int c1 = T1 - W > 0 ? T1 - W : 0;
+  const int pg0 = c0 / L.P, pg1 = c1 > c0 ? (c1 - 1) / L.P : pg0 - 1;
+  const int32_t* bt = a.block_table + static_cast<int64_t>(b) * a.max_pages;
+  bool ok = !bad_count && (c1 <= c0 || pg1 < a.max_pages);
+  for (int pg = pg0 + tid; ok && pg <= pg1; pg += kCommitThreads) {
+    const int pid = bt[pg];
+    if (pid < 0 || pid >= a.num_pages) ok = false;
+  }
+  // (every thread has read seq_lens[b] before this barrier)
+  ok = __syncthreads_and(ok) != 0;
+  if (!ok) {
+    if (tid == 0) atomicOr(t.status, bad_count ? TQ_STATUS_BAD_COUNT : TQ_STATUS_BAD_PAGE);
+    return;
+  }
+  const int nw = c1 > c0 ? (pg1 - pg0 + 1) * 4 : 0;
+  for (int e = tid; e < nw; e += kCommitThreads) {
+    const int pg = pg0 + (e >> 2), j = e & 3;
+    const int valid = c1 - pg * L.P < L.P ? c1 - pg * L.P : L.P;
+    reinterpret_cast<uint4*>(a.pool + static_cast<int64_t>(bt[pg]) * L.page_bytes)[j] =
+        header_words(L, ci, pg, valid, j);
+  }
+  if (tid == 0) a.seq_lens[b] = T1;
 }
 
 }  // namespace
@@ -970,8 +1014,7 @@ int launch_append(const tq_ctx* c, const AppendArgs& a, void* stream) {
     hipLaunchKernelGGL(append_ring_kernel, dim3(L.H, a.batch), dim3(kThreads), 0, s, a, c->t, L, W);
     if (hipGetLastError() != hipSuccess) return 1;
   }
-  const int cb = (a.batch + 255) / 256;
-  hipLaunchKernelGGL(append_commit_kernel, dim3(cb), dim3(256), 0, s, a, c->t, L, W, ci);
+  hipLaunchKernelGGL(append_commit_kernel, dim3(a.batch), dim3(kCommitThreads), 0, s, a, c->t, L, W, ci);
   return hipGetLastError() == hipSuccess ? 0 : 1;
 }
 
