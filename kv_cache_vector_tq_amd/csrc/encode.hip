@@ -284,29 +284,26 @@ struct SeqPlan {
   bool ok;
 };
 
-__device__ inline SeqPlan plan_seq(const AppendArgs& a, const Layout& L, int W, int b, int* status, bool report) {
+// Called by every thread of the work-group (it ends with a barrier): the
+// page ids are checked by all threads at once, since a check that stops at
+// the first bad page waits a round trip per page.
+__device__ inline SeqPlan plan_seq(const AppendArgs& a, const Layout& L, int W, int b) {
   SeqPlan s;
   s.T0 = a.seq_lens[b];
   s.cnt = a.counts ? a.counts[b] : a.n_new;
-  s.ok = true;
-  if (s.cnt < 0 || s.cnt > a.n_new || s.T0 < 0) {
-    s.ok = false;
-    if (report) atomicOr(status, TQ_STATUS_BAD_COUNT);
-    s.c0 = s.c1 = 0;
-    return s;
-  }
+  bool ok = !(s.cnt < 0 || s.cnt > a.n_new || s.T0 < 0);
   const int T1 = s.T0 + s.cnt;
-  s.c0 = s.T0 - W > 0 ? s.T0 - W : 0;
-  s.c1 = T1 - W > 0 ? T1 - W : 0;
-  if (s.c1 > s.c0) {
+  s.c0 = ok && s.T0 - W > 0 ? s.T0 - W : 0;
+  s.c1 = ok && T1 - W > 0 ? T1 - W : 0;
+  if (ok && s.c1 > s.c0) {
     const int pg0 = s.c0 / L.P, pg1 = (s.c1 - 1) / L.P;
-    if (pg1 >= a.max_pages) s.ok = false;
-    for (int pg = pg0; s.ok && pg <= pg1; ++pg) {
+    ok = pg1 < a.max_pages;
+    for (int pg = pg0 + static_cast<int>(threadIdx.x); ok && pg <= pg1; pg += static_cast<int>(blockDim.x)) {
       const int pid = a.block_table[static_cast<int64_t>(b) * a.max_pages + pg];
-      if (pid < 0 || pid >= a.num_pages) s.ok = false;
+      if (pid < 0 || pid >= a.num_pages) ok = false;
     }
-    if (!s.ok && report) atomicOr(status, TQ_STATUS_BAD_PAGE);
   }
+  s.ok = __syncthreads_and(ok) != 0;
   return s;
 }
 
@@ -420,7 +417,7 @@ __global__ __launch_bounds__(kThreads) void append_encode_kernel(AppendArgs a, D
   __shared__ Smem sm;
   const int tid = threadIdx.x, h = blockIdx.y, b = blockIdx.z;
   // every work-group of b evaluates the same plan; the commit kernel reports
-  const SeqPlan sp = plan_seq(a, L, W, b, t.status, false);
+  const SeqPlan sp = plan_seq(a, L, W, b);
   if (!sp.ok) return;
   const int kv = static_cast<int>(blockIdx.x & 1u);  // 0: keys, 1: values
   const int gr = static_cast<int>(blockIdx.x >> 1);
