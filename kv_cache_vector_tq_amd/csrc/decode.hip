@@ -40,6 +40,25 @@ constexpr int kSmallThreads = 256;
 constexpr int kPrepGroups = 128;  // fewest prep work-groups (of each kind) before heads are spread out
 constexpr int kPrepMaxHeads = 4;  // most query heads per prep work-group
 
+typedef _Float16 win_h8 __attribute__((ext_vector_type(8)));
+typedef float win_f4 __attribute__((ext_vector_type(4)));
+typedef uint32_t win_u4 __attribute__((ext_vector_type(4)));
+
+// D = A B + C, A 16x32 and B 32x16 fp16 (eight per lane), C and D fp32
+__device__ inline win_f4 win_mfma(win_u4 a, win_u4 b, win_f4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(win_h8, a), __builtin_bit_cast(win_h8, b), c, 0,
+                                                 0, 0);
+}
+
+// two floats as fp16 pairs: part 0 rounded to fp16, part 1 the remainder
+__device__ inline uint32_t win_pack(float x0, float x1, int part) {
+  const _Float16 h0 = static_cast<_Float16>(x0), h1 = static_cast<_Float16>(x1);
+  const _Float16 r0 = part ? static_cast<_Float16>(x0 - static_cast<float>(h0)) : h0;
+  const _Float16 r1 = part ? static_cast<_Float16>(x1 - static_cast<float>(h1)) : h1;
+  return static_cast<uint32_t>(__builtin_bit_cast(uint16_t, r0)) |
+         (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, r1)) << 16);
+}
+
 // y[g][i] = sum_j M[j*kD + i] x[g][j] for the G vectors x (LDS), M a kD x kD
 // row-major table in global memory.  Thread (c, r) owns columns 4c..4c+3 and
 // rows 16r..16r+15: its 16 float4 loads (load_cols, issued early by the
@@ -194,18 +213,27 @@ __device__ void window_partial(const DecodeArgs& a, const KParams& k, int b, int
   const int64_t qr0 = static_cast<int64_t>(b) * k.Hq + static_cast<int64_t>(h) * k.G + g0;  // first query row
   if (TO_GLOBAL && g0 == 0 && tid == 0) a.ctr[bh] = 0;
   const float c2 = a.sm_scale * kLog2e;
-  // window keys: thread pair (tk, half) holds slot tk = tid / 2, coordinates
-  // 64 half .. 64 half + 63 (past d: zero); rows hold d coordinates.  The
+  // window keys as matrix-core B operands: wave wv takes 16-slot tiles wv,
+  // wv + 4, ...; lane (n, kg) holds slot 16 tile + n, coordinates 32 kg + 8 i
+  // .. +7 for product i = 0..3 (16 bytes of the fp16 row; past d: zero).  The
   // ring has W slots whatever the length, so the loads are bounded by W and
   // issued at once, beside the length's own load; slots at or past the
   // length are loaded but never used.
-  const int tk0 = tid >> 1, half = tid & 1;
-  uint4 kv[8];
-  if (tk0 < k.W) {
-    const uint4* kr = reinterpret_cast<const uint4*>(a.k_win + (bh * k.W + tk0) * k.d + 64 * half);
+  const int n16 = lane & 15, kg = lane >> 4;
+  const int ntile_w = (k.W + 15) / 16;
+  auto load_tile = [&](int tile, win_u4 (&kt)[4]) {
+    const int slot = 16 * tile + n16;
 #pragma unroll
-    for (int c = 0; c < 8; ++c) kv[c] = 64 * half + 8 * c < k.d ? kr[c] : make_uint4(0u, 0u, 0u, 0u);
-  }
+    for (int i = 0; i < 4; ++i) {
+      const int c = 32 * kg + 8 * i;
+      kt[i] = win_u4{0u, 0u, 0u, 0u};
+      if (slot < k.W && c < k.d)
+        kt[i] = *reinterpret_cast<const win_u4*>(a.k_win + (bh * k.W + slot) * k.d + c);
+    }
+  };
+  win_u4 kb0[4], kb1[4];
+  if (wv < ntile_w) load_tile(wv, kb0);
+  if (wv + 4 < ntile_w) load_tile(wv + 4, kb1);
   // window values: thread (c4, q8) holds slots q8, q8 + 8, ... (first 16), coordinates c4 .. c4+3
   // (threads with c4 >= d read slot 0's first coordinates and discard them)
   const bool vlive = c4 < k.d;
@@ -220,41 +248,48 @@ __device__ void window_partial(const DecodeArgs& a, const KParams& k, int b, int
     qw[g][i] = i < k.d ? load_any(a.q, (qr0 + g) * k.d + i, a.q_dtype) * c2 : 0.0f;
   }
   lds_barrier();
-  // scores: two threads per slot, 64 coordinates each; slots past the first
-  // 128 are loaded here
-  for (int e = tid; e < 2 * nwin; e += kSmallThreads) {
-    const int tk = e >> 1;
-    if (e >= kSmallThreads) {
-      const uint4* kr = reinterpret_cast<const uint4*>(a.k_win + (bh * k.W + tk) * k.d + 64 * half);
+  // scores on the matrix cores (16x16x32 fp16 products, fp32 sums): A row r
+  // of a product is query 2 (r >> 2) + (r & 1), its fp16 part (r >> 1) & 1
+  // (the value rounded to fp16, then the remainder: about 22 bits of the
+  // scaled query); the keys are fp16 already.  Lane (n, kg) of the result
+  // then holds slot n of the tile for queries 2 kg and 2 kg + 1, each the sum
+  // of its two parts.
+  const int ag = 2 * (n16 >> 2) + (n16 & 1), apart = (n16 >> 1) & 1;
+  win_u4 aq[4];
 #pragma unroll
-      for (int c = 0; c < 8; ++c) kv[c] = 64 * half + 8 * c < k.d ? kr[c] : make_uint4(0u, 0u, 0u, 0u);
-    }
-    float sg[GW];
+  for (int i = 0; i < 4; ++i) {
+    const float* qa = &qw[ag < GW ? ag : 0][32 * kg + 8 * i];
+    const float4 q0 = *reinterpret_cast<const float4*>(qa), q1 = *reinterpret_cast<const float4*>(qa + 4);
+    aq[i] = win_u4{win_pack(q0.x, q0.y, apart), win_pack(q0.z, q0.w, apart), win_pack(q1.x, q1.y, apart),
+                   win_pack(q1.z, q1.w, apart)};
+    if (ag >= GW) aq[i] = win_u4{0u, 0u, 0u, 0u};
+  }
+  const int ntile = (nwin + 15) / 16;
+  auto score_tile = [&](int tile, const win_u4 (&kt)[4]) {
+    win_f4 dm = win_f4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-    for (int g = 0; g < GW; ++g) sg[g] = 0.0f;
-#pragma unroll
-    for (int c = 0; c < 8; ++c) {
-      const uint32_t u4v[4] = {kv[c].x, kv[c].y, kv[c].z, kv[c].w};
-#pragma unroll
-      for (int e2 = 0; e2 < 4; ++e2) {
-        const int i = 64 * half + 8 * c + 2 * e2;
-        const float k0 = half_bits_to_float(static_cast<uint16_t>(u4v[e2] & 0xffffu));
-        const float k1 = half_bits_to_float(static_cast<uint16_t>(u4v[e2] >> 16));
-#pragma unroll
-        for (int g = 0; g < GW; ++g) sg[g] = fmaf(qw[g][i + 1], k1, fmaf(qw[g][i], k0, sg[g]));
-      }
-    }
-#pragma unroll
-    for (int g = 0; g < GW; ++g) sg[g] += __shfl_xor(sg[g], 1, 64);
-    if (half == 0) {
+    for (int i = 0; i < 4; ++i) dm = win_mfma(aq[i], kt[i], dm);
+    const int tk = 16 * tile + n16;
+    if (tk < nwin) {
       // slot tk holds the largest position p < T with p = tk (mod W)
       const int pos = tk + k.W * ((T - 1 - tk) / k.W);
 #pragma unroll
-      for (int g = 0; g < GW; ++g) {
-        ls[g][tk] = sg[g];
-        if (a.dbg_logits) a.dbg_logits[(qr0 + g) * a.logits_stride + pos] = sg[g] * kLn2;
+      for (int i2 = 0; i2 < 2; ++i2) {
+        const int g = 2 * kg + i2;
+        if (g < GW) {
+          const float sg = dm[i2] + dm[i2 + 2];
+          ls[g][tk] = sg;
+          if (a.dbg_logits) a.dbg_logits[(qr0 + g) * a.logits_stride + pos] = sg * kLn2;
+        }
       }
     }
+  };
+  if (wv < ntile) score_tile(wv, kb0);
+  if (wv + 4 < ntile) score_tile(wv + 4, kb1);
+  for (int tile = wv + 8; tile < ntile; tile += 4) {  // windows past 128 slots
+    win_u4 kt[4];
+    load_tile(tile, kt);
+    score_tile(tile, kt);
   }
   lds_barrier();
   // per query head (one wave each): maximum, weights, their sum
@@ -449,7 +484,10 @@ __device__ void make_plan(const DecodeArgs& a, const KParams& k) {
 // a short chain of memory round trips).
 template <int GW>
 __global__ __launch_bounds__(kSmallThreads) void prep_kernel(DecodeArgs a, DevTables t, KParams k, int qjl) {
-  __shared__ float qv[GW][kD], qr[GW][kD], part[8][GW][kD];
+  // (rows read as float4: 16-byte aligned)
+  __shared__ __attribute__((aligned(16))) float qv[GW][kD];
+  __shared__ __attribute__((aligned(16))) float qr[GW][kD];
+  __shared__ __attribute__((aligned(16))) float part[8][GW][kD];
   __shared__ float ls[GW][kMaxWindow];
   __shared__ float sMw[GW], sLw[GW];
   // with balanced splits the grid has one more row, the last: its first
@@ -665,7 +703,11 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(DecodeArgs a, DevTab
 // matrix-core scan when it has more than kFuseMaxSplits splits.
 template <int GW>
 __global__ __launch_bounds__(kSmallThreads) void finalize_kernel(DecodeArgs a, DevTables t, KParams k) {
-  __shared__ float acc[GW][kD], qw[GW][kD], wacc[GW][kD], part[8][GW][kD];
+  // (rows read as float4: 16-byte aligned)
+  __shared__ __attribute__((aligned(16))) float acc[GW][kD];
+  __shared__ __attribute__((aligned(16))) float qw[GW][kD];
+  __shared__ __attribute__((aligned(16))) float wacc[GW][kD];
+  __shared__ __attribute__((aligned(16))) float part[8][GW][kD];
   __shared__ float ls[GW][kMaxWindow];
   __shared__ float fin[finalize_scratch_floats<kSmallThreads, GW>()];
   __shared__ float sL[GW], sW[GW], sMw[GW], sLw[GW];
