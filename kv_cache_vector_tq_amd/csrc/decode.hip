@@ -50,6 +50,31 @@ __device__ inline win_f4 win_mfma(win_u4 a, win_u4 b, win_f4 c) {
                                                  0, 0);
 }
 
+// max / sum over a wave: within each row of 16 lanes by DPP (row rotations
+// by 8 and 4, then quad swaps), then the four rows' results read from lanes
+// 0, 16, 32 and 48 (no LDS round trips, unlike a shuffle butterfly)
+template <int CTRL>
+__device__ inline float win_dpp(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xF, 0xF, false));
+}
+__device__ inline float win_rows4(float x, int i) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 16 * i));
+}
+__device__ inline float win_wave_max(float x) {
+  x = fmaxf(x, win_dpp<0x128>(x));
+  x = fmaxf(x, win_dpp<0x124>(x));
+  x = fmaxf(x, win_dpp<0x4E>(x));
+  x = fmaxf(x, win_dpp<0xB1>(x));
+  return fmaxf(fmaxf(win_rows4(x, 0), win_rows4(x, 1)), fmaxf(win_rows4(x, 2), win_rows4(x, 3)));
+}
+__device__ inline float win_wave_sum(float x) {
+  x += win_dpp<0x128>(x);
+  x += win_dpp<0x124>(x);
+  x += win_dpp<0x4E>(x);
+  x += win_dpp<0xB1>(x);
+  return (win_rows4(x, 0) + win_rows4(x, 1)) + (win_rows4(x, 2) + win_rows4(x, 3));
+}
+
 // two floats as fp16 pairs: part 0 rounded to fp16, part 1 the remainder
 __device__ inline uint32_t win_pack(float x0, float x1, int part) {
   const _Float16 h0 = static_cast<_Float16>(x0), h1 = static_cast<_Float16>(x1);
@@ -296,14 +321,14 @@ __device__ void window_partial(const DecodeArgs& a, const KParams& k, int b, int
   for (int g = wv; g < GW; g += kSmallThreads / 64) {
     float m = -INFINITY;
     for (int tk = lane; tk < nwin; tk += 64) m = fmaxf(m, ls[g][tk]);
-    m = wave_max(m);
+    m = win_wave_max(m);
     float lw = 0.0f;
     for (int tk = lane; tk < nwin; tk += 64) {
       const float w = exp2f(ls[g][tk] - m);
       ls[g][tk] = w;
       lw += w;
     }
-    lw = wave_sum(lw);
+    lw = win_wave_sum(lw);
     if (lane == 0) {
       sMw[g] = m;
       sLw[g] = lw;
